@@ -1,0 +1,431 @@
+"""Plain, slow CPU reference of one MoE layer, forward and backward.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Every function below is
+written from its definition, in float64 unless a precision is stated, with
+NumPy matmul / sort / cumsum as the only library steps.
+
+Citations use [MCore-MoE] = the page "Scalable Training of Mixture-of-Experts
+Models with Megatron Core", section 2 (Megatron-Core MoE Architecture), whose
+four bullets Route / Dispatch / Expert Computation / Combine define the four
+stages, and section 5 (Reduced-Precision Training), bullet "Selective
+precision" (the router stays in FP32).
+
+Readings where the page is silent (each is also listed in the design notes):
+  * Selection key: z = fp32(logit + bias).  Softmax and sigmoid are strictly
+    increasing, so the top-k of the probabilities is the top-k of z; ordering
+    on z avoids ulp differences of exp between implementations.
+  * Ties: equal keys go to the lower expert index; the k slots of a token are
+    listed by (key descending, index ascending).
+  * Bias: a per-expert constant added to the logits before scoring; it gets
+    no gradient.
+  * Within an expert's segment, rows are in ascending token order (stable).
+  * SwiGLU expert: h = silu(x W1) * (x W3), y = h W2, silu(a) = a * sigmoid(a);
+    W13 = [W1 | W3] concatenated along the ffn axis.
+  * Shared expert: same SwiGLU form, weight 1, added after the routed sum.
+  * Scaling factor on the routed sum: 1.
+"""
+
+import numpy as np
+
+SOFTMAX = "softmax"
+SIGMOID = "sigmoid"
+
+__all__ = [
+    "SOFTMAX", "SIGMOID", "f64", "router_logits", "select_topk", "gates", "dispatch_map",
+    "route", "route_bwd", "router_logits_bwd", "permute", "permute_bwd",
+    "grouped_gemm_fwd", "grouped_gemm_dgrad", "grouped_gemm_wgrad", "sigmoid", "silu",
+    "swiglu", "swiglu_bwd", "unpermute_combine", "unpermute_combine_bwd",
+    "expert_ffn", "expert_ffn_bwd", "layer_forward", "layer_backward",
+    "expert_wgrad_columns",
+]
+
+
+def f64(a):
+    """Exact widening of an fp32/bf16-valued array to float64."""
+    return np.asarray(a, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Route  ([MCore-MoE] section 2, Route; section 5, Selective precision)
+# ---------------------------------------------------------------------------
+
+def router_logits(x, w_r, logit_bias=None):
+    """Token hidden states -> expert logits, kept in fp32.
+
+    logits = x @ W_r evaluated in float64 and rounded once to fp32; a bias, if
+    given, is then added with one IEEE fp32 addition (round to nearest even).
+    The result is the fp32 selection key z of every later step.
+    """
+    l32 = (f64(x) @ f64(w_r)).astype(np.float32)
+    if logit_bias is not None:
+        l32 = (l32 + np.asarray(logit_bias, dtype=np.float32)).astype(np.float32)
+    return l32
+
+
+def select_topk(z, k):
+    """The k highest-scoring experts of each token.
+
+    Order: key descending, then expert index ascending, so that among equal
+    keys the lower expert index wins.  Returns int32 [T, k].
+    """
+    z = np.asarray(z, dtype=np.float32)
+    assert np.all(np.isfinite(z)), "non-finite router logits are a caller error"
+    T, E = z.shape
+    assert 1 <= k <= E
+    idx = np.broadcast_to(np.arange(E), (T, E))
+    # lexsort sorts by the last key first: primary -z (descending z), then index.
+    # -(+0.0) and -(-0.0) compare equal, so signed zeros tie as they should.
+    order = np.lexsort((idx, -z.astype(np.float64)), axis=-1)
+    return order[:, :k].astype(np.int32)
+
+
+def sigmoid(v):
+    v = f64(v)
+    return 1.0 / (1.0 + np.exp(-v))
+
+
+def gates(z, topk_idx, score, renorm):
+    """Routing weights of the chosen experts (float64).
+
+    softmax, renorm   : softmax over the chosen keys (= full softmax
+                        renormalised over the chosen k).
+    softmax, no renorm: full softmax over all E experts, read at the chosen.
+    sigmoid, renorm   : sigmoid(z_j) / sum over chosen of sigmoid.
+    sigmoid, no renorm: sigmoid(z_j).
+    """
+    z = f64(z)
+    zk = np.take_along_axis(z, topk_idx.astype(np.int64), axis=1)
+    if score == SOFTMAX:
+        if renorm:
+            ex = np.exp(zk - zk.max(axis=1, keepdims=True))
+            return ex / ex.sum(axis=1, keepdims=True)
+        ex = np.exp(z - z.max(axis=1, keepdims=True))
+        p = ex / ex.sum(axis=1, keepdims=True)
+        return np.take_along_axis(p, topk_idx.astype(np.int64), axis=1)
+    if score == SIGMOID:
+        s = sigmoid(zk)
+        return s / s.sum(axis=1, keepdims=True) if renorm else s
+    raise ValueError(score)
+
+
+def dispatch_map(topk_idx, E):
+    """Per-expert counts, segment offsets and the permutation into
+    expert-contiguous order ([MCore-MoE] section 2, Dispatch: tokens are
+    permuted by destination expert).
+
+    Stable counting sort: experts in ascending order, and inside each
+    expert's segment the tokens in ascending order.  Returns
+      counts   int64 [E]      number of (token, slot) pairs routed to e
+      offsets  int64 [E+1]    offsets[0] = 0, offsets[e+1] = offsets[e] + counts[e]
+      dst_row  int32 [T, k]   row of the permuted matrix holding (t, j)
+      src_token int32 [T*k]   token held by each permuted row
+    """
+    T, k = topk_idx.shape
+    counts = np.zeros(E, dtype=np.int64)
+    for e in topk_idx.ravel():
+        counts[e] += 1
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    dst_row = np.full((T, k), -1, dtype=np.int32)
+    src_token = np.full(T * k, -1, dtype=np.int32)
+    r = 0
+    for e in range(E):
+        ts, js = np.nonzero(topk_idx == e)  # row-major scan: ascending t
+        n = len(ts)
+        src_token[r:r + n] = ts
+        dst_row[ts, js] = r + np.arange(n)
+        r += n
+    assert r == T * k
+    return counts, offsets, dst_row, src_token
+
+
+def route(z, k, score, renorm):
+    """Route stage on fp32 keys z [T, E]: selection, weights and the dispatch
+    map.  Dropless: every (token, slot) pair gets a row."""
+    z = np.asarray(z, dtype=np.float32)
+    idx = select_topk(z, k)
+    w = gates(z, idx, score, renorm)
+    counts, offsets, dst_row, src_token = dispatch_map(idx, z.shape[1])
+    return dict(topk_idx=idx, topk_w=w, counts=counts, offsets=offsets,
+                dst_row=dst_row, src_token=src_token)
+
+
+def route_bwd(z, topk_idx, topk_w, d_topk_w, score, renorm):
+    """Gradient of the routing weights with respect to the keys z (= logits,
+    the bias being constant).  The discrete selection itself carries no
+    gradient.  With g = sum over chosen of w_l * dw_l:
+      softmax, renorm   : dz_j = w_j (dw_j - g) on chosen, 0 elsewhere
+      softmax, no renorm: dz_e = p_e (G_e - g) for every e, G_e = dw_j if
+                          e is chosen slot j else 0
+      sigmoid, renorm   : dz_j = (dw_j - g) / S * s_j (1 - s_j), S = sum s
+      sigmoid, no renorm: dz_j = dw_j * s_j (1 - s_j)
+    """
+    z = f64(z)
+    T, E = z.shape
+    idx = topk_idx.astype(np.int64)
+    w = f64(topk_w)
+    dw = f64(d_topk_w)
+    dz = np.zeros((T, E))
+    g = (w * dw).sum(axis=1, keepdims=True)
+    if score == SOFTMAX:
+        if renorm:
+            np.put_along_axis(dz, idx, w * (dw - g), axis=1)
+        else:
+            ex = np.exp(z - z.max(axis=1, keepdims=True))
+            p = ex / ex.sum(axis=1, keepdims=True)
+            G = np.zeros((T, E))
+            np.put_along_axis(G, idx, dw, axis=1)
+            dz = p * (G - g)
+    elif score == SIGMOID:
+        s = sigmoid(np.take_along_axis(z, idx, axis=1))
+        if renorm:
+            S = s.sum(axis=1, keepdims=True)
+            np.put_along_axis(dz, idx, (dw - g) / S * s * (1.0 - s), axis=1)
+        else:
+            np.put_along_axis(dz, idx, dw * s * (1.0 - s), axis=1)
+    else:
+        raise ValueError(score)
+    return dz
+
+
+def router_logits_bwd(x, w_r, dz):
+    """dW_r = x^T dz and the router's share of dx, dz W_r^T (float64)."""
+    return f64(x).T @ f64(dz), f64(dz) @ f64(w_r).T
+
+
+# ---------------------------------------------------------------------------
+# Dispatch ([MCore-MoE] section 2, Dispatch) and Combine (section 2, Combine)
+# ---------------------------------------------------------------------------
+
+def permute(x, src_token):
+    """Rows in expert-contiguous order: X_perm[r] = x[src_token[r]]."""
+    return np.asarray(x)[np.asarray(src_token, dtype=np.int64)]
+
+
+def permute_bwd(dx_perm, dst_row, addends=()):
+    """Adjoint of ``permute``: dx[t] = sum_j dX_perm[dst_row[t, j]] (+ addends)."""
+    dx_perm = f64(dx_perm)
+    T, k = dst_row.shape
+    dx = np.zeros((T, dx_perm.shape[1]))
+    for t in range(T):
+        for j in range(k):
+            dx[t] += dx_perm[dst_row[t, j]]
+    for a in addends:
+        dx += f64(a)
+    return dx
+
+
+def unpermute_combine(y_perm, topk_w, dst_row, shared_y=None):
+    """out[t] = sum_j w[t, j] * Y[dst_row[t, j]] (+ shared expert output):
+    tokens return to sequence order weighted by their routing weights."""
+    y_perm = f64(y_perm)
+    w = f64(topk_w)
+    T, k = dst_row.shape
+    out = np.zeros((T, y_perm.shape[1]))
+    for t in range(T):
+        for j in range(k):
+            out[t] += w[t, j] * y_perm[dst_row[t, j]]
+    if shared_y is not None:
+        out += f64(shared_y)
+    return out
+
+
+def unpermute_combine_bwd(dout, y_perm, topk_w, dst_row):
+    """Adjoint of ``unpermute_combine``:
+    dY[dst_row[t, j]] = w[t, j] * dout[t],  d_w[t, j] = <dout[t], Y[dst_row[t, j]]>.
+    (The shared expert's output gradient is dout itself.)"""
+    dout = f64(dout)
+    y_perm = f64(y_perm)
+    w = f64(topk_w)
+    T, k = dst_row.shape
+    dy = np.zeros_like(y_perm)
+    dw = np.zeros((T, k))
+    for t in range(T):
+        for j in range(k):
+            r = dst_row[t, j]
+            dy[r] = w[t, j] * dout[t]
+            dw[t, j] = dout[t] @ y_perm[r]
+    return dy, dw
+
+
+# ---------------------------------------------------------------------------
+# Expert computation ([MCore-MoE] section 2, Expert Computation)
+# ---------------------------------------------------------------------------
+
+def grouped_gemm_fwd(A, B, offsets):
+    """C[rows of g] = A[rows of g] @ B[g]; rows of g = [offsets[g], offsets[g+1])."""
+    A = f64(A)
+    G = len(offsets) - 1
+    C = np.zeros((A.shape[0], B.shape[2]))
+    for g in range(G):
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        C[lo:hi] = A[lo:hi] @ f64(B[g])
+    return C
+
+
+def grouped_gemm_dgrad(dC, B, offsets):
+    """dA[rows of g] = dC[rows of g] @ B[g]^T."""
+    dC = f64(dC)
+    G = len(offsets) - 1
+    dA = np.zeros((dC.shape[0], B.shape[1]))
+    for g in range(G):
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        dA[lo:hi] = dC[lo:hi] @ f64(B[g]).T
+    return dA
+
+
+def grouped_gemm_wgrad(A, dC, offsets):
+    """dB[g] = A[rows of g]^T @ dC[rows of g] (zero for an empty group)."""
+    A = f64(A)
+    dC = f64(dC)
+    G = len(offsets) - 1
+    dB = np.zeros((G, A.shape[1], dC.shape[1]))
+    for g in range(G):
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        dB[g] = A[lo:hi].T @ dC[lo:hi]
+    return dB
+
+
+def silu(a):
+    a = f64(a)
+    return a / (1.0 + np.exp(-a))
+
+
+def swiglu(ab):
+    """H = silu(A) * B with A = ab[:, :f] and B = ab[:, f:]."""
+    ab = f64(ab)
+    f = ab.shape[1] // 2
+    return silu(ab[:, :f]) * ab[:, f:]
+
+
+def swiglu_bwd(dh, ab):
+    """dA = dH * B * s (1 + A (1 - s)),  dB = dH * silu(A),  s = sigmoid(A)."""
+    ab = f64(ab)
+    dh = f64(dh)
+    f = ab.shape[1] // 2
+    a, b = ab[:, :f], ab[:, f:]
+    s = sigmoid(a)
+    return np.concatenate([dh * b * s * (1.0 + a * (1.0 - s)), dh * a * s], axis=1)
+
+
+def expert_ffn(x_t, w13_e, w2_e):
+    """One SwiGLU expert on one token row: returns (a, b, h, y)."""
+    x_t = f64(x_t)
+    w13_e = f64(w13_e)
+    f = w13_e.shape[1] // 2
+    a = x_t @ w13_e[:, :f]
+    b = x_t @ w13_e[:, f:]
+    h = silu(a) * b
+    return a, b, h, h @ f64(w2_e)
+
+
+def expert_ffn_bwd(x_t, w13_e, w2_e, a, b, h, dy):
+    """Backward of ``expert_ffn`` for one row: returns (dx_t, dW13_e, dW2_e)."""
+    x_t = f64(x_t)
+    w13_e = f64(w13_e)
+    w2_e = f64(w2_e)
+    dh = dy @ w2_e.T
+    s = sigmoid(a)
+    da = dh * b * s * (1.0 + a * (1.0 - s))
+    db = dh * a * s
+    dab = np.concatenate([da, db])
+    return dab @ w13_e.T, np.outer(x_t, dab), np.outer(h, dy)
+
+
+def layer_forward(x, w_r, w13, w2, k, score, renorm, logit_bias=None,
+                  shared=None, z=None):
+    """The four-stage forward pass as a per-token loop over each token's k
+    experts (the one-expert-at-a-time view of [MCore-MoE] section 2, Expert
+    Computation).  ``shared`` = (ws13 [d, 2fs], ws2 [fs, d]) or None.
+    ``z`` may give the fp32 keys directly; by default they are computed with
+    ``router_logits``.  Returns a cache dict consumed by ``layer_backward``."""
+    x = f64(x)
+    T, d = x.shape
+    if z is None:
+        z = router_logits(x, w_r, logit_bias)
+    r = route(z, k, score, renorm)
+    idx, w = r["topk_idx"], r["topk_w"]
+    out = np.zeros((T, d))
+    acts = {}
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j])
+            a, b, h, y = expert_ffn(x[t], w13[e], w2[e])
+            acts[(t, j)] = (a, b, h, y)
+            out[t] += w[t, j] * y
+    shared_acts = None
+    if shared is not None:
+        shared_acts = []
+        for t in range(T):
+            a, b, h, y = expert_ffn(x[t], shared[0], shared[1])
+            shared_acts.append((a, b, h, y))
+            out[t] += y
+    return dict(out=out, z=z, route=r, acts=acts, shared_acts=shared_acts,
+                x=x, w_r=w_r, w13=w13, w2=w2, k=k, score=score, renorm=renorm,
+                shared=shared)
+
+
+def layer_backward(cache, dout):
+    """Backward of ``layer_forward`` by the chain rule, the same per-token
+    loop in reverse.  Returns dx, d_logits (= dz), dW_r, dW13, dW2 and, with a
+    shared expert, dWs13 and dWs2."""
+    dout = f64(dout)
+    x, w13, w2 = cache["x"], cache["w13"], cache["w2"]
+    r = cache["route"]
+    idx, w = r["topk_idx"], r["topk_w"]
+    T, k = idx.shape
+    dx = np.zeros_like(x)
+    dW13 = np.zeros(np.shape(w13))
+    dW2 = np.zeros(np.shape(w2))
+    dw = np.zeros((T, k))
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j])
+            a, b, h, y = cache["acts"][(t, j)]
+            dw[t, j] = dout[t] @ y
+            dxt, dw13, dw2 = expert_ffn_bwd(x[t], w13[e], w2[e], a, b, h, w[t, j] * dout[t])
+            dx[t] += dxt
+            dW13[e] += dw13
+            dW2[e] += dw2
+    res = {}
+    if cache["shared"] is not None:
+        ws13, ws2 = cache["shared"]
+        dWs13 = np.zeros(np.shape(ws13))
+        dWs2 = np.zeros(np.shape(ws2))
+        for t in range(T):
+            a, b, h, _ = cache["shared_acts"][t]
+            dxt, dw13, dw2 = expert_ffn_bwd(x[t], ws13, ws2, a, b, h, dout[t])
+            dx[t] += dxt
+            dWs13 += dw13
+            dWs2 += dw2
+        res.update(dWs13=dWs13, dWs2=dWs2)
+    dz = route_bwd(cache["z"], idx, w, dw, cache["score"], cache["renorm"])
+    dWr, dx_router = router_logits_bwd(x, cache["w_r"], dz)
+    dx += dx_router
+    res.update(dx=dx, d_logits=dz, dW_r=dWr, dW13=dW13, dW2=dW2, d_topk_w=dw)
+    return res
+
+
+def expert_wgrad_columns(x_rows, dy_rows, w13_e, w2_e, cols):
+    """Weight gradients of one expert restricted to ffn columns ``cols``.
+
+    x_rows [n, d] are the token rows routed to the expert and dy_rows [n, d]
+    their output gradients (routing weight already applied).  Column c of W1
+    and W3 and row c of W2 depend only on activation column c, so
+      dW1[:, c] = sum_rows x * dA[:, c],  dW3[:, c] = sum_rows x * dB[:, c],
+      dW2[c, :] = sum_rows h[:, c] * dy.
+    Returns (dW1[:, cols], dW3[:, cols], dW2[cols, :]).
+    """
+    x_rows = f64(x_rows)
+    dy_rows = f64(dy_rows)
+    w13_e = f64(w13_e)
+    f = w13_e.shape[1] // 2
+    cols = np.asarray(cols)
+    a = x_rows @ w13_e[:, cols]
+    b = x_rows @ w13_e[:, f + cols]
+    s = sigmoid(a)
+    h = a * s * b
+    dh = dy_rows @ f64(w2_e)[cols, :].T
+    da = dh * b * s * (1.0 + a * (1.0 - s))
+    db = dh * a * s
+    return x_rows.T @ da, x_rows.T @ db, h.T @ dy_rows

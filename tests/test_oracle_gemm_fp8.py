@@ -1,0 +1,124 @@
+"""Pins of the oracle's grouped GEMMs (against one dense block-diagonal
+product) and of its FP8 E4M3 codec (against the format's definition worked by
+hand, torch's float8_e4m3fn cast, and exhaustive round trips)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import fp8
+from golden_io import read_sections
+
+
+def _block_diag(A, offsets, G):
+    M, K = A.shape
+    out = np.zeros((M, G * K))
+    for g in range(G):
+        lo, hi = offsets[g], offsets[g + 1]
+        out[lo:hi, g * K:(g + 1) * K] = A[lo:hi]
+    return out
+
+
+@pytest.mark.parametrize("offsets", [[0, 5, 5, 12, 30], [0, 30], [0, 0, 0, 30, 30]])
+def test_grouped_gemm_is_one_block_diagonal_product(offsets):
+    rng = np.random.default_rng(0)
+    G = len(offsets) - 1
+    M, K, N = 30, 7, 9
+    A = rng.standard_normal((M, K))
+    B = rng.standard_normal((G, K, N))
+    dC = rng.standard_normal((M, N))
+    Abd = _block_diag(A, offsets, G)
+    Bst = B.reshape(G * K, N)
+    np.testing.assert_allclose(oracle.grouped_gemm_fwd(A, B, offsets), Abd @ Bst, rtol=0, atol=1e-12)
+    dAbd = dC @ Bst.T
+    dA = oracle.grouped_gemm_dgrad(dC, B, offsets)
+    for g in range(G):
+        lo, hi = offsets[g], offsets[g + 1]
+        np.testing.assert_allclose(dA[lo:hi], dAbd[lo:hi, g * K:(g + 1) * K], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(oracle.grouped_gemm_wgrad(A, dC, offsets).reshape(G * K, N),
+                               Abd.T @ dC, rtol=0, atol=1e-12)
+
+
+def test_swiglu_bwd_finite_differences():
+    rng = np.random.default_rng(1)
+    ab = rng.standard_normal((5, 8))
+    dh = rng.standard_normal((5, 4))
+    got = oracle.swiglu_bwd(dh, ab)
+    eps = 1e-6
+    num = np.zeros_like(ab)
+    for pos in np.ndindex(ab.shape):
+        p, m = ab.copy(), ab.copy()
+        p[pos] += eps
+        m[pos] -= eps
+        num[pos] = ((oracle.swiglu(p) - oracle.swiglu(m)) * dh).sum() / (2 * eps)
+    np.testing.assert_allclose(got, num, rtol=0, atol=1e-8)
+
+
+def test_e4m3_landmarks():
+    g = read_sections("e4m3_landmarks.txt")
+    for code, val in g["decode"]:
+        got = fp8.decode(int(code, 16))
+        want = float(val)
+        if np.isnan(want):
+            assert np.isnan(got)
+        else:
+            assert got == want and np.signbit(got) == np.signbit(want), code
+    for val, code in g["encode"]:
+        assert int(fp8.encode(np.float32(float(val)))) == int(code, 16), val
+
+
+def test_e4m3_decode_matches_torch_for_all_codes():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = fp8.decode(np.arange(256))
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[fin], ref[fin])
+
+
+def test_e4m3_encode_round_trip_and_torch_cast():
+    vals = fp8.decode(np.arange(256))
+    fin = ~np.isnan(vals)
+    codes = np.arange(256)[fin]
+    back = fp8.encode(vals[fin].astype(np.float32)).astype(np.int64)
+    # -0.0 keeps its sign code
+    np.testing.assert_array_equal(back, codes)
+    rng = np.random.default_rng(2)
+    v = np.concatenate([rng.standard_normal(20000) * s for s in (1e-3, 1e-1, 1.0, 30.0, 200.0)])
+    v = np.clip(v, -448, 448).astype(np.float32)
+    # midpoints between neighbours exercise ties-to-even
+    pos = np.sort(vals[fin & (vals >= 0)])
+    mids = ((pos[1:] + pos[:-1]) / 2).astype(np.float32)
+    v = np.concatenate([v, mids, -mids])
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(fp8.encode(v), ref)
+
+
+def test_e4m3_saturates():
+    v = np.array([449.0, 480.0, 1e6, np.inf, -np.inf, -1e6], dtype=np.float32)
+    np.testing.assert_array_equal(fp8.encode(v), [0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE])
+    assert fp8.encode(np.float32(np.nan)) == 0x7F
+
+
+def test_blockwise_quantizers():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((4, 256)).astype(np.float32)
+    x[1, :128] = 0.0
+    q, s = fp8.quantize_rows(x)
+    assert s.shape == (4, 2) and s[1, 0] == 1.0
+    deq = fp8.dequantize_rows(q, s)
+    # amax of each tile maps to +-448 exactly, and the relative error of
+    # E4M3 with 3 mantissa bits is at most 2^-4 of the tile's amax.
+    for i in range(4):
+        for b in range(2):
+            tile = x[i, b * 128:(b + 1) * 128]
+            am = np.abs(tile).max()
+            if am == 0:
+                assert np.all(q[i, b * 128:(b + 1) * 128] == 0)
+                continue
+            assert np.abs(fp8.decode(q[i, b * 128:(b + 1) * 128])).max() == 448.0
+            assert np.abs(deq[i, b * 128:(b + 1) * 128] - tile).max() <= am * 2.0 ** -4
+    w = rng.standard_normal((256, 384)).astype(np.float32)
+    qw, sw = fp8.quantize_blocks(w)
+    assert sw.shape == (2, 3)
+    assert np.abs(fp8.dequantize_blocks(qw, sw) - w).max() <= np.abs(w).max() * 2.0 ** -4

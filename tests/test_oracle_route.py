@@ -1,0 +1,149 @@
+"""Pins of the oracle's Route and Dispatch stages against things other than
+itself: a hand-worked example, brute force over all k-subsets, invariants,
+and the k = E special case (full softmax, checked against SciPy)."""
+import itertools
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+from golden_io import read_sections
+
+
+
+def _floats(rows):
+    return np.array([[float(v) for v in r] for r in rows])
+
+
+def test_worked_example():
+    g = read_sections("route_worked_example.txt")
+    z = _floats(g["keys"]).astype(np.float32)
+    k = 2
+    r = oracle.route(z, k, oracle.SOFTMAX, True)
+    np.testing.assert_array_equal(r["topk_idx"], _floats(g["topk_idx"]).astype(np.int32))
+    np.testing.assert_allclose(r["topk_w"], _floats(g["topk_w_softmax_renorm"]), rtol=0, atol=1e-15)
+    np.testing.assert_array_equal(r["counts"], _floats(g["counts"]).ravel())
+    np.testing.assert_array_equal(r["offsets"], _floats(g["offsets"]).ravel())
+    np.testing.assert_array_equal(r["src_token"], _floats(g["src_token"]).ravel())
+    np.testing.assert_array_equal(r["dst_row"], _floats(g["dst_row"]).astype(np.int32))
+    rs = oracle.route(z, k, oracle.SIGMOID, True)
+    np.testing.assert_array_equal(rs["topk_idx"], r["topk_idx"])
+    np.testing.assert_allclose(rs["topk_w"], _floats(g["topk_w_sigmoid_renorm"]), rtol=0, atol=1e-15)
+
+
+def _brute_topk(zrow, k):
+    """The unique k-subset S with: every chosen key > every unchosen key, or
+    equal with a lower index.  Found by trying all subsets."""
+    E = len(zrow)
+    hits = []
+    for S in itertools.combinations(range(E), k):
+        ok = all((zrow[c] > zrow[u]) or (zrow[c] == zrow[u] and c < u)
+                 for c in S for u in range(E) if u not in S)
+        if ok:
+            hits.append(S)
+    assert len(hits) == 1
+    S = hits[0]
+    return sorted(S, key=lambda e: (-zrow[e], e))
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("E,k", [(4, 2), (6, 3), (8, 1), (5, 5)])
+def test_topk_brute_force(seed, E, k):
+    rng = np.random.default_rng(seed)
+    T = 40
+    # coarse values so that many ties occur
+    z = (rng.integers(-3, 4, size=(T, E)) * 0.5).astype(np.float32)
+    idx = oracle.select_topk(z, k)
+    for t in range(T):
+        assert list(idx[t]) == _brute_topk([float(v) for v in z[t]], k)
+
+
+def test_all_equal_keys_pick_lowest_indices():
+    z = np.full((3, 8), 0.25, dtype=np.float32)
+    idx = oracle.select_topk(z, 3)
+    np.testing.assert_array_equal(idx, np.tile(np.arange(3), (3, 1)))
+
+
+@pytest.mark.parametrize("score", [oracle.SOFTMAX, oracle.SIGMOID])
+@pytest.mark.parametrize("renorm", [True, False])
+def test_dispatch_invariants(score, renorm):
+    rng = np.random.default_rng(7)
+    T, E, k = 257, 16, 4
+    z = rng.standard_normal((T, E)).astype(np.float32)
+    r = oracle.route(z, k, score, renorm)
+    idx, dst, src = r["topk_idx"], r["dst_row"], r["src_token"]
+    assert r["counts"].sum() == T * k
+    assert np.all(np.diff(r["offsets"]) >= 0) and r["offsets"][-1] == T * k
+    # each token's k experts are distinct
+    assert all(len(set(row)) == k for row in idx)
+    # src_token and dst_row are mutually inverse bijections
+    assert sorted(dst.ravel()) == list(range(T * k))
+    for t in range(T):
+        for j in range(k):
+            assert src[dst[t, j]] == t
+            e = idx[t, j]
+            assert r["offsets"][e] <= dst[t, j] < r["offsets"][e + 1]
+    # ascending tokens inside every segment
+    for e in range(E):
+        seg = src[r["offsets"][e]:r["offsets"][e + 1]]
+        assert np.all(np.diff(seg) > 0)
+    # renormalised weights sum to one
+    if renorm:
+        np.testing.assert_allclose(r["topk_w"].sum(1), 1.0, rtol=1e-14)
+
+
+def test_k_equals_E_is_full_softmax():
+    rng = np.random.default_rng(3)
+    z = rng.standard_normal((50, 6)).astype(np.float32)
+    r = oracle.route(z, 6, oracle.SOFTMAX, True)
+    full = scipy.special.softmax(z.astype(np.float64), axis=1)
+    np.testing.assert_allclose(r["topk_w"], np.take_along_axis(full, r["topk_idx"].astype(int), 1),
+                               rtol=1e-13)
+    r2 = oracle.route(z, 2, oracle.SOFTMAX, False)
+    np.testing.assert_allclose(r2["topk_w"], np.take_along_axis(full, r2["topk_idx"].astype(int), 1),
+                               rtol=1e-13)
+
+
+def test_sigmoid_no_renorm_is_scipy_expit():
+    rng = np.random.default_rng(4)
+    z = rng.standard_normal((20, 8)).astype(np.float32)
+    r = oracle.route(z, 3, oracle.SIGMOID, False)
+    np.testing.assert_allclose(r["topk_w"],
+                               scipy.special.expit(np.take_along_axis(z, r["topk_idx"].astype(int), 1)
+                                                   .astype(np.float64)), rtol=1e-14)
+
+
+def test_router_logits_fp32_and_bias_add():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((9, 16)).astype(np.float32)
+    w = rng.standard_normal((16, 4)).astype(np.float32)
+    b = rng.standard_normal(4).astype(np.float32)
+    l = oracle.router_logits(x, w, b)
+    assert l.dtype == np.float32
+    exact = x.astype(np.float64) @ w.astype(np.float64)
+    # one rounding of the exact dot product, then one fp32 add
+    np.testing.assert_array_equal(l, exact.astype(np.float32) + b)
+
+
+@pytest.mark.parametrize("score", [oracle.SOFTMAX, oracle.SIGMOID])
+@pytest.mark.parametrize("renorm", [True, False])
+def test_route_bwd_finite_differences(score, renorm):
+    """dz = J^T dw with J the Jacobian of the weights at fixed selection."""
+    rng = np.random.default_rng(11)
+    T, E, k = 6, 7, 3
+    z = rng.standard_normal((T, E))
+    idx = oracle.select_topk(z.astype(np.float32), k)
+    dw = rng.standard_normal((T, k))
+    w = oracle.gates(z, idx, score, renorm)
+    dz = oracle.route_bwd(z, idx, w, dw, score, renorm)
+    eps = 1e-6
+    num = np.zeros_like(z)
+    for t in range(T):
+        for e in range(E):
+            zp, zm = z.copy(), z.copy()
+            zp[t, e] += eps
+            zm[t, e] -= eps
+            num[t, e] = ((oracle.gates(zp, idx, score, renorm) - oracle.gates(zm, idx, score, renorm))
+                         * dw).sum() / (2 * eps)
+    np.testing.assert_allclose(dz, num, rtol=0, atol=1e-8)
