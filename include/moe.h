@@ -1,0 +1,216 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE-layer hot path.
+ *
+ * One Mixture-of-Experts layer, forward and backward, on one GPU, in the four
+ * stages of "Scalable Training of Mixture-of-Experts Models with Megatron
+ * Core" (section 2, Megatron-Core MoE Architecture):
+ *   Route    -- router logits, probabilities, top-k experts, routing weights
+ *   Dispatch -- tokens permuted by destination expert (expert-contiguous rows)
+ *   Compute  -- all experts' SwiGLU FFNs as one grouped GEMM over ragged rows
+ *   Combine  -- rows return to sequence order, weighted by the routing
+ *               weights, plus an optional shared expert's output
+ * and their backward passes.  The router stays in FP32 (section 5, Selective
+ * precision).
+ *
+ * Conventions (every entry point):
+ *   - Tensor arguments are DEVICE pointers to contiguous row-major arrays on
+ *     the current HIP device; scalars are host values.  `stream` is a
+ *     hipStream_t (NULL = the default stream).
+ *   - Every call validates its arguments on the host first.  On failure it
+ *     returns a negative moe_status, enqueues nothing and sets a thread-local
+ *     message (moe_last_error).  On success it enqueues kernels on `stream`
+ *     and returns MOE_OK without synchronising; outputs are valid once the
+ *     stream reaches the call.  No call allocates device memory, copies device
+ *     to host, or keeps a pointer after returning; the caller owns every
+ *     buffer, including workspaces sized by the *_workspace_bytes functions.
+ *   - Device-resident index data (offsets, dst_row, topk_idx) is range-checked
+ *     inside the kernels: entries outside the valid range are skipped, never
+ *     dereferenced.  Results for such inputs are unspecified.
+ *   - Identical inputs give bit-identical outputs (no order-deciding atomics).
+ *   - Sizes are 64-bit; the kernels address with 64-bit offsets.
+ *   - Zero-sized problems (T == 0, M == 0) are valid; a weight gradient of an
+ *     empty group is written as zeros (or left unchanged when accumulating).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,        /* a required pointer is NULL */
+  MOE_ERR_SHAPE = -2,       /* a size is negative or inconsistent */
+  MOE_ERR_DTYPE = -3,       /* unknown dtype or unsupported dtype combination */
+  MOE_ERR_UNSUPPORTED = -4, /* valid request outside this build's limits */
+  MOE_ERR_WORKSPACE = -5,   /* workspace missing or too small */
+  MOE_ERR_HIP = -6          /* a HIP runtime call or launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score;
+typedef enum {
+  MOE_EPI_NONE = 0,
+  MOE_EPI_SWIGLU = 1,     /* forward GEMM 1: also write H = silu(A) * B */
+  MOE_EPI_SWIGLU_BWD = 2  /* dgrad of GEMM 2: turn dH into dAB in the epilogue */
+} moe_epilogue;
+
+/* Text for a status code; never NULL. */
+const char* moe_status_string(int status);
+/* Detail of the last failing call on this host thread ("" if none). */
+const char* moe_last_error(void);
+/* ABI version of this header: 1. */
+int moe_abi_version(void);
+
+/* ---------------------------------------------------------------- Route -- */
+
+/* Router projection, forward (section 2, Route: token hidden states to expert
+ * logits; section 5, Selective precision: FP32).
+ *   logits[t, e] = fp32( sum_i x[t, i] * w_r[i, e] ) + logit_bias[e]
+ * fp32 multiply-add on the vector ALUs (bf16 x widened exactly).
+ *   x          [T, d]  x_dtype (MOE_F32 or MOE_BF16)
+ *   w_r        [d, E]  fp32
+ *   logit_bias [E]     fp32 or NULL: a per-expert constant added to the
+ *                      logits before scoring (no gradient)
+ *   logits     [T, E]  fp32 out: the selection key of moe_route_topk
+ * Limits: 1 <= E <= 1024, d >= 1. */
+int moe_router_logits(const void* x, int x_dtype, const float* w_r, const float* logit_bias,
+                      int64_t T, int64_t d, int32_t E, float* logits, void* stream);
+
+/* Router projection, backward: d_w_r = x^T d_logits ([d, E], fp32, overwritten)
+ * and dx_router = d_logits w_r^T ([T, d], fp32, overwritten).  Either output
+ * may be NULL to skip it. */
+int moe_router_logits_bwd(const void* x, int x_dtype, const float* w_r, const float* d_logits,
+                          int64_t T, int64_t d, int32_t E, float* d_w_r, float* dx_router,
+                          void* stream);
+
+/* Bytes of workspace moe_route_topk needs (device memory, any contents). */
+size_t moe_route_topk_workspace_bytes(int64_t T, int32_t E, int32_t k);
+
+/* Top-k selection, routing weights and the dispatch map (section 2, Route and
+ * Dispatch).  Dropless: all T*k (token, slot) pairs get a permuted row.
+ *   logits    [T, E] fp32 keys (bias already added).  Must be finite.
+ *   selection: per token the k experts of largest key; equal keys go to the
+ *              lower expert index; slots are listed by key descending, then
+ *              index ascending.
+ *   topk_idx  [T, k] int32 out
+ *   topk_w    [T, k] fp32 out: score = MOE_SOFTMAX: softmax of the keys over
+ *              the k chosen (renorm != 0) or over all E (renorm == 0);
+ *              MOE_SIGMOID: sigmoid(key), divided by the sum over the chosen
+ *              k when renorm != 0
+ *   counts    [E]    int32 out: rows routed to each expert
+ *   offsets   [E+1]  int64 out: exclusive prefix sum of counts (offsets[E] = T*k)
+ *   dst_row   [T, k] int32 out: permuted row of (t, j); rows of expert e are
+ *              offsets[e] .. offsets[e+1]-1 in ascending token order
+ *   src_token [T*k]  int32 out: token of each permuted row (inverse of dst_row)
+ *   workspace moe_route_topk_workspace_bytes(T, E, k) bytes
+ * Limits: 1 <= k <= E <= 1024, T * k < 2^31. */
+int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int score, int renorm,
+                   int32_t* topk_idx, float* topk_w, int32_t* counts, int64_t* offsets,
+                   int32_t* dst_row, int32_t* src_token, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* Gradient of the routing weights with respect to the keys (the selection
+ * itself carries none).  With g = sum_j w_j dw_j over a token's chosen slots:
+ *   softmax, renorm   : d_logits[e_j] = w_j (dw_j - g), 0 elsewhere
+ *   softmax, no renorm: d_logits[e]   = p_e (G_e - g) for all e, where p is the
+ *                       softmax over all E and G_e = dw_j if e = e_j else 0
+ *   sigmoid, renorm   : d_logits[e_j] = (dw_j - g) / S * s_j (1 - s_j), S = sum s_j
+ *   sigmoid, no renorm: d_logits[e_j] = dw_j s_j (1 - s_j)
+ * logits [T, E], topk_idx/topk_w/d_topk_w [T, k] as produced above;
+ * d_logits [T, E] fp32 out (every entry written). */
+int moe_route_topk_bwd(const float* logits, const int32_t* topk_idx, const float* topk_w,
+                       const float* d_topk_w, int64_t T, int32_t E, int32_t k, int score,
+                       int renorm, float* d_logits, void* stream);
+
+/* ------------------------------------------------------------- Dispatch -- */
+
+/* Permute tokens into expert-contiguous rows (section 2, Dispatch):
+ *   x_perm[dst_row[t, j]] = x[t]     for all t < T, j < k
+ * x [T, d] and x_perm [T*k, d] of `dtype`; each token row is read once.
+ * Limits: d % 8 == 0 (bf16) or d % 4 == 0 (fp32). */
+int moe_permute(const void* x, int dtype, const int32_t* dst_row, int64_t T, int64_t d, int32_t k,
+                void* x_perm, void* stream);
+
+/* Adjoint of moe_permute plus optional addends (fp32 accumulation, one
+ * rounding to `dtype`):
+ *   dx[t] = sum_j dx_perm[dst_row[t, j]] + addend[t] + addend_f32[t]
+ * dx_perm [T*k, d], dx [T, d], addend [T, d] of `dtype` or NULL,
+ * addend_f32 [T, d] fp32 or NULL. */
+int moe_permute_bwd(const void* dx_perm, int dtype, const int32_t* dst_row, int64_t T, int64_t d,
+                    int32_t k, const void* addend, const float* addend_f32, void* dx, void* stream);
+
+/* -------------------------------------------------------------- Compute -- */
+
+/* Grouped GEMM over G groups of contiguous rows (section 2, Expert
+ * Computation: the local experts' GEMMs run together).  Group g owns rows
+ * offsets[g] .. offsets[g+1]-1 of the M rows; offsets is DEVICE int64 [G+1],
+ * non-decreasing, offsets[0] = 0, offsets[G] = M (rows outside every group
+ * are left untouched).  A, B and outputs share `dtype` (MOE_BF16: bf16 MFMA
+ * with fp32 accumulation; MOE_F32: fp32 FMA).
+ *
+ * Forward:  C[rows g] = A[rows g] . B[g]     A [M, K], B [G, K, N], C [M, N]
+ *   epilogue MOE_EPI_NONE  : write C.
+ *   epilogue MOE_EPI_SWIGLU: N = 2f, columns [0, f) are the gate a and [f, 2f)
+ *     the up projection b; write C (may be NULL to skip) and
+ *     H [M, f] = silu(a) * b, silu(a) = a / (1 + exp(-a)), from the fp32 sums.
+ * Limits (bf16): K % 64 == 0, N % 128 == 0 (SWIGLU: f % 64 == 0);
+ *        (fp32): none beyond sizes >= 1.  G <= 1024. */
+int moe_grouped_gemm_fwd(const void* A, const void* B, const int64_t* offsets, int32_t G, int64_t M,
+                         int64_t K, int64_t N, int dtype, int epilogue, void* C, void* H,
+                         void* stream);
+
+/* Data gradient: dA[rows g] = dC[rows g] . B[g]^T    dC [M, N], B [G, K, N], dA [M, K].
+ *   epilogue MOE_EPI_SWIGLU_BWD: the product is dH [M, K] of a SwiGLU whose
+ *     pre-activations are ab [M, 2K] (a = ab[:, :K], b = ab[:, K:]); write
+ *     dA = dAB [M, 2K] with dAB[:, :K] = dH * b * s * (1 + a (1 - s)),
+ *     dAB[:, K:] = dH * silu(a), s = sigmoid(a).  `ab` is NULL otherwise.
+ * Limits (bf16): N % 64 == 0, K % 128 == 0.  (fp32): none.  G <= 1024. */
+int moe_grouped_gemm_dgrad(const void* dC, const void* B, const int64_t* offsets, int32_t G,
+                           int64_t M, int64_t K, int64_t N, int dtype, int epilogue,
+                           const void* ab, void* dA, void* stream);
+
+/* Weight gradient: dB[g] = A[rows g]^T . dC[rows g]   A [M, K], dC [M, N], dB [G, K, N].
+ * The contraction runs over each group's rows (ragged).  dB_dtype is `dtype`
+ * or MOE_F32.  accumulate != 0 adds into dB instead of overwriting it.
+ * Limits (bf16): K % 128 == 0, N % 128 == 0.  (fp32): none.  G <= 1024. */
+int moe_grouped_gemm_wgrad(const void* A, const void* dC, const int64_t* offsets, int32_t G,
+                           int64_t M, int64_t K, int64_t N, int dtype, int dB_dtype,
+                           int accumulate, void* dB, void* stream);
+
+/* SwiGLU on its own: h [M, f] = silu(ab[:, :f]) * ab[:, f:], ab [M, 2f]. */
+int moe_swiglu(const void* ab, int dtype, int64_t M, int64_t f, void* h, void* stream);
+
+/* SwiGLU backward on its own: dab [M, 2f] from dh [M, f] and ab [M, 2f]
+ * (formulas as in MOE_EPI_SWIGLU_BWD). */
+int moe_swiglu_bwd(const void* dh, const void* ab, int dtype, int64_t M, int64_t f, void* dab,
+                   void* stream);
+
+/* -------------------------------------------------------------- Combine -- */
+
+/* Unpermute and combine (section 2, Combine: rows return to sequence order,
+ * weighted by the routing weights, plus an optional shared expert's output):
+ *   out[t] = sum_j topk_w[t, j] * y_perm[dst_row[t, j]] + shared_y[t]
+ * fp32 accumulation in slot order, one rounding to `dtype`.
+ * y_perm [T*k, d], shared_y [T, d] or NULL, out [T, d], all `dtype`;
+ * topk_w [T, k] fp32. */
+int moe_unpermute_combine(const void* y_perm, int dtype, const float* topk_w,
+                          const int32_t* dst_row, const void* shared_y, int64_t T, int64_t d,
+                          int32_t k, void* out, void* stream);
+
+/* Backward of moe_unpermute_combine:
+ *   dy_perm[dst_row[t, j]] = topk_w[t, j] * dout[t]
+ *   d_topk_w[t, j]         = < dout[t], y_perm[dst_row[t, j]] >   (fp32)
+ * (the shared expert's output gradient is dout itself). */
+int moe_unpermute_combine_bwd(const void* dout, const void* y_perm, int dtype, const float* topk_w,
+                              const int32_t* dst_row, int64_t T, int64_t d, int32_t k,
+                              void* dy_perm, float* d_topk_w, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,201 @@
+"""ctypes binding of the C-ABI library (include/moe.h).
+
+Each function has the name of its C entry point and only marshals
+arguments: torch tensors become device pointers, the current torch stream
+becomes the hipStream_t, and a negative status raises ``MoeError`` carrying
+``moe_last_error()``.  All computation happens in the HIP kernels; there is
+no fallback: if the library is missing, ``lib()`` raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_LIB_NAME = "libmoe_mi355x.so"
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), _LIB_NAME)
+
+F32, BF16 = 0, 1
+SOFTMAX, SIGMOID = 0, 1
+EPI_NONE, EPI_SWIGLU, EPI_SWIGLU_BWD = 0, 1, 2
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_int = ctypes.c_int
+_sz = ctypes.c_size_t
+
+# name -> (restype, argtypes)
+SIGNATURES = {
+    "moe_status_string": (ctypes.c_char_p, [_int]),
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_abi_version": (_int, []),
+    "moe_router_logits": (_int, [_p, _int, _p, _p, _i64, _i64, _i32, _p, _p]),
+    "moe_router_logits_bwd": (_int, [_p, _int, _p, _p, _i64, _i64, _i32, _p, _p, _p]),
+    "moe_route_topk_workspace_bytes": (_sz, [_i64, _i32, _i32]),
+    "moe_route_topk": (_int, [_p, _i64, _i32, _i32, _int, _int, _p, _p, _p, _p, _p, _p, _p, _sz,
+                              _p]),
+    "moe_route_topk_bwd": (_int, [_p, _p, _p, _p, _i64, _i32, _i32, _int, _int, _p, _p]),
+    "moe_permute": (_int, [_p, _int, _p, _i64, _i64, _i32, _p, _p]),
+    "moe_permute_bwd": (_int, [_p, _int, _p, _i64, _i64, _i32, _p, _p, _p, _p]),
+    "moe_grouped_gemm_fwd": (_int, [_p, _p, _p, _i32, _i64, _i64, _i64, _int, _int, _p, _p, _p]),
+    "moe_grouped_gemm_dgrad": (_int, [_p, _p, _p, _i32, _i64, _i64, _i64, _int, _int, _p, _p,
+                                      _p]),
+    "moe_grouped_gemm_wgrad": (_int, [_p, _p, _p, _i32, _i64, _i64, _i64, _int, _int, _int, _p,
+                                      _p]),
+    "moe_swiglu": (_int, [_p, _int, _i64, _i64, _p, _p]),
+    "moe_swiglu_bwd": (_int, [_p, _p, _int, _i64, _i64, _p, _p]),
+    "moe_unpermute_combine": (_int, [_p, _int, _p, _p, _p, _i64, _i64, _i32, _p, _p]),
+    "moe_unpermute_combine_bwd": (_int, [_p, _p, _int, _p, _p, _i64, _i64, _i32, _p, _p, _p]),
+}
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status, detail):
+        super().__init__(f"{fn} failed ({status}): {detail}")
+        self.status = status
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded library.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"HIP library {_LIB_PATH} is missing: run "
+                               "`python -m routing_grouped_gemm_router_amd.build` first")
+        l = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the MoE library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    return torch.cuda.current_stream().cuda_stream
+
+
+def dtype_code(t):
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _call(name, *args):
+    st = getattr(lib(), name)(*args)
+    if st != 0:
+        raise MoeError(name, st, lib().moe_last_error().decode())
+
+
+def moe_last_error():
+    return lib().moe_last_error().decode()
+
+
+def moe_status_string(status):
+    return lib().moe_status_string(status).decode()
+
+
+def moe_abi_version():
+    return lib().moe_abi_version()
+
+
+def moe_router_logits(x, w_r, logit_bias, logits, stream=None):
+    T, d = x.shape
+    _call("moe_router_logits", _ptr(x), dtype_code(x), _ptr(w_r), _ptr(logit_bias), T, d,
+          w_r.shape[1], _ptr(logits), _stream(stream))
+
+
+def moe_router_logits_bwd(x, w_r, d_logits, d_w_r, dx_router, stream=None):
+    T, d = x.shape
+    _call("moe_router_logits_bwd", _ptr(x), dtype_code(x), _ptr(w_r), _ptr(d_logits), T, d,
+          w_r.shape[1], _ptr(d_w_r), _ptr(dx_router), _stream(stream))
+
+
+def moe_route_topk_workspace_bytes(T, E, k):
+    return lib().moe_route_topk_workspace_bytes(T, E, k)
+
+
+def moe_route_topk(logits, k, score, renorm, topk_idx, topk_w, counts, offsets, dst_row,
+                   src_token, workspace, stream=None):
+    T, E = logits.shape
+    _call("moe_route_topk", _ptr(logits), T, E, k, score, int(renorm), _ptr(topk_idx),
+          _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(dst_row), _ptr(src_token),
+          _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def moe_route_topk_bwd(logits, topk_idx, topk_w, d_topk_w, score, renorm, d_logits, stream=None):
+    T, E = logits.shape
+    _call("moe_route_topk_bwd", _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(d_topk_w), T, E,
+          topk_idx.shape[1], score, int(renorm), _ptr(d_logits), _stream(stream))
+
+
+def moe_permute(x, dst_row, x_perm, stream=None):
+    T, d = x.shape
+    _call("moe_permute", _ptr(x), dtype_code(x), _ptr(dst_row), T, d, dst_row.shape[1],
+          _ptr(x_perm), _stream(stream))
+
+
+def moe_permute_bwd(dx_perm, dst_row, addend, addend_f32, dx, stream=None):
+    T, d = dx.shape
+    _call("moe_permute_bwd", _ptr(dx_perm), dtype_code(dx), _ptr(dst_row), T, d,
+          dst_row.shape[1], _ptr(addend), _ptr(addend_f32), _ptr(dx), _stream(stream))
+
+
+def moe_grouped_gemm_fwd(A, B, offsets, C, H=None, epilogue=EPI_NONE, stream=None):
+    G, K, N = B.shape
+    _call("moe_grouped_gemm_fwd", _ptr(A), _ptr(B), _ptr(offsets), G, A.shape[0], K, N,
+          dtype_code(A), epilogue, _ptr(C), _ptr(H), _stream(stream))
+
+
+def moe_grouped_gemm_dgrad(dC, B, offsets, dA, epilogue=EPI_NONE, ab=None, stream=None):
+    G, K, N = B.shape
+    _call("moe_grouped_gemm_dgrad", _ptr(dC), _ptr(B), _ptr(offsets), G, dC.shape[0], K, N,
+          dtype_code(dC), epilogue, _ptr(ab), _ptr(dA), _stream(stream))
+
+
+def moe_grouped_gemm_wgrad(A, dC, offsets, dB, accumulate=False, stream=None):
+    G, K, N = dB.shape
+    _call("moe_grouped_gemm_wgrad", _ptr(A), _ptr(dC), _ptr(offsets), G, A.shape[0], K, N,
+          dtype_code(A), dtype_code(dB), int(accumulate), _ptr(dB), _stream(stream))
+
+
+def moe_swiglu(ab, h, stream=None):
+    M, f = h.shape
+    _call("moe_swiglu", _ptr(ab), dtype_code(ab), M, f, _ptr(h), _stream(stream))
+
+
+def moe_swiglu_bwd(dh, ab, dab, stream=None):
+    M, f = dh.shape
+    _call("moe_swiglu_bwd", _ptr(dh), _ptr(ab), dtype_code(ab), M, f, _ptr(dab), _stream(stream))
+
+
+def moe_unpermute_combine(y_perm, topk_w, dst_row, shared_y, out, stream=None):
+    T, d = out.shape
+    _call("moe_unpermute_combine", _ptr(y_perm), dtype_code(y_perm), _ptr(topk_w), _ptr(dst_row),
+          _ptr(shared_y), T, d, dst_row.shape[1], _ptr(out), _stream(stream))
+
+
+def moe_unpermute_combine_bwd(dout, y_perm, topk_w, dst_row, dy_perm, d_topk_w, stream=None):
+    T, d = dout.shape
+    _call("moe_unpermute_combine_bwd", _ptr(dout), _ptr(y_perm), dtype_code(dout), _ptr(topk_w),
+          _ptr(dst_row), T, d, dst_row.shape[1], _ptr(dy_perm), _ptr(d_topk_w), _stream(stream))

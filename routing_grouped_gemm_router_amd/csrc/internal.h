@@ -1,0 +1,63 @@
+// Launchers of the HIP kernels, called by the C-ABI layer after validation.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace moe {
+
+enum { GRP_NONE = 0, GRP_M = 1, GRP_K = 2 };
+enum { EPI_NONE = 0, EPI_SWIGLU = 1, EPI_SWIGLU_BWD = 2, EPI_BIAS = 3 };
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+
+// route.hip
+size_t route_topk_workspace(int64_t T, int E);
+hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int score, int renorm,
+                             int32_t* topk_idx, float* topk_w, int32_t* counts, int64_t* offsets,
+                             int32_t* dst_row, int32_t* src_token, void* ws, hipStream_t s);
+hipError_t launch_route_topk_bwd(const float* logits, const int32_t* topk_idx, const float* topk_w,
+                                 const float* d_topk_w, int64_t T, int E, int k, int score,
+                                 int renorm, float* d_logits, hipStream_t s);
+
+// permute.hip
+hipError_t launch_permute(const void* x, int dtype, const int32_t* dst_row, int64_t T, int64_t d,
+                          int k, void* xp, hipStream_t s);
+hipError_t launch_permute_bwd(const void* dxp, int dtype, const int32_t* dst_row, int64_t T,
+                              int64_t d, int k, const void* addend, const float* addend_f32,
+                              void* dx, hipStream_t s);
+hipError_t launch_combine(const void* y, int dtype, const float* topk_w, const int32_t* dst_row,
+                          const void* shared, int64_t T, int64_t d, int k, void* out,
+                          hipStream_t s);
+hipError_t launch_combine_bwd(const void* dout, const void* y, int dtype, const float* topk_w,
+                              const int32_t* dst_row, int64_t T, int64_t d, int k, void* dy,
+                              float* d_w, hipStream_t s);
+hipError_t launch_swiglu(const void* ab, int dtype, int64_t M, int64_t f, void* h, hipStream_t s);
+hipError_t launch_swiglu_bwd(const void* dh, const void* ab, int dtype, int64_t M, int64_t f,
+                             void* dab, hipStream_t s);
+
+// gemm_f32.hip
+hipError_t launch_router_fwd(const void* x, int x_dtype, const float* w_r, const float* bias,
+                             int64_t T, int64_t d, int E, float* logits, hipStream_t s);
+hipError_t launch_router_bwd(const void* x, int x_dtype, const float* w_r, const float* dz,
+                             int64_t T, int64_t d, int E, float* dw_r, float* dx_r, hipStream_t s);
+hipError_t launch_gg_f32_fwd(const float* A, const float* B, const int64_t* off, int G, int64_t M,
+                             int64_t K, int64_t N, int epi, float* C, float* H, hipStream_t s);
+hipError_t launch_gg_f32_dgrad(const float* dC, const float* B, const int64_t* off, int G,
+                               int64_t M, int64_t K, int64_t N, int epi, const float* ab,
+                               float* dA, hipStream_t s);
+hipError_t launch_gg_f32_wgrad(const float* A, const float* dC, const int64_t* off, int G,
+                               int64_t M, int64_t K, int64_t N, int accumulate, float* dB,
+                               hipStream_t s);
+
+// gemm_bf16.hip
+hipError_t launch_gg_bf16_fwd(const void* A, const void* B, const int64_t* off, int G, int64_t M,
+                              int64_t K, int64_t N, int epi, void* C, void* H, hipStream_t s);
+hipError_t launch_gg_bf16_dgrad(const void* dC, const void* B, const int64_t* off, int G,
+                                int64_t M, int64_t K, int64_t N, int epi, const void* ab, void* dA,
+                                hipStream_t s);
+hipError_t launch_gg_bf16_wgrad(const void* A, const void* dC, const int64_t* off, int G,
+                                int64_t M, int64_t K, int64_t N, int db_f32, int accumulate,
+                                void* dB, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,354 @@
+// C-ABI entry points of the MoE hot path (declared in include/moe.h):
+// host-side validation, then kernel launches on the caller's stream.
+// Validation never touches the HIP runtime, so every error path can be
+// exercised without a GPU.
+#include "moe.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_dtype(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+#define REQUIRE(cond, status, ...) \
+  do {                             \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+int check_row_vectors(int dtype, int64_t d, const char* what) {
+  const int64_t q = dtype == MOE_BF16 ? 8 : 4;
+  REQUIRE(d % q == 0, MOE_ERR_UNSUPPORTED, "%s: row length %lld must be a multiple of %lld", what,
+          static_cast<long long>(d), static_cast<long long>(q));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "null pointer";
+    case MOE_ERR_SHAPE: return "invalid shape";
+    case MOE_ERR_DTYPE: return "invalid dtype";
+    case MOE_ERR_UNSUPPORTED: return "unsupported";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+int moe_abi_version(void) { return 1; }
+
+int moe_router_logits(const void* x, int x_dtype, const float* w_r, const float* logit_bias,
+                      int64_t T, int64_t d, int32_t E, float* logits, void* stream) {
+  REQUIRE(valid_dtype(x_dtype), MOE_ERR_DTYPE, "moe_router_logits: bad x dtype %d", x_dtype);
+  REQUIRE(T >= 0 && d >= 1, MOE_ERR_SHAPE, "moe_router_logits: T=%lld d=%lld",
+          static_cast<long long>(T), static_cast<long long>(d));
+  REQUIRE(E >= 1 && E <= 1024, MOE_ERR_UNSUPPORTED, "moe_router_logits: E=%d outside [1, 1024]", E);
+  if (T == 0) return ok();
+  REQUIRE(x && w_r && logits, MOE_ERR_NULL, "moe_router_logits: x, w_r and logits are required");
+  return hip_status(moe::launch_router_fwd(x, x_dtype, w_r, logit_bias, T, d, E, logits,
+                                           as_stream(stream)),
+                    "moe_router_logits");
+}
+
+int moe_router_logits_bwd(const void* x, int x_dtype, const float* w_r, const float* d_logits,
+                          int64_t T, int64_t d, int32_t E, float* d_w_r, float* dx_router,
+                          void* stream) {
+  REQUIRE(valid_dtype(x_dtype), MOE_ERR_DTYPE, "moe_router_logits_bwd: bad x dtype %d", x_dtype);
+  REQUIRE(T >= 0 && d >= 1, MOE_ERR_SHAPE, "moe_router_logits_bwd: T=%lld d=%lld",
+          static_cast<long long>(T), static_cast<long long>(d));
+  REQUIRE(E >= 1 && E <= 1024, MOE_ERR_UNSUPPORTED, "moe_router_logits_bwd: E=%d outside [1, 1024]",
+          E);
+  if (!d_w_r && !dx_router) return ok();
+  REQUIRE(T == 0 || d_logits, MOE_ERR_NULL, "moe_router_logits_bwd: d_logits is required");
+  REQUIRE(!d_w_r || T == 0 || x, MOE_ERR_NULL, "moe_router_logits_bwd: x is required for d_w_r");
+  REQUIRE(!dx_router || T == 0 || w_r, MOE_ERR_NULL,
+          "moe_router_logits_bwd: w_r is required for dx_router");
+  return hip_status(moe::launch_router_bwd(x, x_dtype, w_r, d_logits, T, d, E, d_w_r, dx_router,
+                                           as_stream(stream)),
+                    "moe_router_logits_bwd");
+}
+
+size_t moe_route_topk_workspace_bytes(int64_t T, int32_t E, int32_t k) {
+  (void)k;
+  if (T < 0 || E < 1) return 0;
+  return moe::route_topk_workspace(T, E);
+}
+
+static int check_route_shape(const char* fn, int64_t T, int32_t E, int32_t k, int score) {
+  REQUIRE(T >= 0, MOE_ERR_SHAPE, "%s: T=%lld", fn, static_cast<long long>(T));
+  REQUIRE(E >= 1 && E <= 1024, MOE_ERR_UNSUPPORTED, "%s: E=%d outside [1, 1024]", fn, E);
+  REQUIRE(k >= 1 && k <= E, MOE_ERR_SHAPE, "%s: k=%d outside [1, E=%d]", fn, k, E);
+  REQUIRE(k <= 64, MOE_ERR_UNSUPPORTED, "%s: k=%d above 64", fn, k);
+  REQUIRE(T * k < (int64_t(1) << 31), MOE_ERR_UNSUPPORTED, "%s: T*k must be below 2^31", fn);
+  REQUIRE(score == MOE_SOFTMAX || score == MOE_SIGMOID, MOE_ERR_SHAPE, "%s: bad score %d", fn,
+          score);
+  return MOE_OK;
+}
+
+int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int score, int renorm,
+                   int32_t* topk_idx, float* topk_w, int32_t* counts, int64_t* offsets,
+                   int32_t* dst_row, int32_t* src_token, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  int st = check_route_shape("moe_route_topk", T, E, k, score);
+  if (st != MOE_OK) return st;
+  REQUIRE(counts && offsets, MOE_ERR_NULL, "moe_route_topk: counts and offsets are required");
+  REQUIRE(T == 0 || (logits && topk_idx && topk_w && dst_row && src_token), MOE_ERR_NULL,
+          "moe_route_topk: logits, topk_idx, topk_w, dst_row and src_token are required");
+  const size_t need = moe::route_topk_workspace(T, E);
+  REQUIRE(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE,
+          "moe_route_topk: workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 7u) == 0, MOE_ERR_UNSUPPORTED,
+          "moe_route_topk: workspace must be 8-byte aligned");
+  return hip_status(moe::launch_route_topk(logits, T, E, k, score, renorm != 0, topk_idx, topk_w,
+                                           counts, offsets, dst_row, src_token, workspace,
+                                           as_stream(stream)),
+                    "moe_route_topk");
+}
+
+int moe_route_topk_bwd(const float* logits, const int32_t* topk_idx, const float* topk_w,
+                       const float* d_topk_w, int64_t T, int32_t E, int32_t k, int score,
+                       int renorm, float* d_logits, void* stream) {
+  int st = check_route_shape("moe_route_topk_bwd", T, E, k, score);
+  if (st != MOE_OK) return st;
+  if (T == 0) return ok();
+  REQUIRE(logits && topk_idx && topk_w && d_topk_w && d_logits, MOE_ERR_NULL,
+          "moe_route_topk_bwd: all pointers are required");
+  return hip_status(moe::launch_route_topk_bwd(logits, topk_idx, topk_w, d_topk_w, T, E, k, score,
+                                               renorm != 0, d_logits, as_stream(stream)),
+                    "moe_route_topk_bwd");
+}
+
+int moe_permute(const void* x, int dtype, const int32_t* dst_row, int64_t T, int64_t d, int32_t k,
+                void* x_perm, void* stream) {
+  REQUIRE(valid_dtype(dtype), MOE_ERR_DTYPE, "moe_permute: bad dtype %d", dtype);
+  REQUIRE(T >= 0 && d >= 1 && k >= 1, MOE_ERR_SHAPE, "moe_permute: T=%lld d=%lld k=%d",
+          static_cast<long long>(T), static_cast<long long>(d), k);
+  int st = check_row_vectors(dtype, d, "moe_permute");
+  if (st != MOE_OK) return st;
+  if (T == 0) return ok();
+  REQUIRE(x && dst_row && x_perm, MOE_ERR_NULL, "moe_permute: x, dst_row and x_perm are required");
+  REQUIRE(aligned16(x) && aligned16(x_perm), MOE_ERR_UNSUPPORTED,
+          "moe_permute: x and x_perm must be 16-byte aligned");
+  return hip_status(moe::launch_permute(x, dtype, dst_row, T, d, k, x_perm, as_stream(stream)),
+                    "moe_permute");
+}
+
+int moe_permute_bwd(const void* dx_perm, int dtype, const int32_t* dst_row, int64_t T, int64_t d,
+                    int32_t k, const void* addend, const float* addend_f32, void* dx, void* stream) {
+  REQUIRE(valid_dtype(dtype), MOE_ERR_DTYPE, "moe_permute_bwd: bad dtype %d", dtype);
+  REQUIRE(T >= 0 && d >= 1 && k >= 1, MOE_ERR_SHAPE, "moe_permute_bwd: T=%lld d=%lld k=%d",
+          static_cast<long long>(T), static_cast<long long>(d), k);
+  int st = check_row_vectors(dtype, d, "moe_permute_bwd");
+  if (st != MOE_OK) return st;
+  if (T == 0) return ok();
+  REQUIRE(dx_perm && dst_row && dx, MOE_ERR_NULL,
+          "moe_permute_bwd: dx_perm, dst_row and dx are required");
+  REQUIRE(aligned16(dx_perm) && aligned16(dx) && aligned16(addend) && aligned16(addend_f32),
+          MOE_ERR_UNSUPPORTED, "moe_permute_bwd: tensors must be 16-byte aligned");
+  return hip_status(moe::launch_permute_bwd(dx_perm, dtype, dst_row, T, d, k, addend, addend_f32,
+                                            dx, as_stream(stream)),
+                    "moe_permute_bwd");
+}
+
+static int check_gemm(const char* fn, const void* p0, const void* p1, const int64_t* off, int32_t G,
+                      int64_t M, int64_t K, int64_t N, int dtype) {
+  REQUIRE(valid_dtype(dtype), MOE_ERR_DTYPE, "%s: bad dtype %d", fn, dtype);
+  REQUIRE(G >= 1 && M >= 0 && K >= 1 && N >= 1, MOE_ERR_SHAPE, "%s: G=%d M=%lld K=%lld N=%lld", fn,
+          G, static_cast<long long>(M), static_cast<long long>(K), static_cast<long long>(N));
+  REQUIRE(G <= 1024, MOE_ERR_UNSUPPORTED, "%s: G=%d above 1024", fn, G);
+  REQUIRE(M / 64 + G < (int64_t(1) << 31) / 64, MOE_ERR_UNSUPPORTED, "%s: M too large", fn);
+  if (M == 0) return MOE_OK;  // nothing to read or write
+  REQUIRE(p0 && p1 && off, MOE_ERR_NULL, "%s: operands and offsets are required", fn);
+  REQUIRE(aligned16(p0) && aligned16(p1), MOE_ERR_UNSUPPORTED, "%s: operands must be 16-byte aligned",
+          fn);
+  return MOE_OK;
+}
+
+int moe_grouped_gemm_fwd(const void* A, const void* B, const int64_t* offsets, int32_t G, int64_t M,
+                         int64_t K, int64_t N, int dtype, int epilogue, void* C, void* H,
+                         void* stream) {
+  const char* fn = "moe_grouped_gemm_fwd";
+  int st = check_gemm(fn, A, B, offsets, G, M, K, N, dtype);
+  if (st != MOE_OK) return st;
+  REQUIRE(epilogue == MOE_EPI_NONE || epilogue == MOE_EPI_SWIGLU, MOE_ERR_SHAPE,
+          "%s: epilogue %d not available in the forward", fn, epilogue);
+  if (epilogue == MOE_EPI_SWIGLU) {
+    REQUIRE(N % 2 == 0, MOE_ERR_SHAPE, "%s: SWIGLU needs an even N", fn);
+    REQUIRE(M == 0 || H, MOE_ERR_NULL, "%s: SWIGLU needs H", fn);
+  } else {
+    REQUIRE(M == 0 || C, MOE_ERR_NULL, "%s: C is required", fn);
+  }
+  if (dtype == MOE_BF16) {
+    REQUIRE(K % 64 == 0, MOE_ERR_UNSUPPORTED, "%s: bf16 needs K %% 64 == 0 (K=%lld)", fn,
+            static_cast<long long>(K));
+    REQUIRE(epilogue == MOE_EPI_SWIGLU ? (N / 2) % 64 == 0 : N % 128 == 0, MOE_ERR_UNSUPPORTED,
+            "%s: bf16 needs N %% 128 == 0 (SWIGLU: f %% 64 == 0), N=%lld", fn,
+            static_cast<long long>(N));
+  }
+  if (M == 0) return ok();
+  hipError_t e = dtype == MOE_BF16
+                     ? moe::launch_gg_bf16_fwd(A, B, offsets, G, M, K, N, epilogue, C, H,
+                                               as_stream(stream))
+                     : moe::launch_gg_f32_fwd(static_cast<const float*>(A),
+                                              static_cast<const float*>(B), offsets, G, M, K, N,
+                                              epilogue, static_cast<float*>(C),
+                                              static_cast<float*>(H), as_stream(stream));
+  return hip_status(e, fn);
+}
+
+int moe_grouped_gemm_dgrad(const void* dC, const void* B, const int64_t* offsets, int32_t G,
+                           int64_t M, int64_t K, int64_t N, int dtype, int epilogue,
+                           const void* ab, void* dA, void* stream) {
+  const char* fn = "moe_grouped_gemm_dgrad";
+  int st = check_gemm(fn, dC, B, offsets, G, M, K, N, dtype);
+  if (st != MOE_OK) return st;
+  REQUIRE(epilogue == MOE_EPI_NONE || epilogue == MOE_EPI_SWIGLU_BWD, MOE_ERR_SHAPE,
+          "%s: epilogue %d not available in dgrad", fn, epilogue);
+  REQUIRE(M == 0 || dA, MOE_ERR_NULL, "%s: dA is required", fn);
+  REQUIRE(M == 0 || epilogue != MOE_EPI_SWIGLU_BWD || ab, MOE_ERR_NULL,
+          "%s: SWIGLU_BWD needs ab", fn);
+  if (dtype == MOE_BF16) {
+    REQUIRE(N % 64 == 0 && K % 128 == 0, MOE_ERR_UNSUPPORTED,
+            "%s: bf16 needs N %% 64 == 0 and K %% 128 == 0 (K=%lld N=%lld)", fn,
+            static_cast<long long>(K), static_cast<long long>(N));
+  }
+  if (M == 0) return ok();
+  hipError_t e = dtype == MOE_BF16
+                     ? moe::launch_gg_bf16_dgrad(dC, B, offsets, G, M, K, N, epilogue, ab, dA,
+                                                 as_stream(stream))
+                     : moe::launch_gg_f32_dgrad(static_cast<const float*>(dC),
+                                                static_cast<const float*>(B), offsets, G, M, K, N,
+                                                epilogue, static_cast<const float*>(ab),
+                                                static_cast<float*>(dA), as_stream(stream));
+  return hip_status(e, fn);
+}
+
+int moe_grouped_gemm_wgrad(const void* A, const void* dC, const int64_t* offsets, int32_t G,
+                           int64_t M, int64_t K, int64_t N, int dtype, int dB_dtype,
+                           int accumulate, void* dB, void* stream) {
+  const char* fn = "moe_grouped_gemm_wgrad";
+  REQUIRE(G >= 1 && M >= 0 && K >= 1 && N >= 1, MOE_ERR_SHAPE, "%s: G=%d M=%lld K=%lld N=%lld", fn,
+          G, static_cast<long long>(M), static_cast<long long>(K), static_cast<long long>(N));
+  REQUIRE(valid_dtype(dtype), MOE_ERR_DTYPE, "%s: bad dtype %d", fn, dtype);
+  REQUIRE(dB_dtype == dtype || dB_dtype == MOE_F32, MOE_ERR_DTYPE,
+          "%s: dB dtype must be the input dtype or fp32", fn);
+  REQUIRE(G <= 1024, MOE_ERR_UNSUPPORTED, "%s: G=%d above 1024", fn, G);
+  REQUIRE(offsets && dB, MOE_ERR_NULL, "%s: offsets and dB are required", fn);
+  REQUIRE(M == 0 || (A && dC), MOE_ERR_NULL, "%s: A and dC are required", fn);
+  if (dtype == MOE_BF16) {
+    REQUIRE(K % 128 == 0 && N % 128 == 0, MOE_ERR_UNSUPPORTED,
+            "%s: bf16 needs K %% 128 == 0 and N %% 128 == 0 (K=%lld N=%lld)", fn,
+            static_cast<long long>(K), static_cast<long long>(N));
+    REQUIRE(aligned16(A) && aligned16(dC), MOE_ERR_UNSUPPORTED, "%s: operands must be 16-byte aligned",
+            fn);
+  }
+  hipError_t e = dtype == MOE_BF16
+                     ? moe::launch_gg_bf16_wgrad(A, dC, offsets, G, M, K, N, dB_dtype == MOE_F32,
+                                                 accumulate != 0, dB, as_stream(stream))
+                     : moe::launch_gg_f32_wgrad(static_cast<const float*>(A),
+                                                static_cast<const float*>(dC), offsets, G, M, K, N,
+                                                accumulate != 0, static_cast<float*>(dB),
+                                                as_stream(stream));
+  return hip_status(e, fn);
+}
+
+int moe_swiglu(const void* ab, int dtype, int64_t M, int64_t f, void* h, void* stream) {
+  REQUIRE(valid_dtype(dtype), MOE_ERR_DTYPE, "moe_swiglu: bad dtype %d", dtype);
+  REQUIRE(M >= 0 && f >= 1, MOE_ERR_SHAPE, "moe_swiglu: M=%lld f=%lld", static_cast<long long>(M),
+          static_cast<long long>(f));
+  int st = check_row_vectors(dtype, f, "moe_swiglu");
+  if (st != MOE_OK) return st;
+  if (M == 0) return ok();
+  REQUIRE(ab && h, MOE_ERR_NULL, "moe_swiglu: ab and h are required");
+  REQUIRE(aligned16(ab) && aligned16(h), MOE_ERR_UNSUPPORTED, "moe_swiglu: 16-byte alignment needed");
+  return hip_status(moe::launch_swiglu(ab, dtype, M, f, h, as_stream(stream)), "moe_swiglu");
+}
+
+int moe_swiglu_bwd(const void* dh, const void* ab, int dtype, int64_t M, int64_t f, void* dab,
+                   void* stream) {
+  REQUIRE(valid_dtype(dtype), MOE_ERR_DTYPE, "moe_swiglu_bwd: bad dtype %d", dtype);
+  REQUIRE(M >= 0 && f >= 1, MOE_ERR_SHAPE, "moe_swiglu_bwd: M=%lld f=%lld",
+          static_cast<long long>(M), static_cast<long long>(f));
+  int st = check_row_vectors(dtype, f, "moe_swiglu_bwd");
+  if (st != MOE_OK) return st;
+  if (M == 0) return ok();
+  REQUIRE(dh && ab && dab, MOE_ERR_NULL, "moe_swiglu_bwd: dh, ab and dab are required");
+  REQUIRE(aligned16(dh) && aligned16(ab) && aligned16(dab), MOE_ERR_UNSUPPORTED,
+          "moe_swiglu_bwd: 16-byte alignment needed");
+  return hip_status(moe::launch_swiglu_bwd(dh, ab, dtype, M, f, dab, as_stream(stream)),
+                    "moe_swiglu_bwd");
+}
+
+int moe_unpermute_combine(const void* y_perm, int dtype, const float* topk_w,
+                          const int32_t* dst_row, const void* shared_y, int64_t T, int64_t d,
+                          int32_t k, void* out, void* stream) {
+  REQUIRE(valid_dtype(dtype), MOE_ERR_DTYPE, "moe_unpermute_combine: bad dtype %d", dtype);
+  REQUIRE(T >= 0 && d >= 1 && k >= 1, MOE_ERR_SHAPE, "moe_unpermute_combine: T=%lld d=%lld k=%d",
+          static_cast<long long>(T), static_cast<long long>(d), k);
+  int st = check_row_vectors(dtype, d, "moe_unpermute_combine");
+  if (st != MOE_OK) return st;
+  if (T == 0) return ok();
+  REQUIRE(y_perm && topk_w && dst_row && out, MOE_ERR_NULL,
+          "moe_unpermute_combine: y_perm, topk_w, dst_row and out are required");
+  REQUIRE(aligned16(y_perm) && aligned16(out) && aligned16(shared_y), MOE_ERR_UNSUPPORTED,
+          "moe_unpermute_combine: 16-byte alignment needed");
+  return hip_status(moe::launch_combine(y_perm, dtype, topk_w, dst_row, shared_y, T, d, k, out,
+                                        as_stream(stream)),
+                    "moe_unpermute_combine");
+}
+
+int moe_unpermute_combine_bwd(const void* dout, const void* y_perm, int dtype, const float* topk_w,
+                              const int32_t* dst_row, int64_t T, int64_t d, int32_t k,
+                              void* dy_perm, float* d_topk_w, void* stream) {
+  REQUIRE(valid_dtype(dtype), MOE_ERR_DTYPE, "moe_unpermute_combine_bwd: bad dtype %d", dtype);
+  REQUIRE(T >= 0 && d >= 1 && k >= 1, MOE_ERR_SHAPE,
+          "moe_unpermute_combine_bwd: T=%lld d=%lld k=%d", static_cast<long long>(T),
+          static_cast<long long>(d), k);
+  REQUIRE(k <= 64, MOE_ERR_UNSUPPORTED, "moe_unpermute_combine_bwd: k=%d above 64", k);
+  int st = check_row_vectors(dtype, d, "moe_unpermute_combine_bwd");
+  if (st != MOE_OK) return st;
+  if (T == 0) return ok();
+  REQUIRE(dout && y_perm && topk_w && dst_row && dy_perm && d_topk_w, MOE_ERR_NULL,
+          "moe_unpermute_combine_bwd: all pointers are required");
+  REQUIRE(aligned16(dout) && aligned16(y_perm) && aligned16(dy_perm), MOE_ERR_UNSUPPORTED,
+          "moe_unpermute_combine_bwd: 16-byte alignment needed");
+  return hip_status(moe::launch_combine_bwd(dout, y_perm, dtype, topk_w, dst_row, T, d, k, dy_perm,
+                                            d_topk_w, as_stream(stream)),
+                    "moe_unpermute_combine_bwd");
+}
+
+}  // extern "C"

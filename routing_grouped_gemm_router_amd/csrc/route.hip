@@ -1,0 +1,283 @@
+// Route stage kernels: top-k selection and routing weights, the per-expert
+// histogram with prefix-sum offsets, and the permutation map; plus the
+// backward of the routing weights.
+//
+// Definition: "Scalable Training of Mixture-of-Experts Models with Megatron
+// Core", section 2, Route (logits -> probabilities -> top-k experts, routing
+// weights and assignment) and Dispatch (tokens permuted by destination
+// expert).  Selection is on the fp32 key (monotone in the probability); equal
+// keys go to the lower expert index; segment rows are in ascending token order.
+//
+// Determinism without order-deciding atomics: tokens are processed in tiles of
+// 64; each tile records, per expert, a 64-bit mask of its tokens that chose the
+// expert (built with LDS bitwise OR, which is order independent).  A scan over
+// tiles gives each (tile, expert) its base row; a token's rank inside its tile
+// is the popcount of the mask below its bit.
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+
+constexpr int ROUTE_TILE = 64;  // tokens per tile = bits of one mask word
+
+// Strict order on (key, index): larger key first, then lower index.
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+template <int EPL>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int64_t T, int E,
+                                                   int k, int score, int renorm,
+                                                   int32_t* __restrict__ topk_idx,
+                                                   float* __restrict__ topk_w,
+                                                   unsigned long long* __restrict__ tile_bits) {
+  __shared__ unsigned long long bits[1024];
+  const int tid = threadIdx.x;
+  const int64_t tile = blockIdx.x;
+  for (int e = tid; e < E; e += 256) bits[e] = 0ull;
+  __syncthreads();
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int tt = wave; tt < ROUTE_TILE; tt += 4) {
+    const int64_t t = tile * ROUTE_TILE + tt;
+    if (t >= T) break;
+    const float* row = logits + t * E;
+    float v[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + 64 * i;
+      v[i] = e < E ? row[e] : 0.f;
+    }
+    unsigned taken = 0;  // bit i: element i of this lane already selected
+    int my_idx = -1;
+    float my_key = 0.f;
+    for (int j = 0; j < k; ++j) {
+      float bv = 0.f;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E && !((taken >> i) & 1u) && (bi == 0x7fffffff || better(v[i], e, bv, bi))) {
+          bv = v[i];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (oi != 0x7fffffff && (bi == 0x7fffffff || better(ov, oi, bv, bi))) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+      if (lane == j) {
+        my_idx = bi;
+        my_key = bv;
+      }
+    }
+    // routing weights from the chosen keys (slot 0 holds the largest key)
+    const bool active = lane < k;
+    float w;
+    if (score == 0) {  // softmax
+      const float m = __shfl(my_key, 0, 64);
+      const float ex = active ? expf(my_key - m) : 0.f;
+      float denom;
+      if (renorm) {
+        denom = wave_sum(ex);
+      } else {
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+          if (lane + 64 * i < E) part += expf(v[i] - m);
+        denom = wave_sum(part);
+      }
+      w = ex / denom;
+    } else {  // sigmoid
+      const float s = active ? 1.0f / (1.0f + expf(-my_key)) : 0.f;
+      w = renorm ? s / wave_sum(s) : s;
+    }
+    if (active) {
+      topk_idx[t * k + lane] = my_idx;
+      topk_w[t * k + lane] = w;
+      atomicOr(&bits[my_idx], 1ull << tt);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) tile_bits[tile * E + e] = bits[e];
+}
+
+// One block: per expert, the running row count over tiles (tile_base), the
+// totals (counts) and their exclusive prefix sum (offsets).
+__global__ __launch_bounds__(1024) void route_scan_kernel(const unsigned long long* __restrict__ tile_bits,
+                                                          int64_t ntiles, int E,
+                                                          int32_t* __restrict__ tile_base,
+                                                          int32_t* __restrict__ counts,
+                                                          int64_t* __restrict__ offsets) {
+  __shared__ long long s[1024];
+  const int e = threadIdx.x;
+  long long run = 0;
+  if (e < E) {
+    for (int64_t tl = 0; tl < ntiles; ++tl) {
+      tile_base[tl * E + e] = static_cast<int32_t>(run);
+      run += __popcll(tile_bits[tl * E + e]);
+    }
+    counts[e] = static_cast<int32_t>(run);
+  }
+  s[e] = e < E ? run : 0;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const long long add = e >= o ? s[e - o] : 0;
+    __syncthreads();
+    s[e] += add;
+    __syncthreads();
+  }
+  if (e < E) offsets[e + 1] = s[e];
+  if (e == 0) offsets[0] = 0;
+}
+
+__global__ __launch_bounds__(256) void route_rank_kernel(const int32_t* __restrict__ topk_idx,
+                                                         const unsigned long long* __restrict__ tile_bits,
+                                                         const int32_t* __restrict__ tile_base,
+                                                         const int64_t* __restrict__ offsets, int64_t T,
+                                                         int E, int k, int32_t* __restrict__ dst_row,
+                                                         int32_t* __restrict__ src_token) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= T * k) return;
+  const int64_t t = i / k;
+  const int e = topk_idx[i];
+  if (e < 0 || e >= E) return;
+  const int64_t tile = t / ROUTE_TILE;
+  const int bit = static_cast<int>(t % ROUTE_TILE);
+  const unsigned long long below = bit ? (tile_bits[tile * E + e] & ((1ull << bit) - 1ull)) : 0ull;
+  const int64_t r = offsets[e] + tile_base[tile * E + e] + __popcll(below);
+  if (r < 0 || r >= T * k) return;
+  dst_row[i] = static_cast<int32_t>(r);
+  src_token[r] = static_cast<int32_t>(t);
+}
+
+// d_logits from d_topk_w: one wave per token.
+template <int EPL>
+__global__ __launch_bounds__(256) void route_bwd_kernel(const float* __restrict__ logits,
+                                                        const int32_t* __restrict__ topk_idx,
+                                                        const float* __restrict__ topk_w,
+                                                        const float* __restrict__ d_topk_w, int64_t T,
+                                                        int E, int k, int score, int renorm,
+                                                        float* __restrict__ d_logits) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + t * E;
+  const bool active = lane < k;
+  int e_j = active ? topk_idx[t * k + lane] : -1;
+  if (e_j >= E) e_j = -1;
+  const float w_j = active ? topk_w[t * k + lane] : 0.f;
+  const float dw_j = active ? d_topk_w[t * k + lane] : 0.f;
+  const float g = wave_sum(w_j * dw_j);
+  float dz_j = 0.f;
+  if (score == 1) {
+    const float z = e_j >= 0 ? row[e_j] : 0.f;
+    const float s = 1.0f / (1.0f + expf(-z));
+    if (renorm) {
+      const float S = wave_sum(active ? s : 0.f);
+      dz_j = (dw_j - g) / S * s * (1.0f - s);
+    } else {
+      dz_j = dw_j * s * (1.0f - s);
+    }
+  } else if (renorm) {
+    dz_j = w_j * (dw_j - g);
+  }
+  float v[EPL];
+  float m = -INFINITY, denom = 0.f;
+  if (score == 0 && !renorm) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + 64 * i;
+      v[i] = e < E ? row[e] : -INFINITY;
+      m = fmaxf(m, v[i]);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (lane + 64 * i < E) part += expf(v[i] - m);
+    denom = wave_sum(part);
+  }
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    float out = 0.f;
+    float G = 0.f;
+    bool chosen = false;
+    for (int j = 0; j < k; ++j) {
+      const int ej = __shfl(e_j, j, 64);
+      const float dzj = __shfl(dz_j, j, 64);
+      const float dwj = __shfl(dw_j, j, 64);
+      if (ej == e) {
+        chosen = true;
+        out = dzj;
+        G = dwj;
+      }
+    }
+    if (score == 0 && !renorm) {
+      const float p = e < E ? expf(v[i] - m) / denom : 0.f;
+      out = p * (G - g);
+    } else if (!chosen) {
+      out = 0.f;
+    }
+    if (e < E) d_logits[t * E + e] = out;
+  }
+}
+
+static int epl_for(int E) { return E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : E <= 512 ? 8 : 16; }
+
+hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int score, int renorm,
+                             int32_t* topk_idx, float* topk_w, int32_t* counts, int64_t* offsets,
+                             int32_t* dst_row, int32_t* src_token, void* ws, hipStream_t stream) {
+  const int64_t ntiles = (T + ROUTE_TILE - 1) / ROUTE_TILE;
+  unsigned long long* tile_bits = static_cast<unsigned long long*>(ws);
+  int32_t* tile_base = reinterpret_cast<int32_t*>(tile_bits + ntiles * E);
+  if (ntiles > 0) {
+    switch (epl_for(E)) {
+#define MOE_TOPK(n)                                                                               \
+  case n:                                                                                         \
+    topk_kernel<n><<<dim3(static_cast<unsigned>(ntiles)), 256, 0, stream>>>(                      \
+        logits, T, E, k, score, renorm, topk_idx, topk_w, tile_bits);                             \
+    break;
+      MOE_TOPK(1) MOE_TOPK(2) MOE_TOPK(4) MOE_TOPK(8) MOE_TOPK(16)
+#undef MOE_TOPK
+    }
+  }
+  route_scan_kernel<<<1, 1024, 0, stream>>>(tile_bits, ntiles, E, tile_base, counts, offsets);
+  if (T > 0) {
+    const int64_t n = T * k;
+    route_rank_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), 256, 0, stream>>>(
+        topk_idx, tile_bits, tile_base, offsets, T, E, k, dst_row, src_token);
+  }
+  return hipGetLastError();
+}
+
+size_t route_topk_workspace(int64_t T, int E) {
+  const int64_t ntiles = (T + ROUTE_TILE - 1) / ROUTE_TILE;
+  return static_cast<size_t>(ntiles) * E * (sizeof(unsigned long long) + sizeof(int32_t)) + 256;
+}
+
+hipError_t launch_route_topk_bwd(const float* logits, const int32_t* topk_idx, const float* topk_w,
+                                 const float* d_topk_w, int64_t T, int E, int k, int score,
+                                 int renorm, float* d_logits, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((T + 3) / 4));
+  switch (epl_for(E)) {
+#define MOE_RB(n)                                                                        \
+  case n:                                                                                \
+    route_bwd_kernel<n><<<grid, 256, 0, stream>>>(logits, topk_idx, topk_w, d_topk_w, T, \
+                                                  E, k, score, renorm, d_logits);        \
+    break;
+    MOE_RB(1) MOE_RB(2) MOE_RB(4) MOE_RB(8) MOE_RB(16)
+#undef MOE_RB
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,290 @@
+"""Per-operation parity of every C-ABI call against the CPU oracle on the
+same seeded inputs: bit-exact for routing indices, counts, offsets and the
+permutation; max|err|/max|ref| within 1e-5 (fp32) or 2e-2 (bf16) otherwise.
+Sizes span several tiles and ragged tails; edge cases include ties, empty
+experts, zero tokens and the largest supported E and k."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from routing_grouped_gemm_router_amd import abi, inputs
+from gpu_util import TOL, assert_close, np64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _route_gpu(z, k, score, renorm):
+    T, E = z.shape
+    zz = torch.from_numpy(z).to(DEV)
+    out = dict(
+        topk_idx=torch.empty((T, k), dtype=torch.int32, device=DEV),
+        topk_w=torch.empty((T, k), dtype=torch.float32, device=DEV),
+        counts=torch.empty(E, dtype=torch.int32, device=DEV),
+        offsets=torch.empty(E + 1, dtype=torch.int64, device=DEV),
+        dst_row=torch.empty((T, k), dtype=torch.int32, device=DEV),
+        src_token=torch.empty(T * k, dtype=torch.int32, device=DEV),
+    )
+    ws = torch.empty(abi.moe_route_topk_workspace_bytes(T, E, k), dtype=torch.uint8, device=DEV)
+    abi.moe_route_topk(zz, k, abi.SOFTMAX if score == "softmax" else abi.SIGMOID, renorm,
+                       out["topk_idx"], out["topk_w"], out["counts"], out["offsets"],
+                       out["dst_row"], out["src_token"], ws)
+    torch.cuda.synchronize()
+    return zz, out
+
+
+def _keys(T, E, seed, kind):
+    g = torch.Generator().manual_seed(seed)
+    z = torch.randn((T, E), generator=g, dtype=torch.float32)
+    if kind == "ties":
+        z = torch.round(z * 2) / 2          # many exact ties
+    elif kind == "equal":
+        z = torch.full((T, E), 0.375)
+    elif kind == "zeros":
+        z = torch.zeros((T, E))
+        z[::2] = -0.0                        # signed zeros must tie
+    elif kind == "zipf":
+        z = z + inputs.logit_bias(inputs.CONFIGS["qwen3_235b_e128k8"], seed)
+    elif kind == "bias05":
+        z = (z + torch.randn(E, generator=g) * 0.5 ** 0.5).float()
+    return z.numpy().astype(np.float32)
+
+
+ROUTE_CASES = [
+    # T, E, k, score, renorm, kind
+    (64, 4, 2, "softmax", True, "normal"),
+    (1000, 128, 8, "softmax", True, "ties"),
+    (16384, 128, 8, "softmax", True, "zipf"),
+    (8192, 256, 8, "sigmoid", True, "bias05"),
+    (32768, 256, 8, "sigmoid", True, "bias05"),
+    (333, 1000, 64, "softmax", False, "normal"),
+    (130, 16, 4, "sigmoid", False, "equal"),
+    (77, 8, 8, "softmax", True, "zeros"),
+    (1, 8, 2, "softmax", False, "normal"),
+    (100, 1, 1, "sigmoid", True, "normal"),
+]
+
+
+@pytest.mark.parametrize("T,E,k,score,renorm,kind", ROUTE_CASES)
+def test_route_topk_bit_exact(gpu, T, E, k, score, renorm, kind):
+    print(f"route T={T} E={E} k={k} {score} renorm={renorm} {kind}", flush=True)
+    z = _keys(T, E, 1234 + T, kind)
+    _, g = _route_gpu(z, k, score, renorm)
+    r = oracle.route(z, k, score, renorm)
+    np.testing.assert_array_equal(g["topk_idx"].cpu().numpy(), r["topk_idx"])
+    np.testing.assert_array_equal(g["counts"].cpu().numpy(), r["counts"])
+    np.testing.assert_array_equal(g["offsets"].cpu().numpy(), r["offsets"])
+    np.testing.assert_array_equal(g["dst_row"].cpu().numpy(), r["dst_row"])
+    np.testing.assert_array_equal(g["src_token"].cpu().numpy(), r["src_token"])
+    assert_close("topk_w", g["topk_w"], r["topk_w"], TOL["f32"])
+
+
+def test_route_topk_zero_tokens(gpu):
+    z = np.zeros((0, 16), np.float32)
+    _, g = _route_gpu(z, 4, "softmax", True)
+    assert int(g["counts"].abs().sum()) == 0
+    assert int(g["offsets"].abs().sum()) == 0
+
+
+def test_route_topk_deterministic(gpu):
+    z = _keys(5000, 256, 5, "ties")
+    _, a = _route_gpu(z, 8, "sigmoid", True)
+    _, b = _route_gpu(z, 8, "sigmoid", True)
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("score,renorm", [("softmax", True), ("softmax", False),
+                                          ("sigmoid", True), ("sigmoid", False)])
+def test_route_topk_bwd(gpu, score, renorm):
+    T, E, k = 700, 64, 6
+    z = _keys(T, E, 77, "normal")
+    zz, g = _route_gpu(z, k, score, renorm)
+    dw = torch.randn((T, k), generator=torch.Generator().manual_seed(3), dtype=torch.float32)
+    dz = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    abi.moe_route_topk_bwd(zz, g["topk_idx"], g["topk_w"], dw.to(DEV),
+                           abi.SOFTMAX if score == "softmax" else abi.SIGMOID, renorm, dz)
+    r = oracle.route(z, k, score, renorm)
+    ref = oracle.route_bwd(z, r["topk_idx"], r["topk_w"], dw.numpy(), score, renorm)
+    assert_close("d_logits", dz, ref, TOL["f32"])
+
+
+def _perm_dst(T, k, seed):
+    p = torch.randperm(T * k, generator=torch.Generator().manual_seed(seed)).to(torch.int32)
+    dst = p.reshape(T, k)
+    src = torch.empty(T * k, dtype=torch.int32)
+    src[p.long()] = torch.arange(T, dtype=torch.int32).repeat_interleave(k)
+    return dst, src
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("T,d,k", [(257, 128, 2), (1000, 7168, 8), (3, 8, 1)])
+def test_permute_exact(gpu, dt, T, d, k):
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    x = inputs.normal((T, d), 1.0, 11, 0, "cpu", tdt)
+    dst, src = _perm_dst(T, k, 5)
+    xp = torch.full((T * k, d), float("nan"), dtype=tdt, device=DEV)
+    abi.moe_permute(x.to(DEV), dst.to(DEV), xp)
+    ref = oracle.permute(x.float().numpy(), src.numpy())
+    np.testing.assert_array_equal(xp.float().cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("T,d,k,shared", [(257, 128, 2, True), (1000, 7168, 8, False),
+                                          (64, 64, 4, True)])
+def test_unpermute_combine(gpu, dt, T, d, k, shared):
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    y = inputs.normal((T * k, d), 1.0, 21, 0, "cpu", tdt)
+    w = torch.rand((T, k), generator=torch.Generator().manual_seed(2), dtype=torch.float32)
+    sh = inputs.normal((T, d), 1.0, 22, 0, "cpu", tdt) if shared else None
+    dst, _ = _perm_dst(T, k, 6)
+    out = torch.empty((T, d), dtype=tdt, device=DEV)
+    abi.moe_unpermute_combine(y.to(DEV), w.to(DEV), dst.to(DEV),
+                              None if sh is None else sh.to(DEV), out)
+    ref = oracle.unpermute_combine(np64(y), w.numpy(), dst.numpy(), None if sh is None else np64(sh))
+    assert_close("out", out, ref, TOL[dt])
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("T,d,k", [(257, 128, 2), (700, 7168, 8), (40, 32, 64)])
+def test_unpermute_combine_bwd(gpu, dt, T, d, k):
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    y = inputs.normal((T * k, d), 1.0, 31, 0, "cpu", tdt)
+    dout = inputs.normal((T, d), 1.0, 32, 0, "cpu", tdt)
+    w = torch.rand((T, k), generator=torch.Generator().manual_seed(4), dtype=torch.float32)
+    dst, _ = _perm_dst(T, k, 7)
+    dy = torch.empty((T * k, d), dtype=tdt, device=DEV)
+    dw = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    abi.moe_unpermute_combine_bwd(dout.to(DEV), y.to(DEV), w.to(DEV), dst.to(DEV), dy, dw)
+    rdy, rdw = oracle.unpermute_combine_bwd(np64(dout), np64(y), w.numpy(), dst.numpy())
+    assert_close("dy_perm", dy, rdy, TOL[dt])
+    assert_close("d_topk_w", dw, rdw, TOL["f32"] if dt == "f32" else 1e-4)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("T,d,k", [(257, 128, 2), (700, 7168, 8)])
+def test_permute_bwd(gpu, dt, T, d, k):
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    dxp = inputs.normal((T * k, d), 1.0, 41, 0, "cpu", tdt)
+    add = inputs.normal((T, d), 1.0, 42, 0, "cpu", tdt)
+    add32 = inputs.normal((T, d), 1.0, 43, 0, "cpu", torch.float32)
+    dst, _ = _perm_dst(T, k, 8)
+    dx = torch.empty((T, d), dtype=tdt, device=DEV)
+    abi.moe_permute_bwd(dxp.to(DEV), dst.to(DEV), add.to(DEV), add32.to(DEV), dx)
+    ref = oracle.permute_bwd(np64(dxp), dst.numpy(), addends=(np64(add), np64(add32)))
+    assert_close("dx", dx, ref, TOL[dt])
+    dx2 = torch.empty((T, d), dtype=tdt, device=DEV)
+    abi.moe_permute_bwd(dxp.to(DEV), dst.to(DEV), None, None, dx2)
+    assert_close("dx (no addends)", dx2, oracle.permute_bwd(np64(dxp), dst.numpy()), TOL[dt])
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_swiglu_standalone(gpu, dt):
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    M, f = 333, 256
+    ab = inputs.normal((M, 2 * f), 2.0, 51, 0, "cpu", tdt)
+    dh = inputs.normal((M, f), 1.0, 52, 0, "cpu", tdt)
+    h = torch.empty((M, f), dtype=tdt, device=DEV)
+    dab = torch.empty((M, 2 * f), dtype=tdt, device=DEV)
+    abi.moe_swiglu(ab.to(DEV), h)
+    abi.moe_swiglu_bwd(dh.to(DEV), ab.to(DEV), dab)
+    assert_close("h", h, oracle.swiglu(np64(ab)), TOL[dt])
+    assert_close("dab", dab, oracle.swiglu_bwd(np64(dh), np64(ab)), TOL[dt])
+
+
+GEMM_CASES = [
+    # M, G, K, N, empty_frac, skew
+    (1000, 5, 256, 384, 0.0, 0.0),
+    (777, 8, 512, 256, 0.3, 0.0),
+    (2600, 4, 128, 128, 0.0, 1.0),
+    (129, 1, 256, 128, 0.0, 0.0),
+    (0, 3, 128, 128, 0.0, 0.0),
+]
+
+
+def _gemm_inputs(M, G, K, N, empty_frac, skew, tdt, seed=0):
+    off = inputs.random_segments(M, G, seed, empty_frac=empty_frac, skew=skew) if M else \
+        torch.zeros(G + 1, dtype=torch.int64)
+    A = inputs.normal((M, K), 1.0, seed + 1, 0, "cpu", tdt)
+    B = inputs.normal((G, K, N), K ** -0.5, seed + 2, 0, "cpu", tdt)
+    dC = inputs.normal((M, N), 1.0, seed + 3, 0, "cpu", tdt)
+    return off, A, B, dC
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("M,G,K,N,empty_frac,skew", GEMM_CASES)
+def test_grouped_gemm(gpu, dt, M, G, K, N, empty_frac, skew):
+    print(f"grouped gemm {dt} M={M} G={G} K={K} N={N}", flush=True)
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    off, A, B, dC = _gemm_inputs(M, G, K, N, empty_frac, skew, tdt)
+    offd = off.to(DEV)
+    Ad, Bd, dCd = A.to(DEV), B.to(DEV), dC.to(DEV)
+    C = torch.empty((M, N), dtype=tdt, device=DEV)
+    abi.moe_grouped_gemm_fwd(Ad, Bd, offd, C)
+    dA = torch.empty((M, K), dtype=tdt, device=DEV)
+    abi.moe_grouped_gemm_dgrad(dCd, Bd, offd, dA)
+    dB = torch.full((G, K, N), float("nan"), dtype=tdt, device=DEV)
+    abi.moe_grouped_gemm_wgrad(Ad, dCd, offd, dB)
+    dB32 = torch.full((G, K, N), float("nan"), dtype=torch.float32, device=DEV)
+    abi.moe_grouped_gemm_wgrad(Ad, dCd, offd, dB32)
+    torch.cuda.synchronize()
+    o = off.numpy()
+    if M:
+        assert_close("C", C, oracle.grouped_gemm_fwd(np64(A), np64(B), o), TOL[dt])
+        assert_close("dA", dA, oracle.grouped_gemm_dgrad(np64(dC), np64(B), o), TOL[dt])
+    ref_dB = oracle.grouped_gemm_wgrad(np64(A), np64(dC), o)
+    assert_close("dB", dB, ref_dB, TOL[dt])
+    assert_close("dB fp32", dB32, ref_dB, TOL[dt])
+    # accumulate: dB32 += A^T dC again
+    abi.moe_grouped_gemm_wgrad(Ad, dCd, offd, dB32, accumulate=True)
+    assert_close("dB accumulate", dB32, 2 * ref_dB, TOL[dt])
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_grouped_gemm_swiglu_epilogues(gpu, dt):
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    M, G, d, f = 900, 6, 256, 256
+    off, X, W13, _ = _gemm_inputs(M, G, d, 2 * f, 0.2, 0.0, tdt, seed=10)
+    dH = inputs.normal((M, f), 1.0, 99, 0, "cpu", tdt)
+    W2 = inputs.normal((G, f, d), f ** -0.5, 98, 0, "cpu", tdt)
+    dY = inputs.normal((M, d), 1.0, 97, 0, "cpu", tdt)
+    offd = off.to(DEV)
+    AB = torch.empty((M, 2 * f), dtype=tdt, device=DEV)
+    H = torch.empty((M, f), dtype=tdt, device=DEV)
+    abi.moe_grouped_gemm_fwd(X.to(DEV), W13.to(DEV), offd, AB, H, epilogue=abi.EPI_SWIGLU)
+    H2 = torch.empty((M, f), dtype=tdt, device=DEV)
+    abi.moe_grouped_gemm_fwd(X.to(DEV), W13.to(DEV), offd, None, H2, epilogue=abi.EPI_SWIGLU)
+    o = off.numpy()
+    ref_ab = oracle.grouped_gemm_fwd(np64(X), np64(W13), o)
+    assert_close("AB", AB, ref_ab, TOL[dt])
+    assert_close("H", H, oracle.swiglu(ref_ab), TOL[dt])
+    assert torch.equal(H, H2)
+    # dgrad of GEMM 2 with the SwiGLU backward in the epilogue, from the GPU's AB
+    dAB = torch.empty((M, 2 * f), dtype=tdt, device=DEV)
+    abi.moe_grouped_gemm_dgrad(dY.to(DEV), W2.to(DEV), offd, dAB, epilogue=abi.EPI_SWIGLU_BWD,
+                               ab=AB)
+    ab_in = np64(AB)  # the epilogue's own input, rounded as the GPU stored it
+    ref_dh = oracle.grouped_gemm_dgrad(np64(dY), np64(W2), o)
+    assert_close("dAB", dAB, oracle.swiglu_bwd(ref_dh, ab_in), TOL[dt])
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("T,d,E,bias", [(64, 128, 4, False), (1000, 4096, 128, True),
+                                        (515, 7168, 256, True)])
+def test_router_logits(gpu, dt, T, d, E, bias):
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    x = inputs.normal((T, d), 1.0, 61, 0, "cpu", tdt)
+    w_r = inputs.normal((d, E), d ** -0.5, 62, 0, "cpu", torch.float32)
+    b = inputs.normal((E,), 0.7, 63, 0, "cpu", torch.float32) if bias else None
+    dz = inputs.normal((T, E), 1.0, 64, 0, "cpu", torch.float32)
+    lg = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    abi.moe_router_logits(x.to(DEV), w_r.to(DEV), None if b is None else b.to(DEV), lg)
+    ref = oracle.router_logits(np64(x), w_r.numpy(), None if b is None else b.numpy())
+    assert_close("logits", lg, ref, TOL["f32"])
+    dwr = torch.empty((d, E), dtype=torch.float32, device=DEV)
+    dxr = torch.empty((T, d), dtype=torch.float32, device=DEV)
+    abi.moe_router_logits_bwd(x.to(DEV), w_r.to(DEV), dz.to(DEV), dwr, dxr)
+    rw, rx = oracle.router_logits_bwd(np64(x), w_r.numpy(), dz.numpy())
+    assert_close("dW_r", dwr, rw, TOL["f32"])
+    assert_close("dx_router", dxr, rx, TOL["f32"])
