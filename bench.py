@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of one MoE layer, forward + backward, on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--seed S] [--no-cpu-baseline]
+
+Default workload: the DeepSeek-V3-shaped layer (T=8192 tokens, d=7168, 256
+routed SwiGLU experts with ffn 2048, sigmoid top-8 renormalised over k, one
+shared expert of ffn 2048; bf16 storage, fp32 accumulation; fp32 router).
+Inputs are seeded synthetic tensors generated on the GPU; weights resident in
+HBM before the timed region.  A step is the whole hot path: router, top-k,
+permute, both grouped GEMMs (SwiGLU fused), shared expert, combine, and the
+backward of every one of them.
+
+Prints ONE JSON line.  ``value`` is the layer's algorithmic FLOP rate (expert
+GEMM FLOPs over the routed rows plus the fp32 router FLOPs, divided by the
+measured time per step).  Per-call times come from HIP events recorded on the
+launch stream inside the timed region; ``roofline`` reports the dominant
+kernel against MI355X's published peaks; ``cpu_baseline`` times the CPU
+oracle on a bounded token sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer fwd+bwd TFLOPS + permute/combine GB/s on 1 MI355X (roofline %)"
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0    # dense bf16 MFMA, published
+PEAK_F32_TFLOPS = 157.3      # fp32 vector, published
+RIDGE_BF16 = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="deepseek_v3_e256k8")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target duration of the CPU oracle sample")
+    return ap.parse_args()
+
+
+def kernel_work(cfg, n_nonempty):
+    """Algorithmic FLOPs and HBM bytes per call of every span.
+
+    FLOPs: 2 per multiply-add over the routed rows only.  Bytes: every
+    operand read once and every result written once; an expert's weights
+    count once per GEMM pass when the expert received rows; index and
+    routing-weight arrays included."""
+    T, d, E, k, f, fs = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.fs
+    N = T * k
+    s = 2 if cfg.dtype == "bf16" else 4      # activation / weight element bytes
+    w13 = n_nonempty * d * 2 * f * s
+    w2 = n_nonempty * f * d * s
+    idx = T * k * 4
+    w = {
+        "router_logits": (2.0 * T * d * E, T * d * s + d * E * 4 + T * E * 4),
+        "route_topk": (0.0, T * E * 4 + 3 * idx + T * k * 4 + N * 4),
+        "permute": (0.0, T * d * s + idx + N * d * s),
+        "gemm1_fwd": (2.0 * N * d * 2 * f, N * d * s + w13 + N * 2 * f * s + N * f * s),
+        "gemm2_fwd": (2.0 * N * f * d, N * f * s + w2 + N * d * s),
+        "combine": (0.0, N * d * s + 2 * idx + T * d * s * (2 if fs else 1)),
+        "combine_bwd": (0.0, T * d * s + 2 * N * d * s + 3 * idx),
+        "gemm2_dgrad": (2.0 * N * d * f, N * d * s + w2 + N * 2 * f * s * 2),
+        "gemm2_wgrad": (2.0 * N * f * d, N * f * s + N * d * s + E * f * d * s),
+        "gemm1_dgrad": (2.0 * N * 2 * f * d, N * 2 * f * s + w13 + N * d * s),
+        "gemm1_wgrad": (2.0 * N * d * 2 * f, N * d * s + N * 2 * f * s + E * d * 2 * f * s),
+        "route_topk_bwd": (0.0, T * E * 4 * 2 + 3 * idx),
+        "router_logits_bwd": (4.0 * T * d * E, T * d * s + T * E * 4 + d * E * 4 * 2 + T * d * 4),
+        "permute_bwd": (0.0, N * d * s + idx + T * d * (s + 4 + (s if fs else 0))),
+    }
+    if fs:
+        w.update({
+            "shared_gemm1_fwd": (2.0 * T * d * 2 * fs, T * d * s + d * 2 * fs * s + T * 3 * fs * s),
+            "shared_gemm2_fwd": (2.0 * T * fs * d, T * fs * s + fs * d * s + T * d * s),
+            "shared_gemm2_dgrad": (2.0 * T * d * fs, T * d * s + fs * d * s + T * 4 * fs * s),
+            "shared_gemm2_wgrad": (2.0 * T * fs * d, T * fs * s + T * d * s + fs * d * s),
+            "shared_gemm1_dgrad": (2.0 * T * 2 * fs * d, T * 2 * fs * s + d * 2 * fs * s + T * d * s),
+            "shared_gemm1_wgrad": (2.0 * T * d * 2 * fs, T * d * s + T * 2 * fs * s + d * 2 * fs * s),
+        })
+    return w
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch measured with rocprofv3 counters, if the committed
+    measurement was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec:
+        return None
+    src = os.path.join(ROOT, "routing_grouped_gemm_router_amd", "csrc", rec["source"])
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["sha256"]:
+        return None
+    return rec["bytes_per_launch"]
+
+
+def cpu_baseline(cfg, inp, budget_s):
+    """The CPU oracle (untuned, one thread) on the first tokens of the same
+    workload: routing, each token's k experts forward and backward, the
+    shared expert and the router backward.  Weight copies to the host are
+    outside the timing."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle
+
+    def host(t):
+        return t.detach().float().cpu().numpy()
+
+    k = cfg.k
+    per_token = 18.0 * k * cfg.d * cfg.f + 18.0 * cfg.d * cfg.fs + 6.0 * cfg.d * cfg.E
+    w_r = host(inp["w_r"])
+    bias = None if inp["logit_bias"] is None else host(inp["logit_bias"])
+    shared = (host(inp["ws13"]), host(inp["ws2"])) if cfg.fs else None
+    spent, ntok = 0.0, 0
+    with threadpool_limits(1):
+        while spent < budget_s and ntok < 256:
+            t = ntok
+            x_t = host(inp["x"][t:t + 1]).astype(np.float64)
+            dout_t = host(inp["dout"][t]).astype(np.float64)
+            c0 = time.perf_counter()
+            z = oracle.router_logits(x_t, w_r, bias)
+            r = oracle.route(z, k, cfg.score, cfg.renorm)
+            spent += time.perf_counter() - c0
+            dw = np.zeros((1, k))
+            for j in range(k):
+                e = int(r["topk_idx"][0, j])
+                w13e, w2e = host(inp["w13"][e]), host(inp["w2"][e])
+                c0 = time.perf_counter()
+                a, b, h, y = oracle.expert_ffn(x_t[0], w13e, w2e)
+                dw[0, j] = dout_t @ y
+                oracle.expert_ffn_bwd(x_t[0], w13e, w2e, a, b, h, r["topk_w"][0, j] * dout_t)
+                spent += time.perf_counter() - c0
+            c0 = time.perf_counter()
+            if shared is not None:
+                a, b, h, y = oracle.expert_ffn(x_t[0], *shared)
+                oracle.expert_ffn_bwd(x_t[0], shared[0], shared[1], a, b, h, dout_t)
+            dz = oracle.route_bwd(z, r["topk_idx"], r["topk_w"], dw, cfg.score, cfg.renorm)
+            oracle.router_logits_bwd(x_t, w_r, dz)
+            spent += time.perf_counter() - c0
+            ntok += 1
+    return {
+        "value": per_token * ntok / spent / 1e12,
+        "unit": "TFLOP/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"first {ntok} tokens of the {cfg.name} layer through the oracle's per-token "
+                   f"loop (routing, {ntok * k} token-expert SwiGLU forward+backward pairs, shared "
+                   f"expert, router backward), float64 NumPy, 1 thread, {spent:.1f} s; same "
+                   f"algorithmic FLOPs per token as the GPU line"),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the single-GPU hot path only: this build runs on one GPU "
+              "(no collectives); run it with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    from routing_grouped_gemm_router_amd import inputs
+    from routing_grouped_gemm_router_amd.layer import EventTimer, MoELayer
+
+    cfg = inputs.CONFIGS[args.config]
+    if cfg.gemm == "fp8":
+        print(f"{cfg.name}: fp8 expert GEMMs are not available in this build", file=sys.stderr)
+        return 2
+    dev = "cuda"
+    inp = inputs.layer_inputs(cfg, args.seed, dev)
+    layer = MoELayer(cfg, inp, dev)
+    x, dout = inp["x"], inp["dout"]
+    for _ in range(args.warmup):
+        layer.forward(x)
+        layer.backward(dout)
+    torch.cuda.synchronize()
+
+    timer = EventTimer()
+    layer.timer = timer
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        layer.forward(x)
+        layer.backward(dout)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    layer.timer = None
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    spans = timer.summary()
+    counts = layer.counts.cpu()
+    n_nonempty = int((counts > 0).sum())
+    work = kernel_work(cfg, n_nonempty)
+    kernels = {}
+    for name, (ms, n) in spans.items():
+        fl, by = work[name]
+        kernels[name] = {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 2) if fl else None,
+                         "GB/s": round(by / ms / 1e6, 1), "alg_bytes": int(by), "alg_flops": fl}
+    total_flops = sum(fl for fl, _ in work.values())
+    value = total_flops / (ms_step / 1e3) / 1e12
+
+    gemm_names = [n for n in kernels if "gemm" in n]
+    gemm_ms = sum(kernels[n]["ms"] for n in gemm_names)
+    gemm_flops = sum(work[n][0] for n in gemm_names)
+    pc_names = ["permute", "combine", "combine_bwd", "permute_bwd"]
+    pc_ms = sum(kernels[n]["ms"] for n in pc_names)
+    pc_bytes = sum(work[n][1] for n in pc_names)
+
+    dom = max(kernels, key=lambda n: kernels[n]["ms"])
+    fl, by = work[dom]
+    ms = kernels[dom]["ms"]
+    if fl and fl / by >= RIDGE_BF16:
+        roof = {"bound": "mfma", "achieved": round(fl / ms / 1e9, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(by / ms / 1e6, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["kernel"] = dom
+    roof["alg_flops_per_launch"] = fl
+    roof["alg_bytes_per_launch"] = int(by)
+    roof["ms_per_launch"] = ms
+    roof["traffic"] = traffic_for(dom)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.gemm,
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights, generated on the GPU)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
+                   "ffn": cfg.f, "shared_ffn": cfg.fs, "score": cfg.score, "renorm": cfg.renorm,
+                   "router_bias": cfg.bias, "experts_with_rows": n_nonempty,
+                   "max_rows_per_expert": int(counts.max())},
+        "grouped_gemm": {"TFLOP/s": round(gemm_flops / gemm_ms / 1e9, 1),
+                         "frac_bf16_peak": round(gemm_flops / gemm_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                         "ms": round(gemm_ms, 3)},
+        "permute_combine": {"GB/s": round(pc_bytes / pc_ms / 1e6, 1),
+                            "frac_hbm_peak": round(pc_bytes / pc_ms / 1e6 / PEAK_HBM_GBS, 4),
+                            "ms": round(pc_ms, 4)},
+        "roofline": roof,
+        "kernels": kernels,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

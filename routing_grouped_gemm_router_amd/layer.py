@@ -17,9 +17,37 @@ No step synchronises with the host: per-expert row counts stay on the device
 and every buffer is sized from T * k.  Buffers are allocated once per layer
 and reused across steps.  Python here only allocates and orders the calls.
 """
+import contextlib
+
 import torch
 
 from . import abi
+
+
+class EventTimer:
+    """Per-call device timing with HIP events on the current stream.
+
+    ``span(name)`` brackets the enqueued calls with two events; ``summary()``
+    (after a synchronize) returns name -> (mean ms per span, count)."""
+
+    def __init__(self):
+        self.spans = {}
+
+    @contextlib.contextmanager
+    def span(self, name):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        yield
+        b.record()
+        self.spans.setdefault(name, []).append((a, b))
+
+    def summary(self):
+        return {n: (sum(a.elapsed_time(b) for a, b in v) / len(v), len(v))
+                for n, v in self.spans.items()}
+
+
+_NO_SPAN = contextlib.nullcontext()
 
 
 class MoELayer:
@@ -31,6 +59,7 @@ class MoELayer:
 
     def __init__(self, cfg, weights, device="cuda"):
         self.cfg = cfg
+        self.timer = None
         self.dev = torch.device(device)
         self.w = weights
         T, d, E, k, f = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f
@@ -79,48 +108,72 @@ class MoELayer:
             self.dws2 = emp(1, fs, d)
 
     # ------------------------------------------------------------ forward --
+    def _span(self, name):
+        return self.timer.span(name) if self.timer is not None else _NO_SPAN
+
     def forward(self, x):
         c, w = self.cfg, self.w
         self.x = x
-        abi.moe_router_logits(x, w["w_r"], w.get("logit_bias"), self.logits)
-        abi.moe_route_topk(self.logits, c.k, self.score, c.renorm, self.topk_idx, self.topk_w,
-                           self.counts, self.offsets, self.dst_row, self.src_token, self.route_ws)
-        abi.moe_permute(x, self.dst_row, self.x_perm)
-        abi.moe_grouped_gemm_fwd(self.x_perm, w["w13"], self.offsets, self.ab, self.h,
-                                 epilogue=abi.EPI_SWIGLU)
-        abi.moe_grouped_gemm_fwd(self.h, w["w2"], self.offsets, self.y)
+        with self._span("router_logits"):
+            abi.moe_router_logits(x, w["w_r"], w.get("logit_bias"), self.logits)
+        with self._span("route_topk"):
+            abi.moe_route_topk(self.logits, c.k, self.score, c.renorm, self.topk_idx, self.topk_w,
+                               self.counts, self.offsets, self.dst_row, self.src_token,
+                               self.route_ws)
+        with self._span("permute"):
+            abi.moe_permute(x, self.dst_row, self.x_perm)
+        with self._span("gemm1_fwd"):
+            abi.moe_grouped_gemm_fwd(self.x_perm, w["w13"], self.offsets, self.ab, self.h,
+                                     epilogue=abi.EPI_SWIGLU)
+        with self._span("gemm2_fwd"):
+            abi.moe_grouped_gemm_fwd(self.h, w["w2"], self.offsets, self.y)
         ys = None
         if self.shared:
-            abi.moe_grouped_gemm_fwd(x, self.ws13, self.off_all, self.abs_, self.hs,
-                                     epilogue=abi.EPI_SWIGLU)
-            abi.moe_grouped_gemm_fwd(self.hs, self.ws2, self.off_all, self.ys)
+            with self._span("shared_gemm1_fwd"):
+                abi.moe_grouped_gemm_fwd(x, self.ws13, self.off_all, self.abs_, self.hs,
+                                         epilogue=abi.EPI_SWIGLU)
+            with self._span("shared_gemm2_fwd"):
+                abi.moe_grouped_gemm_fwd(self.hs, self.ws2, self.off_all, self.ys)
             ys = self.ys
-        abi.moe_unpermute_combine(self.y, self.topk_w, self.dst_row, ys, self.out)
+        with self._span("combine"):
+            abi.moe_unpermute_combine(self.y, self.topk_w, self.dst_row, ys, self.out)
         return self.out
 
     # ----------------------------------------------------------- backward --
     def backward(self, dout):
         c, w = self.cfg, self.w
         x = self.x
-        abi.moe_unpermute_combine_bwd(dout, self.y, self.topk_w, self.dst_row, self.dy,
-                                      self.d_topk_w)
-        abi.moe_grouped_gemm_dgrad(self.dy, w["w2"], self.offsets, self.dab,
-                                   epilogue=abi.EPI_SWIGLU_BWD, ab=self.ab)
-        abi.moe_grouped_gemm_wgrad(self.h, self.dy, self.offsets, self.dw2)
-        abi.moe_grouped_gemm_dgrad(self.dab, w["w13"], self.offsets, self.dx_perm)
-        abi.moe_grouped_gemm_wgrad(self.x_perm, self.dab, self.offsets, self.dw13)
+        with self._span("combine_bwd"):
+            abi.moe_unpermute_combine_bwd(dout, self.y, self.topk_w, self.dst_row, self.dy,
+                                          self.d_topk_w)
+        with self._span("gemm2_dgrad"):
+            abi.moe_grouped_gemm_dgrad(self.dy, w["w2"], self.offsets, self.dab,
+                                       epilogue=abi.EPI_SWIGLU_BWD, ab=self.ab)
+        with self._span("gemm2_wgrad"):
+            abi.moe_grouped_gemm_wgrad(self.h, self.dy, self.offsets, self.dw2)
+        with self._span("gemm1_dgrad"):
+            abi.moe_grouped_gemm_dgrad(self.dab, w["w13"], self.offsets, self.dx_perm)
+        with self._span("gemm1_wgrad"):
+            abi.moe_grouped_gemm_wgrad(self.x_perm, self.dab, self.offsets, self.dw13)
         dxs = None
         if self.shared:
-            abi.moe_grouped_gemm_dgrad(dout, self.ws2, self.off_all, self.dabs,
-                                       epilogue=abi.EPI_SWIGLU_BWD, ab=self.abs_)
-            abi.moe_grouped_gemm_wgrad(self.hs, dout, self.off_all, self.dws2)
-            abi.moe_grouped_gemm_dgrad(self.dabs, self.ws13, self.off_all, self.dxs)
-            abi.moe_grouped_gemm_wgrad(x, self.dabs, self.off_all, self.dws13)
+            with self._span("shared_gemm2_dgrad"):
+                abi.moe_grouped_gemm_dgrad(dout, self.ws2, self.off_all, self.dabs,
+                                           epilogue=abi.EPI_SWIGLU_BWD, ab=self.abs_)
+            with self._span("shared_gemm2_wgrad"):
+                abi.moe_grouped_gemm_wgrad(self.hs, dout, self.off_all, self.dws2)
+            with self._span("shared_gemm1_dgrad"):
+                abi.moe_grouped_gemm_dgrad(self.dabs, self.ws13, self.off_all, self.dxs)
+            with self._span("shared_gemm1_wgrad"):
+                abi.moe_grouped_gemm_wgrad(x, self.dabs, self.off_all, self.dws13)
             dxs = self.dxs
-        abi.moe_route_topk_bwd(self.logits, self.topk_idx, self.topk_w, self.d_topk_w, self.score,
-                               c.renorm, self.d_logits)
-        abi.moe_router_logits_bwd(x, w["w_r"], self.d_logits, self.dw_r, self.dx_router)
-        abi.moe_permute_bwd(self.dx_perm, self.dst_row, dxs, self.dx_router, self.dx)
+        with self._span("route_topk_bwd"):
+            abi.moe_route_topk_bwd(self.logits, self.topk_idx, self.topk_w, self.d_topk_w,
+                                   self.score, c.renorm, self.d_logits)
+        with self._span("router_logits_bwd"):
+            abi.moe_router_logits_bwd(x, w["w_r"], self.d_logits, self.dw_r, self.dx_router)
+        with self._span("permute_bwd"):
+            abi.moe_permute_bwd(self.dx_perm, self.dst_row, dxs, self.dx_router, self.dx)
         return self.dx
 
     def grads(self):
