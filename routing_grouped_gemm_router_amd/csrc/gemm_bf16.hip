@@ -3,42 +3,56 @@
 // Mixture-of-Experts Models with Megatron Core", section 2, Expert Computation
 // (the local experts' GEMMs run together over their ragged row groups).
 //
-// Three products, each over G groups (experts):
-//   forward  C[rows g]  = A[rows g] . B[g]       A [M,K]  B [G,K,N]   (NN)
-//   dgrad    dA[rows g] = dC[rows g] . B[g]^T    dC [M,N] B [G,K,N]   (NT)
-//   wgrad    dB[g]      = A[rows g]^T . dC[rows g]                   (TN)
+//   forward  C[rows g]  = A[rows g] . B[g]       A [M,K]  B [G,K,N]
+//   dgrad    dA[rows g] = dC[rows g] . B[g]^T    dC [M,N] B [G,K,N]
+//   wgrad    dB[g]      = A[rows g]^T . dC[rows g]
 //
-// Design (MI355X):
-//  * Persistent grid of 2 workgroups per CU.  Each workgroup rebuilds the
-//    per-group row-tile prefix from the device offsets in LDS (no host sync,
-//    no workspace), then walks tiles tau = v, v + P, ...  The virtual id v
-//    makes the workgroups of one XCD (hardware dispatches workgroup b to XCD
-//    b mod 8) own consecutive tiles, so the N tiles of one expert row block run
-//    on one XCD and share its activations in that XCD's L2, while each weight
-//    tile is streamed from HBM once per row block.
-//  * 128 x 128 x 64 tiles, 4 waves in a 2 x 2 arrangement, each wave 64 x 64 =
-//    2 x 2 MFMA 32x32x16 blocks.  LDS holds both operands k-contiguous
-//    ([row][k], pitch 72 elements = 144 B, so 16 consecutive rows fall in 16
-//    distinct bank quads); two buffers, one barrier per k step, the next k
-//    step's global loads in flight during the MFMAs.
-//  * Operands whose contraction axis is strided in memory (the weights in the
-//    forward, both operands of wgrad) are loaded as 8 x 8 blocks of 16-byte
-//    vectors and transposed in registers before the LDS store.
-//  * Epilogues: SwiGLU (H = silu(A) * B from the fp32 sums; the tile holds
+// Design for gfx950:
+//  * Persistent grid, one 256-thread workgroup per CU.  Each workgroup builds
+//    the per-group row-tile prefix from the device offsets in LDS (no host
+//    sync), then walks tiles tau = v, v + P, ...; the virtual id v gives the
+//    workgroups of one XCD (workgroup b runs on XCD b mod 8) consecutive tiles,
+//    so the N tiles of one expert row block share that XCD's L2.
+//  * Operands go HBM -> LDS directly (buffer_load ... lds, 16 bytes per lane),
+//    through a 4-stage ring of 32 KiB stages (128 x 64 of A and of B), three
+//    k steps in flight.  The ring runs across tile boundaries: the next tile's
+//    first steps load during the current tile's epilogue.  Buffer resources
+//    bound every tile's rows, so rows past a group's end read as zero and
+//    nothing outside the operands is touched.
+//  * Operands that are k-contiguous in memory are stored [row][k] (128 B rows)
+//    and read with ds_read_b128; operands whose contraction axis is strided
+//    (weights in the forward, both operands of wgrad) are stored as in memory,
+//    [k][row] (256 B rows), and read with ds_read_b64_tr_b16, which hands each
+//    lane four k values of its column.  16-byte chunks are XOR-swizzled by row
+//    so that both the DMA writes and the fragment reads spread over all banks.
+//  * 4 waves in a 2 x 2 arrangement, each 64 x 64 = 2 x 2 MFMA 32x32x16 blocks,
+//    issued as C^T = B^T A^T so that each lane holds 4 consecutive output
+//    columns; the epilogue stages the wave's tile through the ring slot just
+//    consumed and writes 16-byte vectors, 128 bytes per row.
+//  * Epilogues: SwiGLU (AB and H = silu(A) * B from the fp32 sums; a tile holds
 //    matching gate and up columns) and SwiGLU backward (dH -> dAB, reading AB).
 #include "common.h"
 #include "internal.h"
 
 namespace moe {
 
+#define LDS_AS __attribute__((address_space(3)))
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LP = BK + 8;  // LDS row pitch (bf16 elements)
+constexpr int STAGES = 4;
+constexpr int OP_BYTES = 16384;            // one operand of one stage
+constexpr int STAGE_BYTES = 2 * OP_BYTES;  // A then B
 constexpr int MAX_GROUPS = 1024;
+constexpr uint32_t RSRC_DW3 = 0x00020000u; // raw buffer, 32-bit elements, bounds-checked
 
-enum { MODE_FWD = 0, MODE_FWD_SWIGLU = 1, MODE_DGRAD = 2, MODE_DGRAD_SWIGLU_BWD = 3 };
+enum Mode { FWD = 0, FWD_SWIGLU = 1, DGRAD = 2, DGRAD_SWIGLU_BWD = 3, WGRAD = 4 };
 
 static int g_cu_count[64];
 
@@ -58,86 +72,46 @@ __device__ __forceinline__ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) {
   return v < lo ? lo : (v > hi ? hi : v);
 }
 
-// ---- operand staging -----------------------------------------------------
+// chunk swizzles: KC layout [row][8 chunks], NC layout [k][16 chunks]
+__device__ __forceinline__ int swz_kc(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_nc(int kr) { return (kr & 3) << 1; }
 
-// k-contiguous operand: 128 rows x 64 k = 1024 16-byte vectors, 4 per thread.
-__device__ __forceinline__ void kc_load(uint4 (&r)[4], const bf16_t* __restrict__ base, int64_t ld,
-                                        int rows_valid, int tid) {
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int idx = tid + v * 256;
-    const int row = idx >> 3, c = idx & 7;
-    r[v] = row < rows_valid ? *reinterpret_cast<const uint4*>(base + row * ld + c * 8)
-                            : make_uint4(0u, 0u, 0u, 0u);
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over [base, base + bytes): loads past the end return 0.
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t n = bytes > 0xffffffffull ? 0xffffffffu : static_cast<uint32_t>(bytes);
+  i32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(a & 0xffffffffu));
+  r.y = __builtin_amdgcn_readfirstlane(static_cast<int32_t>((a >> 32) & 0xffffu));
+  r.z = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(n));
+  r.w = static_cast<int32_t>(RSRC_DW3);
+  return r;
+}
+
+// 16 bytes per lane from the buffer at byte offset voff into LDS at dst + 16 * lane.
+// Issued as inline assembly so that the compiler adds no waits of its own: the
+// ring is ordered by the explicit vmcnt waits and barriers below.
+__device__ __forceinline__ void dma16(i32x4_t rs, LDS_AS void* dst, uint32_t voff) {
+  const int32_t m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<int32_t>(reinterpret_cast<uintptr_t>(dst)));
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rs), "s"(m0)
+               : "memory", "m0");
+}
+
+// wait until at most n of this wave's vector-memory ops are outstanding, then
+// a workgroup barrier (no implicit fence: the DMA ring is ordered by vmcnt)
+__device__ __forceinline__ void wait_barrier(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
   }
-}
-
-__device__ __forceinline__ void kc_store(bf16_t* __restrict__ lds, const uint4 (&r)[4], int tid) {
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int idx = tid + v * 256;
-    const int row = idx >> 3, c = idx & 7;
-    *reinterpret_cast<uint4*>(lds + row * LP + c * 8) = r[v];
-  }
-}
-
-// Row-contiguous operand (contraction strided): thread lt < 128 owns the 8 x 8
-// block kb = lt % 8 (k), rb = lt / 8 (rows).  Element (kk, row) of the tile is
-// at base + kk * ld + row; `col` is this thread's row offset for its block.
-__device__ __forceinline__ void nc_load(uint4 (&r)[8], const bf16_t* __restrict__ base, int64_t ld,
-                                        int64_t col, int k_valid, int lt) {
-  const int kb = lt & 7;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int kk = kb * 8 + i;
-    r[i] = kk < k_valid ? *reinterpret_cast<const uint4*>(base + kk * ld + col)
-                        : make_uint4(0u, 0u, 0u, 0u);
-  }
-}
-
-__device__ __forceinline__ uint32_t wsel(const uint4& v, int w) {
-  return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
-}
-
-__device__ __forceinline__ void nc_store(bf16_t* __restrict__ lds, const uint4 (&r)[8], int lt) {
-  const int kb = lt & 7, rb = lt >> 3;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    uint32_t o[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t lo = wsel(r[2 * p], q >> 1), hi = wsel(r[2 * p + 1], q >> 1);
-      o[p] = (q & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-    }
-    *reinterpret_cast<uint4*>(lds + (rb * 8 + q) * LP + kb * 8) = make_uint4(o[0], o[1], o[2], o[3]);
-  }
-}
-
-// ---- MFMA on one staged k step ---------------------------------------------
-
-__device__ __forceinline__ void mma_step(f32x16_t (&acc)[2][2], const bf16_t* __restrict__ As,
-                                         const bf16_t* __restrict__ Bs, int wm, int wn, int lane) {
-  const int r = lane & 31, kq = (lane >> 5) * 8;
-#pragma unroll
-  for (int kk = 0; kk < BK; kk += 16) {
-    bf16x8_t a[2], b[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      a[i] = *reinterpret_cast<const bf16x8_t*>(As + (wm * 64 + i * 32 + r) * LP + kk + kq);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      b[j] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * 64 + j * 32 + r) * LP + kk + kq);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-  }
-}
-
-// row (within the 128 x 128 tile) of accumulator element v of block (i, .)
-__device__ __forceinline__ int acc_row(int wm, int i, int v, int lane) {
-  return wm * 64 + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ int virtual_block() {
@@ -145,311 +119,523 @@ __device__ __forceinline__ int virtual_block() {
   return (P % 8 == 0) ? (b % 8) * (P / 8) + b / 8 : b;
 }
 
-// ---- row-grouped products: forward and dgrad ---------------------------------
-//
-// MODE_FWD*:   A [M, Kc] (lda = Kc); B_g = B + g * Kc * N, element (k, n) at k * N + n.
-//              NONE: tile columns nt * 128 + c of C [M, N].
-//              SWIGLU: N = 2f; tile = 64 h columns; B rows of the tile are
-//              [gate 0..31 | up 0..31] for wave column 0 then for wave column 1.
-// MODE_DGRAD*: A = dC [M, Kc] (Kc = N); B_g = B + g * Nout * Kc, element (k, n)
-//              at n * Kc + k; product columns Nout = K.
+struct Params {
+  const bf16_t* A;
+  const bf16_t* B;
+  const int64_t* off;
+  int G;
+  int64_t M;
+  int64_t Kc;    // contraction length (row groups) / K of dB (wgrad)
+  int64_t Nout;  // product columns (row groups) / N of dB (wgrad)
+  void* C;       // C, dA or dAB, or dB
+  bf16_t* H;
+  const bf16_t* ab;
+  int out_f32;
+  int accumulate;
+};
+
+// What a tile is: a ragged row block x 128 columns of one group (forward,
+// dgrad), or a 128 x 128 block of one group's weight gradient (wgrad).
+struct Tile {
+  int g;
+  int64_t row0;   // first output row (row groups) or first dB row (wgrad)
+  int rows;       // valid output rows (row groups)
+  int64_t nt;     // column tile
+  int64_t lo;     // wgrad: first contraction row of the group
+  int64_t nrows;  // wgrad: contraction rows of the group
+  int nk;         // k steps (>= 1)
+};
+
 template <int MODE>
-__global__ __launch_bounds__(256) void gg_bf16_rows_kernel(const bf16_t* __restrict__ A,
-                                                           const bf16_t* __restrict__ B,
-                                                           const int64_t* __restrict__ off, int G,
-                                                           int64_t M, int64_t Kc, int64_t Nout,
-                                                           bf16_t* __restrict__ C,
-                                                           bf16_t* __restrict__ H,
-                                                           const bf16_t* __restrict__ ab) {
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * LP];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * LP];
-  __shared__ int s_pre[MAX_GROUPS + 1];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  constexpr bool FWD = MODE == MODE_FWD || MODE == MODE_FWD_SWIGLU;
-  constexpr bool SWI = MODE == MODE_FWD_SWIGLU;
-
-  // row-tile prefix over groups, built by wave 0
-  if (wave == 0) {
-    const int per = (G + 63) / 64;
-    const int g0 = lane * per, g1 = min(G, g0 + per);
-    int sum = 0;
-    for (int g = g0; g < g1; ++g) {
-      const int64_t lo = clamp64(off[g], 0, M), hi = clamp64(off[g + 1], lo, M);
-      sum += static_cast<int>((hi - lo + BM - 1) / BM);
-    }
-    int incl = sum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += y;
-    }
-    int run = incl - sum;
-    for (int g = g0; g < g1; ++g) {
-      s_pre[g] = run;
-      const int64_t lo = clamp64(off[g], 0, M), hi = clamp64(off[g + 1], lo, M);
-      run += static_cast<int>((hi - lo + BM - 1) / BM);
-    }
-    if (lane == 63) s_pre[G] = incl;
-  }
-  __syncthreads();
-
-  const int64_t NT = SWI ? Nout / 128 : Nout / BN;  // SWIGLU: Nout = 2f, 64 h columns per tile
-  const int64_t fh = Nout / 2;
-  const int64_t total = static_cast<int64_t>(s_pre[G]) * NT;
-  const int P = gridDim.x;
-  const int nk = static_cast<int>(Kc / BK);
-  const int lt = tid & 127;
-  const bool b_loader = !FWD || tid < 128;
-
-  for (int64_t tau = virtual_block(); tau < total; tau += P) {
+__device__ __forceinline__ bool decode(int64_t tau, const Params& p, const int* s_pre,
+                                       const int64_t* s_off, int64_t NT, int64_t total, Tile& t) {
+  if (tau >= total) return false;
+  if (MODE == WGRAD) {
+    const int64_t MT = p.Kc / BM;
+    t.g = static_cast<int>(tau / (MT * NT));
+    const int64_t rem = tau % (MT * NT);
+    t.row0 = (rem / NT) * BM;
+    t.nt = rem % NT;
+    t.rows = BM;
+    t.lo = s_off[t.g];
+    t.nrows = s_off[t.g + 1] - t.lo;
+    t.nk = t.nrows > 0 ? static_cast<int>((t.nrows + BK - 1) / BK) : 1;
+  } else {
     const int mtg = static_cast<int>(tau / NT);
-    const int64_t nt = tau % NT;
-    int glo = 0, ghi = G;
+    t.nt = tau % NT;
+    int glo = 0, ghi = p.G;
     while (ghi - glo > 1) {
       const int mid = (glo + ghi) >> 1;
       if (s_pre[mid] <= mtg) glo = mid; else ghi = mid;
     }
-    const int g = glo;
-    const int64_t lo = clamp64(off[g], 0, M), hi = clamp64(off[g + 1], lo, M);
-    const int64_t row0 = lo + static_cast<int64_t>(mtg - s_pre[g]) * BM;
-    const int rows = static_cast<int>(min<int64_t>(BM, hi - row0));
+    const int g = __builtin_amdgcn_readfirstlane(glo);
+    t.g = g;
+    const int64_t lo = s_off[g], hi = s_off[g + 1];
+    t.row0 = lo + static_cast<int64_t>(mtg - s_pre[g]) * BM;
+    t.rows = static_cast<int>(min<int64_t>(BM, hi - t.row0));
+    t.nk = static_cast<int>(p.Kc / BK);
+    t.lo = lo;
+    t.nrows = hi - lo;
+  }
+  return true;
+}
 
-    const bf16_t* Ab = A + row0 * Kc;
-    const bf16_t* Bb;
-    int64_t bcol = 0;
-    if (FWD) {
-      Bb = B + static_cast<int64_t>(g) * Kc * Nout;
-      const int rb = lt >> 3;
-      if (SWI)
-        bcol = ((rb >> 2) & 1) * fh + nt * 64 + (rb >> 3) * 32 + (rb & 3) * 8;
+// Loader state of one tile: buffer resources and this lane's byte offsets
+// for its 4 A and 4 B DMA instructions at k step 0, plus per-step deltas.
+struct Loader {
+  i32x4_t ra, rb;
+  uint32_t va[4], vb[4];
+  uint32_t da, db;
+};
+
+template <int MODE>
+__device__ __forceinline__ void setup_loader(const Params& p, const Tile& t, int wave, int lane,
+                                             Loader& L) {
+  const int64_t fh = p.Nout / 2;
+  if (MODE == WGRAD) {
+    // A = X [M, Kc] rows of the group, [k][row] layout; B = dC [M, Nout] likewise
+    const int64_t K = p.Kc, N = p.Nout;
+    L.ra = make_rsrc(p.A + t.lo * K, static_cast<uint64_t>(t.nrows) * K * 2);
+    L.rb = make_rsrc(p.B + t.lo * N, static_cast<uint64_t>(t.nrows) * N * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = wave * 4 + i;
+      const int kr = 4 * q + (lane >> 4), c = (lane & 15) ^ swz_nc(kr);
+      L.va[i] = static_cast<uint32_t>(kr * K * 2 + (t.row0 + 8 * c) * 2);
+      L.vb[i] = static_cast<uint32_t>(kr * N * 2 + (t.nt * BN + 8 * c) * 2);
+    }
+    L.da = static_cast<uint32_t>(BK * K * 2);
+    L.db = static_cast<uint32_t>(BK * N * 2);
+    return;
+  }
+  // A: k-contiguous rows of the tile, [row][k] layout
+  const int64_t Kc = p.Kc;
+  L.ra = make_rsrc(p.A + t.row0 * Kc, static_cast<uint64_t>(t.rows) * Kc * 2);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = wave * 4 + i;
+    const int r = 8 * q + (lane >> 3), c = (lane & 7) ^ swz_kc(r);
+    L.va[i] = static_cast<uint32_t>(r * Kc * 2 + c * 16);
+  }
+  L.da = BK * 2;
+  if (MODE == FWD || MODE == FWD_SWIGLU) {
+    // B = W_g [Kc, Nout], [k][col] layout
+    const int64_t N = p.Nout;
+    L.rb = make_rsrc(p.B + static_cast<int64_t>(t.g) * Kc * N, static_cast<uint64_t>(Kc) * N * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = wave * 4 + i;
+      const int kr = 4 * q + (lane >> 4), c = (lane & 15) ^ swz_nc(kr);
+      int64_t col;
+      if (MODE == FWD_SWIGLU)  // tile column 8c: wave column c / 8, gate/up (c / 4) % 2
+        col = ((c >> 2) & 1) * fh + t.nt * 64 + (c >> 3) * 32 + (c & 3) * 8;
       else
-        bcol = nt * BN + rb * 8;
-    } else {
-      Bb = B + static_cast<int64_t>(g) * Nout * Kc + nt * BN * Kc;
+        col = t.nt * BN + 8 * c;
+      L.vb[i] = static_cast<uint32_t>(kr * N * 2 + col * 2);
     }
-
-    f32x16_t acc[2][2];
+    L.db = static_cast<uint32_t>(BK * N * 2);
+  } else {
+    // B = W_g [Nout, Kc] rows nt*128.., [row][k] layout
+    L.rb = make_rsrc(p.B + (static_cast<int64_t>(t.g) * p.Nout + t.nt * BN) * Kc,
+                     static_cast<uint64_t>(BN) * Kc * 2);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-    uint4 ra[4], rbk[4], rbn[8];
-    kc_load(ra, Ab, Kc, rows, tid);
-    if (FWD) {
-      if (b_loader) nc_load(rbn, Bb, Nout, bcol, BK, lt);
-    } else {
-      kc_load(rbk, Bb, Kc, BN, tid);
+    for (int i = 0; i < 4; ++i) {
+      const int q = wave * 4 + i;
+      const int r = 8 * q + (lane >> 3), c = (lane & 7) ^ swz_kc(r);
+      L.vb[i] = static_cast<uint32_t>(r * Kc * 2 + c * 16);
     }
-    kc_store(sA[0], ra, tid);
-    if (FWD) {
-      if (b_loader) nc_store(sB[0], rbn, lt);
-    } else {
-      kc_store(sB[0], rbk, tid);
-    }
-    __syncthreads();
+    L.db = BK * 2;
+  }
+}
 
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      const bool more = kt + 1 < nk;
-      if (more) {
-        const int64_t k0 = static_cast<int64_t>(kt + 1) * BK;
-        kc_load(ra, Ab + k0, Kc, rows, tid);
-        if (FWD) {
-          if (b_loader) nc_load(rbn, Bb + k0 * Nout, Nout, bcol, BK, lt);
-        } else {
-          kc_load(rbk, Bb + k0, Kc, BN, tid);
-        }
+__device__ __forceinline__ void issue(const Loader& L, int kt, LDS_AS char* stage, int wave) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    dma16(L.ra, stage + (wave * 4 + i) * 1024, L.va[i] + kt * L.da);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    dma16(L.rb, stage + OP_BYTES + (wave * 4 + i) * 1024, L.vb[i] + kt * L.db);
+}
+
+// ---- fragment reads ----------------------------------------------------------
+
+// [row][k] layout: 8 k values of row r, chunk c
+__device__ __forceinline__ bf16x8_t frag_kc(const LDS_AS char* op, int r, int c) {
+  return *(const LDS_AS bf16x8_t*)(op + r * 128 + ((c ^ swz_kc(r)) << 4));
+}
+
+// [k][col] layout: 8 k values (k0 .. k0+7 of this lane's half) of one column,
+// with two transpose reads of 4 k x 16 columns each
+__device__ __forceinline__ bf16x8_t frag_nc(const LDS_AS char* op, int col_base, int k_base,
+                                            int lane) {
+  const int i = lane & 15;
+  const int col = col_base + ((lane >> 4) & 1) * 16 + 4 * (i & 3);
+  const int k0 = k_base + (lane >> 5) * 8 + (i >> 2);
+  const int cc = col >> 3, half = ((col >> 2) & 1) * 8;
+  const LDS_AS char* p0 = op + k0 * 256 + ((cc ^ swz_nc(k0)) << 4) + half;
+  const LDS_AS char* p1 = op + (k0 + 4) * 256 + ((cc ^ swz_nc(k0 + 4)) << 4) + half;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)p0);
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)p1);
+  const i16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+template <int MODE>
+__device__ __forceinline__ void compute_stage(f32x16_t (&acc)[2][2], const LDS_AS char* stage,
+                                              int wm, int wn, int lane) {
+  constexpr bool A_NC = MODE == WGRAD;
+  constexpr bool B_NC = MODE == FWD || MODE == FWD_SWIGLU || MODE == WGRAD;
+  const LDS_AS char* opA = stage;
+  const LDS_AS char* opB = stage + OP_BYTES;
+#pragma unroll
+  for (int kk = 0; kk < BK / 16; ++kk) {
+    bf16x8_t a[2], b[2];
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+      a[ii] = A_NC ? frag_nc(opA, wm * 64 + ii * 32, kk * 16, lane)
+                   : frag_kc(opA, wm * 64 + ii * 32 + (lane & 31), kk * 2 + (lane >> 5));
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+      b[jj] = B_NC ? frag_nc(opB, wn * 64 + jj * 32, kk * 16, lane)
+                   : frag_kc(opB, wn * 64 + jj * 32 + (lane & 31), kk * 2 + (lane >> 5));
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        acc[ii][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[jj], a[ii], acc[ii][jj], 0, 0, 0);
+  }
+}
+
+// ---- epilogue ------------------------------------------------------------------
+// acc[ii][jj][v] = C[m][n], m = wm*64 + ii*32 + (lane & 31),
+//                          n = wn*64 + jj*32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3).
+// Staging per wave: [64 m][64 n] bf16 (128 B rows, chunks swizzled by m & 7).
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+
+__device__ __forceinline__ int stg_off(int m, int chunk) { return m * 128 + ((chunk ^ (m & 7)) << 4); }
+
+// write the wave's acc (columns [jj0, jj0 + njj) blocks) into staging as bf16
+__device__ __forceinline__ void stage_acc(LDS_AS char* stg, const f32x16_t (&acc)[2][2], int lane) {
+#pragma unroll
+  for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int vg = 0; vg < 4; ++vg) {
+        const int m = ii * 32 + (lane & 31);
+        const int n = jj * 32 + vg * 8 + (lane >> 5) * 4;
+        u32x2_t w;
+        w.x = pack2(acc[ii][jj][vg * 4 + 0], acc[ii][jj][vg * 4 + 1]);
+        w.y = pack2(acc[ii][jj][vg * 4 + 2], acc[ii][jj][vg * 4 + 3]);
+        *(LDS_AS u32x2_t*)(stg + stg_off(m, n >> 3) + (n & 7) * 2) = w;
       }
-      mma_step(acc, sA[cur], sB[cur], wm, wn, lane);
-      if (more) {
-        kc_store(sA[cur ^ 1], ra, tid);
-        if (FWD) {
-          if (b_loader) nc_store(sB[cur ^ 1], rbn, lt);
-        } else {
-          kc_store(sB[cur ^ 1], rbk, tid);
-        }
-      }
-      __syncthreads();
-    }
+}
 
-    // epilogue
+__device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
+  return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
+}
+
+template <int MODE>
+__device__ __forceinline__ void epilogue(const Params& p, const Tile& t, const f32x16_t (&acc)[2][2],
+                                         LDS_AS char* stg, int wm, int wn, int lane) {
+  const int rows_w = MODE == WGRAD ? 64 : t.rows - wm * 64;  // valid rows of this wave
+  if (rows_w <= 0) return;
+  if (MODE == WGRAD && p.out_f32) {
+    // direct 16-byte stores of 4 consecutive fp32 columns
+    float* out = static_cast<float*>(p.C) + static_cast<int64_t>(t.g) * p.Kc * p.Nout;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int rl = acc_row(wm, i, v, lane);
-        if (rl >= rows) continue;
-        const int64_t row = row0 + rl;
-        if (SWI) {
-          const int64_t hc = nt * 64 + wn * 32 + (lane & 31);
-          const float a = acc[i][0][v], b = acc[i][1][v];
-          if (C) {
-            C[row * Nout + hc] = f32_to_bf16(a);
-            C[row * Nout + fh + hc] = f32_to_bf16(b);
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int vg = 0; vg < 4; ++vg) {
+          const int64_t m = t.row0 + wm * 64 + ii * 32 + (lane & 31);
+          const int64_t n = t.nt * BN + wn * 64 + jj * 32 + vg * 8 + (lane >> 5) * 4;
+          float4* q = reinterpret_cast<float4*>(out + m * p.Nout + n);
+          float4 v = make_float4(acc[ii][jj][vg * 4], acc[ii][jj][vg * 4 + 1],
+                                 acc[ii][jj][vg * 4 + 2], acc[ii][jj][vg * 4 + 3]);
+          if (p.accumulate) {
+            const float4 o = *q;
+            v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
           }
-          H[row * fh + hc] = f32_to_bf16(a / (1.0f + expf(-a)) * b);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int64_t col = nt * BN + wn * 64 + j * 32 + (lane & 31);
-            const float x = acc[i][j][v];
-            if (MODE == MODE_DGRAD_SWIGLU_BWD) {
-              const float a = bf16_to_f32(ab[row * 2 * Nout + col]);
-              const float b = bf16_to_f32(ab[row * 2 * Nout + Nout + col]);
-              const float s = 1.0f / (1.0f + expf(-a));
-              C[row * 2 * Nout + col] = f32_to_bf16(x * b * s * (1.0f + a * (1.0f - s)));
-              C[row * 2 * Nout + Nout + col] = f32_to_bf16(x * a * s);
-            } else {
-              C[row * Nout + col] = f32_to_bf16(x);
-            }
-          }
+          *q = v;
         }
+    return;
+  }
+  stage_acc(stg, acc, lane);
+  const int64_t fh = p.Nout / 2;
+  // 64 rows x 8 chunks; lane handles chunks lane + 64 i
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int idx = lane + 64 * i;
+    const int m = idx >> 3, c = idx & 7;
+    if (m >= rows_w) continue;
+    const u32x4_t vv = *(const LDS_AS u32x4_t*)(stg + stg_off(m, c));
+    const uint4 v = make_uint4(vv.x, vv.y, vv.z, vv.w);
+    const int64_t row = t.row0 + wm * 64 + m;
+    if (MODE == FWD) {
+      bf16_t* C = static_cast<bf16_t*>(p.C);
+      *reinterpret_cast<uint4*>(C + row * p.Nout + t.nt * BN + wn * 64 + 8 * c) = v;
+    } else if (MODE == FWD_SWIGLU) {
+      if (p.C) {
+        bf16_t* C = static_cast<bf16_t*>(p.C);
+        const int64_t col = (c >> 2) * fh + t.nt * 64 + wn * 32 + (c & 3) * 8;
+        *reinterpret_cast<uint4*>(C + row * p.Nout + col) = v;
       }
+    } else if (MODE == DGRAD) {
+      bf16_t* C = static_cast<bf16_t*>(p.C);
+      *reinterpret_cast<uint4*>(C + row * p.Nout + t.nt * BN + wn * 64 + 8 * c) = v;
+    } else if (MODE == DGRAD_SWIGLU_BWD) {
+      // v = dH[row, col .. col+7]; read the matching a and b, write dA and dB
+      const int64_t col = t.nt * BN + wn * 64 + 8 * c;
+      const int64_t w2 = 2 * p.Nout;
+      float dh[8], a[8], b[8], da[8], db[8];
+      unpack8(v, dh);
+      unpack8(*reinterpret_cast<const uint4*>(p.ab + row * w2 + col), a);
+      unpack8(*reinterpret_cast<const uint4*>(p.ab + row * w2 + p.Nout + col), b);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float s = 1.0f / (1.0f + expf(-a[e]));
+        da[e] = dh[e] * b[e] * s * (1.0f + a[e] * (1.0f - s));
+        db[e] = dh[e] * a[e] * s;
+      }
+      bf16_t* C = static_cast<bf16_t*>(p.C);
+      *reinterpret_cast<uint4*>(C + row * w2 + col) = pack8(da);
+      *reinterpret_cast<uint4*>(C + row * w2 + p.Nout + col) = pack8(db);
+    } else {  // WGRAD, bf16 out
+      bf16_t* C = static_cast<bf16_t*>(p.C) + static_cast<int64_t>(t.g) * p.Kc * p.Nout;
+      uint4* q = reinterpret_cast<uint4*>(C + row * p.Nout + t.nt * BN + wn * 64 + 8 * c);
+      if (p.accumulate) {
+        float x[8], y[8];
+        unpack8(v, x);
+        unpack8(*q, y);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] += y[e];
+        *q = pack8(x);
+      } else {
+        *q = v;
+      }
+    }
+  }
+  if (MODE == FWD_SWIGLU) {
+    // second pass: H = silu(gate) * up, 32 columns per wave
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int vg = 0; vg < 4; ++vg) {
+        const int m = ii * 32 + (lane & 31);
+        const int n = vg * 8 + (lane >> 5) * 4;
+        float h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float g = acc[ii][0][vg * 4 + e], u = acc[ii][1][vg * 4 + e];
+          h[e] = g / (1.0f + expf(-g)) * u;
+        }
+        u32x2_t w;
+        w.x = pack2(h[0], h[1]);
+        w.y = pack2(h[2], h[3]);
+        *(LDS_AS u32x2_t*)(stg + stg_off(m, n >> 3) + (n & 7) * 2) = w;
+      }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = lane + 64 * i;
+      const int m = idx >> 2, c = idx & 3;
+      if (m >= rows_w) continue;
+      const u32x4_t vv = *(const LDS_AS u32x4_t*)(stg + stg_off(m, c));
+      const uint4 v = make_uint4(vv.x, vv.y, vv.z, vv.w);
+      const int64_t row = t.row0 + wm * 64 + m;
+      *reinterpret_cast<uint4*>(p.H + row * fh + t.nt * 64 + wn * 32 + 8 * c) = v;
     }
   }
 }
 
-// ---- wgrad: dB[g] = A[rows g]^T . dC[rows g] ---------------------------------
-// Output tile (mt, nt) of group g; contraction over the group's rows in steps
-// of 64 (the last one zero-padded).  Threads 0..127 stage A, 128..255 stage dC.
-template <bool OUT_F32>
-__global__ __launch_bounds__(256) void gg_bf16_wgrad_kernel(const bf16_t* __restrict__ A,
-                                                            const bf16_t* __restrict__ dC,
-                                                            const int64_t* __restrict__ off, int G,
-                                                            int64_t M, int64_t K, int64_t N,
-                                                            void* __restrict__ dB, int accumulate) {
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * LP];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * LP];
+// ---- the kernel ----------------------------------------------------------------
+
+template <int MODE>
+__global__ __launch_bounds__(256, 1) void gg_bf16_kernel(Params p) {
+  __shared__ __attribute__((aligned(1024))) char ring[STAGES * STAGE_BYTES];
+  __shared__ int s_pre[MAX_GROUPS + 1];
+  __shared__ int64_t s_off[MAX_GROUPS + 1];
+  LDS_AS char* lring = (LDS_AS char*)(ring);
+
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int lt = tid & 127;
-  const bool loads_a = tid < 128;
-  const int64_t MT = K / BM, NT = N / BN;
-  const int64_t total = static_cast<int64_t>(G) * MT * NT;
-  const int P = gridDim.x;
 
-  for (int64_t tau = virtual_block(); tau < total; tau += P) {
-    const int g = static_cast<int>(tau / (MT * NT));
-    const int64_t rem = tau % (MT * NT);
-    const int64_t mt = rem / NT, nt = rem % NT;
-    const int64_t lo = clamp64(off[g], 0, M), hi = clamp64(off[g + 1], lo, M);
-    const int64_t nrows = hi - lo;
-    const int nk = static_cast<int>((nrows + BK - 1) / BK);
-    const int rb = lt >> 3;
-    const bf16_t* base = loads_a ? A + lo * K + mt * BM : dC + lo * N + nt * BN;
-    const int64_t ld = loads_a ? K : N;
-    bf16_t(*sX)[BM * LP] = loads_a ? sA : sB;
-
-    f32x16_t acc[2][2];
+  // group offsets, clamped to a non-decreasing sequence in [0, M], kept in LDS
+  // so that tile decoding never waits on vector memory
+  for (int g = tid; g <= p.G; g += 256) s_off[g] = clamp64(p.off[g], 0, p.M);
+  __syncthreads();
+  if (wave == 0) {  // running maximum makes the offsets non-decreasing
+    const int per = (p.G + 1 + 63) / 64;
+    const int g0 = lane * per, g1 = min(p.G + 1, g0 + per);
+    int64_t mx = 0;
+    for (int g = g0; g < g1; ++g) mx = max(mx, s_off[g]);
+    int64_t incl = mx;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-    if (nk > 0) {
-      uint4 r[8];
-      nc_load(r, base, ld, rb * 8, static_cast<int>(min<int64_t>(BK, nrows)), lt);
-      nc_store(sX[0], r, lt);
-      __syncthreads();
-      for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) {
-          const int64_t k0 = static_cast<int64_t>(kt + 1) * BK;
-          nc_load(r, base + k0 * ld, ld, rb * 8, static_cast<int>(min<int64_t>(BK, nrows - k0)), lt);
-        }
-        mma_step(acc, sA[cur], sB[cur], wm, wn, lane);
-        if (more) nc_store(sX[cur ^ 1], r, lt);
-        __syncthreads();
-      }
-    } else if (accumulate) {
-      continue;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl = max(incl, y);
     }
-
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = mt * BM + acc_row(wm, i, v, lane);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int64_t col = nt * BN + wn * 64 + j * 32 + (lane & 31);
-          const int64_t o = static_cast<int64_t>(g) * K * N + row * N + col;
-          float x = acc[i][j][v];
-          if (OUT_F32) {
-            float* p = static_cast<float*>(dB) + o;
-            if (accumulate) x += *p;
-            *p = x;
-          } else {
-            bf16_t* p = static_cast<bf16_t*>(dB) + o;
-            if (accumulate) x += bf16_to_f32(*p);
-            *p = f32_to_bf16(x);
-          }
-        }
-      }
+    int64_t run = incl;
+    run = __shfl_up(incl, 1, 64);
+    if (lane == 0) run = 0;
+    for (int g = g0; g < g1; ++g) {
+      run = max(run, s_off[g]);
+      s_off[g] = run;
     }
   }
+  __syncthreads();
+
+  int64_t NT, total;
+  if (MODE == WGRAD) {
+    NT = p.Nout / BN;
+    total = static_cast<int64_t>(p.G) * (p.Kc / BM) * NT;
+  } else {
+    if (wave == 0) {
+      const int per = (p.G + 63) / 64;
+      const int g0 = lane * per, g1 = min(p.G, g0 + per);
+      int sum = 0;
+      for (int g = g0; g < g1; ++g) sum += static_cast<int>((s_off[g + 1] - s_off[g] + BM - 1) / BM);
+      int incl = sum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      int run = incl - sum;
+      for (int g = g0; g < g1; ++g) {
+        s_pre[g] = run;
+        run += static_cast<int>((s_off[g + 1] - s_off[g] + BM - 1) / BM);
+      }
+      if (lane == 63) s_pre[p.G] = incl;
+    }
+    __syncthreads();
+    NT = MODE == FWD_SWIGLU ? p.Nout / 128 : p.Nout / BN;
+    total = static_cast<int64_t>(s_pre[p.G]) * NT;
+  }
+
+  const int P = gridDim.x;
+  int64_t ld_tau = virtual_block(), cp_tau = ld_tau;
+  Tile ld_t, cp_t;
+  bool ld_ok = decode<MODE>(ld_tau, p, s_pre, s_off, NT, total, ld_t);
+  bool cp_ok = ld_ok;
+  cp_t = ld_t;
+  Loader L;
+  if (ld_ok) setup_loader<MODE>(p, ld_t, wave, lane, L);
+  int ld_kt = 0, cp_kt = 0;
+  int inflight = 0, ld_slot = 0, cp_slot = 0;
+
+  // prologue: STAGES - 1 steps in flight
+  for (int s = 0; s < STAGES - 1 && ld_ok; ++s) {
+    issue(L, ld_kt, lring + ld_slot * STAGE_BYTES, wave);
+    ++inflight;
+    ld_slot = ld_slot + 1 == STAGES ? 0 : ld_slot + 1;
+    if (++ld_kt == ld_t.nk) {
+      ld_kt = 0;
+      ld_tau += P;
+      ld_ok = decode<MODE>(ld_tau, p, s_pre, s_off, NT, total, ld_t);
+      if (ld_ok) setup_loader<MODE>(p, ld_t, wave, lane, L);
+    }
+  }
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[ii][jj][v] = 0.f;
+
+  while (cp_ok) {
+    wait_barrier(inflight - 1);  // this step's stage has landed in LDS for all waves
+    if (ld_ok) {                 // refill the slot consumed in the previous step
+      issue(L, ld_kt, lring + ld_slot * STAGE_BYTES, wave);
+      ++inflight;
+      ld_slot = ld_slot + 1 == STAGES ? 0 : ld_slot + 1;
+      if (++ld_kt == ld_t.nk) {
+        ld_kt = 0;
+        ld_tau += P;
+        ld_ok = decode<MODE>(ld_tau, p, s_pre, s_off, NT, total, ld_t);
+        if (ld_ok) setup_loader<MODE>(p, ld_t, wave, lane, L);
+      }
+    }
+    compute_stage<MODE>(acc, lring + cp_slot * STAGE_BYTES, wm, wn, lane);
+    --inflight;
+    if (++cp_kt == cp_t.nk) {
+      // the slot just consumed is not refilled before the next barrier: stage
+      // there, once every wave has finished reading its fragments from it
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      epilogue<MODE>(p, cp_t, acc, lring + cp_slot * STAGE_BYTES + wave * 8192, wm, wn, lane);
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[ii][jj][v] = 0.f;
+      cp_kt = 0;
+      cp_tau += P;
+      cp_ok = decode<MODE>(cp_tau, p, s_pre, s_off, NT, total, cp_t);
+    }
+    cp_slot = cp_slot + 1 == STAGES ? 0 : cp_slot + 1;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 static unsigned persistent_grid(int64_t tiles_upper_bound) {
-  int64_t p = static_cast<int64_t>(cu_count()) * 2;
+  int64_t p = cu_count();
   if (tiles_upper_bound < p) p = tiles_upper_bound;
   if (p < 1) p = 1;
   return static_cast<unsigned>(p);
 }
 
+template <int MODE>
+static hipError_t run(const Params& p, int64_t tiles_upper_bound, hipStream_t s) {
+  if (tiles_upper_bound <= 0) return hipSuccess;
+  gg_bf16_kernel<MODE><<<dim3(persistent_grid(tiles_upper_bound)), 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
 hipError_t launch_gg_bf16_fwd(const void* A, const void* B, const int64_t* off, int G, int64_t M,
                               int64_t K, int64_t N, int epi, void* C, void* H, hipStream_t s) {
   if (M == 0) return hipSuccess;
+  Params p{static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(B), off, G, M, K, N, C,
+           static_cast<bf16_t*>(H), nullptr, 0, 0};
   const int64_t nt = epi == EPI_SWIGLU ? N / 128 : N / BN;
-  const dim3 grid(persistent_grid((M / BM + G) * nt));
-  const bf16_t* a = static_cast<const bf16_t*>(A);
-  const bf16_t* b = static_cast<const bf16_t*>(B);
-  if (epi == EPI_SWIGLU)
-    gg_bf16_rows_kernel<MODE_FWD_SWIGLU><<<grid, 256, 0, s>>>(
-        a, b, off, G, M, K, N, static_cast<bf16_t*>(C), static_cast<bf16_t*>(H), nullptr);
-  else
-    gg_bf16_rows_kernel<MODE_FWD><<<grid, 256, 0, s>>>(a, b, off, G, M, K, N,
-                                                       static_cast<bf16_t*>(C), nullptr, nullptr);
-  return hipGetLastError();
+  if (epi == EPI_SWIGLU) return run<FWD_SWIGLU>(p, (M / BM + G) * nt, s);
+  return run<FWD>(p, (M / BM + G) * nt, s);
 }
 
 hipError_t launch_gg_bf16_dgrad(const void* dC, const void* B, const int64_t* off, int G,
                                 int64_t M, int64_t K, int64_t N, int epi, const void* ab, void* dA,
                                 hipStream_t s) {
   if (M == 0) return hipSuccess;
-  const dim3 grid(persistent_grid((M / BM + G) * (K / BN)));
-  const bf16_t* a = static_cast<const bf16_t*>(dC);
-  const bf16_t* b = static_cast<const bf16_t*>(B);
-  if (epi == EPI_SWIGLU_BWD)
-    gg_bf16_rows_kernel<MODE_DGRAD_SWIGLU_BWD><<<grid, 256, 0, s>>>(
-        a, b, off, G, M, N, K, static_cast<bf16_t*>(dA), nullptr, static_cast<const bf16_t*>(ab));
-  else
-    gg_bf16_rows_kernel<MODE_DGRAD><<<grid, 256, 0, s>>>(a, b, off, G, M, N, K,
-                                                         static_cast<bf16_t*>(dA), nullptr, nullptr);
-  return hipGetLastError();
+  // contraction over N, product columns K
+  Params p{static_cast<const bf16_t*>(dC), static_cast<const bf16_t*>(B), off, G, M, N, K, dA,
+           nullptr, static_cast<const bf16_t*>(ab), 0, 0};
+  if (epi == EPI_SWIGLU_BWD) return run<DGRAD_SWIGLU_BWD>(p, (M / BM + G) * (K / BN), s);
+  return run<DGRAD>(p, (M / BM + G) * (K / BN), s);
 }
 
 hipError_t launch_gg_bf16_wgrad(const void* A, const void* dC, const int64_t* off, int G,
                                 int64_t M, int64_t K, int64_t N, int db_f32, int accumulate,
                                 void* dB, hipStream_t s) {
-  const int64_t tiles = static_cast<int64_t>(G) * (K / BM) * (N / BN);
-  if (tiles == 0) return hipSuccess;
-  const dim3 grid(persistent_grid(tiles));
-  const bf16_t* a = static_cast<const bf16_t*>(A);
-  const bf16_t* c = static_cast<const bf16_t*>(dC);
-  if (db_f32)
-    gg_bf16_wgrad_kernel<true><<<grid, 256, 0, s>>>(a, c, off, G, M, K, N, dB, accumulate);
-  else
-    gg_bf16_wgrad_kernel<false><<<grid, 256, 0, s>>>(a, c, off, G, M, K, N, dB, accumulate);
-  return hipGetLastError();
+  Params p{static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(dC), off, G, M, K, N, dB,
+           nullptr, nullptr, db_f32, accumulate};
+  return run<WGRAD>(p, static_cast<int64_t>(G) * (K / BM) * (N / BN), s);
 }
 
 }  // namespace moe

@@ -200,6 +200,7 @@ GEMM_CASES = [
     (2600, 4, 128, 128, 0.0, 1.0),
     (129, 1, 256, 128, 0.0, 0.0),
     (0, 3, 128, 128, 0.0, 0.0),
+    (20000, 40, 256, 1024, 0.2, 1.0),   # many tiles per workgroup, skewed, empty groups
 ]
 
 
