@@ -38,23 +38,31 @@ def boundary_gaps(z, k):
     return s[:, k - 1] - s[:, k]
 
 
+def near_tie_tokens(z, k, rel_gap):
+    """Tokens whose selection or slot order an fp32 rounding difference could
+    change: two of the top k+1 keys (by the oracle) closer than
+    rel_gap * (1 + |key|)."""
+    s = -np.sort(-np.asarray(z, np.float64), axis=1)[:, :k + 1]
+    if s.shape[1] < 2:
+        return np.zeros(0, dtype=np.int64)
+    gaps = s[:, :-1] - s[:, 1:]
+    close = gaps < rel_gap * (1.0 + np.abs(s[:, :-1]))
+    return np.nonzero(close.any(axis=1))[0]
+
+
 def layer_inputs_without_near_ties(cfg, seed, device="cpu", rel_gap=1e-4, attempts=20):
     """Seeded layer inputs whose routing is not decided by fp32 rounding: a
-    token whose k-th and (k+1)-th keys (by the oracle) are closer than
+    token with two of its top k+1 keys (by the oracle) closer than
     rel_gap * (1 + |key|) gets a fresh x row, so the GPU's fp32 router (a
-    different summation order) must select the same experts."""
+    different summation order) must select the same experts in the same slot
+    order."""
     inp = inputs.layer_inputs(cfg, seed, device)
     bias = None if inp["logit_bias"] is None else inp["logit_bias"].cpu().numpy()
     w_r = inp["w_r"].cpu().numpy()
     for attempt in range(attempts):
         x = inp["x"].cpu()
         z = oracle.router_logits(np64(x), w_r, bias)
-        s = -np.sort(-z.astype(np.float64), axis=1)
-        if cfg.k < cfg.E:
-            gap = s[:, cfg.k - 1] - s[:, cfg.k]
-            bad = np.nonzero(gap < rel_gap * (1.0 + np.abs(s[:, cfg.k - 1])))[0]
-        else:
-            bad = []
+        bad = near_tie_tokens(z, cfg.k, rel_gap)
         if len(bad) == 0:
             return inp
         inputs.resample_rows(inp["x"], [int(t) for t in bad], seed, attempt)
