@@ -8,14 +8,15 @@
 //   wgrad    dB[g]      = A[rows g]^T . dC[rows g]
 //
 // Design for gfx950:
-//  * Persistent grid, one 256-thread workgroup per CU.  Each workgroup builds
+//  * Persistent grid, two 256-thread workgroups per CU (two waves per SIMD:
+//    one issues MFMAs while the other waits on LDS).  Each workgroup builds
 //    the per-group row-tile prefix from the device offsets in LDS (no host
 //    sync), then walks tiles tau = v, v + P, ...; the virtual id v gives the
 //    workgroups of one XCD (workgroup b runs on XCD b mod 8) consecutive tiles,
 //    so the N tiles of one expert row block share that XCD's L2.
 //  * Operands go HBM -> LDS directly (buffer_load ... lds, 16 bytes per lane),
-//    through a 4-stage ring of 32 KiB stages (128 x 64 of A and of B), three
-//    k steps in flight.  The ring runs across tile boundaries: the next tile's
+//    through a 2-stage ring of 32 KiB stages (128 x 64 of A and of B) per
+//    workgroup, so that two workgroups fit in the CU's 160 KiB of LDS.  The ring runs across tile boundaries: the next tile's
 //    first steps load during the current tile's epilogue.  Buffer resources
 //    bound every tile's rows, so rows past a group's end read as zero and
 //    nothing outside the operands is touched.
@@ -46,7 +47,7 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int STAGES = 4;
+constexpr int STAGES = 2;              // x 2 workgroups per CU
 constexpr int OP_BYTES = 16384;            // one operand of one stage
 constexpr int STAGE_BYTES = 2 * OP_BYTES;  // A then B
 constexpr int MAX_GROUPS = 1024;
@@ -74,7 +75,7 @@ __device__ __forceinline__ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) {
 
 // chunk swizzles: KC layout [row][8 chunks], NC layout [k][16 chunks]
 __device__ __forceinline__ int swz_kc(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-__device__ __forceinline__ int swz_nc(int kr) { return (kr & 3) << 1; }
+__device__ __forceinline__ int swz_nc(int kr) { return (kr & 3) << 2; }
 
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
@@ -96,9 +97,14 @@ __device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint64_t bytes) {
 __device__ __forceinline__ void dma16(i32x4_t rs, LDS_AS void* dst, uint32_t voff) {
   const int32_t m0 = __builtin_amdgcn_readfirstlane(
       static_cast<int32_t>(reinterpret_cast<uintptr_t>(dst)));
+  i32x4_t r;  // the descriptor must sit in scalar registers at the instruction
+  r.x = __builtin_amdgcn_readfirstlane(rs.x);
+  r.y = __builtin_amdgcn_readfirstlane(rs.y);
+  r.z = __builtin_amdgcn_readfirstlane(rs.z);
+  r.w = __builtin_amdgcn_readfirstlane(rs.w);
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "v"(voff), "s"(rs), "s"(m0)
+               : "v"(voff), "s"(r), "s"(m0)
                : "memory", "m0");
 }
 
@@ -146,32 +152,56 @@ struct Tile {
   int nk;         // k steps (>= 1)
 };
 
+// Order of a group's tiles: blocks of up to 4 row tiles; inside a block,
+// chunks of 8 column tiles, row-major inside a chunk.  Consecutive tiles,
+// which run on one XCD, then form a 4 x 8 patch that shares 4 row slabs of A
+// and 8 column slabs of B in that XCD's L2.
+__device__ __forceinline__ void tile_in_group(uint32_t tl, uint32_t mt_g, uint32_t NT, uint32_t& m,
+                                              uint32_t& n) {
+  constexpr uint32_t SM = 4, SN = 8;
+  const uint32_t blk = tl / (SM * NT);
+  const uint32_t r = tl - blk * SM * NT;
+  const uint32_t sm = min(SM, mt_g - blk * SM);
+  const uint32_t chunk = r / (sm * SN);
+  const uint32_t rr = r - chunk * sm * SN;
+  const uint32_t cw = min(SN, NT - chunk * SN);
+  m = blk * SM + rr / cw;
+  n = chunk * SN + rr % cw;
+}
+
 template <int MODE>
-__device__ __forceinline__ bool decode(int64_t tau, const Params& p, const int* s_pre,
-                                       const int64_t* s_off, int64_t NT, int64_t total, Tile& t) {
-  if (tau >= total) return false;
+__device__ __forceinline__ bool decode(int64_t tau64, const Params& p, const int* s_pre,
+                                       const int64_t* s_off, int64_t NT64, int64_t total, Tile& t) {
+  if (tau64 >= total) return false;
+  const uint32_t tau = static_cast<uint32_t>(tau64), NT = static_cast<uint32_t>(NT64);
   if (MODE == WGRAD) {
-    const int64_t MT = p.Kc / BM;
-    t.g = static_cast<int>(tau / (MT * NT));
-    const int64_t rem = tau % (MT * NT);
-    t.row0 = (rem / NT) * BM;
-    t.nt = rem % NT;
+    const uint32_t MT = static_cast<uint32_t>(p.Kc / BM);
+    const uint32_t per_g = MT * NT;
+    t.g = static_cast<int>(tau / per_g);
+    uint32_t m, n;
+    tile_in_group(tau - static_cast<uint32_t>(t.g) * per_g, MT, NT, m, n);
+    t.row0 = static_cast<int64_t>(m) * BM;
+    t.nt = n;
     t.rows = BM;
     t.lo = s_off[t.g];
     t.nrows = s_off[t.g + 1] - t.lo;
     t.nk = t.nrows > 0 ? static_cast<int>((t.nrows + BK - 1) / BK) : 1;
   } else {
-    const int mtg = static_cast<int>(tau / NT);
-    t.nt = tau % NT;
+    // group g owns tiles [s_pre[g] * NT, s_pre[g+1] * NT)
     int glo = 0, ghi = p.G;
     while (ghi - glo > 1) {
       const int mid = (glo + ghi) >> 1;
-      if (s_pre[mid] <= mtg) glo = mid; else ghi = mid;
+      if (static_cast<uint32_t>(s_pre[mid]) * NT <= tau) glo = mid; else ghi = mid;
     }
     const int g = __builtin_amdgcn_readfirstlane(glo);
     t.g = g;
+    const uint32_t base = static_cast<uint32_t>(s_pre[g]);
+    const uint32_t mt_g = static_cast<uint32_t>(s_pre[g + 1]) - base;
+    uint32_t m, n;
+    tile_in_group(tau - base * NT, mt_g, NT, m, n);
     const int64_t lo = s_off[g], hi = s_off[g + 1];
-    t.row0 = lo + static_cast<int64_t>(mtg - s_pre[g]) * BM;
+    t.row0 = lo + static_cast<int64_t>(m) * BM;
+    t.nt = n;
     t.rows = static_cast<int>(min<int64_t>(BM, hi - t.row0));
     t.nk = static_cast<int>(p.Kc / BK);
     t.lo = lo;
@@ -464,7 +494,7 @@ __device__ __forceinline__ void epilogue(const Params& p, const Tile& t, const f
 // ---- the kernel ----------------------------------------------------------------
 
 template <int MODE>
-__global__ __launch_bounds__(256, 1) void gg_bf16_kernel(Params p) {
+__global__ __launch_bounds__(256, 2) void gg_bf16_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) char ring[STAGES * STAGE_BYTES];
   __shared__ int s_pre[MAX_GROUPS + 1];
   __shared__ int64_t s_off[MAX_GROUPS + 1];
@@ -596,7 +626,7 @@ __global__ __launch_bounds__(256, 1) void gg_bf16_kernel(Params p) {
 }
 
 static unsigned persistent_grid(int64_t tiles_upper_bound) {
-  int64_t p = cu_count();
+  int64_t p = static_cast<int64_t>(cu_count()) * 2;  // two resident workgroups per CU
   if (tiles_upper_bound < p) p = tiles_upper_bound;
   if (p < 1) p = 1;
   return static_cast<unsigned>(p);
