@@ -51,7 +51,7 @@ typedef enum {
   MOE_ERR_HIP = -6          /* a HIP runtime call or launch failed */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;  /* fp8 codes are uint8_t arrays */
 typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score;
 typedef enum {
   MOE_EPI_NONE = 0,
@@ -189,6 +189,73 @@ int moe_swiglu(const void* ab, int dtype, int64_t M, int64_t f, void* h, void* s
  * (formulas as in MOE_EPI_SWIGLU_BWD). */
 int moe_swiglu_bwd(const void* dh, const void* ab, int dtype, int64_t M, int64_t f, void* dab,
                    void* stream);
+
+/* ------------------------------------------------------- FP8 (E4M3) -- */
+/* Blockwise FP8 ("Scalable Training of Mixture-of-Experts Models with Megatron
+ * Core", section 5, Platform-specific recipes): 1 x 128 tiles for activations
+ * and gradients, 128 x 128 blocks for weights, fp32 scales.  Codes are OCP
+ * E4M3 (bias 7, no infinities, largest finite 448).  Per block:
+ *   amax = max |v|,  scale = amax / 448,  inv = 448 / amax   (one IEEE fp32
+ *   division each; scale = inv = 1 when amax = 0),
+ *   code = nearest E4M3 value of fp32(v * inv), ties to the even code,
+ *   saturated to +-448;  value = decode(code) * scale.
+ * The weight gradients contract over tokens, so their operands use 128-token
+ * x 1 tiles, each group's rows zero-padded to a multiple of 128.  Layouts are
+ * those the fp8 grouped GEMM reads (every operand k-contiguous, every scale a
+ * contiguous vector over a 128-row tile).  All inputs are bf16.
+ * Limits: K and N multiples of 128 wherever they are blocked. */
+
+/* 1 x 128 tiles along rows: q [M, K] codes, scale_t [K/128, M] (block-major). */
+int moe_quant_fp8_rows(const void* x, int64_t M, int64_t K, uint8_t* q, float* scale_t,
+                       void* stream);
+
+/* 128 x 128 blocks of w [G, K, N], written in both GEMM operand layouts from
+ * the same block scale s[g][kb][nb]:
+ *   q_fwd [G, N, K] (transposed) with s_fwd [G, K/128, N] = s[g][kb][n / 128]
+ *   q_dgrad [G, K, N]           with s_dgrad [G, N/128, K] = s[g][k / 128][nb] */
+int moe_quant_fp8_weights(const void* w, int32_t G, int64_t K, int64_t N, uint8_t* q_fwd,
+                          float* s_fwd, uint8_t* q_dgrad, float* s_dgrad, void* stream);
+
+/* Host helper: rows a padded layout of M rows in G groups can need,
+ * M + G * (align - 1) rounded up to align (the row length `ldm` of the
+ * token-tile operands). */
+int64_t moe_padded_rows_bound(int64_t M, int32_t G, int32_t align);
+
+/* padded [G+1] (device): padded[0] = 0, padded[g+1] = padded[g] +
+ * round_up(offsets[g+1] - offsets[g], align).  1 <= G <= 1024. */
+int moe_padded_offsets(const int64_t* offsets, int32_t G, int64_t M, int32_t align,
+                       int64_t* padded, void* stream);
+
+/* 128-token x 1 tiles of x [M, K]: group g's rows offsets[g].. land at padded
+ * rows padded[g].. (zero codes past the group's end); written transposed,
+ * q_t [K, ldm] (row c holds column c's codes), scale [ldm/128, K].
+ * ldm = moe_padded_rows_bound(M, G, 128) or larger, a multiple of 128. */
+int moe_quant_fp8_token_tiles(const void* x, const int64_t* offsets, const int64_t* padded,
+                              int32_t G, int64_t M, int64_t K, int64_t ldm, uint8_t* q_t,
+                              float* scale, void* stream);
+
+/* fp8 grouped GEMMs, fp32 accumulation, each 128-wide k block promoted with
+ * its two scales; outputs bf16 (dB: bf16 or fp32).  Groups as in the bf16
+ * calls.  Epilogues as in the bf16 calls.
+ *   forward: C[rows g] = deq(A)[rows g] . deq(B_g)   A [M, K] + scale_t [K/128, M]
+ *            from moe_quant_fp8_rows; B from moe_quant_fp8_weights (q_fwd, s_fwd)
+ *   dgrad:   dA[rows g] = deq(dC)[rows g] . deq(B_g)^T   dC [M, N] + scale_t
+ *            [N/128, M]; B (q_dgrad, s_dgrad)
+ *   wgrad:   dB[g] = deq(A)^T . deq(dC) over group g's padded rows; A_t [K, ldm],
+ *            dC_t [N, ldm] and scales from moe_quant_fp8_token_tiles
+ * Limits: K % 128 == 0, N % 128 == 0 (forward SWIGLU: N / 2 % 64 == 0). */
+int moe_grouped_gemm_fp8_fwd(const uint8_t* A, const float* a_scale_t, const uint8_t* B_fwd,
+                             const float* b_scale_fwd, const int64_t* offsets, int32_t G,
+                             int64_t M, int64_t K, int64_t N, int epilogue, void* C, void* H,
+                             void* stream);
+int moe_grouped_gemm_fp8_dgrad(const uint8_t* dC, const float* dc_scale_t, const uint8_t* B_dgrad,
+                               const float* b_scale_dgrad, const int64_t* offsets, int32_t G,
+                               int64_t M, int64_t K, int64_t N, int epilogue, const void* ab,
+                               void* dA, void* stream);
+int moe_grouped_gemm_fp8_wgrad(const uint8_t* A_t, const float* a_scale, const uint8_t* dC_t,
+                               const float* dc_scale, const int64_t* padded, int32_t G,
+                               int64_t ldm, int64_t K, int64_t N, int dB_dtype, int accumulate,
+                               void* dB, void* stream);
 
 /* -------------------------------------------------------------- Combine -- */
 

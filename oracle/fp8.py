@@ -109,3 +109,138 @@ def dequantize_rows(q, s, block=128):
 def dequantize_blocks(q, s, block=128):
     s = np.asarray(s, np.float64)
     return decode(q) * np.repeat(np.repeat(s, block, axis=0), block, axis=1)
+
+
+def to_bf16(a):
+    """Round to the nearest bfloat16 (ties to even), returned as float32: the
+    storage dtype of the tensors the fp8 quantizers read."""
+    u = np.asarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
+def padded_offsets(offsets, block=128):
+    """Each group's row count rounded up to a multiple of ``block``."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    sizes = np.diff(offsets)
+    padded = (sizes + block - 1) // block * block
+    out = np.zeros(len(offsets), dtype=np.int64)
+    out[1:] = np.cumsum(padded)
+    return out
+
+
+def quantize_token_tiles(x, offsets, block=128):
+    """``block`` tokens x 1 tiles along the rows of x [M, K], per group of
+    rows [offsets[g], offsets[g+1]), each group zero-padded to a multiple of
+    ``block`` rows (the contraction axis of a weight gradient is the tokens).
+    Returns codes uint8 [M_pad, K], fp32 scales [M_pad / block, K] and the
+    padded offsets."""
+    x = np.asarray(x, dtype=np.float32)
+    M, K = x.shape
+    poff = padded_offsets(offsets, block)
+    M_pad = int(poff[-1])
+    q = np.zeros((M_pad, K), dtype=np.uint8)
+    s = np.ones((M_pad // block, K), dtype=np.float32)
+    for g in range(len(offsets) - 1):
+        lo, hi, plo = int(offsets[g]), int(offsets[g + 1]), int(poff[g])
+        for b in range((hi - lo + block - 1) // block):
+            r0 = lo + b * block
+            r1 = min(hi, r0 + block)
+            tile = x[r0:r1]                                   # [rows, K]
+            for col in range(K):
+                scale, inv = block_scale(np.max(np.abs(tile[:, col])))
+                q[plo + b * block:plo + b * block + (r1 - r0), col] = \
+                    encode((tile[:, col] * inv).astype(np.float32))
+                s[plo // block + b, col] = scale
+    return q, s, poff
+
+
+def dequantize_token_tiles(q, s, block=128):
+    return decode(q) * np.repeat(np.asarray(s, np.float64), block, axis=0)
+
+
+def layer_fp8(x, w_r, w13, w2, dout, k, score, renorm, logit_bias=None, shared=None,
+              quantize=True, block=128):
+    """Forward and backward of the MoE layer with every expert-GEMM input
+    quantized blockwise to E4M3 (the fp8 recipe above), computed as fp64
+    grouped GEMMs on the dequantized values.
+
+    Forward and dgrad operands use 1 x block tiles along their contraction
+    axis (rows of X_perm, H, dY, dAB); weights use block x block blocks (the
+    same blocks serve the transposed use in dgrad); weight-gradient operands
+    use block-token x 1 tiles, each expert's rows zero-padded to a multiple
+    of block.  The quantizers read bf16 tensors (the storage dtype of the
+    activations), so a value is rounded to bf16 before it is quantized.
+    Routing, permutation, SwiGLU and combine are exact (fp64, fp32 keys).
+    ``quantize=False`` replaces every quantize/dequantize pair with the
+    identity (the exact layer).  Returns a dict of outputs and gradients.
+    """
+    from . import moe_oracle as o
+
+    def q_rows(a):
+        if not quantize:
+            return o.f64(a)
+        qq, ss = quantize_rows(to_bf16(a), block)
+        return dequantize_rows(qq, ss, block)
+
+    def q_weights(w):
+        if not quantize:
+            return o.f64(w)
+        return np.stack([dequantize_blocks(*quantize_blocks(to_bf16(wg), block), block)
+                         for wg in w])
+
+    def q_tiles(a, offsets):
+        """Returns the padded dequantized rows and the padded offsets."""
+        if not quantize:
+            return o.f64(a), np.asarray(offsets, np.int64)
+        qq, ss, poff = quantize_token_tiles(to_bf16(a), offsets, block)
+        return dequantize_token_tiles(qq, ss, block), poff
+
+    x = o.f64(x)
+    T = x.shape[0]
+    z = o.router_logits(x, w_r, logit_bias)
+    r = o.route(z, k, score, renorm)
+    off = r["offsets"]
+    w13d, w2d = q_weights(w13), q_weights(w2)
+    xp = o.permute(x, r["src_token"])
+    ab = o.grouped_gemm_fwd(q_rows(xp), w13d, off)
+    h = o.swiglu(ab)
+    y = o.grouped_gemm_fwd(q_rows(h), w2d, off)
+    ys = None
+    if shared is not None:
+        ws13d, ws2d = q_weights(np.asarray(shared[0])[None]), q_weights(np.asarray(shared[1])[None])
+        all_rows = np.array([0, T])
+        abs_ = o.grouped_gemm_fwd(q_rows(x), ws13d, all_rows)
+        hs = o.swiglu(abs_)
+        ys = o.grouped_gemm_fwd(q_rows(hs), ws2d, all_rows)
+    out = o.unpermute_combine(y, r["topk_w"], r["dst_row"], ys)
+
+    dout = o.f64(dout)
+    dy, dw = o.unpermute_combine_bwd(dout, y, r["topk_w"], r["dst_row"])
+    dh = o.grouped_gemm_dgrad(q_rows(dy), w2d, off)
+    dab = o.swiglu_bwd(dh, ab)
+    dxp = o.grouped_gemm_dgrad(q_rows(dab), w13d, off)
+    hp, poff = q_tiles(h, off)
+    dyp, _ = q_tiles(dy, off)
+    dW2 = o.grouped_gemm_wgrad(hp, dyp, poff)
+    xpp, _ = q_tiles(xp, off)
+    dabp, _ = q_tiles(dab, off)
+    dW13 = o.grouped_gemm_wgrad(xpp, dabp, poff)
+    res = {}
+    addends = []
+    if shared is not None:
+        dhs = o.grouped_gemm_dgrad(q_rows(dout), ws2d, all_rows)
+        dabs = o.swiglu_bwd(dhs, abs_)
+        addends.append(o.grouped_gemm_dgrad(q_rows(dabs), ws13d, all_rows))
+        hsp, ps = q_tiles(hs, all_rows)
+        doutp, _ = q_tiles(dout, all_rows)
+        xsp, _ = q_tiles(x, all_rows)
+        dabsp, _ = q_tiles(dabs, all_rows)
+        res["dWs2"] = o.grouped_gemm_wgrad(hsp, doutp, ps)[0]
+        res["dWs13"] = o.grouped_gemm_wgrad(xsp, dabsp, ps)[0]
+    dz = o.route_bwd(z, r["topk_idx"], r["topk_w"], dw, score, renorm)
+    dWr, dxr = o.router_logits_bwd(x, w_r, dz)
+    addends.append(dxr)
+    dx = o.permute_bwd(dxp, r["dst_row"], addends=tuple(addends))
+    res.update(out=out, dx=dx, d_logits=dz, dW_r=dWr, dW13=dW13, dW2=dW2, z=z, route=r)
+    return res

@@ -46,6 +46,17 @@ SIGNATURES = {
     "moe_swiglu_bwd": (_int, [_p, _p, _int, _i64, _i64, _p, _p]),
     "moe_unpermute_combine": (_int, [_p, _int, _p, _p, _p, _i64, _i64, _i32, _p, _p]),
     "moe_unpermute_combine_bwd": (_int, [_p, _p, _int, _p, _p, _i64, _i64, _i32, _p, _p, _p]),
+    "moe_quant_fp8_rows": (_int, [_p, _i64, _i64, _p, _p, _p]),
+    "moe_quant_fp8_weights": (_int, [_p, _i32, _i64, _i64, _p, _p, _p, _p, _p]),
+    "moe_padded_rows_bound": (_i64, [_i64, _i32, _i32]),
+    "moe_padded_offsets": (_int, [_p, _i32, _i64, _i32, _p, _p]),
+    "moe_quant_fp8_token_tiles": (_int, [_p, _p, _p, _i32, _i64, _i64, _i64, _p, _p, _p]),
+    "moe_grouped_gemm_fp8_fwd": (_int, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _int, _p, _p,
+                                        _p]),
+    "moe_grouped_gemm_fp8_dgrad": (_int, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _int, _p,
+                                          _p, _p]),
+    "moe_grouped_gemm_fp8_wgrad": (_int, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _int, _int,
+                                          _p, _p]),
 }
 
 _lib = None
@@ -199,3 +210,54 @@ def moe_unpermute_combine_bwd(dout, y_perm, topk_w, dst_row, dy_perm, d_topk_w, 
     T, d = dout.shape
     _call("moe_unpermute_combine_bwd", _ptr(dout), _ptr(y_perm), dtype_code(dout), _ptr(topk_w),
           _ptr(dst_row), T, d, dst_row.shape[1], _ptr(dy_perm), _ptr(d_topk_w), _stream(stream))
+
+
+# ---- fp8 (E4M3 codes as torch.uint8 tensors, fp32 scales)
+
+def moe_quant_fp8_rows(x, q, scale_t, stream=None):
+    M, K = x.shape
+    _call("moe_quant_fp8_rows", _ptr(x), M, K, _ptr(q), _ptr(scale_t), _stream(stream))
+
+
+def moe_quant_fp8_weights(w, q_fwd, s_fwd, q_dgrad, s_dgrad, stream=None):
+    G, K, N = w.shape
+    _call("moe_quant_fp8_weights", _ptr(w), G, K, N, _ptr(q_fwd), _ptr(s_fwd), _ptr(q_dgrad),
+          _ptr(s_dgrad), _stream(stream))
+
+
+def moe_padded_rows_bound(M, G, align=128):
+    return lib().moe_padded_rows_bound(M, G, align)
+
+
+def moe_padded_offsets(offsets, M, padded, align=128, stream=None):
+    _call("moe_padded_offsets", _ptr(offsets), offsets.numel() - 1, M, align, _ptr(padded),
+          _stream(stream))
+
+
+def moe_quant_fp8_token_tiles(x, offsets, padded, q_t, scale, stream=None):
+    M, K = x.shape
+    _call("moe_quant_fp8_token_tiles", _ptr(x), _ptr(offsets), _ptr(padded), offsets.numel() - 1,
+          M, K, q_t.shape[1], _ptr(q_t), _ptr(scale), _stream(stream))
+
+
+def moe_grouped_gemm_fp8_fwd(A, a_scale_t, B_fwd, b_scale_fwd, offsets, C, H=None,
+                             epilogue=EPI_NONE, stream=None):
+    G, N, K = B_fwd.shape
+    _call("moe_grouped_gemm_fp8_fwd", _ptr(A), _ptr(a_scale_t), _ptr(B_fwd), _ptr(b_scale_fwd),
+          _ptr(offsets), G, A.shape[0], K, N, epilogue, _ptr(C), _ptr(H), _stream(stream))
+
+
+def moe_grouped_gemm_fp8_dgrad(dC, dc_scale_t, B_dgrad, b_scale_dgrad, offsets, dA,
+                               epilogue=EPI_NONE, ab=None, stream=None):
+    G, K, N = B_dgrad.shape
+    _call("moe_grouped_gemm_fp8_dgrad", _ptr(dC), _ptr(dc_scale_t), _ptr(B_dgrad),
+          _ptr(b_scale_dgrad), _ptr(offsets), G, dC.shape[0], K, N, epilogue, _ptr(ab), _ptr(dA),
+          _stream(stream))
+
+
+def moe_grouped_gemm_fp8_wgrad(A_t, a_scale, dC_t, dc_scale, padded, dB, accumulate=False,
+                               stream=None):
+    G, K, N = dB.shape
+    _call("moe_grouped_gemm_fp8_wgrad", _ptr(A_t), _ptr(a_scale), _ptr(dC_t), _ptr(dc_scale),
+          _ptr(padded), G, A_t.shape[1], K, N, dtype_code(dB), int(accumulate), _ptr(dB),
+          _stream(stream))

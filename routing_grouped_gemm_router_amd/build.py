@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "libmoe_mi355x.so"
-SOURCES = ["moe_api.cpp", "route.hip", "permute.hip", "gemm_f32.hip", "gemm_bf16.hip"]
+SOURCES = ["moe_api.cpp", "route.hip", "permute.hip", "gemm_f32.hip", "quant.hip", "grouped_gemm.hip"]
 ARCH = "gfx950"
 
 

@@ -1,7 +1,10 @@
-// bf16 grouped GEMM on CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16, fp32
-// accumulation): the experts' SwiGLU FFNs of "Scalable Training of
+// Grouped GEMM on CDNA4 matrix cores, bf16 (v_mfma_f32_32x32x16_bf16) and fp8
+// E4M3 with fp32 block scales (v_mfma_scale_f32_32x32x64_f8f6f4 at unit
+// scale), fp32 accumulation: the experts' SwiGLU FFNs of "Scalable Training of
 // Mixture-of-Experts Models with Megatron Core", section 2, Expert Computation
-// (the local experts' GEMMs run together over their ragged row groups).
+// (the local experts' GEMMs run together over their ragged row groups), and
+// its section 5 blockwise FP8 recipe (1 x 128 activation tiles, 128 x 128
+// weight blocks).
 //
 //   forward  C[rows g]  = A[rows g] . B[g]       A [M,K]  B [G,K,N]
 //   dgrad    dA[rows g] = dC[rows g] . B[g]^T    dC [M,N] B [G,K,N]
@@ -32,6 +35,10 @@
 //    consumed and writes 16-byte vectors, 128 bytes per row.
 //  * Epilogues: SwiGLU (AB and H = silu(A) * B from the fp32 sums; a tile holds
 //    matching gate and up columns) and SwiGLU backward (dH -> dAB, reading AB).
+//  * fp8: every operand arrives k-contiguous (the quantizers write the layouts
+//    the GEMM wants), a k step is one 128-wide scale block, and each step's
+//    MFMA partial is promoted into the fp32 accumulator times the row scale of
+//    A and the row scale of B, both DMA'd into LDS with the stage.
 #include "common.h"
 #include "internal.h"
 
@@ -45,11 +52,17 @@ typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int BM = 128, BN = 128;
 constexpr int STAGES = 2;              // x 2 workgroups per CU
-constexpr int OP_BYTES = 16384;            // one operand of one stage
-constexpr int STAGE_BYTES = 2 * OP_BYTES;  // A then B
+constexpr int OP_BYTES = 16384;        // one operand of one stage: 128 rows x 128 bytes
+constexpr int SCALE_BYTES = 1024;      // fp8: 128 row scales of A, then 128 of B
+
+// k elements per step: 128 bytes of each row
+template <bool F8> struct KStep { static constexpr int value = F8 ? 128 : 64; };
+template <bool F8> constexpr int stage_bytes() { return 2 * OP_BYTES + (F8 ? SCALE_BYTES : 0); }
 constexpr int MAX_GROUPS = 1024;
 constexpr uint32_t RSRC_DW3 = 0x00020000u; // raw buffer, 32-bit elements, bounds-checked
 
@@ -108,14 +121,30 @@ __device__ __forceinline__ void dma16(i32x4_t rs, LDS_AS void* dst, uint32_t vof
                : "memory", "m0");
 }
 
-// wait until at most n of this wave's vector-memory ops are outstanding, then
-// a workgroup barrier (no implicit fence: the DMA ring is ordered by vmcnt)
+// 4 bytes per lane into LDS at dst + 4 * lane (fp8 scale vectors)
+__device__ __forceinline__ void dma4(i32x4_t rs, LDS_AS void* dst, uint32_t voff) {
+  const int32_t m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<int32_t>(reinterpret_cast<uintptr_t>(dst)));
+  i32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane(rs.x);
+  r.y = __builtin_amdgcn_readfirstlane(rs.y);
+  r.z = __builtin_amdgcn_readfirstlane(rs.z);
+  r.w = __builtin_amdgcn_readfirstlane(rs.w);
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(m0)
+               : "memory", "m0");
+}
+
+// wait until this wave's DMA for the oldest in-flight stage has landed (at
+// most n younger stages of PER instructions outstanding), then a workgroup
+// barrier (no implicit fence: the DMA ring is ordered by vmcnt)
+template <int PER>
 __device__ __forceinline__ void wait_barrier(int n) {
-  switch (n) {
-    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 1: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
-  }
+  if (n <= 0)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER) : "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -126,11 +155,11 @@ __device__ __forceinline__ int virtual_block() {
 }
 
 struct Params {
-  const bf16_t* A;
-  const bf16_t* B;
+  const char* A;   // element bytes: 2 (bf16) or 1 (fp8 codes)
+  const char* B;
   const int64_t* off;
   int G;
-  int64_t M;
+  int64_t M;     // rows (row groups); contraction rows (wgrad; fp8: padded bound)
   int64_t Kc;    // contraction length (row groups) / K of dB (wgrad)
   int64_t Nout;  // product columns (row groups) / N of dB (wgrad)
   void* C;       // C, dA or dAB, or dB
@@ -138,6 +167,9 @@ struct Params {
   const bf16_t* ab;
   int out_f32;
   int accumulate;
+  const float* sa;  // fp8 row scales of A: [Kc/128][M] (row groups), [M/128][Kc] (wgrad)
+  const float* sb;  // fp8 row scales of B: [G][Kc/128][Nout] (row groups), [M/128][Nout] (wgrad)
+  int64_t ldm;      // fp8 wgrad: row length of the transposed operands
 };
 
 // What a tile is: a ragged row block x 128 columns of one group (forward,
@@ -169,7 +201,7 @@ __device__ __forceinline__ void tile_in_group(uint32_t tl, uint32_t mt_g, uint32
   n = chunk * SN + rr % cw;
 }
 
-template <int MODE>
+template <int MODE, bool F8>
 __device__ __forceinline__ bool decode(int64_t tau64, const Params& p, const int* s_pre,
                                        const int64_t* s_off, int64_t NT64, int64_t total, Tile& t) {
   if (tau64 >= total) return false;
@@ -185,6 +217,7 @@ __device__ __forceinline__ bool decode(int64_t tau64, const Params& p, const int
     t.rows = BM;
     t.lo = s_off[t.g];
     t.nrows = s_off[t.g + 1] - t.lo;
+    constexpr int BK = KStep<F8>::value;
     t.nk = t.nrows > 0 ? static_cast<int>((t.nrows + BK - 1) / BK) : 1;
   } else {
     // group g owns tiles [s_pre[g] * NT, s_pre[g+1] * NT)
@@ -203,7 +236,7 @@ __device__ __forceinline__ bool decode(int64_t tau64, const Params& p, const int
     t.row0 = lo + static_cast<int64_t>(m) * BM;
     t.nt = n;
     t.rows = static_cast<int>(min<int64_t>(BM, hi - t.row0));
-    t.nk = static_cast<int>(p.Kc / BK);
+    t.nk = static_cast<int>(p.Kc / KStep<F8>::value);
     t.lo = lo;
     t.nrows = hi - lo;
   }
@@ -211,73 +244,129 @@ __device__ __forceinline__ bool decode(int64_t tau64, const Params& p, const int
 }
 
 // Loader state of one tile: buffer resources and this lane's byte offsets
-// for its 4 A and 4 B DMA instructions at k step 0, plus per-step deltas.
+// for its 4 A and 4 B DMA instructions at k step 0, plus per-step deltas; for
+// fp8 also the one scale-vector instruction of this wave.
 struct Loader {
-  i32x4_t ra, rb;
-  uint32_t va[4], vb[4];
-  uint32_t da, db;
+  i32x4_t ra, rb, rs;
+  uint32_t va[4], vb[4], vs;
+  uint32_t da, db, ds;
 };
 
+// Which operand layouts a mode uses in LDS: KC = [row][k] (k-contiguous in
+// memory), otherwise [k][row] read by transposing.
+template <int MODE, bool F8> struct Layout {
+  static constexpr bool A_KC = F8 || MODE != WGRAD;
+  static constexpr bool B_KC = F8 || MODE == DGRAD || MODE == DGRAD_SWIGLU_BWD;
+};
+
+// B-operand row of tile row rho (0..127): the forward with SwiGLU pairs 64
+// gate columns with the matching 64 up columns
 template <int MODE>
+__device__ __forceinline__ int64_t b_row(const Tile& t, int rho, int64_t fh) {
+  if (MODE == FWD_SWIGLU) return ((rho >> 5) & 1) * fh + t.nt * 64 + (rho >> 6) * 32 + (rho & 31);
+  return t.nt * BN + rho;
+}
+
+template <int MODE, bool F8>
 __device__ __forceinline__ void setup_loader(const Params& p, const Tile& t, int wave, int lane,
                                              Loader& L) {
+  constexpr int ES = F8 ? 1 : 2;  // element bytes
+  constexpr int BK = KStep<F8>::value;
   const int64_t fh = p.Nout / 2;
-  if (MODE == WGRAD) {
+  if (MODE == WGRAD && !F8) {
     // A = X [M, Kc] rows of the group, [k][row] layout; B = dC [M, Nout] likewise
     const int64_t K = p.Kc, N = p.Nout;
-    L.ra = make_rsrc(p.A + t.lo * K, static_cast<uint64_t>(t.nrows) * K * 2);
-    L.rb = make_rsrc(p.B + t.lo * N, static_cast<uint64_t>(t.nrows) * N * 2);
+    L.ra = make_rsrc(p.A + t.lo * K * ES, static_cast<uint64_t>(t.nrows) * K * ES);
+    L.rb = make_rsrc(p.B + t.lo * N * ES, static_cast<uint64_t>(t.nrows) * N * ES);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int q = wave * 4 + i;
       const int kr = 4 * q + (lane >> 4), c = (lane & 15) ^ swz_nc(kr);
-      L.va[i] = static_cast<uint32_t>(kr * K * 2 + (t.row0 + 8 * c) * 2);
-      L.vb[i] = static_cast<uint32_t>(kr * N * 2 + (t.nt * BN + 8 * c) * 2);
+      L.va[i] = static_cast<uint32_t>((kr * K + t.row0 + 8 * c) * ES);
+      L.vb[i] = static_cast<uint32_t>((kr * N + t.nt * BN + 8 * c) * ES);
     }
-    L.da = static_cast<uint32_t>(BK * K * 2);
-    L.db = static_cast<uint32_t>(BK * N * 2);
+    L.da = static_cast<uint32_t>(BK * K * ES);
+    L.db = static_cast<uint32_t>(BK * N * ES);
     return;
   }
-  // A: k-contiguous rows of the tile, [row][k] layout
-  const int64_t Kc = p.Kc;
-  L.ra = make_rsrc(p.A + t.row0 * Kc, static_cast<uint64_t>(t.rows) * Kc * 2);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = wave * 4 + i;
-    const int r = 8 * q + (lane >> 3), c = (lane & 7) ^ swz_kc(r);
-    L.va[i] = static_cast<uint32_t>(r * Kc * 2 + c * 16);
-  }
-  L.da = BK * 2;
-  if (MODE == FWD || MODE == FWD_SWIGLU) {
-    // B = W_g [Kc, Nout], [k][col] layout
-    const int64_t N = p.Nout;
-    L.rb = make_rsrc(p.B + static_cast<int64_t>(t.g) * Kc * N, static_cast<uint64_t>(Kc) * N * 2);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = wave * 4 + i;
-      const int kr = 4 * q + (lane >> 4), c = (lane & 15) ^ swz_nc(kr);
-      int64_t col;
-      if (MODE == FWD_SWIGLU)  // tile column 8c: wave column c / 8, gate/up (c / 4) % 2
-        col = ((c >> 2) & 1) * fh + t.nt * 64 + (c >> 3) * 32 + (c & 3) * 8;
-      else
-        col = t.nt * BN + 8 * c;
-      L.vb[i] = static_cast<uint32_t>(kr * N * 2 + col * 2);
-    }
-    L.db = static_cast<uint32_t>(BK * N * 2);
-  } else {
-    // B = W_g [Nout, Kc] rows nt*128.., [row][k] layout
-    L.rb = make_rsrc(p.B + (static_cast<int64_t>(t.g) * p.Nout + t.nt * BN) * Kc,
-                     static_cast<uint64_t>(BN) * Kc * 2);
+  if (MODE == WGRAD && F8) {
+    // A = X^T codes [Kc, ldm], B = dC^T codes [Nout, ldm]: rows of the tile,
+    // contraction over the group's padded token range [lo, lo + nrows)
+    const int64_t ldm = p.ldm;
+    const uint64_t na = t.nrows > 0 ? static_cast<uint64_t>(BM) * ldm : 0;
+    L.ra = make_rsrc(p.A + t.row0 * ldm + t.lo, na);
+    L.rb = make_rsrc(p.B + t.nt * BN * ldm + t.lo, na);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int q = wave * 4 + i;
       const int r = 8 * q + (lane >> 3), c = (lane & 7) ^ swz_kc(r);
-      L.vb[i] = static_cast<uint32_t>(r * Kc * 2 + c * 16);
+      L.va[i] = L.vb[i] = static_cast<uint32_t>(r * ldm + c * 16);
     }
-    L.db = BK * 2;
+    L.da = L.db = 128;
+    // scales [ldm/128][Kc] and [ldm/128][Nout], block lo/128 + kt
+    const int64_t kb0 = t.lo / 128;
+    if (wave < 2) {
+      L.rs = make_rsrc(p.sa, static_cast<uint64_t>(ldm / 128) * p.Kc * 4);
+      L.vs = static_cast<uint32_t>((kb0 * p.Kc + t.row0 + wave * 64 + lane) * 4);
+      L.ds = static_cast<uint32_t>(p.Kc * 4);
+    } else {
+      L.rs = make_rsrc(p.sb, static_cast<uint64_t>(ldm / 128) * p.Nout * 4);
+      L.vs = static_cast<uint32_t>((kb0 * p.Nout + t.nt * BN + (wave - 2) * 64 + lane) * 4);
+      L.ds = static_cast<uint32_t>(p.Nout * 4);
+    }
+    return;
+  }
+  // A: k-contiguous rows of the tile, [row][k] layout
+  const int64_t Kc = p.Kc;
+  L.ra = make_rsrc(p.A + t.row0 * Kc * ES, static_cast<uint64_t>(t.rows) * Kc * ES);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = wave * 4 + i;
+    const int r = 8 * q + (lane >> 3), c = (lane & 7) ^ swz_kc(r);
+    L.va[i] = static_cast<uint32_t>(r * Kc * ES + c * 16);
+  }
+  L.da = 128;
+  if (Layout<MODE, F8>::B_KC) {
+    // B rows (output columns) are k-contiguous: bf16 dgrad W_g [Nout, Kc];
+    // fp8 forward W_g^T codes [Nout, Kc]; fp8 dgrad W_g codes [Nout, Kc]
+    const char* bg = p.B + static_cast<int64_t>(t.g) * p.Nout * Kc * ES;
+    L.rb = make_rsrc(bg, static_cast<uint64_t>(p.Nout) * Kc * ES);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = wave * 4 + i;
+      const int r = 8 * q + (lane >> 3), c = (lane & 7) ^ swz_kc(r);
+      L.vb[i] = static_cast<uint32_t>(b_row<MODE>(t, r, fh) * Kc * ES + c * 16);
+    }
+    L.db = 128;
+  } else {
+    // bf16 forward: B = W_g [Kc, Nout], [k][col] layout
+    const int64_t N = p.Nout;
+    L.rb = make_rsrc(p.B + static_cast<int64_t>(t.g) * Kc * N * ES, static_cast<uint64_t>(Kc) * N * ES);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = wave * 4 + i;
+      const int kr = 4 * q + (lane >> 4), c = (lane & 15) ^ swz_nc(kr);
+      L.vb[i] = static_cast<uint32_t>((kr * N + b_row<MODE>(t, 8 * c, fh)) * ES);
+    }
+    L.db = static_cast<uint32_t>(BK * N * ES);
+  }
+  if (F8) {
+    // scales: A [Kc/128][M] at row row0 + rho; B [G][Kc/128][Nout] at b_row(rho)
+    const int64_t nkb = Kc / 128;
+    if (wave < 2) {
+      L.rs = make_rsrc(p.sa, static_cast<uint64_t>(nkb) * p.M * 4);
+      L.vs = static_cast<uint32_t>((t.row0 + wave * 64 + lane) * 4);
+      L.ds = static_cast<uint32_t>(p.M * 4);
+    } else {
+      L.rs = make_rsrc(p.sb + static_cast<int64_t>(t.g) * nkb * p.Nout,
+                       static_cast<uint64_t>(nkb) * p.Nout * 4);
+      L.vs = static_cast<uint32_t>(b_row<MODE>(t, (wave - 2) * 64 + lane, fh) * 4);
+      L.ds = static_cast<uint32_t>(p.Nout * 4);
+    }
   }
 }
 
+template <bool F8>
 __device__ __forceinline__ void issue(const Loader& L, int kt, LDS_AS char* stage, int wave) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -285,13 +374,26 @@ __device__ __forceinline__ void issue(const Loader& L, int kt, LDS_AS char* stag
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     dma16(L.rb, stage + OP_BYTES + (wave * 4 + i) * 1024, L.vb[i] + kt * L.db);
+  if (F8) dma4(L.rs, stage + 2 * OP_BYTES + wave * 256, L.vs + kt * L.ds);
 }
 
 // ---- fragment reads ----------------------------------------------------------
 
-// [row][k] layout: 8 k values of row r, chunk c
+// [row][k] layout: 16 bytes of row r, chunk c
+__device__ __forceinline__ u32x4_t chunk_kc(const LDS_AS char* op, int r, int c) {
+  return *(const LDS_AS u32x4_t*)(op + r * 128 + ((c ^ swz_kc(r)) << 4));
+}
+
 __device__ __forceinline__ bf16x8_t frag_kc(const LDS_AS char* op, int r, int c) {
-  return *(const LDS_AS bf16x8_t*)(op + r * 128 + ((c ^ swz_kc(r)) << 4));
+  return __builtin_bit_cast(bf16x8_t, chunk_kc(op, r, c));
+}
+
+// fp8 operand for one 32x32x64 MFMA: 32 k codes of row r (this lane's half
+// of the 64), the same k positions for A and for B
+__device__ __forceinline__ i32x8_t frag_kc8(const LDS_AS char* op, int r, int c0) {
+  const u32x4_t lo = chunk_kc(op, r, c0), hi = chunk_kc(op, r, c0 + 1);
+  const u32x4_t v[2] = {lo, hi};
+  return __builtin_bit_cast(i32x8_t, v);
 }
 
 // [k][col] layout: 8 k values (k0 .. k0+7 of this lane's half) of one column,
@@ -311,14 +413,14 @@ __device__ __forceinline__ bf16x8_t frag_nc(const LDS_AS char* op, int col_base,
 }
 
 template <int MODE>
-__device__ __forceinline__ void compute_stage(f32x16_t (&acc)[2][2], const LDS_AS char* stage,
-                                              int wm, int wn, int lane) {
-  constexpr bool A_NC = MODE == WGRAD;
-  constexpr bool B_NC = MODE == FWD || MODE == FWD_SWIGLU || MODE == WGRAD;
+__device__ __forceinline__ void compute_stage_bf16(f32x16_t (&acc)[2][2], const LDS_AS char* stage,
+                                                   int wm, int wn, int lane) {
+  constexpr bool A_NC = !Layout<MODE, false>::A_KC;
+  constexpr bool B_NC = !Layout<MODE, false>::B_KC;
   const LDS_AS char* opA = stage;
   const LDS_AS char* opB = stage + OP_BYTES;
 #pragma unroll
-  for (int kk = 0; kk < BK / 16; ++kk) {
+  for (int kk = 0; kk < 4; ++kk) {
     bf16x8_t a[2], b[2];
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii)
@@ -334,6 +436,59 @@ __device__ __forceinline__ void compute_stage(f32x16_t (&acc)[2][2], const LDS_A
       for (int jj = 0; jj < 2; ++jj)
         acc[ii][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[jj], a[ii], acc[ii][jj], 0, 0, 0);
   }
+}
+
+// fp8: one 128-wide scale block per stage, as two MFMAs of 64 k per output
+// block; each partial is promoted as acc += partial * scale_A(row) *
+// scale_B(column) (the scale is constant over the block, so promoting the two
+// halves separately is the same sum and keeps half the fragments live)
+__device__ __forceinline__ void compute_stage_fp8(f32x16_t (&acc)[2][2], const LDS_AS char* stage,
+                                                  int wm, int wn, int lane) {
+  const LDS_AS char* opA = stage;
+  const LDS_AS char* opB = stage + OP_BYTES;
+  const LDS_AS float* sA = (const LDS_AS float*)(stage + 2 * OP_BYTES);
+  const LDS_AS float* sB = sA + 128;
+  const int h = lane >> 5;
+  float sa[2];
+#pragma unroll
+  for (int ii = 0; ii < 2; ++ii) sa[ii] = sA[wm * 64 + ii * 32 + (lane & 31)];
+#pragma unroll 1
+  for (int s = 0; s < 2; ++s) {
+    i32x8_t a[2], b[2];
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) a[ii] = frag_kc8(opA, wm * 64 + ii * 32 + (lane & 31), 4 * s + 2 * h);
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) b[jj] = frag_kc8(opB, wn * 64 + jj * 32 + (lane & 31), 4 * s + 2 * h);
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      f32x4 sb[4];
+#pragma unroll
+      for (int vg = 0; vg < 4; ++vg) sb[vg] = *(const LDS_AS f32x4*)(sB + wn * 64 + jj * 32 + vg * 8 + h * 4);
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        f32x16_t part;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) part[v] = 0.f;
+        // format 0 = E4M3 for both operands; E8M0 scale 127 = 1.0
+        part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[jj], a[ii], part, 0, 0, 0, 127, 0,
+                                                               127);
+#pragma unroll
+        for (int vg = 0; vg < 4; ++vg)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[ii][jj][vg * 4 + e] += part[vg * 4 + e] * (sa[ii] * sb[vg][e]);
+      }
+    }
+  }
+}
+
+template <int MODE, bool F8>
+__device__ __forceinline__ void compute_stage(f32x16_t (&acc)[2][2], const LDS_AS char* stage,
+                                              int wm, int wn, int lane) {
+  if (F8)
+    compute_stage_fp8(acc, stage, wm, wn, lane);
+  else
+    compute_stage_bf16<MODE>(acc, stage, wm, wn, lane);
 }
 
 // ---- epilogue ------------------------------------------------------------------
@@ -493,9 +648,11 @@ __device__ __forceinline__ void epilogue(const Params& p, const Tile& t, const f
 
 // ---- the kernel ----------------------------------------------------------------
 
-template <int MODE>
-__global__ __launch_bounds__(256, 2) void gg_bf16_kernel(Params p) {
-  __shared__ __attribute__((aligned(1024))) char ring[STAGES * STAGE_BYTES];
+template <int MODE, bool F8>
+__global__ __launch_bounds__(256, 2) void gg_kernel(Params p) {
+  constexpr int SB = stage_bytes<F8>();
+  constexpr int PER = F8 ? 9 : 8;  // DMA instructions per wave per stage
+  __shared__ __attribute__((aligned(1024))) char ring[STAGES * SB];
   __shared__ int s_pre[MAX_GROUPS + 1];
   __shared__ int64_t s_off[MAX_GROUPS + 1];
   LDS_AS char* lring = (LDS_AS char*)(ring);
@@ -559,24 +716,24 @@ __global__ __launch_bounds__(256, 2) void gg_bf16_kernel(Params p) {
   const int P = gridDim.x;
   int64_t ld_tau = virtual_block(), cp_tau = ld_tau;
   Tile ld_t, cp_t;
-  bool ld_ok = decode<MODE>(ld_tau, p, s_pre, s_off, NT, total, ld_t);
+  bool ld_ok = decode<MODE, F8>(ld_tau, p, s_pre, s_off, NT, total, ld_t);
   bool cp_ok = ld_ok;
   cp_t = ld_t;
   Loader L;
-  if (ld_ok) setup_loader<MODE>(p, ld_t, wave, lane, L);
+  if (ld_ok) setup_loader<MODE, F8>(p, ld_t, wave, lane, L);
   int ld_kt = 0, cp_kt = 0;
   int inflight = 0, ld_slot = 0, cp_slot = 0;
 
   // prologue: STAGES - 1 steps in flight
   for (int s = 0; s < STAGES - 1 && ld_ok; ++s) {
-    issue(L, ld_kt, lring + ld_slot * STAGE_BYTES, wave);
+    issue<F8>(L, ld_kt, lring + ld_slot * SB, wave);
     ++inflight;
     ld_slot = ld_slot + 1 == STAGES ? 0 : ld_slot + 1;
     if (++ld_kt == ld_t.nk) {
       ld_kt = 0;
       ld_tau += P;
-      ld_ok = decode<MODE>(ld_tau, p, s_pre, s_off, NT, total, ld_t);
-      if (ld_ok) setup_loader<MODE>(p, ld_t, wave, lane, L);
+      ld_ok = decode<MODE, F8>(ld_tau, p, s_pre, s_off, NT, total, ld_t);
+      if (ld_ok) setup_loader<MODE, F8>(p, ld_t, wave, lane, L);
     }
   }
 
@@ -589,19 +746,19 @@ __global__ __launch_bounds__(256, 2) void gg_bf16_kernel(Params p) {
       for (int v = 0; v < 16; ++v) acc[ii][jj][v] = 0.f;
 
   while (cp_ok) {
-    wait_barrier(inflight - 1);  // this step's stage has landed in LDS for all waves
+    wait_barrier<PER>(inflight - 1);  // this step's stage has landed in LDS for all waves
     if (ld_ok) {                 // refill the slot consumed in the previous step
-      issue(L, ld_kt, lring + ld_slot * STAGE_BYTES, wave);
+      issue<F8>(L, ld_kt, lring + ld_slot * SB, wave);
       ++inflight;
       ld_slot = ld_slot + 1 == STAGES ? 0 : ld_slot + 1;
       if (++ld_kt == ld_t.nk) {
         ld_kt = 0;
         ld_tau += P;
-        ld_ok = decode<MODE>(ld_tau, p, s_pre, s_off, NT, total, ld_t);
-        if (ld_ok) setup_loader<MODE>(p, ld_t, wave, lane, L);
+        ld_ok = decode<MODE, F8>(ld_tau, p, s_pre, s_off, NT, total, ld_t);
+        if (ld_ok) setup_loader<MODE, F8>(p, ld_t, wave, lane, L);
       }
     }
-    compute_stage<MODE>(acc, lring + cp_slot * STAGE_BYTES, wm, wn, lane);
+    compute_stage<MODE, F8>(acc, lring + cp_slot * SB, wm, wn, lane);
     --inflight;
     if (++cp_kt == cp_t.nk) {
       // the slot just consumed is not refilled before the next barrier: stage
@@ -609,7 +766,7 @@ __global__ __launch_bounds__(256, 2) void gg_bf16_kernel(Params p) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      epilogue<MODE>(p, cp_t, acc, lring + cp_slot * STAGE_BYTES + wave * 8192, wm, wn, lane);
+      epilogue<MODE>(p, cp_t, acc, lring + cp_slot * SB + wave * 8192, wm, wn, lane);
 #pragma unroll
       for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
@@ -618,7 +775,7 @@ __global__ __launch_bounds__(256, 2) void gg_bf16_kernel(Params p) {
           for (int v = 0; v < 16; ++v) acc[ii][jj][v] = 0.f;
       cp_kt = 0;
       cp_tau += P;
-      cp_ok = decode<MODE>(cp_tau, p, s_pre, s_off, NT, total, cp_t);
+      cp_ok = decode<MODE, F8>(cp_tau, p, s_pre, s_off, NT, total, cp_t);
     }
     cp_slot = cp_slot + 1 == STAGES ? 0 : cp_slot + 1;
   }
@@ -632,21 +789,36 @@ static unsigned persistent_grid(int64_t tiles_upper_bound) {
   return static_cast<unsigned>(p);
 }
 
-template <int MODE>
+template <int MODE, bool F8>
 static hipError_t run(const Params& p, int64_t tiles_upper_bound, hipStream_t s) {
   if (tiles_upper_bound <= 0) return hipSuccess;
-  gg_bf16_kernel<MODE><<<dim3(persistent_grid(tiles_upper_bound)), 256, 0, s>>>(p);
+  gg_kernel<MODE, F8><<<dim3(persistent_grid(tiles_upper_bound)), 256, 0, s>>>(p);
   return hipGetLastError();
+}
+
+static Params make_params(const void* A, const void* B, const int64_t* off, int G, int64_t M,
+                          int64_t Kc, int64_t Nout, void* C, void* H, const void* ab) {
+  Params p{};
+  p.A = static_cast<const char*>(A);
+  p.B = static_cast<const char*>(B);
+  p.off = off;
+  p.G = G;
+  p.M = M;
+  p.Kc = Kc;
+  p.Nout = Nout;
+  p.C = C;
+  p.H = static_cast<bf16_t*>(H);
+  p.ab = static_cast<const bf16_t*>(ab);
+  return p;
 }
 
 hipError_t launch_gg_bf16_fwd(const void* A, const void* B, const int64_t* off, int G, int64_t M,
                               int64_t K, int64_t N, int epi, void* C, void* H, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  Params p{static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(B), off, G, M, K, N, C,
-           static_cast<bf16_t*>(H), nullptr, 0, 0};
-  const int64_t nt = epi == EPI_SWIGLU ? N / 128 : N / BN;
-  if (epi == EPI_SWIGLU) return run<FWD_SWIGLU>(p, (M / BM + G) * nt, s);
-  return run<FWD>(p, (M / BM + G) * nt, s);
+  const Params p = make_params(A, B, off, G, M, K, N, C, H, nullptr);
+  const int64_t nt = N / BN;
+  if (epi == EPI_SWIGLU) return run<FWD_SWIGLU, false>(p, (M / BM + G) * nt, s);
+  return run<FWD, false>(p, (M / BM + G) * nt, s);
 }
 
 hipError_t launch_gg_bf16_dgrad(const void* dC, const void* B, const int64_t* off, int G,
@@ -654,18 +826,53 @@ hipError_t launch_gg_bf16_dgrad(const void* dC, const void* B, const int64_t* of
                                 hipStream_t s) {
   if (M == 0) return hipSuccess;
   // contraction over N, product columns K
-  Params p{static_cast<const bf16_t*>(dC), static_cast<const bf16_t*>(B), off, G, M, N, K, dA,
-           nullptr, static_cast<const bf16_t*>(ab), 0, 0};
-  if (epi == EPI_SWIGLU_BWD) return run<DGRAD_SWIGLU_BWD>(p, (M / BM + G) * (K / BN), s);
-  return run<DGRAD>(p, (M / BM + G) * (K / BN), s);
+  const Params p = make_params(dC, B, off, G, M, N, K, dA, nullptr, ab);
+  if (epi == EPI_SWIGLU_BWD) return run<DGRAD_SWIGLU_BWD, false>(p, (M / BM + G) * (K / BN), s);
+  return run<DGRAD, false>(p, (M / BM + G) * (K / BN), s);
 }
 
 hipError_t launch_gg_bf16_wgrad(const void* A, const void* dC, const int64_t* off, int G,
                                 int64_t M, int64_t K, int64_t N, int db_f32, int accumulate,
                                 void* dB, hipStream_t s) {
-  Params p{static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(dC), off, G, M, K, N, dB,
-           nullptr, nullptr, db_f32, accumulate};
-  return run<WGRAD>(p, static_cast<int64_t>(G) * (K / BM) * (N / BN), s);
+  Params p = make_params(A, dC, off, G, M, K, N, dB, nullptr, nullptr);
+  p.out_f32 = db_f32;
+  p.accumulate = accumulate;
+  return run<WGRAD, false>(p, static_cast<int64_t>(G) * (K / BM) * (N / BN), s);
+}
+
+hipError_t launch_gg_fp8_fwd(const uint8_t* A, const float* sa, const uint8_t* Bt, const float* sb,
+                             const int64_t* off, int G, int64_t M, int64_t K, int64_t N, int epi,
+                             void* C, void* H, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  Params p = make_params(A, Bt, off, G, M, K, N, C, H, nullptr);
+  p.sa = sa;
+  p.sb = sb;
+  const int64_t nt = N / BN;
+  if (epi == EPI_SWIGLU) return run<FWD_SWIGLU, true>(p, (M / BM + G) * nt, s);
+  return run<FWD, true>(p, (M / BM + G) * nt, s);
+}
+
+hipError_t launch_gg_fp8_dgrad(const uint8_t* dC, const float* sa, const uint8_t* B,
+                               const float* sb, const int64_t* off, int G, int64_t M, int64_t K,
+                               int64_t N, int epi, const void* ab, void* dA, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  Params p = make_params(dC, B, off, G, M, N, K, dA, nullptr, ab);
+  p.sa = sa;
+  p.sb = sb;
+  if (epi == EPI_SWIGLU_BWD) return run<DGRAD_SWIGLU_BWD, true>(p, (M / BM + G) * (K / BN), s);
+  return run<DGRAD, true>(p, (M / BM + G) * (K / BN), s);
+}
+
+hipError_t launch_gg_fp8_wgrad(const uint8_t* At, const float* sa, const uint8_t* dCt,
+                               const float* sb, const int64_t* poff, int G, int64_t ldm, int64_t K,
+                               int64_t N, int db_f32, int accumulate, void* dB, hipStream_t s) {
+  Params p = make_params(At, dCt, poff, G, ldm, K, N, dB, nullptr, nullptr);
+  p.sa = sa;
+  p.sb = sb;
+  p.ldm = ldm;
+  p.out_f32 = db_f32;
+  p.accumulate = accumulate;
+  return run<WGRAD, true>(p, static_cast<int64_t>(G) * (K / BM) * (N / BN), s);
 }
 
 }  // namespace moe

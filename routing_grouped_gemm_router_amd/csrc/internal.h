@@ -60,4 +60,26 @@ hipError_t launch_gg_bf16_wgrad(const void* A, const void* dC, const int64_t* of
                                 int64_t M, int64_t K, int64_t N, int db_f32, int accumulate,
                                 void* dB, hipStream_t s);
 
+// grouped_gemm.hip, fp8 E4M3 operands (all k-contiguous) with fp32 row scales
+hipError_t launch_gg_fp8_fwd(const uint8_t* A, const float* sa, const uint8_t* Bt, const float* sb,
+                             const int64_t* off, int G, int64_t M, int64_t K, int64_t N, int epi,
+                             void* C, void* H, hipStream_t s);
+hipError_t launch_gg_fp8_dgrad(const uint8_t* dC, const float* sa, const uint8_t* B,
+                               const float* sb, const int64_t* off, int G, int64_t M, int64_t K,
+                               int64_t N, int epi, const void* ab, void* dA, hipStream_t s);
+hipError_t launch_gg_fp8_wgrad(const uint8_t* At, const float* sa, const uint8_t* dCt,
+                               const float* sb, const int64_t* poff, int G, int64_t ldm, int64_t K,
+                               int64_t N, int db_f32, int accumulate, void* dB, hipStream_t s);
+
+// quant.hip
+hipError_t launch_quant_rows(const void* x, int64_t M, int64_t K, uint8_t* q, float* sT,
+                             hipStream_t s);
+hipError_t launch_quant_weights(const void* w, int G, int64_t K, int64_t N, uint8_t* qf, float* sf,
+                                uint8_t* qd, float* sd, hipStream_t s);
+hipError_t launch_padded_offsets(const int64_t* off, int G, int64_t M, int64_t align,
+                                 int64_t* poff, hipStream_t s);
+hipError_t launch_quant_token_tiles(const void* x, const int64_t* off, const int64_t* poff, int G,
+                                    int64_t M, int64_t K, int64_t ldm, uint8_t* qT, float* s,
+                                    hipStream_t st);
+
 }  // namespace moe

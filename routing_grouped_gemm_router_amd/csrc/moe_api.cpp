@@ -351,4 +351,145 @@ int moe_unpermute_combine_bwd(const void* dout, const void* y_perm, int dtype, c
                     "moe_unpermute_combine_bwd");
 }
 
+
+int moe_quant_fp8_rows(const void* x, int64_t M, int64_t K, uint8_t* q, float* scale_t,
+                       void* stream) {
+  const char* fn = "moe_quant_fp8_rows";
+  REQUIRE(M >= 0 && K >= 1, MOE_ERR_SHAPE, "%s: M=%lld K=%lld", fn, static_cast<long long>(M),
+          static_cast<long long>(K));
+  REQUIRE(K % 128 == 0, MOE_ERR_UNSUPPORTED, "%s: K %% 128 != 0", fn);
+  if (M == 0) return ok();
+  REQUIRE(x && q && scale_t, MOE_ERR_NULL, "%s: x, q and scale_t are required", fn);
+  REQUIRE(aligned16(x) && (reinterpret_cast<uintptr_t>(q) & 7u) == 0, MOE_ERR_UNSUPPORTED,
+          "%s: x must be 16-byte and q 8-byte aligned", fn);
+  return hip_status(moe::launch_quant_rows(x, M, K, q, scale_t, as_stream(stream)), fn);
+}
+
+int moe_quant_fp8_weights(const void* w, int32_t G, int64_t K, int64_t N, uint8_t* q_fwd,
+                          float* s_fwd, uint8_t* q_dgrad, float* s_dgrad, void* stream) {
+  const char* fn = "moe_quant_fp8_weights";
+  REQUIRE(G >= 1 && K >= 1 && N >= 1, MOE_ERR_SHAPE, "%s: G=%d K=%lld N=%lld", fn, G,
+          static_cast<long long>(K), static_cast<long long>(N));
+  REQUIRE(K % 128 == 0 && N % 128 == 0, MOE_ERR_UNSUPPORTED, "%s: K and N must be multiples of 128",
+          fn);
+  REQUIRE(w && q_fwd && s_fwd && q_dgrad && s_dgrad, MOE_ERR_NULL, "%s: all pointers are required",
+          fn);
+  REQUIRE(aligned16(w) && (reinterpret_cast<uintptr_t>(q_fwd) & 7u) == 0 &&
+              (reinterpret_cast<uintptr_t>(q_dgrad) & 7u) == 0,
+          MOE_ERR_UNSUPPORTED, "%s: alignment", fn);
+  return hip_status(moe::launch_quant_weights(w, G, K, N, q_fwd, s_fwd, q_dgrad, s_dgrad,
+                                              as_stream(stream)),
+                    fn);
+}
+
+int64_t moe_padded_rows_bound(int64_t M, int32_t G, int32_t align) {
+  if (M < 0 || G < 1 || align < 1) return 0;
+  const int64_t n = M + static_cast<int64_t>(G) * (align - 1);
+  return (n + align - 1) / align * align;
+}
+
+int moe_padded_offsets(const int64_t* offsets, int32_t G, int64_t M, int32_t align,
+                       int64_t* padded, void* stream) {
+  const char* fn = "moe_padded_offsets";
+  REQUIRE(G >= 1 && M >= 0 && align >= 1, MOE_ERR_SHAPE, "%s: G=%d M=%lld align=%d", fn, G,
+          static_cast<long long>(M), align);
+  REQUIRE(G <= 1024, MOE_ERR_UNSUPPORTED, "%s: G=%d above 1024", fn, G);
+  REQUIRE(offsets && padded, MOE_ERR_NULL, "%s: offsets and padded are required", fn);
+  return hip_status(moe::launch_padded_offsets(offsets, G, M, align, padded, as_stream(stream)), fn);
+}
+
+int moe_quant_fp8_token_tiles(const void* x, const int64_t* offsets, const int64_t* padded,
+                              int32_t G, int64_t M, int64_t K, int64_t ldm, uint8_t* q_t,
+                              float* scale, void* stream) {
+  const char* fn = "moe_quant_fp8_token_tiles";
+  REQUIRE(G >= 1 && M >= 0 && K >= 1 && ldm >= 0, MOE_ERR_SHAPE, "%s: G=%d M=%lld K=%lld ldm=%lld",
+          fn, G, static_cast<long long>(M), static_cast<long long>(K), static_cast<long long>(ldm));
+  REQUIRE(G <= 1024, MOE_ERR_UNSUPPORTED, "%s: G=%d above 1024", fn, G);
+  REQUIRE(K % 128 == 0 && ldm % 128 == 0, MOE_ERR_UNSUPPORTED, "%s: K and ldm must be multiples of 128",
+          fn);
+  REQUIRE(ldm >= moe_padded_rows_bound(M, G, 128), MOE_ERR_SHAPE,
+          "%s: ldm=%lld below the padded bound %lld", fn, static_cast<long long>(ldm),
+          static_cast<long long>(moe_padded_rows_bound(M, G, 128)));
+  REQUIRE(offsets && padded && q_t && scale && (M == 0 || x), MOE_ERR_NULL,
+          "%s: pointers are required", fn);
+  REQUIRE(aligned16(x) && (reinterpret_cast<uintptr_t>(q_t) & 7u) == 0, MOE_ERR_UNSUPPORTED,
+          "%s: alignment", fn);
+  return hip_status(moe::launch_quant_token_tiles(x, offsets, padded, G, M, K, ldm, q_t, scale,
+                                                  as_stream(stream)),
+                    fn);
+}
+
+static int check_gemm_fp8(const char* fn, const void* a, const void* sa, const void* b,
+                          const void* sb, const int64_t* off, int32_t G, int64_t M, int64_t K,
+                          int64_t N) {
+  REQUIRE(G >= 1 && M >= 0 && K >= 1 && N >= 1, MOE_ERR_SHAPE, "%s: G=%d M=%lld K=%lld N=%lld", fn,
+          G, static_cast<long long>(M), static_cast<long long>(K), static_cast<long long>(N));
+  REQUIRE(G <= 1024, MOE_ERR_UNSUPPORTED, "%s: G=%d above 1024", fn, G);
+  REQUIRE(K % 128 == 0 && N % 128 == 0, MOE_ERR_UNSUPPORTED, "%s: K and N must be multiples of 128",
+          fn);
+  REQUIRE(M / 64 + G < (int64_t(1) << 31) / 64, MOE_ERR_UNSUPPORTED, "%s: M too large", fn);
+  if (M == 0) return MOE_OK;
+  REQUIRE(a && sa && b && sb && off, MOE_ERR_NULL, "%s: operands, scales and offsets are required",
+          fn);
+  REQUIRE(aligned16(a) && aligned16(b), MOE_ERR_UNSUPPORTED, "%s: operands must be 16-byte aligned",
+          fn);
+  return MOE_OK;
+}
+
+int moe_grouped_gemm_fp8_fwd(const uint8_t* A, const float* a_scale_t, const uint8_t* B_fwd,
+                             const float* b_scale_fwd, const int64_t* offsets, int32_t G,
+                             int64_t M, int64_t K, int64_t N, int epilogue, void* C, void* H,
+                             void* stream) {
+  const char* fn = "moe_grouped_gemm_fp8_fwd";
+  int st = check_gemm_fp8(fn, A, a_scale_t, B_fwd, b_scale_fwd, offsets, G, M, K, N);
+  if (st != MOE_OK) return st;
+  REQUIRE(epilogue == MOE_EPI_NONE || epilogue == MOE_EPI_SWIGLU, MOE_ERR_SHAPE,
+          "%s: epilogue %d not available in the forward", fn, epilogue);
+  if (epilogue == MOE_EPI_SWIGLU)
+    REQUIRE((N / 2) % 64 == 0, MOE_ERR_UNSUPPORTED, "%s: SWIGLU needs N / 2 %% 64 == 0", fn);
+  if (M == 0) return ok();
+  REQUIRE(epilogue == MOE_EPI_SWIGLU ? H != nullptr : C != nullptr, MOE_ERR_NULL,
+          "%s: output missing", fn);
+  return hip_status(moe::launch_gg_fp8_fwd(A, a_scale_t, B_fwd, b_scale_fwd, offsets, G, M, K, N,
+                                           epilogue, C, H, as_stream(stream)),
+                    fn);
+}
+
+int moe_grouped_gemm_fp8_dgrad(const uint8_t* dC, const float* dc_scale_t, const uint8_t* B_dgrad,
+                               const float* b_scale_dgrad, const int64_t* offsets, int32_t G,
+                               int64_t M, int64_t K, int64_t N, int epilogue, const void* ab,
+                               void* dA, void* stream) {
+  const char* fn = "moe_grouped_gemm_fp8_dgrad";
+  int st = check_gemm_fp8(fn, dC, dc_scale_t, B_dgrad, b_scale_dgrad, offsets, G, M, K, N);
+  if (st != MOE_OK) return st;
+  REQUIRE(epilogue == MOE_EPI_NONE || epilogue == MOE_EPI_SWIGLU_BWD, MOE_ERR_SHAPE,
+          "%s: epilogue %d not available in dgrad", fn, epilogue);
+  if (M == 0) return ok();
+  REQUIRE(dA && (epilogue != MOE_EPI_SWIGLU_BWD || ab), MOE_ERR_NULL, "%s: output missing", fn);
+  return hip_status(moe::launch_gg_fp8_dgrad(dC, dc_scale_t, B_dgrad, b_scale_dgrad, offsets, G, M,
+                                             K, N, epilogue, ab, dA, as_stream(stream)),
+                    fn);
+}
+
+int moe_grouped_gemm_fp8_wgrad(const uint8_t* A_t, const float* a_scale, const uint8_t* dC_t,
+                               const float* dc_scale, const int64_t* padded, int32_t G,
+                               int64_t ldm, int64_t K, int64_t N, int dB_dtype, int accumulate,
+                               void* dB, void* stream) {
+  const char* fn = "moe_grouped_gemm_fp8_wgrad";
+  REQUIRE(G >= 1 && ldm >= 0 && K >= 1 && N >= 1, MOE_ERR_SHAPE, "%s: G=%d ldm=%lld K=%lld N=%lld",
+          fn, G, static_cast<long long>(ldm), static_cast<long long>(K), static_cast<long long>(N));
+  REQUIRE(G <= 1024, MOE_ERR_UNSUPPORTED, "%s: G=%d above 1024", fn, G);
+  REQUIRE(K % 128 == 0 && N % 128 == 0 && ldm % 128 == 0, MOE_ERR_UNSUPPORTED,
+          "%s: K, N and ldm must be multiples of 128", fn);
+  REQUIRE(dB_dtype == MOE_BF16 || dB_dtype == MOE_F32, MOE_ERR_DTYPE, "%s: dB must be bf16 or fp32",
+          fn);
+  REQUIRE(padded && dB && a_scale && dc_scale && (ldm == 0 || (A_t && dC_t)), MOE_ERR_NULL,
+          "%s: pointers are required", fn);
+  REQUIRE(aligned16(A_t) && aligned16(dC_t), MOE_ERR_UNSUPPORTED, "%s: alignment", fn);
+  return hip_status(moe::launch_gg_fp8_wgrad(A_t, a_scale, dC_t, dc_scale, padded, G, ldm, K, N,
+                                             dB_dtype == MOE_F32, accumulate != 0, dB,
+                                             as_stream(stream)),
+                    fn);
+}
+
 }  // extern "C"

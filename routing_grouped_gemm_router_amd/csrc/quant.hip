@@ -1,0 +1,291 @@
+// FP8 E4M3 block quantizers for the fp8 expert GEMMs.
+//
+// Granularity from "Scalable Training of Mixture-of-Experts Models with
+// Megatron Core", section 5, Platform-specific recipes (blockwise FP8): 1 x 128
+// tiles for activations and gradients, 128 x 128 blocks for weights; the
+// weight gradients contract over tokens, so their operands use 128-token x 1
+// tiles with each expert's rows zero-padded to a multiple of 128.
+//
+// Codes: OCP E4M3 ("FN": bias 7, no infinities, 448 the largest finite).
+// Per block: amax = max |v|; scale = amax / 448 and inv = 448 / amax (one IEEE
+// fp32 division each; 1 and 1 when amax = 0); code = nearest E4M3 value of
+// v * inv, ties to the even code, saturated to +-448.
+//
+// Output layouts are chosen for the fp8 GEMM, which reads every operand
+// k-contiguous and every scale as a contiguous vector over a tile's rows:
+//   rows         q [M, K],           scales [K/128, M]
+//   weights      qf [G, N, K] with sf [G, K/128, N]  (forward operand)
+//                qd [G, K, N] with sd [G, N/128, K]  (dgrad operand)
+//                (one 128 x 128 block scale, repeated along the block's rows)
+//   token tiles  qT [K, ldm],        scales [ldm/128, K], rows of group g at
+//                padded offsets poff[g] .. poff[g+1]-1
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+
+// nearest E4M3 code of a finite fp32 value, ties to even, saturating
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  if (a >= 448.0f) return sign | 0x7eu;
+  if (a < 0.015625f) {  // below 2^-6: subnormal step 2^-9 (exact scaling, then RNE)
+    return sign | static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
+  }
+  int e = static_cast<int>((__float_as_uint(a) >> 23) & 0xffu) - 127;  // -6 .. 8
+  float q = __builtin_rintf(ldexpf(a, 3 - e));                         // 8 .. 16
+  if (q >= 16.0f) {
+    q = 8.0f;
+    ++e;
+  }
+  return sign | (static_cast<uint32_t>(e + 7) << 3) | (static_cast<uint32_t>(q) - 8u);
+}
+
+__device__ __forceinline__ void block_scale(float amax, float& scale, float& inv) {
+  if (amax == 0.0f) {
+    scale = 1.0f;
+    inv = 1.0f;
+  } else {
+    scale = __fdiv_rn(amax, 448.0f);
+    inv = __fdiv_rn(448.0f, amax);
+  }
+}
+
+__device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ uint2 encode8(const float (&f)[8], float inv) {
+  uint32_t c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = e4m3_encode(f[i] * inv);
+  return make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                    c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+}
+
+// ---- 1 x 128 tiles along rows: 16 lanes per block, 4 blocks per wave -------
+__global__ __launch_bounds__(256) void quant_rows_kernel(const bf16_t* __restrict__ x, int64_t M,
+                                                         int64_t K, uint8_t* __restrict__ q,
+                                                         float* __restrict__ sT) {
+  const int64_t nb = K / 128;
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t chunks = (nb + 3) / 4;
+  const int64_t row = wid / chunks;
+  if (row >= M) return;
+  const int64_t b = (wid % chunks) * 4 + (lane >> 4);
+  const bool active = b < nb;
+  float f[8] = {};
+  float amax = 0.f;
+  const int64_t off = row * K + b * 128 + (lane & 15) * 8;
+  if (active) {
+    unpack8(*reinterpret_cast<const uint4*>(x + off), f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  }
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  float scale, inv;
+  block_scale(amax, scale, inv);
+  if (active) {
+    *reinterpret_cast<uint2*>(q + off) = encode8(f, inv);
+    if ((lane & 15) == 0) sT[b * M + row] = scale;
+  }
+}
+
+// ---- 128 x 128 weight blocks, written in both operand layouts ----------------
+__global__ __launch_bounds__(256) void quant_weights_kernel(const bf16_t* __restrict__ w, int G,
+                                                            int64_t K, int64_t N,
+                                                            uint8_t* __restrict__ qf,
+                                                            float* __restrict__ sf,
+                                                            uint8_t* __restrict__ qd,
+                                                            float* __restrict__ sd) {
+  __shared__ uint8_t tile[128][128 + 8];
+  __shared__ float red[4];
+  const int64_t nkb = K / 128, nnb = N / 128;
+  const int64_t blk = blockIdx.x;
+  const int64_t g = blk / (nkb * nnb);
+  const int64_t kb = (blk / nnb) % nkb, nb = blk % nnb;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int c8 = (t & 15) * 8, r8 = (t >> 4) * 8;  // 8 columns x 8 rows per thread
+  const bf16_t* src = w + (g * K + kb * 128) * N + nb * 128;
+  float f[8][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    unpack8(*reinterpret_cast<const uint4*>(src + (r8 + i) * N + c8), f[i]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[i][j]));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  if (lane == 0) red[wave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float scale, inv;
+  block_scale(amax, scale, inv);
+  // dgrad layout: same as the input
+  uint8_t* dq = qd + (g * K + kb * 128) * N + nb * 128;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint2 c = encode8(f[i], inv);
+    *reinterpret_cast<uint2*>(dq + (r8 + i) * N + c8) = c;
+    *reinterpret_cast<uint2*>(&tile[r8 + i][c8]) = c;
+  }
+  __syncthreads();
+  // forward layout: transposed through LDS, row n holds 128 k codes
+  uint8_t* fq = qf + (g * N + nb * 128) * K + kb * 128;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int n = (t >> 4) * 8 + i;  // 0..127
+    const int k0 = (t & 15) * 8;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo |= static_cast<uint32_t>(tile[k0 + j][n]) << (8 * j);
+      hi |= static_cast<uint32_t>(tile[k0 + 4 + j][n]) << (8 * j);
+    }
+    *reinterpret_cast<uint2*>(fq + static_cast<int64_t>(n) * K + k0) = make_uint2(lo, hi);
+  }
+  if (t < 128) {
+    sf[(g * nkb + kb) * N + nb * 128 + t] = scale;
+    sd[(g * nnb + nb) * K + kb * 128 + t] = scale;
+  }
+}
+
+// ---- padded group offsets ---------------------------------------------------------
+__global__ __launch_bounds__(1024) void padded_offsets_kernel(const int64_t* __restrict__ off, int G,
+                                                              int64_t M, int64_t align,
+                                                              int64_t* __restrict__ poff) {
+  __shared__ int64_t s[1024];
+  const int g = threadIdx.x;
+  int64_t n = 0;
+  if (g < G) {
+    int64_t lo = off[g], hi = off[g + 1];
+    lo = lo < 0 ? 0 : (lo > M ? M : lo);
+    hi = hi < lo ? lo : (hi > M ? M : hi);
+    n = (hi - lo + align - 1) / align * align;
+  }
+  s[g] = n;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int64_t add = g >= o ? s[g - o] : 0;
+    __syncthreads();
+    s[g] += add;
+    __syncthreads();
+  }
+  if (g < G) poff[g + 1] = s[g];
+  if (g == 0) poff[0] = 0;
+}
+
+// ---- 128-token x 1 tiles, padded per group, written transposed --------------
+// One workgroup per (padded 128-row block, 128 columns).
+__global__ __launch_bounds__(256) void quant_token_tiles_kernel(
+    const bf16_t* __restrict__ x, const int64_t* __restrict__ off,
+    const int64_t* __restrict__ poff, int G, int64_t M, int64_t K, int64_t ldm,
+    uint8_t* __restrict__ qT, float* __restrict__ s) {
+  __shared__ uint8_t tile[128][128 + 8];
+  __shared__ float cmax[16][128];
+  const int64_t rb = blockIdx.y;               // padded row block
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 128;
+  const int64_t prow0 = rb * 128;
+  if (prow0 >= poff[G]) return;
+  // the group whose padded range holds this block
+  int lo_g = 0, hi_g = G;
+  while (hi_g - lo_g > 1) {
+    const int mid = (lo_g + hi_g) >> 1;
+    if (poff[mid] <= prow0) lo_g = mid; else hi_g = mid;
+  }
+  int64_t glo = off[lo_g], ghi = off[lo_g + 1];
+  glo = glo < 0 ? 0 : (glo > M ? M : glo);
+  ghi = ghi < glo ? glo : (ghi > M ? M : ghi);
+  const int64_t row0 = glo + (prow0 - poff[lo_g]);  // first source row of the block
+  const int64_t nvalid = min<int64_t>(128, ghi - row0);
+  const int t = threadIdx.x;
+  const int c8 = (t & 15) * 8, r8 = (t >> 4) * 8;
+  float f[8][8];
+  float mx[8] = {};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (r8 + i < nvalid) {
+      unpack8(*reinterpret_cast<const uint4*>(x + (row0 + r8 + i) * K + c0 + c8), f[i]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[i][j] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mx[j] = fmaxf(mx[j], fabsf(f[i][j]));
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) cmax[t >> 4][c8 + j] = mx[j];
+  __syncthreads();
+  float inv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float a = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) a = fmaxf(a, cmax[r][c8 + j]);
+    float sc;
+    block_scale(a, sc, inv[j]);
+    if ((t >> 4) == 0) s[rb * K + c0 + c8 + j] = sc;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tile[r8 + i][c8 + j] = static_cast<uint8_t>(e4m3_encode(f[i][j] * inv[j]));
+  __syncthreads();
+  // transposed store: column c holds this block's 128 token codes
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = (t >> 4) * 8 + i;
+    const int r0 = (t & 15) * 8;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo |= static_cast<uint32_t>(tile[r0 + j][c]) << (8 * j);
+      hi |= static_cast<uint32_t>(tile[r0 + 4 + j][c]) << (8 * j);
+    }
+    *reinterpret_cast<uint2*>(qT + (c0 + c) * ldm + prow0 + r0) = make_uint2(lo, hi);
+  }
+}
+
+hipError_t launch_quant_rows(const void* x, int64_t M, int64_t K, uint8_t* q, float* sT,
+                             hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  const int64_t waves = M * ((K / 128 + 3) / 4);
+  quant_rows_kernel<<<dim3(static_cast<unsigned>((waves + 3) / 4)), 256, 0, s>>>(
+      static_cast<const bf16_t*>(x), M, K, q, sT);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_weights(const void* w, int G, int64_t K, int64_t N, uint8_t* qf, float* sf,
+                                uint8_t* qd, float* sd, hipStream_t s) {
+  const int64_t blocks = static_cast<int64_t>(G) * (K / 128) * (N / 128);
+  if (blocks == 0) return hipSuccess;
+  quant_weights_kernel<<<dim3(static_cast<unsigned>(blocks)), 256, 0, s>>>(
+      static_cast<const bf16_t*>(w), G, K, N, qf, sf, qd, sd);
+  return hipGetLastError();
+}
+
+hipError_t launch_padded_offsets(const int64_t* off, int G, int64_t M, int64_t align,
+                                 int64_t* poff, hipStream_t s) {
+  padded_offsets_kernel<<<1, 1024, 0, s>>>(off, G, M, align, poff);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_token_tiles(const void* x, const int64_t* off, const int64_t* poff, int G,
+                                    int64_t M, int64_t K, int64_t ldm, uint8_t* qT, float* s,
+                                    hipStream_t st) {
+  if (ldm == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(K / 128), static_cast<unsigned>(ldm / 128));
+  quant_token_tiles_kernel<<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), off, poff, G, M, K,
+                                                 ldm, qT, s);
+  return hipGetLastError();
+}
+
+}  // namespace moe

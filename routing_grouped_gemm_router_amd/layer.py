@@ -13,6 +13,14 @@ their backward, each one or more HIP kernels on the current stream:
             -> moe_grouped_gemm_wgrad [-> shared expert] -> moe_route_topk_bwd
             -> moe_router_logits_bwd -> moe_permute_bwd (+ shared and router dx)
 
+With fp8 expert GEMMs (the blockwise recipe of the same report, section 5)
+every expert-GEMM input is quantized on the way in: activations and gradients
+in 1 x 128 tiles (moe_quant_fp8_rows), weights in 128 x 128 blocks
+(moe_quant_fp8_weights, once per pass), and the operands of the weight
+gradients in 128-token x 1 tiles of each expert's zero-padded rows
+(moe_quant_fp8_token_tiles); routing, permute, SwiGLU and combine stay bf16 /
+fp32.
+
 No step synchronises with the host: per-expert row counts stay on the device
 and every buffer is sized from T * k.  Buffers are allocated once per layer
 and reused across steps.  Python here only allocates and orders the calls.
@@ -106,6 +114,122 @@ class MoELayer:
             self.dxs = emp(T, d)
             self.dws13 = emp(1, d, 2 * fs)
             self.dws2 = emp(1, fs, d)
+        self.fp8 = cfg.gemm == "fp8"
+        if self.fp8:
+            self._alloc_fp8()
+
+    def _alloc_fp8(self):
+        c, dev = self.cfg, self.dev
+        T, d, E, k, f, fs = c.T, c.d, c.E, c.k, c.f, c.fs
+        N = T * k
+        u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)  # noqa: E731
+        f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)  # noqa: E731
+
+        def wq(G, K, Nn):  # both operand layouts of a [G, K, N] weight
+            return dict(qf=u8(G, Nn, K), sf=f32(G, K // 128, Nn), qd=u8(G, K, Nn),
+                        sd=f32(G, Nn // 128, K))
+
+        def rows(M, K):  # 1 x 128 row tiles
+            return dict(q=u8(M, K), s=f32(K // 128, M))
+
+        self.q = dict(w13=wq(E, d, 2 * f), w2=wq(E, f, d), x=rows(N, d), h=rows(N, f),
+                      dy=rows(N, d), dab=rows(N, 2 * f))
+        self.ldm = abi.moe_padded_rows_bound(N, E, 128)
+        self.poff = torch.empty(E + 1, dtype=torch.int64, device=dev)
+
+        def tiles(K, ldm):  # 128-token x 1 tiles, transposed
+            return dict(q=u8(K, ldm), s=f32(ldm // 128, K))
+
+        self.qt = dict(x=tiles(d, self.ldm), dab=tiles(2 * f, self.ldm), h=tiles(f, self.ldm),
+                       dy=tiles(d, self.ldm))
+        if self.shared:
+            self.ldm_s = abi.moe_padded_rows_bound(T, 1, 128)
+            self.poff_all = torch.tensor([0, (T + 127) // 128 * 128], dtype=torch.int64,
+                                         device=dev)
+            self.q.update(ws13=wq(1, d, 2 * fs), ws2=wq(1, fs, d), xs=rows(T, d), hs=rows(T, fs),
+                          douts=rows(T, d), dabs=rows(T, 2 * fs))
+            self.qt.update(xs=tiles(d, self.ldm_s), dabs=tiles(2 * fs, self.ldm_s),
+                           hs=tiles(fs, self.ldm_s), douts=tiles(d, self.ldm_s))
+
+    # --------------------------------------------------------------- fp8 ---
+    def _qrows(self, name, a):
+        abi.moe_quant_fp8_rows(a, self.q[name]["q"], self.q[name]["s"])
+        return self.q[name]["q"], self.q[name]["s"]
+
+    def _qtiles(self, name, a, offsets, poff):
+        t = self.qt[name]
+        abi.moe_quant_fp8_token_tiles(a, offsets, poff, t["q"], t["s"])
+        return t["q"], t["s"]
+
+    def _qweights(self, name, w):
+        t = self.q[name]
+        abi.moe_quant_fp8_weights(w, t["qf"], t["sf"], t["qd"], t["sd"])
+
+    def _forward_fp8(self, x):
+        c, w, q = self.cfg, self.w, self.q
+        with self._span("quant_weights"):
+            self._qweights("w13", w["w13"])
+            self._qweights("w2", w["w2"])
+            if self.shared:
+                self._qweights("ws13", self.ws13)
+                self._qweights("ws2", self.ws2)
+        with self._span("quant_x"):
+            xq, xs = self._qrows("x", self.x_perm)
+        with self._span("gemm1_fwd"):
+            abi.moe_grouped_gemm_fp8_fwd(xq, xs, q["w13"]["qf"], q["w13"]["sf"], self.offsets,
+                                         self.ab, self.h, epilogue=abi.EPI_SWIGLU)
+        with self._span("quant_h"):
+            hq, hs = self._qrows("h", self.h)
+        with self._span("gemm2_fwd"):
+            abi.moe_grouped_gemm_fp8_fwd(hq, hs, q["w2"]["qf"], q["w2"]["sf"], self.offsets, self.y)
+        if self.shared:
+            with self._span("shared_fwd"):
+                xq_, xs_ = self._qrows("xs", x)
+                abi.moe_grouped_gemm_fp8_fwd(xq_, xs_, q["ws13"]["qf"], q["ws13"]["sf"],
+                                             self.off_all, self.abs_, self.hs,
+                                             epilogue=abi.EPI_SWIGLU)
+                hq_, hs_ = self._qrows("hs", self.hs)
+                abi.moe_grouped_gemm_fp8_fwd(hq_, hs_, q["ws2"]["qf"], q["ws2"]["sf"],
+                                             self.off_all, self.ys)
+
+    def _backward_fp8(self, dout):
+        q, x = self.q, self.x
+        with self._span("quant_dy"):
+            dyq, dys = self._qrows("dy", self.dy)
+        with self._span("gemm2_dgrad"):
+            abi.moe_grouped_gemm_fp8_dgrad(dyq, dys, q["w2"]["qd"], q["w2"]["sd"], self.offsets,
+                                           self.dab, epilogue=abi.EPI_SWIGLU_BWD, ab=self.ab)
+        with self._span("quant_tiles_h_dy"):
+            abi.moe_padded_offsets(self.offsets, self.x_perm.shape[0], self.poff)
+            hT, hTs = self._qtiles("h", self.h, self.offsets, self.poff)
+            dyT, dyTs = self._qtiles("dy", self.dy, self.offsets, self.poff)
+        with self._span("gemm2_wgrad"):
+            abi.moe_grouped_gemm_fp8_wgrad(hT, hTs, dyT, dyTs, self.poff, self.dw2)
+        with self._span("quant_dab"):
+            dabq, dabs = self._qrows("dab", self.dab)
+        with self._span("gemm1_dgrad"):
+            abi.moe_grouped_gemm_fp8_dgrad(dabq, dabs, q["w13"]["qd"], q["w13"]["sd"],
+                                           self.offsets, self.dx_perm)
+        with self._span("quant_tiles_x_dab"):
+            xT, xTs = self._qtiles("x", self.x_perm, self.offsets, self.poff)
+            dabT, dabTs = self._qtiles("dab", self.dab, self.offsets, self.poff)
+        with self._span("gemm1_wgrad"):
+            abi.moe_grouped_gemm_fp8_wgrad(xT, xTs, dabT, dabTs, self.poff, self.dw13)
+        if self.shared:
+            with self._span("shared_bwd"):
+                dq, ds = self._qrows("douts", dout)
+                abi.moe_grouped_gemm_fp8_dgrad(dq, ds, q["ws2"]["qd"], q["ws2"]["sd"],
+                                               self.off_all, self.dabs,
+                                               epilogue=abi.EPI_SWIGLU_BWD, ab=self.abs_)
+                a, sa = self._qtiles("hs", self.hs, self.off_all, self.poff_all)
+                b, sb = self._qtiles("douts", dout, self.off_all, self.poff_all)
+                abi.moe_grouped_gemm_fp8_wgrad(a, sa, b, sb, self.poff_all, self.dws2)
+                dq, ds = self._qrows("dabs", self.dabs)
+                abi.moe_grouped_gemm_fp8_dgrad(dq, ds, q["ws13"]["qd"], q["ws13"]["sd"],
+                                               self.off_all, self.dxs)
+                a, sa = self._qtiles("xs", x, self.off_all, self.poff_all)
+                b, sb = self._qtiles("dabs", self.dabs, self.off_all, self.poff_all)
+                abi.moe_grouped_gemm_fp8_wgrad(a, sa, b, sb, self.poff_all, self.dws13)
 
     # ------------------------------------------------------------ forward --
     def _span(self, name):
@@ -122,6 +246,12 @@ class MoELayer:
                                self.route_ws)
         with self._span("permute"):
             abi.moe_permute(x, self.dst_row, self.x_perm)
+        if self.fp8:
+            self._forward_fp8(x)
+            with self._span("combine"):
+                abi.moe_unpermute_combine(self.y, self.topk_w, self.dst_row,
+                                          self.ys if self.shared else None, self.out)
+            return self.out
         with self._span("gemm1_fwd"):
             abi.moe_grouped_gemm_fwd(self.x_perm, w["w13"], self.offsets, self.ab, self.h,
                                      epilogue=abi.EPI_SWIGLU)
@@ -146,6 +276,9 @@ class MoELayer:
         with self._span("combine_bwd"):
             abi.moe_unpermute_combine_bwd(dout, self.y, self.topk_w, self.dst_row, self.dy,
                                           self.d_topk_w)
+        if self.fp8:
+            self._backward_fp8(dout)
+            return self._backward_tail(dout, self.dxs if self.shared else None)
         with self._span("gemm2_dgrad"):
             abi.moe_grouped_gemm_dgrad(self.dy, w["w2"], self.offsets, self.dab,
                                        epilogue=abi.EPI_SWIGLU_BWD, ab=self.ab)
@@ -167,6 +300,10 @@ class MoELayer:
             with self._span("shared_gemm1_wgrad"):
                 abi.moe_grouped_gemm_wgrad(x, self.dabs, self.off_all, self.dws13)
             dxs = self.dxs
+        return self._backward_tail(dout, dxs)
+
+    def _backward_tail(self, dout, dxs):
+        c, w, x = self.cfg, self.w, self.x
         with self._span("route_topk_bwd"):
             abi.moe_route_topk_bwd(self.logits, self.topk_idx, self.topk_w, self.d_topk_w,
                                    self.score, c.renorm, self.d_logits)

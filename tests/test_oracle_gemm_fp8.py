@@ -122,3 +122,58 @@ def test_blockwise_quantizers():
     qw, sw = fp8.quantize_blocks(w)
     assert sw.shape == (2, 3)
     assert np.abs(fp8.dequantize_blocks(qw, sw) - w).max() <= np.abs(w).max() * 2.0 ** -4
+
+
+def test_token_tiles_equal_row_quantizer_on_transpose():
+    """A 128-token x 1 tile is the row quantizer applied to the transposed
+    tile; padding rows are zero codes."""
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((300, 256)) * rng.uniform(0.01, 10, 256)).astype(np.float32)
+    off = np.array([0, 0, 130, 131, 300])
+    q, s, poff = fp8.quantize_token_tiles(x, off)
+    np.testing.assert_array_equal(poff, [0, 0, 256, 384, 640])
+    for g in range(4):
+        lo, hi, plo = off[g], off[g + 1], poff[g]
+        for b in range((hi - lo + 127) // 128):
+            r0, r1 = lo + b * 128, min(hi, lo + b * 128 + 128)
+            tile = np.zeros((128, 256), np.float32)
+            tile[:r1 - r0] = x[r0:r1]
+            qr, sr = fp8.quantize_rows(tile.T, block=128)
+            np.testing.assert_array_equal(q[plo + b * 128:plo + b * 128 + 128].T, qr)
+            np.testing.assert_array_equal(s[plo // 128 + b], sr[:, 0])
+
+
+def test_fp8_layer_chain_without_quantization_is_the_exact_layer():
+    from test_oracle_layer import _make
+    x, w_r, w13, w2, b, shared, dout = _make(5, T=40, d=12, E=4, k=2, f=10, fs=6, bias=True)
+    for score, renorm in [(oracle.SIGMOID, True), (oracle.SOFTMAX, False)]:
+        c = oracle.layer_forward(x, w_r, w13, w2, 2, score, renorm, logit_bias=b, shared=shared)
+        g = oracle.layer_backward(c, dout)
+        e = fp8.layer_fp8(x, w_r, w13, w2, dout, 2, score, renorm, logit_bias=b, shared=shared,
+                          quantize=False)
+        np.testing.assert_allclose(e["out"], c["out"], rtol=0, atol=1e-12)
+        for name in ["dx", "d_logits", "dW_r", "dW13", "dW2", "dWs13", "dWs2"]:
+            np.testing.assert_allclose(e[name], g[name], rtol=0, atol=1e-11, err_msg=name)
+
+
+def test_fp8_layer_chain_close_to_exact_layer():
+    """Sanity check of the chain's quantization error against the exact layer:
+    E4M3 keeps 3 mantissa bits, so a few per cent of max|ref|, well below 20 %.
+    (The 6e-2 bound applies between two quantized computations.)"""
+    from test_oracle_layer import _make
+    x, w_r, w13, w2, b, shared, dout = _make(6, T=150, d=256, E=4, k=2, f=128, fs=128, bias=True)
+    e = fp8.layer_fp8(x, w_r, w13, w2, dout, 2, oracle.SIGMOID, True, logit_bias=b, shared=shared)
+    c = oracle.layer_forward(x, w_r, w13, w2, 2, oracle.SIGMOID, True, logit_bias=b, shared=shared)
+    g = oracle.layer_backward(c, dout)
+    rel = lambda a, r: np.abs(a - r).max() / np.abs(r).max()  # noqa: E731
+    assert 1e-3 < rel(e["out"], c["out"]) < 0.2
+    for name in ["dx", "dW13", "dW2", "dWs13", "dWs2"]:
+        assert 1e-3 < rel(e[name], g[name]) < 0.2, name
+
+
+def test_to_bf16_matches_torch():
+    rng = np.random.default_rng(7)
+    v = np.concatenate([rng.standard_normal(50000) * 10.0 ** rng.integers(-30, 30, 50000),
+                        [0.0, -0.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 65504.0]]).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(fp8.to_bf16(v), ref)
