@@ -11,6 +11,8 @@ HBM before the timed region.  A step is the whole hot path: router, top-k,
 permute, both grouped GEMMs (SwiGLU fused), shared expert, combine, and the
 backward of every one of them.
 
+Also times the fp8 (E4M3 blockwise) variant with ``--config deepseek_v3_fp8``.
+
 Prints ONE JSON line.  ``value`` is the layer's algorithmic FLOP rate (expert
 GEMM FLOPs over the routed rows plus the fp32 router FLOPs, divided by the
 measured time per step).  Per-call times come from HIP events recorded on the
@@ -31,8 +33,8 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer fwd+bwd TFLOPS + permute/combine GB/s on 1 MI355X (roofline %)"
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0    # dense bf16 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0     # dense fp8 MFMA, published
 PEAK_F32_TFLOPS = 157.3      # fp32 vector, published
-RIDGE_BF16 = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 
 
 def parse():
@@ -77,6 +79,9 @@ def kernel_work(cfg, n_nonempty):
         "router_logits_bwd": (4.0 * T * d * E, T * d * s + T * E * 4 + d * E * 4 * 2 + T * d * 4),
         "permute_bwd": (0.0, N * d * s + idx + T * d * (s + 4 + (s if fs else 0))),
     }
+    if cfg.gemm == "fp8":
+        w.update(fp8_work(cfg, n_nonempty))
+        return w
     if fs:
         w.update({
             "shared_gemm1_fwd": (2.0 * T * d * 2 * fs, T * d * s + d * 2 * fs * s + T * 3 * fs * s),
@@ -85,6 +90,59 @@ def kernel_work(cfg, n_nonempty):
             "shared_gemm2_wgrad": (2.0 * T * fs * d, T * fs * s + T * d * s + fs * d * s),
             "shared_gemm1_dgrad": (2.0 * T * 2 * fs * d, T * 2 * fs * s + d * 2 * fs * s + T * d * s),
             "shared_gemm1_wgrad": (2.0 * T * d * 2 * fs, T * d * s + T * 2 * fs * s + d * 2 * fs * s),
+        })
+    return w
+
+
+def fp8_work(cfg, n_nonempty):
+    """FLOPs and bytes of the spans of the fp8 expert path.  Activations are
+    stored in bf16 (2 bytes) and quantized to 1-byte E4M3 codes with one fp32
+    scale per 128 elements before each GEMM; weights are re-quantized every
+    step (they change every step), to two copies (k-contiguous along each
+    GEMM's reduction); GEMM outputs are bf16."""
+    T, d, E, k, f, fs = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.fs
+    N = T * k
+
+    def q(n):            # bytes of n fp8 codes with their block scales
+        return n + n / 128 * 4
+
+    def rows(m, n):      # bf16 in, fp8 rows out
+        return m * n * 2 + q(m * n)
+
+    def wq(n):           # bf16 weight in, two quantized copies out
+        return n * 2 + 2 * q(n)
+
+    w13, w2 = n_nonempty * d * 2 * f, n_nonempty * f * d
+    w = {
+        "quant_weights": (0.0, wq(E * d * 2 * f) + wq(E * f * d)
+                          + (wq(d * 2 * fs) + wq(fs * d) if fs else 0)),
+        "quant_x": (0.0, rows(N, d)),
+        "gemm1_fwd": (2.0 * N * d * 2 * f, q(N * d) + q(w13) + N * 2 * f * 2 + N * f * 2),
+        "quant_h": (0.0, rows(N, f)),
+        "gemm2_fwd": (2.0 * N * f * d, q(N * f) + q(w2) + N * d * 2),
+        "quant_dy": (0.0, rows(N, d)),
+        "gemm2_dgrad": (2.0 * N * d * f, q(N * d) + q(w2) + N * 2 * f * 2 * 2),
+        "quant_tiles_h_dy": (0.0, rows(N, f) + rows(N, d)),
+        "gemm2_wgrad": (2.0 * N * f * d, q(N * f) + q(N * d) + E * f * d * 2),
+        "quant_dab": (0.0, rows(N, 2 * f)),
+        "gemm1_dgrad": (2.0 * N * 2 * f * d, q(N * 2 * f) + q(w13) + N * d * 2),
+        "quant_tiles_x_dab": (0.0, rows(N, d) + rows(N, 2 * f)),
+        "gemm1_wgrad": (2.0 * N * d * 2 * f, q(N * d) + q(N * 2 * f) + E * d * 2 * f * 2),
+    }
+    if fs:
+        w.update({
+            "shared_quant_x": (0.0, rows(T, d)),
+            "shared_gemm1_fwd": (2.0 * T * d * 2 * fs, q(T * d) + q(d * 2 * fs) + T * 3 * fs * 2),
+            "shared_quant_h": (0.0, rows(T, fs)),
+            "shared_gemm2_fwd": (2.0 * T * fs * d, q(T * fs) + q(fs * d) + T * d * 2),
+            "shared_quant_dout": (0.0, rows(T, d)),
+            "shared_gemm2_dgrad": (2.0 * T * d * fs, q(T * d) + q(fs * d) + T * 4 * fs * 2),
+            "shared_quant_tiles_h_dout": (0.0, rows(T, fs) + rows(T, d)),
+            "shared_gemm2_wgrad": (2.0 * T * fs * d, q(T * fs) + q(T * d) + fs * d * 2),
+            "shared_quant_dab": (0.0, rows(T, 2 * fs)),
+            "shared_gemm1_dgrad": (2.0 * T * 2 * fs * d, q(T * 2 * fs) + q(d * 2 * fs) + T * d * 2),
+            "shared_quant_tiles_x_dab": (0.0, rows(T, d) + rows(T, 2 * fs)),
+            "shared_gemm1_wgrad": (2.0 * T * d * 2 * fs, q(T * d) + q(T * 2 * fs) + d * 2 * fs * 2),
         })
     return w
 
@@ -176,9 +234,10 @@ def main():
     from routing_grouped_gemm_router_amd.layer import EventTimer, MoELayer
 
     cfg = inputs.CONFIGS[args.config]
-    if cfg.gemm == "fp8":
-        print(f"{cfg.name}: fp8 expert GEMMs are not available in this build", file=sys.stderr)
+    if cfg.gemm not in ("bf16", "fp8"):
+        print(f"{cfg.name}: bench.py times the bf16 and fp8 expert paths", file=sys.stderr)
         return 2
+    gemm_peak = PEAK_FP8_TFLOPS if cfg.gemm == "fp8" else PEAK_BF16_TFLOPS
     dev = "cuda"
     inp = inputs.layer_inputs(cfg, args.seed, dev)
     layer = MoELayer(cfg, inp, dev)
@@ -222,8 +281,9 @@ def main():
     dom = max(kernels, key=lambda n: kernels[n]["ms"])
     fl, by = work[dom]
     ms = kernels[dom]["ms"]
-    if fl and fl / by >= RIDGE_BF16:
-        roof = {"bound": "mfma", "achieved": round(fl / ms / 1e9, 1), "peak": PEAK_BF16_TFLOPS,
+    ridge = gemm_peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if fl and "gemm" in dom and fl / by >= ridge:
+        roof = {"bound": "mfma", "achieved": round(fl / ms / 1e9, 1), "peak": gemm_peak,
                 "unit": "TFLOP/s"}
     else:
         roof = {"bound": "hbm", "achieved": round(by / ms / 1e6, 1), "peak": PEAK_HBM_GBS,
@@ -253,7 +313,8 @@ def main():
                    "router_bias": cfg.bias, "experts_with_rows": n_nonempty,
                    "max_rows_per_expert": int(counts.max())},
         "grouped_gemm": {"TFLOP/s": round(gemm_flops / gemm_ms / 1e9, 1),
-                         "frac_bf16_peak": round(gemm_flops / gemm_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                         "frac_peak": round(gemm_flops / gemm_ms / 1e9 / gemm_peak, 4),
+                         "peak": gemm_peak,
                          "ms": round(gemm_ms, 3)},
         "permute_combine": {"GB/s": round(pc_bytes / pc_ms / 1e6, 1),
                             "frac_hbm_peak": round(pc_bytes / pc_ms / 1e6 / PEAK_HBM_GBS, 4),

@@ -183,12 +183,15 @@ class MoELayer:
         with self._span("gemm2_fwd"):
             abi.moe_grouped_gemm_fp8_fwd(hq, hs, q["w2"]["qf"], q["w2"]["sf"], self.offsets, self.y)
         if self.shared:
-            with self._span("shared_fwd"):
+            with self._span("shared_quant_x"):
                 xq_, xs_ = self._qrows("xs", x)
+            with self._span("shared_gemm1_fwd"):
                 abi.moe_grouped_gemm_fp8_fwd(xq_, xs_, q["ws13"]["qf"], q["ws13"]["sf"],
                                              self.off_all, self.abs_, self.hs,
                                              epilogue=abi.EPI_SWIGLU)
+            with self._span("shared_quant_h"):
                 hq_, hs_ = self._qrows("hs", self.hs)
+            with self._span("shared_gemm2_fwd"):
                 abi.moe_grouped_gemm_fp8_fwd(hq_, hs_, q["ws2"]["qf"], q["ws2"]["sf"],
                                              self.off_all, self.ys)
 
@@ -216,19 +219,26 @@ class MoELayer:
         with self._span("gemm1_wgrad"):
             abi.moe_grouped_gemm_fp8_wgrad(xT, xTs, dabT, dabTs, self.poff, self.dw13)
         if self.shared:
-            with self._span("shared_bwd"):
+            with self._span("shared_quant_dout"):
                 dq, ds = self._qrows("douts", dout)
+            with self._span("shared_gemm2_dgrad"):
                 abi.moe_grouped_gemm_fp8_dgrad(dq, ds, q["ws2"]["qd"], q["ws2"]["sd"],
                                                self.off_all, self.dabs,
                                                epilogue=abi.EPI_SWIGLU_BWD, ab=self.abs_)
+            with self._span("shared_quant_tiles_h_dout"):
                 a, sa = self._qtiles("hs", self.hs, self.off_all, self.poff_all)
                 b, sb = self._qtiles("douts", dout, self.off_all, self.poff_all)
+            with self._span("shared_gemm2_wgrad"):
                 abi.moe_grouped_gemm_fp8_wgrad(a, sa, b, sb, self.poff_all, self.dws2)
+            with self._span("shared_quant_dab"):
                 dq, ds = self._qrows("dabs", self.dabs)
+            with self._span("shared_gemm1_dgrad"):
                 abi.moe_grouped_gemm_fp8_dgrad(dq, ds, q["ws13"]["qd"], q["ws13"]["sd"],
                                                self.off_all, self.dxs)
+            with self._span("shared_quant_tiles_x_dab"):
                 a, sa = self._qtiles("xs", x, self.off_all, self.poff_all)
                 b, sb = self._qtiles("dabs", self.dabs, self.off_all, self.poff_all)
+            with self._span("shared_gemm1_wgrad"):
                 abi.moe_grouped_gemm_fp8_wgrad(a, sa, b, sb, self.poff_all, self.dws13)
 
     # ------------------------------------------------------------ forward --
