@@ -11,28 +11,34 @@
 //   wgrad    dB[g]      = A[rows g]^T . dC[rows g]
 //
 // Design for gfx950:
-//  * Persistent grid, two 256-thread workgroups per CU (two waves per SIMD:
-//    one issues MFMAs while the other waits on LDS).  Each workgroup builds
-//    the per-group row-tile prefix from the device offsets in LDS (no host
-//    sync), then walks tiles tau = v, v + P, ...; the virtual id v gives the
-//    workgroups of one XCD (workgroup b runs on XCD b mod 8) consecutive tiles,
-//    so the N tiles of one expert row block share that XCD's L2.
+//  * Two tile shapes, both with 64 x 64 per wave and two waves per SIMD (one
+//    issues MFMAs while the other waits on LDS):
+//      narrow: 128 x 128 tiles, 4 waves, two workgroups per CU, each with a
+//              2-stage ring of 32 KiB stages;
+//      wide:   128 x 256 tiles, 8 waves, one workgroup per CU with a 3-stage
+//              ring of 48 KiB stages (two stages in flight while one is
+//              consumed); a quarter less operand traffic per MFMA and half
+//              again as many bytes in flight per CU.  Used whenever the
+//              output width is a multiple of 256.
+//    Persistent grid.  Each workgroup builds the per-group row-tile prefix
+//    from the device offsets in LDS (no host sync), then walks the tiles: the
+//    workgroups of one XCD take windows of consecutive tiles together, so
+//    that a window's operand slabs are fetched into that XCD's L2 once.
 //  * Operands go HBM -> LDS directly (buffer_load ... lds, 16 bytes per lane),
-//    through a 2-stage ring of 32 KiB stages (128 x 64 of A and of B) per
-//    workgroup, so that two workgroups fit in the CU's 160 KiB of LDS.  The ring runs across tile boundaries: the next tile's
-//    first steps load during the current tile's epilogue.  Buffer resources
-//    bound every tile's rows, so rows past a group's end read as zero and
-//    nothing outside the operands is touched.
+//    in slabs of 16 KiB (128 rows x 128 bytes); the ring runs across tile
+//    boundaries: the next tile's first steps load during the current tile's
+//    epilogue.  Buffer resources bound every tile's rows, so rows past a
+//    group's end read as zero and nothing outside the operands is touched.
 //  * Operands that are k-contiguous in memory are stored [row][k] (128 B rows)
 //    and read with ds_read_b128; operands whose contraction axis is strided
 //    (weights in the forward, both operands of wgrad) are stored as in memory,
 //    [k][row] (256 B rows), and read with ds_read_b64_tr_b16, which hands each
 //    lane four k values of its column.  16-byte chunks are XOR-swizzled by row
 //    so that both the DMA writes and the fragment reads spread over all banks.
-//  * 4 waves in a 2 x 2 arrangement, each 64 x 64 = 2 x 2 MFMA 32x32x16 blocks,
+//  * Waves in a 2 x WN arrangement, each 64 x 64 = 2 x 2 MFMA 32x32x16 blocks,
 //    issued as C^T = B^T A^T so that each lane holds 4 consecutive output
-//    columns; the epilogue stages the wave's tile through the ring slot just
-//    consumed and writes 16-byte vectors, 128 bytes per row.
+//    columns; the epilogue stages the wave's tile, 32 rows at a time, through
+//    the ring slot just consumed and writes 16-byte vectors, 128 bytes per row.
 //  * Epilogues: SwiGLU (AB and H = silu(A) * B from the fp32 sums; a tile holds
 //    matching gate and up columns) and SwiGLU backward (dH -> dAB, reading AB).
 //  * fp8: every operand arrives k-contiguous (the quantizers write the layouts
@@ -55,15 +61,32 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128, BN = 128;
-constexpr int STAGES = 2;              // x 2 workgroups per CU
-constexpr int OP_BYTES = 16384;        // one operand of one stage: 128 rows x 128 bytes
-constexpr int SCALE_BYTES = 1024;      // fp8: 128 row scales of A, then 128 of B
+constexpr int BM = 128;
+constexpr int OP_BYTES = 16384;        // one operand slab of one stage: 128 rows x 128 bytes
+
+// Tile shape: 2 x WN waves of 64 x 64; A is one slab, B is BN / 128 slabs.
+template <int WN> struct Cfg {
+  static constexpr int NW = 2 * WN;
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int BN = 64 * WN;
+  static constexpr int B_SLABS = BN / 128;
+  static constexpr int STAGES = WN == 2 ? 2 : 3;
+  static constexpr int WG_PER_CU = WN == 2 ? 2 : 1;
+  static constexpr int A_PER = 16 / NW;            // DMA instructions per wave per stage, A
+  static constexpr int B_PER = 16 * B_SLABS / NW;  // and B
+  // fp8: row scales of A (128), then of B (BN); one 64-float vector per wave
+  static constexpr int SCALE_BYTES = NW * 256;
+};
 
 // k elements per step: 128 bytes of each row
 template <bool F8> struct KStep { static constexpr int value = F8 ? 128 : 64; };
-template <bool F8> constexpr int stage_bytes() { return 2 * OP_BYTES + (F8 ? SCALE_BYTES : 0); }
+template <int WN, bool F8> constexpr int stage_bytes() {
+  return (1 + Cfg<WN>::B_SLABS) * OP_BYTES + (F8 ? Cfg<WN>::SCALE_BYTES : 0);
+}
 constexpr int MAX_GROUPS = 1024;
+// tile patches: row-group modes (chunks of ROW_SN column tiles over all of a
+// group's row tiles), weight gradient (WG_SM x WG_SN)
+constexpr uint32_t ROW_SN = 4, WG_SM = 8, WG_SN = 4;
 constexpr uint32_t RSRC_DW3 = 0x00020000u; // raw buffer, 32-bit elements, bounds-checked
 
 enum Mode { FWD = 0, FWD_SWIGLU = 1, DGRAD = 2, DGRAD_SWIGLU_BWD = 3, WGRAD = 4 };
@@ -149,9 +172,44 @@ __device__ __forceinline__ void wait_barrier(int n) {
   asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ int virtual_block() {
+// Which tiles a workgroup takes.  Workgroup b runs on XCD b mod 8; the Q =
+// P / 8 workgroups of one XCD take the Q consecutive tiles of a window
+// together (so the window's operand slabs meet in that XCD's L2), and XCD x
+// takes windows x, x + 8, x + 16, ...: at any time the XCDs work on
+// neighbouring windows, which keeps their output writes close together in
+// DRAM (starting the XCDs at different points of the list measured slower).
+struct Walk {
+  int64_t Q;   // workgroups per XCD (window size)
+  int x, j;    // XCD, position inside the window
+  int n;       // windows of this XCD
+};
+
+__device__ __forceinline__ Walk make_walk(int64_t total) {
   const int P = gridDim.x, b = blockIdx.x;
-  return (P % 8 == 0) ? (b % 8) * (P / 8) + b / 8 : b;
+  Walk w;
+  if (P % 8 == 0) {
+    w.Q = P / 8;
+    w.x = b % 8;
+    w.j = b / 8;
+    const int64_t W = (total + w.Q - 1) / w.Q;  // windows
+    w.n = static_cast<int>(W > w.x ? (W - w.x + 7) / 8 : 0);
+  } else {
+    w.Q = P;
+    w.x = 0;
+    w.j = b;
+    w.n = static_cast<int>((total + P - 1) / P);
+  }
+  return w;
+}
+
+// the next valid tile at or after step i of the walk; false once it is done
+__device__ __forceinline__ bool walk_next(const Walk& w, int& i, int64_t total, int64_t& tau) {
+  const int stride = w.Q == gridDim.x ? 1 : 8;
+  for (; i < w.n; ++i) {
+    tau = static_cast<int64_t>(w.x + stride * i) * w.Q + w.j;
+    if (tau < total) return true;
+  }
+  return false;
 }
 
 struct Params {
@@ -184,13 +242,16 @@ struct Tile {
   int nk;         // k steps (>= 1)
 };
 
-// Order of a group's tiles: blocks of up to 4 row tiles; inside a block,
-// chunks of 8 column tiles, row-major inside a chunk.  Consecutive tiles,
-// which run on one XCD, then form a 4 x 8 patch that shares 4 row slabs of A
-// and 8 column slabs of B in that XCD's L2.
-__device__ __forceinline__ void tile_in_group(uint32_t tl, uint32_t mt_g, uint32_t NT, uint32_t& m,
-                                              uint32_t& n) {
-  constexpr uint32_t SM = 4, SN = 8;
+// Order of a group's tiles: blocks of up to SM row tiles; inside a block,
+// chunks of SN column tiles, row-major inside a chunk.  The 32 consecutive
+// tiles that one XCD's workgroups take at a time then form a compact patch
+// (about 32 / SN row tiles x SN column tiles) wherever the run starts, so
+// the patch's row slabs of A and column slabs of B are fetched into that
+// XCD's L2 once.  Row-group modes use one block per group (SM = all of the
+// group's row tiles).
+template <uint32_t SN>
+__device__ __forceinline__ void tile_in_group(uint32_t tl, uint32_t mt_g, uint32_t NT, uint32_t SM,
+                                              uint32_t& m, uint32_t& n) {
   const uint32_t blk = tl / (SM * NT);
   const uint32_t r = tl - blk * SM * NT;
   const uint32_t sm = min(SM, mt_g - blk * SM);
@@ -201,9 +262,9 @@ __device__ __forceinline__ void tile_in_group(uint32_t tl, uint32_t mt_g, uint32
   n = chunk * SN + rr % cw;
 }
 
-template <int MODE, bool F8>
+template <int MODE, bool F8, int BN>
 __device__ __forceinline__ bool decode(int64_t tau64, const Params& p, const int* s_pre,
-                                       const int64_t* s_off, int64_t NT64, int64_t total, Tile& t) {
+                                       const int* s_off, int64_t NT64, int64_t total, Tile& t) {
   if (tau64 >= total) return false;
   const uint32_t tau = static_cast<uint32_t>(tau64), NT = static_cast<uint32_t>(NT64);
   if (MODE == WGRAD) {
@@ -211,7 +272,7 @@ __device__ __forceinline__ bool decode(int64_t tau64, const Params& p, const int
     const uint32_t per_g = MT * NT;
     t.g = static_cast<int>(tau / per_g);
     uint32_t m, n;
-    tile_in_group(tau - static_cast<uint32_t>(t.g) * per_g, MT, NT, m, n);
+    tile_in_group<WG_SN>(tau - static_cast<uint32_t>(t.g) * per_g, MT, NT, WG_SM, m, n);
     t.row0 = static_cast<int64_t>(m) * BM;
     t.nt = n;
     t.rows = BM;
@@ -231,7 +292,7 @@ __device__ __forceinline__ bool decode(int64_t tau64, const Params& p, const int
     const uint32_t base = static_cast<uint32_t>(s_pre[g]);
     const uint32_t mt_g = static_cast<uint32_t>(s_pre[g + 1]) - base;
     uint32_t m, n;
-    tile_in_group(tau - base * NT, mt_g, NT, m, n);
+    tile_in_group<ROW_SN>(tau - base * NT, mt_g, NT, mt_g, m, n);
     const int64_t lo = s_off[g], hi = s_off[g + 1];
     t.row0 = lo + static_cast<int64_t>(m) * BM;
     t.nt = n;
@@ -246,9 +307,9 @@ __device__ __forceinline__ bool decode(int64_t tau64, const Params& p, const int
 // Loader state of one tile: buffer resources and this lane's byte offsets
 // for its 4 A and 4 B DMA instructions at k step 0, plus per-step deltas; for
 // fp8 also the one scale-vector instruction of this wave.
-struct Loader {
+template <int WN> struct Loader {
   i32x4_t ra, rb, rs;
-  uint32_t va[4], vb[4], vs;
+  uint32_t va[Cfg<WN>::A_PER], vb[Cfg<WN>::B_PER], vs;
   uint32_t da, db, ds;
 };
 
@@ -259,17 +320,23 @@ template <int MODE, bool F8> struct Layout {
   static constexpr bool B_KC = F8 || MODE == DGRAD || MODE == DGRAD_SWIGLU_BWD;
 };
 
-// B-operand row of tile row rho (0..127): the forward with SwiGLU pairs 64
-// gate columns with the matching 64 up columns
-template <int MODE>
+// B-operand row of tile row rho (0..BN-1): the forward with SwiGLU pairs BN/2
+// gate columns with the matching BN/2 up columns, 32 + 32 per wave
+template <int MODE, int BN>
 __device__ __forceinline__ int64_t b_row(const Tile& t, int rho, int64_t fh) {
-  if (MODE == FWD_SWIGLU) return ((rho >> 5) & 1) * fh + t.nt * 64 + (rho >> 6) * 32 + (rho & 31);
+  if (MODE == FWD_SWIGLU)
+    return ((rho >> 5) & 1) * fh + t.nt * (BN / 2) + (rho >> 6) * 32 + (rho & 31);
   return t.nt * BN + rho;
 }
 
-template <int MODE, bool F8>
+// DMA instruction q of an operand (0 .. 16 x slabs - 1) fills 1 KiB of slab
+// q / 16: in the [row][k] layout rows 8 (q % 16) .. + 7, in the [k][row] layout
+// k rows 4 (q % 16) .. + 3.
+template <int MODE, bool F8, int WN>
 __device__ __forceinline__ void setup_loader(const Params& p, const Tile& t, int wave, int lane,
-                                             Loader& L) {
+                                             Loader<WN>& L) {
+  using C = Cfg<WN>;
+  constexpr int BN = C::BN;
   constexpr int ES = F8 ? 1 : 2;  // element bytes
   constexpr int BK = KStep<F8>::value;
   const int64_t fh = p.Nout / 2;
@@ -279,11 +346,16 @@ __device__ __forceinline__ void setup_loader(const Params& p, const Tile& t, int
     L.ra = make_rsrc(p.A + t.lo * K * ES, static_cast<uint64_t>(t.nrows) * K * ES);
     L.rb = make_rsrc(p.B + t.lo * N * ES, static_cast<uint64_t>(t.nrows) * N * ES);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = wave * 4 + i;
+    for (int i = 0; i < C::A_PER; ++i) {
+      const int q = wave * C::A_PER + i;
       const int kr = 4 * q + (lane >> 4), c = (lane & 15) ^ swz_nc(kr);
       L.va[i] = static_cast<uint32_t>((kr * K + t.row0 + 8 * c) * ES);
-      L.vb[i] = static_cast<uint32_t>((kr * N + t.nt * BN + 8 * c) * ES);
+    }
+#pragma unroll
+    for (int i = 0; i < C::B_PER; ++i) {
+      const int q = wave * C::B_PER + i, slab = q >> 4;
+      const int kr = 4 * (q & 15) + (lane >> 4), c = (lane & 15) ^ swz_nc(kr);
+      L.vb[i] = static_cast<uint32_t>((kr * N + t.nt * BN + slab * 128 + 8 * c) * ES);
     }
     L.da = static_cast<uint32_t>(BK * K * ES);
     L.db = static_cast<uint32_t>(BK * N * ES);
@@ -293,21 +365,29 @@ __device__ __forceinline__ void setup_loader(const Params& p, const Tile& t, int
     // A = X^T codes [Kc, ldm], B = dC^T codes [Nout, ldm]: rows of the tile,
     // contraction over the group's padded token range [lo, lo + nrows)
     const int64_t ldm = p.ldm;
-    const uint64_t na = t.nrows > 0 ? static_cast<uint64_t>(BM) * ldm : 0;
-    L.ra = make_rsrc(p.A + t.row0 * ldm + t.lo, na);
-    L.rb = make_rsrc(p.B + t.nt * BN * ldm + t.lo, na);
+    const bool any = t.nrows > 0;
+    L.ra = make_rsrc(p.A + t.row0 * ldm + t.lo, any ? static_cast<uint64_t>(BM) * ldm : 0);
+    L.rb = make_rsrc(p.B + t.nt * BN * ldm + t.lo, any ? static_cast<uint64_t>(BN) * ldm : 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = wave * 4 + i;
+    for (int i = 0; i < C::A_PER; ++i) {
+      const int q = wave * C::A_PER + i;
       const int r = 8 * q + (lane >> 3), c = (lane & 7) ^ swz_kc(r);
-      L.va[i] = L.vb[i] = static_cast<uint32_t>(r * ldm + c * 16);
+      L.va[i] = static_cast<uint32_t>(r * ldm + c * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < C::B_PER; ++i) {
+      const int q = wave * C::B_PER + i, slab = q >> 4;
+      const int r = 8 * (q & 15) + (lane >> 3), c = (lane & 7) ^ swz_kc(r);
+      L.vb[i] = static_cast<uint32_t>((slab * 128 + r) * ldm + c * 16);
     }
     L.da = L.db = 128;
-    // scales [ldm/128][Kc] and [ldm/128][Nout], block lo/128 + kt
+    // scales [ldm/128][Kc] and [ldm/128][Nout], block lo/128 + kt; waves past
+    // the A and B vectors repeat wave 0's load into their own unused slot
     const int64_t kb0 = t.lo / 128;
-    if (wave < 2) {
+    if (wave < 2 || wave >= 2 + 2 * C::B_SLABS) {
+      const int w = wave < 2 ? wave : 0;
       L.rs = make_rsrc(p.sa, static_cast<uint64_t>(ldm / 128) * p.Kc * 4);
-      L.vs = static_cast<uint32_t>((kb0 * p.Kc + t.row0 + wave * 64 + lane) * 4);
+      L.vs = static_cast<uint32_t>((kb0 * p.Kc + t.row0 + w * 64 + lane) * 4);
       L.ds = static_cast<uint32_t>(p.Kc * 4);
     } else {
       L.rs = make_rsrc(p.sb, static_cast<uint64_t>(ldm / 128) * p.Nout * 4);
@@ -320,8 +400,8 @@ __device__ __forceinline__ void setup_loader(const Params& p, const Tile& t, int
   const int64_t Kc = p.Kc;
   L.ra = make_rsrc(p.A + t.row0 * Kc * ES, static_cast<uint64_t>(t.rows) * Kc * ES);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = wave * 4 + i;
+  for (int i = 0; i < C::A_PER; ++i) {
+    const int q = wave * C::A_PER + i;
     const int r = 8 * q + (lane >> 3), c = (lane & 7) ^ swz_kc(r);
     L.va[i] = static_cast<uint32_t>(r * Kc * ES + c * 16);
   }
@@ -332,10 +412,10 @@ __device__ __forceinline__ void setup_loader(const Params& p, const Tile& t, int
     const char* bg = p.B + static_cast<int64_t>(t.g) * p.Nout * Kc * ES;
     L.rb = make_rsrc(bg, static_cast<uint64_t>(p.Nout) * Kc * ES);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = wave * 4 + i;
-      const int r = 8 * q + (lane >> 3), c = (lane & 7) ^ swz_kc(r);
-      L.vb[i] = static_cast<uint32_t>(b_row<MODE>(t, r, fh) * Kc * ES + c * 16);
+    for (int i = 0; i < C::B_PER; ++i) {
+      const int q = wave * C::B_PER + i, slab = q >> 4;
+      const int r = 8 * (q & 15) + (lane >> 3), c = (lane & 7) ^ swz_kc(r);
+      L.vb[i] = static_cast<uint32_t>(b_row<MODE, BN>(t, slab * 128 + r, fh) * Kc * ES + c * 16);
     }
     L.db = 128;
   } else {
@@ -343,38 +423,41 @@ __device__ __forceinline__ void setup_loader(const Params& p, const Tile& t, int
     const int64_t N = p.Nout;
     L.rb = make_rsrc(p.B + static_cast<int64_t>(t.g) * Kc * N * ES, static_cast<uint64_t>(Kc) * N * ES);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = wave * 4 + i;
-      const int kr = 4 * q + (lane >> 4), c = (lane & 15) ^ swz_nc(kr);
-      L.vb[i] = static_cast<uint32_t>((kr * N + b_row<MODE>(t, 8 * c, fh)) * ES);
+    for (int i = 0; i < C::B_PER; ++i) {
+      const int q = wave * C::B_PER + i, slab = q >> 4;
+      const int kr = 4 * (q & 15) + (lane >> 4), c = (lane & 15) ^ swz_nc(kr);
+      L.vb[i] = static_cast<uint32_t>((kr * N + b_row<MODE, BN>(t, slab * 128 + 8 * c, fh)) * ES);
     }
     L.db = static_cast<uint32_t>(BK * N * ES);
   }
   if (F8) {
-    // scales: A [Kc/128][M] at row row0 + rho; B [G][Kc/128][Nout] at b_row(rho)
+    // scales: A [Kc/128][M] at row row0 + rho; B [G][Kc/128][Nout] at b_row(rho);
+    // waves past the A and B vectors repeat wave 0's load into their own slot
     const int64_t nkb = Kc / 128;
-    if (wave < 2) {
+    if (wave < 2 || wave >= 2 + 2 * C::B_SLABS) {
+      const int w = wave < 2 ? wave : 0;
       L.rs = make_rsrc(p.sa, static_cast<uint64_t>(nkb) * p.M * 4);
-      L.vs = static_cast<uint32_t>((t.row0 + wave * 64 + lane) * 4);
+      L.vs = static_cast<uint32_t>((t.row0 + w * 64 + lane) * 4);
       L.ds = static_cast<uint32_t>(p.M * 4);
     } else {
       L.rs = make_rsrc(p.sb + static_cast<int64_t>(t.g) * nkb * p.Nout,
                        static_cast<uint64_t>(nkb) * p.Nout * 4);
-      L.vs = static_cast<uint32_t>(b_row<MODE>(t, (wave - 2) * 64 + lane, fh) * 4);
+      L.vs = static_cast<uint32_t>(b_row<MODE, BN>(t, (wave - 2) * 64 + lane, fh) * 4);
       L.ds = static_cast<uint32_t>(p.Nout * 4);
     }
   }
 }
 
-template <bool F8>
-__device__ __forceinline__ void issue(const Loader& L, int kt, LDS_AS char* stage, int wave) {
+template <bool F8, int WN>
+__device__ __forceinline__ void issue(const Loader<WN>& L, int kt, LDS_AS char* stage, int wave) {
+  using C = Cfg<WN>;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    dma16(L.ra, stage + (wave * 4 + i) * 1024, L.va[i] + kt * L.da);
+  for (int i = 0; i < C::A_PER; ++i)
+    dma16(L.ra, stage + (wave * C::A_PER + i) * 1024, L.va[i] + kt * L.da);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    dma16(L.rb, stage + OP_BYTES + (wave * 4 + i) * 1024, L.vb[i] + kt * L.db);
-  if (F8) dma4(L.rs, stage + 2 * OP_BYTES + wave * 256, L.vs + kt * L.ds);
+  for (int i = 0; i < C::B_PER; ++i)
+    dma16(L.rb, stage + OP_BYTES + (wave * C::B_PER + i) * 1024, L.vb[i] + kt * L.db);
+  if (F8) dma4(L.rs, stage + (1 + C::B_SLABS) * OP_BYTES + wave * 256, L.vs + kt * L.ds);
 }
 
 // ---- fragment reads ----------------------------------------------------------
@@ -412,13 +495,13 @@ __device__ __forceinline__ bf16x8_t frag_nc(const LDS_AS char* op, int col_base,
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// opB points at the wave's B slab; wnl is the wave's 64-column half in it
 template <int MODE>
-__device__ __forceinline__ void compute_stage_bf16(f32x16_t (&acc)[2][2], const LDS_AS char* stage,
-                                                   int wm, int wn, int lane) {
+__device__ __forceinline__ void compute_stage_bf16(f32x16_t (&acc)[2][2], const LDS_AS char* opA,
+                                                   const LDS_AS char* opB, int wm, int wnl,
+                                                   int lane) {
   constexpr bool A_NC = !Layout<MODE, false>::A_KC;
   constexpr bool B_NC = !Layout<MODE, false>::B_KC;
-  const LDS_AS char* opA = stage;
-  const LDS_AS char* opB = stage + OP_BYTES;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     bf16x8_t a[2], b[2];
@@ -428,8 +511,8 @@ __device__ __forceinline__ void compute_stage_bf16(f32x16_t (&acc)[2][2], const 
                    : frag_kc(opA, wm * 64 + ii * 32 + (lane & 31), kk * 2 + (lane >> 5));
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
-      b[jj] = B_NC ? frag_nc(opB, wn * 64 + jj * 32, kk * 16, lane)
-                   : frag_kc(opB, wn * 64 + jj * 32 + (lane & 31), kk * 2 + (lane >> 5));
+      b[jj] = B_NC ? frag_nc(opB, wnl * 64 + jj * 32, kk * 16, lane)
+                   : frag_kc(opB, wnl * 64 + jj * 32 + (lane & 31), kk * 2 + (lane >> 5));
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
@@ -442,12 +525,10 @@ __device__ __forceinline__ void compute_stage_bf16(f32x16_t (&acc)[2][2], const 
 // block; each partial is promoted as acc += partial * scale_A(row) *
 // scale_B(column) (the scale is constant over the block, so promoting the two
 // halves separately is the same sum and keeps half the fragments live)
-__device__ __forceinline__ void compute_stage_fp8(f32x16_t (&acc)[2][2], const LDS_AS char* stage,
-                                                  int wm, int wn, int lane) {
-  const LDS_AS char* opA = stage;
-  const LDS_AS char* opB = stage + OP_BYTES;
-  const LDS_AS float* sA = (const LDS_AS float*)(stage + 2 * OP_BYTES);
-  const LDS_AS float* sB = sA + 128;
+__device__ __forceinline__ void compute_stage_fp8(f32x16_t (&acc)[2][2], const LDS_AS char* opA,
+                                                  const LDS_AS char* opB, const LDS_AS float* sA,
+                                                  int wm, int wn, int wnl, int lane) {
+  const LDS_AS float* sB = sA + BM;
   const int h = lane >> 5;
   float sa[2];
 #pragma unroll
@@ -458,7 +539,7 @@ __device__ __forceinline__ void compute_stage_fp8(f32x16_t (&acc)[2][2], const L
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) a[ii] = frag_kc8(opA, wm * 64 + ii * 32 + (lane & 31), 4 * s + 2 * h);
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) b[jj] = frag_kc8(opB, wn * 64 + jj * 32 + (lane & 31), 4 * s + 2 * h);
+    for (int jj = 0; jj < 2; ++jj) b[jj] = frag_kc8(opB, wnl * 64 + jj * 32 + (lane & 31), 4 * s + 2 * h);
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
       f32x4 sb[4];
@@ -482,19 +563,24 @@ __device__ __forceinline__ void compute_stage_fp8(f32x16_t (&acc)[2][2], const L
   }
 }
 
-template <int MODE, bool F8>
+template <int MODE, bool F8, int WN>
 __device__ __forceinline__ void compute_stage(f32x16_t (&acc)[2][2], const LDS_AS char* stage,
                                               int wm, int wn, int lane) {
+  const LDS_AS char* opA = stage;
+  const LDS_AS char* opB = stage + OP_BYTES * (1 + (wn >> 1));
   if (F8)
-    compute_stage_fp8(acc, stage, wm, wn, lane);
+    compute_stage_fp8(acc, opA, opB,
+                      (const LDS_AS float*)(stage + (1 + Cfg<WN>::B_SLABS) * OP_BYTES), wm, wn,
+                      wn & 1, lane);
   else
-    compute_stage_bf16<MODE>(acc, stage, wm, wn, lane);
+    compute_stage_bf16<MODE>(acc, opA, opB, wm, wn & 1, lane);
 }
 
 // ---- epilogue ------------------------------------------------------------------
 // acc[ii][jj][v] = C[m][n], m = wm*64 + ii*32 + (lane & 31),
 //                          n = wn*64 + jj*32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3).
-// Staging per wave: [64 m][64 n] bf16 (128 B rows, chunks swizzled by m & 7).
+// Staging per wave: 4 KiB = [32 m][64 n] bf16 (128 B rows, chunks swizzled by
+// m & 7), one half (ii) of the wave's rows at a time.
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
@@ -502,21 +588,20 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 
 __device__ __forceinline__ int stg_off(int m, int chunk) { return m * 128 + ((chunk ^ (m & 7)) << 4); }
 
-// write the wave's acc (columns [jj0, jj0 + njj) blocks) into staging as bf16
-__device__ __forceinline__ void stage_acc(LDS_AS char* stg, const f32x16_t (&acc)[2][2], int lane) {
+// write rows ii*32 .. ii*32+31 of the wave's acc into staging as bf16
+__device__ __forceinline__ void stage_acc(LDS_AS char* stg, const f32x16_t (&acc)[2][2], int ii,
+                                          int lane) {
 #pragma unroll
-  for (int ii = 0; ii < 2; ++ii)
+  for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-      for (int vg = 0; vg < 4; ++vg) {
-        const int m = ii * 32 + (lane & 31);
-        const int n = jj * 32 + vg * 8 + (lane >> 5) * 4;
-        u32x2_t w;
-        w.x = pack2(acc[ii][jj][vg * 4 + 0], acc[ii][jj][vg * 4 + 1]);
-        w.y = pack2(acc[ii][jj][vg * 4 + 2], acc[ii][jj][vg * 4 + 3]);
-        *(LDS_AS u32x2_t*)(stg + stg_off(m, n >> 3) + (n & 7) * 2) = w;
-      }
+    for (int vg = 0; vg < 4; ++vg) {
+      const int m = lane & 31;
+      const int n = jj * 32 + vg * 8 + (lane >> 5) * 4;
+      u32x2_t w;
+      w.x = pack2(acc[ii][jj][vg * 4 + 0], acc[ii][jj][vg * 4 + 1]);
+      w.y = pack2(acc[ii][jj][vg * 4 + 2], acc[ii][jj][vg * 4 + 3]);
+      *(LDS_AS u32x2_t*)(stg + stg_off(m, n >> 3) + (n & 7) * 2) = w;
+    }
 }
 
 __device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
@@ -532,7 +617,7 @@ __device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
   return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
 }
 
-template <int MODE>
+template <int MODE, int BN>
 __device__ __forceinline__ void epilogue(const Params& p, const Tile& t, const f32x16_t (&acc)[2][2],
                                          LDS_AS char* stg, int wm, int wn, int lane) {
   const int rows_w = MODE == WGRAD ? 64 : t.rows - wm * 64;  // valid rows of this wave
@@ -559,68 +644,68 @@ __device__ __forceinline__ void epilogue(const Params& p, const Tile& t, const f
         }
     return;
   }
-  stage_acc(stg, acc, lane);
   const int64_t fh = p.Nout / 2;
-  // 64 rows x 8 chunks; lane handles chunks lane + 64 i
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int idx = lane + 64 * i;
-    const int m = idx >> 3, c = idx & 7;
-    if (m >= rows_w) continue;
-    const u32x4_t vv = *(const LDS_AS u32x4_t*)(stg + stg_off(m, c));
-    const uint4 v = make_uint4(vv.x, vv.y, vv.z, vv.w);
-    const int64_t row = t.row0 + wm * 64 + m;
-    if (MODE == FWD) {
-      bf16_t* C = static_cast<bf16_t*>(p.C);
-      *reinterpret_cast<uint4*>(C + row * p.Nout + t.nt * BN + wn * 64 + 8 * c) = v;
-    } else if (MODE == FWD_SWIGLU) {
-      if (p.C) {
-        bf16_t* C = static_cast<bf16_t*>(p.C);
-        const int64_t col = (c >> 2) * fh + t.nt * 64 + wn * 32 + (c & 3) * 8;
-        *reinterpret_cast<uint4*>(C + row * p.Nout + col) = v;
-      }
-    } else if (MODE == DGRAD) {
-      bf16_t* C = static_cast<bf16_t*>(p.C);
-      *reinterpret_cast<uint4*>(C + row * p.Nout + t.nt * BN + wn * 64 + 8 * c) = v;
-    } else if (MODE == DGRAD_SWIGLU_BWD) {
-      // v = dH[row, col .. col+7]; read the matching a and b, write dA and dB
-      const int64_t col = t.nt * BN + wn * 64 + 8 * c;
-      const int64_t w2 = 2 * p.Nout;
-      float dh[8], a[8], b[8], da[8], db[8];
-      unpack8(v, dh);
-      unpack8(*reinterpret_cast<const uint4*>(p.ab + row * w2 + col), a);
-      unpack8(*reinterpret_cast<const uint4*>(p.ab + row * w2 + p.Nout + col), b);
+  for (int ii = 0; ii < 2; ++ii) {
+    if (ii * 32 >= rows_w) break;
+    const bool store_c = MODE != FWD_SWIGLU || p.C != nullptr;
+    if (store_c) {
+      stage_acc(stg, acc, ii, lane);
+      // 32 rows x 8 chunks; lane handles chunks lane + 64 i
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float s = 1.0f / (1.0f + expf(-a[e]));
-        da[e] = dh[e] * b[e] * s * (1.0f + a[e] * (1.0f - s));
-        db[e] = dh[e] * a[e] * s;
-      }
-      bf16_t* C = static_cast<bf16_t*>(p.C);
-      *reinterpret_cast<uint4*>(C + row * w2 + col) = pack8(da);
-      *reinterpret_cast<uint4*>(C + row * w2 + p.Nout + col) = pack8(db);
-    } else {  // WGRAD, bf16 out
-      bf16_t* C = static_cast<bf16_t*>(p.C) + static_cast<int64_t>(t.g) * p.Kc * p.Nout;
-      uint4* q = reinterpret_cast<uint4*>(C + row * p.Nout + t.nt * BN + wn * 64 + 8 * c);
-      if (p.accumulate) {
-        float x[8], y[8];
-        unpack8(v, x);
-        unpack8(*q, y);
+      for (int i = 0; i < 4; ++i) {
+        const int idx = lane + 64 * i;
+        const int m = idx >> 3, c = idx & 7;
+        if (ii * 32 + m >= rows_w) continue;
+        const u32x4_t vv = *(const LDS_AS u32x4_t*)(stg + stg_off(m, c));
+        const uint4 v = make_uint4(vv.x, vv.y, vv.z, vv.w);
+        const int64_t row = t.row0 + wm * 64 + ii * 32 + m;
+        if (MODE == FWD || MODE == DGRAD) {
+          bf16_t* C = static_cast<bf16_t*>(p.C);
+          *reinterpret_cast<uint4*>(C + row * p.Nout + t.nt * BN + wn * 64 + 8 * c) = v;
+        } else if (MODE == FWD_SWIGLU) {
+          bf16_t* C = static_cast<bf16_t*>(p.C);
+          const int64_t col = (c >> 2) * fh + t.nt * (BN / 2) + wn * 32 + (c & 3) * 8;
+          *reinterpret_cast<uint4*>(C + row * p.Nout + col) = v;
+        } else if (MODE == DGRAD_SWIGLU_BWD) {
+          // v = dH[row, col .. col+7]; read the matching a and b, write dA and dB
+          const int64_t col = t.nt * BN + wn * 64 + 8 * c;
+          const int64_t w2 = 2 * p.Nout;
+          float dh[8], a[8], b[8], da[8], db[8];
+          unpack8(v, dh);
+          unpack8(*reinterpret_cast<const uint4*>(p.ab + row * w2 + col), a);
+          unpack8(*reinterpret_cast<const uint4*>(p.ab + row * w2 + p.Nout + col), b);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] += y[e];
-        *q = pack8(x);
-      } else {
-        *q = v;
+          for (int e = 0; e < 8; ++e) {
+            const float sg = 1.0f / (1.0f + expf(-a[e]));
+            da[e] = dh[e] * b[e] * sg * (1.0f + a[e] * (1.0f - sg));
+            db[e] = dh[e] * a[e] * sg;
+          }
+          bf16_t* C = static_cast<bf16_t*>(p.C);
+          *reinterpret_cast<uint4*>(C + row * w2 + col) = pack8(da);
+          *reinterpret_cast<uint4*>(C + row * w2 + p.Nout + col) = pack8(db);
+        } else {  // WGRAD, bf16 out
+          bf16_t* C = static_cast<bf16_t*>(p.C) + static_cast<int64_t>(t.g) * p.Kc * p.Nout;
+          uint4* q = reinterpret_cast<uint4*>(C + row * p.Nout + t.nt * BN + wn * 64 + 8 * c);
+          if (p.accumulate) {
+            float x[8], y[8];
+            unpack8(v, x);
+            unpack8(*q, y);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] += y[e];
+            *q = pack8(x);
+          } else {
+            // streaming store: the gradient is not read again by this layer
+            __builtin_nontemporal_store(vv, reinterpret_cast<u32x4_t*>(q));
+          }
+        }
       }
     }
-  }
-  if (MODE == FWD_SWIGLU) {
-    // second pass: H = silu(gate) * up, 32 columns per wave
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
+    if (MODE == FWD_SWIGLU) {
+      // H = silu(gate) * up for these 32 rows: 32 columns per wave
 #pragma unroll
       for (int vg = 0; vg < 4; ++vg) {
-        const int m = ii * 32 + (lane & 31);
+        const int m = lane & 31;
         const int n = vg * 8 + (lane >> 5) * 4;
         float h[4];
 #pragma unroll
@@ -634,49 +719,52 @@ __device__ __forceinline__ void epilogue(const Params& p, const Tile& t, const f
         *(LDS_AS u32x2_t*)(stg + stg_off(m, n >> 3) + (n & 7) * 2) = w;
       }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = lane + 64 * i;
-      const int m = idx >> 2, c = idx & 3;
-      if (m >= rows_w) continue;
-      const u32x4_t vv = *(const LDS_AS u32x4_t*)(stg + stg_off(m, c));
-      const uint4 v = make_uint4(vv.x, vv.y, vv.z, vv.w);
-      const int64_t row = t.row0 + wm * 64 + m;
-      *reinterpret_cast<uint4*>(p.H + row * fh + t.nt * 64 + wn * 32 + 8 * c) = v;
+      for (int i = 0; i < 2; ++i) {
+        const int idx = lane + 64 * i;
+        const int m = idx >> 2, c = idx & 3;
+        if (ii * 32 + m >= rows_w) continue;
+        const u32x4_t vv = *(const LDS_AS u32x4_t*)(stg + stg_off(m, c));
+        const uint4 v = make_uint4(vv.x, vv.y, vv.z, vv.w);
+        const int64_t row = t.row0 + wm * 64 + ii * 32 + m;
+        *reinterpret_cast<uint4*>(p.H + row * fh + t.nt * (BN / 2) + wn * 32 + 8 * c) = v;
+      }
     }
   }
 }
 
 // ---- the kernel ----------------------------------------------------------------
 
-template <int MODE, bool F8>
-__global__ __launch_bounds__(256, 2) void gg_kernel(Params p) {
-  constexpr int SB = stage_bytes<F8>();
-  constexpr int PER = F8 ? 9 : 8;  // DMA instructions per wave per stage
-  __shared__ __attribute__((aligned(1024))) char ring[STAGES * SB];
+template <int MODE, bool F8, int WN>
+__global__ __launch_bounds__(Cfg<WN>::THREADS, Cfg<WN>::WG_PER_CU) void gg_kernel(Params p) {
+  using C = Cfg<WN>;
+  constexpr int BN = C::BN;
+  constexpr int NTH = C::THREADS;
+  constexpr int SB = stage_bytes<WN, F8>();
+  constexpr int PER = C::A_PER + C::B_PER + (F8 ? 1 : 0);  // DMA instructions per wave per stage
+  __shared__ __attribute__((aligned(1024))) char ring[C::STAGES * SB];
   __shared__ int s_pre[MAX_GROUPS + 1];
-  __shared__ int64_t s_off[MAX_GROUPS + 1];
+  __shared__ int s_off[MAX_GROUPS + 1];  // row offsets (below 2^31)
   LDS_AS char* lring = (LDS_AS char*)(ring);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
 
   // group offsets, clamped to a non-decreasing sequence in [0, M], kept in LDS
   // so that tile decoding never waits on vector memory
-  for (int g = tid; g <= p.G; g += 256) s_off[g] = clamp64(p.off[g], 0, p.M);
+  for (int g = tid; g <= p.G; g += NTH) s_off[g] = static_cast<int>(clamp64(p.off[g], 0, p.M));
   __syncthreads();
   if (wave == 0) {  // running maximum makes the offsets non-decreasing
     const int per = (p.G + 1 + 63) / 64;
     const int g0 = lane * per, g1 = min(p.G + 1, g0 + per);
-    int64_t mx = 0;
+    int mx = 0;
     for (int g = g0; g < g1; ++g) mx = max(mx, s_off[g]);
-    int64_t incl = mx;
+    int incl = mx;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const int64_t y = __shfl_up(incl, o, 64);
+      const int y = __shfl_up(incl, o, 64);
       if (lane >= o) incl = max(incl, y);
     }
-    int64_t run = incl;
-    run = __shfl_up(incl, 1, 64);
+    int run = __shfl_up(incl, 1, 64);
     if (lane == 0) run = 0;
     for (int g = g0; g < g1; ++g) {
       run = max(run, s_off[g]);
@@ -694,7 +782,7 @@ __global__ __launch_bounds__(256, 2) void gg_kernel(Params p) {
       const int per = (p.G + 63) / 64;
       const int g0 = lane * per, g1 = min(p.G, g0 + per);
       int sum = 0;
-      for (int g = g0; g < g1; ++g) sum += static_cast<int>((s_off[g + 1] - s_off[g] + BM - 1) / BM);
+      for (int g = g0; g < g1; ++g) sum += (s_off[g + 1] - s_off[g] + BM - 1) / BM;
       int incl = sum;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -704,36 +792,40 @@ __global__ __launch_bounds__(256, 2) void gg_kernel(Params p) {
       int run = incl - sum;
       for (int g = g0; g < g1; ++g) {
         s_pre[g] = run;
-        run += static_cast<int>((s_off[g + 1] - s_off[g] + BM - 1) / BM);
+        run += (s_off[g + 1] - s_off[g] + BM - 1) / BM;
       }
       if (lane == 63) s_pre[p.G] = incl;
     }
     __syncthreads();
-    NT = MODE == FWD_SWIGLU ? p.Nout / 128 : p.Nout / BN;
+    NT = p.Nout / BN;
     total = static_cast<int64_t>(s_pre[p.G]) * NT;
   }
 
-  const int P = gridDim.x;
-  int64_t ld_tau = virtual_block(), cp_tau = ld_tau;
+  const Walk walk = make_walk(total);
+  int ld_i = 0, cp_i = 0;
+  int64_t ld_tau = 0;
   Tile ld_t, cp_t;
-  bool ld_ok = decode<MODE, F8>(ld_tau, p, s_pre, s_off, NT, total, ld_t);
+  bool ld_ok = walk_next(walk, ld_i, total, ld_tau) &&
+               decode<MODE, F8, BN>(ld_tau, p, s_pre, s_off, NT, total, ld_t);
   bool cp_ok = ld_ok;
   cp_t = ld_t;
-  Loader L;
-  if (ld_ok) setup_loader<MODE, F8>(p, ld_t, wave, lane, L);
+  cp_i = ld_i;
+  Loader<WN> L;
+  if (ld_ok) setup_loader<MODE, F8, WN>(p, ld_t, wave, lane, L);
   int ld_kt = 0, cp_kt = 0;
   int inflight = 0, ld_slot = 0, cp_slot = 0;
 
   // prologue: STAGES - 1 steps in flight
-  for (int s = 0; s < STAGES - 1 && ld_ok; ++s) {
-    issue<F8>(L, ld_kt, lring + ld_slot * SB, wave);
+  for (int s = 0; s < C::STAGES - 1 && ld_ok; ++s) {
+    issue<F8, WN>(L, ld_kt, lring + ld_slot * SB, wave);
     ++inflight;
-    ld_slot = ld_slot + 1 == STAGES ? 0 : ld_slot + 1;
+    ld_slot = ld_slot + 1 == C::STAGES ? 0 : ld_slot + 1;
     if (++ld_kt == ld_t.nk) {
       ld_kt = 0;
-      ld_tau += P;
-      ld_ok = decode<MODE, F8>(ld_tau, p, s_pre, s_off, NT, total, ld_t);
-      if (ld_ok) setup_loader<MODE, F8>(p, ld_t, wave, lane, L);
+      ++ld_i;
+      ld_ok = walk_next(walk, ld_i, total, ld_tau) &&
+              decode<MODE, F8, BN>(ld_tau, p, s_pre, s_off, NT, total, ld_t);
+      if (ld_ok) setup_loader<MODE, F8, WN>(p, ld_t, wave, lane, L);
     }
   }
 
@@ -746,19 +838,22 @@ __global__ __launch_bounds__(256, 2) void gg_kernel(Params p) {
       for (int v = 0; v < 16; ++v) acc[ii][jj][v] = 0.f;
 
   while (cp_ok) {
-    wait_barrier<PER>(inflight - 1);  // this step's stage has landed in LDS for all waves
-    if (ld_ok) {                 // refill the slot consumed in the previous step
-      issue<F8>(L, ld_kt, lring + ld_slot * SB, wave);
+    // this step's stage has landed in LDS for all waves (at most one younger
+    // stage of this wave still outstanding)
+    wait_barrier<PER>(inflight - 1);
+    if (ld_ok) {  // refill the slot consumed in the previous step
+      issue<F8, WN>(L, ld_kt, lring + ld_slot * SB, wave);
       ++inflight;
-      ld_slot = ld_slot + 1 == STAGES ? 0 : ld_slot + 1;
+      ld_slot = ld_slot + 1 == C::STAGES ? 0 : ld_slot + 1;
       if (++ld_kt == ld_t.nk) {
         ld_kt = 0;
-        ld_tau += P;
-        ld_ok = decode<MODE, F8>(ld_tau, p, s_pre, s_off, NT, total, ld_t);
-        if (ld_ok) setup_loader<MODE, F8>(p, ld_t, wave, lane, L);
+        ++ld_i;
+        ld_ok = walk_next(walk, ld_i, total, ld_tau) &&
+                decode<MODE, F8, BN>(ld_tau, p, s_pre, s_off, NT, total, ld_t);
+        if (ld_ok) setup_loader<MODE, F8, WN>(p, ld_t, wave, lane, L);
       }
     }
-    compute_stage<MODE, F8>(acc, lring + cp_slot * SB, wm, wn, lane);
+    compute_stage<MODE, F8, WN>(acc, lring + cp_slot * SB, wm, wn, lane);
     --inflight;
     if (++cp_kt == cp_t.nk) {
       // the slot just consumed is not refilled before the next barrier: stage
@@ -766,7 +861,7 @@ __global__ __launch_bounds__(256, 2) void gg_kernel(Params p) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      epilogue<MODE>(p, cp_t, acc, lring + cp_slot * SB + wave * 8192, wm, wn, lane);
+      epilogue<MODE, BN>(p, cp_t, acc, lring + cp_slot * SB + wave * 4096, wm, wn, lane);
 #pragma unroll
       for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
@@ -774,26 +869,42 @@ __global__ __launch_bounds__(256, 2) void gg_kernel(Params p) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[ii][jj][v] = 0.f;
       cp_kt = 0;
-      cp_tau += P;
-      cp_ok = decode<MODE, F8>(cp_tau, p, s_pre, s_off, NT, total, cp_t);
+      // the compute cursor follows the loader's walk one tile behind
+      ++cp_i;
+      int64_t cp_tau = 0;
+      cp_ok = walk_next(walk, cp_i, total, cp_tau) &&
+              decode<MODE, F8, BN>(cp_tau, p, s_pre, s_off, NT, total, cp_t);
     }
-    cp_slot = cp_slot + 1 == STAGES ? 0 : cp_slot + 1;
+    cp_slot = cp_slot + 1 == C::STAGES ? 0 : cp_slot + 1;
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-static unsigned persistent_grid(int64_t tiles_upper_bound) {
-  int64_t p = static_cast<int64_t>(cu_count()) * 2;  // two resident workgroups per CU
-  if (tiles_upper_bound < p) p = tiles_upper_bound;
-  if (p < 1) p = 1;
-  return static_cast<unsigned>(p);
+template <int MODE, bool F8, int WN>
+static hipError_t run_cfg(const Params& p, int64_t tiles_upper_bound, hipStream_t s) {
+  if (tiles_upper_bound <= 0) return hipSuccess;
+  int64_t grid = static_cast<int64_t>(cu_count()) * Cfg<WN>::WG_PER_CU;  // persistent
+  if (tiles_upper_bound < grid) grid = tiles_upper_bound;
+  if (grid < 1) grid = 1;
+  gg_kernel<MODE, F8, WN><<<dim3(static_cast<unsigned>(grid)), Cfg<WN>::THREADS, 0, s>>>(p);
+  return hipGetLastError();
 }
 
+// Row-group modes: tiles of BM rows of a group x BN product columns (SwiGLU:
+// BN/2 gate + BN/2 up columns); at most M/BM + G row tiles.  The wide tile
+// whenever the product width allows it.
 template <int MODE, bool F8>
-static hipError_t run(const Params& p, int64_t tiles_upper_bound, hipStream_t s) {
-  if (tiles_upper_bound <= 0) return hipSuccess;
-  gg_kernel<MODE, F8><<<dim3(persistent_grid(tiles_upper_bound)), 256, 0, s>>>(p);
-  return hipGetLastError();
+static hipError_t run_rows(const Params& p, hipStream_t s) {
+  const int64_t mt = p.M / BM + p.G;
+  if (p.Nout % 256 == 0) return run_cfg<MODE, F8, 4>(p, mt * (p.Nout / 256), s);
+  return run_cfg<MODE, F8, 2>(p, mt * (p.Nout / 128), s);
+}
+
+template <bool F8>
+static hipError_t run_wgrad(const Params& p, hipStream_t s) {
+  const int64_t mt = static_cast<int64_t>(p.G) * (p.Kc / BM);
+  if (p.Nout % 256 == 0) return run_cfg<WGRAD, F8, 4>(p, mt * (p.Nout / 256), s);
+  return run_cfg<WGRAD, F8, 2>(p, mt * (p.Nout / 128), s);
 }
 
 static Params make_params(const void* A, const void* B, const int64_t* off, int G, int64_t M,
@@ -816,9 +927,8 @@ hipError_t launch_gg_bf16_fwd(const void* A, const void* B, const int64_t* off, 
                               int64_t K, int64_t N, int epi, void* C, void* H, hipStream_t s) {
   if (M == 0) return hipSuccess;
   const Params p = make_params(A, B, off, G, M, K, N, C, H, nullptr);
-  const int64_t nt = N / BN;
-  if (epi == EPI_SWIGLU) return run<FWD_SWIGLU, false>(p, (M / BM + G) * nt, s);
-  return run<FWD, false>(p, (M / BM + G) * nt, s);
+  if (epi == EPI_SWIGLU) return run_rows<FWD_SWIGLU, false>(p, s);
+  return run_rows<FWD, false>(p, s);
 }
 
 hipError_t launch_gg_bf16_dgrad(const void* dC, const void* B, const int64_t* off, int G,
@@ -827,8 +937,8 @@ hipError_t launch_gg_bf16_dgrad(const void* dC, const void* B, const int64_t* of
   if (M == 0) return hipSuccess;
   // contraction over N, product columns K
   const Params p = make_params(dC, B, off, G, M, N, K, dA, nullptr, ab);
-  if (epi == EPI_SWIGLU_BWD) return run<DGRAD_SWIGLU_BWD, false>(p, (M / BM + G) * (K / BN), s);
-  return run<DGRAD, false>(p, (M / BM + G) * (K / BN), s);
+  if (epi == EPI_SWIGLU_BWD) return run_rows<DGRAD_SWIGLU_BWD, false>(p, s);
+  return run_rows<DGRAD, false>(p, s);
 }
 
 hipError_t launch_gg_bf16_wgrad(const void* A, const void* dC, const int64_t* off, int G,
@@ -837,7 +947,7 @@ hipError_t launch_gg_bf16_wgrad(const void* A, const void* dC, const int64_t* of
   Params p = make_params(A, dC, off, G, M, K, N, dB, nullptr, nullptr);
   p.out_f32 = db_f32;
   p.accumulate = accumulate;
-  return run<WGRAD, false>(p, static_cast<int64_t>(G) * (K / BM) * (N / BN), s);
+  return run_wgrad<false>(p, s);
 }
 
 hipError_t launch_gg_fp8_fwd(const uint8_t* A, const float* sa, const uint8_t* Bt, const float* sb,
@@ -847,9 +957,8 @@ hipError_t launch_gg_fp8_fwd(const uint8_t* A, const float* sa, const uint8_t* B
   Params p = make_params(A, Bt, off, G, M, K, N, C, H, nullptr);
   p.sa = sa;
   p.sb = sb;
-  const int64_t nt = N / BN;
-  if (epi == EPI_SWIGLU) return run<FWD_SWIGLU, true>(p, (M / BM + G) * nt, s);
-  return run<FWD, true>(p, (M / BM + G) * nt, s);
+  if (epi == EPI_SWIGLU) return run_rows<FWD_SWIGLU, true>(p, s);
+  return run_rows<FWD, true>(p, s);
 }
 
 hipError_t launch_gg_fp8_dgrad(const uint8_t* dC, const float* sa, const uint8_t* B,
@@ -859,8 +968,8 @@ hipError_t launch_gg_fp8_dgrad(const uint8_t* dC, const float* sa, const uint8_t
   Params p = make_params(dC, B, off, G, M, N, K, dA, nullptr, ab);
   p.sa = sa;
   p.sb = sb;
-  if (epi == EPI_SWIGLU_BWD) return run<DGRAD_SWIGLU_BWD, true>(p, (M / BM + G) * (K / BN), s);
-  return run<DGRAD, true>(p, (M / BM + G) * (K / BN), s);
+  if (epi == EPI_SWIGLU_BWD) return run_rows<DGRAD_SWIGLU_BWD, true>(p, s);
+  return run_rows<DGRAD, true>(p, s);
 }
 
 hipError_t launch_gg_fp8_wgrad(const uint8_t* At, const float* sa, const uint8_t* dCt,
@@ -872,7 +981,7 @@ hipError_t launch_gg_fp8_wgrad(const uint8_t* At, const float* sa, const uint8_t
   p.ldm = ldm;
   p.out_f32 = db_f32;
   p.accumulate = accumulate;
-  return run<WGRAD, true>(p, static_cast<int64_t>(G) * (K / BM) * (N / BN), s);
+  return run_wgrad<true>(p, s);
 }
 
 }  // namespace moe

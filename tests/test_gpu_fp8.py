@@ -129,7 +129,7 @@ def rel_small(got, ref):
     return rel_err(got, ref) < 1e-2
 
 
-@pytest.mark.parametrize("M,G,K,N", [(1500, 6, 256, 384), (300, 1, 128, 128)])
+@pytest.mark.parametrize("M,G,K,N", [(1500, 6, 256, 384), (1500, 6, 256, 512), (300, 1, 128, 128)])
 def test_fp8_grouped_gemm_wgrad(gpu, M, G, K, N):
     off = inputs.random_segments(M, G, 11, empty_frac=0.3, skew=0.5)
     A = _bf16_data((M, K), 12)
