@@ -582,9 +582,7 @@ __device__ __forceinline__ void compute_stage(f32x16_t (&acc)[2][2], const LDS_A
 // Staging per wave: 4 KiB = [32 m][64 n] bf16 (128 B rows, chunks swizzled by
 // m & 7), one half (ii) of the wave's rows at a time.
 
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
-}
+__device__ __forceinline__ uint32_t pack2(float a, float b) { return f32x2_to_bf16x2(a, b); }
 
 __device__ __forceinline__ int stg_off(int m, int chunk) { return m * 128 + ((chunk ^ (m & 7)) << 4); }
 

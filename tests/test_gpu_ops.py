@@ -289,3 +289,36 @@ def test_router_logits(gpu, dt, T, d, E, bias):
     rw, rx = oracle.router_logits_bwd(np64(x), w_r.numpy(), dz.numpy())
     assert_close("dW_r", dwr, rw, TOL["f32"])
     assert_close("dx_router", dxr, rx, TOL["f32"])
+
+
+def test_bf16_rounding_bit_exact(gpu):
+    """The kernels' fp32 -> bf16 rounding is round-to-nearest-even, pinned bit-exactly
+    against torch's CPU cast: permute backward with k = 1, a zero gradient and an fp32
+    addend returns bf16(addend).  Values cover many binades, exact ties (low half 0x8000)
+    of odd and even bf16 mantissas, their neighbours, fp32 subnormals, the largest finite
+    values and infinities."""
+    rng = np.random.default_rng(4)
+    n_rand = 1 << 16
+    mant = rng.integers(0, 1 << 23, n_rand, dtype=np.uint32)
+    expo = rng.integers(1, 255, n_rand, dtype=np.uint32)
+    sign = rng.integers(0, 2, n_rand, dtype=np.uint32)
+    u = (sign << 31) | (expo << 23) | mant
+    base = u & 0xFFFF0000
+    ties = base | 0x8000
+    special = np.array([0x00000001, 0x00007FFF, 0x00008000, 0x00018000, 0x007FFFFF, 0x7F7FFFFF,
+                        0xFF7FFFFF, 0x7F7F8000, 0x7F800000, 0xFF800000, 0x3F808000, 0x3F818000,
+                        0x00000000], dtype=np.uint32)
+    bits = np.concatenate([u, ties, ties + 1, ties - 1, special])
+    d = 64
+    bits = np.concatenate([bits, np.zeros((-len(bits)) % d, dtype=np.uint32)])
+    v = bits.view(np.float32).reshape(-1, d)
+    T = v.shape[0]
+    dst = torch.arange(T, dtype=torch.int32).reshape(T, 1).to(DEV)
+    dx_perm = torch.zeros((T, d), dtype=torch.bfloat16, device=DEV)
+    dx = torch.empty((T, d), dtype=torch.bfloat16, device=DEV)
+    abi.moe_permute_bwd(dx_perm, dst, None, torch.from_numpy(v).to(DEV), dx)
+    got = dx.cpu().view(torch.int16).numpy()
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy()
+    bad = np.nonzero(got != ref)
+    assert len(bad[0]) == 0, (f"{len(bad[0])} mismatches, first: x={v[bad][:4].view(np.uint32)} "
+                              f"got={got[bad][:4]} ref={ref[bad][:4]}")
