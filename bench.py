@@ -148,8 +148,9 @@ def fp8_work(cfg, n_nonempty):
 
 
 def traffic_for(kernel):
-    """HBM bytes per launch measured with rocprofv3 counters, if the committed
-    measurement was taken on the current kernel source; else None."""
+    """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE and
+    WRITE_SIZE, scaled by a copy of known size), if the committed measurement
+    was taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -159,8 +160,10 @@ def traffic_for(kernel):
         return None
     if not rec:
         return None
-    src = os.path.join(ROOT, "routing_grouped_gemm_router_amd", "csrc", rec["source"])
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["sha256"]:
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        h.update(open(os.path.join(ROOT, "routing_grouped_gemm_router_amd", "csrc", src), "rb").read())
+    if h.hexdigest() != rec["sha256"]:
         return None
     return rec["bytes_per_launch"]
 
