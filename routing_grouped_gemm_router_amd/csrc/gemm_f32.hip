@@ -177,6 +177,235 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const TA* __restrict__ A,
   }
 }
 
+
+// ---- router GEMMs: one wave per 64 x 64 output tile ---------------------------
+// The router projection and its two backward products (fp32 VALU, no packed
+// fp32): lane (tx, ty) = (lane & 7, lane >> 3) of a wave owns rows
+// {4ty..4ty+3, 32+4ty..} x columns {4tx..4tx+3, 32+4tx..} of its tile, 64 FMAs
+// per k for four 16-byte LDS reads.  Each wave stages its own 16-deep operand
+// slices in its own 8 KiB of LDS and prefetches the next slice into registers
+// while it computes, so the main loop has no workgroup barrier.  SK = 8: the
+// workgroup's 8 waves split the contraction of one tile and add their partial
+// sums through LDS in wave order (deterministic, no workspace); SK = 1: the 8
+// waves take 8 tiles.  Requires 16-byte aligned operands, the A and B
+// contiguous extents multiples of 8 (bf16) or 4 (fp32) elements.
+enum { RA_KC_BF16 = 0, RA_KC_F32 = 1, RA_MC_BF16 = 2, RA_MC_F32 = 3 };  // A: k- or m-contiguous
+enum { RB_NC = 0, RB_KC = 1 };                                          // B (fp32): n- or k-contiguous
+
+struct RSlice {  // one lane's share of a 16-deep slice of A and B
+  float4 a[4];
+  float4 b[4];
+};
+
+__device__ __forceinline__ float4 ld4_f32(const float* p, bool ok) {
+  return ok ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// 8 bf16 -> two float4
+__device__ __forceinline__ void ld8_bf16(const bf16_t* p, bool ok, float4& lo, float4& hi) {
+  uint4 v = ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
+  lo = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                   __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+  hi = make_float4(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xffff0000u),
+                   __uint_as_float(v.w << 16), __uint_as_float(v.w & 0xffff0000u));
+}
+
+template <int AL, int BL>
+__device__ __forceinline__ void router_load(RSlice& r, const void* A, int64_t lda, const float* B,
+                                            int64_t ldb, int64_t m0, int64_t n0, int64_t k0,
+                                            int64_t k_hi, int64_t M, int64_t N, int lane) {
+  if (AL == RA_KC_BF16 || AL == RA_KC_F32) {
+    // lane = row m0 + lane, k0 .. k0 + 15
+    const int64_t m = m0 + lane;
+    const bool row_ok = m < M;
+    if (AL == RA_KC_BF16) {
+      const bf16_t* p = static_cast<const bf16_t*>(A) + m * lda + k0;
+      ld8_bf16(p, row_ok && k0 + 8 <= k_hi, r.a[0], r.a[1]);
+      ld8_bf16(p + 8, row_ok && k0 + 16 <= k_hi, r.a[2], r.a[3]);
+    } else {
+      const float* p = static_cast<const float*>(A) + m * lda + k0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r.a[j] = ld4_f32(p + 4 * j, row_ok && k0 + 4 * j + 4 <= k_hi);
+    }
+  } else {
+    // lane -> k row k0 + (lane >> 2), rows m0 + 16 (lane & 3) .. + 15
+    const int64_t k = k0 + (lane >> 2), m = m0 + 16 * (lane & 3);
+    const bool k_ok = k < k_hi;
+    if (AL == RA_MC_BF16) {
+      const bf16_t* p = static_cast<const bf16_t*>(A) + k * lda + m;
+      ld8_bf16(p, k_ok && m + 8 <= M, r.a[0], r.a[1]);
+      ld8_bf16(p + 8, k_ok && m + 16 <= M, r.a[2], r.a[3]);
+    } else {
+      const float* p = static_cast<const float*>(A) + k * lda + m;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r.a[j] = ld4_f32(p + 4 * j, k_ok && m + 4 * j + 4 <= M);
+    }
+  }
+  if (BL == RB_NC) {
+    const int64_t k = k0 + (lane >> 2), n = n0 + 16 * (lane & 3);
+    const float* p = B + k * ldb + n;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r.b[j] = ld4_f32(p + 4 * j, k < k_hi && n + 4 * j + 4 <= N);
+  } else {
+    const int64_t n = n0 + lane;
+    const float* p = B + n * ldb + k0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r.b[j] = ld4_f32(p + 4 * j, n < N && k0 + 4 * j + 4 <= k_hi);
+  }
+}
+
+// slice -> LDS as [k][64] for A and for B
+template <int AL, int BL>
+__device__ __forceinline__ void router_stage(const RSlice& r, float (*As)[64], float (*Bs)[64],
+                                             int lane) {
+  if (AL == RA_KC_BF16 || AL == RA_KC_F32) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      As[4 * j + 0][lane] = r.a[j].x;
+      As[4 * j + 1][lane] = r.a[j].y;
+      As[4 * j + 2][lane] = r.a[j].z;
+      As[4 * j + 3][lane] = r.a[j].w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<float4*>(&As[lane >> 2][16 * (lane & 3) + 4 * j]) = r.a[j];
+  }
+  if (BL == RB_NC) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<float4*>(&Bs[lane >> 2][16 * (lane & 3) + 4 * j]) = r.b[j];
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      Bs[4 * j + 0][lane] = r.b[j].x;
+      Bs[4 * j + 1][lane] = r.b[j].y;
+      Bs[4 * j + 2][lane] = r.b[j].z;
+      Bs[4 * j + 3][lane] = r.b[j].w;
+    }
+  }
+}
+
+template <int AL, int BL, int SK, bool BIAS>
+__global__ __launch_bounds__(512) void router_gemm_kernel(const void* __restrict__ A, int64_t lda,
+                                                          const float* __restrict__ B,
+                                                          int64_t ldb, float* __restrict__ C,
+                                                          int64_t ldc, int64_t M, int64_t N,
+                                                          int64_t K,
+                                                          const float* __restrict__ bias) {
+  __shared__ __attribute__((aligned(16))) float lds[8][2][16][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tx = lane & 7, ty = lane >> 3;
+  const int64_t ntn = (N + 63) / 64;
+  const int64_t tile = SK > 1 ? static_cast<int64_t>(blockIdx.x)
+                              : static_cast<int64_t>(blockIdx.x) * 8 + wave;
+  const int64_t m0 = (tile / ntn) * 64, n0 = (tile % ntn) * 64;
+  int64_t k_lo = 0, k_hi = K;
+  if (SK > 1) {
+    const int64_t per = ((K + SK - 1) / SK + 15) / 16 * 16;
+    k_lo = min(K, wave * per);
+    k_hi = min(K, k_lo + per);
+  }
+  float(*As)[64] = lds[wave][0];
+  float(*Bs)[64] = lds[wave][1];
+  float acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+
+  if (m0 < M) {  // SK == 1: trailing waves of the last block may have no tile
+    RSlice r;
+    if (k_lo < k_hi) router_load<AL, BL>(r, A, lda, B, ldb, m0, n0, k_lo, k_hi, M, N, lane);
+    for (int64_t k0 = k_lo; k0 < k_hi; k0 += 16) {
+      router_stage<AL, BL>(r, As, Bs, lane);
+      __builtin_amdgcn_wave_barrier();
+      if (k0 + 16 < k_hi) router_load<AL, BL>(r, A, lda, B, ldb, m0, n0, k0 + 16, k_hi, M, N, lane);
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) {
+        const float4 a0 = *reinterpret_cast<const float4*>(&As[kk][4 * ty]);
+        const float4 a1 = *reinterpret_cast<const float4*>(&As[kk][32 + 4 * ty]);
+        const float4 b0 = *reinterpret_cast<const float4*>(&Bs[kk][4 * tx]);
+        const float4 b1 = *reinterpret_cast<const float4*>(&Bs[kk][32 + 4 * tx]);
+        const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+
+  // row of acc[i] and column of acc[.][j] inside the tile
+  auto row_of = [&](int i) { return (i < 4 ? 4 * ty : 32 + 4 * ty) + (i & 3); };
+  auto col_of = [&](int h) { return (h == 0 ? 4 * tx : 32 + 4 * tx); };
+  if (SK == 1) {
+    if (m0 >= M) return;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t m = m0 + row_of(i);
+      if (m >= M) continue;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t n = n0 + col_of(h);
+        if (n >= N) continue;
+        float4 v = make_float4(acc[i][4 * h], acc[i][4 * h + 1], acc[i][4 * h + 2], acc[i][4 * h + 3]);
+        if (BIAS) {
+          v.x += bias[n]; v.y += bias[n + 1]; v.z += bias[n + 2]; v.w += bias[n + 3];
+        }
+        *reinterpret_cast<float4*>(C + m * ldc + n) = v;
+      }
+    }
+    return;
+  }
+  // SK > 1: two rounds of 32 rows; wave w's partials in its own 8 KiB as [32][64]
+  float* part = &lds[wave][0][0][0];
+#pragma unroll
+  for (int rnd = 0; rnd < 2; ++rnd) {
+    __syncthreads();  // every wave is done with its slices / the previous round
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int i = 4 * rnd + ii;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        *reinterpret_cast<float4*>(part + (4 * ty + ii) * 64 + col_of(h)) =
+            make_float4(acc[i][4 * h], acc[i][4 * h + 1], acc[i][4 * h + 2], acc[i][4 * h + 3]);
+    }
+    __syncthreads();
+    // thread t sums elements 4t .. 4t+3 of the 32 x 64 half over the waves in order
+    const int e = 4 * static_cast<int>(threadIdx.x);
+    float4 sum = *reinterpret_cast<const float4*>(&lds[0][0][0][0] + e);
+#pragma unroll
+    for (int w = 1; w < 8; ++w) {
+      const float4 q = *reinterpret_cast<const float4*>(&lds[w][0][0][0] + e);
+      sum.x += q.x; sum.y += q.y; sum.z += q.z; sum.w += q.w;
+    }
+    const int64_t m = m0 + 32 * rnd + e / 64, n = n0 + (e % 64);
+    if (m < M && n < N) {
+      if (BIAS) {
+        sum.x += bias[n]; sum.y += bias[n + 1]; sum.z += bias[n + 2]; sum.w += bias[n + 3];
+      }
+      *reinterpret_cast<float4*>(C + m * ldc + n) = sum;
+    }
+  }
+}
+
+template <int AL, int BL, int SK, bool BIAS>
+static hipError_t run_router(const void* A, int64_t lda, const float* B, int64_t ldb, float* C,
+                             int64_t ldc, int64_t M, int64_t N, int64_t K, const float* bias,
+                             hipStream_t s) {
+  const int64_t tiles = ((M + 63) / 64) * ((N + 63) / 64);
+  const int64_t blocks = SK > 1 ? tiles : (tiles + 7) / 8;
+  if (blocks <= 0) return hipSuccess;
+  router_gemm_kernel<AL, BL, SK, BIAS><<<dim3(static_cast<unsigned>(blocks)), 512, 0, s>>>(
+      A, lda, B, ldb, C, ldc, M, N, K, bias);
+  return hipGetLastError();
+}
+
+static bool aligned16p(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 template <typename TA, bool A_MC, bool B_KC, int GRP, int EPI, typename TC>
 static hipError_t run_f32(const TA* A, int64_t lda, const float* B, int64_t ldb, int64_t strideB,
                           TC* C, int64_t ldc, int64_t strideC, const int64_t* off, int G,
@@ -199,6 +428,14 @@ static hipError_t run_f32(const TA* A, int64_t lda, const float* B, int64_t ldb,
 hipError_t launch_router_fwd(const void* x, int x_dtype, const float* w_r, const float* bias,
                              int64_t T, int64_t d, int E, float* logits, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  if (d % 8 == 0 && E % 4 == 0 && aligned16p(x) && aligned16p(w_r) && aligned16p(logits)) {
+    // logits [T, E] = x [T, d] . W_r [d, E] (+ bias): contraction split over the 8 waves
+    if (x_dtype == 0)
+      return bias ? run_router<RA_KC_F32, RB_NC, 8, true>(x, d, w_r, E, logits, E, T, E, d, bias, s)
+                  : run_router<RA_KC_F32, RB_NC, 8, false>(x, d, w_r, E, logits, E, T, E, d, bias, s);
+    return bias ? run_router<RA_KC_BF16, RB_NC, 8, true>(x, d, w_r, E, logits, E, T, E, d, bias, s)
+                : run_router<RA_KC_BF16, RB_NC, 8, false>(x, d, w_r, E, logits, E, T, E, d, bias, s);
+  }
   if (x_dtype == 0)
     return run_f32<float, false, false, GRP_NONE, EPI_BIAS, float>(
         static_cast<const float*>(x), d, w_r, E, 0, logits, E, 0, nullptr, 1, T, E, d, bias,
@@ -212,6 +449,24 @@ hipError_t launch_router_bwd(const void* x, int x_dtype, const float* w_r, const
                              int64_t T, int64_t d, int E, float* dw_r, float* dx_r,
                              hipStream_t s) {
   hipError_t err = hipSuccess;
+  const bool fast = d % 8 == 0 && E % 4 == 0 && aligned16p(x) && aligned16p(w_r) &&
+                    aligned16p(dz) && aligned16p(dw_r) && aligned16p(dx_r);
+  if (fast) {
+    if (dw_r) {
+      // dW_r [d, E] = x^T [d, T] . dz [T, E]: contraction over tokens split over the 8 waves
+      if (T == 0)
+        err = launch_fill_zero(dw_r, d * E, s);
+      else if (x_dtype == 0)
+        err = run_router<RA_MC_F32, RB_NC, 8, false>(x, d, dz, E, dw_r, E, d, E, T, nullptr, s);
+      else
+        err = run_router<RA_MC_BF16, RB_NC, 8, false>(x, d, dz, E, dw_r, E, d, E, T, nullptr, s);
+      if (err != hipSuccess) return err;
+    }
+    if (dx_r && T > 0)
+      // dx_r [T, d] = dz [T, E] . W_r^T (Bop(k = e, n = i) = W_r[i * E + e])
+      err = run_router<RA_KC_F32, RB_KC, 1, false>(dz, E, w_r, E, dx_r, d, T, d, E, nullptr, s);
+    return err;
+  }
   if (dw_r) {
     // dW_r [d, E] = x^T [d, T] . dz [T, E]
     if (T == 0) {
