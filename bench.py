@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--config", default="deepseek_v3_e256k8")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--recompute-act", action="store_true",
+                    help="rebuild H = silu(A) * B in the backward instead of keeping it")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the CPU oracle sample")
     return ap.parse_args()
@@ -76,6 +78,7 @@ def kernel_work(cfg, n_nonempty):
         "gemm1_dgrad": (2.0 * N * 2 * f * d, N * 2 * f * s + w13 + N * d * s),
         "gemm1_wgrad": (2.0 * N * d * 2 * f, N * d * s + N * 2 * f * s + E * d * 2 * f * s),
         "route_topk_bwd": (0.0, T * E * 4 * 2 + 3 * idx),
+        "swiglu_recompute": (0.0, N * 2 * f * s + N * f * s),
         "router_logits_bwd": (4.0 * T * d * E, T * d * s + T * E * 4 + d * E * 4 * 2 + T * d * 4),
         "permute_bwd": (0.0, N * d * s + idx + T * d * (s + 4 + (s if fs else 0))),
     }
@@ -243,7 +246,7 @@ def main():
     gemm_peak = PEAK_FP8_TFLOPS if cfg.gemm == "fp8" else PEAK_BF16_TFLOPS
     dev = "cuda"
     inp = inputs.layer_inputs(cfg, args.seed, dev)
-    layer = MoELayer(cfg, inp, dev)
+    layer = MoELayer(cfg, inp, dev, recompute_act=args.recompute_act)
     x, dout = inp["x"], inp["dout"]
     for _ in range(args.warmup):
         layer.forward(x)
@@ -311,7 +314,9 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.gemm,
         "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights, generated on the GPU)",
-        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
+        "config": {"workload": cfg.name, "routing": cfg.routing,
+                   "recompute_act": bool(args.recompute_act),
+                   "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
                    "ffn": cfg.f, "shared_ffn": cfg.fs, "score": cfg.score, "renorm": cfg.renorm,
                    "router_bias": cfg.bias, "experts_with_rows": n_nonempty,
                    "max_rows_per_expert": int(counts.max())},

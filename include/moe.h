@@ -114,6 +114,25 @@ int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int sco
                    int32_t* dst_row, int32_t* src_token, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* Router replay: routing with the experts given (e.g. recorded from an
+ * earlier pass, or a forced assignment such as the balanced routing of the
+ * benchmark setting in section 8, Performance Evaluation), the routing weights
+ * recomputed from the keys exactly as in moe_route_topk, and the same
+ * dispatch map.  Arguments as moe_route_topk, plus:
+ *   topk_idx_in [T, k] int32: expert of each (t, j), slots in the given order.
+ *               A slot outside [0, E) or repeating an earlier slot of its
+ *               token is replaced, in slot order, by the smallest expert the
+ *               token does not use yet (so the dispatch map stays a
+ *               bijection); topk_idx receives the experts used.
+ *   status      int32 device word or NULL: set to 1 when a slot was replaced
+ *               (never cleared by the library).
+ *   workspace   moe_route_topk_workspace_bytes(T, E, k) bytes
+ * Limits as moe_route_topk.  The backward is moe_route_topk_bwd. */
+int moe_route_replay(const float* logits, const int32_t* topk_idx_in, int64_t T, int32_t E,
+                     int32_t k, int score, int renorm, int32_t* topk_idx, float* topk_w,
+                     int32_t* counts, int64_t* offsets, int32_t* dst_row, int32_t* src_token,
+                     int32_t* status, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Gradient of the routing weights with respect to the keys (the selection
  * itself carries none).  With g = sum_j w_j dw_j over a token's chosen slots:
  *   softmax, renorm   : d_logits[e_j] = w_j (dw_j - g), 0 elsewhere

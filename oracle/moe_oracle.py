@@ -32,7 +32,7 @@ SIGMOID = "sigmoid"
 
 __all__ = [
     "SOFTMAX", "SIGMOID", "f64", "router_logits", "select_topk", "gates", "dispatch_map",
-    "route", "route_bwd", "router_logits_bwd", "permute", "permute_bwd",
+    "route", "route_replay", "canonical_experts", "route_bwd", "router_logits_bwd", "permute", "permute_bwd",
     "grouped_gemm_fwd", "grouped_gemm_dgrad", "grouped_gemm_wgrad", "sigmoid", "silu",
     "swiglu", "swiglu_bwd", "unpermute_combine", "unpermute_combine_bwd",
     "expert_ffn", "expert_ffn_bwd", "layer_forward", "layer_backward",
@@ -148,6 +148,38 @@ def route(z, k, score, renorm):
     counts, offsets, dst_row, src_token = dispatch_map(idx, z.shape[1])
     return dict(topk_idx=idx, topk_w=w, counts=counts, offsets=offsets,
                 dst_row=dst_row, src_token=src_token)
+
+
+def canonical_experts(topk_idx, E):
+    """Given experts per token, made usable as a routing: a slot whose expert
+    is outside [0, E) or repeats an earlier slot of its token is replaced, in
+    slot order, by the smallest expert the token does not use yet.  (The pages
+    say nothing of replayed routings; this keeps every token's k experts
+    distinct, so the dispatch map is a bijection.)  Returns (experts, changed)."""
+    idx = np.array(topk_idx, dtype=np.int64, copy=True)
+    T, k = idx.shape
+    changed = False
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            if 0 <= e < E and e not in idx[t, :j]:
+                continue
+            others = {int(idx[t, s]) for s in range(k) if s != j}
+            idx[t, j] = min(c for c in range(E) if c not in others)
+            changed = True
+    return idx.astype(np.int32), changed
+
+
+def route_replay(z, topk_idx, score, renorm):
+    """Route stage with the experts given (a recorded or forced assignment):
+    the routing weights and the dispatch map of ``route`` for those experts,
+    in the given slot order (after ``canonical_experts``)."""
+    z = np.asarray(z, dtype=np.float32)
+    idx, changed = canonical_experts(topk_idx, z.shape[1])
+    w = gates(z, idx, score, renorm)
+    counts, offsets, dst_row, src_token = dispatch_map(idx, z.shape[1])
+    return dict(topk_idx=idx, topk_w=w, counts=counts, offsets=offsets,
+                dst_row=dst_row, src_token=src_token, changed=changed)
 
 
 def route_bwd(z, topk_idx, topk_w, d_topk_w, score, renorm):
@@ -333,17 +365,22 @@ def expert_ffn_bwd(x_t, w13_e, w2_e, a, b, h, dy):
 
 
 def layer_forward(x, w_r, w13, w2, k, score, renorm, logit_bias=None,
-                  shared=None, z=None):
+                  shared=None, z=None, given_experts=None):
     """The four-stage forward pass as a per-token loop over each token's k
     experts (the one-expert-at-a-time view of [MCore-MoE] section 2, Expert
     Computation).  ``shared`` = (ws13 [d, 2fs], ws2 [fs, d]) or None.
     ``z`` may give the fp32 keys directly; by default they are computed with
-    ``router_logits``.  Returns a cache dict consumed by ``layer_backward``."""
+    ``router_logits``.  ``given_experts`` [T, k] replays a routing
+    (``route_replay``) instead of selecting the top k.  Returns a cache dict
+    consumed by ``layer_backward``."""
     x = f64(x)
     T, d = x.shape
     if z is None:
         z = router_logits(x, w_r, logit_bias)
-    r = route(z, k, score, renorm)
+    if given_experts is None:
+        r = route(z, k, score, renorm)
+    else:
+        r = route_replay(z, given_experts, score, renorm)
     idx, w = r["topk_idx"], r["topk_w"]
     out = np.zeros((T, d))
     acts = {}

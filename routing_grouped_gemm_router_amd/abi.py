@@ -34,6 +34,8 @@ SIGNATURES = {
     "moe_route_topk_workspace_bytes": (_sz, [_i64, _i32, _i32]),
     "moe_route_topk": (_int, [_p, _i64, _i32, _i32, _int, _int, _p, _p, _p, _p, _p, _p, _p, _sz,
                               _p]),
+    "moe_route_replay": (_int, [_p, _p, _i64, _i32, _i32, _int, _int, _p, _p, _p, _p, _p, _p, _p,
+                                _p, _sz, _p]),
     "moe_route_topk_bwd": (_int, [_p, _p, _p, _p, _i64, _i32, _i32, _int, _int, _p, _p]),
     "moe_permute": (_int, [_p, _int, _p, _i64, _i64, _i32, _p, _p]),
     "moe_permute_bwd": (_int, [_p, _int, _p, _i64, _i64, _i32, _p, _p, _p, _p]),
@@ -152,6 +154,15 @@ def moe_route_topk(logits, k, score, renorm, topk_idx, topk_w, counts, offsets, 
     _call("moe_route_topk", _ptr(logits), T, E, k, score, int(renorm), _ptr(topk_idx),
           _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(dst_row), _ptr(src_token),
           _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def moe_route_replay(logits, topk_idx_in, score, renorm, topk_idx, topk_w, counts, offsets,
+                     dst_row, src_token, workspace, status=None, stream=None):
+    T, E = logits.shape
+    _call("moe_route_replay", _ptr(logits), _ptr(topk_idx_in), T, E, topk_idx_in.shape[1], score,
+          int(renorm), _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(dst_row),
+          _ptr(src_token), _ptr(status), _ptr(workspace),
+          workspace.numel() * workspace.element_size(), _stream(stream))
 
 
 def moe_route_topk_bwd(logits, topk_idx, topk_w, d_topk_w, score, renorm, d_logits, stream=None):

@@ -16,6 +16,10 @@ size_t route_topk_workspace(int64_t T, int E);
 hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int score, int renorm,
                              int32_t* topk_idx, float* topk_w, int32_t* counts, int64_t* offsets,
                              int32_t* dst_row, int32_t* src_token, void* ws, hipStream_t s);
+hipError_t launch_route_replay(const float* logits, const int32_t* idx_in, int64_t T, int E, int k,
+                               int score, int renorm, int32_t* topk_idx, float* topk_w,
+                               int32_t* counts, int64_t* offsets, int32_t* dst_row,
+                               int32_t* src_token, int32_t* status, void* ws, hipStream_t stream);
 hipError_t launch_route_topk_bwd(const float* logits, const int32_t* topk_idx, const float* topk_w,
                                  const float* d_topk_w, int64_t T, int E, int k, int score,
                                  int renorm, float* d_logits, hipStream_t s);

@@ -139,6 +139,28 @@ int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int sco
                     "moe_route_topk");
 }
 
+int moe_route_replay(const float* logits, const int32_t* topk_idx_in, int64_t T, int32_t E,
+                     int32_t k, int score, int renorm, int32_t* topk_idx, float* topk_w,
+                     int32_t* counts, int64_t* offsets, int32_t* dst_row, int32_t* src_token,
+                     int32_t* status, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_route_shape("moe_route_replay", T, E, k, score);
+  if (st != MOE_OK) return st;
+  REQUIRE(counts && offsets, MOE_ERR_NULL, "moe_route_replay: counts and offsets are required");
+  REQUIRE(T == 0 || (logits && topk_idx_in && topk_idx && topk_w && dst_row && src_token),
+          MOE_ERR_NULL,
+          "moe_route_replay: logits, topk_idx_in, topk_idx, topk_w, dst_row and src_token are "
+          "required");
+  const size_t need = moe::route_topk_workspace(T, E);
+  REQUIRE(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE,
+          "moe_route_replay: workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 7u) == 0, MOE_ERR_UNSUPPORTED,
+          "moe_route_replay: workspace must be 8-byte aligned");
+  return hip_status(moe::launch_route_replay(logits, topk_idx_in, T, E, k, score, renorm != 0,
+                                             topk_idx, topk_w, counts, offsets, dst_row,
+                                             src_token, status, workspace, as_stream(stream)),
+                    "moe_route_replay");
+}
+
 int moe_route_topk_bwd(const float* logits, const int32_t* topk_idx, const float* topk_w,
                        const float* d_topk_w, int64_t T, int32_t E, int32_t k, int score,
                        int renorm, float* d_logits, void* stream) {

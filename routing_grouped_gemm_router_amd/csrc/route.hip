@@ -1,6 +1,6 @@
-// Route stage kernels: top-k selection and routing weights, the per-expert
-// histogram with prefix-sum offsets, and the permutation map; plus the
-// backward of the routing weights.
+// Route stage kernels: top-k selection and routing weights (or routing
+// replayed from given experts), the per-expert histogram with prefix-sum
+// offsets, and the permutation map; plus the backward of the routing weights.
 //
 // Definition: "Scalable Training of Mixture-of-Experts Models with Megatron
 // Core", section 2, Route (logits -> probabilities -> top-k experts, routing
@@ -101,6 +101,97 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
       topk_idx[t * k + lane] = my_idx;
       topk_w[t * k + lane] = w;
       atomicOr(&bits[my_idx], 1ull << tt);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) tile_bits[tile * E + e] = bits[e];
+}
+
+// Router replay: the k experts of every token are given, in slot order; the
+// routing weights are computed from the logits as in the top-k route.  A slot
+// whose expert is outside [0, E) or repeats an earlier slot of the token is
+// replaced, in slot order, by the smallest expert the token does not use yet,
+// and *status (if given) is set to 1: the dispatch map stays a bijection.
+template <int EPL>
+__global__ __launch_bounds__(256) void replay_kernel(const float* __restrict__ logits,
+                                                     const int32_t* __restrict__ idx_in,
+                                                     int64_t T, int E, int k, int score,
+                                                     int renorm, int32_t* __restrict__ topk_idx,
+                                                     float* __restrict__ topk_w,
+                                                     unsigned long long* __restrict__ tile_bits,
+                                                     int32_t* __restrict__ status) {
+  __shared__ unsigned long long bits[1024];
+  const int tid = threadIdx.x;
+  const int64_t tile = blockIdx.x;
+  for (int e = tid; e < E; e += 256) bits[e] = 0ull;
+  __syncthreads();
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int tt = wave; tt < ROUTE_TILE; tt += 4) {
+    const int64_t t = tile * ROUTE_TILE + tt;
+    if (t >= T) break;
+    const float* row = logits + t * E;
+    const bool active = lane < k;
+    int my = active ? idx_in[t * k + lane] : -1;
+    bool ok = active && my >= 0 && my < E;
+    for (int i = 0; i < k; ++i) {
+      const int o = __shfl(my, i, 64);
+      if (i < lane && o == my) ok = false;
+    }
+    const unsigned long long bad = __ballot(active && !ok);
+    if (bad) {
+      for (int j = 0; j < k; ++j) {
+        if (!((bad >> j) & 1ull)) continue;  // uniform across the wave
+        int best = 0x7fffffff;
+        for (int e = lane; e < E; e += 64) {
+          bool used = false;
+          for (int sl = 0; sl < k; ++sl) {
+            const int o = __shfl(my, sl, 64);
+            if (sl != j && o == e) used = true;
+          }
+          if (!used) best = min(best, e);
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) best = min(best, __shfl_xor(best, o, 64));
+        if (lane == j) my = best;
+      }
+      if (lane == 0 && status) status[0] = 1;
+    }
+    const float key = active ? row[my] : 0.f;
+    float w;
+    if (score == 0) {  // softmax
+      float m;
+      if (renorm) {
+        m = active ? key : -INFINITY;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      } else {
+        m = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+          if (lane + 64 * i < E) m = fmaxf(m, row[lane + 64 * i]);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      }
+      const float ex = active ? expf(key - m) : 0.f;
+      float denom;
+      if (renorm) {
+        denom = wave_sum(ex);
+      } else {
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+          if (lane + 64 * i < E) part += expf(row[lane + 64 * i] - m);
+        denom = wave_sum(part);
+      }
+      w = ex / denom;
+    } else {  // sigmoid
+      const float sg = active ? 1.0f / (1.0f + expf(-key)) : 0.f;
+      w = renorm ? sg / wave_sum(sg) : sg;
+    }
+    if (active) {
+      topk_idx[t * k + lane] = my;
+      topk_w[t * k + lane] = w;
+      atomicOr(&bits[my], 1ull << tt);
     }
   }
   __syncthreads();
@@ -247,6 +338,33 @@ hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int s
     break;
       MOE_TOPK(1) MOE_TOPK(2) MOE_TOPK(4) MOE_TOPK(8) MOE_TOPK(16)
 #undef MOE_TOPK
+    }
+  }
+  route_scan_kernel<<<1, 1024, 0, stream>>>(tile_bits, ntiles, E, tile_base, counts, offsets);
+  if (T > 0) {
+    const int64_t n = T * k;
+    route_rank_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), 256, 0, stream>>>(
+        topk_idx, tile_bits, tile_base, offsets, T, E, k, dst_row, src_token);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_route_replay(const float* logits, const int32_t* idx_in, int64_t T, int E, int k,
+                               int score, int renorm, int32_t* topk_idx, float* topk_w,
+                               int32_t* counts, int64_t* offsets, int32_t* dst_row,
+                               int32_t* src_token, int32_t* status, void* ws, hipStream_t stream) {
+  const int64_t ntiles = (T + ROUTE_TILE - 1) / ROUTE_TILE;
+  unsigned long long* tile_bits = static_cast<unsigned long long*>(ws);
+  int32_t* tile_base = reinterpret_cast<int32_t*>(tile_bits + ntiles * E);
+  if (ntiles > 0) {
+    switch (epl_for(E)) {
+#define MOE_REPLAY(n)                                                                             \
+  case n:                                                                                         \
+    replay_kernel<n><<<dim3(static_cast<unsigned>(ntiles)), 256, 0, stream>>>(                    \
+        logits, idx_in, T, E, k, score, renorm, topk_idx, topk_w, tile_bits, status);             \
+    break;
+      MOE_REPLAY(1) MOE_REPLAY(2) MOE_REPLAY(4) MOE_REPLAY(8) MOE_REPLAY(16)
+#undef MOE_REPLAY
     }
   }
   route_scan_kernel<<<1, 1024, 0, stream>>>(tile_bits, ntiles, E, tile_base, counts, offsets);

@@ -15,6 +15,10 @@ all tensors synthetic, N(0, 1) activations and N(0, 1/fan_in) weights):
   deepseek_v3_e256k8 T=8192  d=7168 E=256 k=8 f=2048  bf16, sigmoid top-8, renorm,
                      logit bias N(0, variance 0.5), one shared expert fs=2048
   deepseek_v3_fp8    as deepseek_v3_e256k8 with T=32768 and fp8 E4M3 expert GEMMs
+  deepseek_v3_balanced as deepseek_v3_e256k8 with force-balanced routing (the
+                     benchmark setting of section 8: every expert gets exactly
+                     T*k/E rows), replayed from a seeded assignment
+  small_balanced     T=512 d=256 E=16 k=4 f=256 shared 128, bf16, force-balanced
 
 Generation: each tensor (and each expert's slice of a weight) is drawn from
 its own torch generator seeded from (seed, stream id), as float32 normals
@@ -44,6 +48,7 @@ class LayerConfig:
     bias: str = "none"          # none | zipf | normal
     bias_var: float = 0.5
     zipf_s: float = 1.0
+    routing: str = "topk"       # topk | balanced (experts given, replayed)
     note: str = field(default="", compare=False)
 
     @property
@@ -63,11 +68,28 @@ CONFIGS = {
                                       fs=2048, score="sigmoid", bias="normal"),
     "deepseek_v3_fp8": LayerConfig("deepseek_v3_fp8", T=32768, d=7168, E=256, k=8, f=2048,
                                    fs=2048, gemm="fp8", score="sigmoid", bias="normal"),
+    "deepseek_v3_balanced": LayerConfig("deepseek_v3_balanced", T=8192, d=7168, E=256, k=8,
+                                        f=2048, fs=2048, score="sigmoid", bias="normal",
+                                        routing="balanced"),
+    "small_balanced": LayerConfig("small_balanced", T=512, d=256, E=16, k=4, f=256, fs=128,
+                                  score="sigmoid", bias="normal", routing="balanced"),
 }
 
 # stream ids: one per tensor; expert weights add the expert index
-_S_X, _S_WR, _S_BIAS, _S_DOUT, _S_SHARED = 1, 2, 3, 4, 5
+_S_X, _S_WR, _S_BIAS, _S_DOUT, _S_SHARED, _S_ROUTE = 1, 2, 3, 4, 5, 6
 _S_W1, _S_W3, _S_W2 = 1 << 20, 2 << 20, 3 << 20
+
+
+def balanced_experts(T, E, k, seed, device="cpu"):
+    """A forced assignment in which every expert gets exactly T*k/E (token,
+    slot) pairs (T*k divisible by E, k <= E): with a seeded permutation pi of
+    the tokens, slot j of token t goes to expert (pi(t)*k + j) mod E, so a
+    token's k experts are k consecutive experts (distinct) and the pairs cycle
+    through all experts evenly.  int32 [T, k]."""
+    assert k <= E and (T * k) % E == 0
+    pi = torch.randperm(T, generator=generator(seed, _S_ROUTE, "cpu"))
+    idx = (pi[:, None] * k + torch.arange(k)[None, :]) % E
+    return idx.to(torch.int32).to(device)
 
 
 def generator(seed, stream, device):
@@ -128,6 +150,8 @@ def layer_inputs(cfg, seed, device="cpu"):
     if cfg.fs:
         ws13, ws2 = expert_weights(cfg, seed, device, E=1, f=cfg.fs, stream_base=_S_SHARED << 24)
         inp["ws13"], inp["ws2"] = ws13[0], ws2[0]
+    if cfg.routing == "balanced":
+        inp["topk_idx_in"] = balanced_experts(cfg.T, cfg.E, cfg.k, seed, device)
     return inp
 
 

@@ -65,8 +65,16 @@ class MoELayer:
     w13 [E, d, 2f], w2 [E, f, d] and, with a shared expert, ws13 [d, 2fs],
     ws2 [fs, d] (activation dtype)."""
 
-    def __init__(self, cfg, weights, device="cuda"):
+    def __init__(self, cfg, weights, device="cuda", recompute_act=False):
         self.cfg = cfg
+        # recompute_act: H = silu(A) * B is not kept from the forward to the
+        # backward; the backward rebuilds it from AB (moe_swiglu).  H then lives
+        # in the storage of dAB, which holds nothing until the backward.
+        self.recompute = recompute_act
+        self.replay = cfg.routing == "balanced"
+        if self.replay:
+            self.topk_idx_in = weights["topk_idx_in"]
+            self.route_status = torch.zeros(1, dtype=torch.int32, device=device)
         self.timer = None
         self.dev = torch.device(device)
         self.w = weights
@@ -87,13 +95,13 @@ class MoELayer:
         self.route_ws = emp(abi.moe_route_topk_workspace_bytes(T, E, k), dtype=torch.uint8)
         self.x_perm = emp(N, d)
         self.ab = emp(N, 2 * f)
-        self.h = emp(N, f)
         self.y = emp(N, d)
         self.out = emp(T, d)
         # backward state
         self.d_topk_w = emp(T, k, dtype=torch.float32)
         self.dy = emp(N, d)
         self.dab = emp(N, 2 * f)
+        self.h = self.dab.view(-1)[:N * f].view(N, f) if recompute_act else emp(N, f)
         self.dx_perm = emp(N, d)
         self.dw13 = emp(E, d, 2 * f)
         self.dw2 = emp(E, f, d)
@@ -197,17 +205,31 @@ class MoELayer:
 
     def _backward_fp8(self, dout):
         q, x = self.q, self.x
-        with self._span("quant_dy"):
-            dyq, dys = self._qrows("dy", self.dy)
-        with self._span("gemm2_dgrad"):
-            abi.moe_grouped_gemm_fp8_dgrad(dyq, dys, q["w2"]["qd"], q["w2"]["sd"], self.offsets,
-                                           self.dab, epilogue=abi.EPI_SWIGLU_BWD, ab=self.ab)
-        with self._span("quant_tiles_h_dy"):
-            abi.moe_padded_offsets(self.offsets, self.x_perm.shape[0], self.poff)
-            hT, hTs = self._qtiles("h", self.h, self.offsets, self.poff)
-            dyT, dyTs = self._qtiles("dy", self.dy, self.offsets, self.poff)
-        with self._span("gemm2_wgrad"):
-            abi.moe_grouped_gemm_fp8_wgrad(hT, hTs, dyT, dyTs, self.poff, self.dw2)
+
+        def gemm2_dgrad():
+            with self._span("quant_dy"):
+                dyq, dys = self._qrows("dy", self.dy)
+            with self._span("gemm2_dgrad"):
+                abi.moe_grouped_gemm_fp8_dgrad(dyq, dys, q["w2"]["qd"], q["w2"]["sd"],
+                                               self.offsets, self.dab,
+                                               epilogue=abi.EPI_SWIGLU_BWD, ab=self.ab)
+
+        def gemm2_wgrad():
+            with self._span("quant_tiles_h_dy"):
+                abi.moe_padded_offsets(self.offsets, self.x_perm.shape[0], self.poff)
+                hT, hTs = self._qtiles("h", self.h, self.offsets, self.poff)
+                dyT, dyTs = self._qtiles("dy", self.dy, self.offsets, self.poff)
+            with self._span("gemm2_wgrad"):
+                abi.moe_grouped_gemm_fp8_wgrad(hT, hTs, dyT, dyTs, self.poff, self.dw2)
+
+        if self.recompute:  # H in dAB's storage: use it before the dgrad writes dAB
+            with self._span("swiglu_recompute"):
+                abi.moe_swiglu(self.ab, self.h)
+            gemm2_wgrad()
+            gemm2_dgrad()
+        else:
+            gemm2_dgrad()
+            gemm2_wgrad()
         with self._span("quant_dab"):
             dabq, dabs = self._qrows("dab", self.dab)
         with self._span("gemm1_dgrad"):
@@ -251,9 +273,15 @@ class MoELayer:
         with self._span("router_logits"):
             abi.moe_router_logits(x, w["w_r"], w.get("logit_bias"), self.logits)
         with self._span("route_topk"):
-            abi.moe_route_topk(self.logits, c.k, self.score, c.renorm, self.topk_idx, self.topk_w,
-                               self.counts, self.offsets, self.dst_row, self.src_token,
-                               self.route_ws)
+            if self.replay:
+                abi.moe_route_replay(self.logits, self.topk_idx_in, self.score, c.renorm,
+                                     self.topk_idx, self.topk_w, self.counts, self.offsets,
+                                     self.dst_row, self.src_token, self.route_ws,
+                                     status=self.route_status)
+            else:
+                abi.moe_route_topk(self.logits, c.k, self.score, c.renorm, self.topk_idx,
+                                   self.topk_w, self.counts, self.offsets, self.dst_row,
+                                   self.src_token, self.route_ws)
         with self._span("permute"):
             abi.moe_permute(x, self.dst_row, self.x_perm)
         if self.fp8:
@@ -289,11 +317,22 @@ class MoELayer:
         if self.fp8:
             self._backward_fp8(dout)
             return self._backward_tail(dout, self.dxs if self.shared else None)
-        with self._span("gemm2_dgrad"):
-            abi.moe_grouped_gemm_dgrad(self.dy, w["w2"], self.offsets, self.dab,
-                                       epilogue=abi.EPI_SWIGLU_BWD, ab=self.ab)
-        with self._span("gemm2_wgrad"):
-            abi.moe_grouped_gemm_wgrad(self.h, self.dy, self.offsets, self.dw2)
+        if self.recompute:
+            # H again from AB, into dAB's storage; used by the weight gradient
+            # before the dgrad overwrites that storage with dAB
+            with self._span("swiglu_recompute"):
+                abi.moe_swiglu(self.ab, self.h)
+            with self._span("gemm2_wgrad"):
+                abi.moe_grouped_gemm_wgrad(self.h, self.dy, self.offsets, self.dw2)
+            with self._span("gemm2_dgrad"):
+                abi.moe_grouped_gemm_dgrad(self.dy, w["w2"], self.offsets, self.dab,
+                                           epilogue=abi.EPI_SWIGLU_BWD, ab=self.ab)
+        else:
+            with self._span("gemm2_dgrad"):
+                abi.moe_grouped_gemm_dgrad(self.dy, w["w2"], self.offsets, self.dab,
+                                           epilogue=abi.EPI_SWIGLU_BWD, ab=self.ab)
+            with self._span("gemm2_wgrad"):
+                abi.moe_grouped_gemm_wgrad(self.h, self.dy, self.offsets, self.dw2)
         with self._span("gemm1_dgrad"):
             abi.moe_grouped_gemm_dgrad(self.dab, w["w13"], self.offsets, self.dx_perm)
         with self._span("gemm1_wgrad"):

@@ -23,19 +23,21 @@ SMALL_BF16_SOFTMAX = inputs.LayerConfig("small_bf16_zipf", T=513, d=128, E=16, k
                                         bias="zipf")
 
 
-def _run(cfg, seed):
-    print(f"layer {cfg.name} seed={seed}", flush=True)
-    inp = layer_inputs_without_near_ties(cfg, seed)
+def _run(cfg, seed, recompute_act=False):
+    print(f"layer {cfg.name} seed={seed} recompute={recompute_act}", flush=True)
+    inp = (inputs.layer_inputs(cfg, seed) if cfg.routing == "balanced"
+           else layer_inputs_without_near_ties(cfg, seed))
     w = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
-    layer = MoELayer(cfg, w, DEV)
+    layer = MoELayer(cfg, w, DEV, recompute_act=recompute_act)
     layer.forward(w["x"])
     layer.backward(w["dout"])
     torch.cuda.synchronize()
     shared = (np64(inp["ws13"]), np64(inp["ws2"])) if cfg.fs else None
     bias = None if inp["logit_bias"] is None else inp["logit_bias"].numpy()
+    given = inp["topk_idx_in"].numpy() if cfg.routing == "balanced" else None
     c = oracle.layer_forward(np64(inp["x"]), inp["w_r"].numpy(), np64(inp["w13"]),
                              np64(inp["w2"]), cfg.k, cfg.score, cfg.renorm, logit_bias=bias,
-                             shared=shared)
+                             shared=shared, given_experts=given)
     g = oracle.layer_backward(c, np64(inp["dout"]))
     return layer, c, g
 
@@ -69,6 +71,23 @@ def test_layer_tiny_fp32_with_shared_and_sigmoid(gpu):
     cfg = dataclasses.replace(inputs.CONFIGS["tiny_fp32"], name="tiny_fp32_shared", fs=64,
                               score="sigmoid", bias="normal")
     _check(cfg, *_run(cfg, 3))
+
+
+def test_layer_balanced_routing_replayed(gpu):
+    """Force-balanced routing (every expert exactly T*k/E rows), the experts
+    given and replayed; the routing weights still come from the keys."""
+    cfg = inputs.CONFIGS["small_balanced"]
+    layer, c, g = _run(cfg, 0)
+    assert (layer.counts.cpu().numpy() == cfg.T * cfg.k // cfg.E).all()
+    assert int(layer.route_status.item()) == 0
+    _check(cfg, layer, c, g)
+
+
+@pytest.mark.parametrize("cfg", [SMALL_BF16, inputs.CONFIGS["small_balanced"]],
+                         ids=lambda c: c.name)
+def test_layer_recompute_activation(gpu, cfg):
+    """H = silu(A) * B rebuilt from AB in the backward instead of kept."""
+    _check(cfg, *_run(cfg, 1, recompute_act=True))
 
 
 def test_layer_repeat_is_bitwise_deterministic(gpu):

@@ -322,3 +322,42 @@ def test_bf16_rounding_bit_exact(gpu):
     bad = np.nonzero(got != ref)
     assert len(bad[0]) == 0, (f"{len(bad[0])} mismatches, first: x={v[bad][:4].view(np.uint32)} "
                               f"got={got[bad][:4]} ref={ref[bad][:4]}")
+
+
+@pytest.mark.parametrize("E,k,score,renorm,kind", [
+    (13, 3, "softmax", True, "topk"), (256, 8, "sigmoid", True, "balanced"),
+    (300, 5, "softmax", False, "corrupt"), (64, 64, "sigmoid", False, "corrupt"),
+    (1000, 7, "sigmoid", True, "corrupt")])
+def test_route_replay_bit_exact(gpu, E, k, score, renorm, kind):
+    """Routing replayed from given experts: weights from the keys, the same
+    dispatch map; invalid slots (out of range, repeated) replaced by the
+    oracle's rule, with the status word set."""
+    T = 700 if kind != "balanced" else 512
+    print(f"route replay E={E} k={k} {score} renorm={renorm} {kind}", flush=True)
+    z = _keys(T, E, 4321 + E, "normal")
+    if kind == "topk":
+        idx = oracle.route(z, k, score, renorm)["topk_idx"]
+    elif kind == "balanced":
+        idx = inputs.balanced_experts(T, E, k, seed=1).numpy()
+    else:
+        rng = np.random.default_rng(E)
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        hit = rng.random((T, k)) < 0.05
+        idx[hit] = rng.integers(-3, E + 3, size=int(hit.sum()))
+        idx[::7, -1] = idx[::7, 0]  # repeats
+    r = oracle.route_replay(z, idx, score, renorm)
+    zz = torch.from_numpy(z).to(DEV)
+    ws = torch.empty(abi.moe_route_topk_workspace_bytes(T, E, k), dtype=torch.uint8, device=DEV)
+    g = {n: torch.empty(sh, dtype=dt, device=DEV) for n, sh, dt in [
+        ("topk_idx", (T, k), torch.int32), ("topk_w", (T, k), torch.float32),
+        ("counts", (E,), torch.int32), ("offsets", (E + 1,), torch.int64),
+        ("dst_row", (T, k), torch.int32), ("src_token", (T * k,), torch.int32)]}
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    abi.moe_route_replay(zz, torch.from_numpy(idx).to(DEV), abi.SOFTMAX if score == "softmax"
+                         else abi.SIGMOID, renorm, g["topk_idx"], g["topk_w"], g["counts"],
+                         g["offsets"], g["dst_row"], g["src_token"], ws, status=status)
+    for key in ("topk_idx", "counts", "offsets", "dst_row", "src_token"):
+        np.testing.assert_array_equal(g[key].cpu().numpy(), r[key], err_msg=key)
+    assert_close("topk_w", g["topk_w"], r["topk_w"], TOL["f32"])
+    assert int(status.item()) == int(r["changed"])
+    assert r["changed"] == (kind == "corrupt")

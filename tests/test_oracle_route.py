@@ -147,3 +147,59 @@ def test_route_bwd_finite_differences(score, renorm):
             num[t, e] = ((oracle.gates(zp, idx, score, renorm) - oracle.gates(zm, idx, score, renorm))
                          * dw).sum() / (2 * eps)
     np.testing.assert_allclose(dz, num, rtol=0, atol=1e-8)
+
+
+@pytest.mark.parametrize("score,renorm", [("softmax", True), ("softmax", False),
+                                          ("sigmoid", True), ("sigmoid", False)])
+def test_replaying_the_topk_selection_is_the_route(score, renorm):
+    """Replaying the experts the top-k route chose reproduces that route: same
+    weights, counts, offsets and permutation, and nothing was replaced."""
+    rng = np.random.default_rng(11)
+    z = rng.standard_normal((97, 13)).astype(np.float32)
+    r = oracle.route(z, 3, score, renorm)
+    rr = oracle.route_replay(z, r["topk_idx"], score, renorm)
+    assert not rr["changed"]
+    for key in ("topk_idx", "counts", "offsets", "dst_row", "src_token"):
+        np.testing.assert_array_equal(rr[key], r[key])
+    np.testing.assert_array_equal(rr["topk_w"], r["topk_w"])
+
+
+def test_canonical_experts_rule_brute_force():
+    """Invalid slots (outside [0, E) or repeating an earlier slot) get the
+    smallest expert the token does not use; valid slots are untouched; the
+    result is k distinct experts per token.  Checked against a direct
+    enumeration of the rule on small random cases."""
+    rng = np.random.default_rng(5)
+    for _ in range(300):
+        E = int(rng.integers(2, 7))
+        k = int(rng.integers(1, E + 1))
+        idx = rng.integers(-2, E + 2, size=(4, k))
+        got, changed = oracle.canonical_experts(idx, E)
+        any_bad = False
+        for t in range(4):
+            orig = list(idx[t])
+            bad = [not (0 <= orig[j] < E) or orig[j] in orig[:j] for j in range(k)]
+            any_bad |= any(bad)
+            row = list(got[t])
+            assert len(set(row)) == k and all(0 <= e < E for e in row)
+            for j in range(k):
+                if not bad[j]:
+                    assert row[j] == orig[j]
+                else:
+                    others = {row[s] for s in range(k) if s != j}
+                    assert row[j] == min(c for c in range(E) if c not in others)
+        assert changed == any_bad
+
+
+def test_balanced_assignment_is_exactly_balanced():
+    """The forced assignment of the balanced workload: every expert gets
+    exactly T*k/E pairs and each token's k experts are distinct."""
+    from routing_grouped_gemm_router_amd import inputs
+    for T, E, k in [(512, 16, 4), (8192, 256, 8), (96, 8, 8)]:
+        idx = inputs.balanced_experts(T, E, k, seed=3).numpy()
+        counts = np.bincount(idx.ravel(), minlength=E)
+        assert (counts == T * k // E).all()
+        assert all(len(set(row)) == k for row in idx)
+        r = oracle.route_replay(np.zeros((T, E), np.float32), idx, "sigmoid", True)
+        assert not r["changed"]
+        assert (r["counts"] == T * k // E).all()
