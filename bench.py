@@ -47,12 +47,15 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--recompute-act", action="store_true",
                     help="rebuild H = silu(A) * B in the backward instead of keeping it")
+    ap.add_argument("--gate-in-ffn", action="store_true",
+                    help="apply the routing weight before W2 (unweighted combine, no Y in the "
+                         "backward)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the CPU oracle sample")
     return ap.parse_args()
 
 
-def kernel_work(cfg, n_nonempty):
+def kernel_work(cfg, n_nonempty, gated=False):
     """Algorithmic FLOPs and HBM bytes per call of every span.
 
     FLOPs: 2 per multiply-add over the routed rows only.  Bytes: every
@@ -85,6 +88,16 @@ def kernel_work(cfg, n_nonempty):
     if cfg.gemm == "fp8":
         w.update(fp8_work(cfg, n_nonempty))
         return w
+    if gated:
+        # routing weight inside the expert: the combine backward is a gather of
+        # dout (no Y, no dot products); GEMM 2 dgrad also writes the gate partials
+        w.update({
+            "permute_weights": (0.0, 2 * idx + N * 4),
+            "combine_bwd": (0.0, T * d * s + idx + N * d * s),
+            "gate_grad": (0.0, N * (f // 64) * 4 + idx + N * 4),
+        })
+        fl, by = w["gemm2_dgrad"]
+        w["gemm2_dgrad"] = (fl, by + N * 4 + N * (f // 64) * 4)
     if fs:
         w.update({
             "shared_gemm1_fwd": (2.0 * T * d * 2 * fs, T * d * s + d * 2 * fs * s + T * 3 * fs * s),
@@ -150,15 +163,16 @@ def fp8_work(cfg, n_nonempty):
     return w
 
 
-def traffic_for(kernel):
+def traffic_for(workload, kernel):
     """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE and
-    WRITE_SIZE, scaled by a copy of known size), if the committed measurement
-    was taken on the current kernel sources; else None."""
+    WRITE_SIZE, scaled by a copy of known size) for this workload and kernel,
+    if the committed measurement was taken on the current kernel sources;
+    else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(path)).get(kernel)
+        rec = json.load(open(path)).get(f"{workload}/{kernel}")
     except (OSError, ValueError):
         return None
     if not rec:
@@ -246,7 +260,8 @@ def main():
     gemm_peak = PEAK_FP8_TFLOPS if cfg.gemm == "fp8" else PEAK_BF16_TFLOPS
     dev = "cuda"
     inp = inputs.layer_inputs(cfg, args.seed, dev)
-    layer = MoELayer(cfg, inp, dev, recompute_act=args.recompute_act)
+    layer = MoELayer(cfg, inp, dev, recompute_act=args.recompute_act,
+                     gate_in_ffn=args.gate_in_ffn)
     x, dout = inp["x"], inp["dout"]
     for _ in range(args.warmup):
         layer.forward(x)
@@ -268,7 +283,7 @@ def main():
     spans = timer.summary()
     counts = layer.counts.cpu()
     n_nonempty = int((counts > 0).sum())
-    work = kernel_work(cfg, n_nonempty)
+    work = kernel_work(cfg, n_nonempty, gated=args.gate_in_ffn)
     kernels = {}
     for name, (ms, n) in spans.items():
         fl, by = work[name]
@@ -299,7 +314,7 @@ def main():
     roof["alg_flops_per_launch"] = fl
     roof["alg_bytes_per_launch"] = int(by)
     roof["ms_per_launch"] = ms
-    roof["traffic"] = traffic_for(dom)
+    roof["traffic"] = traffic_for(cfg.name, dom)
 
     line = {
         "metric": METRIC,
@@ -315,7 +330,7 @@ def main():
         "dtype": cfg.gemm,
         "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights, generated on the GPU)",
         "config": {"workload": cfg.name, "routing": cfg.routing,
-                   "recompute_act": bool(args.recompute_act),
+                   "recompute_act": bool(args.recompute_act), "gate_in_ffn": bool(args.gate_in_ffn),
                    "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
                    "ffn": cfg.f, "shared_ffn": cfg.fs, "score": cfg.score, "renorm": cfg.renorm,
                    "router_bias": cfg.bias, "experts_with_rows": n_nonempty,

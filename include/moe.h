@@ -276,6 +276,46 @@ int moe_grouped_gemm_fp8_wgrad(const uint8_t* A_t, const float* a_scale, const u
                                int64_t ldm, int64_t K, int64_t N, int dB_dtype, int accumulate,
                                void* dB, void* stream);
 
+/* ------------------------------- Routing weight applied inside the expert -- */
+/* The memory-saving arrangement of the permutation (section 4, Memory): the
+ * routing weight of each permuted row scales H before W2,
+ *   y'[r] = (w_perm[r] * silu(a[r]) * b[r]) . W2[e],
+ * so the combine is an unweighted sum (moe_unpermute_combine with topk_w NULL)
+ * and its backward is a plain gather of dout (moe_permute of dout), with no
+ * need to keep Y.  The routing-weight gradient is <dH'[r], h[r]> over the ffn
+ * axis, dH' = dout[t] . W2[e]^T. */
+
+/* w_perm[dst_row[t, j]] = topk_w[t, j]: the routing weight of every permuted
+ * row.  topk_w, dst_row [T, k]; w_perm [T*k] fp32. */
+int moe_permute_weights(const float* topk_w, const int32_t* dst_row, int64_t T, int32_t k,
+                        float* w_perm, void* stream);
+
+/* Forward GEMM 1 with the SwiGLU epilogue and the routing weight applied:
+ * as moe_grouped_gemm_fwd with MOE_EPI_SWIGLU, except
+ *   H [M, N/2] = row_scale[row] * silu(a) * b   (AB [M, N] unscaled, or NULL).
+ * row_scale [M] fp32 (moe_permute_weights).  bf16 only; K % 64 == 0,
+ * (N/2) % 64 == 0. */
+int moe_grouped_gemm_gated_fwd(const void* A, const void* B, const int64_t* offsets, int32_t G,
+                               int64_t M, int64_t K, int64_t N, int dtype, const float* row_scale,
+                               void* AB, void* H, void* stream);
+
+/* Data gradient of GEMM 2 with the SwiGLU backward and the routing weight
+ * applied: dH' = dC[rows g] . B[g]^T ([M, K], not stored), then
+ *   dAB [M, 2K] = SwiGLU'(row_scale[row] * dH')  (as MOE_EPI_SWIGLU_BWD, from ab)
+ *   gate_partials[row, c] = sum over columns 64c .. 64c+63 of dH' * h,
+ *     h = silu(a) * b from ab; gate_partials [M, K/64] fp32.
+ * bf16 only; N % 64 == 0, K % 128 == 0. */
+int moe_grouped_gemm_gated_dgrad(const void* dC, const void* B, const int64_t* offsets, int32_t G,
+                                 int64_t M, int64_t K, int64_t N, int dtype, const void* ab,
+                                 const float* row_scale, void* dAB, float* gate_partials,
+                                 void* stream);
+
+/* Routing-weight gradient from the partials, summed in column order:
+ *   d_topk_w[t, j] = sum_{c < P} gate_partials[dst_row[t, j], c].
+ * gate_partials [T*k, P] fp32, dst_row [T, k], d_topk_w [T, k] fp32 out. */
+int moe_gate_grad(const float* gate_partials, int64_t P, const int32_t* dst_row, int64_t T,
+                  int32_t k, float* d_topk_w, void* stream);
+
 /* -------------------------------------------------------------- Combine -- */
 
 /* Unpermute and combine (section 2, Combine: rows return to sequence order,
@@ -283,7 +323,8 @@ int moe_grouped_gemm_fp8_wgrad(const uint8_t* A_t, const float* a_scale, const u
  *   out[t] = sum_j topk_w[t, j] * y_perm[dst_row[t, j]] + shared_y[t]
  * fp32 accumulation in slot order, one rounding to `dtype`.
  * y_perm [T*k, d], shared_y [T, d] or NULL, out [T, d], all `dtype`;
- * topk_w [T, k] fp32. */
+ * topk_w [T, k] fp32, or NULL for an unweighted sum (the routing weights
+ * already applied inside the experts, moe_grouped_gemm_gated_fwd). */
 int moe_unpermute_combine(const void* y_perm, int dtype, const float* topk_w,
                           const int32_t* dst_row, const void* shared_y, int64_t T, int64_t d,
                           int32_t k, void* out, void* stream);

@@ -36,7 +36,7 @@ __all__ = [
     "grouped_gemm_fwd", "grouped_gemm_dgrad", "grouped_gemm_wgrad", "sigmoid", "silu",
     "swiglu", "swiglu_bwd", "unpermute_combine", "unpermute_combine_bwd",
     "expert_ffn", "expert_ffn_bwd", "layer_forward", "layer_backward",
-    "expert_wgrad_columns",
+    "expert_wgrad_columns", "layer_forward_gated", "layer_backward_gated",
 ]
 
 
@@ -424,6 +424,93 @@ def layer_backward(cache, dout):
             dx[t] += dxt
             dW13[e] += dw13
             dW2[e] += dw2
+    res = {}
+    if cache["shared"] is not None:
+        ws13, ws2 = cache["shared"]
+        dWs13 = np.zeros(np.shape(ws13))
+        dWs2 = np.zeros(np.shape(ws2))
+        for t in range(T):
+            a, b, h, _ = cache["shared_acts"][t]
+            dxt, dw13, dw2 = expert_ffn_bwd(x[t], ws13, ws2, a, b, h, dout[t])
+            dx[t] += dxt
+            dWs13 += dw13
+            dWs2 += dw2
+        res.update(dWs13=dWs13, dWs2=dWs2)
+    dz = route_bwd(cache["z"], idx, w, dw, cache["score"], cache["renorm"])
+    dWr, dx_router = router_logits_bwd(x, cache["w_r"], dz)
+    dx += dx_router
+    res.update(dx=dx, d_logits=dz, dW_r=dWr, dW13=dW13, dW2=dW2, d_topk_w=dw)
+    return res
+
+
+def layer_forward_gated(x, w_r, w13, w2, k, score, renorm, logit_bias=None,
+                        shared=None, z=None, given_experts=None):
+    """The forward with each routing weight applied inside its expert, before
+    W2: y'_tj = (w_tj h_tj) W2 and out_t = sum_j y'_tj (+ shared), an
+    unweighted combine.  This is the memory-saving rearrangement of the
+    permutation the pages' section 4 (Memory) mentions -- the plain reading:
+    by linearity it moves the weight across W2 without extra compute, and the
+    backward then needs no Y.  Equal to ``layer_forward`` up to rounding."""
+    x = f64(x)
+    T, d = x.shape
+    if z is None:
+        z = router_logits(x, w_r, logit_bias)
+    r = (route(z, k, score, renorm) if given_experts is None
+         else route_replay(z, given_experts, score, renorm))
+    idx, w = r["topk_idx"], r["topk_w"]
+    out = np.zeros((T, d))
+    acts = {}
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j])
+            f = w13[e].shape[1] // 2
+            a = x[t] @ f64(w13[e][:, :f])
+            b = x[t] @ f64(w13[e][:, f:])
+            h = silu(a) * b
+            hg = w[t, j] * h
+            out[t] += hg @ f64(w2[e])
+            acts[(t, j)] = (a, b, h, hg)
+    shared_acts = None
+    if shared is not None:
+        shared_acts = []
+        for t in range(T):
+            a, b, h, y = expert_ffn(x[t], shared[0], shared[1])
+            shared_acts.append((a, b, h, y))
+            out[t] += y
+    return dict(out=out, z=z, route=r, acts=acts, shared_acts=shared_acts,
+                x=x, w_r=w_r, w13=w13, w2=w2, k=k, score=score, renorm=renorm,
+                shared=shared)
+
+
+def layer_backward_gated(cache, dout):
+    """Backward of ``layer_forward_gated``.  For each (t, j): dy' = dout_t
+    (the combine is unweighted); dh' = dy' W2^T; the routing-weight gradient
+    is <dh', h> over the ffn axis; dh = w dh' goes through SwiGLU' as usual;
+    dW2 gets (w h)^T dy'.  Same outputs as ``layer_backward``."""
+    dout = f64(dout)
+    x, w13, w2 = cache["x"], cache["w13"], cache["w2"]
+    r = cache["route"]
+    idx, w = r["topk_idx"], r["topk_w"]
+    T, k = idx.shape
+    dx = np.zeros_like(x)
+    dW13 = np.zeros(np.shape(w13))
+    dW2 = np.zeros(np.shape(w2))
+    dw = np.zeros((T, k))
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j])
+            f = w13[e].shape[1] // 2
+            a, b, h, hg = cache["acts"][(t, j)]
+            dhg = f64(w2[e]) @ dout[t]
+            dw[t, j] = dhg @ h
+            dh = w[t, j] * dhg
+            s = sigmoid(a)
+            da = dh * b * s * (1.0 + a * (1.0 - s))
+            db = dh * a * s
+            dW2[e] += np.outer(hg, dout[t])
+            dW13[e][:, :f] += np.outer(x[t], da)
+            dW13[e][:, f:] += np.outer(x[t], db)
+            dx[t] += f64(w13[e][:, :f]) @ da + f64(w13[e][:, f:]) @ db
     res = {}
     if cache["shared"] is not None:
         ws13, ws2 = cache["shared"]

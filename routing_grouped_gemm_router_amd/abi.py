@@ -37,6 +37,12 @@ SIGNATURES = {
     "moe_route_replay": (_int, [_p, _p, _i64, _i32, _i32, _int, _int, _p, _p, _p, _p, _p, _p, _p,
                                 _p, _sz, _p]),
     "moe_route_topk_bwd": (_int, [_p, _p, _p, _p, _i64, _i32, _i32, _int, _int, _p, _p]),
+    "moe_permute_weights": (_int, [_p, _p, _i64, _i32, _p, _p]),
+    "moe_grouped_gemm_gated_fwd": (_int, [_p, _p, _p, _i32, _i64, _i64, _i64, _int, _p, _p, _p,
+                                          _p]),
+    "moe_grouped_gemm_gated_dgrad": (_int, [_p, _p, _p, _i32, _i64, _i64, _i64, _int, _p, _p, _p,
+                                            _p, _p]),
+    "moe_gate_grad": (_int, [_p, _i64, _p, _i64, _i32, _p, _p]),
     "moe_permute": (_int, [_p, _int, _p, _i64, _i64, _i32, _p, _p]),
     "moe_permute_bwd": (_int, [_p, _int, _p, _i64, _i64, _i32, _p, _p, _p, _p]),
     "moe_grouped_gemm_fwd": (_int, [_p, _p, _p, _i32, _i64, _i64, _i64, _int, _int, _p, _p, _p]),
@@ -163,6 +169,30 @@ def moe_route_replay(logits, topk_idx_in, score, renorm, topk_idx, topk_w, count
           int(renorm), _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(dst_row),
           _ptr(src_token), _ptr(status), _ptr(workspace),
           workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def moe_permute_weights(topk_w, dst_row, w_perm, stream=None):
+    T, k = dst_row.shape
+    _call("moe_permute_weights", _ptr(topk_w), _ptr(dst_row), T, k, _ptr(w_perm), _stream(stream))
+
+
+def moe_grouped_gemm_gated_fwd(A, B, offsets, row_scale, AB, H, stream=None):
+    G, K, N = B.shape
+    _call("moe_grouped_gemm_gated_fwd", _ptr(A), _ptr(B), _ptr(offsets), G, A.shape[0], K, N,
+          dtype_code(A), _ptr(row_scale), _ptr(AB), _ptr(H), _stream(stream))
+
+
+def moe_grouped_gemm_gated_dgrad(dC, B, offsets, ab, row_scale, dAB, gate_partials, stream=None):
+    G, K, N = B.shape
+    _call("moe_grouped_gemm_gated_dgrad", _ptr(dC), _ptr(B), _ptr(offsets), G, dC.shape[0], K, N,
+          dtype_code(dC), _ptr(ab), _ptr(row_scale), _ptr(dAB), _ptr(gate_partials),
+          _stream(stream))
+
+
+def moe_gate_grad(gate_partials, dst_row, d_topk_w, stream=None):
+    T, k = dst_row.shape
+    _call("moe_gate_grad", _ptr(gate_partials), gate_partials.shape[1], _ptr(dst_row), T, k,
+          _ptr(d_topk_w), _stream(stream))
 
 
 def moe_route_topk_bwd(logits, topk_idx, topk_w, d_topk_w, score, renorm, d_logits, stream=None):

@@ -228,6 +228,11 @@ struct Params {
   const float* sa;  // fp8 row scales of A: [Kc/128][M] (row groups), [M/128][Kc] (wgrad)
   const float* sb;  // fp8 row scales of B: [G][Kc/128][Nout] (row groups), [M/128][Nout] (wgrad)
   int64_t ldm;      // fp8 wgrad: row length of the transposed operands
+  // Routing weight applied inside the expert (row-group modes with SwiGLU):
+  // forward H = row_scale[row] * silu(a) * b; backward dH = row_scale[row] *
+  // dH' and gate_part[row, c] = sum over the 64 columns 64c.. of dH' * h.
+  const float* row_scale;
+  float* gate_part;
 };
 
 // What a tile is: a ragged row block x 128 columns of one group (forward,
@@ -654,7 +659,41 @@ __device__ __forceinline__ void epilogue(const Params& p, const Tile& t, const f
       for (int i = 0; i < 4; ++i) {
         const int idx = lane + 64 * i;
         const int m = idx >> 3, c = idx & 7;
-        if (ii * 32 + m >= rows_w) continue;
+        const bool valid = ii * 32 + m < rows_w;
+        if (MODE == DGRAD_SWIGLU_BWD && p.row_scale) {
+          // gated: dH = w dH', and the partial <dH', h> of this row over the
+          // wave's 64 columns (8 consecutive lanes hold the row's 8 chunks)
+          const u32x4_t vv = *(const LDS_AS u32x4_t*)(stg + stg_off(m, c));
+          const int64_t row = t.row0 + wm * 64 + ii * 32 + m;
+          const int64_t col = t.nt * BN + wn * 64 + 8 * c;
+          const int64_t w2 = 2 * p.Nout;
+          float dot = 0.0f;
+          if (valid) {
+            float dh[8], a[8], b[8], da[8], db[8];
+            unpack8(make_uint4(vv.x, vv.y, vv.z, vv.w), dh);
+            unpack8(*reinterpret_cast<const uint4*>(p.ab + row * w2 + col), a);
+            unpack8(*reinterpret_cast<const uint4*>(p.ab + row * w2 + p.Nout + col), b);
+            const float rs = p.row_scale[row];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float sg = 1.0f / (1.0f + expf(-a[e]));
+              dot += dh[e] * (a[e] * sg * b[e]);
+              const float d = rs * dh[e];
+              da[e] = d * b[e] * sg * (1.0f + a[e] * (1.0f - sg));
+              db[e] = d * a[e] * sg;
+            }
+            bf16_t* C = static_cast<bf16_t*>(p.C);
+            *reinterpret_cast<uint4*>(C + row * w2 + col) = pack8(da);
+            *reinterpret_cast<uint4*>(C + row * w2 + p.Nout + col) = pack8(db);
+          }
+          dot += __shfl_xor(dot, 1, 64);
+          dot += __shfl_xor(dot, 2, 64);
+          dot += __shfl_xor(dot, 4, 64);
+          if (valid && c == 0)
+            p.gate_part[row * (p.Nout / 64) + (t.nt * BN + wn * 64) / 64] = dot;
+          continue;
+        }
+        if (!valid) continue;
         const u32x4_t vv = *(const LDS_AS u32x4_t*)(stg + stg_off(m, c));
         const uint4 v = make_uint4(vv.x, vv.y, vv.z, vv.w);
         const int64_t row = t.row0 + wm * 64 + ii * 32 + m;
@@ -700,7 +739,13 @@ __device__ __forceinline__ void epilogue(const Params& p, const Tile& t, const f
       }
     }
     if (MODE == FWD_SWIGLU) {
-      // H = silu(gate) * up for these 32 rows: 32 columns per wave
+      // H = silu(gate) * up (times the row's routing weight when it is
+      // applied inside the expert) for these 32 rows: 32 columns per wave
+      float rs = 1.0f;
+      if (p.row_scale) {
+        const int m = lane & 31;
+        rs = ii * 32 + m < rows_w ? p.row_scale[t.row0 + wm * 64 + ii * 32 + m] : 0.0f;
+      }
 #pragma unroll
       for (int vg = 0; vg < 4; ++vg) {
         const int m = lane & 31;
@@ -709,7 +754,7 @@ __device__ __forceinline__ void epilogue(const Params& p, const Tile& t, const f
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float g = acc[ii][0][vg * 4 + e], u = acc[ii][1][vg * 4 + e];
-          h[e] = g / (1.0f + expf(-g)) * u;
+          h[e] = g / (1.0f + expf(-g)) * u * rs;
         }
         u32x2_t w;
         w.x = pack2(h[0], h[1]);
@@ -946,6 +991,26 @@ hipError_t launch_gg_bf16_wgrad(const void* A, const void* dC, const int64_t* of
   p.out_f32 = db_f32;
   p.accumulate = accumulate;
   return run_wgrad<false>(p, s);
+}
+
+hipError_t launch_gg_bf16_gated_fwd(const void* A, const void* B, const int64_t* off, int G,
+                                    int64_t M, int64_t K, int64_t N, const float* row_scale,
+                                    void* AB, void* H, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  Params p = make_params(A, B, off, G, M, K, N, AB, H, nullptr);
+  p.row_scale = row_scale;
+  return run_rows<FWD_SWIGLU, false>(p, s);
+}
+
+hipError_t launch_gg_bf16_gated_dgrad(const void* dC, const void* B, const int64_t* off, int G,
+                                      int64_t M, int64_t K, int64_t N, const void* ab,
+                                      const float* row_scale, void* dAB, float* gate_part,
+                                      hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  Params p = make_params(dC, B, off, G, M, N, K, dAB, nullptr, ab);
+  p.row_scale = row_scale;
+  p.gate_part = gate_part;
+  return run_rows<DGRAD_SWIGLU_BWD, false>(p, s);
 }
 
 hipError_t launch_gg_fp8_fwd(const uint8_t* A, const float* sa, const uint8_t* Bt, const float* sb,

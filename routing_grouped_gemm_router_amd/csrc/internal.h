@@ -65,6 +65,17 @@ hipError_t launch_gg_bf16_wgrad(const void* A, const void* dC, const int64_t* of
                                 void* dB, hipStream_t s);
 
 // grouped_gemm.hip, fp8 E4M3 operands (all k-contiguous) with fp32 row scales
+hipError_t launch_gg_bf16_gated_fwd(const void* A, const void* B, const int64_t* off, int G,
+                                    int64_t M, int64_t K, int64_t N, const float* row_scale,
+                                    void* AB, void* H, hipStream_t s);
+hipError_t launch_gg_bf16_gated_dgrad(const void* dC, const void* B, const int64_t* off, int G,
+                                      int64_t M, int64_t K, int64_t N, const void* ab,
+                                      const float* row_scale, void* dAB, float* gate_part,
+                                      hipStream_t s);
+hipError_t launch_permute_weights(const float* topk_w, const int32_t* dst_row, int64_t T, int k,
+                                  float* w_perm, hipStream_t s);
+hipError_t launch_gate_grad(const float* gate_part, int64_t P, const int32_t* dst_row, int64_t T,
+                            int k, float* d_topk_w, hipStream_t s);
 hipError_t launch_gg_fp8_fwd(const uint8_t* A, const float* sa, const uint8_t* Bt, const float* sb,
                              const int64_t* off, int G, int64_t M, int64_t K, int64_t N, int epi,
                              void* C, void* H, hipStream_t s);

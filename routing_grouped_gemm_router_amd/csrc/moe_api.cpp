@@ -344,13 +344,36 @@ int moe_unpermute_combine(const void* y_perm, int dtype, const float* topk_w,
   int st = check_row_vectors(dtype, d, "moe_unpermute_combine");
   if (st != MOE_OK) return st;
   if (T == 0) return ok();
-  REQUIRE(y_perm && topk_w && dst_row && out, MOE_ERR_NULL,
-          "moe_unpermute_combine: y_perm, topk_w, dst_row and out are required");
+  REQUIRE(y_perm && dst_row && out, MOE_ERR_NULL,
+          "moe_unpermute_combine: y_perm, dst_row and out are required");
   REQUIRE(aligned16(y_perm) && aligned16(out) && aligned16(shared_y), MOE_ERR_UNSUPPORTED,
           "moe_unpermute_combine: 16-byte alignment needed");
   return hip_status(moe::launch_combine(y_perm, dtype, topk_w, dst_row, shared_y, T, d, k, out,
                                         as_stream(stream)),
                     "moe_unpermute_combine");
+}
+
+int moe_permute_weights(const float* topk_w, const int32_t* dst_row, int64_t T, int32_t k,
+                        float* w_perm, void* stream) {
+  REQUIRE(T >= 0 && k >= 1 && T * k < (int64_t(1) << 31), MOE_ERR_SHAPE,
+          "moe_permute_weights: T=%lld k=%d", static_cast<long long>(T), k);
+  if (T == 0) return ok();
+  REQUIRE(topk_w && dst_row && w_perm, MOE_ERR_NULL, "moe_permute_weights: all pointers are required");
+  return hip_status(moe::launch_permute_weights(topk_w, dst_row, T, k, w_perm, as_stream(stream)),
+                    "moe_permute_weights");
+}
+
+int moe_gate_grad(const float* gate_partials, int64_t P, const int32_t* dst_row, int64_t T,
+                  int32_t k, float* d_topk_w, void* stream) {
+  REQUIRE(T >= 0 && k >= 1 && P >= 1 && T * k < (int64_t(1) << 31), MOE_ERR_SHAPE,
+          "moe_gate_grad: T=%lld k=%d P=%lld", static_cast<long long>(T), k,
+          static_cast<long long>(P));
+  if (T == 0) return ok();
+  REQUIRE(gate_partials && dst_row && d_topk_w, MOE_ERR_NULL,
+          "moe_gate_grad: all pointers are required");
+  return hip_status(moe::launch_gate_grad(gate_partials, P, dst_row, T, k, d_topk_w,
+                                          as_stream(stream)),
+                    "moe_gate_grad");
 }
 
 int moe_unpermute_combine_bwd(const void* dout, const void* y_perm, int dtype, const float* topk_w,
@@ -373,6 +396,46 @@ int moe_unpermute_combine_bwd(const void* dout, const void* y_perm, int dtype, c
                     "moe_unpermute_combine_bwd");
 }
 
+
+int moe_grouped_gemm_gated_fwd(const void* A, const void* B, const int64_t* offsets, int32_t G,
+                               int64_t M, int64_t K, int64_t N, int dtype, const float* row_scale,
+                               void* AB, void* H, void* stream) {
+  const char* fn = "moe_grouped_gemm_gated_fwd";
+  int st = check_gemm(fn, A, B, offsets, G, M, K, N, dtype);
+  if (st != MOE_OK) return st;
+  REQUIRE(dtype == MOE_BF16, MOE_ERR_UNSUPPORTED, "%s: bf16 only", fn);
+  REQUIRE(K % 64 == 0 && N % 2 == 0 && (N / 2) % 64 == 0, MOE_ERR_UNSUPPORTED,
+          "%s: needs K %% 64 == 0 and f %% 64 == 0 (K=%lld, N=%lld)", fn,
+          static_cast<long long>(K), static_cast<long long>(N));
+  if (M == 0) return ok();
+  REQUIRE(row_scale && H, MOE_ERR_NULL, "%s: row_scale and H are required", fn);
+  REQUIRE(aligned16(H) && (AB == nullptr || aligned16(AB)), MOE_ERR_UNSUPPORTED,
+          "%s: outputs must be 16-byte aligned", fn);
+  return hip_status(moe::launch_gg_bf16_gated_fwd(A, B, offsets, G, M, K, N, row_scale, AB, H,
+                                                  as_stream(stream)),
+                    fn);
+}
+
+int moe_grouped_gemm_gated_dgrad(const void* dC, const void* B, const int64_t* offsets, int32_t G,
+                                 int64_t M, int64_t K, int64_t N, int dtype, const void* ab,
+                                 const float* row_scale, void* dAB, float* gate_partials,
+                                 void* stream) {
+  const char* fn = "moe_grouped_gemm_gated_dgrad";
+  int st = check_gemm(fn, dC, B, offsets, G, M, K, N, dtype);
+  if (st != MOE_OK) return st;
+  REQUIRE(dtype == MOE_BF16, MOE_ERR_UNSUPPORTED, "%s: bf16 only", fn);
+  REQUIRE(N % 64 == 0 && K % 128 == 0, MOE_ERR_UNSUPPORTED,
+          "%s: needs N %% 64 == 0 and K %% 128 == 0 (K=%lld, N=%lld)", fn,
+          static_cast<long long>(K), static_cast<long long>(N));
+  if (M == 0) return ok();
+  REQUIRE(ab && row_scale && dAB && gate_partials, MOE_ERR_NULL,
+          "%s: ab, row_scale, dAB and gate_partials are required", fn);
+  REQUIRE(aligned16(ab) && aligned16(dAB), MOE_ERR_UNSUPPORTED, "%s: ab and dAB must be 16-byte aligned",
+          fn);
+  return hip_status(moe::launch_gg_bf16_gated_dgrad(dC, B, offsets, G, M, K, N, ab, row_scale,
+                                                    dAB, gate_partials, as_stream(stream)),
+                    fn);
+}
 
 int moe_quant_fp8_rows(const void* x, int64_t M, int64_t K, uint8_t* q, float* scale_t,
                        void* stream) {

@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void permute_bwd_kernel(const T* __restrict__ 
   }
 }
 
-// out[t] = sum_j w[t, j] * y[dst_row[t, j]] + shared[t]
+// out[t] = sum_j w[t, j] * y[dst_row[t, j]] + shared[t]  (w = 1 without topk_w)
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y,
                                                       const float* __restrict__ topk_w,
@@ -133,10 +133,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y,
     for (int j = 0; j < k; ++j) {
       const int64_t r = dst_row[t * k + j];
       if (r < 0 || r >= nrows) continue;
-      const float w = topk_w[t * k + j];
       Vec<T>::unpack(reinterpret_cast<const uint4*>(y + r * d)[v], tmp);
+      if (topk_w) {
+        const float w = topk_w[t * k + j];
 #pragma unroll
-      for (int i = 0; i < VN; ++i) acc[i] += w * tmp[i];
+        for (int i = 0; i < VN; ++i) acc[i] += w * tmp[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < VN; ++i) acc[i] += tmp[i];
+      }
     }
     if (shared) {
       Vec<T>::unpack(reinterpret_cast<const uint4*>(shared + t * d)[v], tmp);
@@ -191,6 +196,31 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ 
     const float s = wave_sum(dot[j]);
     if (lane == 0) d_w[t * k + j] = s;
   }
+}
+
+// Routing weight of every permuted row: w_perm[dst_row[t, j]] = w[t, j].
+__global__ __launch_bounds__(256) void permute_weights_kernel(const float* __restrict__ topk_w,
+                                                              const int32_t* __restrict__ dst_row,
+                                                              int64_t n, float* __restrict__ w_perm) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int64_t r = dst_row[i];
+  if (r >= 0 && r < n) w_perm[r] = topk_w[i];
+}
+
+// Gradient of the routing weights applied inside the experts:
+// d_w[t, j] = sum_c gate_part[dst_row[t, j], c], c = 0 .. P-1 in order.
+__global__ __launch_bounds__(256) void gate_grad_kernel(const float* __restrict__ gate_part,
+                                                        int64_t P,
+                                                        const int32_t* __restrict__ dst_row,
+                                                        int64_t n, float* __restrict__ d_w) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int64_t r = dst_row[i];
+  float s = 0.0f;
+  if (r >= 0 && r < n)
+    for (int64_t c = 0; c < P; ++c) s += gate_part[r * P + c];
+  d_w[i] = s;
 }
 
 // h = silu(a) * b over rows of ab = [a | b]
@@ -316,6 +346,24 @@ hipError_t launch_combine_bwd(const void* dout, const void* y, int dtype, const 
   else
     combine_bwd_dispatch<bf16_t>(static_cast<const bf16_t*>(dout), static_cast<const bf16_t*>(y),
                                  topk_w, dst_row, T, d, k, static_cast<bf16_t*>(dy), d_w, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_weights(const float* topk_w, const int32_t* dst_row, int64_t T, int k,
+                                  float* w_perm, hipStream_t s) {
+  const int64_t n = T * k;
+  if (n == 0) return hipSuccess;
+  permute_weights_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), 256, 0, s>>>(
+      topk_w, dst_row, n, w_perm);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_grad(const float* gate_part, int64_t P, const int32_t* dst_row, int64_t T,
+                            int k, float* d_topk_w, hipStream_t s) {
+  const int64_t n = T * k;
+  if (n == 0) return hipSuccess;
+  gate_grad_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), 256, 0, s>>>(
+      gate_part, P, dst_row, n, d_topk_w);
   return hipGetLastError();
 }
 

@@ -65,8 +65,16 @@ class MoELayer:
     w13 [E, d, 2f], w2 [E, f, d] and, with a shared expert, ws13 [d, 2fs],
     ws2 [fs, d] (activation dtype)."""
 
-    def __init__(self, cfg, weights, device="cuda", recompute_act=False):
+    def __init__(self, cfg, weights, device="cuda", recompute_act=False, gate_in_ffn=False):
         self.cfg = cfg
+        # gate_in_ffn: the routing weight scales H before W2 (moe_permute_weights,
+        # moe_grouped_gemm_gated_fwd); the combine is an unweighted sum and its
+        # backward a gather of dout, so Y is not needed by the backward; the
+        # routing-weight gradient comes from the GEMM 2 dgrad epilogue
+        # (moe_grouped_gemm_gated_dgrad, moe_gate_grad).  bf16 only.
+        self.gated = gate_in_ffn
+        if gate_in_ffn and (cfg.gemm != "bf16" or recompute_act):
+            raise ValueError("gate_in_ffn: bf16 expert GEMMs, without recompute_act")
         # recompute_act: H = silu(A) * B is not kept from the forward to the
         # backward; the backward rebuilds it from AB (moe_swiglu).  H then lives
         # in the storage of dAB, which holds nothing until the backward.
@@ -122,6 +130,9 @@ class MoELayer:
             self.dxs = emp(T, d)
             self.dws13 = emp(1, d, 2 * fs)
             self.dws2 = emp(1, fs, d)
+        if self.gated:
+            self.w_perm = emp(N, dtype=torch.float32)
+            self.gate_part = emp(N, f // 64, dtype=torch.float32)
         self.fp8 = cfg.gemm == "fp8"
         if self.fp8:
             self._alloc_fp8()
@@ -290,9 +301,16 @@ class MoELayer:
                 abi.moe_unpermute_combine(self.y, self.topk_w, self.dst_row,
                                           self.ys if self.shared else None, self.out)
             return self.out
-        with self._span("gemm1_fwd"):
-            abi.moe_grouped_gemm_fwd(self.x_perm, w["w13"], self.offsets, self.ab, self.h,
-                                     epilogue=abi.EPI_SWIGLU)
+        if self.gated:
+            with self._span("permute_weights"):
+                abi.moe_permute_weights(self.topk_w, self.dst_row, self.w_perm)
+            with self._span("gemm1_fwd"):
+                abi.moe_grouped_gemm_gated_fwd(self.x_perm, w["w13"], self.offsets, self.w_perm,
+                                               self.ab, self.h)
+        else:
+            with self._span("gemm1_fwd"):
+                abi.moe_grouped_gemm_fwd(self.x_perm, w["w13"], self.offsets, self.ab, self.h,
+                                         epilogue=abi.EPI_SWIGLU)
         with self._span("gemm2_fwd"):
             abi.moe_grouped_gemm_fwd(self.h, w["w2"], self.offsets, self.y)
         ys = None
@@ -304,7 +322,8 @@ class MoELayer:
                 abi.moe_grouped_gemm_fwd(self.hs, self.ws2, self.off_all, self.ys)
             ys = self.ys
         with self._span("combine"):
-            abi.moe_unpermute_combine(self.y, self.topk_w, self.dst_row, ys, self.out)
+            abi.moe_unpermute_combine(self.y, None if self.gated else self.topk_w, self.dst_row,
+                                      ys, self.out)
         return self.out
 
     # ----------------------------------------------------------- backward --
@@ -312,12 +331,23 @@ class MoELayer:
         c, w = self.cfg, self.w
         x = self.x
         with self._span("combine_bwd"):
-            abi.moe_unpermute_combine_bwd(dout, self.y, self.topk_w, self.dst_row, self.dy,
-                                          self.d_topk_w)
+            if self.gated:  # unweighted combine: its backward gathers dout
+                abi.moe_permute(dout, self.dst_row, self.dy)
+            else:
+                abi.moe_unpermute_combine_bwd(dout, self.y, self.topk_w, self.dst_row, self.dy,
+                                              self.d_topk_w)
         if self.fp8:
             self._backward_fp8(dout)
             return self._backward_tail(dout, self.dxs if self.shared else None)
-        if self.recompute:
+        if self.gated:
+            with self._span("gemm2_dgrad"):
+                abi.moe_grouped_gemm_gated_dgrad(self.dy, w["w2"], self.offsets, self.ab,
+                                                 self.w_perm, self.dab, self.gate_part)
+            with self._span("gate_grad"):
+                abi.moe_gate_grad(self.gate_part, self.dst_row, self.d_topk_w)
+            with self._span("gemm2_wgrad"):
+                abi.moe_grouped_gemm_wgrad(self.h, self.dy, self.offsets, self.dw2)
+        elif self.recompute:
             # H again from AB, into dAB's storage; used by the weight gradient
             # before the dgrad overwrites that storage with dAB
             with self._span("swiglu_recompute"):

@@ -23,22 +23,24 @@ SMALL_BF16_SOFTMAX = inputs.LayerConfig("small_bf16_zipf", T=513, d=128, E=16, k
                                         bias="zipf")
 
 
-def _run(cfg, seed, recompute_act=False):
-    print(f"layer {cfg.name} seed={seed} recompute={recompute_act}", flush=True)
+def _run(cfg, seed, recompute_act=False, gate_in_ffn=False):
+    print(f"layer {cfg.name} seed={seed} recompute={recompute_act} gated={gate_in_ffn}",
+          flush=True)
     inp = (inputs.layer_inputs(cfg, seed) if cfg.routing == "balanced"
            else layer_inputs_without_near_ties(cfg, seed))
     w = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
-    layer = MoELayer(cfg, w, DEV, recompute_act=recompute_act)
+    layer = MoELayer(cfg, w, DEV, recompute_act=recompute_act, gate_in_ffn=gate_in_ffn)
     layer.forward(w["x"])
     layer.backward(w["dout"])
     torch.cuda.synchronize()
     shared = (np64(inp["ws13"]), np64(inp["ws2"])) if cfg.fs else None
     bias = None if inp["logit_bias"] is None else inp["logit_bias"].numpy()
     given = inp["topk_idx_in"].numpy() if cfg.routing == "balanced" else None
-    c = oracle.layer_forward(np64(inp["x"]), inp["w_r"].numpy(), np64(inp["w13"]),
-                             np64(inp["w2"]), cfg.k, cfg.score, cfg.renorm, logit_bias=bias,
-                             shared=shared, given_experts=given)
-    g = oracle.layer_backward(c, np64(inp["dout"]))
+    fwd = oracle.layer_forward_gated if gate_in_ffn else oracle.layer_forward
+    bwd = oracle.layer_backward_gated if gate_in_ffn else oracle.layer_backward
+    c = fwd(np64(inp["x"]), inp["w_r"].numpy(), np64(inp["w13"]), np64(inp["w2"]), cfg.k,
+            cfg.score, cfg.renorm, logit_bias=bias, shared=shared, given_experts=given)
+    g = bwd(c, np64(inp["dout"]))
     return layer, c, g
 
 
@@ -88,6 +90,16 @@ def test_layer_balanced_routing_replayed(gpu):
 def test_layer_recompute_activation(gpu, cfg):
     """H = silu(A) * B rebuilt from AB in the backward instead of kept."""
     _check(cfg, *_run(cfg, 1, recompute_act=True))
+
+
+@pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_BF16_SOFTMAX, inputs.CONFIGS["small_balanced"]],
+                         ids=lambda c: c.name)
+def test_layer_gate_in_ffn(gpu, cfg):
+    """Routing weight applied before W2: unweighted combine, no Y in the
+    backward, the weight gradient from the GEMM 2 dgrad epilogue."""
+    layer, c, g = _run(cfg, 2, gate_in_ffn=True)
+    _check(cfg, layer, c, g)
+    assert_close("d_topk_w", layer.d_topk_w, g["d_topk_w"], TOL[cfg.gemm])
 
 
 def test_layer_repeat_is_bitwise_deterministic(gpu):

@@ -361,3 +361,53 @@ def test_route_replay_bit_exact(gpu, E, k, score, renorm, kind):
     assert_close("topk_w", g["topk_w"], r["topk_w"], TOL["f32"])
     assert int(status.item()) == int(r["changed"])
     assert r["changed"] == (kind == "corrupt")
+
+
+@pytest.mark.parametrize("M,G,d,f", [(900, 6, 256, 256), (3000, 9, 512, 384)])
+def test_gated_ffn_ops(gpu, M, G, d, f):
+    """Routing weight applied inside the expert: the permuted-row weights
+    (bit copy), GEMM 1 with H' = w * silu(a) * b, GEMM 2's dgrad with
+    dAB = SwiGLU'(w * dH') and the partial <dH', h> per 64 columns, and the
+    reduction of the partials into d_topk_w."""
+    print(f"gated ffn ops M={M} G={G} d={d} f={f}", flush=True)
+    tdt = torch.bfloat16
+    off, X, W13, _ = _gemm_inputs(M, G, d, 2 * f, 0.2, 0.5, tdt, seed=12)
+    W2 = inputs.normal((G, f, d), f ** -0.5, 96, 0, "cpu", tdt)
+    dY = inputs.normal((M, d), 1.0, 95, 0, "cpu", tdt)
+    o = off.numpy()
+    offd = off.to(DEV)
+    # a permutation of M = T*k rows with random weights
+    k = 3
+    T = M // k
+    M = T * k
+    rng = np.random.default_rng(M)
+    dst = torch.from_numpy(rng.permutation(M).astype(np.int32).reshape(T, k))
+    topk_w = torch.from_numpy(rng.random((T, k)).astype(np.float32))
+    w_perm = torch.empty(M, dtype=torch.float32, device=DEV)
+    abi.moe_permute_weights(topk_w.to(DEV), dst.to(DEV), w_perm)
+    ref_wp = np.zeros(M, np.float32)
+    ref_wp[dst.numpy().ravel()] = topk_w.numpy().ravel()
+    np.testing.assert_array_equal(w_perm.cpu().numpy(), ref_wp)
+    X, dY = X[:M], dY[:M]
+    off = torch.clamp(off, max=M)
+    o = off.numpy()
+    offd = off.to(DEV)
+    AB = torch.empty((M, 2 * f), dtype=tdt, device=DEV)
+    H = torch.empty((M, f), dtype=tdt, device=DEV)
+    abi.moe_grouped_gemm_gated_fwd(X.to(DEV), W13.to(DEV), offd, w_perm, AB, H)
+    ref_ab = oracle.grouped_gemm_fwd(np64(X), np64(W13), o)
+    assert_close("AB", AB, ref_ab, TOL["bf16"])
+    assert_close("H'", H, ref_wp[:, None] * oracle.swiglu(ref_ab), TOL["bf16"])
+    dAB = torch.empty((M, 2 * f), dtype=tdt, device=DEV)
+    part = torch.full((M, f // 64), float("nan"), dtype=torch.float32, device=DEV)
+    abi.moe_grouped_gemm_gated_dgrad(dY.to(DEV), W2.to(DEV), offd, AB, w_perm, dAB, part)
+    ab_in = np64(AB)
+    ref_dh = oracle.grouped_gemm_dgrad(np64(dY), np64(W2), o)  # dH'
+    h = oracle.swiglu(ab_in)
+    assert_close("dAB", dAB, oracle.swiglu_bwd(ref_wp[:, None] * ref_dh, ab_in), TOL["bf16"])
+    ref_part = (ref_dh * h).reshape(M, f // 64, 64).sum(axis=2)
+    assert_close("gate partials", part, ref_part, TOL["bf16"])
+    dw = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    abi.moe_gate_grad(part, dst.to(DEV), dw)
+    ref_dw = part.cpu().double().numpy().sum(axis=1)[dst.numpy()]
+    assert_close("d_topk_w (from the partials)", dw, ref_dw, TOL["f32"])

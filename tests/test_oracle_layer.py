@@ -194,3 +194,22 @@ def test_expert_wgrad_columns_match_full_backward():
         np.testing.assert_allclose(d1, g["dW13"][e][:, cols], rtol=0, atol=1e-12)
         np.testing.assert_allclose(d3, g["dW13"][e][:, f + cols], rtol=0, atol=1e-12)
         np.testing.assert_allclose(d2, g["dW2"][e][cols, :], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("score,renorm", MODES)
+def test_gated_arrangement_equals_baseline(score, renorm):
+    """The memory-saving arrangement (routing weight applied before W2, an
+    unweighted combine, the weight gradient taken over the ffn axis) computes
+    the same output and gradients as the baseline, by linearity: agreement to
+    fp64 rounding, with routing replayed and with a shared expert."""
+    x, w_r, w13, w2, b, shared, dout = _make(21, T=20, d=12, E=5, k=2, f=7, fs=4, bias=True)
+    for given in (None, np.stack([np.array([t % 5, (t + 2) % 5]) for t in range(20)])):
+        c0 = oracle.layer_forward(x, w_r, w13, w2, 2, score, renorm, logit_bias=b, shared=shared,
+                                  given_experts=given)
+        c1 = oracle.layer_forward_gated(x, w_r, w13, w2, 2, score, renorm, logit_bias=b,
+                                        shared=shared, given_experts=given)
+        np.testing.assert_allclose(c1["out"], c0["out"], rtol=0, atol=1e-12)
+        g0 = oracle.layer_backward(c0, dout)
+        g1 = oracle.layer_backward_gated(c1, dout)
+        for name in ["dx", "d_logits", "dW_r", "dW13", "dW2", "d_topk_w", "dWs13", "dWs2"]:
+            np.testing.assert_allclose(g1[name], g0[name], rtol=0, atol=1e-11, err_msg=name)
