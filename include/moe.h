@@ -133,6 +133,24 @@ int moe_route_replay(const float* logits, const int32_t* topk_idx_in, int64_t T,
                      int32_t* counts, int64_t* offsets, int32_t* dst_row, int32_t* src_token,
                      int32_t* status, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Capacity-limited dropping (section 7, Load Balancing: capacity-limited
+ * dropping), applied to the dispatch map of moe_route_topk or
+ * moe_route_replay: expert e keeps the first `capacity` of its (token, slot)
+ * pairs in token order -- the first rows of its segment -- and drops the rest.
+ *   counts_out [E]    int32: kept rows per expert (min(counts, capacity))
+ *   offsets_out [E+1] int64: their exclusive prefix sum
+ *   dst_row_out [T,k] int32: new row of each kept pair, -1 for a dropped one
+ *   src_token_out     int32: token of each kept row; entries at and past
+ *                     offsets_out[E] are not written
+ * A dropped pair contributes nothing downstream (permute, combine and their
+ * backward skip rows < 0; the grouped GEMMs see only the kept segments); the
+ * routing weights are left as computed.  Outputs must not alias the inputs.
+ * The usual capacity is ceil(capacity_factor * T * k / E). */
+int moe_apply_capacity(const int32_t* topk_idx, const int32_t* counts, const int64_t* offsets,
+                       const int32_t* dst_row, int64_t T, int32_t E, int32_t k, int64_t capacity,
+                       int32_t* counts_out, int64_t* offsets_out, int32_t* dst_row_out,
+                       int32_t* src_token_out, void* stream);
+
 /* Gradient of the routing weights with respect to the keys (the selection
  * itself carries none).  With g = sum_j w_j dw_j over a token's chosen slots:
  *   softmax, renorm   : d_logits[e_j] = w_j (dw_j - g), 0 elsewhere

@@ -25,6 +25,8 @@ Readings where the page is silent (each is also listed in the design notes):
   * Scaling factor on the routed sum: 1.
 """
 
+import math
+
 import numpy as np
 
 SOFTMAX = "softmax"
@@ -32,7 +34,8 @@ SIGMOID = "sigmoid"
 
 __all__ = [
     "SOFTMAX", "SIGMOID", "f64", "router_logits", "select_topk", "gates", "dispatch_map",
-    "route", "route_replay", "canonical_experts", "route_bwd", "router_logits_bwd", "permute", "permute_bwd",
+    "route", "route_replay", "canonical_experts", "capacity_of", "apply_capacity", "route_bwd",
+    "router_logits_bwd", "permute", "permute_bwd",
     "grouped_gemm_fwd", "grouped_gemm_dgrad", "grouped_gemm_wgrad", "sigmoid", "silu",
     "swiglu", "swiglu_bwd", "unpermute_combine", "unpermute_combine_bwd",
     "expert_ffn", "expert_ffn_bwd", "layer_forward", "layer_backward",
@@ -180,6 +183,48 @@ def route_replay(z, topk_idx, score, renorm):
     counts, offsets, dst_row, src_token = dispatch_map(idx, z.shape[1])
     return dict(topk_idx=idx, topk_w=w, counts=counts, offsets=offsets,
                 dst_row=dst_row, src_token=src_token, changed=changed)
+
+
+def capacity_of(capacity_factor, T, k, E):
+    """Rows each expert may keep: ceil(capacity_factor * T * k / E) (the
+    pages name capacity-limited dropping without a formula; this is the usual
+    definition, with the factor as the workload's knob)."""
+    return int(math.ceil(capacity_factor * T * k / E))
+
+
+def apply_capacity(r, capacity):
+    """Capacity-limited dropping of a routing ``r`` (a ``route`` or
+    ``route_replay`` result): each expert keeps the (token, slot) pairs of its
+    ``capacity`` lowest tokens and drops the rest; dropped pairs get no row
+    (dst_row -1) and contribute nothing.  The routing weights are unchanged.
+    Written as its own scan over tokens, not from the dropless map."""
+    idx = r["topk_idx"]
+    T, k = idx.shape
+    E = len(r["counts"])
+    kept = np.zeros(E, dtype=np.int64)
+    keep = np.zeros((T, k), dtype=bool)
+    for t in range(T):                   # tokens in ascending order
+        for j in range(k):
+            e = idx[t, j]
+            if kept[e] < capacity:
+                kept[e] += 1
+                keep[t, j] = True
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(kept)
+    dst_row = np.full((T, k), -1, dtype=np.int32)
+    src_token = np.full(int(offsets[-1]), -1, dtype=np.int32)
+    nxt = offsets[:-1].copy()
+    for t in range(T):
+        for j in range(k):
+            if keep[t, j]:
+                e = idx[t, j]
+                dst_row[t, j] = nxt[e]
+                src_token[nxt[e]] = t
+                nxt[e] += 1
+    out = dict(r)
+    out.update(counts=kept, offsets=offsets, dst_row=dst_row, src_token=src_token,
+               capacity=capacity)
+    return out
 
 
 def route_bwd(z, topk_idx, topk_w, d_topk_w, score, renorm):
@@ -365,14 +410,15 @@ def expert_ffn_bwd(x_t, w13_e, w2_e, a, b, h, dy):
 
 
 def layer_forward(x, w_r, w13, w2, k, score, renorm, logit_bias=None,
-                  shared=None, z=None, given_experts=None):
+                  shared=None, z=None, given_experts=None, capacity=None):
     """The four-stage forward pass as a per-token loop over each token's k
     experts (the one-expert-at-a-time view of [MCore-MoE] section 2, Expert
     Computation).  ``shared`` = (ws13 [d, 2fs], ws2 [fs, d]) or None.
     ``z`` may give the fp32 keys directly; by default they are computed with
     ``router_logits``.  ``given_experts`` [T, k] replays a routing
-    (``route_replay``) instead of selecting the top k.  Returns a cache dict
-    consumed by ``layer_backward``."""
+    (``route_replay``) instead of selecting the top k; ``capacity`` drops
+    what exceeds it (``apply_capacity``).  Returns a cache dict consumed by
+    ``layer_backward``."""
     x = f64(x)
     T, d = x.shape
     if z is None:
@@ -381,11 +427,15 @@ def layer_forward(x, w_r, w13, w2, k, score, renorm, logit_bias=None,
         r = route(z, k, score, renorm)
     else:
         r = route_replay(z, given_experts, score, renorm)
+    if capacity is not None:
+        r = apply_capacity(r, capacity)
     idx, w = r["topk_idx"], r["topk_w"]
     out = np.zeros((T, d))
     acts = {}
     for t in range(T):
         for j in range(k):
+            if r["dst_row"][t, j] < 0:
+                continue  # dropped
             e = int(idx[t, j])
             a, b, h, y = expert_ffn(x[t], w13[e], w2[e])
             acts[(t, j)] = (a, b, h, y)
@@ -417,6 +467,8 @@ def layer_backward(cache, dout):
     dw = np.zeros((T, k))
     for t in range(T):
         for j in range(k):
+            if (t, j) not in cache["acts"]:
+                continue  # dropped: no output, no gradient
             e = int(idx[t, j])
             a, b, h, y = cache["acts"][(t, j)]
             dw[t, j] = dout[t] @ y
@@ -444,7 +496,7 @@ def layer_backward(cache, dout):
 
 
 def layer_forward_gated(x, w_r, w13, w2, k, score, renorm, logit_bias=None,
-                        shared=None, z=None, given_experts=None):
+                        shared=None, z=None, given_experts=None, capacity=None):
     """The forward with each routing weight applied inside its expert, before
     W2: y'_tj = (w_tj h_tj) W2 and out_t = sum_j y'_tj (+ shared), an
     unweighted combine.  This is the memory-saving rearrangement of the
@@ -457,11 +509,15 @@ def layer_forward_gated(x, w_r, w13, w2, k, score, renorm, logit_bias=None,
         z = router_logits(x, w_r, logit_bias)
     r = (route(z, k, score, renorm) if given_experts is None
          else route_replay(z, given_experts, score, renorm))
+    if capacity is not None:
+        r = apply_capacity(r, capacity)
     idx, w = r["topk_idx"], r["topk_w"]
     out = np.zeros((T, d))
     acts = {}
     for t in range(T):
         for j in range(k):
+            if r["dst_row"][t, j] < 0:
+                continue  # dropped
             e = int(idx[t, j])
             f = w13[e].shape[1] // 2
             a = x[t] @ f64(w13[e][:, :f])
@@ -498,6 +554,8 @@ def layer_backward_gated(cache, dout):
     dw = np.zeros((T, k))
     for t in range(T):
         for j in range(k):
+            if (t, j) not in cache["acts"]:
+                continue  # dropped
             e = int(idx[t, j])
             f = w13[e].shape[1] // 2
             a, b, h, hg = cache["acts"][(t, j)]

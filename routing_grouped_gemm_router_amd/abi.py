@@ -38,6 +38,7 @@ SIGNATURES = {
                                 _p, _sz, _p]),
     "moe_route_topk_bwd": (_int, [_p, _p, _p, _p, _i64, _i32, _i32, _int, _int, _p, _p]),
     "moe_permute_weights": (_int, [_p, _p, _i64, _i32, _p, _p]),
+    "moe_apply_capacity": (_int, [_p, _p, _p, _p, _i64, _i32, _i32, _i64, _p, _p, _p, _p, _p]),
     "moe_grouped_gemm_gated_fwd": (_int, [_p, _p, _p, _i32, _i64, _i64, _i64, _int, _p, _p, _p,
                                           _p]),
     "moe_grouped_gemm_gated_dgrad": (_int, [_p, _p, _p, _i32, _i64, _i64, _i64, _int, _p, _p, _p,
@@ -169,6 +170,14 @@ def moe_route_replay(logits, topk_idx_in, score, renorm, topk_idx, topk_w, count
           int(renorm), _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(dst_row),
           _ptr(src_token), _ptr(status), _ptr(workspace),
           workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def moe_apply_capacity(topk_idx, counts, offsets, dst_row, capacity, counts_out, offsets_out,
+                       dst_row_out, src_token_out, stream=None):
+    T, k = topk_idx.shape
+    _call("moe_apply_capacity", _ptr(topk_idx), _ptr(counts), _ptr(offsets), _ptr(dst_row), T,
+          counts.shape[0], k, int(capacity), _ptr(counts_out), _ptr(offsets_out),
+          _ptr(dst_row_out), _ptr(src_token_out), _stream(stream))
 
 
 def moe_permute_weights(topk_w, dst_row, w_perm, stream=None):

@@ -161,6 +161,27 @@ int moe_route_replay(const float* logits, const int32_t* topk_idx_in, int64_t T,
                     "moe_route_replay");
 }
 
+int moe_apply_capacity(const int32_t* topk_idx, const int32_t* counts, const int64_t* offsets,
+                       const int32_t* dst_row, int64_t T, int32_t E, int32_t k, int64_t capacity,
+                       int32_t* counts_out, int64_t* offsets_out, int32_t* dst_row_out,
+                       int32_t* src_token_out, void* stream) {
+  const char* fn = "moe_apply_capacity";
+  REQUIRE(T >= 0 && E >= 1 && k >= 1 && k <= E && T * k < (int64_t(1) << 31), MOE_ERR_SHAPE,
+          "%s: T=%lld E=%d k=%d", fn, static_cast<long long>(T), E, k);
+  REQUIRE(E <= 1024, MOE_ERR_UNSUPPORTED, "%s: E=%d above 1024", fn, E);
+  REQUIRE(capacity >= 0, MOE_ERR_SHAPE, "%s: capacity=%lld", fn, static_cast<long long>(capacity));
+  REQUIRE(counts && offsets && counts_out && offsets_out, MOE_ERR_NULL,
+          "%s: counts and offsets (in and out) are required", fn);
+  REQUIRE(T == 0 || (topk_idx && dst_row && dst_row_out && src_token_out), MOE_ERR_NULL,
+          "%s: topk_idx, dst_row, dst_row_out and src_token_out are required", fn);
+  REQUIRE(dst_row_out != dst_row && offsets_out != offsets, MOE_ERR_SHAPE,
+          "%s: outputs must not alias the inputs", fn);
+  return hip_status(moe::launch_apply_capacity(topk_idx, counts, offsets, dst_row, T, E, k,
+                                               capacity, counts_out, offsets_out, dst_row_out,
+                                               src_token_out, as_stream(stream)),
+                    fn);
+}
+
 int moe_route_topk_bwd(const float* logits, const int32_t* topk_idx, const float* topk_w,
                        const float* d_topk_w, int64_t T, int32_t E, int32_t k, int score,
                        int renorm, float* d_logits, void* stream) {

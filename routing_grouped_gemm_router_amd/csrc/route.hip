@@ -376,6 +376,65 @@ hipError_t launch_route_replay(const float* logits, const int32_t* idx_in, int64
   return hipGetLastError();
 }
 
+// Capacity-limited dropping on a dropless dispatch map: expert e keeps the
+// first C of its rows (its lowest tokens, rows being in ascending token order
+// inside a segment); kept rows are renumbered into the new segments, dropped
+// (token, slot) pairs get dst_row = -1.
+__global__ __launch_bounds__(1024) void capacity_scan_kernel(const int32_t* __restrict__ counts,
+                                                             int E, int64_t C,
+                                                             int32_t* __restrict__ counts_out,
+                                                             int64_t* __restrict__ offsets_out) {
+  __shared__ long long s[1024];
+  const int e = threadIdx.x;
+  const long long kept = e < E ? min(static_cast<long long>(counts[e]), static_cast<long long>(C)) : 0;
+  s[e] = kept;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // inclusive scan
+    const long long v = e >= o ? s[e - o] : 0;
+    __syncthreads();
+    s[e] += v;
+    __syncthreads();
+  }
+  if (e < E) {
+    counts_out[e] = static_cast<int32_t>(kept);
+    offsets_out[e + 1] = s[e];
+  }
+  if (e == 0) offsets_out[0] = 0;
+}
+
+__global__ __launch_bounds__(256) void capacity_remap_kernel(
+    const int32_t* __restrict__ topk_idx, const int64_t* __restrict__ offsets,
+    const int32_t* __restrict__ dst_row, int64_t n, int E, int k, int64_t C,
+    const int64_t* __restrict__ offsets_out, int32_t* __restrict__ dst_out,
+    int32_t* __restrict__ src_out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int e = topk_idx[i];
+  const int64_t r = dst_row[i];
+  int32_t out = -1;
+  if (e >= 0 && e < E && r >= 0) {
+    const int64_t rank = r - offsets[e];
+    if (rank >= 0 && rank < C) {
+      const int64_t row = offsets_out[e] + rank;
+      out = static_cast<int32_t>(row);
+      src_out[row] = static_cast<int32_t>(i / k);
+    }
+  }
+  dst_out[i] = out;
+}
+
+hipError_t launch_apply_capacity(const int32_t* topk_idx, const int32_t* counts,
+                                 const int64_t* offsets, const int32_t* dst_row, int64_t T, int E,
+                                 int k, int64_t C, int32_t* counts_out, int64_t* offsets_out,
+                                 int32_t* dst_out, int32_t* src_out, hipStream_t stream) {
+  capacity_scan_kernel<<<1, 1024, 0, stream>>>(counts, E, C, counts_out, offsets_out);
+  const int64_t n = T * k;
+  if (n > 0)
+    capacity_remap_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), 256, 0, stream>>>(
+        topk_idx, offsets, dst_row, n, E, k, C, offsets_out, dst_out, src_out);
+  return hipGetLastError();
+}
+
 size_t route_topk_workspace(int64_t T, int E) {
   const int64_t ntiles = (T + ROUTE_TILE - 1) / ROUTE_TILE;
   return static_cast<size_t>(ntiles) * E * (sizeof(unsigned long long) + sizeof(int32_t)) + 256;

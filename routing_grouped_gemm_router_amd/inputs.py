@@ -19,6 +19,10 @@ all tensors synthetic, N(0, 1) activations and N(0, 1/fan_in) weights):
                      benchmark setting of section 8: every expert gets exactly
                      T*k/E rows), replayed from a seeded assignment
   small_balanced     T=512 d=256 E=16 k=4 f=256 shared 128, bf16, force-balanced
+  deepseek_v3_capacity as deepseek_v3_e256k8 with capacity-limited dropping
+                     (capacity factor 1.0: at most T*k/E rows per expert)
+  small_capacity     T=513 d=128 E=16 k=4 f=128, Zipf-biased softmax routing,
+                     capacity factor 1.25
 
 Generation: each tensor (and each expert's slice of a weight) is drawn from
 its own torch generator seeded from (seed, stream id), as float32 normals
@@ -49,6 +53,7 @@ class LayerConfig:
     bias_var: float = 0.5
     zipf_s: float = 1.0
     routing: str = "topk"       # topk | balanced (experts given, replayed)
+    capacity_factor: float = 0.0  # > 0: each expert keeps ceil(factor*T*k/E) rows
     note: str = field(default="", compare=False)
 
     @property
@@ -73,6 +78,11 @@ CONFIGS = {
                                         routing="balanced"),
     "small_balanced": LayerConfig("small_balanced", T=512, d=256, E=16, k=4, f=256, fs=128,
                                   score="sigmoid", bias="normal", routing="balanced"),
+    "deepseek_v3_capacity": LayerConfig("deepseek_v3_capacity", T=8192, d=7168, E=256, k=8,
+                                        f=2048, fs=2048, score="sigmoid", bias="normal",
+                                        capacity_factor=1.0),
+    "small_capacity": LayerConfig("small_capacity", T=513, d=128, E=16, k=4, f=128, bias="zipf",
+                                  capacity_factor=1.25),
 }
 
 # stream ids: one per tensor; expert weights add the expert index

@@ -27,6 +27,8 @@ and reused across steps.  Python here only allocates and orders the calls.
 """
 import contextlib
 
+import math
+
 import torch
 
 from . import abi
@@ -101,6 +103,13 @@ class MoELayer:
         self.dst_row = emp(T, k, dtype=torch.int32)
         self.src_token = emp(N, dtype=torch.int32)
         self.route_ws = emp(abi.moe_route_topk_workspace_bytes(T, E, k), dtype=torch.uint8)
+        # capacity-limited dropping: the route writes the dropless map here and
+        # moe_apply_capacity the kept one into counts / offsets / dst_row / src_token
+        self.capacity = (int(math.ceil(cfg.capacity_factor * T * k / E))
+                         if cfg.capacity_factor > 0 else None)
+        if self.capacity is not None:
+            self.full = dict(counts=emp(E, dtype=torch.int32), offsets=emp(E + 1, dtype=torch.int64),
+                             dst_row=emp(T, k, dtype=torch.int32), src_token=emp(N, dtype=torch.int32))
         self.x_perm = emp(N, d)
         self.ab = emp(N, 2 * f)
         self.y = emp(N, d)
@@ -284,15 +293,22 @@ class MoELayer:
         with self._span("router_logits"):
             abi.moe_router_logits(x, w["w_r"], w.get("logit_bias"), self.logits)
         with self._span("route_topk"):
+            m = self.full if self.capacity is not None else dict(
+                counts=self.counts, offsets=self.offsets, dst_row=self.dst_row,
+                src_token=self.src_token)
             if self.replay:
                 abi.moe_route_replay(self.logits, self.topk_idx_in, self.score, c.renorm,
-                                     self.topk_idx, self.topk_w, self.counts, self.offsets,
-                                     self.dst_row, self.src_token, self.route_ws,
+                                     self.topk_idx, self.topk_w, m["counts"], m["offsets"],
+                                     m["dst_row"], m["src_token"], self.route_ws,
                                      status=self.route_status)
             else:
                 abi.moe_route_topk(self.logits, c.k, self.score, c.renorm, self.topk_idx,
-                                   self.topk_w, self.counts, self.offsets, self.dst_row,
-                                   self.src_token, self.route_ws)
+                                   self.topk_w, m["counts"], m["offsets"], m["dst_row"],
+                                   m["src_token"], self.route_ws)
+            if self.capacity is not None:
+                abi.moe_apply_capacity(self.topk_idx, m["counts"], m["offsets"], m["dst_row"],
+                                       self.capacity, self.counts, self.offsets, self.dst_row,
+                                       self.src_token)
         with self._span("permute"):
             abi.moe_permute(x, self.dst_row, self.x_perm)
         if self.fp8:

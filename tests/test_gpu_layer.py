@@ -38,8 +38,11 @@ def _run(cfg, seed, recompute_act=False, gate_in_ffn=False):
     given = inp["topk_idx_in"].numpy() if cfg.routing == "balanced" else None
     fwd = oracle.layer_forward_gated if gate_in_ffn else oracle.layer_forward
     bwd = oracle.layer_backward_gated if gate_in_ffn else oracle.layer_backward
+    cap = (oracle.capacity_of(cfg.capacity_factor, cfg.T, cfg.k, cfg.E)
+           if cfg.capacity_factor > 0 else None)
     c = fwd(np64(inp["x"]), inp["w_r"].numpy(), np64(inp["w13"]), np64(inp["w2"]), cfg.k,
-            cfg.score, cfg.renorm, logit_bias=bias, shared=shared, given_experts=given)
+            cfg.score, cfg.renorm, logit_bias=bias, shared=shared, given_experts=given,
+            capacity=cap)
     g = bwd(c, np64(inp["dout"]))
     return layer, c, g
 
@@ -50,7 +53,8 @@ def _check(cfg, layer, c, g):
     np.testing.assert_array_equal(layer.topk_idx.cpu().numpy(), r["topk_idx"])
     np.testing.assert_array_equal(layer.offsets.cpu().numpy(), r["offsets"])
     np.testing.assert_array_equal(layer.dst_row.cpu().numpy(), r["dst_row"])
-    np.testing.assert_array_equal(layer.src_token.cpu().numpy(), r["src_token"])
+    n_rows = int(r["offsets"][-1])
+    np.testing.assert_array_equal(layer.src_token.cpu().numpy()[:n_rows], r["src_token"])
     assert_close("logits", layer.logits, c["z"], TOL["f32"])
     assert_close("out", layer.out, c["out"], tol)
     grads = layer.grads()
@@ -98,6 +102,17 @@ def test_layer_gate_in_ffn(gpu, cfg):
     """Routing weight applied before W2: unweighted combine, no Y in the
     backward, the weight gradient from the GEMM 2 dgrad epilogue."""
     layer, c, g = _run(cfg, 2, gate_in_ffn=True)
+    _check(cfg, layer, c, g)
+    assert_close("d_topk_w", layer.d_topk_w, g["d_topk_w"], TOL[cfg.gemm])
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_layer_capacity_dropping(gpu, gated):
+    """Capacity-limited dropping on a skewed (Zipf-biased) routing: pairs past
+    an expert's capacity are dropped and contribute nothing."""
+    cfg = inputs.CONFIGS["small_capacity"]
+    layer, c, g = _run(cfg, 0, gate_in_ffn=gated)
+    assert (c["route"]["dst_row"] < 0).sum() > 0  # the case really drops
     _check(cfg, layer, c, g)
     assert_close("d_topk_w", layer.d_topk_w, g["d_topk_w"], TOL[cfg.gemm])
 

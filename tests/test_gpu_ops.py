@@ -411,3 +411,28 @@ def test_gated_ffn_ops(gpu, M, G, d, f):
     abi.moe_gate_grad(part, dst.to(DEV), dw)
     ref_dw = part.cpu().double().numpy().sum(axis=1)[dst.numpy()]
     assert_close("d_topk_w (from the partials)", dw, ref_dw, TOL["f32"])
+
+
+@pytest.mark.parametrize("T,E,k,C", [(700, 13, 3, 100), (700, 13, 3, 0), (4096, 256, 8, 128),
+                                     (300, 5, 2, 10 ** 6)])
+def test_apply_capacity_bit_exact(gpu, T, E, k, C):
+    print(f"capacity T={T} E={E} k={k} C={C}", flush=True)
+    z = _keys(T, E, 99 + E, "normal")
+    z[:, :3] += 2.0  # skew: the first experts overflow
+    r = oracle.route(z, k, "softmax", True)
+    ref = oracle.apply_capacity(r, C)
+    g = {n: torch.from_numpy(np.ascontiguousarray(r[n])).to(DEV) for n in
+         ("topk_idx", "counts", "offsets", "dst_row")}
+    g["counts"] = g["counts"].to(torch.int32)
+    out = dict(counts=torch.empty(E, dtype=torch.int32, device=DEV),
+               offsets=torch.empty(E + 1, dtype=torch.int64, device=DEV),
+               dst_row=torch.empty((T, k), dtype=torch.int32, device=DEV),
+               src_token=torch.full((T * k,), -7, dtype=torch.int32, device=DEV))
+    abi.moe_apply_capacity(g["topk_idx"], g["counts"], g["offsets"], g["dst_row"], C,
+                           out["counts"], out["offsets"], out["dst_row"], out["src_token"])
+    for key in ("counts", "offsets", "dst_row"):
+        np.testing.assert_array_equal(out[key].cpu().numpy(), ref[key], err_msg=key)
+    n = int(ref["offsets"][-1])
+    src = out["src_token"].cpu().numpy()
+    np.testing.assert_array_equal(src[:n], ref["src_token"])
+    assert (src[n:] == -7).all()  # past the kept rows: not written

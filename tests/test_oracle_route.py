@@ -203,3 +203,30 @@ def test_balanced_assignment_is_exactly_balanced():
         r = oracle.route_replay(np.zeros((T, E), np.float32), idx, "sigmoid", True)
         assert not r["changed"]
         assert (r["counts"] == T * k // E).all()
+
+
+def test_capacity_keeps_the_lowest_tokens_of_each_expert():
+    """Capacity-limited dropping: each expert keeps the pairs of its C lowest
+    tokens; with C at least the largest count nothing is dropped (the
+    dropless map); kept rows form a bijection with the kept pairs, in
+    ascending token order inside each segment; dropped pairs have no row."""
+    rng = np.random.default_rng(8)
+    z = (rng.standard_normal((200, 6)) + np.array([2.0, 1.0, 0, 0, -1, -2])).astype(np.float32)
+    r = oracle.route(z, 2, "softmax", True)
+    full = oracle.apply_capacity(r, int(r["counts"].max()))
+    for key in ("counts", "offsets", "dst_row", "src_token"):
+        np.testing.assert_array_equal(full[key], r[key])
+    for C in (0, 1, 7, 40):
+        c = oracle.apply_capacity(r, C)
+        np.testing.assert_array_equal(c["counts"], np.minimum(r["counts"], C))
+        for e in range(6):
+            toks = [t for t in range(200) for j in range(2) if r["topk_idx"][t, j] == e]
+            kept = sorted(toks)[:C]
+            seg = c["src_token"][c["offsets"][e]:c["offsets"][e + 1]]
+            np.testing.assert_array_equal(seg, kept)
+        kept_pairs = np.argwhere(c["dst_row"] >= 0)
+        assert len(kept_pairs) == c["offsets"][-1]
+        for t, j in kept_pairs:
+            assert c["src_token"][c["dst_row"][t, j]] == t
+        np.testing.assert_array_equal(c["topk_w"], r["topk_w"])
+    assert oracle.capacity_of(1.0, 200, 2, 6) == 67
