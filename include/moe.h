@@ -133,6 +133,23 @@ int moe_route_replay(const float* logits, const int32_t* topk_idx_in, int64_t T,
                      int32_t* counts, int64_t* offsets, int32_t* dst_row, int32_t* src_token,
                      int32_t* status, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of workspace moe_aux_loss needs to produce the loss value. */
+size_t moe_aux_loss_workspace_bytes(int64_t T, int32_t E);
+
+/* Auxiliary load-balancing loss (section 7, Load Balancing: auxiliary loss):
+ *   loss = coeff * E * sum_e f_e * P_e,
+ *   f_e = counts[e] / (T k)                  (fraction of routed pairs; no gradient)
+ *   P_e = (1/T) sum_t p[t, e],  p[t, .] = softmax of the keys (MOE_SOFTMAX) or
+ *         the sigmoid scores divided by their sum over the E experts (MOE_SIGMOID).
+ *   logits [T, E] fp32 keys; counts [E] int32 (of moe_route_topk / _replay).
+ *   loss     fp32 device scalar out, or NULL (no workspace needed then)
+ *   d_logits [T, E] fp32 or NULL: dloss/dlogits is ADDED (call after
+ *            moe_route_topk_bwd, which overwrites d_logits)
+ * Deterministic (fixed-order sums).  Limits as moe_route_topk, T >= 1. */
+int moe_aux_loss(const float* logits, const int32_t* counts, int64_t T, int32_t E, int32_t k,
+                 int score, float coeff, float* loss, float* d_logits, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
 /* Capacity-limited dropping (section 7, Load Balancing: capacity-limited
  * dropping), applied to the dispatch map of moe_route_topk or
  * moe_route_replay: expert e keeps the first `capacity` of its (token, slot)

@@ -34,7 +34,8 @@ SIGMOID = "sigmoid"
 
 __all__ = [
     "SOFTMAX", "SIGMOID", "f64", "router_logits", "select_topk", "gates", "dispatch_map",
-    "route", "route_replay", "canonical_experts", "capacity_of", "apply_capacity", "route_bwd",
+    "route", "route_replay", "canonical_experts", "capacity_of", "apply_capacity", "aux_loss",
+    "route_bwd",
     "router_logits_bwd", "permute", "permute_bwd",
     "grouped_gemm_fwd", "grouped_gemm_dgrad", "grouped_gemm_wgrad", "sigmoid", "silu",
     "swiglu", "swiglu_bwd", "unpermute_combine", "unpermute_combine_bwd",
@@ -225,6 +226,34 @@ def apply_capacity(r, capacity):
     out.update(counts=kept, offsets=offsets, dst_row=dst_row, src_token=src_token,
                capacity=capacity)
     return out
+
+
+def aux_loss(z, counts, k, score, coeff):
+    """Auxiliary load-balancing loss (named by the pages among the balancing
+    strategies, without a formula; this is the usual form):
+      L = coeff * E * sum_e f_e P_e,  f_e = counts_e / (T k),
+      P_e = mean over tokens of p[t, e], the router's probabilities: the
+      softmax of the keys, or the sigmoid scores normalised over the E experts.
+    Returns (L, dL/dz) with f held fixed (the counts come from a discrete
+    selection)."""
+    z = f64(z)
+    T, E = z.shape
+    f = f64(counts) / (T * k)
+    if score == SOFTMAX:
+        ex = np.exp(z - z.max(axis=1, keepdims=True))
+        p = ex / ex.sum(axis=1, keepdims=True)
+    else:
+        s = sigmoid(z)
+        p = s / s.sum(axis=1, keepdims=True)
+    P = p.mean(axis=0)
+    L = coeff * E * float(f @ P)
+    g = coeff * E * f / T                    # dL/dp[t, e]
+    pg = (p * g).sum(axis=1, keepdims=True)
+    if score == SOFTMAX:
+        dz = p * (g - pg)
+    else:
+        dz = s * (1.0 - s) / s.sum(axis=1, keepdims=True) * (g - pg)
+    return L, dz
 
 
 def route_bwd(z, topk_idx, topk_w, d_topk_w, score, renorm):

@@ -23,6 +23,7 @@ _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
 _int = ctypes.c_int
 _sz = ctypes.c_size_t
+_f32 = ctypes.c_float
 
 # name -> (restype, argtypes)
 SIGNATURES = {
@@ -39,6 +40,8 @@ SIGNATURES = {
     "moe_route_topk_bwd": (_int, [_p, _p, _p, _p, _i64, _i32, _i32, _int, _int, _p, _p]),
     "moe_permute_weights": (_int, [_p, _p, _i64, _i32, _p, _p]),
     "moe_apply_capacity": (_int, [_p, _p, _p, _p, _i64, _i32, _i32, _i64, _p, _p, _p, _p, _p]),
+    "moe_aux_loss_workspace_bytes": (_sz, [_i64, _i32]),
+    "moe_aux_loss": (_int, [_p, _p, _i64, _i32, _i32, _int, _f32, _p, _p, _p, _sz, _p]),
     "moe_grouped_gemm_gated_fwd": (_int, [_p, _p, _p, _i32, _i64, _i64, _i64, _int, _p, _p, _p,
                                           _p]),
     "moe_grouped_gemm_gated_dgrad": (_int, [_p, _p, _p, _i32, _i64, _i64, _i64, _int, _p, _p, _p,
@@ -170,6 +173,18 @@ def moe_route_replay(logits, topk_idx_in, score, renorm, topk_idx, topk_w, count
           int(renorm), _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(dst_row),
           _ptr(src_token), _ptr(status), _ptr(workspace),
           workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def moe_aux_loss_workspace_bytes(T, E):
+    return lib().moe_aux_loss_workspace_bytes(T, E)
+
+
+def moe_aux_loss(logits, counts, k, score, coeff, loss=None, d_logits=None, workspace=None,
+                 stream=None):
+    T, E = logits.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _call("moe_aux_loss", _ptr(logits), _ptr(counts), T, E, k, score, float(coeff), _ptr(loss),
+          _ptr(d_logits), _ptr(workspace), ws_bytes, _stream(stream))
 
 
 def moe_apply_capacity(topk_idx, counts, offsets, dst_row, capacity, counts_out, offsets_out,

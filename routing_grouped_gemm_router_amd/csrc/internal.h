@@ -24,6 +24,10 @@ hipError_t launch_apply_capacity(const int32_t* topk_idx, const int32_t* counts,
                                  const int64_t* offsets, const int32_t* dst_row, int64_t T, int E,
                                  int k, int64_t C, int32_t* counts_out, int64_t* offsets_out,
                                  int32_t* dst_out, int32_t* src_out, hipStream_t stream);
+size_t aux_loss_workspace(int64_t T, int E);
+hipError_t launch_aux_loss(const float* logits, const int32_t* counts, int64_t T, int E, int k,
+                           int score, float coeff, float* loss, float* d_logits, void* ws,
+                           hipStream_t stream);
 hipError_t launch_route_topk_bwd(const float* logits, const int32_t* topk_idx, const float* topk_w,
                                  const float* d_topk_w, int64_t T, int E, int k, int score,
                                  int renorm, float* d_logits, hipStream_t s);

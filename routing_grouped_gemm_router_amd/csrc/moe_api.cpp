@@ -182,6 +182,30 @@ int moe_apply_capacity(const int32_t* topk_idx, const int32_t* counts, const int
                     fn);
 }
 
+size_t moe_aux_loss_workspace_bytes(int64_t T, int32_t E) {
+  if (T < 0 || E < 1) return 0;
+  return moe::aux_loss_workspace(T, E);
+}
+
+int moe_aux_loss(const float* logits, const int32_t* counts, int64_t T, int32_t E, int32_t k,
+                 int score, float coeff, float* loss, float* d_logits, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_aux_loss";
+  int st = check_route_shape(fn, T, E, k, score);
+  if (st != MOE_OK) return st;
+  REQUIRE(T >= 1, MOE_ERR_SHAPE, "%s: T must be at least 1", fn);
+  REQUIRE(logits && counts && (loss || d_logits), MOE_ERR_NULL,
+          "%s: logits, counts and at least one of loss / d_logits are required", fn);
+  const size_t need = moe::aux_loss_workspace(T, E);
+  REQUIRE(!loss || (workspace && workspace_bytes >= need), MOE_ERR_WORKSPACE,
+          "%s: workspace needs %zu bytes, got %zu", fn, need, workspace_bytes);
+  REQUIRE(!loss || (reinterpret_cast<uintptr_t>(workspace) & 3u) == 0, MOE_ERR_UNSUPPORTED,
+          "%s: workspace must be 4-byte aligned", fn);
+  return hip_status(moe::launch_aux_loss(logits, counts, T, E, k, score, coeff, loss, d_logits,
+                                         workspace, as_stream(stream)),
+                    fn);
+}
+
 int moe_route_topk_bwd(const float* logits, const int32_t* topk_idx, const float* topk_w,
                        const float* d_topk_w, int64_t T, int32_t E, int32_t k, int score,
                        int renorm, float* d_logits, void* stream) {

@@ -435,6 +435,141 @@ hipError_t launch_apply_capacity(const int32_t* topk_idx, const int32_t* counts,
   return hipGetLastError();
 }
 
+// Auxiliary load-balancing loss L = coeff * E * sum_e f_e P_e, with
+// f_e = counts[e] / (T k) and P_e = mean over tokens of the router
+// probability p[t, e] (softmax of the keys, or the sigmoid scores normalised
+// over the E experts).  One pass: per 64-token tile, the column sums of p
+// (fixed order: waves, then lanes) go to part[tile, e]; optionally the
+// gradient dL/dz (f held fixed) is added into d_logits:
+//   softmax: dz_e = p_e (g_e - sum p g),  sigmoid: dz_e = s_e (1 - s_e) / S (g_e - sum p g),
+//   g_e = coeff * E * f_e / T.
+template <int EPL>
+__global__ __launch_bounds__(256) void aux_loss_kernel(const float* __restrict__ logits,
+                                                       const int32_t* __restrict__ counts,
+                                                       int64_t T, int E, int k, int score,
+                                                       float coeff, float* __restrict__ part,
+                                                       float* __restrict__ d_logits) {
+  __shared__ float colsum[4][1024];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t tile = blockIdx.x;
+  float g[EPL], acc[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    g[i] = e < E ? coeff * E * (static_cast<float>(counts[e]) / static_cast<float>(T * k)) /
+                       static_cast<float>(T)
+                 : 0.f;
+    acc[i] = 0.f;
+  }
+  for (int tt = wave; tt < ROUTE_TILE; tt += 4) {
+    const int64_t t = tile * ROUTE_TILE + tt;
+    if (t >= T) break;
+    const float* row = logits + t * E;
+    float v[EPL], pr[EPL], sv[EPL];
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + 64 * i;
+      v[i] = e < E ? row[e] : -INFINITY;
+      m = fmaxf(m, v[i]);
+    }
+    float denom = 0.f;
+    if (score == 0) {
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        pr[i] = lane + 64 * i < E ? expf(v[i] - m) : 0.f;
+        denom += pr[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        sv[i] = lane + 64 * i < E ? 1.0f / (1.0f + expf(-v[i])) : 0.f;
+        pr[i] = sv[i];
+        denom += pr[i];
+      }
+    }
+    denom = wave_sum(denom);
+    float pg = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      pr[i] /= denom;
+      acc[i] += pr[i];
+      pg += pr[i] * g[i];
+    }
+    if (d_logits) {
+      pg = wave_sum(pg);
+      float* drow = d_logits + t * E;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int e = lane + 64 * i;
+        if (e >= E) continue;
+        const float dz = score == 0 ? pr[i] * (g[i] - pg)
+                                    : sv[i] * (1.0f - sv[i]) / denom * (g[i] - pg);
+        drow[e] += dz;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E) colsum[wave][e] = acc[i];
+  }
+  __syncthreads();
+  if (part)
+    for (int e = tid; e < E; e += 256)
+      part[tile * E + e] = ((colsum[0][e] + colsum[1][e]) + colsum[2][e]) + colsum[3][e];
+}
+
+// loss = coeff * E * sum_e f_e * (sum_tiles part[tile, e]) / T, fixed order
+__global__ __launch_bounds__(1024) void aux_loss_final_kernel(const float* __restrict__ part,
+                                                             int64_t ntiles,
+                                                             const int32_t* __restrict__ counts,
+                                                             int64_t T, int E, int k, float coeff,
+                                                             float* __restrict__ loss) {
+  __shared__ float s[1024];
+  const int e = threadIdx.x;
+  float v = 0.f;
+  if (e < E) {
+    float P = 0.f;
+    for (int64_t tl = 0; tl < ntiles; ++tl) P += part[tl * E + e];
+    v = (static_cast<float>(counts[e]) / static_cast<float>(T * k)) * (P / static_cast<float>(T));
+  }
+  s[e] = v;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if (e < o) s[e] += s[e + o];
+    __syncthreads();
+  }
+  if (e == 0) loss[0] = coeff * static_cast<float>(E) * s[0];
+}
+
+size_t aux_loss_workspace(int64_t T, int E) {
+  return static_cast<size_t>((T + ROUTE_TILE - 1) / ROUTE_TILE) * E * sizeof(float) + 256;
+}
+
+hipError_t launch_aux_loss(const float* logits, const int32_t* counts, int64_t T, int E, int k,
+                           int score, float coeff, float* loss, float* d_logits, void* ws,
+                           hipStream_t stream) {
+  const int64_t ntiles = (T + ROUTE_TILE - 1) / ROUTE_TILE;
+  float* part = loss ? static_cast<float*>(ws) : nullptr;
+  if (ntiles > 0) {
+    switch (epl_for(E)) {
+#define MOE_AUX(n)                                                                        \
+  case n:                                                                                 \
+    aux_loss_kernel<n><<<dim3(static_cast<unsigned>(ntiles)), 256, 0, stream>>>(         \
+        logits, counts, T, E, k, score, coeff, part, d_logits);                           \
+    break;
+      MOE_AUX(1) MOE_AUX(2) MOE_AUX(4) MOE_AUX(8) MOE_AUX(16)
+#undef MOE_AUX
+    }
+  }
+  if (loss)
+    aux_loss_final_kernel<<<1, 1024, 0, stream>>>(part, ntiles, counts, T, E, k, coeff, loss);
+  return hipGetLastError();
+}
+
 size_t route_topk_workspace(int64_t T, int E) {
   const int64_t ntiles = (T + ROUTE_TILE - 1) / ROUTE_TILE;
   return static_cast<size_t>(ntiles) * E * (sizeof(unsigned long long) + sizeof(int32_t)) + 256;

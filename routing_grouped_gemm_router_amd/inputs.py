@@ -23,6 +23,8 @@ all tensors synthetic, N(0, 1) activations and N(0, 1/fan_in) weights):
                      (capacity factor 1.0: at most T*k/E rows per expert)
   small_capacity     T=513 d=128 E=16 k=4 f=128, Zipf-biased softmax routing,
                      capacity factor 1.25
+  small_aux          T=300 d=256 E=8 k=2 f=256 shared 128, sigmoid routing with
+                     an auxiliary load-balancing loss (coefficient 0.01)
 
 Generation: each tensor (and each expert's slice of a weight) is drawn from
 its own torch generator seeded from (seed, stream id), as float32 normals
@@ -54,6 +56,7 @@ class LayerConfig:
     zipf_s: float = 1.0
     routing: str = "topk"       # topk | balanced (experts given, replayed)
     capacity_factor: float = 0.0  # > 0: each expert keeps ceil(factor*T*k/E) rows
+    aux_loss_coeff: float = 0.0   # > 0: auxiliary load-balancing loss
     note: str = field(default="", compare=False)
 
     @property
@@ -83,6 +86,8 @@ CONFIGS = {
                                         capacity_factor=1.0),
     "small_capacity": LayerConfig("small_capacity", T=513, d=128, E=16, k=4, f=128, bias="zipf",
                                   capacity_factor=1.25),
+    "small_aux": LayerConfig("small_aux", T=300, d=256, E=8, k=2, f=256, fs=128, score="sigmoid",
+                             bias="normal", aux_loss_coeff=0.01),
 }
 
 # stream ids: one per tensor; expert weights add the expert index

@@ -107,6 +107,10 @@ class MoELayer:
         # moe_apply_capacity the kept one into counts / offsets / dst_row / src_token
         self.capacity = (int(math.ceil(cfg.capacity_factor * T * k / E))
                          if cfg.capacity_factor > 0 else None)
+        self.aux = cfg.aux_loss_coeff > 0
+        if self.aux:
+            self.aux_loss = emp(1, dtype=torch.float32)
+            self.aux_ws = emp(abi.moe_aux_loss_workspace_bytes(T, E), dtype=torch.uint8)
         if self.capacity is not None:
             self.full = dict(counts=emp(E, dtype=torch.int32), offsets=emp(E + 1, dtype=torch.int64),
                              dst_row=emp(T, k, dtype=torch.int32), src_token=emp(N, dtype=torch.int32))
@@ -309,6 +313,11 @@ class MoELayer:
                 abi.moe_apply_capacity(self.topk_idx, m["counts"], m["offsets"], m["dst_row"],
                                        self.capacity, self.counts, self.offsets, self.dst_row,
                                        self.src_token)
+        self.routed_counts = m["counts"]  # before any dropping
+        if self.aux:
+            with self._span("aux_loss"):
+                abi.moe_aux_loss(self.logits, self.routed_counts, c.k, self.score,
+                                 c.aux_loss_coeff, loss=self.aux_loss, workspace=self.aux_ws)
         with self._span("permute"):
             abi.moe_permute(x, self.dst_row, self.x_perm)
         if self.fp8:
@@ -402,6 +411,10 @@ class MoELayer:
         with self._span("route_topk_bwd"):
             abi.moe_route_topk_bwd(self.logits, self.topk_idx, self.topk_w, self.d_topk_w,
                                    self.score, c.renorm, self.d_logits)
+        if self.aux:  # the loss's gradient is added to d_logits
+            with self._span("aux_loss_bwd"):
+                abi.moe_aux_loss(self.logits, self.routed_counts, c.k, self.score,
+                                 c.aux_loss_coeff, d_logits=self.d_logits)
         with self._span("router_logits_bwd"):
             abi.moe_router_logits_bwd(x, w["w_r"], self.d_logits, self.dw_r, self.dx_router)
         with self._span("permute_bwd"):

@@ -44,6 +44,11 @@ def _run(cfg, seed, recompute_act=False, gate_in_ffn=False):
             cfg.score, cfg.renorm, logit_bias=bias, shared=shared, given_experts=given,
             capacity=cap)
     g = bwd(c, np64(inp["dout"]))
+    if cfg.aux_loss_coeff > 0:
+        # the auxiliary loss adds its gradient to d_logits (counts of the routing)
+        L, dz = oracle.aux_loss(c["z"], c["route"]["counts"], cfg.k, cfg.score, cfg.aux_loss_coeff)
+        dWr, dxr = oracle.router_logits_bwd(np64(inp["x"]), inp["w_r"].numpy(), dz)
+        g = dict(g, d_logits=g["d_logits"] + dz, dW_r=g["dW_r"] + dWr, dx=g["dx"] + dxr, aux=L)
     return layer, c, g
 
 
@@ -115,6 +120,15 @@ def test_layer_capacity_dropping(gpu, gated):
     assert (c["route"]["dst_row"] < 0).sum() > 0  # the case really drops
     _check(cfg, layer, c, g)
     assert_close("d_topk_w", layer.d_topk_w, g["d_topk_w"], TOL[cfg.gemm])
+
+
+def test_layer_aux_loss(gpu):
+    """Auxiliary load-balancing loss: its value, and its gradient added to the
+    router's (through d_logits into dW_r and dx)."""
+    cfg = inputs.CONFIGS["small_aux"]
+    layer, c, g = _run(cfg, 0)
+    _check(cfg, layer, c, g)
+    assert abs(float(layer.aux_loss.item()) - g["aux"]) <= 1e-5 * abs(g["aux"])
 
 
 def test_layer_repeat_is_bitwise_deterministic(gpu):

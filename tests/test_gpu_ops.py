@@ -436,3 +436,27 @@ def test_apply_capacity_bit_exact(gpu, T, E, k, C):
     src = out["src_token"].cpu().numpy()
     np.testing.assert_array_equal(src[:n], ref["src_token"])
     assert (src[n:] == -7).all()  # past the kept rows: not written
+
+
+@pytest.mark.parametrize("T,E,k,score", [(700, 13, 3, "softmax"), (4096, 256, 8, "sigmoid"),
+                                         (65, 1000, 4, "softmax")])
+def test_aux_loss(gpu, T, E, k, score):
+    """Auxiliary load-balancing loss and its gradient (added to d_logits)."""
+    print(f"aux loss T={T} E={E} k={k} {score}", flush=True)
+    z = _keys(T, E, 7 + E, "normal")
+    r = oracle.route(z, k, score, True)
+    L, dz = oracle.aux_loss(z, r["counts"], k, score, 0.01)
+    zz = torch.from_numpy(z).to(DEV)
+    counts = torch.from_numpy(r["counts"].astype(np.int32)).to(DEV)
+    loss = torch.empty(1, dtype=torch.float32, device=DEV)
+    ws = torch.empty(abi.moe_aux_loss_workspace_bytes(T, E), dtype=torch.uint8, device=DEV)
+    sc = abi.SOFTMAX if score == "softmax" else abi.SIGMOID
+    abi.moe_aux_loss(zz, counts, k, sc, 0.01, loss=loss, workspace=ws)
+    assert abs(float(loss.item()) - L) <= 1e-5 * abs(L), (float(loss.item()), L)
+    # the gradient is added to d_logits: twice onto zeros gives 2 dz (the
+    # values are ~1e-7, so compare without a large base that would cancel)
+    dl = torch.zeros((T, E), dtype=torch.float32, device=DEV)
+    abi.moe_aux_loss(zz, counts, k, sc, 0.01, d_logits=dl)
+    assert_close("d_logits", dl, dz, TOL["f32"])
+    abi.moe_aux_loss(zz, counts, k, sc, 0.01, d_logits=dl)
+    assert_close("d_logits (added twice)", dl, 2 * dz, TOL["f32"])

@@ -230,3 +230,26 @@ def test_capacity_keeps_the_lowest_tokens_of_each_expert():
             assert c["src_token"][c["dst_row"][t, j]] == t
         np.testing.assert_array_equal(c["topk_w"], r["topk_w"])
     assert oracle.capacity_of(1.0, 200, 2, 6) == 67
+
+
+@pytest.mark.parametrize("score", ["softmax", "sigmoid"])
+def test_aux_loss_balanced_value_and_finite_differences(score):
+    """At perfect balance (equal counts, equal probabilities) the loss is
+    exactly coeff; its gradient matches central differences of the loss with
+    the counts held fixed."""
+    T, E, k, coeff = 40, 8, 2, 0.01
+    L, dz = oracle.aux_loss(np.zeros((T, E), np.float32), np.full(E, T * k // E), k, score, coeff)
+    assert abs(L - coeff) < 1e-15
+    rng = np.random.default_rng(3)
+    z = rng.standard_normal((T, E))
+    counts = rng.multinomial(T * k, np.ones(E) / E)
+    L, dz = oracle.aux_loss(z, counts, k, score, coeff)
+    num = np.zeros_like(z)
+    eps = 1e-6
+    for pos in np.ndindex(z.shape):
+        zp, zm = z.copy(), z.copy()
+        zp[pos] += eps
+        zm[pos] -= eps
+        num[pos] = (oracle.aux_loss(zp, counts, k, score, coeff)[0] -
+                    oracle.aux_loss(zm, counts, k, score, coeff)[0]) / (2 * eps)
+    np.testing.assert_allclose(dz, num, rtol=0, atol=1e-10)
