@@ -10,7 +10,19 @@ weights.  The scale arithmetic is fp32 (read where the page is silent):
     inv   = fp32(448 / amax), or 1.0 when amax == 0
     code  = E4M3 round-to-nearest-even, saturated to +-448, of fp32(v * inv)
     value = decode(code) * scale
+
+MX recipe (the OCP Microscaling Formats specification, MXFP8 with E4M3
+elements, cited as [OCP-MX]): blocks of 32 elements along the contraction
+axis share one E8M0 scale 2^X with
+    X     = floor(log2(amax)) - 8   (8: exponent of the largest power of two
+                                     an E4M3 element holds), clamped to
+                                     [-127, 127]; -127 when amax == 0
+    code  = E4M3 round-to-nearest-even, saturated to +-448, of v * 2^-X
+            (an exact scaling)
+    value = decode(code) * 2^X;   stored scale byte = X + 127
 """
+
+import math
 
 import numpy as np
 
@@ -160,7 +172,7 @@ def dequantize_token_tiles(q, s, block=128):
 
 
 def layer_fp8(x, w_r, w13, w2, dout, k, score, renorm, logit_bias=None, shared=None,
-              quantize=True, block=128):
+              quantize=True, block=128, recipe="block"):
     """Forward and backward of the MoE layer with every expert-GEMM input
     quantized blockwise to E4M3 (the fp8 recipe above), computed as fp64
     grouped GEMMs on the dequantized values.
@@ -173,19 +185,33 @@ def layer_fp8(x, w_r, w13, w2, dout, k, score, renorm, logit_bias=None, shared=N
     activations), so a value is rounded to bf16 before it is quantized.
     Routing, permutation, SwiGLU and combine are exact (fp64, fp32 keys).
     ``quantize=False`` replaces every quantize/dequantize pair with the
-    identity (the exact layer).  Returns a dict of outputs and gradients.
+    identity (the exact layer).  ``recipe="mx"``: MXFP8 instead (1 x 32
+    blocks along every operand's contraction axis, E8M0 scales; a weight then
+    has one quantization per GEMM that reads it).  Returns a dict of outputs
+    and gradients.
     """
     from . import moe_oracle as o
+
+    mx = recipe == "mx"
 
     def q_rows(a):
         if not quantize:
             return o.f64(a)
+        if mx:
+            return dequantize_mx_rows(*quantize_mx_rows(to_bf16(a)))
         qq, ss = quantize_rows(to_bf16(a), block)
         return dequantize_rows(qq, ss, block)
 
-    def q_weights(w):
+    def q_weights(w, use="fwd"):
         if not quantize:
             return o.f64(w)
+        if mx:
+            out = []
+            for wg in w:
+                qf, sf, qd, sd = quantize_mx_weight(to_bf16(wg))
+                out.append(dequantize_mx_rows(qf, sf).T if use == "fwd"
+                           else dequantize_mx_rows(qd, sd))
+            return np.stack(out)
         return np.stack([dequantize_blocks(*quantize_blocks(to_bf16(wg), block), block)
                          for wg in w])
 
@@ -193,6 +219,9 @@ def layer_fp8(x, w_r, w13, w2, dout, k, score, renorm, logit_bias=None, shared=N
         """Returns the padded dequantized rows and the padded offsets."""
         if not quantize:
             return o.f64(a), np.asarray(offsets, np.int64)
+        if mx:
+            qq, ss, poff = quantize_mx_token_tiles(to_bf16(a), offsets)
+            return dequantize_mx_token_tiles(qq, ss), poff
         qq, ss, poff = quantize_token_tiles(to_bf16(a), offsets, block)
         return dequantize_token_tiles(qq, ss, block), poff
 
@@ -202,6 +231,7 @@ def layer_fp8(x, w_r, w13, w2, dout, k, score, renorm, logit_bias=None, shared=N
     r = o.route(z, k, score, renorm)
     off = r["offsets"]
     w13d, w2d = q_weights(w13), q_weights(w2)
+    w13g, w2g = (q_weights(w13, "dgrad"), q_weights(w2, "dgrad")) if mx else (w13d, w2d)
     xp = o.permute(x, r["src_token"])
     ab = o.grouped_gemm_fwd(q_rows(xp), w13d, off)
     h = o.swiglu(ab)
@@ -209,6 +239,8 @@ def layer_fp8(x, w_r, w13, w2, dout, k, score, renorm, logit_bias=None, shared=N
     ys = None
     if shared is not None:
         ws13d, ws2d = q_weights(np.asarray(shared[0])[None]), q_weights(np.asarray(shared[1])[None])
+        ws13g, ws2g = ((q_weights(np.asarray(shared[0])[None], "dgrad"),
+                        q_weights(np.asarray(shared[1])[None], "dgrad")) if mx else (ws13d, ws2d))
         all_rows = np.array([0, T])
         abs_ = o.grouped_gemm_fwd(q_rows(x), ws13d, all_rows)
         hs = o.swiglu(abs_)
@@ -217,9 +249,9 @@ def layer_fp8(x, w_r, w13, w2, dout, k, score, renorm, logit_bias=None, shared=N
 
     dout = o.f64(dout)
     dy, dw = o.unpermute_combine_bwd(dout, y, r["topk_w"], r["dst_row"])
-    dh = o.grouped_gemm_dgrad(q_rows(dy), w2d, off)
+    dh = o.grouped_gemm_dgrad(q_rows(dy), w2g, off)
     dab = o.swiglu_bwd(dh, ab)
-    dxp = o.grouped_gemm_dgrad(q_rows(dab), w13d, off)
+    dxp = o.grouped_gemm_dgrad(q_rows(dab), w13g, off)
     hp, poff = q_tiles(h, off)
     dyp, _ = q_tiles(dy, off)
     dW2 = o.grouped_gemm_wgrad(hp, dyp, poff)
@@ -229,9 +261,9 @@ def layer_fp8(x, w_r, w13, w2, dout, k, score, renorm, logit_bias=None, shared=N
     res = {}
     addends = []
     if shared is not None:
-        dhs = o.grouped_gemm_dgrad(q_rows(dout), ws2d, all_rows)
+        dhs = o.grouped_gemm_dgrad(q_rows(dout), ws2g, all_rows)
         dabs = o.swiglu_bwd(dhs, abs_)
-        addends.append(o.grouped_gemm_dgrad(q_rows(dabs), ws13d, all_rows))
+        addends.append(o.grouped_gemm_dgrad(q_rows(dabs), ws13g, all_rows))
         hsp, ps = q_tiles(hs, all_rows)
         doutp, _ = q_tiles(dout, all_rows)
         xsp, _ = q_tiles(x, all_rows)
@@ -244,3 +276,79 @@ def layer_fp8(x, w_r, w13, w2, dout, k, score, renorm, logit_bias=None, shared=N
     dx = o.permute_bwd(dxp, r["dst_row"], addends=tuple(addends))
     res.update(out=out, dx=dx, d_logits=dz, dW_r=dWr, dW13=dW13, dW2=dW2, z=z, route=r)
     return res
+
+
+# ---------------------------------------------------------------- MXFP8 --
+MX_BLOCK = 32
+MX_EMAX = 8
+
+
+def mx_exponent(amax):
+    """Shared exponent X of an MX block with max magnitude ``amax`` (exact:
+    frexp gives floor(log2) for normal and subnormal values alike)."""
+    amax = float(np.float32(amax))
+    if amax == 0.0:
+        return -127
+    _, e = math.frexp(amax)          # amax = m 2^e, 0.5 <= m < 1
+    return int(min(127, max(-127, (e - 1) - MX_EMAX)))
+
+
+def mx_quantize_block(v):
+    """Codes and scale byte of one block (1-D, float32 values)."""
+    v = np.asarray(v, dtype=np.float32)
+    x = mx_exponent(np.max(np.abs(v)) if v.size else 0.0)
+    return encode(np.ldexp(v.astype(np.float64), -x).astype(np.float32)), x + 127
+
+
+def mx_dequantize(q, sbytes):
+    """decode(q) * 2^(byte - 127), sbytes broadcast to q's shape by the caller."""
+    return decode(q) * np.ldexp(1.0, np.asarray(sbytes, np.int64) - 127)
+
+
+def quantize_mx_rows(x):
+    """1 x 32 blocks along the rows of x [M, K]: codes uint8 [M, K] and
+    scale bytes uint8 [M, K / 32]."""
+    x = np.asarray(x, dtype=np.float32)
+    M, K = x.shape
+    q = np.empty((M, K), dtype=np.uint8)
+    s = np.empty((M, K // MX_BLOCK), dtype=np.uint8)
+    for i in range(M):
+        for b in range(K // MX_BLOCK):
+            q[i, b * 32:(b + 1) * 32], s[i, b] = mx_quantize_block(x[i, b * 32:(b + 1) * 32])
+    return q, s
+
+
+def dequantize_mx_rows(q, s):
+    return mx_dequantize(q, np.repeat(s, MX_BLOCK, axis=1))
+
+
+def quantize_mx_weight(w):
+    """One expert's weight [K, N] for both GEMMs that read it: the forward
+    contracts over K (blocks of 32 along K for each column: codes transposed
+    [N, K], scales [N, K/32]); the data gradient contracts over N (blocks of
+    32 along N for each row: codes [K, N], scales [K, N/32])."""
+    w = np.asarray(w, dtype=np.float32)
+    qf, sf = quantize_mx_rows(w.T)
+    qd, sd = quantize_mx_rows(w)
+    return qf, sf, qd, sd
+
+
+def quantize_mx_token_tiles(x, offsets):
+    """32-token x 1 blocks along the rows of x [M, K] per group of rows,
+    each group zero-padded to a multiple of 128 rows: codes uint8 [M_pad, K],
+    scale bytes uint8 [M_pad / 32, K], padded offsets."""
+    x = np.asarray(x, dtype=np.float32)
+    M, K = x.shape
+    poff = padded_offsets(offsets, 128)
+    M_pad = int(poff[-1])
+    xp = np.zeros((M_pad, K), dtype=np.float32)
+    for g in range(len(offsets) - 1):
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        xp[poff[g]:poff[g] + hi - lo] = x[lo:hi]
+    qT, sT = quantize_mx_rows(xp.T) if M_pad else (np.zeros((K, 0), np.uint8),
+                                                   np.zeros((K, 0), np.uint8))
+    return qT.T.copy(), sT.T.copy(), poff
+
+
+def dequantize_mx_token_tiles(q, s):
+    return mx_dequantize(q, np.repeat(s, MX_BLOCK, axis=0))

@@ -177,3 +177,99 @@ def test_to_bf16_matches_torch():
                         [0.0, -0.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 65504.0]]).astype(np.float32)
     ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float32).numpy()
     np.testing.assert_array_equal(fp8.to_bf16(v), ref)
+
+
+def test_mx_exponent_landmarks():
+    """Shared exponent floor(log2(amax)) - 8 on landmarks: powers of two and
+    their neighbours, fp32 subnormals, clamping, zero."""
+    assert fp8.mx_exponent(0.0) == -127
+    assert fp8.mx_exponent(256.0) == 0 and fp8.mx_exponent(511.99) == 0
+    assert fp8.mx_exponent(255.99) == -1 and fp8.mx_exponent(512.0) == 1
+    assert fp8.mx_exponent(1.0) == -8 and fp8.mx_exponent(np.float32(2.0 ** -100)) == -108
+    assert fp8.mx_exponent(np.float32(2.0 ** -140)) == -127          # subnormal, clamped
+    assert fp8.mx_exponent(np.float32(2.0 ** -119 * 1.5)) == -127    # -119 - 8 clamped
+    assert fp8.mx_exponent(np.float32(3.0e38)) == 127 - 8
+
+
+def test_mx_blocks_round_trip_exactly():
+    """Blocks built from E4M3 codes and a shared exponent X, with the largest
+    magnitude in [256, 448]: their MX quantization returns exactly those codes
+    and X (the scale is the block's power of two, every value is
+    representable).  Also: elements in (448, 512) x 2^X saturate to 448."""
+    rng = np.random.default_rng(9)
+    big = [c for c in range(0x7F) if 256 <= fp8.decode(c) <= 448]
+    for _ in range(200):
+        X = int(rng.integers(-100, 100))
+        codes = rng.integers(0, 0x7F, 32).astype(np.uint8)
+        codes[rng.integers(0, 32)] = rng.choice(big)
+        codes |= (rng.integers(0, 2, 32) << 7).astype(np.uint8)
+        v = (fp8.decode(codes) * 2.0 ** X).astype(np.float32)
+        q, sb = fp8.mx_quantize_block(v)
+        assert sb == X + 127
+        np.testing.assert_array_equal(q, codes)
+    v = np.zeros(32, np.float32)
+    v[0], v[1] = 500.0 * 2.0 ** -20, 1.0 * 2.0 ** -20
+    q, sb = fp8.mx_quantize_block(v)
+    assert sb == -20 + 127 and q[0] == 0x7E and fp8.decode(q[1]) == 1.0
+
+
+def test_mx_weight_layouts_and_layer_wiring():
+    """The two MX quantizations of a weight cover it along K (forward) and
+    along N (dgrad).  Each dequantizes to within half an E4M3 step (2^-4
+    relative) of the weight, except elements above 448 x 2^X, which saturate
+    (error below 1/8 relative: the block maximum is below 512 x 2^X).  And the
+    MX layer chain with quantization switched off is the exact layer."""
+    rng = np.random.default_rng(2)
+    w = rng.standard_normal((64, 96)).astype(np.float32)
+    qf, sf, qd, sd = fp8.quantize_mx_weight(w)
+    assert qf.shape == (96, 64) and sf.shape == (96, 2) and qd.shape == (64, 96) and sd.shape == (64, 3)
+    for deq in (fp8.dequantize_mx_rows(qf, sf).T, fp8.dequantize_mx_rows(qd, sd)):
+        err = np.abs(deq - w)
+        assert (err <= np.abs(w) * 2.0 ** -3 + 2.0 ** -17 * np.abs(w).max()).all()
+        assert np.median(err / np.abs(w)) < 2.0 ** -5
+    from test_oracle_layer import _make
+    x, w_r, w13, w2, b, shared, dout = _make(5, T=40, d=12, E=4, k=2, f=10, fs=6, bias=True)
+    c = oracle.layer_forward(x, w_r, w13, w2, 2, oracle.SOFTMAX, True, logit_bias=b, shared=shared)
+    g = oracle.layer_backward(c, dout)
+    r = fp8.layer_fp8(x, w_r, w13, w2, dout, 2, oracle.SOFTMAX, True, logit_bias=b, shared=shared,
+                      quantize=False, recipe="mx")
+    np.testing.assert_allclose(r["out"], c["out"], rtol=0, atol=1e-12)
+    for n in ("dx", "d_logits", "dW_r", "dW13", "dW2", "dWs13", "dWs2"):
+        np.testing.assert_allclose(r[n], g[n], rtol=0, atol=1e-11, err_msg=n)
+
+
+def test_mx_token_tiles_are_32_token_blocks():
+    """A 32-token x 1 MX block is the row quantizer applied to the transposed
+    block; groups pad to 128 rows with zero codes and scale byte 0."""
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((300, 64)) * rng.uniform(0.01, 10, 64)).astype(np.float32)
+    off = np.array([0, 0, 130, 131, 300])
+    q, s, poff = fp8.quantize_mx_token_tiles(x, off)
+    np.testing.assert_array_equal(poff, [0, 0, 256, 384, 640])
+    assert q.shape == (640, 64) and s.shape == (20, 64)
+    for g in range(4):
+        lo, hi, plo = off[g], off[g + 1], poff[g]
+        for b in range((poff[g + 1] - plo) // 32):
+            r0, r1 = lo + b * 32, min(hi, lo + b * 32 + 32)
+            blk = np.zeros((32, 64), np.float32)
+            if r1 > r0:
+                blk[:r1 - r0] = x[r0:r1]
+            qr, sr = fp8.quantize_mx_rows(blk.T)
+            np.testing.assert_array_equal(q[plo + b * 32:plo + b * 32 + 32].T, qr)
+            np.testing.assert_array_equal(s[plo // 32 + b], sr[:, 0])
+    assert (s[9:12] == 0).all() and (q[288:384] == 0).all()      # group 2: one row, then padding
+
+
+def test_mx_layer_chain_close_to_exact_layer():
+    """MXFP8's power-of-two scales lose up to one more bit than an exact
+    per-block scale: still a few per cent of max|ref|."""
+    from test_oracle_layer import _make
+    x, w_r, w13, w2, b, shared, dout = _make(6, T=150, d=256, E=4, k=2, f=128, fs=128, bias=True)
+    e = fp8.layer_fp8(x, w_r, w13, w2, dout, 2, oracle.SIGMOID, True, logit_bias=b, shared=shared,
+                      recipe="mx")
+    c = oracle.layer_forward(x, w_r, w13, w2, 2, oracle.SIGMOID, True, logit_bias=b, shared=shared)
+    g = oracle.layer_backward(c, dout)
+    rel = lambda a, r: np.abs(a - r).max() / np.abs(r).max()  # noqa: E731
+    assert 1e-3 < rel(e["out"], c["out"]) < 0.2
+    for name in ["dx", "dW13", "dW2", "dWs13", "dWs2"]:
+        assert 1e-3 < rel(e[name], g[name]) < 0.2, name
