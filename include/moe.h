@@ -311,6 +311,80 @@ int moe_grouped_gemm_fp8_wgrad(const uint8_t* A_t, const float* a_scale, const u
                                int64_t ldm, int64_t K, int64_t N, int dB_dtype, int accumulate,
                                void* dB, void* stream);
 
+/* ----------------------------------------------------------------- MXFP8 -- */
+/* The microscaling FP8 recipe (section 5, Platform-specific recipes), in the
+ * OCP Microscaling Formats encoding: every operand of every expert GEMM is
+ * quantized in blocks of 32 consecutive elements along its contraction axis,
+ * each block sharing one E8M0 scale byte that the gfx950 matrix cores apply
+ * themselves (v_mfma_scale_f32_32x32x64_f8f6f4).  Per block:
+ *   X = floor(log2(amax)) - 8, clamped to [-127, 127]  (X = -127 if amax = 0)
+ *   byte = X + 127
+ *   code = E4M3 nearest value of v * 2^-X, ties to the even code, saturated
+ *          to +-448 (v * 2^-X < 512, so values in (448, 512) * 2^X clamp)
+ *   value = decode(code) * 2^X
+ * Codes are OCP E4M3 as in the fp8 calls; every input is bf16.  Scale arrays
+ * hold one byte per block, a row's blocks contiguous.
+ * Limits: every blocked size (K, N, ldm) a multiple of 128; code arrays
+ * 8-byte aligned, scale arrays 4-byte aligned, bf16 inputs 16-byte aligned. */
+
+/* 1 x 32 blocks along rows: x [M, K] -> q [M, K], scale [M, K/32]. */
+int moe_quant_mxfp8_rows(const void* x, int64_t M, int64_t K, uint8_t* q, uint8_t* scale,
+                         void* stream);
+
+/* The permutation fused into the row quantizer (section 2, Dispatch): row r
+ * of q / scale is the quantization of x[src_token[r]] for r < offsets[G], so
+ * the permuted bf16 rows are never written.  x [T, K]; src_token [M] int32
+ * (moe_route_topk / moe_apply_capacity); offsets [G+1]; q [M, K] and scale
+ * [M, K/32] out, rows at and past offsets[G] not written.  A src_token entry
+ * outside [0, T) reads as a zero row. */
+int moe_permute_quant_mxfp8(const void* x, int64_t T, int64_t K, const int32_t* src_token,
+                            const int64_t* offsets, int32_t G, int64_t M, uint8_t* q,
+                            uint8_t* scale, void* stream);
+
+/* Both GEMM operand layouts of w [G, K, N], each blocked along the axis its
+ * GEMM contracts:
+ *   q_fwd [G, N, K] (transposed) with s_fwd [G, N, K/32]  (blocks along K)
+ *   q_dgrad [G, K, N]            with s_dgrad [G, K, N/32] (blocks along N) */
+int moe_quant_mxfp8_weights(const void* w, int32_t G, int64_t K, int64_t N, uint8_t* q_fwd,
+                            uint8_t* s_fwd, uint8_t* q_dgrad, uint8_t* s_dgrad, void* stream);
+
+/* 32-token x 1 blocks for the weight gradients, which contract over tokens:
+ * group g's rows offsets[g].. land at padded rows padded[g]..
+ * (moe_padded_offsets with align 128; zero codes past the group's end),
+ * written transposed: q_t [K, ldm] (row c holds column c's codes) and
+ * scale_t [K, ldm/32].  Row r of the groups is x[r] (src_row NULL, x_rows =
+ * M) or x[src_row[r]] (the permutation fused in; entries outside
+ * [0, x_rows) read as zero rows).  ldm = moe_padded_rows_bound(M, G, 128) or
+ * larger, a multiple of 128; padded blocks past padded[G] are not written. */
+int moe_quant_mxfp8_token_tiles(const void* x, int64_t x_rows, const int32_t* src_row,
+                                const int64_t* offsets, const int64_t* padded, int32_t G,
+                                int64_t M, int64_t K, int64_t ldm, uint8_t* q_t, uint8_t* scale_t,
+                                void* stream);
+
+/* MXFP8 grouped GEMMs: the products of the dequantized operands, summed in
+ * fp32; outputs and epilogues as in the bf16 calls.
+ *   forward: C[rows g] = deq(A)[rows g] . deq(B_g)
+ *            A, a_scale from moe_quant_mxfp8_rows / moe_permute_quant_mxfp8
+ *            ([M, K], [M, K/32]); B (q_fwd, s_fwd) of moe_quant_mxfp8_weights
+ *   dgrad:   dA[rows g] = deq(dC)[rows g] . deq(B_g)^T
+ *            dC [M, N] with dc_scale [M, N/32]; B (q_dgrad, s_dgrad)
+ *   wgrad:   dB[g] = deq(A)^T . deq(dC) over group g's padded rows; A_t
+ *            [K, ldm], dC_t [N, ldm] and their scales from
+ *            moe_quant_mxfp8_token_tiles
+ * Limits: K % 128 == 0, N % 128 == 0 (forward SWIGLU: N / 2 % 64 == 0). */
+int moe_grouped_gemm_mxfp8_fwd(const uint8_t* A, const uint8_t* a_scale, const uint8_t* B_fwd,
+                               const uint8_t* b_scale_fwd, const int64_t* offsets, int32_t G,
+                               int64_t M, int64_t K, int64_t N, int epilogue, void* C, void* H,
+                               void* stream);
+int moe_grouped_gemm_mxfp8_dgrad(const uint8_t* dC, const uint8_t* dc_scale,
+                                 const uint8_t* B_dgrad, const uint8_t* b_scale_dgrad,
+                                 const int64_t* offsets, int32_t G, int64_t M, int64_t K, int64_t N,
+                                 int epilogue, const void* ab, void* dA, void* stream);
+int moe_grouped_gemm_mxfp8_wgrad(const uint8_t* A_t, const uint8_t* a_scale_t,
+                                 const uint8_t* dC_t, const uint8_t* dc_scale_t,
+                                 const int64_t* padded, int32_t G, int64_t ldm, int64_t K,
+                                 int64_t N, int dB_dtype, int accumulate, void* dB, void* stream);
+
 /* ------------------------------- Routing weight applied inside the expert -- */
 /* The memory-saving arrangement of the permutation (section 4, Memory): the
  * routing weight of each permuted row scales H before W2,

@@ -284,20 +284,24 @@ MX_EMAX = 8
 
 
 def mx_exponent(amax):
-    """Shared exponent X of an MX block with max magnitude ``amax`` (exact:
-    frexp gives floor(log2) for normal and subnormal values alike)."""
-    amax = float(np.float32(amax))
-    if amax == 0.0:
-        return -127
-    _, e = math.frexp(amax)          # amax = m 2^e, 0.5 <= m < 1
-    return int(min(127, max(-127, (e - 1) - MX_EMAX)))
+    """Shared exponent X of MX blocks with max magnitude ``amax`` (a scalar or
+    an array; exact: frexp gives floor(log2) for normal and subnormal values
+    alike)."""
+    a = np.asarray(amax, dtype=np.float32).astype(np.float64)
+    _, e = np.frexp(a)                     # a = m 2^e, 0.5 <= m < 1
+    x = np.clip((e.astype(np.int64) - 1) - MX_EMAX, -127, 127)
+    x = np.where(a == 0.0, -127, x)
+    return int(x) if x.ndim == 0 else x
 
 
 def mx_quantize_block(v):
-    """Codes and scale byte of one block (1-D, float32 values)."""
+    """Codes and scale bytes of blocks along the last axis of ``v`` (float32
+    values; one block per row of that axis)."""
     v = np.asarray(v, dtype=np.float32)
-    x = mx_exponent(np.max(np.abs(v)) if v.size else 0.0)
-    return encode(np.ldexp(v.astype(np.float64), -x).astype(np.float32)), x + 127
+    x = np.asarray(mx_exponent(np.max(np.abs(v), axis=-1)))
+    scaled = np.ldexp(v.astype(np.float64), -x[..., None]).astype(np.float32)
+    sb = (x + 127).astype(np.uint8)
+    return encode(scaled), (int(sb) if sb.ndim == 0 else sb)
 
 
 def mx_dequantize(q, sbytes):
@@ -310,12 +314,8 @@ def quantize_mx_rows(x):
     scale bytes uint8 [M, K / 32]."""
     x = np.asarray(x, dtype=np.float32)
     M, K = x.shape
-    q = np.empty((M, K), dtype=np.uint8)
-    s = np.empty((M, K // MX_BLOCK), dtype=np.uint8)
-    for i in range(M):
-        for b in range(K // MX_BLOCK):
-            q[i, b * 32:(b + 1) * 32], s[i, b] = mx_quantize_block(x[i, b * 32:(b + 1) * 32])
-    return q, s
+    q, s = mx_quantize_block(x.reshape(M, K // MX_BLOCK, MX_BLOCK))
+    return q.reshape(M, K), np.asarray(s, dtype=np.uint8).reshape(M, K // MX_BLOCK)
 
 
 def dequantize_mx_rows(q, s):

@@ -69,6 +69,17 @@ SIGNATURES = {
                                           _p, _p]),
     "moe_grouped_gemm_fp8_wgrad": (_int, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _int, _int,
                                           _p, _p]),
+    "moe_quant_mxfp8_rows": (_int, [_p, _i64, _i64, _p, _p, _p]),
+    "moe_permute_quant_mxfp8": (_int, [_p, _i64, _i64, _p, _p, _i32, _i64, _p, _p, _p]),
+    "moe_quant_mxfp8_weights": (_int, [_p, _i32, _i64, _i64, _p, _p, _p, _p, _p]),
+    "moe_quant_mxfp8_token_tiles": (_int, [_p, _i64, _p, _p, _p, _i32, _i64, _i64, _i64, _p, _p,
+                                           _p]),
+    "moe_grouped_gemm_mxfp8_fwd": (_int, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _int, _p,
+                                          _p, _p]),
+    "moe_grouped_gemm_mxfp8_dgrad": (_int, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _int, _p,
+                                            _p, _p]),
+    "moe_grouped_gemm_mxfp8_wgrad": (_int, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _int,
+                                            _int, _p, _p]),
 }
 
 _lib = None
@@ -326,3 +337,57 @@ def moe_grouped_gemm_fp8_wgrad(A_t, a_scale, dC_t, dc_scale, padded, dB, accumul
     _call("moe_grouped_gemm_fp8_wgrad", _ptr(A_t), _ptr(a_scale), _ptr(dC_t), _ptr(dc_scale),
           _ptr(padded), G, A_t.shape[1], K, N, dtype_code(dB), int(accumulate), _ptr(dB),
           _stream(stream))
+
+
+# ---- MXFP8 (E4M3 codes and E8M0 scale bytes as torch.uint8 tensors)
+
+def moe_quant_mxfp8_rows(x, q, scale, stream=None):
+    M, K = x.shape
+    _call("moe_quant_mxfp8_rows", _ptr(x), M, K, _ptr(q), _ptr(scale), _stream(stream))
+
+
+def moe_permute_quant_mxfp8(x, src_token, offsets, q, scale, stream=None):
+    T, K = x.shape
+    _call("moe_permute_quant_mxfp8", _ptr(x), T, K, _ptr(src_token), _ptr(offsets),
+          offsets.numel() - 1, q.shape[0], _ptr(q), _ptr(scale), _stream(stream))
+
+
+def moe_quant_mxfp8_weights(w, q_fwd, s_fwd, q_dgrad, s_dgrad, stream=None):
+    G, K, N = w.shape
+    _call("moe_quant_mxfp8_weights", _ptr(w), G, K, N, _ptr(q_fwd), _ptr(s_fwd), _ptr(q_dgrad),
+          _ptr(s_dgrad), _stream(stream))
+
+
+def moe_quant_mxfp8_token_tiles(x, offsets, padded, q_t, scale_t, src_row=None, M=None,
+                                stream=None):
+    """Rows of the groups are x's rows, or x[src_row[r]] with M rows in the
+    groups (the permutation fused in)."""
+    x_rows, K = x.shape
+    if src_row is None:
+        M = x_rows
+    _call("moe_quant_mxfp8_token_tiles", _ptr(x), x_rows, _ptr(src_row), _ptr(offsets),
+          _ptr(padded), offsets.numel() - 1, M, K, q_t.shape[1], _ptr(q_t), _ptr(scale_t),
+          _stream(stream))
+
+
+def moe_grouped_gemm_mxfp8_fwd(A, a_scale, B_fwd, b_scale_fwd, offsets, C, H=None,
+                               epilogue=EPI_NONE, stream=None):
+    G, N, K = B_fwd.shape
+    _call("moe_grouped_gemm_mxfp8_fwd", _ptr(A), _ptr(a_scale), _ptr(B_fwd), _ptr(b_scale_fwd),
+          _ptr(offsets), G, A.shape[0], K, N, epilogue, _ptr(C), _ptr(H), _stream(stream))
+
+
+def moe_grouped_gemm_mxfp8_dgrad(dC, dc_scale, B_dgrad, b_scale_dgrad, offsets, dA,
+                                 epilogue=EPI_NONE, ab=None, stream=None):
+    G, K, N = B_dgrad.shape
+    _call("moe_grouped_gemm_mxfp8_dgrad", _ptr(dC), _ptr(dc_scale), _ptr(B_dgrad),
+          _ptr(b_scale_dgrad), _ptr(offsets), G, dC.shape[0], K, N, epilogue, _ptr(ab), _ptr(dA),
+          _stream(stream))
+
+
+def moe_grouped_gemm_mxfp8_wgrad(A_t, a_scale_t, dC_t, dc_scale_t, padded, dB, accumulate=False,
+                                 stream=None):
+    G, K, N = dB.shape
+    _call("moe_grouped_gemm_mxfp8_wgrad", _ptr(A_t), _ptr(a_scale_t), _ptr(dC_t),
+          _ptr(dc_scale_t), _ptr(padded), G, A_t.shape[1], K, N, dtype_code(dB), int(accumulate),
+          _ptr(dB), _stream(stream))

@@ -1,10 +1,11 @@
-// Grouped GEMM on CDNA4 matrix cores, bf16 (v_mfma_f32_32x32x16_bf16) and fp8
+// Grouped GEMM on CDNA4 matrix cores, bf16 (v_mfma_f32_32x32x16_bf16), fp8
 // E4M3 with fp32 block scales (v_mfma_scale_f32_32x32x64_f8f6f4 at unit
-// scale), fp32 accumulation: the experts' SwiGLU FFNs of "Scalable Training of
+// scale) and MXFP8 (the same instruction with the operands' E8M0 scales),
+// fp32 accumulation: the experts' SwiGLU FFNs of "Scalable Training of
 // Mixture-of-Experts Models with Megatron Core", section 2, Expert Computation
 // (the local experts' GEMMs run together over their ragged row groups), and
-// its section 5 blockwise FP8 recipe (1 x 128 activation tiles, 128 x 128
-// weight blocks).
+// its section 5 low-precision recipes (blockwise FP8: 1 x 128 activation
+// tiles, 128 x 128 weight blocks; MXFP8: 1 x 32 blocks).
 //
 //   forward  C[rows g]  = A[rows g] . B[g]       A [M,K]  B [G,K,N]
 //   dgrad    dA[rows g] = dC[rows g] . B[g]^T    dC [M,N] B [G,K,N]
@@ -45,6 +46,10 @@
 //    the GEMM wants), a k step is one 128-wide scale block, and each step's
 //    MFMA partial is promoted into the fp32 accumulator times the row scale of
 //    A and the row scale of B, both DMA'd into LDS with the stage.
+//  * MXFP8: the same operand path; each row's four E8M0 bytes of a stage (one
+//    per 32 k) arrive as one dword DMA'd like the fp8 scales, and every lane
+//    hands one block's byte to the MFMA, which applies both operands' scales
+//    itself: the partials go straight into the accumulator.
 #include "common.h"
 #include "internal.h"
 
@@ -90,6 +95,8 @@ constexpr uint32_t ROW_SN = 4, WG_SM = 8, WG_SN = 4;
 constexpr uint32_t RSRC_DW3 = 0x00020000u; // raw buffer, 32-bit elements, bounds-checked
 
 enum Mode { FWD = 0, FWD_SWIGLU = 1, DGRAD = 2, DGRAD_SWIGLU_BWD = 3, WGRAD = 4 };
+// operand precision: bf16, fp8 with fp32 block scales, MXFP8 (E8M0 per 32 k)
+enum Prec { P_BF16 = 0, P_FP8 = 1, P_MX = 2 };
 
 static int g_cu_count[64];
 
@@ -227,6 +234,11 @@ struct Params {
   int accumulate;
   const float* sa;  // fp8 row scales of A: [Kc/128][M] (row groups), [M/128][Kc] (wgrad)
   const float* sb;  // fp8 row scales of B: [G][Kc/128][Nout] (row groups), [M/128][Nout] (wgrad)
+  // MXFP8 E8M0 bytes, one per 32 contraction elements of each operand row:
+  // A [M][Kc/32] and B [G][Nout][Kc/32] (row groups), A [Kc][ldm/32] and
+  // B [Nout][ldm/32] (wgrad)
+  const uint8_t* ea;
+  const uint8_t* eb;
   int64_t ldm;      // fp8 wgrad: row length of the transposed operands
   // Routing weight applied inside the expert (row-group modes with SwiGLU):
   // forward H = row_scale[row] * silu(a) * b; backward dH = row_scale[row] *
@@ -337,10 +349,11 @@ __device__ __forceinline__ int64_t b_row(const Tile& t, int rho, int64_t fh) {
 // DMA instruction q of an operand (0 .. 16 x slabs - 1) fills 1 KiB of slab
 // q / 16: in the [row][k] layout rows 8 (q % 16) .. + 7, in the [k][row] layout
 // k rows 4 (q % 16) .. + 3.
-template <int MODE, bool F8, int WN>
+template <int MODE, int Q, int WN>
 __device__ __forceinline__ void setup_loader(const Params& p, const Tile& t, int wave, int lane,
                                              Loader<WN>& L) {
   using C = Cfg<WN>;
+  constexpr bool F8 = Q != P_BF16;
   constexpr int BN = C::BN;
   constexpr int ES = F8 ? 1 : 2;  // element bytes
   constexpr int BK = KStep<F8>::value;
@@ -386,8 +399,22 @@ __device__ __forceinline__ void setup_loader(const Params& p, const Tile& t, int
       L.vb[i] = static_cast<uint32_t>((slab * 128 + r) * ldm + c * 16);
     }
     L.da = L.db = 128;
-    // scales [ldm/128][Kc] and [ldm/128][Nout], block lo/128 + kt; waves past
-    // the A and B vectors repeat wave 0's load into their own unused slot
+    // waves past the A and B vectors repeat wave 0's load into their own
+    // unused slot
+    if (Q == P_MX) {
+      // E8M0 [Kc][ldm/32] and [Nout][ldm/32]: dword lo/128 + kt of each row
+      const int64_t nb = ldm / 32;
+      const int64_t r = wave < 2 || wave >= 2 + 2 * C::B_SLABS
+                            ? t.row0 + (wave < 2 ? wave : 0) * 64 + lane
+                            : t.nt * BN + (wave - 2) * 64 + lane;
+      const uint8_t* e = wave < 2 || wave >= 2 + 2 * C::B_SLABS ? p.ea : p.eb;
+      const int64_t rows = wave < 2 || wave >= 2 + 2 * C::B_SLABS ? p.Kc : p.Nout;
+      L.rs = make_rsrc(e, static_cast<uint64_t>(rows) * nb);
+      L.vs = static_cast<uint32_t>(r * nb + t.lo / 32);
+      L.ds = 4;
+      return;
+    }
+    // scales [ldm/128][Kc] and [ldm/128][Nout], block lo/128 + kt
     const int64_t kb0 = t.lo / 128;
     if (wave < 2 || wave >= 2 + 2 * C::B_SLABS) {
       const int w = wave < 2 ? wave : 0;
@@ -435,7 +462,22 @@ __device__ __forceinline__ void setup_loader(const Params& p, const Tile& t, int
     }
     L.db = static_cast<uint32_t>(BK * N * ES);
   }
-  if (F8) {
+  if (Q == P_MX) {
+    // E8M0: A [M][Kc/32] rows of the tile (rows past the group read as zero
+    // bytes, beside zero codes); B [G][Nout][Kc/32] at b_row(rho); dword kt of
+    // each row; waves past the A and B vectors repeat wave 0's load
+    const int64_t nb = Kc / 32;
+    if (wave < 2 || wave >= 2 + 2 * C::B_SLABS) {
+      const int w = wave < 2 ? wave : 0;
+      L.rs = make_rsrc(p.ea + t.row0 * nb, static_cast<uint64_t>(t.rows) * nb);
+      L.vs = static_cast<uint32_t>((w * 64 + lane) * nb);
+    } else {
+      L.rs = make_rsrc(p.eb + static_cast<int64_t>(t.g) * p.Nout * nb,
+                       static_cast<uint64_t>(p.Nout) * nb);
+      L.vs = static_cast<uint32_t>(b_row<MODE, BN>(t, (wave - 2) * 64 + lane, fh) * nb);
+    }
+    L.ds = 4;
+  } else if (F8) {
     // scales: A [Kc/128][M] at row row0 + rho; B [G][Kc/128][Nout] at b_row(rho);
     // waves past the A and B vectors repeat wave 0's load into their own slot
     const int64_t nkb = Kc / 128;
@@ -568,12 +610,59 @@ __device__ __forceinline__ void compute_stage_fp8(f32x16_t (&acc)[2][2], const L
   }
 }
 
-template <int MODE, bool F8, int WN>
+// MXFP8: the stage's 128 k are four 32-blocks; the dword of a row holds their
+// E8M0 bytes, block b in byte b.  The scaled 32x32x64 MFMA splits its 64 k
+// into two 32-blocks by byte position, not by lane half: bytes 0..15 of both
+// halves form its first block, bytes 16..31 its second, and the scale of
+// block j of a row comes from lane row + 32 j (measured with a one-wave probe
+// of single non-zero codes under distinct per-lane scales).  So in step s
+// lane half h loads the h-th 16 k of block 2 s into bytes 0..15 and the h-th
+// 16 k of block 2 s + 1 into bytes 16..31, and passes the byte of block
+// 2 s + h; the MFMA scales the products itself.
+__device__ __forceinline__ i32x8_t frag_mx(const LDS_AS char* op, int r, int s, int h) {
+  const u32x4_t lo = chunk_kc(op, r, 4 * s + h), hi = chunk_kc(op, r, 4 * s + 2 + h);
+  const u32x4_t v[2] = {lo, hi};
+  return __builtin_bit_cast(i32x8_t, v);
+}
+
+__device__ __forceinline__ void compute_stage_mx(f32x16_t (&acc)[2][2], const LDS_AS char* opA,
+                                                 const LDS_AS char* opB, const LDS_AS uint32_t* eA,
+                                                 int wm, int wn, int wnl, int lane) {
+  const LDS_AS uint32_t* eB = eA + BM;
+  const int h = lane >> 5;
+  uint32_t xa[2], xb[2];
+#pragma unroll
+  for (int ii = 0; ii < 2; ++ii) xa[ii] = eA[wm * 64 + ii * 32 + (lane & 31)] >> (8 * h);
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) xb[jj] = eB[wn * 64 + jj * 32 + (lane & 31)] >> (8 * h);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    i32x8_t a[2], b[2];
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) a[ii] = frag_mx(opA, wm * 64 + ii * 32 + (lane & 31), s, h);
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) b[jj] = frag_mx(opB, wnl * 64 + jj * 32 + (lane & 31), s, h);
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        // format 0 = E4M3 for both; byte 0 of each scale operand is used
+        acc[ii][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            b[jj], a[ii], acc[ii][jj], 0, 0, 0, static_cast<int>(xb[jj] >> (16 * s)), 0,
+            static_cast<int>(xa[ii] >> (16 * s)));
+  }
+}
+
+template <int MODE, int Q, int WN>
 __device__ __forceinline__ void compute_stage(f32x16_t (&acc)[2][2], const LDS_AS char* stage,
                                               int wm, int wn, int lane) {
   const LDS_AS char* opA = stage;
   const LDS_AS char* opB = stage + OP_BYTES * (1 + (wn >> 1));
-  if (F8)
+  if (Q == P_MX)
+    compute_stage_mx(acc, opA, opB,
+                     (const LDS_AS uint32_t*)(stage + (1 + Cfg<WN>::B_SLABS) * OP_BYTES), wm, wn,
+                     wn & 1, lane);
+  else if (Q == P_FP8)
     compute_stage_fp8(acc, opA, opB,
                       (const LDS_AS float*)(stage + (1 + Cfg<WN>::B_SLABS) * OP_BYTES), wm, wn,
                       wn & 1, lane);
@@ -777,9 +866,10 @@ __device__ __forceinline__ void epilogue(const Params& p, const Tile& t, const f
 
 // ---- the kernel ----------------------------------------------------------------
 
-template <int MODE, bool F8, int WN>
+template <int MODE, int Q, int WN>
 __global__ __launch_bounds__(Cfg<WN>::THREADS, Cfg<WN>::WG_PER_CU) void gg_kernel(Params p) {
   using C = Cfg<WN>;
+  constexpr bool F8 = Q != P_BF16;
   constexpr int BN = C::BN;
   constexpr int NTH = C::THREADS;
   constexpr int SB = stage_bytes<WN, F8>();
@@ -854,7 +944,7 @@ __global__ __launch_bounds__(Cfg<WN>::THREADS, Cfg<WN>::WG_PER_CU) void gg_kerne
   cp_t = ld_t;
   cp_i = ld_i;
   Loader<WN> L;
-  if (ld_ok) setup_loader<MODE, F8, WN>(p, ld_t, wave, lane, L);
+  if (ld_ok) setup_loader<MODE, Q, WN>(p, ld_t, wave, lane, L);
   int ld_kt = 0, cp_kt = 0;
   int inflight = 0, ld_slot = 0, cp_slot = 0;
 
@@ -868,7 +958,7 @@ __global__ __launch_bounds__(Cfg<WN>::THREADS, Cfg<WN>::WG_PER_CU) void gg_kerne
       ++ld_i;
       ld_ok = walk_next(walk, ld_i, total, ld_tau) &&
               decode<MODE, F8, BN>(ld_tau, p, s_pre, s_off, NT, total, ld_t);
-      if (ld_ok) setup_loader<MODE, F8, WN>(p, ld_t, wave, lane, L);
+      if (ld_ok) setup_loader<MODE, Q, WN>(p, ld_t, wave, lane, L);
     }
   }
 
@@ -893,10 +983,10 @@ __global__ __launch_bounds__(Cfg<WN>::THREADS, Cfg<WN>::WG_PER_CU) void gg_kerne
         ++ld_i;
         ld_ok = walk_next(walk, ld_i, total, ld_tau) &&
                 decode<MODE, F8, BN>(ld_tau, p, s_pre, s_off, NT, total, ld_t);
-        if (ld_ok) setup_loader<MODE, F8, WN>(p, ld_t, wave, lane, L);
+        if (ld_ok) setup_loader<MODE, Q, WN>(p, ld_t, wave, lane, L);
       }
     }
-    compute_stage<MODE, F8, WN>(acc, lring + cp_slot * SB, wm, wn, lane);
+    compute_stage<MODE, Q, WN>(acc, lring + cp_slot * SB, wm, wn, lane);
     --inflight;
     if (++cp_kt == cp_t.nk) {
       // the slot just consumed is not refilled before the next barrier: stage
@@ -923,31 +1013,31 @@ __global__ __launch_bounds__(Cfg<WN>::THREADS, Cfg<WN>::WG_PER_CU) void gg_kerne
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int MODE, bool F8, int WN>
+template <int MODE, int Q, int WN>
 static hipError_t run_cfg(const Params& p, int64_t tiles_upper_bound, hipStream_t s) {
   if (tiles_upper_bound <= 0) return hipSuccess;
   int64_t grid = static_cast<int64_t>(cu_count()) * Cfg<WN>::WG_PER_CU;  // persistent
   if (tiles_upper_bound < grid) grid = tiles_upper_bound;
   if (grid < 1) grid = 1;
-  gg_kernel<MODE, F8, WN><<<dim3(static_cast<unsigned>(grid)), Cfg<WN>::THREADS, 0, s>>>(p);
+  gg_kernel<MODE, Q, WN><<<dim3(static_cast<unsigned>(grid)), Cfg<WN>::THREADS, 0, s>>>(p);
   return hipGetLastError();
 }
 
 // Row-group modes: tiles of BM rows of a group x BN product columns (SwiGLU:
 // BN/2 gate + BN/2 up columns); at most M/BM + G row tiles.  The wide tile
 // whenever the product width allows it.
-template <int MODE, bool F8>
+template <int MODE, int Q>
 static hipError_t run_rows(const Params& p, hipStream_t s) {
   const int64_t mt = p.M / BM + p.G;
-  if (p.Nout % 256 == 0) return run_cfg<MODE, F8, 4>(p, mt * (p.Nout / 256), s);
-  return run_cfg<MODE, F8, 2>(p, mt * (p.Nout / 128), s);
+  if (p.Nout % 256 == 0) return run_cfg<MODE, Q, 4>(p, mt * (p.Nout / 256), s);
+  return run_cfg<MODE, Q, 2>(p, mt * (p.Nout / 128), s);
 }
 
-template <bool F8>
+template <int Q>
 static hipError_t run_wgrad(const Params& p, hipStream_t s) {
   const int64_t mt = static_cast<int64_t>(p.G) * (p.Kc / BM);
-  if (p.Nout % 256 == 0) return run_cfg<WGRAD, F8, 4>(p, mt * (p.Nout / 256), s);
-  return run_cfg<WGRAD, F8, 2>(p, mt * (p.Nout / 128), s);
+  if (p.Nout % 256 == 0) return run_cfg<WGRAD, Q, 4>(p, mt * (p.Nout / 256), s);
+  return run_cfg<WGRAD, Q, 2>(p, mt * (p.Nout / 128), s);
 }
 
 static Params make_params(const void* A, const void* B, const int64_t* off, int G, int64_t M,
@@ -970,8 +1060,8 @@ hipError_t launch_gg_bf16_fwd(const void* A, const void* B, const int64_t* off, 
                               int64_t K, int64_t N, int epi, void* C, void* H, hipStream_t s) {
   if (M == 0) return hipSuccess;
   const Params p = make_params(A, B, off, G, M, K, N, C, H, nullptr);
-  if (epi == EPI_SWIGLU) return run_rows<FWD_SWIGLU, false>(p, s);
-  return run_rows<FWD, false>(p, s);
+  if (epi == EPI_SWIGLU) return run_rows<FWD_SWIGLU, P_BF16>(p, s);
+  return run_rows<FWD, P_BF16>(p, s);
 }
 
 hipError_t launch_gg_bf16_dgrad(const void* dC, const void* B, const int64_t* off, int G,
@@ -980,8 +1070,8 @@ hipError_t launch_gg_bf16_dgrad(const void* dC, const void* B, const int64_t* of
   if (M == 0) return hipSuccess;
   // contraction over N, product columns K
   const Params p = make_params(dC, B, off, G, M, N, K, dA, nullptr, ab);
-  if (epi == EPI_SWIGLU_BWD) return run_rows<DGRAD_SWIGLU_BWD, false>(p, s);
-  return run_rows<DGRAD, false>(p, s);
+  if (epi == EPI_SWIGLU_BWD) return run_rows<DGRAD_SWIGLU_BWD, P_BF16>(p, s);
+  return run_rows<DGRAD, P_BF16>(p, s);
 }
 
 hipError_t launch_gg_bf16_wgrad(const void* A, const void* dC, const int64_t* off, int G,
@@ -990,7 +1080,7 @@ hipError_t launch_gg_bf16_wgrad(const void* A, const void* dC, const int64_t* of
   Params p = make_params(A, dC, off, G, M, K, N, dB, nullptr, nullptr);
   p.out_f32 = db_f32;
   p.accumulate = accumulate;
-  return run_wgrad<false>(p, s);
+  return run_wgrad<P_BF16>(p, s);
 }
 
 hipError_t launch_gg_bf16_gated_fwd(const void* A, const void* B, const int64_t* off, int G,
@@ -999,7 +1089,7 @@ hipError_t launch_gg_bf16_gated_fwd(const void* A, const void* B, const int64_t*
   if (M == 0) return hipSuccess;
   Params p = make_params(A, B, off, G, M, K, N, AB, H, nullptr);
   p.row_scale = row_scale;
-  return run_rows<FWD_SWIGLU, false>(p, s);
+  return run_rows<FWD_SWIGLU, P_BF16>(p, s);
 }
 
 hipError_t launch_gg_bf16_gated_dgrad(const void* dC, const void* B, const int64_t* off, int G,
@@ -1010,7 +1100,7 @@ hipError_t launch_gg_bf16_gated_dgrad(const void* dC, const void* B, const int64
   Params p = make_params(dC, B, off, G, M, N, K, dAB, nullptr, ab);
   p.row_scale = row_scale;
   p.gate_part = gate_part;
-  return run_rows<DGRAD_SWIGLU_BWD, false>(p, s);
+  return run_rows<DGRAD_SWIGLU_BWD, P_BF16>(p, s);
 }
 
 hipError_t launch_gg_fp8_fwd(const uint8_t* A, const float* sa, const uint8_t* Bt, const float* sb,
@@ -1020,8 +1110,8 @@ hipError_t launch_gg_fp8_fwd(const uint8_t* A, const float* sa, const uint8_t* B
   Params p = make_params(A, Bt, off, G, M, K, N, C, H, nullptr);
   p.sa = sa;
   p.sb = sb;
-  if (epi == EPI_SWIGLU) return run_rows<FWD_SWIGLU, true>(p, s);
-  return run_rows<FWD, true>(p, s);
+  if (epi == EPI_SWIGLU) return run_rows<FWD_SWIGLU, P_FP8>(p, s);
+  return run_rows<FWD, P_FP8>(p, s);
 }
 
 hipError_t launch_gg_fp8_dgrad(const uint8_t* dC, const float* sa, const uint8_t* B,
@@ -1031,8 +1121,8 @@ hipError_t launch_gg_fp8_dgrad(const uint8_t* dC, const float* sa, const uint8_t
   Params p = make_params(dC, B, off, G, M, N, K, dA, nullptr, ab);
   p.sa = sa;
   p.sb = sb;
-  if (epi == EPI_SWIGLU_BWD) return run_rows<DGRAD_SWIGLU_BWD, true>(p, s);
-  return run_rows<DGRAD, true>(p, s);
+  if (epi == EPI_SWIGLU_BWD) return run_rows<DGRAD_SWIGLU_BWD, P_FP8>(p, s);
+  return run_rows<DGRAD, P_FP8>(p, s);
 }
 
 hipError_t launch_gg_fp8_wgrad(const uint8_t* At, const float* sa, const uint8_t* dCt,
@@ -1044,7 +1134,41 @@ hipError_t launch_gg_fp8_wgrad(const uint8_t* At, const float* sa, const uint8_t
   p.ldm = ldm;
   p.out_f32 = db_f32;
   p.accumulate = accumulate;
-  return run_wgrad<true>(p, s);
+  return run_wgrad<P_FP8>(p, s);
+}
+
+hipError_t launch_gg_mx_fwd(const uint8_t* A, const uint8_t* ea, const uint8_t* Bt,
+                            const uint8_t* eb, const int64_t* off, int G, int64_t M, int64_t K,
+                            int64_t N, int epi, void* C, void* H, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  Params p = make_params(A, Bt, off, G, M, K, N, C, H, nullptr);
+  p.ea = ea;
+  p.eb = eb;
+  if (epi == EPI_SWIGLU) return run_rows<FWD_SWIGLU, P_MX>(p, s);
+  return run_rows<FWD, P_MX>(p, s);
+}
+
+hipError_t launch_gg_mx_dgrad(const uint8_t* dC, const uint8_t* ea, const uint8_t* B,
+                              const uint8_t* eb, const int64_t* off, int G, int64_t M, int64_t K,
+                              int64_t N, int epi, const void* ab, void* dA, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  Params p = make_params(dC, B, off, G, M, N, K, dA, nullptr, ab);
+  p.ea = ea;
+  p.eb = eb;
+  if (epi == EPI_SWIGLU_BWD) return run_rows<DGRAD_SWIGLU_BWD, P_MX>(p, s);
+  return run_rows<DGRAD, P_MX>(p, s);
+}
+
+hipError_t launch_gg_mx_wgrad(const uint8_t* At, const uint8_t* ea, const uint8_t* dCt,
+                              const uint8_t* eb, const int64_t* poff, int G, int64_t ldm, int64_t K,
+                              int64_t N, int db_f32, int accumulate, void* dB, hipStream_t s) {
+  Params p = make_params(At, dCt, poff, G, ldm, K, N, dB, nullptr, nullptr);
+  p.ea = ea;
+  p.eb = eb;
+  p.ldm = ldm;
+  p.out_f32 = db_f32;
+  p.accumulate = accumulate;
+  return run_wgrad<P_MX>(p, s);
 }
 
 }  // namespace moe

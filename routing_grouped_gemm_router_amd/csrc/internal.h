@@ -93,6 +93,15 @@ hipError_t launch_gg_fp8_dgrad(const uint8_t* dC, const float* sa, const uint8_t
 hipError_t launch_gg_fp8_wgrad(const uint8_t* At, const float* sa, const uint8_t* dCt,
                                const float* sb, const int64_t* poff, int G, int64_t ldm, int64_t K,
                                int64_t N, int db_f32, int accumulate, void* dB, hipStream_t s);
+hipError_t launch_gg_mx_fwd(const uint8_t* A, const uint8_t* ea, const uint8_t* Bt,
+                            const uint8_t* eb, const int64_t* off, int G, int64_t M, int64_t K,
+                            int64_t N, int epi, void* C, void* H, hipStream_t s);
+hipError_t launch_gg_mx_dgrad(const uint8_t* dC, const uint8_t* ea, const uint8_t* B,
+                              const uint8_t* eb, const int64_t* off, int G, int64_t M, int64_t K,
+                              int64_t N, int epi, const void* ab, void* dA, hipStream_t s);
+hipError_t launch_gg_mx_wgrad(const uint8_t* At, const uint8_t* ea, const uint8_t* dCt,
+                              const uint8_t* eb, const int64_t* poff, int G, int64_t ldm, int64_t K,
+                              int64_t N, int db_f32, int accumulate, void* dB, hipStream_t s);
 
 // quant.hip
 hipError_t launch_quant_rows(const void* x, int64_t M, int64_t K, uint8_t* q, float* sT,
@@ -101,6 +110,15 @@ hipError_t launch_quant_weights(const void* w, int G, int64_t K, int64_t N, uint
                                 uint8_t* qd, float* sd, hipStream_t s);
 hipError_t launch_padded_offsets(const int64_t* off, int G, int64_t M, int64_t align,
                                  int64_t* poff, hipStream_t s);
+hipError_t launch_quant_mx_rows(const void* x, int64_t x_rows, const int32_t* src,
+                                const int64_t* rows_end, int64_t M, int64_t K, uint8_t* q,
+                                uint8_t* e, hipStream_t s);
+hipError_t launch_quant_mx_weights(const void* w, int G, int64_t K, int64_t N, uint8_t* qf,
+                                   uint8_t* ef, uint8_t* qd, uint8_t* ed, hipStream_t s);
+hipError_t launch_quant_mx_token_tiles(const void* x, int64_t x_rows, const int32_t* src,
+                                       const int64_t* off, const int64_t* poff, int G, int64_t M,
+                                       int64_t K, int64_t ldm, uint8_t* qT, uint8_t* eT,
+                                       hipStream_t st);
 hipError_t launch_quant_token_tiles(const void* x, const int64_t* off, const int64_t* poff, int G,
                                     int64_t M, int64_t K, int64_t ldm, uint8_t* qT, float* s,
                                     hipStream_t st);

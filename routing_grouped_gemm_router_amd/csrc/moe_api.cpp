@@ -622,4 +622,145 @@ int moe_grouped_gemm_fp8_wgrad(const uint8_t* A_t, const float* a_scale, const u
                     fn);
 }
 
+static bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+static bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+
+int moe_quant_mxfp8_rows(const void* x, int64_t M, int64_t K, uint8_t* q, uint8_t* scale,
+                         void* stream) {
+  const char* fn = "moe_quant_mxfp8_rows";
+  REQUIRE(M >= 0 && K >= 1, MOE_ERR_SHAPE, "%s: M=%lld K=%lld", fn, static_cast<long long>(M),
+          static_cast<long long>(K));
+  REQUIRE(K % 128 == 0, MOE_ERR_UNSUPPORTED, "%s: K %% 128 != 0", fn);
+  if (M == 0) return ok();
+  REQUIRE(x && q && scale, MOE_ERR_NULL, "%s: x, q and scale are required", fn);
+  REQUIRE(aligned16(x) && aligned8(q) && aligned4(scale), MOE_ERR_UNSUPPORTED, "%s: alignment", fn);
+  return hip_status(moe::launch_quant_mx_rows(x, M, nullptr, nullptr, M, K, q, scale,
+                                              as_stream(stream)),
+                    fn);
+}
+
+int moe_permute_quant_mxfp8(const void* x, int64_t T, int64_t K, const int32_t* src_token,
+                            const int64_t* offsets, int32_t G, int64_t M, uint8_t* q,
+                            uint8_t* scale, void* stream) {
+  const char* fn = "moe_permute_quant_mxfp8";
+  REQUIRE(T >= 0 && K >= 1 && G >= 1 && M >= 0, MOE_ERR_SHAPE, "%s: T=%lld K=%lld G=%d M=%lld", fn,
+          static_cast<long long>(T), static_cast<long long>(K), G, static_cast<long long>(M));
+  REQUIRE(K % 128 == 0, MOE_ERR_UNSUPPORTED, "%s: K %% 128 != 0", fn);
+  if (M == 0) return ok();
+  REQUIRE(src_token && offsets && q && scale && (T == 0 || x), MOE_ERR_NULL,
+          "%s: pointers are required", fn);
+  REQUIRE(aligned16(x) && aligned8(q) && aligned4(scale), MOE_ERR_UNSUPPORTED, "%s: alignment", fn);
+  return hip_status(moe::launch_quant_mx_rows(x, T, src_token, offsets + G, M, K, q, scale,
+                                              as_stream(stream)),
+                    fn);
+}
+
+int moe_quant_mxfp8_weights(const void* w, int32_t G, int64_t K, int64_t N, uint8_t* q_fwd,
+                            uint8_t* s_fwd, uint8_t* q_dgrad, uint8_t* s_dgrad, void* stream) {
+  const char* fn = "moe_quant_mxfp8_weights";
+  REQUIRE(G >= 1 && K >= 1 && N >= 1, MOE_ERR_SHAPE, "%s: G=%d K=%lld N=%lld", fn, G,
+          static_cast<long long>(K), static_cast<long long>(N));
+  REQUIRE(K % 128 == 0 && N % 128 == 0, MOE_ERR_UNSUPPORTED, "%s: K and N must be multiples of 128",
+          fn);
+  REQUIRE(w && q_fwd && s_fwd && q_dgrad && s_dgrad, MOE_ERR_NULL, "%s: all pointers are required",
+          fn);
+  REQUIRE(aligned16(w) && aligned8(q_fwd) && aligned8(q_dgrad) && aligned4(s_fwd) &&
+              aligned4(s_dgrad),
+          MOE_ERR_UNSUPPORTED, "%s: alignment", fn);
+  return hip_status(moe::launch_quant_mx_weights(w, G, K, N, q_fwd, s_fwd, q_dgrad, s_dgrad,
+                                                 as_stream(stream)),
+                    fn);
+}
+
+int moe_quant_mxfp8_token_tiles(const void* x, int64_t x_rows, const int32_t* src_row,
+                                const int64_t* offsets, const int64_t* padded, int32_t G,
+                                int64_t M, int64_t K, int64_t ldm, uint8_t* q_t, uint8_t* scale_t,
+                                void* stream) {
+  const char* fn = "moe_quant_mxfp8_token_tiles";
+  REQUIRE(G >= 1 && M >= 0 && K >= 1 && ldm >= 0 && x_rows >= 0, MOE_ERR_SHAPE,
+          "%s: G=%d M=%lld K=%lld ldm=%lld x_rows=%lld", fn, G, static_cast<long long>(M),
+          static_cast<long long>(K), static_cast<long long>(ldm), static_cast<long long>(x_rows));
+  REQUIRE(G <= 1024, MOE_ERR_UNSUPPORTED, "%s: G=%d above 1024", fn, G);
+  REQUIRE(K % 128 == 0 && ldm % 128 == 0, MOE_ERR_UNSUPPORTED,
+          "%s: K and ldm must be multiples of 128", fn);
+  REQUIRE(ldm >= moe_padded_rows_bound(M, G, 128), MOE_ERR_SHAPE,
+          "%s: ldm=%lld below the padded bound %lld", fn, static_cast<long long>(ldm),
+          static_cast<long long>(moe_padded_rows_bound(M, G, 128)));
+  REQUIRE(src_row || x_rows == M, MOE_ERR_SHAPE, "%s: without src_row, x_rows must equal M", fn);
+  REQUIRE(offsets && padded && q_t && scale_t && (x_rows == 0 || x), MOE_ERR_NULL,
+          "%s: pointers are required", fn);
+  REQUIRE(aligned16(x) && aligned8(q_t) && aligned4(scale_t), MOE_ERR_UNSUPPORTED, "%s: alignment",
+          fn);
+  return hip_status(moe::launch_quant_mx_token_tiles(x, x_rows, src_row, offsets, padded, G, M, K,
+                                                     ldm, q_t, scale_t, as_stream(stream)),
+                    fn);
+}
+
+static int check_gemm_mx(const char* fn, const void* a, const void* sa, const void* b,
+                         const void* sb, const int64_t* off, int32_t G, int64_t M, int64_t K,
+                         int64_t N) {
+  int st = check_gemm_fp8(fn, a, sa, b, sb, off, G, M, K, N);
+  if (st != MOE_OK || M == 0) return st;
+  REQUIRE(aligned4(sa) && aligned4(sb), MOE_ERR_UNSUPPORTED, "%s: scales must be 4-byte aligned",
+          fn);
+  return MOE_OK;
+}
+
+int moe_grouped_gemm_mxfp8_fwd(const uint8_t* A, const uint8_t* a_scale, const uint8_t* B_fwd,
+                               const uint8_t* b_scale_fwd, const int64_t* offsets, int32_t G,
+                               int64_t M, int64_t K, int64_t N, int epilogue, void* C, void* H,
+                               void* stream) {
+  const char* fn = "moe_grouped_gemm_mxfp8_fwd";
+  int st = check_gemm_mx(fn, A, a_scale, B_fwd, b_scale_fwd, offsets, G, M, K, N);
+  if (st != MOE_OK) return st;
+  REQUIRE(epilogue == MOE_EPI_NONE || epilogue == MOE_EPI_SWIGLU, MOE_ERR_SHAPE,
+          "%s: epilogue %d not available in the forward", fn, epilogue);
+  if (epilogue == MOE_EPI_SWIGLU)
+    REQUIRE((N / 2) % 64 == 0, MOE_ERR_UNSUPPORTED, "%s: SWIGLU needs N / 2 %% 64 == 0", fn);
+  if (M == 0) return ok();
+  REQUIRE(epilogue == MOE_EPI_SWIGLU ? H != nullptr : C != nullptr, MOE_ERR_NULL,
+          "%s: output missing", fn);
+  return hip_status(moe::launch_gg_mx_fwd(A, a_scale, B_fwd, b_scale_fwd, offsets, G, M, K, N,
+                                          epilogue, C, H, as_stream(stream)),
+                    fn);
+}
+
+int moe_grouped_gemm_mxfp8_dgrad(const uint8_t* dC, const uint8_t* dc_scale,
+                                 const uint8_t* B_dgrad, const uint8_t* b_scale_dgrad,
+                                 const int64_t* offsets, int32_t G, int64_t M, int64_t K, int64_t N,
+                                 int epilogue, const void* ab, void* dA, void* stream) {
+  const char* fn = "moe_grouped_gemm_mxfp8_dgrad";
+  int st = check_gemm_mx(fn, dC, dc_scale, B_dgrad, b_scale_dgrad, offsets, G, M, K, N);
+  if (st != MOE_OK) return st;
+  REQUIRE(epilogue == MOE_EPI_NONE || epilogue == MOE_EPI_SWIGLU_BWD, MOE_ERR_SHAPE,
+          "%s: epilogue %d not available in dgrad", fn, epilogue);
+  if (M == 0) return ok();
+  REQUIRE(dA && (epilogue != MOE_EPI_SWIGLU_BWD || ab), MOE_ERR_NULL, "%s: output missing", fn);
+  return hip_status(moe::launch_gg_mx_dgrad(dC, dc_scale, B_dgrad, b_scale_dgrad, offsets, G, M, K,
+                                            N, epilogue, ab, dA, as_stream(stream)),
+                    fn);
+}
+
+int moe_grouped_gemm_mxfp8_wgrad(const uint8_t* A_t, const uint8_t* a_scale_t,
+                                 const uint8_t* dC_t, const uint8_t* dc_scale_t,
+                                 const int64_t* padded, int32_t G, int64_t ldm, int64_t K,
+                                 int64_t N, int dB_dtype, int accumulate, void* dB, void* stream) {
+  const char* fn = "moe_grouped_gemm_mxfp8_wgrad";
+  REQUIRE(G >= 1 && ldm >= 0 && K >= 1 && N >= 1, MOE_ERR_SHAPE, "%s: G=%d ldm=%lld K=%lld N=%lld",
+          fn, G, static_cast<long long>(ldm), static_cast<long long>(K), static_cast<long long>(N));
+  REQUIRE(G <= 1024, MOE_ERR_UNSUPPORTED, "%s: G=%d above 1024", fn, G);
+  REQUIRE(K % 128 == 0 && N % 128 == 0 && ldm % 128 == 0, MOE_ERR_UNSUPPORTED,
+          "%s: K, N and ldm must be multiples of 128", fn);
+  REQUIRE(dB_dtype == MOE_BF16 || dB_dtype == MOE_F32, MOE_ERR_DTYPE, "%s: dB must be bf16 or fp32",
+          fn);
+  REQUIRE(padded && dB && a_scale_t && dc_scale_t && (ldm == 0 || (A_t && dC_t)), MOE_ERR_NULL,
+          "%s: pointers are required", fn);
+  REQUIRE(aligned16(A_t) && aligned16(dC_t) && aligned4(a_scale_t) && aligned4(dc_scale_t),
+          MOE_ERR_UNSUPPORTED, "%s: alignment", fn);
+  return hip_status(moe::launch_gg_mx_wgrad(A_t, a_scale_t, dC_t, dc_scale_t, padded, G, ldm, K, N,
+                                            dB_dtype == MOE_F32, accumulate != 0, dB,
+                                            as_stream(stream)),
+                    fn);
+}
+
 }  // extern "C"

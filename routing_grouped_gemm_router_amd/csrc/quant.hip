@@ -11,6 +11,21 @@
 // fp32 division each; 1 and 1 when amax = 0); code = nearest E4M3 value of
 // v * inv, ties to the even code, saturated to +-448.
 //
+// MXFP8 (the same section's microscaling recipe, in the OCP Microscaling
+// Formats encoding): 1 x 32 blocks along each operand's contraction axis, one
+// E8M0 scale 2^X per block with X = floor(log2 amax) - 8 clamped to
+// [-127, 127] (8 = exponent of E4M3's largest power of two), stored as the
+// byte X + 127; code = nearest E4M3 value of v * 2^-X (an exact scaling),
+// ties to even, saturated to +-448.  Layouts (codes as for the fp8 GEMM,
+// scale bytes contiguous along each row's blocks):
+//   rows         q [M, K],           bytes [M, K/32]
+//   weights      qf [G, N, K] with bf [G, N, K/32]   (blocks along k)
+//                qd [G, K, N] with bd [G, K, N/32]   (blocks along n)
+//   token tiles  qT [K, ldm],        bytes [K, ldm/32] (32-token blocks)
+// The row and token-tile quantizers can gather their rows through a row map
+// (the permutation's src_token), so that the permuted bf16 activations are
+// never written.
+//
 // Output layouts are chosen for the fp8 GEMM, which reads every operand
 // k-contiguous and every scale as a contiguous vector over a tile's rows:
 //   rows         q [M, K],           scales [K/128, M]
@@ -252,6 +267,243 @@ __global__ __launch_bounds__(256) void quant_token_tiles_kernel(
     }
     *reinterpret_cast<uint2*>(qT + (c0 + c) * ldm + prow0 + r0) = make_uint2(lo, hi);
   }
+}
+
+// ---- MXFP8 -------------------------------------------------------------------
+
+// E8M0 byte of a block whose largest magnitude is amax: with e the biased
+// exponent field of amax, floor(log2 amax) = e - 127 for normal amax, so the
+// byte X + 127 is e - 8; zero and subnormal amax (e = 0) and e < 8 clamp to
+// X = -127, byte 0.
+__device__ __forceinline__ uint32_t mx_byte(float amax) {
+  const int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu);
+  return static_cast<uint32_t>(e > 8 ? e - 8 : 0);
+}
+
+// codes of v * 2^-X = v * 2^(127 - byte), an exact power-of-two scaling
+__device__ __forceinline__ uint32_t mx_code(float v, uint32_t byte) {
+  return e4m3_encode(ldexpf(v, 127 - static_cast<int>(byte)));
+}
+
+__device__ __forceinline__ uint2 encode8_mx(const float (&f)[8], uint32_t byte) {
+  uint32_t c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = mx_code(f[i], byte);
+  return make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                    c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+}
+
+// bf16 row `r` of the quantizer's input, through the row map if there is one;
+// a map entry outside [0, x_rows) reads as a zero row
+__device__ __forceinline__ void load_row8(const bf16_t* __restrict__ x, int64_t x_rows,
+                                          const int32_t* __restrict__ src, int64_t r, int64_t K,
+                                          int64_t col, float (&f)[8]) {
+  const int64_t sr = src ? static_cast<int64_t>(src[r]) : r;
+  if (sr >= 0 && sr < x_rows) {
+    unpack8(*reinterpret_cast<const uint4*>(x + sr * K + col), f);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = 0.f;
+  }
+}
+
+// 1 x 32 blocks along rows: one lane per 8 elements, 4 lanes per block, 16
+// lanes per 128 elements (whose 4 scale bytes go out as one dword).  Rows at
+// and past *rows_end (when given) are not written.
+__global__ __launch_bounds__(256) void quant_mx_rows_kernel(
+    const bf16_t* __restrict__ x, int64_t x_rows, const int32_t* __restrict__ src,
+    const int64_t* __restrict__ rows_end, int64_t M, int64_t K, uint8_t* __restrict__ q,
+    uint8_t* __restrict__ e) {
+  const int64_t per_row = K / 8;  // a multiple of 16
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t row = idx / per_row;
+  const int64_t c = idx - row * per_row;
+  int64_t end = M;
+  if (rows_end) {
+    const int64_t v = *rows_end;
+    end = v < 0 ? 0 : (v > M ? M : v);
+  }
+  const bool live = row < end;  // uniform over each 16-lane run (one row)
+  float f[8] = {};
+  if (live) load_row8(x, x_rows, src, row, K, c * 8, f);
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  const uint32_t b = mx_byte(amax);
+  if (live) *reinterpret_cast<uint2*>(q + row * K + c * 8) = encode8_mx(f, b);
+  const int base = static_cast<int>(threadIdx.x & 63) & ~15;
+  const uint32_t w = __shfl(b, base, 64) | (__shfl(b, base + 4, 64) << 8) |
+                     (__shfl(b, base + 8, 64) << 16) | (__shfl(b, base + 12, 64) << 24);
+  if (live && (c & 15) == 0) *reinterpret_cast<uint32_t*>(e + row * (K / 32) + c / 4) = w;
+}
+
+// 128 x 128 tile of one expert's w [K, N], quantized twice: 32-column blocks
+// of each row for dgrad (4 neighbouring lanes), 32-row blocks of each column
+// for the forward (one wave holds 32 rows).
+__global__ __launch_bounds__(256) void quant_mx_weights_kernel(
+    const bf16_t* __restrict__ w, int G, int64_t K, int64_t N, uint8_t* __restrict__ qf,
+    uint8_t* __restrict__ ef, uint8_t* __restrict__ qd, uint8_t* __restrict__ ed) {
+  __shared__ uint8_t tile[128][128 + 8];
+  __shared__ uint8_t kbyte[4][128];  // forward: per 32-row block, per column
+  __shared__ uint8_t nbyte[128][4];  // dgrad: per row, per 32-column block
+  const int64_t nkb = K / 128, nnb = N / 128;
+  const int64_t blk = blockIdx.x;
+  const int64_t g = blk / (nkb * nnb);
+  const int64_t kb = (blk / nnb) % nkb, nb = blk % nnb;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int c8 = (t & 15) * 8, r8 = (t >> 4) * 8;  // 8 columns x 8 rows per thread
+  const bf16_t* src = w + (g * K + kb * 128) * N + nb * 128;
+  float f[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) unpack8(*reinterpret_cast<const uint4*>(src + (r8 + i) * N + c8), f[i]);
+  // dgrad operand: blocks of 32 columns
+  uint8_t* dq = qd + (g * K + kb * 128) * N + nb * 128;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float am = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(f[i][j]));
+    am = fmaxf(am, __shfl_xor(am, 1, 64));
+    am = fmaxf(am, __shfl_xor(am, 2, 64));
+    const uint32_t b = mx_byte(am);
+    *reinterpret_cast<uint2*>(dq + (r8 + i) * N + c8) = encode8_mx(f[i], b);
+    if ((t & 3) == 0) nbyte[r8 + i][(t & 15) >> 2] = static_cast<uint8_t>(b);
+  }
+  // forward operand: blocks of 32 rows
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float am = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(f[i][j]));
+    am = fmaxf(am, __shfl_xor(am, 16, 64));
+    am = fmaxf(am, __shfl_xor(am, 32, 64));
+    const uint32_t b = mx_byte(am);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tile[r8 + i][c8 + j] = static_cast<uint8_t>(mx_code(f[i][j], b));
+    if (lane < 16) kbyte[wave][c8 + j] = static_cast<uint8_t>(b);
+  }
+  __syncthreads();
+  // forward codes transposed through LDS: row n holds this tile's 128 k codes
+  uint8_t* fq = qf + (g * N + nb * 128) * K + kb * 128;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int n = (t >> 4) * 8 + i;
+    const int k0 = (t & 15) * 8;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo |= static_cast<uint32_t>(tile[k0 + j][n]) << (8 * j);
+      hi |= static_cast<uint32_t>(tile[k0 + 4 + j][n]) << (8 * j);
+    }
+    *reinterpret_cast<uint2*>(fq + static_cast<int64_t>(n) * K + k0) = make_uint2(lo, hi);
+  }
+  if (t < 128) {
+    const uint32_t wf = kbyte[0][t] | (kbyte[1][t] << 8) | (kbyte[2][t] << 16) |
+                        (static_cast<uint32_t>(kbyte[3][t]) << 24);
+    *reinterpret_cast<uint32_t*>(ef + (g * N + nb * 128 + t) * (K / 32) + kb * 4) = wf;
+    const uint32_t wd = nbyte[t][0] | (nbyte[t][1] << 8) | (nbyte[t][2] << 16) |
+                        (static_cast<uint32_t>(nbyte[t][3]) << 24);
+    *reinterpret_cast<uint32_t*>(ed + (g * K + kb * 128 + t) * (N / 32) + nb * 4) = wd;
+  }
+}
+
+// 32-token x 1 blocks, groups padded to 128 rows, written transposed.  One
+// workgroup per (padded 128-row block, 128 columns); wave w holds the block's
+// rows 32 w .. 32 w + 31.
+__global__ __launch_bounds__(256) void quant_mx_token_tiles_kernel(
+    const bf16_t* __restrict__ x, int64_t x_rows, const int32_t* __restrict__ src,
+    const int64_t* __restrict__ off, const int64_t* __restrict__ poff, int G, int64_t M, int64_t K,
+    int64_t ldm, uint8_t* __restrict__ qT, uint8_t* __restrict__ eT) {
+  __shared__ uint8_t tile[128][128 + 8];
+  __shared__ uint8_t kbyte[4][128];
+  const int64_t rb = blockIdx.y;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 128;
+  const int64_t prow0 = rb * 128;
+  if (prow0 >= poff[G]) return;
+  int lo_g = 0, hi_g = G;
+  while (hi_g - lo_g > 1) {
+    const int mid = (lo_g + hi_g) >> 1;
+    if (poff[mid] <= prow0) lo_g = mid; else hi_g = mid;
+  }
+  int64_t glo = off[lo_g], ghi = off[lo_g + 1];
+  glo = glo < 0 ? 0 : (glo > M ? M : glo);
+  ghi = ghi < glo ? glo : (ghi > M ? M : ghi);
+  const int64_t row0 = glo + (prow0 - poff[lo_g]);
+  const int64_t nvalid = min<int64_t>(128, ghi - row0);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int c8 = (t & 15) * 8, r8 = (t >> 4) * 8;
+  float f[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (r8 + i < nvalid) {
+      load_row8(x, x_rows, src, row0 + r8 + i, K, c0 + c8, f[i]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[i][j] = 0.f;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float am = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(f[i][j]));
+    am = fmaxf(am, __shfl_xor(am, 16, 64));
+    am = fmaxf(am, __shfl_xor(am, 32, 64));
+    const uint32_t b = mx_byte(am);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tile[r8 + i][c8 + j] = static_cast<uint8_t>(mx_code(f[i][j], b));
+    if (lane < 16) kbyte[wave][c8 + j] = static_cast<uint8_t>(b);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = (t >> 4) * 8 + i;
+    const int r0 = (t & 15) * 8;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo |= static_cast<uint32_t>(tile[r0 + j][c]) << (8 * j);
+      hi |= static_cast<uint32_t>(tile[r0 + 4 + j][c]) << (8 * j);
+    }
+    *reinterpret_cast<uint2*>(qT + (c0 + c) * ldm + prow0 + r0) = make_uint2(lo, hi);
+  }
+  if (t < 128) {
+    const uint32_t wv = kbyte[0][t] | (kbyte[1][t] << 8) | (kbyte[2][t] << 16) |
+                        (static_cast<uint32_t>(kbyte[3][t]) << 24);
+    *reinterpret_cast<uint32_t*>(eT + (c0 + t) * (ldm / 32) + prow0 / 32) = wv;
+  }
+}
+
+hipError_t launch_quant_mx_rows(const void* x, int64_t x_rows, const int32_t* src,
+                                const int64_t* rows_end, int64_t M, int64_t K, uint8_t* q,
+                                uint8_t* e, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  const int64_t threads = M * (K / 8);
+  quant_mx_rows_kernel<<<dim3(static_cast<unsigned>((threads + 255) / 256)), 256, 0, s>>>(
+      static_cast<const bf16_t*>(x), x_rows, src, rows_end, M, K, q, e);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_mx_weights(const void* w, int G, int64_t K, int64_t N, uint8_t* qf,
+                                   uint8_t* ef, uint8_t* qd, uint8_t* ed, hipStream_t s) {
+  const int64_t blocks = static_cast<int64_t>(G) * (K / 128) * (N / 128);
+  if (blocks == 0) return hipSuccess;
+  quant_mx_weights_kernel<<<dim3(static_cast<unsigned>(blocks)), 256, 0, s>>>(
+      static_cast<const bf16_t*>(w), G, K, N, qf, ef, qd, ed);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_mx_token_tiles(const void* x, int64_t x_rows, const int32_t* src,
+                                       const int64_t* off, const int64_t* poff, int G, int64_t M,
+                                       int64_t K, int64_t ldm, uint8_t* qT, uint8_t* eT,
+                                       hipStream_t st) {
+  if (ldm == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(K / 128), static_cast<unsigned>(ldm / 128));
+  quant_mx_token_tiles_kernel<<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), x_rows, src,
+                                                    off, poff, G, M, K, ldm, qT, eT);
+  return hipGetLastError();
 }
 
 hipError_t launch_quant_rows(const void* x, int64_t M, int64_t K, uint8_t* q, float* sT,

@@ -15,6 +15,8 @@ all tensors synthetic, N(0, 1) activations and N(0, 1/fan_in) weights):
   deepseek_v3_e256k8 T=8192  d=7168 E=256 k=8 f=2048  bf16, sigmoid top-8, renorm,
                      logit bias N(0, variance 0.5), one shared expert fs=2048
   deepseek_v3_fp8    as deepseek_v3_e256k8 with T=32768 and fp8 E4M3 expert GEMMs
+  deepseek_v3_mxfp8  as deepseek_v3_fp8 with MXFP8 expert GEMMs (1 x 32 blocks,
+                     E8M0 scales)
   deepseek_v3_balanced as deepseek_v3_e256k8 with force-balanced routing (the
                      benchmark setting of section 8: every expert gets exactly
                      T*k/E rows), replayed from a seeded assignment
@@ -48,7 +50,7 @@ class LayerConfig:
     f: int
     fs: int = 0                 # shared-expert ffn width, 0 = none
     dtype: str = "bf16"         # storage dtype of activations / expert weights
-    gemm: str = "bf16"          # arithmetic of the expert GEMMs: f32 | bf16 | fp8
+    gemm: str = "bf16"          # arithmetic of the expert GEMMs: f32 | bf16 | fp8 | mxfp8
     score: str = "softmax"      # softmax | sigmoid
     renorm: bool = True
     bias: str = "none"          # none | zipf | normal
@@ -76,6 +78,8 @@ CONFIGS = {
                                       fs=2048, score="sigmoid", bias="normal"),
     "deepseek_v3_fp8": LayerConfig("deepseek_v3_fp8", T=32768, d=7168, E=256, k=8, f=2048,
                                    fs=2048, gemm="fp8", score="sigmoid", bias="normal"),
+    "deepseek_v3_mxfp8": LayerConfig("deepseek_v3_mxfp8", T=32768, d=7168, E=256, k=8, f=2048,
+                                     fs=2048, gemm="mxfp8", score="sigmoid", bias="normal"),
     "deepseek_v3_balanced": LayerConfig("deepseek_v3_balanced", T=8192, d=7168, E=256, k=8,
                                         f=2048, fs=2048, score="sigmoid", bias="normal",
                                         routing="balanced"),

@@ -19,7 +19,12 @@ in 1 x 128 tiles (moe_quant_fp8_rows), weights in 128 x 128 blocks
 (moe_quant_fp8_weights, once per pass), and the operands of the weight
 gradients in 128-token x 1 tiles of each expert's zero-padded rows
 (moe_quant_fp8_token_tiles); routing, permute, SwiGLU and combine stay bf16 /
-fp32.
+fp32.  With MXFP8 expert GEMMs (the same section's microscaling recipe) every
+operand is blocked 1 x 32 along its contraction axis with E8M0 scales that
+the matrix cores apply; the permutation is fused into the quantizers
+(moe_permute_quant_mxfp8 for the forward operand, moe_quant_mxfp8_token_tiles
+gathering through src_token for the weight gradient), so the permuted bf16
+activations are never written.
 
 No step synchronises with the host: per-expert row counts stay on the device
 and every buffer is sized from T * k.  Buffers are allocated once per layer
@@ -114,7 +119,8 @@ class MoELayer:
         if self.capacity is not None:
             self.full = dict(counts=emp(E, dtype=torch.int32), offsets=emp(E + 1, dtype=torch.int64),
                              dst_row=emp(T, k, dtype=torch.int32), src_token=emp(N, dtype=torch.int32))
-        self.x_perm = emp(N, d)
+        # the MXFP8 path gathers x inside its quantizers: no permuted bf16 copy
+        self.x_perm = emp(N, d) if cfg.gemm != "mxfp8" else None
         self.ab = emp(N, 2 * f)
         self.y = emp(N, d)
         self.out = emp(T, d)
@@ -146,22 +152,36 @@ class MoELayer:
         if self.gated:
             self.w_perm = emp(N, dtype=torch.float32)
             self.gate_part = emp(N, f // 64, dtype=torch.float32)
-        self.fp8 = cfg.gemm == "fp8"
-        if self.fp8:
-            self._alloc_fp8()
+        self.lowp = cfg.gemm if cfg.gemm in ("fp8", "mxfp8") else None
+        self.mx = cfg.gemm == "mxfp8"
+        if self.lowp:
+            self._alloc_lowp()
 
-    def _alloc_fp8(self):
-        c, dev = self.cfg, self.dev
+    def _alloc_lowp(self):
+        c, dev, mx = self.cfg, self.dev, self.mx
         T, d, E, k, f, fs = c.T, c.d, c.E, c.k, c.f, c.fs
         N = T * k
         u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)  # noqa: E731
         f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)  # noqa: E731
+        if mx:
+            self._gemm = dict(fwd=abi.moe_grouped_gemm_mxfp8_fwd,
+                              dgrad=abi.moe_grouped_gemm_mxfp8_dgrad,
+                              wgrad=abi.moe_grouped_gemm_mxfp8_wgrad)
+        else:
+            self._gemm = dict(fwd=abi.moe_grouped_gemm_fp8_fwd,
+                              dgrad=abi.moe_grouped_gemm_fp8_dgrad,
+                              wgrad=abi.moe_grouped_gemm_fp8_wgrad)
 
         def wq(G, K, Nn):  # both operand layouts of a [G, K, N] weight
+            if mx:  # E8M0 bytes per 32 along each layout's contraction axis
+                return dict(qf=u8(G, Nn, K), sf=u8(G, Nn, K // 32), qd=u8(G, K, Nn),
+                            sd=u8(G, K, Nn // 32))
             return dict(qf=u8(G, Nn, K), sf=f32(G, K // 128, Nn), qd=u8(G, K, Nn),
                         sd=f32(G, Nn // 128, K))
 
-        def rows(M, K):  # 1 x 128 row tiles
+        def rows(M, K):  # 1 x 128 row tiles (MX: 1 x 32 blocks)
+            if mx:
+                return dict(q=u8(M, K), s=u8(M, K // 32))
             return dict(q=u8(M, K), s=f32(K // 128, M))
 
         self.q = dict(w13=wq(E, d, 2 * f), w2=wq(E, f, d), x=rows(N, d), h=rows(N, f),
@@ -169,7 +189,9 @@ class MoELayer:
         self.ldm = abi.moe_padded_rows_bound(N, E, 128)
         self.poff = torch.empty(E + 1, dtype=torch.int64, device=dev)
 
-        def tiles(K, ldm):  # 128-token x 1 tiles, transposed
+        def tiles(K, ldm):  # 128-token x 1 tiles (MX: 32-token blocks), transposed
+            if mx:
+                return dict(q=u8(K, ldm), s=u8(K, ldm // 32))
             return dict(q=u8(K, ldm), s=f32(ldm // 128, K))
 
         self.qt = dict(x=tiles(d, self.ldm), dab=tiles(2 * f, self.ldm), h=tiles(f, self.ldm),
@@ -183,68 +205,81 @@ class MoELayer:
             self.qt.update(xs=tiles(d, self.ldm_s), dabs=tiles(2 * fs, self.ldm_s),
                            hs=tiles(fs, self.ldm_s), douts=tiles(d, self.ldm_s))
 
-    # --------------------------------------------------------------- fp8 ---
+    # ------------------------------------------------- fp8 and MXFP8 ---
     def _qrows(self, name, a):
-        abi.moe_quant_fp8_rows(a, self.q[name]["q"], self.q[name]["s"])
+        if self.mx:
+            abi.moe_quant_mxfp8_rows(a, self.q[name]["q"], self.q[name]["s"])
+        else:
+            abi.moe_quant_fp8_rows(a, self.q[name]["q"], self.q[name]["s"])
         return self.q[name]["q"], self.q[name]["s"]
 
-    def _qtiles(self, name, a, offsets, poff):
+    def _qtiles(self, name, a, offsets, poff, src_row=None):
         t = self.qt[name]
-        abi.moe_quant_fp8_token_tiles(a, offsets, poff, t["q"], t["s"])
+        if self.mx:
+            abi.moe_quant_mxfp8_token_tiles(a, offsets, poff, t["q"], t["s"], src_row=src_row,
+                                            M=self.cfg.N)
+        else:
+            abi.moe_quant_fp8_token_tiles(a, offsets, poff, t["q"], t["s"])
         return t["q"], t["s"]
 
     def _qweights(self, name, w):
         t = self.q[name]
-        abi.moe_quant_fp8_weights(w, t["qf"], t["sf"], t["qd"], t["sd"])
+        if self.mx:
+            abi.moe_quant_mxfp8_weights(w, t["qf"], t["sf"], t["qd"], t["sd"])
+        else:
+            abi.moe_quant_fp8_weights(w, t["qf"], t["sf"], t["qd"], t["sd"])
 
-    def _forward_fp8(self, x):
-        c, w, q = self.cfg, self.w, self.q
+    def _forward_lowp(self, x):
+        c, w, q, gm = self.cfg, self.w, self.q, self._gemm
         with self._span("quant_weights"):
             self._qweights("w13", w["w13"])
             self._qweights("w2", w["w2"])
             if self.shared:
                 self._qweights("ws13", self.ws13)
                 self._qweights("ws2", self.ws2)
-        with self._span("quant_x"):
-            xq, xs = self._qrows("x", self.x_perm)
+        if self.mx:
+            with self._span("permute_quant_x"):
+                abi.moe_permute_quant_mxfp8(x, self.src_token, self.offsets, q["x"]["q"],
+                                            q["x"]["s"])
+                xq, xs = q["x"]["q"], q["x"]["s"]
+        else:
+            with self._span("quant_x"):
+                xq, xs = self._qrows("x", self.x_perm)
         with self._span("gemm1_fwd"):
-            abi.moe_grouped_gemm_fp8_fwd(xq, xs, q["w13"]["qf"], q["w13"]["sf"], self.offsets,
-                                         self.ab, self.h, epilogue=abi.EPI_SWIGLU)
+            gm["fwd"](xq, xs, q["w13"]["qf"], q["w13"]["sf"], self.offsets, self.ab, self.h,
+                      epilogue=abi.EPI_SWIGLU)
         with self._span("quant_h"):
             hq, hs = self._qrows("h", self.h)
         with self._span("gemm2_fwd"):
-            abi.moe_grouped_gemm_fp8_fwd(hq, hs, q["w2"]["qf"], q["w2"]["sf"], self.offsets, self.y)
+            gm["fwd"](hq, hs, q["w2"]["qf"], q["w2"]["sf"], self.offsets, self.y)
         if self.shared:
             with self._span("shared_quant_x"):
                 xq_, xs_ = self._qrows("xs", x)
             with self._span("shared_gemm1_fwd"):
-                abi.moe_grouped_gemm_fp8_fwd(xq_, xs_, q["ws13"]["qf"], q["ws13"]["sf"],
-                                             self.off_all, self.abs_, self.hs,
-                                             epilogue=abi.EPI_SWIGLU)
+                gm["fwd"](xq_, xs_, q["ws13"]["qf"], q["ws13"]["sf"], self.off_all, self.abs_,
+                          self.hs, epilogue=abi.EPI_SWIGLU)
             with self._span("shared_quant_h"):
                 hq_, hs_ = self._qrows("hs", self.hs)
             with self._span("shared_gemm2_fwd"):
-                abi.moe_grouped_gemm_fp8_fwd(hq_, hs_, q["ws2"]["qf"], q["ws2"]["sf"],
-                                             self.off_all, self.ys)
+                gm["fwd"](hq_, hs_, q["ws2"]["qf"], q["ws2"]["sf"], self.off_all, self.ys)
 
-    def _backward_fp8(self, dout):
-        q, x = self.q, self.x
+    def _backward_lowp(self, dout):
+        q, x, gm = self.q, self.x, self._gemm
 
         def gemm2_dgrad():
             with self._span("quant_dy"):
                 dyq, dys = self._qrows("dy", self.dy)
             with self._span("gemm2_dgrad"):
-                abi.moe_grouped_gemm_fp8_dgrad(dyq, dys, q["w2"]["qd"], q["w2"]["sd"],
-                                               self.offsets, self.dab,
-                                               epilogue=abi.EPI_SWIGLU_BWD, ab=self.ab)
+                gm["dgrad"](dyq, dys, q["w2"]["qd"], q["w2"]["sd"], self.offsets, self.dab,
+                            epilogue=abi.EPI_SWIGLU_BWD, ab=self.ab)
 
         def gemm2_wgrad():
             with self._span("quant_tiles_h_dy"):
-                abi.moe_padded_offsets(self.offsets, self.x_perm.shape[0], self.poff)
+                abi.moe_padded_offsets(self.offsets, self.cfg.N, self.poff)
                 hT, hTs = self._qtiles("h", self.h, self.offsets, self.poff)
                 dyT, dyTs = self._qtiles("dy", self.dy, self.offsets, self.poff)
             with self._span("gemm2_wgrad"):
-                abi.moe_grouped_gemm_fp8_wgrad(hT, hTs, dyT, dyTs, self.poff, self.dw2)
+                gm["wgrad"](hT, hTs, dyT, dyTs, self.poff, self.dw2)
 
         if self.recompute:  # H in dAB's storage: use it before the dgrad writes dAB
             with self._span("swiglu_recompute"):
@@ -257,35 +292,35 @@ class MoELayer:
         with self._span("quant_dab"):
             dabq, dabs = self._qrows("dab", self.dab)
         with self._span("gemm1_dgrad"):
-            abi.moe_grouped_gemm_fp8_dgrad(dabq, dabs, q["w13"]["qd"], q["w13"]["sd"],
-                                           self.offsets, self.dx_perm)
+            gm["dgrad"](dabq, dabs, q["w13"]["qd"], q["w13"]["sd"], self.offsets, self.dx_perm)
         with self._span("quant_tiles_x_dab"):
-            xT, xTs = self._qtiles("x", self.x_perm, self.offsets, self.poff)
+            if self.mx:  # x's rows gathered through the permutation
+                xT, xTs = self._qtiles("x", x, self.offsets, self.poff, src_row=self.src_token)
+            else:
+                xT, xTs = self._qtiles("x", self.x_perm, self.offsets, self.poff)
             dabT, dabTs = self._qtiles("dab", self.dab, self.offsets, self.poff)
         with self._span("gemm1_wgrad"):
-            abi.moe_grouped_gemm_fp8_wgrad(xT, xTs, dabT, dabTs, self.poff, self.dw13)
+            gm["wgrad"](xT, xTs, dabT, dabTs, self.poff, self.dw13)
         if self.shared:
             with self._span("shared_quant_dout"):
                 dq, ds = self._qrows("douts", dout)
             with self._span("shared_gemm2_dgrad"):
-                abi.moe_grouped_gemm_fp8_dgrad(dq, ds, q["ws2"]["qd"], q["ws2"]["sd"],
-                                               self.off_all, self.dabs,
-                                               epilogue=abi.EPI_SWIGLU_BWD, ab=self.abs_)
+                gm["dgrad"](dq, ds, q["ws2"]["qd"], q["ws2"]["sd"], self.off_all, self.dabs,
+                            epilogue=abi.EPI_SWIGLU_BWD, ab=self.abs_)
             with self._span("shared_quant_tiles_h_dout"):
                 a, sa = self._qtiles("hs", self.hs, self.off_all, self.poff_all)
                 b, sb = self._qtiles("douts", dout, self.off_all, self.poff_all)
             with self._span("shared_gemm2_wgrad"):
-                abi.moe_grouped_gemm_fp8_wgrad(a, sa, b, sb, self.poff_all, self.dws2)
+                gm["wgrad"](a, sa, b, sb, self.poff_all, self.dws2)
             with self._span("shared_quant_dab"):
                 dq, ds = self._qrows("dabs", self.dabs)
             with self._span("shared_gemm1_dgrad"):
-                abi.moe_grouped_gemm_fp8_dgrad(dq, ds, q["ws13"]["qd"], q["ws13"]["sd"],
-                                               self.off_all, self.dxs)
+                gm["dgrad"](dq, ds, q["ws13"]["qd"], q["ws13"]["sd"], self.off_all, self.dxs)
             with self._span("shared_quant_tiles_x_dab"):
                 a, sa = self._qtiles("xs", x, self.off_all, self.poff_all)
                 b, sb = self._qtiles("dabs", self.dabs, self.off_all, self.poff_all)
             with self._span("shared_gemm1_wgrad"):
-                abi.moe_grouped_gemm_fp8_wgrad(a, sa, b, sb, self.poff_all, self.dws13)
+                gm["wgrad"](a, sa, b, sb, self.poff_all, self.dws13)
 
     # ------------------------------------------------------------ forward --
     def _span(self, name):
@@ -318,10 +353,11 @@ class MoELayer:
             with self._span("aux_loss"):
                 abi.moe_aux_loss(self.logits, self.routed_counts, c.k, self.score,
                                  c.aux_loss_coeff, loss=self.aux_loss, workspace=self.aux_ws)
-        with self._span("permute"):
-            abi.moe_permute(x, self.dst_row, self.x_perm)
-        if self.fp8:
-            self._forward_fp8(x)
+        if not self.mx:
+            with self._span("permute"):
+                abi.moe_permute(x, self.dst_row, self.x_perm)
+        if self.lowp:
+            self._forward_lowp(x)
             with self._span("combine"):
                 abi.moe_unpermute_combine(self.y, self.topk_w, self.dst_row,
                                           self.ys if self.shared else None, self.out)
@@ -361,8 +397,8 @@ class MoELayer:
             else:
                 abi.moe_unpermute_combine_bwd(dout, self.y, self.topk_w, self.dst_row, self.dy,
                                               self.d_topk_w)
-        if self.fp8:
-            self._backward_fp8(dout)
+        if self.lowp:
+            self._backward_lowp(dout)
             return self._backward_tail(dout, self.dxs if self.shared else None)
         if self.gated:
             with self._span("gemm2_dgrad"):

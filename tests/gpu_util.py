@@ -7,7 +7,7 @@ import oracle
 from routing_grouped_gemm_router_amd import inputs
 
 # max|err| / max|ref| bounds per arithmetic type (the layer's stated tolerances)
-TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2, "mxfp8": 6e-2}
 
 
 def np64(t):

@@ -1,0 +1,231 @@
+"""MXFP8 (E4M3 codes, one E8M0 scale per 32 contraction elements) path
+against the oracle.
+
+Quantizers: codes and scale bytes bit-exact against oracle.fp8's MX
+functions on the same bf16 inputs (rows, rows gathered through a permutation,
+weights in both layouts, token tiles with and without the gather).  GEMMs: the
+GPU consumes the oracle's codes and scale bytes and must match an fp64
+grouped GEMM of the dequantized values within 6e-2 (the products of codes and
+power-of-two scales are exact; only the fp32 sums round).  Layer: MoELayer
+in MXFP8 mode against oracle.fp8.layer_fp8(recipe="mx") within 6e-2."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import fp8
+from routing_grouped_gemm_router_amd import abi, inputs
+from routing_grouped_gemm_router_amd.layer import MoELayer
+from gpu_util import TOL, assert_close, layer_inputs_without_near_ties, np64, rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _bf16_data(shape, seed, special=False):
+    """Normals times a per-column factor exp(2 N(0, 1)), so that the 32-blocks
+    of a row and of a column span many exponents.  With special=True the
+    first rows hold edge blocks (in their first 32 columns)."""
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(shape, generator=g) * torch.exp(torch.randn(shape[-1], generator=g) * 2)
+    if special:
+        flat = x.view(-1, x.shape[-1])
+        flat[0, :32] = 0.0                                          # all-zero block: byte 0
+        flat[1, :32] = torch.tensor([300.0, 1.0625, 1.1875, -1.0625, 0.0009765625, 3 * 2.0 ** -10]
+                                    + [0.5] * 26)                   # X = 0, E4M3 ties
+        flat[2, :32] = 1e-30                                        # X = -108
+        flat[3, :32] = 1e-39                                        # subnormal amax: X = -127
+        flat[4, :32] = 2.0 ** -20                                   # saturation: 500 x 2^-20
+        flat[4, 0] = 500.0 * 2.0 ** -20                             # above 448 x 2^X
+        flat[5, :32] = -3.0e38                                      # large: X = 119
+    return x.to(torch.bfloat16)
+
+
+def _u8(*shape):
+    return torch.full(shape, 0xAA, dtype=torch.uint8, device=DEV)
+
+
+@pytest.mark.parametrize("M,K", [(300, 512), (1000, 7168), (1, 128)])
+def test_mx_quant_rows_bit_exact(gpu, M, K):
+    x = _bf16_data((M, K), 1, special=M >= 6)
+    q, s = _u8(M, K), _u8(M, K // 32)
+    abi.moe_quant_mxfp8_rows(x.to(DEV), q, s)
+    rq, rs = fp8.quantize_mx_rows(x.float().numpy())
+    np.testing.assert_array_equal(q.cpu().numpy(), rq)
+    np.testing.assert_array_equal(s.cpu().numpy(), rs)
+
+
+@pytest.mark.parametrize("T,K,G,M", [(200, 256, 6, 600), (1000, 7168, 16, 4000)])
+def test_mx_permute_quant_bit_exact(gpu, T, K, G, M):
+    """Row r < offsets[G] is the quantization of x[src_token[r]]; an entry out
+    of range reads as a zero row; rows past offsets[G] are left alone."""
+    x = _bf16_data((T, K), 2, special=True)
+    gen = torch.Generator().manual_seed(3)
+    src = torch.randint(0, T, (M,), generator=gen, dtype=torch.int32)
+    src[5] = -1
+    src[7] = T
+    off = inputs.random_segments(M - 37, G, 4, empty_frac=0.2)   # 37 rows past the end
+    q, s = _u8(M, K), _u8(M, K // 32)
+    abi.moe_permute_quant_mxfp8(x.to(DEV), src.to(DEV), off.to(DEV), q, s)
+    end = int(off[-1])
+    xg = torch.zeros((end, K), dtype=torch.bfloat16)
+    ok = (src[:end] >= 0) & (src[:end] < T)
+    xg[ok] = x[src[:end][ok].long()]
+    rq, rs = fp8.quantize_mx_rows(xg.float().numpy())
+    np.testing.assert_array_equal(q[:end].cpu().numpy(), rq)
+    np.testing.assert_array_equal(s[:end].cpu().numpy(), rs)
+    assert (q[end:].cpu() == 0xAA).all() and (s[end:].cpu() == 0xAA).all()
+
+
+@pytest.mark.parametrize("G,K,N", [(3, 256, 384), (2, 7168, 256)])
+def test_mx_quant_weights_bit_exact(gpu, G, K, N):
+    w = _bf16_data((G, K, N), 2, special=True) * 0.05
+    qf, sf, qd, sd = _u8(G, N, K), _u8(G, N, K // 32), _u8(G, K, N), _u8(G, K, N // 32)
+    abi.moe_quant_mxfp8_weights(w.to(DEV), qf, sf, qd, sd)
+    for g in range(G):
+        rqf, rsf, rqd, rsd = fp8.quantize_mx_weight(w[g].float().numpy())
+        np.testing.assert_array_equal(qf[g].cpu().numpy(), rqf)
+        np.testing.assert_array_equal(sf[g].cpu().numpy(), rsf)
+        np.testing.assert_array_equal(qd[g].cpu().numpy(), rqd)
+        np.testing.assert_array_equal(sd[g].cpu().numpy(), rsd)
+
+
+@pytest.mark.parametrize("M,G,K,gather", [(700, 5, 256, False), (3000, 64, 128, False),
+                                          (128, 1, 7168, False), (1500, 9, 256, True)])
+def test_mx_quant_token_tiles_bit_exact(gpu, M, G, K, gather):
+    off = inputs.random_segments(M, G, 5, empty_frac=0.25, skew=0.5)
+    ldm = abi.moe_padded_rows_bound(M, G, 128)
+    poff = torch.empty(G + 1, dtype=torch.int64, device=DEV)
+    abi.moe_padded_offsets(off.to(DEV), M, poff)
+    qT, sT = _u8(K, ldm), _u8(K, ldm // 32)
+    if gather:
+        T = 400
+        x = _bf16_data((T, K), 3, special=True)
+        src = torch.randint(0, T, (M,), generator=torch.Generator().manual_seed(6),
+                            dtype=torch.int32)
+        src[3] = -5
+        abi.moe_quant_mxfp8_token_tiles(x.to(DEV), off.to(DEV), poff, qT, sT,
+                                        src_row=src.to(DEV), M=M)
+        rows = torch.zeros((M, K), dtype=torch.bfloat16)
+        ok = (src >= 0) & (src < T)
+        rows[ok] = x[src[ok].long()]
+    else:
+        rows = _bf16_data((M, K), 3, special=True)
+        abi.moe_quant_mxfp8_token_tiles(rows.to(DEV), off.to(DEV), poff, qT, sT)
+    rq, rs, rpoff = fp8.quantize_mx_token_tiles(rows.float().numpy(), off.numpy())
+    np.testing.assert_array_equal(poff.cpu().numpy(), rpoff)
+    mp = int(rpoff[-1])
+    np.testing.assert_array_equal(qT.cpu().numpy()[:, :mp].T, rq)
+    np.testing.assert_array_equal(sT.cpu().numpy()[:, :mp // 32].T, rs)
+
+
+def _oracle_mx_weights(W):
+    """Oracle MX codes and bytes of W [G, K, N] in both layouts, with the
+    dequantized weight each GEMM sees."""
+    qs = [fp8.quantize_mx_weight(W[g].float().numpy()) for g in range(W.shape[0])]
+    deq_f = np.stack([fp8.dequantize_mx_rows(qf, sf).T for qf, sf, _, _ in qs])
+    deq_d = np.stack([fp8.dequantize_mx_rows(qd, sd) for _, _, qd, sd in qs])
+    t = lambda i: torch.from_numpy(np.stack([z[i] for z in qs]).copy())  # noqa: E731
+    return deq_f, deq_d, t(0), t(1), t(2), t(3)
+
+
+def _oracle_mx_rows(A):
+    q, s = fp8.quantize_mx_rows(A.float().numpy())
+    return fp8.dequantize_mx_rows(q, s), torch.from_numpy(q), torch.from_numpy(s)
+
+
+@pytest.mark.parametrize("M,G,K,N,swiglu", [(1000, 5, 256, 384, False), (2600, 8, 512, 512, True),
+                                             (129, 1, 128, 256, True), (700, 3, 384, 256, False)])
+def test_mx_grouped_gemm_fwd_dgrad(gpu, M, G, K, N, swiglu):
+    print(f"mxfp8 gemm M={M} G={G} K={K} N={N} swiglu={swiglu}", flush=True)
+    off = inputs.random_segments(M, G, 7, empty_frac=0.2)
+    o = off.numpy()
+    A = _bf16_data((M, K), 8)
+    W = _bf16_data((G, K, N), 9) * K ** -0.5
+    Ad, Aq, As = _oracle_mx_rows(A)
+    Wf, Wd, qf, sf, qd, sd = _oracle_mx_weights(W)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    H = torch.empty((M, N // 2), dtype=torch.bfloat16, device=DEV) if swiglu else None
+    abi.moe_grouped_gemm_mxfp8_fwd(Aq.to(DEV), As.to(DEV), qf.to(DEV), sf.to(DEV), off.to(DEV), C,
+                                   H, epilogue=abi.EPI_SWIGLU if swiglu else abi.EPI_NONE)
+    ref = oracle.grouped_gemm_fwd(Ad, Wf, o)
+    assert_close("C", C, ref, TOL["mxfp8"])
+    assert rel_err(C, ref) < 1e-2
+    if swiglu:
+        assert_close("H", H, oracle.swiglu(ref), TOL["mxfp8"])
+    dC = _bf16_data((M, N), 10)
+    dCd, dCq, dCs = _oracle_mx_rows(dC)
+    dA = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
+    abi.moe_grouped_gemm_mxfp8_dgrad(dCq.to(DEV), dCs.to(DEV), qd.to(DEV), sd.to(DEV),
+                                     off.to(DEV), dA)
+    refd = oracle.grouped_gemm_dgrad(dCd, Wd, o)
+    assert_close("dA", dA, refd, TOL["mxfp8"])
+    assert rel_err(dA, refd) < 1e-2
+
+
+@pytest.mark.parametrize("M,G,K,N", [(1500, 6, 256, 384), (1500, 6, 256, 512), (300, 1, 128, 128)])
+def test_mx_grouped_gemm_wgrad(gpu, M, G, K, N):
+    off = inputs.random_segments(M, G, 11, empty_frac=0.3, skew=0.5)
+    A = _bf16_data((M, K), 12)
+    dC = _bf16_data((M, N), 13)
+    qa, sa, poff = fp8.quantize_mx_token_tiles(A.float().numpy(), off.numpy())
+    qc, sc, _ = fp8.quantize_mx_token_tiles(dC.float().numpy(), off.numpy())
+    ldm = abi.moe_padded_rows_bound(M, G, 128)
+    mp = int(poff[-1])
+    At = torch.zeros((K, ldm), dtype=torch.uint8)
+    At[:, :mp] = torch.from_numpy(qa.T.copy())
+    Ct = torch.zeros((N, ldm), dtype=torch.uint8)
+    Ct[:, :mp] = torch.from_numpy(qc.T.copy())
+    Sa = torch.full((K, ldm // 32), 127, dtype=torch.uint8)
+    Sa[:, :mp // 32] = torch.from_numpy(sa.T.copy())
+    Sc = torch.full((N, ldm // 32), 127, dtype=torch.uint8)
+    Sc[:, :mp // 32] = torch.from_numpy(sc.T.copy())
+    ref = oracle.grouped_gemm_wgrad(fp8.dequantize_mx_token_tiles(qa, sa),
+                                    fp8.dequantize_mx_token_tiles(qc, sc), poff)
+    for dt in (torch.bfloat16, torch.float32):
+        dB = torch.full((G, K, N), float("nan"), dtype=dt, device=DEV)
+        abi.moe_grouped_gemm_mxfp8_wgrad(At.to(DEV), Sa.to(DEV), Ct.to(DEV), Sc.to(DEV),
+                                         torch.from_numpy(poff).to(DEV), dB)
+        assert_close(f"dB {dt}", dB, ref, TOL["mxfp8"])
+        assert rel_err(dB, ref) < 1e-2
+
+
+# Sizes: two quantized computations of the same layer differ where a value's
+# rounding (an E4M3 code or a block's exponent) flips under fp32-vs-fp64
+# rounding; the oracle's own chain moves by ~6 % (dW13) under a 2^-9 relative
+# perturbation of dout at 100 tokens per expert, by ~4 % at 400.  So ~400
+# tokens per expert, where the bound measures the kernels and not the flips.
+SMALL_MX = inputs.LayerConfig("small_mxfp8_shared", T=1600, d=256, E=8, k=2, f=256, fs=128,
+                              gemm="mxfp8", score="sigmoid", bias="normal")
+
+
+@pytest.mark.parametrize("cfg,recompute", [
+    (SMALL_MX, False),
+    (dataclasses.replace(SMALL_MX, name="small_mxfp8_softmax", fs=0, score="softmax",
+                         bias="none", k=4, T=800), False),
+    (dataclasses.replace(SMALL_MX, name="small_mxfp8_zipf_recompute", bias="zipf",
+                         score="softmax"), True),
+], ids=lambda c: c.name if hasattr(c, "name") else f"recompute={c}")
+def test_layer_mxfp8(gpu, cfg, recompute):
+    print(f"mxfp8 layer {cfg.name} recompute={recompute}", flush=True)
+    inp = layer_inputs_without_near_ties(cfg, 0)
+    w = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+    layer = MoELayer(cfg, w, DEV, recompute_act=recompute)
+    assert layer.x_perm is None
+    layer.forward(w["x"])
+    layer.backward(w["dout"])
+    torch.cuda.synchronize()
+    shared = (np64(inp["ws13"]), np64(inp["ws2"])) if cfg.fs else None
+    bias = None if inp["logit_bias"] is None else inp["logit_bias"].numpy()
+    ref = fp8.layer_fp8(np64(inp["x"]), inp["w_r"].numpy(), np64(inp["w13"]), np64(inp["w2"]),
+                        np64(inp["dout"]), cfg.k, cfg.score, cfg.renorm, logit_bias=bias,
+                        shared=shared, recipe="mx")
+    r = ref["route"]
+    np.testing.assert_array_equal(layer.dst_row.cpu().numpy(), r["dst_row"])
+    np.testing.assert_array_equal(layer.offsets.cpu().numpy(), r["offsets"])
+    assert_close("out", layer.out, ref["out"], TOL["mxfp8"])
+    g = layer.grads()
+    for name in ["dx", "d_logits", "dW_r", "dW13", "dW2"] + (["dWs13", "dWs2"] if cfg.fs else []):
+        assert_close(name, g[name], ref[name], TOL["mxfp8"])
