@@ -35,6 +35,7 @@ SIGMOID = "sigmoid"
 __all__ = [
     "SOFTMAX", "SIGMOID", "f64", "router_logits", "select_topk", "gates", "dispatch_map",
     "route", "route_replay", "canonical_experts", "capacity_of", "apply_capacity", "aux_loss",
+    "sigmoid_spec", "selection_keys", "route_expert_bias", "expert_bias_update",
     "route_bwd",
     "router_logits_bwd", "permute", "permute_bwd",
     "grouped_gemm_fwd", "grouped_gemm_dgrad", "grouped_gemm_wgrad", "sigmoid", "silu",
@@ -184,6 +185,83 @@ def route_replay(z, topk_idx, score, renorm):
     counts, offsets, dst_row, src_token = dispatch_map(idx, z.shape[1])
     return dict(topk_idx=idx, topk_w=w, counts=counts, offsets=offsets,
                 dst_row=dst_row, src_token=src_token, changed=changed)
+
+
+# ---------------------------------------------------------------------------
+# Selection-only expert bias: the auxiliary-loss-free biasing that the page's
+# section 7 (Load Balancing) lists among its balancing strategies, without a
+# formula.  Reading: a per-expert bias b is added to the sigmoid scores for
+# the choice of the top k only; the routing weights stay the unbiased
+# sigmoid scores of the chosen experts (renormalised over the k); after each
+# step b moves by a fixed rate against each expert's load imbalance.
+# ---------------------------------------------------------------------------
+
+# Constants of the specified sigmoid (fp32 values).  ln 2 in two parts: the
+# high part has 15 significant bits, so n * LN2_HI is exact for |n| < 2^8.
+_SPEC_LOG2E = np.float32(1.44269504)
+_SPEC_LN2_HI = np.float32(0.693145751953125)
+_SPEC_LN2_LO = np.float32(1.42860677e-06)
+_SPEC_CLAMP = np.float32(87.0)
+# exp(r) on |r| <= ln2 / 2: Taylor coefficients 1/i!, i = 0..7, in fp32
+_SPEC_EXP_C = [np.float32(1.0 / math.factorial(i)) for i in range(8)]
+
+
+def sigmoid_spec(z):
+    """A sigmoid whose every step is one correctly rounded fp32 operation, so
+    that two implementations (this one and the GPU's) agree bit for bit --
+    the selection keys built from it decide integer results.
+
+      x = clamp(-z, -87, 87)               (keeps exp(x) and the result normal)
+      n = round_half_even(x * log2e)        (Cody-Waite reduction)
+      r = (x - n * LN2_HI) - n * LN2_LO
+      p = Horner(c7 .. c0) at r, each step p = p * r + c (a multiply, then an
+          add: no fused multiply-add)
+      e = p * 2^n                            (exact: p * 2^n stays normal)
+      sigma = 1 / (1 + e)
+
+    fp32 NumPy arithmetic rounds every operation to nearest even, which is
+    the specification."""
+    z = np.asarray(z, dtype=np.float32)
+    x = np.clip(-z, -_SPEC_CLAMP, _SPEC_CLAMP).astype(np.float32)
+    n = np.rint(x * _SPEC_LOG2E).astype(np.float32)
+    r = ((x - n * _SPEC_LN2_HI) - n * _SPEC_LN2_LO).astype(np.float32)
+    p = np.full_like(r, _SPEC_EXP_C[7])
+    for c in reversed(_SPEC_EXP_C[:7]):
+        p = (p * r).astype(np.float32)
+        p = (p + c).astype(np.float32)
+    e = np.ldexp(p, n.astype(np.int32)).astype(np.float32)
+    return (np.float32(1.0) / (np.float32(1.0) + e)).astype(np.float32)
+
+
+def selection_keys(z, sel_bias):
+    """key[t, e] = sigmoid_spec(z[t, e]) + b[e], one fp32 addition."""
+    return (sigmoid_spec(z) + np.asarray(sel_bias, dtype=np.float32)).astype(np.float32)
+
+
+def route_expert_bias(z, sel_bias, k, renorm):
+    """Route with a selection-only expert bias on sigmoid scores: the top k
+    by ``selection_keys`` (ties and slot order as in ``select_topk``), the
+    routing weights from the unbiased scores sigmoid_spec(z) of the chosen
+    experts (divided by their sum in float64 when ``renorm``), and the
+    dispatch map of ``route``."""
+    z = np.asarray(z, dtype=np.float32)
+    idx = select_topk(selection_keys(z, sel_bias), k)
+    s = f64(np.take_along_axis(sigmoid_spec(z), idx.astype(np.int64), axis=1))
+    w = s / s.sum(axis=1, keepdims=True) if renorm else s
+    counts, offsets, dst_row, src_token = dispatch_map(idx, z.shape[1])
+    return dict(topk_idx=idx, topk_w=w, counts=counts, offsets=offsets,
+                dst_row=dst_row, src_token=src_token)
+
+
+def expert_bias_update(sel_bias, counts, rate):
+    """b[e] += rate * sign(mean load - load[e]) (in fp32; one addition of
+    +-rate or 0): experts that received more than the mean of the (token,
+    slot) pairs become less attractive.  The sign is taken exactly, from the
+    integers sum(counts) - E * counts[e]."""
+    c = np.asarray(counts, dtype=np.int64)
+    sgn = np.sign(c.sum() - c.size * c).astype(np.float32)
+    step = (np.float32(rate) * sgn).astype(np.float32)
+    return (np.asarray(sel_bias, dtype=np.float32) + step).astype(np.float32)
 
 
 def capacity_of(capacity_factor, T, k, E):

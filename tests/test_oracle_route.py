@@ -253,3 +253,85 @@ def test_aux_loss_balanced_value_and_finite_differences(score):
         num[pos] = (oracle.aux_loss(zp, counts, k, score, coeff)[0] -
                     oracle.aux_loss(zm, counts, k, score, coeff)[0]) / (2 * eps)
     np.testing.assert_allclose(dz, num, rtol=0, atol=1e-10)
+
+
+# ---- selection-only expert bias (auxiliary-loss-free balancing) ----------
+
+def _sigmoid_sweep():
+    rng = np.random.default_rng(0)
+    return np.concatenate([np.linspace(-90, 90, 1_000_001), rng.uniform(-20, 20, 1_000_000),
+                           rng.standard_normal(500_000)]).astype(np.float32)
+
+
+def test_sigmoid_spec_against_the_exact_sigmoid():
+    """Within 2 ulp of the correctly rounded sigmoid on |z| <= 87, inexact on
+    under 30 % of a dense sweep, and non-decreasing.  (Measured: dropping the
+    last Taylor term gives 3 ulp and 32 %, a wrong sign of the low part of
+    ln 2 thousands of ulp.)"""
+    z = _sigmoid_sweep()
+    s = oracle.sigmoid_spec(z)
+    assert s.dtype == np.float32
+    ref = (1.0 / (1.0 + np.exp(-z.astype(np.float64)))).astype(np.float32)
+    ulp = np.abs(s.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    inside = np.abs(z) <= 87
+    assert ulp[inside].max() <= 2
+    assert (ulp[inside] > 0).mean() < 0.30
+    order = np.argsort(z, kind="stable")
+    assert np.all(np.diff(s[order].astype(np.float64)) >= 0)
+
+
+def test_sigmoid_spec_landmarks():
+    s = oracle.sigmoid_spec(np.float32([0.0, -0.0, 17.0, 87.0, 1e30, -87.0, -88.0, -1e30]))
+    assert s[0] == 0.5 and s[1] == 0.5
+    assert s[2] == 1.0 and s[3] == 1.0 and s[4] == 1.0        # 1 + e^-17 rounds to 1
+    assert s[5] == s[6] == s[7]                               # clamped at -87: e^87 finite
+    assert np.isclose(float(s[5]), 1.0 / (1.0 + np.exp(87.0)), rtol=1e-6)
+    assert float(s[5]) >= np.finfo(np.float32).tiny           # normal, never subnormal
+
+
+def test_route_expert_bias_selection_and_unbiased_gates():
+    rng = np.random.default_rng(3)
+    T, E, k = 200, 12, 3
+    z = rng.standard_normal((T, E)).astype(np.float32)
+    b = np.zeros(E, np.float32)
+    b[4], b[7] = 2.0, -2.0            # keys lie in (0, 1) before the bias
+    r = oracle.route_expert_bias(z, b, k, renorm=True)
+    assert (r["topk_idx"][:, 0] == 4).all()                  # forced into slot 0
+    assert not (r["topk_idx"] == 7).any()                    # never chosen
+    # the weights ignore the bias: the sigmoid of the chosen logits, renormalised
+    ref = oracle.gates(z, r["topk_idx"], oracle.SIGMOID, True)
+    np.testing.assert_allclose(r["topk_w"], ref, rtol=1e-6)
+    np.testing.assert_allclose(oracle.route_expert_bias(z, b, k, renorm=False)["topk_w"],
+                               oracle.gates(z, r["topk_idx"], oracle.SIGMOID, False), rtol=1e-6)
+    # brute force: the k experts of largest key, ties to the lower index
+    keys = oracle.selection_keys(z, b)
+    for t in range(T):
+        best = sorted(range(E), key=lambda e: (-float(keys[t, e]), e))[:k]
+        assert list(r["topk_idx"][t]) == best
+    # dispatch map consistent with the chosen experts
+    assert r["counts"].sum() == T * k
+    for t in range(T):
+        for j in range(k):
+            row = r["dst_row"][t, j]
+            e = r["topk_idx"][t, j]
+            assert r["offsets"][e] <= row < r["offsets"][e + 1] and r["src_token"][row] == t
+
+
+def test_route_expert_bias_ties_on_equal_scores():
+    """Scores that round to the same fp32 key tie: the lower index wins."""
+    z = np.float32([[30.0, 40.0, 20.0, -3.0]])      # the first three saturate to 1.0
+    r = oracle.route_expert_bias(z, np.zeros(4, np.float32), 2, renorm=False)
+    assert list(r["topk_idx"][0]) == [0, 1]
+    r = oracle.route_expert_bias(z, np.float32([0, 0, 1e-3, 0]), 2, renorm=False)
+    assert list(r["topk_idx"][0]) == [2, 0]
+
+
+def test_expert_bias_update_by_hand():
+    b = oracle.expert_bias_update(np.zeros(4, np.float32), [5, 1, 2, 0], 0.25)
+    np.testing.assert_array_equal(b, np.float32([-0.25, 0.25, 0.0, 0.25]))   # mean load 2
+    b = oracle.expert_bias_update(np.float32([1.0, 0.0, -1.0]), [3, 0, 0], 0.5)
+    np.testing.assert_array_equal(b, np.float32([0.5, 0.5, -0.5]))           # mean load 1
+    b = oracle.expert_bias_update(np.float32([0.1]), [7], 1e-3)
+    assert b[0] == np.float32(0.1)                                           # at the mean
+    b = oracle.expert_bias_update(np.float32([1.0, 1.0]), [2, 1], 1e-8)
+    assert b[0] == np.float32(1.0 - 1e-8) and b[1] == np.float32(1.0 + 1e-8)  # fp32 add
