@@ -11,7 +11,8 @@ HBM before the timed region.  A step is the whole hot path: router, top-k,
 permute, both grouped GEMMs (SwiGLU fused), shared expert, combine, and the
 backward of every one of them.
 
-Also times the fp8 (E4M3 blockwise) variant with ``--config deepseek_v3_fp8``.
+Also times the fp8 variants: E4M3 with fp32 block scales (``--config
+deepseek_v3_fp8``) and MXFP8 (``--config deepseek_v3_mxfp8``).
 
 Prints ONE JSON line.  ``value`` is the layer's algorithmic FLOP rate (expert
 GEMM FLOPs over the routed rows plus the fp32 router FLOPs, divided by the
@@ -81,12 +82,13 @@ def kernel_work(cfg, n_nonempty, gated=False):
         "gemm1_dgrad": (2.0 * N * 2 * f * d, N * 2 * f * s + w13 + N * d * s),
         "gemm1_wgrad": (2.0 * N * d * 2 * f, N * d * s + N * 2 * f * s + E * d * 2 * f * s),
         "route_topk_bwd": (0.0, T * E * 4 * 2 + 3 * idx),
+        "expert_bias_update": (0.0, E * 4 * 3),
         "swiglu_recompute": (0.0, N * 2 * f * s + N * f * s),
         "router_logits_bwd": (4.0 * T * d * E, T * d * s + T * E * 4 + d * E * 4 * 2 + T * d * 4),
         "permute_bwd": (0.0, N * d * s + idx + T * d * (s + 4 + (s if fs else 0))),
     }
-    if cfg.gemm == "fp8":
-        w.update(fp8_work(cfg, n_nonempty))
+    if cfg.gemm in ("fp8", "mxfp8"):
+        w.update(fp8_work(cfg, n_nonempty, mx=cfg.gemm == "mxfp8"))
         return w
     if gated:
         # routing weight inside the expert: the combine backward is a gather of
@@ -110,17 +112,19 @@ def kernel_work(cfg, n_nonempty, gated=False):
     return w
 
 
-def fp8_work(cfg, n_nonempty):
-    """FLOPs and bytes of the spans of the fp8 expert path.  Activations are
-    stored in bf16 (2 bytes) and quantized to 1-byte E4M3 codes with one fp32
-    scale per 128 elements before each GEMM; weights are re-quantized every
-    step (they change every step), to two copies (k-contiguous along each
-    GEMM's reduction); GEMM outputs are bf16."""
+def fp8_work(cfg, n_nonempty, mx=False):
+    """FLOPs and bytes of the spans of the fp8 expert paths.  Activations are
+    stored in bf16 (2 bytes) and quantized to 1-byte E4M3 codes before each
+    GEMM, with one fp32 scale per 128 elements (blockwise) or one E8M0 byte per
+    32 (MXFP8); weights are re-quantized every step (they change every step),
+    to two copies (k-contiguous along each GEMM's reduction); GEMM outputs are
+    bf16.  MXFP8 gathers x through the permutation inside its quantizers (x
+    read once, the row map read, no permuted bf16 copy)."""
     T, d, E, k, f, fs = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.fs
     N = T * k
 
-    def q(n):            # bytes of n fp8 codes with their block scales
-        return n + n / 128 * 4
+    def q(n):            # bytes of n fp8 codes with their scales
+        return n + (n / 32 if mx else n / 128 * 4)
 
     def rows(m, n):      # bf16 in, fp8 rows out
         return m * n * 2 + q(m * n)
@@ -160,6 +164,10 @@ def fp8_work(cfg, n_nonempty):
             "shared_quant_tiles_x_dab": (0.0, rows(T, d) + rows(T, 2 * fs)),
             "shared_gemm1_wgrad": (2.0 * T * d * 2 * fs, q(T * d) + q(T * 2 * fs) + d * 2 * fs * 2),
         })
+    if mx:
+        gather = T * d * 2 + N * 4 + q(N * d)
+        w["permute_quant_x"] = (0.0, gather)
+        w["quant_tiles_x_dab"] = (0.0, gather + rows(N, 2 * f))
     return w
 
 
@@ -254,10 +262,10 @@ def main():
     from routing_grouped_gemm_router_amd.layer import EventTimer, MoELayer
 
     cfg = inputs.CONFIGS[args.config]
-    if cfg.gemm not in ("bf16", "fp8"):
-        print(f"{cfg.name}: bench.py times the bf16 and fp8 expert paths", file=sys.stderr)
+    if cfg.gemm not in ("bf16", "fp8", "mxfp8"):
+        print(f"{cfg.name}: bench.py times the bf16, fp8 and mxfp8 expert paths", file=sys.stderr)
         return 2
-    gemm_peak = PEAK_FP8_TFLOPS if cfg.gemm == "fp8" else PEAK_BF16_TFLOPS
+    gemm_peak = PEAK_FP8_TFLOPS if cfg.gemm in ("fp8", "mxfp8") else PEAK_BF16_TFLOPS
     dev = "cuda"
     inp = inputs.layer_inputs(cfg, args.seed, dev)
     layer = MoELayer(cfg, inp, dev, recompute_act=args.recompute_act,
@@ -295,7 +303,7 @@ def main():
     gemm_names = [n for n in kernels if "gemm" in n]
     gemm_ms = sum(kernels[n]["ms"] for n in gemm_names)
     gemm_flops = sum(work[n][0] for n in gemm_names)
-    pc_names = ["permute", "combine", "combine_bwd", "permute_bwd"]
+    pc_names = [n for n in ("permute", "combine", "combine_bwd", "permute_bwd") if n in kernels]
     pc_ms = sum(kernels[n]["ms"] for n in pc_names)
     pc_bytes = sum(work[n][1] for n in pc_names)
 
@@ -330,6 +338,7 @@ def main():
         "dtype": cfg.gemm,
         "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights, generated on the GPU)",
         "config": {"workload": cfg.name, "routing": cfg.routing,
+                   "expert_bias": cfg.expert_bias_std > 0,
                    "recompute_act": bool(args.recompute_act), "gate_in_ffn": bool(args.gate_in_ffn),
                    "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
                    "ffn": cfg.f, "shared_ffn": cfg.fs, "score": cfg.score, "renorm": cfg.renorm,

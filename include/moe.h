@@ -114,6 +114,35 @@ int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int sco
                    int32_t* dst_row, int32_t* src_token, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* Top-k with a selection-only expert bias on sigmoid scores (the
+ * auxiliary-loss-free biasing of section 7, Load Balancing): the key of
+ * expert e is sigmoid_spec(logits[t, e]) + sel_bias[e] (one fp32 addition);
+ * selection, slot order and the dispatch map as in moe_route_topk on those
+ * keys; the routing weights are the UNBIASED scores sigmoid_spec(logits) of
+ * the chosen experts, divided by their sum over the k when renorm != 0.
+ * sigmoid_spec is a fixed sequence of correctly rounded fp32 operations, so
+ * that any implementation can reproduce the keys bit for bit:
+ *   x = min(max(-z, -87), 87);  n = rint(x * 1.44269504f)  (ties to even)
+ *   r = (x - n * 0.693145751953125f) - n * 1.42860677e-06f
+ *   p = 1/5040; p = p * r + c for c = 1/720, 1/120, 1/24, 1/6, 1/2, 1, 1
+ *       (the fp32 values of 1/i!; a multiply, then an add: no fused multiply-add)
+ *   sigmoid_spec(z) = 1 / (1 + p * 2^n)
+ * sel_bias [E] fp32; other arguments as in moe_route_topk (workspace from
+ * moe_route_topk_workspace_bytes). */
+int moe_route_topk_expert_bias(const float* logits, const float* sel_bias, int64_t T, int32_t E,
+                               int32_t k, int renorm, int32_t* topk_idx, float* topk_w,
+                               int32_t* counts, int64_t* offsets, int32_t* dst_row,
+                               int32_t* src_token, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* The expert-bias update that follows each step: with L = sum(counts) and
+ * E experts, sel_bias[e] += rate * sign(L - E * counts[e]) (fp32; the sign
+ * from exact integers): an expert above the mean load becomes less
+ * attractive, one below it more.  counts [E] int32 (the routed loads, before
+ * any dropping); sel_bias [E] fp32 in/out.  E <= 1024. */
+int moe_expert_bias_update(const int32_t* counts, int32_t E, float rate, float* sel_bias,
+                           void* stream);
+
 /* Router replay: routing with the experts given (e.g. recorded from an
  * earlier pass, or a forced assignment such as the balanced routing of the
  * benchmark setting in section 8, Performance Evaluation), the routing weights

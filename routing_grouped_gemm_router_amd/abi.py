@@ -69,6 +69,9 @@ SIGNATURES = {
                                           _p, _p]),
     "moe_grouped_gemm_fp8_wgrad": (_int, [_p, _p, _p, _p, _p, _i32, _i64, _i64, _i64, _int, _int,
                                           _p, _p]),
+    "moe_route_topk_expert_bias": (_int, [_p, _p, _i64, _i32, _i32, _int, _p, _p, _p, _p, _p,
+                                          _p, _p, _sz, _p]),
+    "moe_expert_bias_update": (_int, [_p, _i32, _f32, _p, _p]),
     "moe_quant_mxfp8_rows": (_int, [_p, _i64, _i64, _p, _p, _p]),
     "moe_permute_quant_mxfp8": (_int, [_p, _i64, _i64, _p, _p, _i32, _i64, _p, _p, _p]),
     "moe_quant_mxfp8_weights": (_int, [_p, _i32, _i64, _i64, _p, _p, _p, _p, _p]),
@@ -175,6 +178,20 @@ def moe_route_topk(logits, k, score, renorm, topk_idx, topk_w, counts, offsets, 
     _call("moe_route_topk", _ptr(logits), T, E, k, score, int(renorm), _ptr(topk_idx),
           _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(dst_row), _ptr(src_token),
           _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def moe_route_topk_expert_bias(logits, sel_bias, k, renorm, topk_idx, topk_w, counts, offsets,
+                               dst_row, src_token, workspace, stream=None):
+    T, E = logits.shape
+    _call("moe_route_topk_expert_bias", _ptr(logits), _ptr(sel_bias), T, E, k, int(renorm),
+          _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(dst_row),
+          _ptr(src_token), _ptr(workspace), workspace.numel() * workspace.element_size(),
+          _stream(stream))
+
+
+def moe_expert_bias_update(counts, rate, sel_bias, stream=None):
+    _call("moe_expert_bias_update", _ptr(counts), counts.numel(), float(rate), _ptr(sel_bias),
+          _stream(stream))
 
 
 def moe_route_replay(logits, topk_idx_in, score, renorm, topk_idx, topk_w, counts, offsets,

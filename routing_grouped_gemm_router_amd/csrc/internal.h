@@ -14,8 +14,11 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 // route.hip
 size_t route_topk_workspace(int64_t T, int E);
 hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int score, int renorm,
-                             int32_t* topk_idx, float* topk_w, int32_t* counts, int64_t* offsets,
-                             int32_t* dst_row, int32_t* src_token, void* ws, hipStream_t s);
+                             const float* sel_bias, int32_t* topk_idx, float* topk_w,
+                             int32_t* counts, int64_t* offsets, int32_t* dst_row,
+                             int32_t* src_token, void* ws, hipStream_t stream);
+hipError_t launch_expert_bias_update(const int32_t* counts, int E, float rate, float* bias,
+                                     hipStream_t stream);
 hipError_t launch_route_replay(const float* logits, const int32_t* idx_in, int64_t T, int E, int k,
                                int score, int renorm, int32_t* topk_idx, float* topk_w,
                                int32_t* counts, int64_t* offsets, int32_t* dst_row,

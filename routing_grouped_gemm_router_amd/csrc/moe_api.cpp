@@ -133,10 +133,43 @@ int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int sco
           "moe_route_topk: workspace needs %zu bytes, got %zu", need, workspace_bytes);
   REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 7u) == 0, MOE_ERR_UNSUPPORTED,
           "moe_route_topk: workspace must be 8-byte aligned");
-  return hip_status(moe::launch_route_topk(logits, T, E, k, score, renorm != 0, topk_idx, topk_w,
-                                           counts, offsets, dst_row, src_token, workspace,
+  return hip_status(moe::launch_route_topk(logits, T, E, k, score, renorm != 0, nullptr, topk_idx,
+                                           topk_w, counts, offsets, dst_row, src_token, workspace,
                                            as_stream(stream)),
                     "moe_route_topk");
+}
+
+int moe_route_topk_expert_bias(const float* logits, const float* sel_bias, int64_t T, int32_t E,
+                               int32_t k, int renorm, int32_t* topk_idx, float* topk_w,
+                               int32_t* counts, int64_t* offsets, int32_t* dst_row,
+                               int32_t* src_token, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  const char* fn = "moe_route_topk_expert_bias";
+  int st = check_route_shape(fn, T, E, k, MOE_SIGMOID);
+  if (st != MOE_OK) return st;
+  REQUIRE(counts && offsets, MOE_ERR_NULL, "%s: counts and offsets are required", fn);
+  REQUIRE(T == 0 || (logits && sel_bias && topk_idx && topk_w && dst_row && src_token),
+          MOE_ERR_NULL, "%s: logits, sel_bias, topk_idx, topk_w, dst_row and src_token are required",
+          fn);
+  const size_t need = moe::route_topk_workspace(T, E);
+  REQUIRE(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE,
+          "%s: workspace needs %zu bytes, got %zu", fn, need, workspace_bytes);
+  REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 7u) == 0, MOE_ERR_UNSUPPORTED,
+          "%s: workspace must be 8-byte aligned", fn);
+  return hip_status(moe::launch_route_topk(logits, T, E, k, MOE_SIGMOID, renorm != 0, sel_bias,
+                                           topk_idx, topk_w, counts, offsets, dst_row, src_token,
+                                           workspace, as_stream(stream)),
+                    fn);
+}
+
+int moe_expert_bias_update(const int32_t* counts, int32_t E, float rate, float* sel_bias,
+                           void* stream) {
+  const char* fn = "moe_expert_bias_update";
+  REQUIRE(E >= 1, MOE_ERR_SHAPE, "%s: E=%d", fn, E);
+  REQUIRE(E <= 1024, MOE_ERR_UNSUPPORTED, "%s: E=%d above 1024", fn, E);
+  REQUIRE(counts && sel_bias, MOE_ERR_NULL, "%s: counts and sel_bias are required", fn);
+  return hip_status(moe::launch_expert_bias_update(counts, E, rate, sel_bias, as_stream(stream)),
+                    fn);
 }
 
 int moe_route_replay(const float* logits, const int32_t* topk_idx_in, int64_t T, int32_t E,

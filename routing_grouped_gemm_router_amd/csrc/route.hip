@@ -20,6 +20,38 @@ namespace moe {
 
 constexpr int ROUTE_TILE = 64;  // tokens per tile = bits of one mask word
 
+// Selection-only expert bias (the auxiliary-loss-free biasing that section 7,
+// Load Balancing, lists): the key of expert e is sigmoid(z) + b[e]; the
+// routing weights stay the unbiased sigmoid scores.  The key decides integer
+// results, so the sigmoid is specified step by step, every step one correctly
+// rounded fp32 operation (contraction into fused multiply-adds is switched
+// off for the function; HIP's __f*_rn helpers are plain operators that the
+// default -ffp-contract=fast would fuse):
+//   x = clamp(-z, -87, 87); n = rint(x * log2e);
+//   r = (x - n * LN2_HI) - n * LN2_LO;  p = Horner of 1/i!, i = 7 .. 0, at r
+//   (each step a multiply, then an add);  sigma = 1 / (1 + ldexp(p, n)).
+// LN2_HI has 15 significant bits, so n * LN2_HI is exact; the clamp keeps
+// exp(x) and sigma normal.
+__device__ __forceinline__ float sigmoid_spec(float z) {
+#pragma clang fp contract(off)
+  constexpr float LOG2E = 1.44269504f, LN2_HI = 0.693145751953125f, LN2_LO = 1.42860677e-06f;
+  constexpr float C[8] = {1.0f, 1.0f, 0.5f, 1.0f / 6.0f, 1.0f / 24.0f, 1.0f / 120.0f,
+                          1.0f / 720.0f, 1.0f / 5040.0f};
+  const float x = fminf(fmaxf(-z, -87.0f), 87.0f);
+  const float n = __builtin_rintf(x * LOG2E);
+  const float hi = n * LN2_HI;
+  const float lo = n * LN2_LO;
+  const float r = (x - hi) - lo;
+  float p = C[7];
+#pragma unroll
+  for (int i = 6; i >= 0; --i) {
+    const float pr = p * r;
+    p = pr + C[i];
+  }
+  const float e = ldexpf(p, static_cast<int>(n));
+  return 1.0f / (1.0f + e);
+}
+
 // Strict order on (key, index): larger key first, then lower index.
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
@@ -28,6 +60,7 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
 template <int EPL>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int64_t T, int E,
                                                    int k, int score, int renorm,
+                                                   const float* __restrict__ sel_bias,
                                                    int32_t* __restrict__ topk_idx,
                                                    float* __restrict__ topk_w,
                                                    unsigned long long* __restrict__ tile_bits) {
@@ -46,6 +79,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     for (int i = 0; i < EPL; ++i) {
       const int e = lane + 64 * i;
       v[i] = e < E ? row[e] : 0.f;
+      if (sel_bias && e < E) v[i] = __fadd_rn(sigmoid_spec(v[i]), sel_bias[e]);
     }
     unsigned taken = 0;  // bit i: element i of this lane already selected
     int my_idx = -1;
@@ -93,6 +127,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
         denom = wave_sum(part);
       }
       w = ex / denom;
+    } else if (sel_bias) {  // sigmoid, biased selection: weights from the logits
+      const float s = active ? sigmoid_spec(row[my_idx]) : 0.f;
+      w = renorm ? s / wave_sum(s) : s;
     } else {  // sigmoid
       const float s = active ? 1.0f / (1.0f + expf(-my_key)) : 0.f;
       w = renorm ? s / wave_sum(s) : s;
@@ -324,8 +361,9 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(const float* __restrict_
 static int epl_for(int E) { return E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : E <= 512 ? 8 : 16; }
 
 hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int score, int renorm,
-                             int32_t* topk_idx, float* topk_w, int32_t* counts, int64_t* offsets,
-                             int32_t* dst_row, int32_t* src_token, void* ws, hipStream_t stream) {
+                             const float* sel_bias, int32_t* topk_idx, float* topk_w,
+                             int32_t* counts, int64_t* offsets, int32_t* dst_row,
+                             int32_t* src_token, void* ws, hipStream_t stream) {
   const int64_t ntiles = (T + ROUTE_TILE - 1) / ROUTE_TILE;
   unsigned long long* tile_bits = static_cast<unsigned long long*>(ws);
   int32_t* tile_base = reinterpret_cast<int32_t*>(tile_bits + ntiles * E);
@@ -334,7 +372,7 @@ hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int s
 #define MOE_TOPK(n)                                                                               \
   case n:                                                                                         \
     topk_kernel<n><<<dim3(static_cast<unsigned>(ntiles)), 256, 0, stream>>>(                      \
-        logits, T, E, k, score, renorm, topk_idx, topk_w, tile_bits);                             \
+        logits, T, E, k, score, renorm, sel_bias, topk_idx, topk_w, tile_bits);                   \
     break;
       MOE_TOPK(1) MOE_TOPK(2) MOE_TOPK(4) MOE_TOPK(8) MOE_TOPK(16)
 #undef MOE_TOPK
@@ -589,6 +627,39 @@ hipError_t launch_route_topk_bwd(const float* logits, const int32_t* topk_idx, c
     MOE_RB(1) MOE_RB(2) MOE_RB(4) MOE_RB(8) MOE_RB(16)
 #undef MOE_RB
   }
+  return hipGetLastError();
+}
+
+}  // namespace moe
+
+namespace moe {
+
+// b[e] += rate * sign(sum(counts) - E * counts[e]): one workgroup; the sum is
+// an exact integer reduction, the update one fp32 addition.
+__global__ __launch_bounds__(1024) void expert_bias_update_kernel(const int32_t* __restrict__ counts,
+                                                                 int E, float rate,
+                                                                 float* __restrict__ bias) {
+  __shared__ long long part[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  long long sum = 0;
+  for (int e = tid; e < E; e += 1024) sum += counts[e];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+  if (lane == 0) part[wave] = sum;
+  __syncthreads();
+  long long total = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) total += part[w];
+  for (int e = tid; e < E; e += 1024) {
+    const long long d = total - static_cast<long long>(E) * counts[e];
+    const float step = d > 0 ? rate : (d < 0 ? -rate : 0.0f);
+    bias[e] = __fadd_rn(bias[e], step);
+  }
+}
+
+hipError_t launch_expert_bias_update(const int32_t* counts, int E, float rate, float* bias,
+                                     hipStream_t stream) {
+  expert_bias_update_kernel<<<1, 1024, 0, stream>>>(counts, E, rate, bias);
   return hipGetLastError();
 }
 

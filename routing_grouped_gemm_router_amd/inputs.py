@@ -27,6 +27,11 @@ all tensors synthetic, N(0, 1) activations and N(0, 1/fan_in) weights):
                      capacity factor 1.25
   small_aux          T=300 d=256 E=8 k=2 f=256 shared 128, sigmoid routing with
                      an auxiliary load-balancing loss (coefficient 0.01)
+  deepseek_v3_expert_bias as deepseek_v3_e256k8 with the selection-only expert
+                     bias (auxiliary-loss-free balancing) instead of the logit
+                     bias: N(0, 0.01^2) initial bias, update rate 1e-3
+  small_expert_bias  T=512 d=256 E=16 k=4 f=256 shared 128, sigmoid scores with
+                     an N(0, 0.05^2) selection bias, update rate 1e-3
 
 Generation: each tensor (and each expert's slice of a weight) is drawn from
 its own torch generator seeded from (seed, stream id), as float32 normals
@@ -59,6 +64,10 @@ class LayerConfig:
     routing: str = "topk"       # topk | balanced (experts given, replayed)
     capacity_factor: float = 0.0  # > 0: each expert keeps ceil(factor*T*k/E) rows
     aux_loss_coeff: float = 0.0   # > 0: auxiliary load-balancing loss
+    # > 0: selection-only expert bias on sigmoid scores (auxiliary-loss-free
+    # balancing), drawn N(0, std^2), moved by the update rate after each route
+    expert_bias_std: float = 0.0
+    expert_bias_rate: float = 0.0
     note: str = field(default="", compare=False)
 
     @property
@@ -90,12 +99,17 @@ CONFIGS = {
                                         capacity_factor=1.0),
     "small_capacity": LayerConfig("small_capacity", T=513, d=128, E=16, k=4, f=128, bias="zipf",
                                   capacity_factor=1.25),
+    "deepseek_v3_expert_bias": LayerConfig("deepseek_v3_expert_bias", T=8192, d=7168, E=256, k=8,
+                                           f=2048, fs=2048, score="sigmoid", expert_bias_std=0.01,
+                                           expert_bias_rate=1e-3),
+    "small_expert_bias": LayerConfig("small_expert_bias", T=512, d=256, E=16, k=4, f=256, fs=128,
+                                     score="sigmoid", expert_bias_std=0.05, expert_bias_rate=1e-3),
     "small_aux": LayerConfig("small_aux", T=300, d=256, E=8, k=2, f=256, fs=128, score="sigmoid",
                              bias="normal", aux_loss_coeff=0.01),
 }
 
 # stream ids: one per tensor; expert weights add the expert index
-_S_X, _S_WR, _S_BIAS, _S_DOUT, _S_SHARED, _S_ROUTE = 1, 2, 3, 4, 5, 6
+_S_X, _S_WR, _S_BIAS, _S_DOUT, _S_SHARED, _S_ROUTE, _S_EBIAS = 1, 2, 3, 4, 5, 6, 8
 _S_W1, _S_W3, _S_W2 = 1 << 20, 2 << 20, 3 << 20
 
 
@@ -171,6 +185,9 @@ def layer_inputs(cfg, seed, device="cpu"):
         inp["ws13"], inp["ws2"] = ws13[0], ws2[0]
     if cfg.routing == "balanced":
         inp["topk_idx_in"] = balanced_experts(cfg.T, cfg.E, cfg.k, seed, device)
+    if cfg.expert_bias_std > 0:
+        inp["expert_bias"] = normal((cfg.E,), cfg.expert_bias_std, seed, _S_EBIAS, device,
+                                    torch.float32)
     return inp
 
 

@@ -87,6 +87,13 @@ class MoELayer:
         # in the storage of dAB, which holds nothing until the backward.
         self.recompute = recompute_act
         self.replay = cfg.routing == "balanced"
+        # selection-only expert bias (auxiliary-loss-free balancing): a copy
+        # that the update after each route moves
+        self.ebias = cfg.expert_bias_std > 0
+        if self.ebias:
+            if cfg.score != "sigmoid" or self.replay:
+                raise ValueError("the expert bias applies to sigmoid top-k routing")
+            self.sel_bias = weights["expert_bias"].detach().clone()
         if self.replay:
             self.topk_idx_in = weights["topk_idx_in"]
             self.route_status = torch.zeros(1, dtype=torch.int32, device=device)
@@ -340,6 +347,11 @@ class MoELayer:
                                      self.topk_idx, self.topk_w, m["counts"], m["offsets"],
                                      m["dst_row"], m["src_token"], self.route_ws,
                                      status=self.route_status)
+            elif self.ebias:
+                abi.moe_route_topk_expert_bias(self.logits, self.sel_bias, c.k, c.renorm,
+                                               self.topk_idx, self.topk_w, m["counts"],
+                                               m["offsets"], m["dst_row"], m["src_token"],
+                                               self.route_ws)
             else:
                 abi.moe_route_topk(self.logits, c.k, self.score, c.renorm, self.topk_idx,
                                    self.topk_w, m["counts"], m["offsets"], m["dst_row"],
@@ -349,6 +361,9 @@ class MoELayer:
                                        self.capacity, self.counts, self.offsets, self.dst_row,
                                        self.src_token)
         self.routed_counts = m["counts"]  # before any dropping
+        if self.ebias and c.expert_bias_rate > 0:  # the next route sees the moved bias
+            with self._span("expert_bias_update"):
+                abi.moe_expert_bias_update(self.routed_counts, c.expert_bias_rate, self.sel_bias)
         if self.aux:
             with self._span("aux_loss"):
                 abi.moe_aux_loss(self.logits, self.routed_counts, c.k, self.score,

@@ -55,13 +55,17 @@ def layer_inputs_without_near_ties(cfg, seed, device="cpu", rel_gap=1e-4, attemp
     token with two of its top k+1 keys (by the oracle) closer than
     rel_gap * (1 + |key|) gets a fresh x row, so the GPU's fp32 router (a
     different summation order) must select the same experts in the same slot
-    order."""
+    order.  With a selection-only expert bias the keys are
+    sigmoid(z) + bias."""
     inp = inputs.layer_inputs(cfg, seed, device)
+    sel = inp.get("expert_bias")
     bias = None if inp["logit_bias"] is None else inp["logit_bias"].cpu().numpy()
     w_r = inp["w_r"].cpu().numpy()
     for attempt in range(attempts):
         x = inp["x"].cpu()
         z = oracle.router_logits(np64(x), w_r, bias)
+        if sel is not None:
+            z = oracle.selection_keys(z, sel.cpu().numpy())
         bad = near_tie_tokens(z, cfg.k, rel_gap)
         if len(bad) == 0:
             return inp

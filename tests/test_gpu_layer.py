@@ -36,6 +36,12 @@ def _run(cfg, seed, recompute_act=False, gate_in_ffn=False):
     shared = (np64(inp["ws13"]), np64(inp["ws2"])) if cfg.fs else None
     bias = None if inp["logit_bias"] is None else inp["logit_bias"].numpy()
     given = inp["topk_idx_in"].numpy() if cfg.routing == "balanced" else None
+    if cfg.expert_bias_std > 0:
+        # the experts chosen on the biased keys; the oracle layer then takes
+        # the routing weights from the unbiased scores, as the route does
+        z = oracle.router_logits(np64(inp["x"]), inp["w_r"].numpy(), bias)
+        given = oracle.route_expert_bias(z, inp["expert_bias"].numpy(), cfg.k,
+                                         cfg.renorm)["topk_idx"]
     fwd = oracle.layer_forward_gated if gate_in_ffn else oracle.layer_forward
     bwd = oracle.layer_backward_gated if gate_in_ffn else oracle.layer_backward
     cap = (oracle.capacity_of(cfg.capacity_factor, cfg.T, cfg.k, cfg.E)
@@ -145,3 +151,17 @@ def test_layer_repeat_is_bitwise_deterministic(gpu):
     assert torch.equal(out1, layer.out)
     for k, v in layer.grads().items():
         assert torch.equal(first[k], v), k
+
+
+def test_layer_expert_bias(gpu):
+    """Selection-only expert bias: the experts of the biased keys, the weights
+    and every gradient of the layer on the unbiased scores, and the bias moved
+    by the update rule (bit-exact) from the step's loads."""
+    cfg = inputs.CONFIGS["small_expert_bias"]
+    layer, c, g = _run(cfg, 0)
+    _check(cfg, layer, c, g)
+    b0 = inputs.layer_inputs(cfg, 0)["expert_bias"].numpy()
+    want = oracle.expert_bias_update(b0, c["route"]["counts"], np.float32(cfg.expert_bias_rate))
+    np.testing.assert_array_equal(layer.sel_bias.cpu().numpy().view(np.int32),
+                                  want.view(np.int32))
+    assert (want != b0).any()

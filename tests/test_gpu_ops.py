@@ -460,3 +460,65 @@ def test_aux_loss(gpu, T, E, k, score):
     assert_close("d_logits", dl, dz, TOL["f32"])
     abi.moe_aux_loss(zz, counts, k, sc, 0.01, d_logits=dl)
     assert_close("d_logits (added twice)", dl, 2 * dz, TOL["f32"])
+
+
+def _route_bufs(T, E, k):
+    return {n: torch.empty(sh, dtype=dt, device=DEV) for n, sh, dt in [
+        ("topk_idx", (T, k), torch.int32), ("topk_w", (T, k), torch.float32),
+        ("counts", (E,), torch.int32), ("offsets", (E + 1,), torch.int64),
+        ("dst_row", (T, k), torch.int32), ("src_token", (T * k,), torch.int32)]}
+
+
+def test_sigmoid_spec_bit_exact(gpu):
+    """The specified sigmoid, read back through the expert-bias route with
+    k = E, no renormalisation and a zero bias: topk_w[t, j] is
+    sigmoid_spec(z[t, topk_idx[t, j]]) -- equal bit for bit to the oracle's
+    on a sweep of [-90, 90], landmarks and random normals."""
+    T, E = 4096, 64
+    rng = np.random.default_rng(11)
+    z = np.concatenate([np.linspace(-90, 90, T * E // 2),
+                        rng.standard_normal(T * E // 2 - 16) * rng.choice([0.01, 1, 10], T * E // 2 - 16),
+                        [0.0, -0.0, 17.0, -17.0, 87.0, -87.0, 88.0, -88.0, 1e-30, -1e-30,
+                         1e-40, 3.4e38, -3.4e38, 0.5, -0.5, 1.0]]).astype(np.float32)
+    z = rng.permutation(z).reshape(T, E)
+    ws = torch.empty(abi.moe_route_topk_workspace_bytes(T, E, E), dtype=torch.uint8, device=DEV)
+    g = _route_bufs(T, E, E)
+    abi.moe_route_topk_expert_bias(torch.from_numpy(z).to(DEV), torch.zeros(E, device=DEV), E,
+                                   False, g["topk_idx"], g["topk_w"], g["counts"], g["offsets"],
+                                   g["dst_row"], g["src_token"], ws)
+    idx = g["topk_idx"].cpu().numpy()
+    want = np.take_along_axis(oracle.sigmoid_spec(z), idx.astype(np.int64), axis=1)
+    got = g["topk_w"].cpu().numpy()
+    np.testing.assert_array_equal(got.view(np.int32), want.view(np.int32))
+    r = oracle.route_expert_bias(z, np.zeros(E, np.float32), E, renorm=False)
+    np.testing.assert_array_equal(idx, r["topk_idx"])
+
+
+@pytest.mark.parametrize("T,E,k,std,renorm", [(3000, 256, 8, 0.05, True), (1000, 16, 4, 0.3, False),
+                                               (257, 64, 6, 0.0, True), (0, 8, 2, 0.1, True)])
+def test_route_expert_bias_bit_exact(gpu, T, E, k, std, renorm):
+    print(f"expert-bias route T={T} E={E} k={k} std={std}", flush=True)
+    z = _keys(T, E, 99 + E, "normal") if T else np.zeros((0, E), np.float32)
+    b = (np.random.default_rng(E).standard_normal(E) * std).astype(np.float32)
+    r = oracle.route_expert_bias(z, b, k, renorm)
+    ws = torch.empty(abi.moe_route_topk_workspace_bytes(T, E, k), dtype=torch.uint8, device=DEV)
+    g = _route_bufs(T, E, k)
+    abi.moe_route_topk_expert_bias(torch.from_numpy(z).to(DEV), torch.from_numpy(b).to(DEV), k,
+                                   renorm, g["topk_idx"], g["topk_w"], g["counts"], g["offsets"],
+                                   g["dst_row"], g["src_token"], ws)
+    for key in ("topk_idx", "counts", "offsets", "dst_row", "src_token"):
+        np.testing.assert_array_equal(g[key].cpu().numpy(), r[key], err_msg=key)
+    if T:
+        assert_close("topk_w", g["topk_w"], r["topk_w"], TOL["f32"])
+
+
+@pytest.mark.parametrize("E", [256, 1000, 1])
+def test_expert_bias_update_bit_exact(gpu, E):
+    rng = np.random.default_rng(E)
+    counts = rng.integers(0, 5000, E).astype(np.int32)
+    counts[: E // 3] = int(counts.sum() // E) if E > 2 else counts[: E // 3]
+    b = (rng.standard_normal(E) * 0.01).astype(np.float32)
+    gb = torch.from_numpy(b).to(DEV)
+    abi.moe_expert_bias_update(torch.from_numpy(counts).to(DEV), 1e-3, gb)
+    want = oracle.expert_bias_update(b, counts, np.float32(1e-3))
+    np.testing.assert_array_equal(gb.cpu().numpy().view(np.int32), want.view(np.int32))
