@@ -35,7 +35,7 @@ SIGMOID = "sigmoid"
 __all__ = [
     "SOFTMAX", "SIGMOID", "f64", "router_logits", "select_topk", "gates", "dispatch_map",
     "route", "route_replay", "canonical_experts", "capacity_of", "apply_capacity", "aux_loss",
-    "sigmoid_spec", "selection_keys", "route_expert_bias", "expert_bias_update",
+    "sigmoid_spec", "selection_keys", "route_expert_bias", "expert_bias_update", "pad_to_max",
     "route_bwd",
     "router_logits_bwd", "permute", "permute_bwd",
     "grouped_gemm_fwd", "grouped_gemm_dgrad", "grouped_gemm_wgrad", "sigmoid", "silu",
@@ -303,6 +303,33 @@ def apply_capacity(r, capacity):
     out = dict(r)
     out.update(counts=kept, offsets=offsets, dst_row=dst_row, src_token=src_token,
                capacity=capacity)
+    return out
+
+
+def pad_to_max(r, capacity):
+    """Pad-to-max (section 7, Load Balancing: variable expert counts made
+    into static shapes): every expert's segment gets the same size C =
+    ``capacity``, expert e owning rows e*C .. e*C + C - 1; its kept pairs (the
+    first C in token order, as ``apply_capacity``) fill the segment's first
+    rows in token order and the rest of the segment is padding (src_token -1,
+    zero rows downstream).  Offsets are the static e*C."""
+    kept = apply_capacity(r, capacity)
+    E = len(kept["counts"])
+    offsets = np.arange(E + 1, dtype=np.int64) * capacity
+    dst_row = np.full_like(kept["dst_row"], -1)
+    src_token = np.full(E * capacity, -1, dtype=np.int32)
+    T, k = dst_row.shape
+    for t in range(T):
+        for j in range(k):
+            row = kept["dst_row"][t, j]
+            if row < 0:
+                continue
+            e = int(kept["topk_idx"][t, j])
+            rank = row - kept["offsets"][e]
+            dst_row[t, j] = e * capacity + rank
+            src_token[e * capacity + rank] = t
+    out = dict(kept)
+    out.update(offsets=offsets, dst_row=dst_row, src_token=src_token, padded_to=capacity)
     return out
 
 

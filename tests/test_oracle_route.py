@@ -335,3 +335,38 @@ def test_expert_bias_update_by_hand():
     assert b[0] == np.float32(0.1)                                           # at the mean
     b = oracle.expert_bias_update(np.float32([1.0, 1.0]), [2, 1], 1e-8)
     assert b[0] == np.float32(1.0 - 1e-8) and b[1] == np.float32(1.0 + 1e-8)  # fp32 add
+
+
+# ---- pad-to-max ------------------------------------------------------------
+
+def test_pad_to_max_by_hand():
+    """Experts 0 and 1, C = 2: expert 0 gets tokens 0, 2, 3 (keeps 0 and 2),
+    expert 1 token 1; rows [0, 2 | 1, pad]."""
+    z = np.float32([[1, 0], [0, 1], [1, 0], [1, 0]])
+    r = oracle.pad_to_max(oracle.route(z, 1, oracle.SOFTMAX, True), 2)
+    np.testing.assert_array_equal(r["offsets"], [0, 2, 4])
+    np.testing.assert_array_equal(r["counts"], [2, 1])
+    np.testing.assert_array_equal(r["dst_row"], [[0], [2], [1], [-1]])
+    np.testing.assert_array_equal(r["src_token"], [0, 2, 1, -1])
+
+
+@pytest.mark.parametrize("C", [1, 7, 40, 500])
+def test_pad_to_max_is_capacity_in_a_static_layout(C):
+    rng = np.random.default_rng(C)
+    T, E, k = 300, 9, 3
+    z = (rng.standard_normal((T, E)) + np.linspace(0, 2, E)).astype(np.float32)
+    r = oracle.route(z, k, oracle.SOFTMAX, True)
+    p = oracle.pad_to_max(r, C)
+    cap = oracle.apply_capacity(r, C)
+    np.testing.assert_array_equal(p["offsets"], np.arange(E + 1) * C)
+    np.testing.assert_array_equal(p["counts"], np.minimum(r["counts"], C))
+    # the same kept pairs; compacting the padded rows gives the capacity layout
+    np.testing.assert_array_equal(p["dst_row"] >= 0, cap["dst_row"] >= 0)
+    np.testing.assert_array_equal(p["src_token"][p["src_token"] >= 0], cap["src_token"])
+    for t in range(T):
+        for j in range(k):
+            row = p["dst_row"][t, j]
+            if row >= 0:
+                e = r["topk_idx"][t, j]
+                assert e * C <= row < e * C + p["counts"][e] and p["src_token"][row] == t
+    assert (p["src_token"] < 0).sum() == E * C - p["counts"].sum()
