@@ -197,6 +197,32 @@ int moe_apply_capacity(const int32_t* topk_idx, const int32_t* counts, const int
                        int32_t* counts_out, int64_t* offsets_out, int32_t* dst_row_out,
                        int32_t* src_token_out, void* stream);
 
+/* Pad-to-max (section 7, Load Balancing: variable expert counts turned into
+ * static shapes): from a dropless dispatch map (moe_route_topk,
+ * moe_route_replay, moe_route_topk_expert_bias), a layout in which every
+ * expert owns `capacity` rows at e * capacity.  A pair whose rank in its
+ * expert's token order is below the capacity keeps that rank as its row
+ * offset; the others are dropped (the pairs capacity-limited dropping keeps).
+ *   counts_out [E]      int32: min(counts, capacity)
+ *   offsets_out [E+1]   int64: e * capacity (static)
+ *   dst_row_out [T, k]  int32: padded row of each kept pair, -1 if dropped
+ *   src_token_out [E * capacity] int32: token of each row, -1 on padding
+ * Padding rows carry no pair: permute writes nothing there and combine never
+ * reads them; moe_zero_unmapped_rows clears them in the buffers the grouped
+ * GEMMs read (the permuted activations and dY), so that they stay zero
+ * through every GEMM.  Outputs must not alias the inputs.  E * capacity <
+ * 2^31. */
+int moe_pad_to_max(const int32_t* topk_idx, const int32_t* counts, const int64_t* offsets,
+                   const int32_t* dst_row, const int32_t* src_token, int64_t T, int32_t E,
+                   int32_t k, int64_t capacity, int32_t* counts_out, int64_t* offsets_out,
+                   int32_t* dst_row_out, int32_t* src_token_out, void* stream);
+
+/* Writes zeros to every row r < M of buf [M, d] (`dtype`) with
+ * src_token[r] < 0 -- the padding rows of a pad-to-max layout.  Rows of d
+ * elements must be a multiple of 16 bytes. */
+int moe_zero_unmapped_rows(void* buf, int dtype, const int32_t* src_token, int64_t M, int64_t d,
+                           void* stream);
+
 /* Gradient of the routing weights with respect to the keys (the selection
  * itself carries none).  With g = sum_j w_j dw_j over a token's chosen slots:
  *   softmax, renorm   : d_logits[e_j] = w_j (dw_j - g), 0 elsewhere
@@ -214,18 +240,23 @@ int moe_route_topk_bwd(const float* logits, const int32_t* topk_idx, const float
 
 /* Permute tokens into expert-contiguous rows (section 2, Dispatch):
  *   x_perm[dst_row[t, j]] = x[t]     for all t < T, j < k
- * x [T, d] and x_perm [T*k, d] of `dtype`; each token row is read once.
+ * x [T, d] and x_perm [n_rows, d] of `dtype`; each token row is read once.
+ * n_rows: rows of the permuted buffer, T*k for the dropless layout (also
+ * after capacity dropping), E*capacity for pad-to-max; dst_row entries < 0
+ * (dropped pairs) or >= n_rows are skipped, here and in the three calls
+ * below that take n_rows.
  * Limits: d % 8 == 0 (bf16) or d % 4 == 0 (fp32). */
 int moe_permute(const void* x, int dtype, const int32_t* dst_row, int64_t T, int64_t d, int32_t k,
-                void* x_perm, void* stream);
+                int64_t n_rows, void* x_perm, void* stream);
 
 /* Adjoint of moe_permute plus optional addends (fp32 accumulation, one
  * rounding to `dtype`):
  *   dx[t] = sum_j dx_perm[dst_row[t, j]] + addend[t] + addend_f32[t]
- * dx_perm [T*k, d], dx [T, d], addend [T, d] of `dtype` or NULL,
+ * dx_perm [n_rows, d], dx [T, d], addend [T, d] of `dtype` or NULL,
  * addend_f32 [T, d] fp32 or NULL. */
 int moe_permute_bwd(const void* dx_perm, int dtype, const int32_t* dst_row, int64_t T, int64_t d,
-                    int32_t k, const void* addend, const float* addend_f32, void* dx, void* stream);
+                    int32_t k, int64_t n_rows, const void* addend, const float* addend_f32,
+                    void* dx, void* stream);
 
 /* -------------------------------------------------------------- Compute -- */
 
@@ -460,12 +491,12 @@ int moe_gate_grad(const float* gate_partials, int64_t P, const int32_t* dst_row,
  * weighted by the routing weights, plus an optional shared expert's output):
  *   out[t] = sum_j topk_w[t, j] * y_perm[dst_row[t, j]] + shared_y[t]
  * fp32 accumulation in slot order, one rounding to `dtype`.
- * y_perm [T*k, d], shared_y [T, d] or NULL, out [T, d], all `dtype`;
+ * y_perm [n_rows, d], shared_y [T, d] or NULL, out [T, d], all `dtype`;
  * topk_w [T, k] fp32, or NULL for an unweighted sum (the routing weights
  * already applied inside the experts, moe_grouped_gemm_gated_fwd). */
 int moe_unpermute_combine(const void* y_perm, int dtype, const float* topk_w,
                           const int32_t* dst_row, const void* shared_y, int64_t T, int64_t d,
-                          int32_t k, void* out, void* stream);
+                          int32_t k, int64_t n_rows, void* out, void* stream);
 
 /* Backward of moe_unpermute_combine:
  *   dy_perm[dst_row[t, j]] = topk_w[t, j] * dout[t]
@@ -473,7 +504,7 @@ int moe_unpermute_combine(const void* y_perm, int dtype, const float* topk_w,
  * (the shared expert's output gradient is dout itself). */
 int moe_unpermute_combine_bwd(const void* dout, const void* y_perm, int dtype, const float* topk_w,
                               const int32_t* dst_row, int64_t T, int64_t d, int32_t k,
-                              void* dy_perm, float* d_topk_w, void* stream);
+                              int64_t n_rows, void* dy_perm, float* d_topk_w, void* stream);
 
 #ifdef __cplusplus
 }

@@ -47,8 +47,8 @@ SIGNATURES = {
     "moe_grouped_gemm_gated_dgrad": (_int, [_p, _p, _p, _i32, _i64, _i64, _i64, _int, _p, _p, _p,
                                             _p, _p]),
     "moe_gate_grad": (_int, [_p, _i64, _p, _i64, _i32, _p, _p]),
-    "moe_permute": (_int, [_p, _int, _p, _i64, _i64, _i32, _p, _p]),
-    "moe_permute_bwd": (_int, [_p, _int, _p, _i64, _i64, _i32, _p, _p, _p, _p]),
+    "moe_permute": (_int, [_p, _int, _p, _i64, _i64, _i32, _i64, _p, _p]),
+    "moe_permute_bwd": (_int, [_p, _int, _p, _i64, _i64, _i32, _i64, _p, _p, _p, _p]),
     "moe_grouped_gemm_fwd": (_int, [_p, _p, _p, _i32, _i64, _i64, _i64, _int, _int, _p, _p, _p]),
     "moe_grouped_gemm_dgrad": (_int, [_p, _p, _p, _i32, _i64, _i64, _i64, _int, _int, _p, _p,
                                       _p]),
@@ -56,8 +56,9 @@ SIGNATURES = {
                                       _p]),
     "moe_swiglu": (_int, [_p, _int, _i64, _i64, _p, _p]),
     "moe_swiglu_bwd": (_int, [_p, _p, _int, _i64, _i64, _p, _p]),
-    "moe_unpermute_combine": (_int, [_p, _int, _p, _p, _p, _i64, _i64, _i32, _p, _p]),
-    "moe_unpermute_combine_bwd": (_int, [_p, _p, _int, _p, _p, _i64, _i64, _i32, _p, _p, _p]),
+    "moe_unpermute_combine": (_int, [_p, _int, _p, _p, _p, _i64, _i64, _i32, _i64, _p, _p]),
+    "moe_unpermute_combine_bwd": (_int, [_p, _p, _int, _p, _p, _i64, _i64, _i32, _i64, _p, _p,
+                                         _p]),
     "moe_quant_fp8_rows": (_int, [_p, _i64, _i64, _p, _p, _p]),
     "moe_quant_fp8_weights": (_int, [_p, _i32, _i64, _i64, _p, _p, _p, _p, _p]),
     "moe_padded_rows_bound": (_i64, [_i64, _i32, _i32]),
@@ -72,6 +73,8 @@ SIGNATURES = {
     "moe_route_topk_expert_bias": (_int, [_p, _p, _i64, _i32, _i32, _int, _p, _p, _p, _p, _p,
                                           _p, _p, _sz, _p]),
     "moe_expert_bias_update": (_int, [_p, _i32, _f32, _p, _p]),
+    "moe_pad_to_max": (_int, [_p, _p, _p, _p, _p, _i64, _i32, _i32, _i64, _p, _p, _p, _p, _p]),
+    "moe_zero_unmapped_rows": (_int, [_p, _int, _p, _i64, _i64, _p]),
     "moe_quant_mxfp8_rows": (_int, [_p, _i64, _i64, _p, _p, _p]),
     "moe_permute_quant_mxfp8": (_int, [_p, _i64, _i64, _p, _p, _i32, _i64, _p, _p, _p]),
     "moe_quant_mxfp8_weights": (_int, [_p, _i32, _i64, _i64, _p, _p, _p, _p, _p]),
@@ -189,6 +192,20 @@ def moe_route_topk_expert_bias(logits, sel_bias, k, renorm, topk_idx, topk_w, co
           _stream(stream))
 
 
+def moe_pad_to_max(topk_idx, counts, offsets, dst_row, src_token, capacity, counts_out,
+                   offsets_out, dst_row_out, src_token_out, stream=None):
+    T, k = topk_idx.shape
+    _call("moe_pad_to_max", _ptr(topk_idx), _ptr(counts), _ptr(offsets), _ptr(dst_row),
+          _ptr(src_token), T, counts.numel(), k, int(capacity), _ptr(counts_out),
+          _ptr(offsets_out), _ptr(dst_row_out), _ptr(src_token_out), _stream(stream))
+
+
+def moe_zero_unmapped_rows(buf, src_token, stream=None):
+    M, d = buf.shape
+    _call("moe_zero_unmapped_rows", _ptr(buf), dtype_code(buf), _ptr(src_token), M, d,
+          _stream(stream))
+
+
 def moe_expert_bias_update(counts, rate, sel_bias, stream=None):
     _call("moe_expert_bias_update", _ptr(counts), counts.numel(), float(rate), _ptr(sel_bias),
           _stream(stream))
@@ -256,13 +273,14 @@ def moe_route_topk_bwd(logits, topk_idx, topk_w, d_topk_w, score, renorm, d_logi
 def moe_permute(x, dst_row, x_perm, stream=None):
     T, d = x.shape
     _call("moe_permute", _ptr(x), dtype_code(x), _ptr(dst_row), T, d, dst_row.shape[1],
-          _ptr(x_perm), _stream(stream))
+          x_perm.shape[0], _ptr(x_perm), _stream(stream))
 
 
 def moe_permute_bwd(dx_perm, dst_row, addend, addend_f32, dx, stream=None):
     T, d = dx.shape
     _call("moe_permute_bwd", _ptr(dx_perm), dtype_code(dx), _ptr(dst_row), T, d,
-          dst_row.shape[1], _ptr(addend), _ptr(addend_f32), _ptr(dx), _stream(stream))
+          dst_row.shape[1], dx_perm.shape[0], _ptr(addend), _ptr(addend_f32), _ptr(dx),
+          _stream(stream))
 
 
 def moe_grouped_gemm_fwd(A, B, offsets, C, H=None, epilogue=EPI_NONE, stream=None):
@@ -296,13 +314,14 @@ def moe_swiglu_bwd(dh, ab, dab, stream=None):
 def moe_unpermute_combine(y_perm, topk_w, dst_row, shared_y, out, stream=None):
     T, d = out.shape
     _call("moe_unpermute_combine", _ptr(y_perm), dtype_code(y_perm), _ptr(topk_w), _ptr(dst_row),
-          _ptr(shared_y), T, d, dst_row.shape[1], _ptr(out), _stream(stream))
+          _ptr(shared_y), T, d, dst_row.shape[1], y_perm.shape[0], _ptr(out), _stream(stream))
 
 
 def moe_unpermute_combine_bwd(dout, y_perm, topk_w, dst_row, dy_perm, d_topk_w, stream=None):
     T, d = dout.shape
     _call("moe_unpermute_combine_bwd", _ptr(dout), _ptr(y_perm), dtype_code(dout), _ptr(topk_w),
-          _ptr(dst_row), T, d, dst_row.shape[1], _ptr(dy_perm), _ptr(d_topk_w), _stream(stream))
+          _ptr(dst_row), T, d, dst_row.shape[1], y_perm.shape[0], _ptr(dy_perm), _ptr(d_topk_w),
+          _stream(stream))
 
 
 # ---- fp8 (E4M3 codes as torch.uint8 tensors, fp32 scales)

@@ -17,6 +17,13 @@ hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int s
                              const float* sel_bias, int32_t* topk_idx, float* topk_w,
                              int32_t* counts, int64_t* offsets, int32_t* dst_row,
                              int32_t* src_token, void* ws, hipStream_t stream);
+hipError_t launch_pad_to_max(const int32_t* topk_idx, const int32_t* counts,
+                             const int64_t* offsets, const int32_t* dst_row,
+                             const int32_t* src_token, int64_t T, int E, int k, int64_t C,
+                             int32_t* counts_out, int64_t* offsets_out, int32_t* dst_row_out,
+                             int32_t* src_token_out, hipStream_t stream);
+hipError_t launch_zero_unmapped_rows(void* buf, int64_t row_bytes, const int32_t* src_token,
+                                     int64_t M, hipStream_t s);
 hipError_t launch_expert_bias_update(const int32_t* counts, int E, float rate, float* bias,
                                      hipStream_t stream);
 hipError_t launch_route_replay(const float* logits, const int32_t* idx_in, int64_t T, int E, int k,
@@ -36,17 +43,19 @@ hipError_t launch_route_topk_bwd(const float* logits, const int32_t* topk_idx, c
                                  int renorm, float* d_logits, hipStream_t s);
 
 // permute.hip
+// nrows: rows of the permuted buffer (T * k dropless, E * capacity padded);
+// dst_row entries outside [0, nrows) are skipped
 hipError_t launch_permute(const void* x, int dtype, const int32_t* dst_row, int64_t T, int64_t d,
-                          int k, void* xp, hipStream_t s);
+                          int k, int64_t nrows, void* xp, hipStream_t s);
 hipError_t launch_permute_bwd(const void* dxp, int dtype, const int32_t* dst_row, int64_t T,
-                              int64_t d, int k, const void* addend, const float* addend_f32,
-                              void* dx, hipStream_t s);
+                              int64_t d, int k, int64_t nrows, const void* addend,
+                              const float* addend_f32, void* dx, hipStream_t s);
 hipError_t launch_combine(const void* y, int dtype, const float* topk_w, const int32_t* dst_row,
-                          const void* shared, int64_t T, int64_t d, int k, void* out,
-                          hipStream_t s);
+                          const void* shared, int64_t T, int64_t d, int k, int64_t nrows,
+                          void* out, hipStream_t s);
 hipError_t launch_combine_bwd(const void* dout, const void* y, int dtype, const float* topk_w,
-                              const int32_t* dst_row, int64_t T, int64_t d, int k, void* dy,
-                              float* d_w, hipStream_t s);
+                              const int32_t* dst_row, int64_t T, int64_t d, int k, int64_t nrows,
+                              void* dy, float* d_w, hipStream_t s);
 hipError_t launch_swiglu(const void* ab, int dtype, int64_t M, int64_t f, void* h, hipStream_t s);
 hipError_t launch_swiglu_bwd(const void* dh, const void* ab, int dtype, int64_t M, int64_t f,
                              void* dab, hipStream_t s);

@@ -162,6 +162,42 @@ int moe_route_topk_expert_bias(const float* logits, const float* sel_bias, int64
                     fn);
 }
 
+int moe_pad_to_max(const int32_t* topk_idx, const int32_t* counts, const int64_t* offsets,
+                   const int32_t* dst_row, const int32_t* src_token, int64_t T, int32_t E,
+                   int32_t k, int64_t capacity, int32_t* counts_out, int64_t* offsets_out,
+                   int32_t* dst_row_out, int32_t* src_token_out, void* stream) {
+  const char* fn = "moe_pad_to_max";
+  REQUIRE(T >= 0 && E >= 1 && k >= 1 && k <= E && capacity >= 1, MOE_ERR_SHAPE,
+          "%s: T=%lld E=%d k=%d capacity=%lld", fn, static_cast<long long>(T), E, k,
+          static_cast<long long>(capacity));
+  REQUIRE(E <= 1024, MOE_ERR_UNSUPPORTED, "%s: E=%d above 1024", fn, E);
+  REQUIRE(static_cast<int64_t>(E) * capacity < (int64_t(1) << 31), MOE_ERR_UNSUPPORTED,
+          "%s: E * capacity must be below 2^31", fn);
+  REQUIRE(counts && offsets && counts_out && offsets_out && src_token_out, MOE_ERR_NULL,
+          "%s: counts, offsets and the outputs are required", fn);
+  REQUIRE(T == 0 || (topk_idx && dst_row && src_token && dst_row_out), MOE_ERR_NULL,
+          "%s: topk_idx, dst_row, src_token and dst_row_out are required", fn);
+  return hip_status(moe::launch_pad_to_max(topk_idx, counts, offsets, dst_row, src_token, T, E, k,
+                                           capacity, counts_out, offsets_out, dst_row_out,
+                                           src_token_out, as_stream(stream)),
+                    fn);
+}
+
+int moe_zero_unmapped_rows(void* buf, int dtype, const int32_t* src_token, int64_t M, int64_t d,
+                           void* stream) {
+  const char* fn = "moe_zero_unmapped_rows";
+  REQUIRE(M >= 0 && d >= 1, MOE_ERR_SHAPE, "%s: M=%lld d=%lld", fn, static_cast<long long>(M),
+          static_cast<long long>(d));
+  REQUIRE(dtype == MOE_F32 || dtype == MOE_BF16, MOE_ERR_DTYPE, "%s: dtype %d", fn, dtype);
+  const int64_t row_bytes = d * (dtype == MOE_F32 ? 4 : 2);
+  REQUIRE(row_bytes % 16 == 0, MOE_ERR_UNSUPPORTED, "%s: rows must be multiples of 16 bytes", fn);
+  if (M == 0) return ok();
+  REQUIRE(buf && src_token, MOE_ERR_NULL, "%s: buf and src_token are required", fn);
+  REQUIRE(aligned16(buf), MOE_ERR_UNSUPPORTED, "%s: buf must be 16-byte aligned", fn);
+  return hip_status(moe::launch_zero_unmapped_rows(buf, row_bytes, src_token, M, as_stream(stream)),
+                    fn);
+}
+
 int moe_expert_bias_update(const int32_t* counts, int32_t E, float rate, float* sel_bias,
                            void* stream) {
   const char* fn = "moe_expert_bias_update";
@@ -253,25 +289,29 @@ int moe_route_topk_bwd(const float* logits, const int32_t* topk_idx, const float
 }
 
 int moe_permute(const void* x, int dtype, const int32_t* dst_row, int64_t T, int64_t d, int32_t k,
-                void* x_perm, void* stream) {
+                int64_t n_rows, void* x_perm, void* stream) {
   REQUIRE(valid_dtype(dtype), MOE_ERR_DTYPE, "moe_permute: bad dtype %d", dtype);
-  REQUIRE(T >= 0 && d >= 1 && k >= 1, MOE_ERR_SHAPE, "moe_permute: T=%lld d=%lld k=%d",
-          static_cast<long long>(T), static_cast<long long>(d), k);
+  REQUIRE(T >= 0 && d >= 1 && k >= 1 && n_rows >= 0, MOE_ERR_SHAPE,
+          "moe_permute: T=%lld d=%lld k=%d n_rows=%lld", static_cast<long long>(T),
+          static_cast<long long>(d), k, static_cast<long long>(n_rows));
   int st = check_row_vectors(dtype, d, "moe_permute");
   if (st != MOE_OK) return st;
   if (T == 0) return ok();
   REQUIRE(x && dst_row && x_perm, MOE_ERR_NULL, "moe_permute: x, dst_row and x_perm are required");
   REQUIRE(aligned16(x) && aligned16(x_perm), MOE_ERR_UNSUPPORTED,
           "moe_permute: x and x_perm must be 16-byte aligned");
-  return hip_status(moe::launch_permute(x, dtype, dst_row, T, d, k, x_perm, as_stream(stream)),
-                    "moe_permute");
+  return hip_status(
+      moe::launch_permute(x, dtype, dst_row, T, d, k, n_rows, x_perm, as_stream(stream)),
+      "moe_permute");
 }
 
 int moe_permute_bwd(const void* dx_perm, int dtype, const int32_t* dst_row, int64_t T, int64_t d,
-                    int32_t k, const void* addend, const float* addend_f32, void* dx, void* stream) {
+                    int32_t k, int64_t n_rows, const void* addend, const float* addend_f32,
+                    void* dx, void* stream) {
   REQUIRE(valid_dtype(dtype), MOE_ERR_DTYPE, "moe_permute_bwd: bad dtype %d", dtype);
-  REQUIRE(T >= 0 && d >= 1 && k >= 1, MOE_ERR_SHAPE, "moe_permute_bwd: T=%lld d=%lld k=%d",
-          static_cast<long long>(T), static_cast<long long>(d), k);
+  REQUIRE(T >= 0 && d >= 1 && k >= 1 && n_rows >= 0, MOE_ERR_SHAPE,
+          "moe_permute_bwd: T=%lld d=%lld k=%d n_rows=%lld", static_cast<long long>(T),
+          static_cast<long long>(d), k, static_cast<long long>(n_rows));
   int st = check_row_vectors(dtype, d, "moe_permute_bwd");
   if (st != MOE_OK) return st;
   if (T == 0) return ok();
@@ -279,8 +319,8 @@ int moe_permute_bwd(const void* dx_perm, int dtype, const int32_t* dst_row, int6
           "moe_permute_bwd: dx_perm, dst_row and dx are required");
   REQUIRE(aligned16(dx_perm) && aligned16(dx) && aligned16(addend) && aligned16(addend_f32),
           MOE_ERR_UNSUPPORTED, "moe_permute_bwd: tensors must be 16-byte aligned");
-  return hip_status(moe::launch_permute_bwd(dx_perm, dtype, dst_row, T, d, k, addend, addend_f32,
-                                            dx, as_stream(stream)),
+  return hip_status(moe::launch_permute_bwd(dx_perm, dtype, dst_row, T, d, k, n_rows, addend,
+                                            addend_f32, dx, as_stream(stream)),
                     "moe_permute_bwd");
 }
 
@@ -415,10 +455,11 @@ int moe_swiglu_bwd(const void* dh, const void* ab, int dtype, int64_t M, int64_t
 
 int moe_unpermute_combine(const void* y_perm, int dtype, const float* topk_w,
                           const int32_t* dst_row, const void* shared_y, int64_t T, int64_t d,
-                          int32_t k, void* out, void* stream) {
+                          int32_t k, int64_t n_rows, void* out, void* stream) {
   REQUIRE(valid_dtype(dtype), MOE_ERR_DTYPE, "moe_unpermute_combine: bad dtype %d", dtype);
-  REQUIRE(T >= 0 && d >= 1 && k >= 1, MOE_ERR_SHAPE, "moe_unpermute_combine: T=%lld d=%lld k=%d",
-          static_cast<long long>(T), static_cast<long long>(d), k);
+  REQUIRE(T >= 0 && d >= 1 && k >= 1 && n_rows >= 0, MOE_ERR_SHAPE,
+          "moe_unpermute_combine: T=%lld d=%lld k=%d n_rows=%lld", static_cast<long long>(T),
+          static_cast<long long>(d), k, static_cast<long long>(n_rows));
   int st = check_row_vectors(dtype, d, "moe_unpermute_combine");
   if (st != MOE_OK) return st;
   if (T == 0) return ok();
@@ -426,8 +467,8 @@ int moe_unpermute_combine(const void* y_perm, int dtype, const float* topk_w,
           "moe_unpermute_combine: y_perm, dst_row and out are required");
   REQUIRE(aligned16(y_perm) && aligned16(out) && aligned16(shared_y), MOE_ERR_UNSUPPORTED,
           "moe_unpermute_combine: 16-byte alignment needed");
-  return hip_status(moe::launch_combine(y_perm, dtype, topk_w, dst_row, shared_y, T, d, k, out,
-                                        as_stream(stream)),
+  return hip_status(moe::launch_combine(y_perm, dtype, topk_w, dst_row, shared_y, T, d, k, n_rows,
+                                        out, as_stream(stream)),
                     "moe_unpermute_combine");
 }
 
@@ -456,11 +497,11 @@ int moe_gate_grad(const float* gate_partials, int64_t P, const int32_t* dst_row,
 
 int moe_unpermute_combine_bwd(const void* dout, const void* y_perm, int dtype, const float* topk_w,
                               const int32_t* dst_row, int64_t T, int64_t d, int32_t k,
-                              void* dy_perm, float* d_topk_w, void* stream) {
+                              int64_t n_rows, void* dy_perm, float* d_topk_w, void* stream) {
   REQUIRE(valid_dtype(dtype), MOE_ERR_DTYPE, "moe_unpermute_combine_bwd: bad dtype %d", dtype);
-  REQUIRE(T >= 0 && d >= 1 && k >= 1, MOE_ERR_SHAPE,
-          "moe_unpermute_combine_bwd: T=%lld d=%lld k=%d", static_cast<long long>(T),
-          static_cast<long long>(d), k);
+  REQUIRE(T >= 0 && d >= 1 && k >= 1 && n_rows >= 0, MOE_ERR_SHAPE,
+          "moe_unpermute_combine_bwd: T=%lld d=%lld k=%d n_rows=%lld", static_cast<long long>(T),
+          static_cast<long long>(d), k, static_cast<long long>(n_rows));
   REQUIRE(k <= 64, MOE_ERR_UNSUPPORTED, "moe_unpermute_combine_bwd: k=%d above 64", k);
   int st = check_row_vectors(dtype, d, "moe_unpermute_combine_bwd");
   if (st != MOE_OK) return st;
@@ -469,8 +510,8 @@ int moe_unpermute_combine_bwd(const void* dout, const void* y_perm, int dtype, c
           "moe_unpermute_combine_bwd: all pointers are required");
   REQUIRE(aligned16(dout) && aligned16(y_perm) && aligned16(dy_perm), MOE_ERR_UNSUPPORTED,
           "moe_unpermute_combine_bwd: 16-byte alignment needed");
-  return hip_status(moe::launch_combine_bwd(dout, y_perm, dtype, topk_w, dst_row, T, d, k, dy_perm,
-                                            d_topk_w, as_stream(stream)),
+  return hip_status(moe::launch_combine_bwd(dout, y_perm, dtype, topk_w, dst_row, T, d, k, n_rows,
+                                            dy_perm, d_topk_w, as_stream(stream)),
                     "moe_unpermute_combine_bwd");
 }
 

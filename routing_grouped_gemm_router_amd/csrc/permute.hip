@@ -57,11 +57,11 @@ __device__ __forceinline__ int64_t wave_token(int per_block) {
 template <typename T>
 __global__ __launch_bounds__(256) void permute_kernel(const T* __restrict__ x,
                                                       const int32_t* __restrict__ dst_row, int64_t T_,
-                                                      int64_t d, int k, T* __restrict__ xp) {
+                                                      int64_t d, int k, int64_t nrows,
+                                                      T* __restrict__ xp) {
   const int64_t t = wave_token(4);
   if (t >= T_) return;
   const int lane = threadIdx.x & 63;
-  const int64_t nrows = T_ * k;
   const int64_t nvec = d / Vec<T>::N;
   const uint4* src = reinterpret_cast<const uint4*>(x + t * d);
   for (int64_t v = lane; v < nvec; v += 64) {
@@ -78,6 +78,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void permute_bwd_kernel(const T* __restrict__ dxp,
                                                           const int32_t* __restrict__ dst_row,
                                                           int64_t T_, int64_t d, int k,
+                                                          int64_t nrows,
                                                           const T* __restrict__ addend,
                                                           const float* __restrict__ addend_f32,
                                                           T* __restrict__ dx) {
@@ -85,7 +86,6 @@ __global__ __launch_bounds__(256) void permute_bwd_kernel(const T* __restrict__ 
   const int64_t t = wave_token(4);
   if (t >= T_) return;
   const int lane = threadIdx.x & 63;
-  const int64_t nrows = T_ * k;
   const int64_t nvec = d / VN;
   for (int64_t v = lane; v < nvec; v += 64) {
     float acc[VN] = {};
@@ -120,12 +120,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y,
                                                       const float* __restrict__ topk_w,
                                                       const int32_t* __restrict__ dst_row,
                                                       const T* __restrict__ shared, int64_t T_,
-                                                      int64_t d, int k, T* __restrict__ out) {
+                                                      int64_t d, int k, int64_t nrows,
+                                                      T* __restrict__ out) {
   constexpr int VN = Vec<T>::N;
   const int64_t t = wave_token(4);
   if (t >= T_) return;
   const int lane = threadIdx.x & 63;
-  const int64_t nrows = T_ * k;
   const int64_t nvec = d / VN;
   for (int64_t v = lane; v < nvec; v += 64) {
     float acc[VN] = {};
@@ -159,13 +159,12 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ 
                                                           const float* __restrict__ topk_w,
                                                           const int32_t* __restrict__ dst_row,
                                                           int64_t T_, int64_t d, int k,
-                                                          T* __restrict__ dy,
+                                                          int64_t nrows, T* __restrict__ dy,
                                                           float* __restrict__ d_w) {
   constexpr int VN = Vec<T>::N;
   const int64_t t = wave_token(4);
   if (t >= T_) return;
   const int lane = threadIdx.x & 63;
-  const int64_t nrows = T_ * k;
   const int64_t nvec = d / VN;
   float dot[KMAX];
 #pragma unroll
@@ -277,75 +276,76 @@ static dim3 elem_grid(int64_t n) {
 }
 
 hipError_t launch_permute(const void* x, int dtype, const int32_t* dst_row, int64_t T, int64_t d,
-                          int k, void* xp, hipStream_t s) {
+                          int k, int64_t nrows, void* xp, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (dtype == 0)
     permute_kernel<float><<<token_grid(T), 256, 0, s>>>(static_cast<const float*>(x), dst_row, T, d,
-                                                        k, static_cast<float*>(xp));
+                                                        k, nrows, static_cast<float*>(xp));
   else
     permute_kernel<bf16_t><<<token_grid(T), 256, 0, s>>>(static_cast<const bf16_t*>(x), dst_row, T,
-                                                         d, k, static_cast<bf16_t*>(xp));
+                                                         d, k, nrows, static_cast<bf16_t*>(xp));
   return hipGetLastError();
 }
 
 hipError_t launch_permute_bwd(const void* dxp, int dtype, const int32_t* dst_row, int64_t T,
-                              int64_t d, int k, const void* addend, const float* addend_f32,
-                              void* dx, hipStream_t s) {
+                              int64_t d, int k, int64_t nrows, const void* addend,
+                              const float* addend_f32, void* dx, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (dtype == 0)
     permute_bwd_kernel<float><<<token_grid(T), 256, 0, s>>>(
-        static_cast<const float*>(dxp), dst_row, T, d, k, static_cast<const float*>(addend),
-        addend_f32, static_cast<float*>(dx));
+        static_cast<const float*>(dxp), dst_row, T, d, k, nrows,
+        static_cast<const float*>(addend), addend_f32, static_cast<float*>(dx));
   else
     permute_bwd_kernel<bf16_t><<<token_grid(T), 256, 0, s>>>(
-        static_cast<const bf16_t*>(dxp), dst_row, T, d, k, static_cast<const bf16_t*>(addend),
-        addend_f32, static_cast<bf16_t*>(dx));
+        static_cast<const bf16_t*>(dxp), dst_row, T, d, k, nrows,
+        static_cast<const bf16_t*>(addend), addend_f32, static_cast<bf16_t*>(dx));
   return hipGetLastError();
 }
 
 hipError_t launch_combine(const void* y, int dtype, const float* topk_w, const int32_t* dst_row,
-                          const void* shared, int64_t T, int64_t d, int k, void* out,
-                          hipStream_t s) {
+                          const void* shared, int64_t T, int64_t d, int k, int64_t nrows,
+                          void* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (dtype == 0)
     combine_kernel<float><<<token_grid(T), 256, 0, s>>>(static_cast<const float*>(y), topk_w,
                                                         dst_row, static_cast<const float*>(shared),
-                                                        T, d, k, static_cast<float*>(out));
+                                                        T, d, k, nrows, static_cast<float*>(out));
   else
     combine_kernel<bf16_t><<<token_grid(T), 256, 0, s>>>(
         static_cast<const bf16_t*>(y), topk_w, dst_row, static_cast<const bf16_t*>(shared), T, d,
-        k, static_cast<bf16_t*>(out));
+        k, nrows, static_cast<bf16_t*>(out));
   return hipGetLastError();
 }
 
 template <typename T>
 static void combine_bwd_dispatch(const T* dout, const T* y, const float* w, const int32_t* dst,
-                                 int64_t Tn, int64_t d, int k, T* dy, float* dw, hipStream_t s) {
+                                 int64_t Tn, int64_t d, int k, int64_t nrows, T* dy, float* dw,
+                                 hipStream_t s) {
   const dim3 g = token_grid(Tn);
   if (k <= 2)
-    combine_bwd_kernel<T, 2><<<g, 256, 0, s>>>(dout, y, w, dst, Tn, d, k, dy, dw);
+    combine_bwd_kernel<T, 2><<<g, 256, 0, s>>>(dout, y, w, dst, Tn, d, k, nrows, dy, dw);
   else if (k <= 4)
-    combine_bwd_kernel<T, 4><<<g, 256, 0, s>>>(dout, y, w, dst, Tn, d, k, dy, dw);
+    combine_bwd_kernel<T, 4><<<g, 256, 0, s>>>(dout, y, w, dst, Tn, d, k, nrows, dy, dw);
   else if (k <= 8)
-    combine_bwd_kernel<T, 8><<<g, 256, 0, s>>>(dout, y, w, dst, Tn, d, k, dy, dw);
+    combine_bwd_kernel<T, 8><<<g, 256, 0, s>>>(dout, y, w, dst, Tn, d, k, nrows, dy, dw);
   else if (k <= 16)
-    combine_bwd_kernel<T, 16><<<g, 256, 0, s>>>(dout, y, w, dst, Tn, d, k, dy, dw);
+    combine_bwd_kernel<T, 16><<<g, 256, 0, s>>>(dout, y, w, dst, Tn, d, k, nrows, dy, dw);
   else if (k <= 32)
-    combine_bwd_kernel<T, 32><<<g, 256, 0, s>>>(dout, y, w, dst, Tn, d, k, dy, dw);
+    combine_bwd_kernel<T, 32><<<g, 256, 0, s>>>(dout, y, w, dst, Tn, d, k, nrows, dy, dw);
   else
-    combine_bwd_kernel<T, 64><<<g, 256, 0, s>>>(dout, y, w, dst, Tn, d, k, dy, dw);
+    combine_bwd_kernel<T, 64><<<g, 256, 0, s>>>(dout, y, w, dst, Tn, d, k, nrows, dy, dw);
 }
 
 hipError_t launch_combine_bwd(const void* dout, const void* y, int dtype, const float* topk_w,
-                              const int32_t* dst_row, int64_t T, int64_t d, int k, void* dy,
-                              float* d_w, hipStream_t s) {
+                              const int32_t* dst_row, int64_t T, int64_t d, int k, int64_t nrows,
+                              void* dy, float* d_w, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (dtype == 0)
     combine_bwd_dispatch<float>(static_cast<const float*>(dout), static_cast<const float*>(y),
-                                topk_w, dst_row, T, d, k, static_cast<float*>(dy), d_w, s);
+                                topk_w, dst_row, T, d, k, nrows, static_cast<float*>(dy), d_w, s);
   else
     combine_bwd_dispatch<bf16_t>(static_cast<const bf16_t*>(dout), static_cast<const bf16_t*>(y),
-                                 topk_w, dst_row, T, d, k, static_cast<bf16_t*>(dy), d_w, s);
+                                 topk_w, dst_row, T, d, k, nrows, static_cast<bf16_t*>(dy), d_w, s);
   return hipGetLastError();
 }
 
@@ -389,6 +389,25 @@ hipError_t launch_swiglu_bwd(const void* dh, const void* ab, int dtype, int64_t 
     swiglu_bwd_kernel<bf16_t><<<elem_grid(M * f / 8), 256, 0, s>>>(
         static_cast<const bf16_t*>(dh), static_cast<const bf16_t*>(ab), M, f,
         static_cast<bf16_t*>(dab));
+  return hipGetLastError();
+}
+
+// Zero the rows of a permuted buffer that hold no (token, slot) pair
+// (src_token < 0: the padding of a pad-to-max layout), 16 bytes per lane.
+__global__ __launch_bounds__(256) void zero_unmapped_rows_kernel(uint4* __restrict__ buf,
+                                                                 const int32_t* __restrict__ src_token,
+                                                                 int64_t M, int64_t chunks) {
+  const int64_t r = blockIdx.x;
+  if (r >= M || src_token[r] >= 0) return;
+  uint4* row = buf + r * chunks;
+  for (int64_t c = threadIdx.x; c < chunks; c += 256) row[c] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+hipError_t launch_zero_unmapped_rows(void* buf, int64_t row_bytes, const int32_t* src_token,
+                                     int64_t M, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  zero_unmapped_rows_kernel<<<dim3(static_cast<unsigned>(M)), 256, 0, s>>>(
+      static_cast<uint4*>(buf), src_token, M, row_bytes / 16);
   return hipGetLastError();
 }
 

@@ -664,3 +664,69 @@ hipError_t launch_expert_bias_update(const int32_t* counts, int E, float rate, f
 }
 
 }  // namespace moe
+
+namespace moe {
+
+// Pad-to-max (section 7, Load Balancing: static shapes from variable expert
+// counts): every expert's segment gets C rows at e * C; a pair keeps its rank
+// in the dropless segment (token order) when that rank is below C, else it is
+// dropped -- the kept pairs of capacity-limited dropping.
+__global__ __launch_bounds__(256) void pad_map_kernel(const int32_t* __restrict__ topk_idx,
+                                                      const int64_t* __restrict__ offsets,
+                                                      const int32_t* __restrict__ dst_row,
+                                                      int64_t n, int E, int64_t C,
+                                                      int32_t* __restrict__ dst_row_out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int e = topk_idx[i];
+  const int64_t row = dst_row[i];
+  int32_t out = -1;
+  if (e >= 0 && e < E && row >= 0) {
+    const int64_t rank = row - offsets[e];
+    if (rank >= 0 && rank < C) out = static_cast<int32_t>(e * C + rank);
+  }
+  dst_row_out[i] = out;
+}
+
+// rows of the padded layout: row e * C + q holds the q-th token of expert e
+// while q < min(counts[e], C), else padding (-1)
+__global__ __launch_bounds__(256) void pad_rows_kernel(const int32_t* __restrict__ counts,
+                                                       const int64_t* __restrict__ offsets,
+                                                       const int32_t* __restrict__ src_token,
+                                                       int64_t n_in, int E, int64_t C,
+                                                       int32_t* __restrict__ counts_out,
+                                                       int64_t* __restrict__ offsets_out,
+                                                       int32_t* __restrict__ src_token_out) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (r <= E) {
+    offsets_out[r] = r * C;
+    if (r < E) {
+      const int64_t c = counts[r];
+      counts_out[r] = static_cast<int32_t>(c < 0 ? 0 : (c < C ? c : C));
+    }
+  }
+  if (r >= static_cast<int64_t>(E) * C) return;
+  const int e = static_cast<int>(r / C);
+  const int64_t q = r - e * C;
+  const int64_t c = counts[e];
+  const int64_t src = offsets[e] + q;
+  src_token_out[r] = q < c && q < C && src >= 0 && src < n_in ? src_token[src] : -1;
+}
+
+hipError_t launch_pad_to_max(const int32_t* topk_idx, const int32_t* counts,
+                             const int64_t* offsets, const int32_t* dst_row,
+                             const int32_t* src_token, int64_t T, int E, int k, int64_t C,
+                             int32_t* counts_out, int64_t* offsets_out, int32_t* dst_row_out,
+                             int32_t* src_token_out, hipStream_t stream) {
+  const int64_t n = T * k;
+  if (n > 0)
+    pad_map_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), 256, 0, stream>>>(
+        topk_idx, offsets, dst_row, n, E, C, dst_row_out);
+  const int64_t rows = static_cast<int64_t>(E) * C;
+  const int64_t m = rows > E + 1 ? rows : E + 1;
+  pad_rows_kernel<<<dim3(static_cast<unsigned>((m + 255) / 256)), 256, 0, stream>>>(
+      counts, offsets, src_token, n, E, C, counts_out, offsets_out, src_token_out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

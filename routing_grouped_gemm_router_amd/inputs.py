@@ -25,6 +25,9 @@ all tensors synthetic, N(0, 1) activations and N(0, 1/fan_in) weights):
                      (capacity factor 1.0: at most T*k/E rows per expert)
   small_capacity     T=513 d=128 E=16 k=4 f=128, Zipf-biased softmax routing,
                      capacity factor 1.25
+  small_pad_to_max   small_capacity with every expert's segment padded to the
+                     capacity (static offsets e * C)
+  deepseek_v3_pad_to_max deepseek_v3_capacity padded to the capacity
   small_aux          T=300 d=256 E=8 k=2 f=256 shared 128, sigmoid routing with
                      an auxiliary load-balancing loss (coefficient 0.01)
   deepseek_v3_expert_bias as deepseek_v3_e256k8 with the selection-only expert
@@ -63,6 +66,7 @@ class LayerConfig:
     zipf_s: float = 1.0
     routing: str = "topk"       # topk | balanced (experts given, replayed)
     capacity_factor: float = 0.0  # > 0: each expert keeps ceil(factor*T*k/E) rows
+    pad_to_max: bool = False      # with a capacity: every expert's segment padded to it
     aux_loss_coeff: float = 0.0   # > 0: auxiliary load-balancing loss
     # > 0: selection-only expert bias on sigmoid scores (auxiliary-loss-free
     # balancing), drawn N(0, std^2), moved by the update rate after each route
@@ -104,6 +108,11 @@ CONFIGS = {
                                            expert_bias_rate=1e-3),
     "small_expert_bias": LayerConfig("small_expert_bias", T=512, d=256, E=16, k=4, f=256, fs=128,
                                      score="sigmoid", expert_bias_std=0.05, expert_bias_rate=1e-3),
+    "small_pad_to_max": LayerConfig("small_pad_to_max", T=513, d=128, E=16, k=4, f=128,
+                                    bias="zipf", capacity_factor=1.25, pad_to_max=True),
+    "deepseek_v3_pad_to_max": LayerConfig("deepseek_v3_pad_to_max", T=8192, d=7168, E=256, k=8,
+                                          f=2048, fs=2048, score="sigmoid", bias="normal",
+                                          capacity_factor=1.0, pad_to_max=True),
     "small_aux": LayerConfig("small_aux", T=300, d=256, E=8, k=2, f=256, fs=128, score="sigmoid",
                              bias="normal", aux_loss_coeff=0.01),
 }

@@ -123,9 +123,18 @@ class MoELayer:
         if self.aux:
             self.aux_loss = emp(1, dtype=torch.float32)
             self.aux_ws = emp(abi.moe_aux_loss_workspace_bytes(T, E), dtype=torch.uint8)
+        # pad-to-max: every expert owns `capacity` rows at e * capacity (static
+        # offsets); padding rows are kept zero in the buffers the GEMMs read
+        self.pad = cfg.pad_to_max
+        if self.pad and (self.capacity is None or cfg.gemm not in ("bf16", "f32") or gate_in_ffn):
+            raise ValueError("pad_to_max: needs a capacity, bf16 / fp32 GEMMs, no gate_in_ffn")
+        if self.pad:
+            N = E * self.capacity  # rows of the permuted buffers
+            self.src_token = emp(N, dtype=torch.int32)
         if self.capacity is not None:
             self.full = dict(counts=emp(E, dtype=torch.int32), offsets=emp(E + 1, dtype=torch.int64),
-                             dst_row=emp(T, k, dtype=torch.int32), src_token=emp(N, dtype=torch.int32))
+                             dst_row=emp(T, k, dtype=torch.int32),
+                             src_token=emp(T * k, dtype=torch.int32))
         # the MXFP8 path gathers x inside its quantizers: no permuted bf16 copy
         self.x_perm = emp(N, d) if cfg.gemm != "mxfp8" else None
         self.ab = emp(N, 2 * f)
@@ -356,7 +365,11 @@ class MoELayer:
                 abi.moe_route_topk(self.logits, c.k, self.score, c.renorm, self.topk_idx,
                                    self.topk_w, m["counts"], m["offsets"], m["dst_row"],
                                    m["src_token"], self.route_ws)
-            if self.capacity is not None:
+            if self.pad:
+                abi.moe_pad_to_max(self.topk_idx, m["counts"], m["offsets"], m["dst_row"],
+                                   m["src_token"], self.capacity, self.counts, self.offsets,
+                                   self.dst_row, self.src_token)
+            elif self.capacity is not None:
                 abi.moe_apply_capacity(self.topk_idx, m["counts"], m["offsets"], m["dst_row"],
                                        self.capacity, self.counts, self.offsets, self.dst_row,
                                        self.src_token)
@@ -371,6 +384,8 @@ class MoELayer:
         if not self.mx:
             with self._span("permute"):
                 abi.moe_permute(x, self.dst_row, self.x_perm)
+                if self.pad:
+                    abi.moe_zero_unmapped_rows(self.x_perm, self.src_token)
         if self.lowp:
             self._forward_lowp(x)
             with self._span("combine"):
@@ -412,6 +427,8 @@ class MoELayer:
             else:
                 abi.moe_unpermute_combine_bwd(dout, self.y, self.topk_w, self.dst_row, self.dy,
                                               self.d_topk_w)
+                if self.pad:
+                    abi.moe_zero_unmapped_rows(self.dy, self.src_token)
         if self.lowp:
             self._backward_lowp(dout)
             return self._backward_tail(dout, self.dxs if self.shared else None)

@@ -49,10 +49,10 @@ def _fake(n=1 << 20):
 
 @pytest.mark.parametrize("case,expect", [
     # (function, args) -> status
-    (("moe_permute", (None, 1, None, 10, 64, 2, None, None)), -1),
-    (("moe_permute", (None, 7, None, 10, 64, 2, None, None)), -3),
-    (("moe_permute", (None, 1, None, -1, 64, 2, None, None)), -2),
-    (("moe_permute", (_fake(), 1, _fake(), 10, 60, 2, _fake(), None)), -4),
+    (("moe_permute", (None, 1, None, 10, 64, 2, 20, None, None)), -1),
+    (("moe_permute", (None, 7, None, 10, 64, 2, 20, None, None)), -3),
+    (("moe_permute", (None, 1, None, -1, 64, 2, 20, None, None)), -2),
+    (("moe_permute", (_fake(), 1, _fake(), 10, 60, 2, 20, _fake(), None)), -4),
     (("moe_route_topk", (None, 10, 4, 5, 0, 1, None, None, None, None, None, None, None, 0, None)), -2),
     (("moe_route_topk", (None, 10, 2000, 5, 0, 1, None, None, None, None, None, None, None, 0, None)), -4),
     (("moe_route_topk", (None, 10, 256, 80, 0, 1, None, None, None, None, None, None, None, 0, None)), -4),
@@ -72,8 +72,25 @@ def _fake(n=1 << 20):
     (("moe_grouped_gemm_wgrad", (_fake(), _fake(), _fake(), 4, 100, 128, 128, 0, 1, 0, _fake(), None)), -3),
     (("moe_swiglu", (None, 1, 10, 12, None, None)), -4),
     (("moe_swiglu_bwd", (None, None, 1, 10, 16, None, None)), -1),
-    (("moe_unpermute_combine", (None, 1, None, None, None, 10, 64, 2, None, None)), -1),
-    (("moe_unpermute_combine_bwd", (None, None, 1, None, None, 10, 64, 65, None, None, None)), -4),
+    (("moe_unpermute_combine", (None, 1, None, None, None, 10, 64, 2, 20, None, None)), -1),
+    (("moe_permute", (None, 1, None, 10, 64, 2, -1, None, None)), -2),
+    (("moe_pad_to_max", (None, None, None, None, None, 10, 8, 2, 0, None, None, None, None, None)),
+     -2),
+    (("moe_pad_to_max", (None, None, None, None, None, 10, 8, 2, 4, None, None, None, None, None)),
+     -1),
+    (("moe_zero_unmapped_rows", (None, 1, None, 10, 60, None)), -4),
+    (("moe_zero_unmapped_rows", (None, 5, None, 10, 64, None)), -3),
+    (("moe_route_topk_expert_bias", (None, None, 10, 8, 9, 1, None, None, None, None, None, None,
+                                     None, 0, None)), -2),
+    (("moe_expert_bias_update", (None, 2000, 0.001, None, None)), -4),
+    (("moe_quant_mxfp8_rows", (None, 10, 100, None, None, None)), -4),
+    (("moe_permute_quant_mxfp8", (None, 10, 128, None, None, 4, 40, None, None, None)), -1),
+    (("moe_quant_mxfp8_token_tiles", (None, 10, None, None, None, 4, 20, 128, 128, None, None,
+                                      None)), -2),
+    (("moe_grouped_gemm_mxfp8_fwd", (None, None, None, None, None, 4, 10, 100, 128, 0, None, None,
+                                     None)), -4),
+    (("moe_unpermute_combine_bwd", (None, None, 1, None, None, 10, 64, 65, 650, None, None,
+                                    None)), -4),
     (("moe_router_logits", (None, 1, None, None, 10, 64, 2000, None, None)), -4),
     (("moe_router_logits", (None, 1, None, None, 10, 64, 8, None, None)), -1),
     (("moe_router_logits_bwd", (None, 1, None, None, 10, 64, 8, _fake(), None, None)), -1),
@@ -86,8 +103,8 @@ def test_validation_rejects_before_launch(lib, case, expect):
 
 
 def test_zero_sized_calls_are_noops(lib):
-    assert lib.moe_permute(None, 1, None, 0, 64, 2, None, None) == 0
-    assert lib.moe_unpermute_combine(None, 1, None, None, None, 0, 64, 2, None, None) == 0
+    assert lib.moe_permute(None, 1, None, 0, 64, 2, 0, None, None) == 0
+    assert lib.moe_unpermute_combine(None, 1, None, None, None, 0, 64, 2, 0, None, None) == 0
     assert lib.moe_swiglu(None, 1, 0, 64, None, None) == 0
     assert lib.moe_router_logits(None, 1, None, None, 0, 64, 8, None, None) == 0
     assert lib.moe_route_topk_bwd(None, None, None, None, 0, 8, 2, 0, 1, None, None) == 0

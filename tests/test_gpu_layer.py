@@ -50,6 +50,10 @@ def _run(cfg, seed, recompute_act=False, gate_in_ffn=False):
             cfg.score, cfg.renorm, logit_bias=bias, shared=shared, given_experts=given,
             capacity=cap)
     g = bwd(c, np64(inp["dout"]))
+    if cfg.pad_to_max:  # the same kept pairs, in the static padded layout
+        routed = (oracle.route(c["z"], cfg.k, cfg.score, cfg.renorm) if given is None
+                  else oracle.route_replay(c["z"], given, cfg.score, cfg.renorm))
+        c = dict(c, route=oracle.pad_to_max(routed, cap))
     if cfg.aux_loss_coeff > 0:
         # the auxiliary loss adds its gradient to d_logits (counts of the routing)
         L, dz = oracle.aux_loss(c["z"], c["route"]["counts"], cfg.k, cfg.score, cfg.aux_loss_coeff)
@@ -165,3 +169,13 @@ def test_layer_expert_bias(gpu):
     np.testing.assert_array_equal(layer.sel_bias.cpu().numpy().view(np.int32),
                                   want.view(np.int32))
     assert (want != b0).any()
+
+
+@pytest.mark.parametrize("recompute", [False, True])
+def test_layer_pad_to_max(gpu, recompute):
+    """Every expert's segment padded to the capacity: the static padded map,
+    and the layer's outputs and gradients equal to capacity dropping."""
+    cfg = inputs.CONFIGS["small_pad_to_max"]
+    layer, c, g = _run(cfg, 0, recompute_act=recompute)
+    assert layer.x_perm.shape[0] == cfg.E * layer.capacity
+    _check(cfg, layer, c, g)

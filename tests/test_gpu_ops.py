@@ -522,3 +522,35 @@ def test_expert_bias_update_bit_exact(gpu, E):
     abi.moe_expert_bias_update(torch.from_numpy(counts).to(DEV), 1e-3, gb)
     want = oracle.expert_bias_update(b, counts, np.float32(1e-3))
     np.testing.assert_array_equal(gb.cpu().numpy().view(np.int32), want.view(np.int32))
+
+
+@pytest.mark.parametrize("T,E,k,C", [(700, 13, 3, 100), (700, 13, 3, 1), (4096, 256, 8, 128),
+                                     (300, 8, 2, 500)])
+def test_pad_to_max_bit_exact(gpu, T, E, k, C):
+    """The padded dispatch map against the oracle; then a permute into it and
+    the padding rows cleared: every row is x of its token or zero."""
+    print(f"pad_to_max T={T} E={E} k={k} C={C}", flush=True)
+    z = _keys(T, E, 7 + C, "zipf" if E == 128 else "normal")
+    z = (z + np.linspace(0.0, 1.5, E, dtype=np.float32)).astype(np.float32)   # uneven loads
+    r = oracle.route(z, k, "softmax", True)
+    p = oracle.pad_to_max(r, C)
+    dev = {n: torch.from_numpy(np.ascontiguousarray(r[n]).astype(
+        np.int64 if n == "offsets" else np.int32)).to(DEV)
+        for n in ("topk_idx", "counts", "offsets", "dst_row", "src_token")}
+    g = {"counts": torch.empty(E, dtype=torch.int32, device=DEV),
+         "offsets": torch.empty(E + 1, dtype=torch.int64, device=DEV),
+         "dst_row": torch.empty((T, k), dtype=torch.int32, device=DEV),
+         "src_token": torch.full((E * C,), 77, dtype=torch.int32, device=DEV)}
+    abi.moe_pad_to_max(dev["topk_idx"], dev["counts"], dev["offsets"], dev["dst_row"],
+                       dev["src_token"], C, g["counts"], g["offsets"], g["dst_row"], g["src_token"])
+    for key in ("counts", "offsets", "dst_row", "src_token"):
+        np.testing.assert_array_equal(g[key].cpu().numpy(), p[key], err_msg=key)
+    d = 64
+    x = torch.randn((T, d), generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
+    xp = torch.full((E * C, d), 3.0, dtype=torch.bfloat16, device=DEV)
+    abi.moe_permute(x.to(DEV), g["dst_row"], xp)
+    abi.moe_zero_unmapped_rows(xp, g["src_token"])
+    want = torch.zeros((E * C, d), dtype=torch.bfloat16)
+    rows = np.nonzero(p["src_token"] >= 0)[0]
+    want[rows] = x[p["src_token"][rows]]
+    assert torch.equal(xp.cpu(), want)
