@@ -53,6 +53,9 @@ def parse():
                          "backward)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the CPU oracle sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only copy BYTES once device to device (the reference that scales the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
 
 
@@ -260,6 +263,16 @@ def main():
     import torch
     from routing_grouped_gemm_router_amd import inputs
     from routing_grouped_gemm_router_amd.layer import EventTimer, MoELayer
+
+    if args.copy_calibration:
+        n = args.copy_calibration // 16 * 16
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").view(torch.int32).fill_(7)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n}), flush=True)
+        return 0
 
     cfg = inputs.CONFIGS[args.config]
     if cfg.gemm not in ("bf16", "fp8", "mxfp8"):
