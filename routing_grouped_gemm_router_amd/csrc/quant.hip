@@ -39,21 +39,19 @@
 
 namespace moe {
 
-// nearest E4M3 code of a finite fp32 value, ties to even, saturating
-__device__ __forceinline__ uint32_t e4m3_encode(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fabsf(v);
-  if (a >= 448.0f) return sign | 0x7eu;
-  if (a < 0.015625f) {  // below 2^-6: subnormal step 2^-9 (exact scaling, then RNE)
-    return sign | static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
-  }
-  int e = static_cast<int>((__float_as_uint(a) >> 23) & 0xffu) - 127;  // -6 .. 8
-  float q = __builtin_rintf(ldexpf(a, 3 - e));                         // 8 .. 16
-  if (q >= 16.0f) {
-    q = 8.0f;
-    ++e;
-  }
-  return sign | (static_cast<uint32_t>(e + 7) << 3) | (static_cast<uint32_t>(q) - 8u);
+// Nearest E4M3 codes of finite fp32 values, ties to the even code, saturated
+// to +-448: gfx950's v_cvt_pk_fp8_f32 (OCP E4M3FN, round to nearest even,
+// subnormals kept) after a clamp to +-448, so that nothing overflows.  Checked
+// equal, on every finite fp32 value, to an encoder written from the format's
+// definition (sign; for |v| < 2^-6 the subnormal step 2^-9; else 3 mantissa
+// bits at the value's binade, a carry into the next binade, saturation).
+__device__ __forceinline__ float e4m3_clamp(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
+
+// four codes in one dword, byte i from v[i]
+__device__ __forceinline__ uint32_t e4m3_encode4(float v0, float v1, float v2, float v3) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(v0), e4m3_clamp(v1), 0, false);
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(v2), e4m3_clamp(v3), lo, true));
 }
 
 __device__ __forceinline__ void block_scale(float amax, float& scale, float& inv) {
@@ -76,11 +74,8 @@ __device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
 }
 
 __device__ __forceinline__ uint2 encode8(const float (&f)[8], float inv) {
-  uint32_t c[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = e4m3_encode(f[i] * inv);
-  return make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
-                    c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+  return make_uint2(e4m3_encode4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv),
+                    e4m3_encode4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv));
 }
 
 // ---- 1 x 128 tiles along rows: 16 lanes per block, 4 blocks per wave -------
@@ -251,8 +246,9 @@ __global__ __launch_bounds__(256) void quant_token_tiles_kernel(
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) tile[r8 + i][c8 + j] = static_cast<uint8_t>(e4m3_encode(f[i][j] * inv[j]));
+    *reinterpret_cast<uint2*>(&tile[r8 + i][c8]) = make_uint2(
+        e4m3_encode4(f[i][0] * inv[0], f[i][1] * inv[1], f[i][2] * inv[2], f[i][3] * inv[3]),
+        e4m3_encode4(f[i][4] * inv[4], f[i][5] * inv[5], f[i][6] * inv[6], f[i][7] * inv[7]));
   __syncthreads();
   // transposed store: column c holds this block's 128 token codes
 #pragma unroll
@@ -281,16 +277,11 @@ __device__ __forceinline__ uint32_t mx_byte(float amax) {
 }
 
 // codes of v * 2^-X = v * 2^(127 - byte), an exact power-of-two scaling
-__device__ __forceinline__ uint32_t mx_code(float v, uint32_t byte) {
-  return e4m3_encode(ldexpf(v, 127 - static_cast<int>(byte)));
-}
-
 __device__ __forceinline__ uint2 encode8_mx(const float (&f)[8], uint32_t byte) {
-  uint32_t c[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = mx_code(f[i], byte);
-  return make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
-                    c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+  const int e = 127 - static_cast<int>(byte);
+  return make_uint2(
+      e4m3_encode4(ldexpf(f[0], e), ldexpf(f[1], e), ldexpf(f[2], e), ldexpf(f[3], e)),
+      e4m3_encode4(ldexpf(f[4], e), ldexpf(f[5], e), ldexpf(f[6], e), ldexpf(f[7], e)));
 }
 
 // bf16 row `r` of the quantizer's input, through the row map if there is one;
@@ -372,6 +363,7 @@ __global__ __launch_bounds__(256) void quant_mx_weights_kernel(
     if ((t & 3) == 0) nbyte[r8 + i][(t & 15) >> 2] = static_cast<uint8_t>(b);
   }
   // forward operand: blocks of 32 rows
+  int ex[8];  // per column: 127 - byte, the exponent of the exact scaling
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     float am = 0.f;
@@ -380,10 +372,16 @@ __global__ __launch_bounds__(256) void quant_mx_weights_kernel(
     am = fmaxf(am, __shfl_xor(am, 16, 64));
     am = fmaxf(am, __shfl_xor(am, 32, 64));
     const uint32_t b = mx_byte(am);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) tile[r8 + i][c8 + j] = static_cast<uint8_t>(mx_code(f[i][j], b));
+    ex[j] = 127 - static_cast<int>(b);
     if (lane < 16) kbyte[wave][c8 + j] = static_cast<uint8_t>(b);
   }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    *reinterpret_cast<uint2*>(&tile[r8 + i][c8]) = make_uint2(
+        e4m3_encode4(ldexpf(f[i][0], ex[0]), ldexpf(f[i][1], ex[1]), ldexpf(f[i][2], ex[2]),
+                     ldexpf(f[i][3], ex[3])),
+        e4m3_encode4(ldexpf(f[i][4], ex[4]), ldexpf(f[i][5], ex[5]), ldexpf(f[i][6], ex[6]),
+                     ldexpf(f[i][7], ex[7])));
   __syncthreads();
   // forward codes transposed through LDS: row n holds this tile's 128 k codes
   uint8_t* fq = qf + (g * N + nb * 128) * K + kb * 128;
@@ -444,6 +442,7 @@ __global__ __launch_bounds__(256) void quant_mx_token_tiles_kernel(
       for (int j = 0; j < 8; ++j) f[i][j] = 0.f;
     }
   }
+  int ex[8];  // per column: 127 - byte, the exponent of the exact scaling
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     float am = 0.f;
@@ -452,10 +451,16 @@ __global__ __launch_bounds__(256) void quant_mx_token_tiles_kernel(
     am = fmaxf(am, __shfl_xor(am, 16, 64));
     am = fmaxf(am, __shfl_xor(am, 32, 64));
     const uint32_t b = mx_byte(am);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) tile[r8 + i][c8 + j] = static_cast<uint8_t>(mx_code(f[i][j], b));
+    ex[j] = 127 - static_cast<int>(b);
     if (lane < 16) kbyte[wave][c8 + j] = static_cast<uint8_t>(b);
   }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    *reinterpret_cast<uint2*>(&tile[r8 + i][c8]) = make_uint2(
+        e4m3_encode4(ldexpf(f[i][0], ex[0]), ldexpf(f[i][1], ex[1]), ldexpf(f[i][2], ex[2]),
+                     ldexpf(f[i][3], ex[3])),
+        e4m3_encode4(ldexpf(f[i][4], ex[4]), ldexpf(f[i][5], ex[5]), ldexpf(f[i][6], ex[6]),
+                     ldexpf(f[i][7], ex[7])));
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
