@@ -29,8 +29,9 @@ import numpy as np
 E4M3_MAX = 448.0
 
 
-def decode(codes):
-    """Value of each E4M3 code (float64; NaN for S.1111.111)."""
+def _decode_definition(codes):
+    """Value of each E4M3 code from the format's fields (float64; NaN for
+    S.1111.111)."""
     c = np.asarray(codes, dtype=np.int64) & 0xFF
     s = np.where(c >> 7, -1.0, 1.0)
     e = (c >> 3) & 0xF
@@ -39,6 +40,15 @@ def decode(codes):
     sub = s * np.ldexp(m / 8.0, -6)
     v = np.where(e == 0, sub, normal)
     return np.where((e == 15) & ((c & 7) == 7), np.nan, v)
+
+
+_DECODE_TABLE = _decode_definition(np.arange(256))
+
+
+def decode(codes):
+    """Value of each E4M3 code (float64; NaN for S.1111.111): the definition
+    above, evaluated once for all 256 codes and looked up."""
+    return _DECODE_TABLE[np.asarray(codes, dtype=np.int64) & 0xFF]
 
 
 # Non-negative finite codes 0x00..0x7E in increasing order of value.
