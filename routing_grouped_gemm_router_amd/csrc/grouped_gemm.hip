@@ -1033,8 +1033,258 @@ static hipError_t run_rows(const Params& p, hipStream_t s) {
   return run_cfg<MODE, Q, 2>(p, mt * (p.Nout / 128), s);
 }
 
+// ---- bf16 weight gradient, 256 x 256 tiles -----------------------------------
+// dB[g] = A[rows g]^T . dC[rows g] with both output dimensions multiples of
+// 256 (no ragged output dimension, so the larger tile wastes nothing): 8 waves
+// in a 4 x 2 arrangement, each 64 x 128 (2 x 4 MFMA 32x32 blocks), a 2-stage
+// ring of 64 KiB stages (A: 64 tokens x 256 columns, B the same, both in the
+// [k][col] layout read with ds_read_b64_tr_b16).  Against the 128 x 256 tile
+// this halves the per-tile work of decoding, loader set-up and epilogue
+// synchronisation per FLOP (a group's token range is short, so a tile is a
+// few k steps), reads a quarter fewer LDS fragments per MFMA, and re-reads the
+// activation slabs a quarter less.
+namespace w256 {
+constexpr int BMN = 256;           // tile rows (dB rows) and columns
+constexpr int SLAB = 16384;        // [64 k][128 cols] bf16
+constexpr int STAGE = 4 * SLAB;    // A: 2 slabs, B: 2 slabs
+constexpr int STAGES = 2;
+constexpr int PER = 8;             // DMA instructions per wave per stage
+}
+
+// [32 m][128 n] bf16 staging rows of 256 B, 16-byte chunks swizzled by m & 15
+__device__ __forceinline__ int stg_off16(int m, int chunk) {
+  return m * 256 + ((chunk ^ (m & 15)) << 4);
+}
+
+__global__ __launch_bounds__(512, 1) void wgrad256_kernel(Params p) {
+  using namespace w256;
+  __shared__ __attribute__((aligned(1024))) char ring[STAGES * STAGE];
+  __shared__ int s_off[MAX_GROUPS + 1];
+  LDS_AS char* lring = (LDS_AS char*)(ring);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  for (int g = tid; g <= p.G; g += 512) s_off[g] = static_cast<int>(clamp64(p.off[g], 0, p.M));
+  __syncthreads();
+  if (wave == 0) {  // running maximum makes the offsets non-decreasing
+    const int per = (p.G + 1 + 63) / 64;
+    const int g0 = lane * per, g1 = min(p.G + 1, g0 + per);
+    int mx = 0;
+    for (int g = g0; g < g1; ++g) mx = max(mx, s_off[g]);
+    int incl = mx;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl = max(incl, y);
+    }
+    int run = __shfl_up(incl, 1, 64);
+    if (lane == 0) run = 0;
+    for (int g = g0; g < g1; ++g) {
+      run = max(run, s_off[g]);
+      s_off[g] = run;
+    }
+  }
+  __syncthreads();
+
+  const uint32_t MT = static_cast<uint32_t>(p.Kc / BMN), NT = static_cast<uint32_t>(p.Nout / BMN);
+  const uint32_t per_g = MT * NT;
+  const int64_t total = static_cast<int64_t>(p.G) * per_g;
+  const int64_t K = p.Kc, N = p.Nout;
+
+  struct T256 {
+    int g;
+    int64_t row0, col0, lo, nrows;
+    int nk;
+  };
+  auto decode256 = [&](int64_t tau, T256& t) {
+    const uint32_t tu = static_cast<uint32_t>(tau);
+    t.g = static_cast<int>(tu / per_g);
+    uint32_t m, n;
+    tile_in_group<WG_SN>(tu - static_cast<uint32_t>(t.g) * per_g, MT, NT, WG_SM, m, n);
+    t.row0 = static_cast<int64_t>(m) * BMN;
+    t.col0 = static_cast<int64_t>(n) * BMN;
+    t.lo = s_off[t.g];
+    t.nrows = s_off[t.g + 1] - t.lo;
+    t.nk = t.nrows > 0 ? static_cast<int>((t.nrows + 63) / 64) : 1;
+  };
+  // loader of a tile: DMA instruction q = wave * 4 + i of each operand fills
+  // 1 KiB of slab q / 16 (k rows 4 (q % 16) .. + 3, 256 bytes each)
+  i32x4_t ra, rb;
+  uint32_t va[4], vb[4];
+  auto setup = [&](const T256& t) {
+    ra = make_rsrc(p.A + t.lo * K * 2, static_cast<uint64_t>(t.nrows) * K * 2);
+    rb = make_rsrc(p.B + t.lo * N * 2, static_cast<uint64_t>(t.nrows) * N * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = wave * 4 + i, slab = q >> 4;
+      const int kr = 4 * (q & 15) + (lane >> 4), c = (lane & 15) ^ swz_nc(kr);
+      va[i] = static_cast<uint32_t>((kr * K + t.row0 + slab * 128 + 8 * c) * 2);
+      vb[i] = static_cast<uint32_t>((kr * N + t.col0 + slab * 128 + 8 * c) * 2);
+    }
+  };
+  const uint32_t da = static_cast<uint32_t>(64 * K * 2), db = static_cast<uint32_t>(64 * N * 2);
+  auto issue = [&](int kt, LDS_AS char* stage) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(ra, stage + (wave * 4 + i) * 1024, va[i] + kt * da);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(rb, stage + 2 * SLAB + (wave * 4 + i) * 1024, vb[i] + kt * db);
+  };
+
+  const Walk walk = make_walk(total);
+  int ld_i = 0, cp_i = 0;
+  int64_t ld_tau = 0;
+  T256 ld_t, cp_t;
+  bool ld_ok = walk_next(walk, ld_i, total, ld_tau);
+  if (ld_ok) {
+    decode256(ld_tau, ld_t);
+    setup(ld_t);
+  }
+  bool cp_ok = ld_ok;
+  cp_t = ld_t;
+  cp_i = ld_i;
+  int ld_kt = 0, cp_kt = 0, ld_slot = 0, cp_slot = 0;
+  auto advance_loader = [&]() {
+    ld_slot ^= 1;
+    if (++ld_kt == ld_t.nk) {
+      ld_kt = 0;
+      ++ld_i;
+      ld_ok = walk_next(walk, ld_i, total, ld_tau);
+      if (ld_ok) {
+        decode256(ld_tau, ld_t);
+        setup(ld_t);
+      }
+    }
+  };
+  if (ld_ok) {  // prologue: the first stage in flight
+    issue(ld_kt, lring + ld_slot * STAGE);
+    advance_loader();
+  }
+
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[ii][jj][v] = 0.f;
+
+  while (cp_ok) {
+    // this step's stage has landed for every wave (nothing younger in flight)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (ld_ok) {  // the other slot was consumed before the barrier
+      issue(ld_kt, lring + ld_slot * STAGE);
+      advance_loader();
+    }
+    {
+      const LDS_AS char* stage = lring + cp_slot * STAGE;
+      const LDS_AS char* opA = stage + (wm >> 1) * SLAB;
+      const LDS_AS char* opB = stage + 2 * SLAB + wn * SLAB;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        bf16x8_t a[2], b[4];
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) a[ii] = frag_nc(opA, (wm & 1) * 64 + ii * 32, kk * 16, lane);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) b[jj] = frag_nc(opB, jj * 32, kk * 16, lane);
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            acc[ii][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[jj], a[ii], acc[ii][jj], 0, 0, 0);
+      }
+    }
+    if (++cp_kt == cp_t.nk) {
+      // the slot just consumed becomes the staging area once every wave has
+      // read its fragments from it
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const int64_t row_w = cp_t.row0 + wm * 64, col_w = cp_t.col0 + wn * 128;
+      if (p.out_f32) {
+        float* out = static_cast<float*>(p.C) + static_cast<int64_t>(cp_t.g) * K * N;
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int vg = 0; vg < 4; ++vg) {
+              const int64_t m = row_w + ii * 32 + (lane & 31);
+              const int64_t n = col_w + jj * 32 + vg * 8 + (lane >> 5) * 4;
+              float4* q = reinterpret_cast<float4*>(out + m * N + n);
+              float4 v = make_float4(acc[ii][jj][vg * 4], acc[ii][jj][vg * 4 + 1],
+                                     acc[ii][jj][vg * 4 + 2], acc[ii][jj][vg * 4 + 3]);
+              if (p.accumulate) {
+                const float4 o = *q;
+                v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+              }
+              *q = v;
+            }
+      } else {
+        LDS_AS char* stg = lring + cp_slot * STAGE + wave * 8192;
+        bf16_t* out = static_cast<bf16_t*>(p.C) + static_cast<int64_t>(cp_t.g) * K * N;
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int vg = 0; vg < 4; ++vg) {
+              const int m = lane & 31;
+              const int n = jj * 32 + vg * 8 + (lane >> 5) * 4;
+              u32x2_t w;
+              w.x = pack2(acc[ii][jj][vg * 4 + 0], acc[ii][jj][vg * 4 + 1]);
+              w.y = pack2(acc[ii][jj][vg * 4 + 2], acc[ii][jj][vg * 4 + 3]);
+              *(LDS_AS u32x2_t*)(stg + stg_off16(m, n >> 3) + (n & 7) * 2) = w;
+            }
+          // 32 rows x 16 chunks; lane handles chunks lane + 64 i
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int idx = lane + 64 * i;
+            const int m = idx >> 4, c = idx & 15;
+            const u32x4_t vv = *(const LDS_AS u32x4_t*)(stg + stg_off16(m, c));
+            uint4* q = reinterpret_cast<uint4*>(out + (row_w + ii * 32 + m) * N + col_w + 8 * c);
+            if (p.accumulate) {
+              float x[8], y[8];
+              unpack8(make_uint4(vv.x, vv.y, vv.z, vv.w), x);
+              unpack8(*q, y);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) x[e] += y[e];
+              *q = pack8(x);
+            } else {
+              // streaming store: the gradient is not read again by this layer
+              __builtin_nontemporal_store(vv, reinterpret_cast<u32x4_t*>(q));
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[ii][jj][v] = 0.f;
+      cp_kt = 0;
+      ++cp_i;
+      int64_t cp_tau = 0;
+      cp_ok = walk_next(walk, cp_i, total, cp_tau);
+      if (cp_ok) decode256(cp_tau, cp_t);
+    }
+    cp_slot ^= 1;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 template <int Q>
 static hipError_t run_wgrad(const Params& p, hipStream_t s) {
+  if (Q == P_BF16 && p.Kc % w256::BMN == 0 && p.Nout % w256::BMN == 0) {
+    const int64_t tiles = static_cast<int64_t>(p.G) * (p.Kc / w256::BMN) * (p.Nout / w256::BMN);
+    if (tiles <= 0) return hipSuccess;
+    int64_t grid = cu_count();  // persistent, one workgroup per CU
+    if (tiles < grid) grid = tiles;
+    wgrad256_kernel<<<dim3(static_cast<unsigned>(grid)), 512, 0, s>>>(p);
+    return hipGetLastError();
+  }
   const int64_t mt = static_cast<int64_t>(p.G) * (p.Kc / BM);
   if (p.Nout % 256 == 0) return run_cfg<WGRAD, Q, 4>(p, mt * (p.Nout / 256), s);
   return run_cfg<WGRAD, Q, 2>(p, mt * (p.Nout / 128), s);

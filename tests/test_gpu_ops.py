@@ -201,6 +201,8 @@ GEMM_CASES = [
     (129, 1, 256, 128, 0.0, 0.0),
     (0, 3, 128, 128, 0.0, 0.0),
     (20000, 40, 256, 1024, 0.2, 1.0),   # many tiles per workgroup, skewed, empty groups
+    (3000, 7, 768, 512, 0.3, 0.5),      # weight gradient in 256 x 256 tiles, ragged tokens
+    (0, 3, 256, 256, 0.0, 0.0),         # every group empty: dB written as zeros
 ]
 
 
@@ -554,3 +556,20 @@ def test_pad_to_max_bit_exact(gpu, T, E, k, C):
     rows = np.nonzero(p["src_token"] >= 0)[0]
     want[rows] = x[p["src_token"][rows]]
     assert torch.equal(xp.cpu(), want)
+
+
+@pytest.mark.parametrize("M,G,K,N", [(3000, 7, 768, 512), (1000, 5, 256, 384), (5, 3, 256, 256)])
+def test_wgrad_bf16_accumulate(gpu, M, G, K, N):
+    """bf16 dB accumulated in place (read, add in fp32, one rounding): both the
+    256 x 256 weight-gradient tiles (K, N multiples of 256) and the general
+    ones; a group with no rows keeps its previous dB."""
+    off, A, _, dC = _gemm_inputs(M, G, K, N, 0.3, 0.5, torch.bfloat16, seed=4)
+    base = (torch.randn((G, K, N), generator=torch.Generator().manual_seed(9)) * 0.1).to(torch.bfloat16)
+    dB = base.to(DEV)
+    abi.moe_grouped_gemm_wgrad(A.to(DEV), dC.to(DEV), off.to(DEV), dB, accumulate=True)
+    ref = np64(base) + oracle.grouped_gemm_wgrad(np64(A), np64(dC), off.numpy())
+    assert_close("dB += A^T dC (bf16)", dB, ref, TOL["bf16"])
+    o = off.numpy()
+    for g in range(G):
+        if o[g + 1] == o[g]:
+            assert torch.equal(dB[g].cpu(), base[g]), g
