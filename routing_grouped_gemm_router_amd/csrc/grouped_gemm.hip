@@ -1033,22 +1033,25 @@ static hipError_t run_rows(const Params& p, hipStream_t s) {
   return run_cfg<MODE, Q, 2>(p, mt * (p.Nout / 128), s);
 }
 
-// ---- bf16 weight gradient, 256 x 256 tiles -----------------------------------
+// ---- weight gradient, 256 x 256 tiles ---------------------------------------
 // dB[g] = A[rows g]^T . dC[rows g] with both output dimensions multiples of
 // 256 (no ragged output dimension, so the larger tile wastes nothing): 8 waves
 // in a 4 x 2 arrangement, each 64 x 128 (2 x 4 MFMA 32x32 blocks), a 2-stage
-// ring of 64 KiB stages (A: 64 tokens x 256 columns, B the same, both in the
-// [k][col] layout read with ds_read_b64_tr_b16).  Against the 128 x 256 tile
-// this halves the per-tile work of decoding, loader set-up and epilogue
-// synchronisation per FLOP (a group's token range is short, so a tile is a
-// few k steps), reads a quarter fewer LDS fragments per MFMA, and re-reads the
-// activation slabs a quarter less.
+// ring of 64 KiB operand stages.  bf16: A is 64 tokens x 256 columns, B the
+// same, both in the [k][col] layout read with ds_read_b64_tr_b16.  fp8 / MX:
+// the transposed token tiles, 256 rows x 128 tokens each in the [row][k]
+// layout, plus one scale (fp32) or E8M0 dword per row and stage.  Against the
+// 128 x 256 tile this halves the per-tile work of decoding, loader set-up and
+// epilogue synchronisation per FLOP (a group's token range is short, so a
+// tile is a few k steps), reads a quarter fewer LDS fragments per MFMA, and
+// re-reads the activation slabs a quarter less.
 namespace w256 {
 constexpr int BMN = 256;           // tile rows (dB rows) and columns
-constexpr int SLAB = 16384;        // [64 k][128 cols] bf16
-constexpr int STAGE = 4 * SLAB;    // A: 2 slabs, B: 2 slabs
+constexpr int SLAB = 16384;        // bf16 [64 k][128 cols]; fp8 [128 rows][128 k]
+constexpr int OPS = 4 * SLAB;      // A: 2 slabs, B: 2 slabs
+constexpr int SCALES = 2048;       // fp8 / MX: 256 + 256 per-row scale words
+template <int Q> constexpr int stage_bytes() { return OPS + (Q == P_BF16 ? 0 : SCALES); }
 constexpr int STAGES = 2;
-constexpr int PER = 8;             // DMA instructions per wave per stage
 }
 
 // [32 m][128 n] bf16 staging rows of 256 B, 16-byte chunks swizzled by m & 15
@@ -1056,8 +1059,11 @@ __device__ __forceinline__ int stg_off16(int m, int chunk) {
   return m * 256 + ((chunk ^ (m & 15)) << 4);
 }
 
+template <int Q>
 __global__ __launch_bounds__(512, 1) void wgrad256_kernel(Params p) {
   using namespace w256;
+  constexpr bool F8 = Q != P_BF16;
+  constexpr int STAGE = stage_bytes<Q>();
   __shared__ __attribute__((aligned(1024))) char ring[STAGES * STAGE];
   __shared__ int s_off[MAX_GROUPS + 1];
   LDS_AS char* lring = (LDS_AS char*)(ring);
@@ -1105,29 +1111,61 @@ __global__ __launch_bounds__(512, 1) void wgrad256_kernel(Params p) {
     t.col0 = static_cast<int64_t>(n) * BMN;
     t.lo = s_off[t.g];
     t.nrows = s_off[t.g + 1] - t.lo;
-    t.nk = t.nrows > 0 ? static_cast<int>((t.nrows + 63) / 64) : 1;
+    t.nk = t.nrows > 0 ? static_cast<int>((t.nrows + KStep<F8>::value - 1) / KStep<F8>::value) : 1;
   };
   // loader of a tile: DMA instruction q = wave * 4 + i of each operand fills
-  // 1 KiB of slab q / 16 (k rows 4 (q % 16) .. + 3, 256 bytes each)
-  i32x4_t ra, rb;
-  uint32_t va[4], vb[4];
+  // 1 KiB of slab q / 16 -- bf16: k rows 4 (q % 16) .. + 3 (256 bytes each);
+  // fp8: rows 8 (q % 16) .. + 7 (128 bytes each) -- and, fp8 / MX, one scale
+  // word per row: waves 0-3 the 256 rows of A, waves 4-7 those of B
+  i32x4_t ra, rb, rs;
+  uint32_t va[4], vb[4], vs = 0, ds = 0;
+  const int64_t ldm = p.ldm;
   auto setup = [&](const T256& t) {
-    ra = make_rsrc(p.A + t.lo * K * 2, static_cast<uint64_t>(t.nrows) * K * 2);
-    rb = make_rsrc(p.B + t.lo * N * 2, static_cast<uint64_t>(t.nrows) * N * 2);
+    if (!F8) {
+      ra = make_rsrc(p.A + t.lo * K * 2, static_cast<uint64_t>(t.nrows) * K * 2);
+      rb = make_rsrc(p.B + t.lo * N * 2, static_cast<uint64_t>(t.nrows) * N * 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = wave * 4 + i, slab = q >> 4;
+        const int kr = 4 * (q & 15) + (lane >> 4), c = (lane & 15) ^ swz_nc(kr);
+        va[i] = static_cast<uint32_t>((kr * K + t.row0 + slab * 128 + 8 * c) * 2);
+        vb[i] = static_cast<uint32_t>((kr * N + t.col0 + slab * 128 + 8 * c) * 2);
+      }
+      return;
+    }
+    // A = X^T codes [K, ldm], B = dC^T codes [N, ldm]: the tile's 256 rows,
+    // contraction over the group's padded token range [lo, lo + nrows)
+    const bool any = t.nrows > 0;
+    ra = make_rsrc(p.A + t.row0 * ldm + t.lo, any ? static_cast<uint64_t>(BMN) * ldm : 0);
+    rb = make_rsrc(p.B + t.col0 * ldm + t.lo, any ? static_cast<uint64_t>(BMN) * ldm : 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int q = wave * 4 + i, slab = q >> 4;
-      const int kr = 4 * (q & 15) + (lane >> 4), c = (lane & 15) ^ swz_nc(kr);
-      va[i] = static_cast<uint32_t>((kr * K + t.row0 + slab * 128 + 8 * c) * 2);
-      vb[i] = static_cast<uint32_t>((kr * N + t.col0 + slab * 128 + 8 * c) * 2);
+      const int r = 8 * (q & 15) + (lane >> 3), c = (lane & 7) ^ swz_kc(r);
+      va[i] = static_cast<uint32_t>((slab * 128 + r) * ldm + c * 16);
+      vb[i] = va[i];
+    }
+    const bool for_a = wave < 4;
+    const int64_t row = (for_a ? t.row0 : t.col0) + (wave & 3) * 64 + lane;
+    if (Q == P_MX) {  // E8M0 [K][ldm/32] / [N][ldm/32]: dword lo/128 + kt of each row
+      rs = make_rsrc(for_a ? p.ea : p.eb, static_cast<uint64_t>(for_a ? K : N) * (ldm / 32));
+      vs = static_cast<uint32_t>(row * (ldm / 32) + t.lo / 32);
+      ds = 4;
+    } else {  // fp32 [ldm/128][K] / [ldm/128][N]: block lo/128 + kt
+      const int64_t W = for_a ? K : N;
+      rs = make_rsrc(for_a ? p.sa : p.sb, static_cast<uint64_t>(ldm / 128) * W * 4);
+      vs = static_cast<uint32_t>(((t.lo / 128) * W + row) * 4);
+      ds = static_cast<uint32_t>(W * 4);
     }
   };
-  const uint32_t da = static_cast<uint32_t>(64 * K * 2), db = static_cast<uint32_t>(64 * N * 2);
+  const uint32_t da = F8 ? 128u : static_cast<uint32_t>(64 * K * 2);
+  const uint32_t db = F8 ? 128u : static_cast<uint32_t>(64 * N * 2);
   auto issue = [&](int kt, LDS_AS char* stage) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma16(ra, stage + (wave * 4 + i) * 1024, va[i] + kt * da);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma16(rb, stage + 2 * SLAB + (wave * 4 + i) * 1024, vb[i] + kt * db);
+    if (F8) dma4(rs, stage + OPS + wave * 256, vs + kt * ds);
   };
 
   const Walk walk = make_walk(total);
@@ -1181,18 +1219,81 @@ __global__ __launch_bounds__(512, 1) void wgrad256_kernel(Params p) {
       const LDS_AS char* stage = lring + cp_slot * STAGE;
       const LDS_AS char* opA = stage + (wm >> 1) * SLAB;
       const LDS_AS char* opB = stage + 2 * SLAB + wn * SLAB;
+      const int ra0 = (wm & 1) * 64;  // the wave's first row inside its A slab
+      if (Q == P_BF16) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        bf16x8_t a[2], b[4];
+        for (int kk = 0; kk < 4; ++kk) {
+          bf16x8_t a[2], b[4];
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii) a[ii] = frag_nc(opA, (wm & 1) * 64 + ii * 32, kk * 16, lane);
+          for (int ii = 0; ii < 2; ++ii) a[ii] = frag_nc(opA, ra0 + ii * 32, kk * 16, lane);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) b[jj] = frag_nc(opB, jj * 32, kk * 16, lane);
+          for (int jj = 0; jj < 4; ++jj) b[jj] = frag_nc(opB, jj * 32, kk * 16, lane);
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii)
+          for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
-            acc[ii][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[jj], a[ii], acc[ii][jj], 0, 0, 0);
+            for (int jj = 0; jj < 4; ++jj)
+              acc[ii][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[jj], a[ii], acc[ii][jj], 0, 0, 0);
+        }
+      } else if (Q == P_MX) {
+        // scale words: A rows at 0.., B rows at 256..; see compute_stage_mx
+        const LDS_AS uint32_t* eA = (const LDS_AS uint32_t*)(stage + OPS);
+        const int h = lane >> 5;
+        uint32_t xa[2], xb[4];
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) xa[ii] = eA[wm * 64 + ii * 32 + (lane & 31)] >> (8 * h);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) xb[jj] = eA[256 + wn * 128 + jj * 32 + (lane & 31)] >> (8 * h);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          i32x8_t a[2], b[4];
+#pragma unroll
+          for (int ii = 0; ii < 2; ++ii) a[ii] = frag_mx(opA, ra0 + ii * 32 + (lane & 31), s2, h);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) b[jj] = frag_mx(opB, jj * 32 + (lane & 31), s2, h);
+#pragma unroll
+          for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+              acc[ii][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  b[jj], a[ii], acc[ii][jj], 0, 0, 0, static_cast<int>(xb[jj] >> (16 * s2)), 0,
+                  static_cast<int>(xa[ii] >> (16 * s2)));
+        }
+      } else {
+        // fp8 with fp32 scales: each 64-k MFMA partial promoted into the
+        // accumulator times the row scale of A and the column scale of B
+        const LDS_AS float* sA = (const LDS_AS float*)(stage + OPS);
+        const LDS_AS float* sB = sA + 256;
+        const int h = lane >> 5;
+        float sa[2];
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) sa[ii] = sA[wm * 64 + ii * 32 + (lane & 31)];
+#pragma unroll 1
+        for (int s2 = 0; s2 < 2; ++s2) {
+          i32x8_t a[2];
+#pragma unroll
+          for (int ii = 0; ii < 2; ++ii) a[ii] = frag_kc8(opA, ra0 + ii * 32 + (lane & 31), 4 * s2 + 2 * h);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const i32x8_t b = frag_kc8(opB, jj * 32 + (lane & 31), 4 * s2 + 2 * h);
+            f32x4 sb[4];
+#pragma unroll
+            for (int vg = 0; vg < 4; ++vg)
+              sb[vg] = *(const LDS_AS f32x4*)(sB + wn * 128 + jj * 32 + vg * 8 + h * 4);
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii) {
+              f32x16_t part;
+#pragma unroll
+              for (int v = 0; v < 16; ++v) part[v] = 0.f;
+              part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a[ii], part, 0, 0, 0, 127, 0,
+                                                                     127);
+#pragma unroll
+              for (int vg = 0; vg < 4; ++vg)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  acc[ii][jj][vg * 4 + e] += part[vg * 4 + e] * (sa[ii] * sb[vg][e]);
+            }
+          }
+        }
       }
     }
     if (++cp_kt == cp_t.nk) {
@@ -1277,12 +1378,14 @@ __global__ __launch_bounds__(512, 1) void wgrad256_kernel(Params p) {
 
 template <int Q>
 static hipError_t run_wgrad(const Params& p, hipStream_t s) {
-  if (Q == P_BF16 && p.Kc % w256::BMN == 0 && p.Nout % w256::BMN == 0) {
+  // (fp8 with fp32 scales keeps the 128-row tiles: its VALU promotion needs
+  // a whole extra accumulator block live, more registers than a wave has)
+  if (Q != P_FP8 && p.Kc % w256::BMN == 0 && p.Nout % w256::BMN == 0) {
     const int64_t tiles = static_cast<int64_t>(p.G) * (p.Kc / w256::BMN) * (p.Nout / w256::BMN);
     if (tiles <= 0) return hipSuccess;
     int64_t grid = cu_count();  // persistent, one workgroup per CU
     if (tiles < grid) grid = tiles;
-    wgrad256_kernel<<<dim3(static_cast<unsigned>(grid)), 512, 0, s>>>(p);
+    wgrad256_kernel<Q == P_MX ? P_MX : P_BF16><<<dim3(static_cast<unsigned>(grid)), 512, 0, s>>>(p);
     return hipGetLastError();
   }
   const int64_t mt = static_cast<int64_t>(p.G) * (p.Kc / BM);
