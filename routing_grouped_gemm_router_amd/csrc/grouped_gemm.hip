@@ -245,6 +245,9 @@ struct Params {
   // dH' and gate_part[row, c] = sum over the 64 columns 64c.. of dH' * h.
   const float* row_scale;
   float* gate_part;
+  // plain bf16 forward / dgrad: the 256-row and the 128-row kernels are both
+  // launched and rows256_preferred picks the one that does the work
+  int pair256;
 };
 
 // What a tile is: a ragged row block x 128 columns of one group (forward,
@@ -277,6 +280,23 @@ __device__ __forceinline__ void tile_in_group(uint32_t tl, uint32_t mt_g, uint32
   const uint32_t cw = min(SN, NT - chunk * SN);
   m = blk * SM + rr / cw;
   n = chunk * SN + rr % cw;
+}
+
+// Of a paired launch, the 256 x 256 tiling does the work when it needs at most
+// 20/31 of the row tiles of the 128-row tiling.  A 256 x 256 tile costs about
+// 1.8 times a 128 x 256 one and its ragged last tile rather less (a wave with
+// no rows idles); over 256 groups with 7168 x 2048 and 4096 x 7168 weights the
+// 256-row tiling measured faster at every tile ratio from 1.59 up and slower
+// at 1.5 and below.
+__device__ __forceinline__ bool rows256_preferred(int t128, int t256) {
+  return 20LL * t128 >= 31LL * t256;
+}
+
+// sum over the 64 lanes of a wave
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
 }
 
 template <int MODE, bool F8, int BN>
@@ -877,6 +897,7 @@ __global__ __launch_bounds__(Cfg<WN>::THREADS, Cfg<WN>::WG_PER_CU) void gg_kerne
   __shared__ __attribute__((aligned(1024))) char ring[C::STAGES * SB];
   __shared__ int s_pre[MAX_GROUPS + 1];
   __shared__ int s_off[MAX_GROUPS + 1];  // row offsets (below 2^31)
+  __shared__ int s_t256;                 // row tiles of the 256-row tiling
   LDS_AS char* lring = (LDS_AS char*)(ring);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -928,8 +949,16 @@ __global__ __launch_bounds__(Cfg<WN>::THREADS, Cfg<WN>::WG_PER_CU) void gg_kerne
         run += (s_off[g + 1] - s_off[g] + BM - 1) / BM;
       }
       if (lane == 63) s_pre[p.G] = incl;
+      if (MODE == FWD || MODE == DGRAD) {
+        int t256 = 0;
+        for (int g = g0; g < g1; ++g) t256 += (s_off[g + 1] - s_off[g] + 255) / 256;
+        t256 = wave_sum(t256);
+        if (lane == 0) s_t256 = t256;
+      }
     }
     __syncthreads();
+    if ((MODE == FWD || MODE == DGRAD) && p.pair256 && rows256_preferred(s_pre[p.G], s_t256))
+      return;  // the paired 256-row launch does the work
     NT = p.Nout / BN;
     total = static_cast<int64_t>(s_pre[p.G]) * NT;
   }
@@ -1023,12 +1052,28 @@ static hipError_t run_cfg(const Params& p, int64_t tiles_upper_bound, hipStream_
   return hipGetLastError();
 }
 
+// bf16 forward / dgrad without epilogue in 256 x 256 tiles (defined below);
+// false when the shape does not fit them
+template <int MODE>
+static bool launch_rows256(const Params& p, hipStream_t s, hipError_t& err);
+
 // Row-group modes: tiles of BM rows of a group x BN product columns (SwiGLU:
 // BN/2 gate + BN/2 up columns); at most M/BM + G row tiles.  The wide tile
 // whenever the product width allows it.
 template <int MODE, int Q>
 static hipError_t run_rows(const Params& p, hipStream_t s) {
   const int64_t mt = p.M / BM + p.G;
+  if constexpr (Q == P_BF16 && (MODE == FWD || MODE == DGRAD)) {
+    // both tilings are launched; from the group sizes each kernel finds on
+    // the device which of the two does the work, and the other one exits
+    Params q = p;
+    q.pair256 = 1;
+    hipError_t err = hipSuccess;
+    if (launch_rows256<MODE>(q, s, err)) {
+      if (err != hipSuccess) return err;
+      return run_cfg<MODE, Q, 4>(q, mt * (p.Nout / 256), s);
+    }
+  }
   if (p.Nout % 256 == 0) return run_cfg<MODE, Q, 4>(p, mt * (p.Nout / 256), s);
   return run_cfg<MODE, Q, 2>(p, mt * (p.Nout / 128), s);
 }
@@ -1374,6 +1419,267 @@ __global__ __launch_bounds__(512, 1) void wgrad256_kernel(Params p) {
     cp_slot ^= 1;
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// ---- bf16 row-group GEMMs (forward, dgrad), 256 x 256 tiles ------------------
+// The forward (B = W_g [K, N] read in the [k][col] layout) and the data
+// gradient (B = W_g [N, K] rows, k-contiguous) in tiles of 256 rows of a group
+// x 256 product columns, waves and ring as in the weight-gradient kernel.  A
+// group's last row tile is ragged (its rows past the group read as zero, so
+// nothing is fetched for them); the larger tile halves the row tiles of a
+// large group, hence its re-reads of the weight slabs, and moves a third
+// fewer operand bytes per FLOP into LDS.
+template <int MODE>
+__global__ __launch_bounds__(512, 1) void rows256_kernel(Params p) {
+  using namespace w256;
+  constexpr int STAGE = OPS;
+  constexpr bool B_NC = MODE == FWD || MODE == FWD_SWIGLU;
+  __shared__ __attribute__((aligned(1024))) char ring[STAGES * STAGE];
+  __shared__ int s_pre[MAX_GROUPS + 1];
+  __shared__ int s_off[MAX_GROUPS + 1];
+  __shared__ int s_t128;  // row tiles of the 128-row tiling
+  LDS_AS char* lring = (LDS_AS char*)(ring);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  for (int g = tid; g <= p.G; g += 512) s_off[g] = static_cast<int>(clamp64(p.off[g], 0, p.M));
+  __syncthreads();
+  if (wave == 0) {  // running maximum makes the offsets non-decreasing
+    const int per = (p.G + 1 + 63) / 64;
+    const int g0 = lane * per, g1 = min(p.G + 1, g0 + per);
+    int mx = 0;
+    for (int g = g0; g < g1; ++g) mx = max(mx, s_off[g]);
+    int incl = mx;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl = max(incl, y);
+    }
+    int run = __shfl_up(incl, 1, 64);
+    if (lane == 0) run = 0;
+    for (int g = g0; g < g1; ++g) {
+      run = max(run, s_off[g]);
+      s_off[g] = run;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {  // row-tile prefix of the groups
+    const int per = (p.G + 63) / 64;
+    const int g0 = lane * per, g1 = min(p.G, g0 + per);
+    int sum = 0;
+    for (int g = g0; g < g1; ++g) sum += (s_off[g + 1] - s_off[g] + BMN - 1) / BMN;
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    int run = incl - sum;
+    for (int g = g0; g < g1; ++g) {
+      s_pre[g] = run;
+      run += (s_off[g + 1] - s_off[g] + BMN - 1) / BMN;
+    }
+    if (lane == 63) s_pre[p.G] = incl;
+    int t128 = 0;
+    for (int g = g0; g < g1; ++g) t128 += (s_off[g + 1] - s_off[g] + BM - 1) / BM;
+    t128 = wave_sum(t128);
+    if (lane == 0) s_t128 = t128;
+  }
+  __syncthreads();
+  if (p.pair256 && !rows256_preferred(s_t128, s_pre[p.G])) return;  // the 128-row launch works
+
+  const uint32_t NT = static_cast<uint32_t>(p.Nout / BMN);
+  const int64_t total = static_cast<int64_t>(s_pre[p.G]) * NT;
+  const int64_t Kc = p.Kc, N = p.Nout;
+  const int nk = static_cast<int>(Kc / 64);
+
+  struct TR {
+    int g;
+    int64_t row0, col0;
+    int rows;
+  };
+  auto decode = [&](int64_t tau64, TR& t) {
+    const uint32_t tau = static_cast<uint32_t>(tau64);
+    int glo = 0, ghi = p.G;
+    while (ghi - glo > 1) {
+      const int mid = (glo + ghi) >> 1;
+      if (static_cast<uint32_t>(s_pre[mid]) * NT <= tau) glo = mid; else ghi = mid;
+    }
+    const int g = __builtin_amdgcn_readfirstlane(glo);
+    t.g = g;
+    const uint32_t base = static_cast<uint32_t>(s_pre[g]);
+    const uint32_t mt_g = static_cast<uint32_t>(s_pre[g + 1]) - base;
+    uint32_t m, n;
+    tile_in_group<ROW_SN>(tau - base * NT, mt_g, NT, mt_g, m, n);
+    const int64_t lo = s_off[g], hi = s_off[g + 1];
+    t.row0 = lo + static_cast<int64_t>(m) * BMN;
+    t.col0 = static_cast<int64_t>(n) * BMN;
+    t.rows = static_cast<int>(min<int64_t>(BMN, hi - t.row0));
+  };
+  i32x4_t ra, rb;
+  uint32_t va[4], vb[4];
+  auto setup = [&](const TR& t) {
+    ra = make_rsrc(p.A + t.row0 * Kc * 2, static_cast<uint64_t>(t.rows) * Kc * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // A: rows 8 (q % 16) .. + 7 of slab q / 16
+      const int q = wave * 4 + i, slab = q >> 4;
+      const int r = 8 * (q & 15) + (lane >> 3), c = (lane & 7) ^ swz_kc(r);
+      va[i] = static_cast<uint32_t>((slab * 128 + r) * Kc * 2 + c * 16);
+    }
+    if (B_NC) {  // W_g [Kc, N]: k rows 4 (q % 16) .. + 3, columns col0 + 128 slab ..
+      rb = make_rsrc(p.B + static_cast<int64_t>(t.g) * Kc * N * 2, static_cast<uint64_t>(Kc) * N * 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = wave * 4 + i, slab = q >> 4;
+        const int kr = 4 * (q & 15) + (lane >> 4), c = (lane & 15) ^ swz_nc(kr);
+        vb[i] = static_cast<uint32_t>((kr * N + t.col0 + slab * 128 + 8 * c) * 2);
+      }
+    } else {  // W_g [N, Kc]: rows col0 + 128 slab + 8 (q % 16) ..
+      rb = make_rsrc(p.B + static_cast<int64_t>(t.g) * N * Kc * 2, static_cast<uint64_t>(N) * Kc * 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = wave * 4 + i, slab = q >> 4;
+        const int r = 8 * (q & 15) + (lane >> 3), c = (lane & 7) ^ swz_kc(r);
+        vb[i] = static_cast<uint32_t>((t.col0 + slab * 128 + r) * Kc * 2 + c * 16);
+      }
+    }
+  };
+  const uint32_t da = 128u, db = B_NC ? static_cast<uint32_t>(64 * N * 2) : 128u;
+  auto issue = [&](int kt, LDS_AS char* stage) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(ra, stage + (wave * 4 + i) * 1024, va[i] + kt * da);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(rb, stage + 2 * SLAB + (wave * 4 + i) * 1024, vb[i] + kt * db);
+  };
+
+  const Walk walk = make_walk(total);
+  int ld_i = 0, cp_i = 0;
+  int64_t ld_tau = 0;
+  TR ld_t, cp_t;
+  bool ld_ok = walk_next(walk, ld_i, total, ld_tau);
+  if (ld_ok) {
+    decode(ld_tau, ld_t);
+    setup(ld_t);
+  }
+  bool cp_ok = ld_ok;
+  cp_t = ld_t;
+  cp_i = ld_i;
+  int ld_kt = 0, cp_kt = 0, ld_slot = 0, cp_slot = 0;
+  auto advance_loader = [&]() {
+    ld_slot ^= 1;
+    if (++ld_kt == nk) {
+      ld_kt = 0;
+      ++ld_i;
+      ld_ok = walk_next(walk, ld_i, total, ld_tau);
+      if (ld_ok) {
+        decode(ld_tau, ld_t);
+        setup(ld_t);
+      }
+    }
+  };
+  if (ld_ok) {
+    issue(ld_kt, lring + ld_slot * STAGE);
+    advance_loader();
+  }
+
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[ii][jj][v] = 0.f;
+
+  while (cp_ok) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (ld_ok) {
+      issue(ld_kt, lring + ld_slot * STAGE);
+      advance_loader();
+    }
+    if (cp_t.rows > wm * 64) {  // a wave whose 64 rows all lie past the group idles
+      const LDS_AS char* stage = lring + cp_slot * STAGE;
+      const LDS_AS char* opA = stage + (wm >> 1) * SLAB;
+      const LDS_AS char* opB = stage + 2 * SLAB + wn * SLAB;
+      const int ra0 = (wm & 1) * 64;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        bf16x8_t a[2], b[4];
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii)
+          a[ii] = frag_kc(opA, ra0 + ii * 32 + (lane & 31), kk * 2 + (lane >> 5));
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          b[jj] = B_NC ? frag_nc(opB, jj * 32, kk * 16, lane)
+                       : frag_kc(opB, jj * 32 + (lane & 31), kk * 2 + (lane >> 5));
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            acc[ii][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[jj], a[ii], acc[ii][jj], 0, 0, 0);
+      }
+    }
+    if (++cp_kt == nk) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const int rows_w = cp_t.rows - wm * 64;  // valid rows of this wave
+      if (rows_w > 0) {
+        LDS_AS char* stg = lring + cp_slot * STAGE + wave * 8192;
+        bf16_t* out = static_cast<bf16_t*>(p.C);
+        const int64_t row_w = cp_t.row0 + wm * 64, col_w = cp_t.col0 + wn * 128;
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+          if (ii * 32 >= rows_w) break;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int vg = 0; vg < 4; ++vg) {
+              const int m = lane & 31;
+              const int n = jj * 32 + vg * 8 + (lane >> 5) * 4;
+              u32x2_t w;
+              w.x = pack2(acc[ii][jj][vg * 4 + 0], acc[ii][jj][vg * 4 + 1]);
+              w.y = pack2(acc[ii][jj][vg * 4 + 2], acc[ii][jj][vg * 4 + 3]);
+              *(LDS_AS u32x2_t*)(stg + stg_off16(m, n >> 3) + (n & 7) * 2) = w;
+            }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int idx = lane + 64 * i;
+            const int m = idx >> 4, c = idx & 15;
+            if (ii * 32 + m >= rows_w) continue;
+            const u32x4_t vv = *(const LDS_AS u32x4_t*)(stg + stg_off16(m, c));
+            *reinterpret_cast<u32x4_t*>(out + (row_w + ii * 32 + m) * N + col_w + 8 * c) = vv;
+          }
+        }
+      }
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[ii][jj][v] = 0.f;
+      cp_kt = 0;
+      ++cp_i;
+      int64_t cp_tau = 0;
+      cp_ok = walk_next(walk, cp_i, total, cp_tau);
+      if (cp_ok) decode(cp_tau, cp_t);
+    }
+    cp_slot ^= 1;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <int MODE>
+static bool launch_rows256(const Params& p, hipStream_t s, hipError_t& err) {
+  if (p.Nout % w256::BMN != 0 || p.Kc % 64 != 0 || p.Kc < 64 || !p.pair256) return false;
+  const int64_t tiles = (p.M / w256::BMN + p.G) * (p.Nout / w256::BMN);
+  int64_t grid = cu_count();  // persistent, one workgroup per CU
+  if (tiles < grid) grid = tiles;
+  if (grid < 1) grid = 1;
+  rows256_kernel<MODE><<<dim3(static_cast<unsigned>(grid)), 512, 0, s>>>(p);
+  err = hipGetLastError();
+  return true;
 }
 
 template <int Q>

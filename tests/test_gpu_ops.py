@@ -203,6 +203,7 @@ GEMM_CASES = [
     (20000, 40, 256, 1024, 0.2, 1.0),   # many tiles per workgroup, skewed, empty groups
     (3000, 7, 768, 512, 0.3, 0.5),      # weight gradient in 256 x 256 tiles, ragged tokens
     (0, 3, 256, 256, 0.0, 0.0),         # every group empty: dB written as zeros
+    (6001, 5, 256, 512, 0.2, 0.5),      # several 256-row tiles per group, ragged tails
 ]
 
 
