@@ -179,16 +179,17 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const TA* __restrict__ A,
 
 
 // ---- router GEMMs: one wave per 64 x 64 output tile ---------------------------
-// The router projection and its two backward products (fp32 VALU, no packed
-// fp32): lane (tx, ty) = (lane & 7, lane >> 3) of a wave owns rows
-// {4ty..4ty+3, 32+4ty..} x columns {4tx..4tx+3, 32+4tx..} of its tile, 64 FMAs
-// per k for four 16-byte LDS reads.  Each wave stages its own 16-deep operand
-// slices in its own 8 KiB of LDS and prefetches the next slice into registers
-// while it computes, so the main loop has no workgroup barrier.  SK = 8: the
-// workgroup's 8 waves split the contraction of one tile and add their partial
-// sums through LDS in wave order (deterministic, no workspace); SK = 1: the 8
-// waves take 8 tiles.  Requires 16-byte aligned operands, the A and B
-// contiguous extents multiples of 8 (bf16) or 4 (fp32) elements.
+// The router projection and its two backward products on the fp32 matrix
+// cores (MFMA 32x32x2 fp32: fp32 products and sums, twice the rate of
+// unpacked fp32 FMAs): a wave owns a 64 x 64 tile as 2 x 2 MFMA blocks.  Each
+// wave stages its own 16-deep operand slices in its own 8 KiB of LDS as
+// [k][64] and prefetches the next slice into registers while it computes, so
+// the main loop has no workgroup barrier.  SK = 8: the workgroup's 8 waves
+// split the contraction of one tile and add their partial sums through LDS in
+// wave order (deterministic, no workspace); SK = 1: the 8 waves take 8 tiles.
+// Requires 16-byte aligned operands, the A and B contiguous extents multiples
+// of 8 (bf16) or 4 (fp32) elements.
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 enum { RA_KC_BF16 = 0, RA_KC_F32 = 1, RA_MC_BF16 = 2, RA_MC_F32 = 3 };  // A: k- or m-contiguous
 enum { RB_NC = 0, RB_KC = 1 };                                          // B (fp32): n- or k-contiguous
 
@@ -295,7 +296,6 @@ __global__ __launch_bounds__(512) void router_gemm_kernel(const void* __restrict
                                                           const float* __restrict__ bias) {
   __shared__ __attribute__((aligned(16))) float lds[8][2][16][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tx = lane & 7, ty = lane >> 3;
   const int64_t ntn = (N + 63) / 64;
   const int64_t tile = SK > 1 ? static_cast<int64_t>(blockIdx.x)
                               : static_cast<int64_t>(blockIdx.x) * 8 + wave;
@@ -308,55 +308,63 @@ __global__ __launch_bounds__(512) void router_gemm_kernel(const void* __restrict
   }
   float(*As)[64] = lds[wave][0];
   float(*Bs)[64] = lds[wave][1];
-  float acc[8][8];
+  // MFMA 32x32x2 fp32, computed as D[n][m] so that lane r of a block holds
+  // output row m = r: acc[mi][ni][v] is C[32 mi + r][32 ni + 8 (v / 4) +
+  // 4 h + v % 4], h = lane / 32.  Lane half h feeds contraction positions
+  // 8 h .. 8 h + 7 of each 16-deep slice, one per MFMA, for A and for B alike.
+  f32x16_t acc[2][2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
+  const int r = lane & 31, h = lane >> 5;
 
   if (m0 < M) {  // SK == 1: trailing waves of the last block may have no tile
-    RSlice r;
-    if (k_lo < k_hi) router_load<AL, BL>(r, A, lda, B, ldb, m0, n0, k_lo, k_hi, M, N, lane);
+    RSlice rs;
+    if (k_lo < k_hi) router_load<AL, BL>(rs, A, lda, B, ldb, m0, n0, k_lo, k_hi, M, N, lane);
     for (int64_t k0 = k_lo; k0 < k_hi; k0 += 16) {
-      router_stage<AL, BL>(r, As, Bs, lane);
+      router_stage<AL, BL>(rs, As, Bs, lane);
       __builtin_amdgcn_wave_barrier();
-      if (k0 + 16 < k_hi) router_load<AL, BL>(r, A, lda, B, ldb, m0, n0, k0 + 16, k_hi, M, N, lane);
+      if (k0 + 16 < k_hi) router_load<AL, BL>(rs, A, lda, B, ldb, m0, n0, k0 + 16, k_hi, M, N, lane);
 #pragma unroll
-      for (int kk = 0; kk < 16; ++kk) {
-        const float4 a0 = *reinterpret_cast<const float4*>(&As[kk][4 * ty]);
-        const float4 a1 = *reinterpret_cast<const float4*>(&As[kk][32 + 4 * ty]);
-        const float4 b0 = *reinterpret_cast<const float4*>(&Bs[kk][4 * tx]);
-        const float4 b1 = *reinterpret_cast<const float4*>(&Bs[kk][32 + 4 * tx]);
-        const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+      for (int i = 0; i < 8; ++i) {
+        const int kk = 8 * h + i;
+        const float a0 = As[kk][r], a1 = As[kk][32 + r];
+        const float b0 = Bs[kk][r], b1 = Bs[kk][32 + r];
+        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(b0, a0, acc[0][0], 0, 0, 0);
+        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(b1, a0, acc[0][1], 0, 0, 0);
+        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(b0, a1, acc[1][0], 0, 0, 0);
+        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(b1, a1, acc[1][1], 0, 0, 0);
       }
       __builtin_amdgcn_wave_barrier();
     }
   }
 
-  // row of acc[i] and column of acc[.][j] inside the tile
-  auto row_of = [&](int i) { return (i < 4 ? 4 * ty : 32 + 4 * ty) + (i & 3); };
-  auto col_of = [&](int h) { return (h == 0 ? 4 * tx : 32 + 4 * tx); };
+  // columns 32 ni + 8 g + 4 h .. + 3 of row 32 mi + r
+  auto quad = [&](int mi, int ni, int g) {
+    return make_float4(acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2],
+                       acc[mi][ni][4 * g + 3]);
+  };
   if (SK == 1) {
     if (m0 >= M) return;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t m = m0 + row_of(i);
+    for (int mi = 0; mi < 2; ++mi) {
+      const int64_t m = m0 + 32 * mi + r;
       if (m >= M) continue;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int64_t n = n0 + col_of(h);
-        if (n >= N) continue;
-        float4 v = make_float4(acc[i][4 * h], acc[i][4 * h + 1], acc[i][4 * h + 2], acc[i][4 * h + 3]);
-        if (BIAS) {
-          v.x += bias[n]; v.y += bias[n + 1]; v.z += bias[n + 2]; v.w += bias[n + 3];
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t n = n0 + 32 * ni + 8 * g + 4 * h;
+          if (n >= N) continue;
+          float4 v = quad(mi, ni, g);
+          if (BIAS) {
+            v.x += bias[n]; v.y += bias[n + 1]; v.z += bias[n + 2]; v.w += bias[n + 3];
+          }
+          *reinterpret_cast<float4*>(C + m * ldc + n) = v;
         }
-        *reinterpret_cast<float4*>(C + m * ldc + n) = v;
-      }
     }
     return;
   }
@@ -366,13 +374,10 @@ __global__ __launch_bounds__(512) void router_gemm_kernel(const void* __restrict
   for (int rnd = 0; rnd < 2; ++rnd) {
     __syncthreads();  // every wave is done with its slices / the previous round
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int i = 4 * rnd + ii;
+    for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        *reinterpret_cast<float4*>(part + (4 * ty + ii) * 64 + col_of(h)) =
-            make_float4(acc[i][4 * h], acc[i][4 * h + 1], acc[i][4 * h + 2], acc[i][4 * h + 3]);
-    }
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(part + r * 64 + 32 * ni + 8 * g + 4 * h) = quad(rnd, ni, g);
     __syncthreads();
     // thread t sums elements 4t .. 4t+3 of the 32 x 64 half over the waves in order
     const int e = 4 * static_cast<int>(threadIdx.x);
