@@ -6,11 +6,14 @@
 // Core", section 2, Dispatch (tokens permuted by destination expert) and
 // Combine (rows return to sequence order, weighted, plus a shared expert).
 //
-// Layout: one wavefront per token row, 16-byte vectors along the row, so each
-// instruction moves 1 KiB of one row.  The permutation is token-major: a token
-// row is read once and written to its k destinations (and the combine reads
-// its k rows and writes once), which is the algorithmic minimum of bytes.
-// Accumulation is fp32 with one rounding at the end.
+// Layout: 16-byte vectors along a row, 64 lanes of a wavefront side by side,
+// so each instruction moves 1 KiB of one row.  The permutation is
+// token-major: a token row is read once and written to its k destinations
+// (and the combine reads its k rows and writes once), which is the
+// algorithmic minimum of bytes.  Every load of a step (the k rows of a slot
+// batch, several vectors per lane) is issued before the first is used, so a
+// wave keeps many requests in flight.  Accumulation is fp32 with one rounding
+// at the end.
 #include "common.h"
 #include "internal.h"
 
@@ -48,33 +51,103 @@ template <> struct Vec<bf16_t> {
   }
 };
 
-__device__ __forceinline__ int64_t wave_token(int per_block) {
-  // the token handled by this wavefront, as a wave-uniform value
-  return __builtin_amdgcn_readfirstlane(static_cast<int64_t>(blockIdx.x) * per_block +
+// 16-byte loads and stores with the non-temporal hint: rows that are read
+// exactly once in a pass (the permuted rows in combine and the backward
+// gathers) stream past the caches instead of evicting reused lines.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Index of this wavefront in the grid (4 waves per 256-thread block), as a
+// wave-uniform value.
+__device__ __forceinline__ int64_t wave_index() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int64_t>(blockIdx.x) * 4 +
                                         (threadIdx.x >> 6));
 }
 
+// Work decomposition of the row kernels: a unit is one token and one chunk of
+// 64*U 16-byte vectors of its row (U per lane).  Chunks of one token are
+// adjacent units, so neighbouring waves read neighbouring pieces of the same
+// rows.  A wave takes units w, w + n_waves, ... (one each at the usual grid).
+struct RowChunks {
+  int64_t nvec, cpr, units;
+  __device__ __forceinline__ RowChunks(int64_t T_, int64_t d, int vn, int U) {
+    nvec = d / vn;
+    cpr = (nvec + 64 * U - 1) / (64 * U);
+    units = T_ * cpr;
+  }
+};
+
+static dim3 unit_grid(int64_t units) {
+  int64_t b = (units + 3) / 4;
+  if (b > (int64_t(1) << 30)) b = int64_t(1) << 30;  // the unit loop covers the rest
+  if (b < 1) b = 1;
+  return dim3(static_cast<unsigned>(b));
+}
+static int64_t host_units(int64_t T_, int64_t d, int vn, int U) {
+  const int64_t nvec = d / vn;
+  return T_ * ((nvec + 64 * U - 1) / (64 * U));
+}
+
+// xp[dst_row[t, j]] = x[t]: each chunk of x is loaded once (U vectors per
+// lane in flight) and stored to the token's k rows.
+constexpr int kPermuteU = 4;
 template <typename T>
 __global__ __launch_bounds__(256) void permute_kernel(const T* __restrict__ x,
                                                       const int32_t* __restrict__ dst_row, int64_t T_,
                                                       int64_t d, int k, int64_t nrows,
                                                       T* __restrict__ xp) {
-  const int64_t t = wave_token(4);
-  if (t >= T_) return;
+  constexpr int U = kPermuteU;
+  const RowChunks rc(T_, d, Vec<T>::N, U);
   const int lane = threadIdx.x & 63;
-  const int64_t nvec = d / Vec<T>::N;
-  const uint4* src = reinterpret_cast<const uint4*>(x + t * d);
-  for (int64_t v = lane; v < nvec; v += 64) {
-    const uint4 val = src[v];
+  const int64_t n_waves = static_cast<int64_t>(gridDim.x) * 4;
+  for (int64_t un = wave_index(); un < rc.units; un += n_waves) {
+    const int64_t t = un / rc.cpr, v0 = (un - t * rc.cpr) * 64 * U;
+    const uint4* src = reinterpret_cast<const uint4*>(x + t * d);
+    uint4 val[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + u * 64 + lane;
+      if (v < rc.nvec) val[u] = load_stream(src + v);
+    }
     for (int j = 0; j < k; ++j) {
       const int64_t r = dst_row[t * k + j];
-      if (r >= 0 && r < nrows) reinterpret_cast<uint4*>(xp + r * d)[v] = val;
+      if (r < 0 || r >= nrows) continue;
+      uint4* dst = reinterpret_cast<uint4*>(xp + r * d);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t v = v0 + u * 64 + lane;
+        if (v < rc.nvec) dst[v] = val[u];
+      }
     }
   }
 }
 
-// dx[t] = sum_j dxp[dst_row[t, j]] + addend[t] + addend_f32[t]
-template <typename T>
+// Rows of slots j0 .. j0+KB-1 of token t (wave-uniform; -1 for an absent or
+// dropped slot) and their weights (0 for those).
+template <int KB>
+__device__ __forceinline__ void slot_batch(const int32_t* __restrict__ dst_row,
+                                           const float* __restrict__ w, int64_t t, int k, int j0,
+                                           int64_t nrows, int64_t (&rr)[KB], float (&ww)[KB]) {
+#pragma unroll
+  for (int j = 0; j < KB; ++j) {
+    int64_t r = -1;
+    float wj = 0.f;
+    if (j0 + j < k) {
+      r = dst_row[t * k + j0 + j];
+      if (r < 0 || r >= nrows) r = -1;
+      else wj = w ? w[t * k + j0 + j] : 1.0f;
+    }
+    rr[j] = r;
+    ww[j] = wj;
+  }
+}
+
+// dx[t] = sum_j dxp[dst_row[t, j]] + addend[t] + addend_f32[t], fp32 sums in
+// slot order; the slots' rows are loaded KB at a time.
+template <typename T, int KB, int U>
 __global__ __launch_bounds__(256) void permute_bwd_kernel(const T* __restrict__ dxp,
                                                           const int32_t* __restrict__ dst_row,
                                                           int64_t T_, int64_t d, int k,
@@ -83,39 +156,67 @@ __global__ __launch_bounds__(256) void permute_bwd_kernel(const T* __restrict__ 
                                                           const float* __restrict__ addend_f32,
                                                           T* __restrict__ dx) {
   constexpr int VN = Vec<T>::N;
-  const int64_t t = wave_token(4);
-  if (t >= T_) return;
+  const RowChunks rc(T_, d, VN, U);
   const int lane = threadIdx.x & 63;
-  const int64_t nvec = d / VN;
-  for (int64_t v = lane; v < nvec; v += 64) {
-    float acc[VN] = {};
-    float tmp[VN];
-    for (int j = 0; j < k; ++j) {
-      const int64_t r = dst_row[t * k + j];
-      if (r < 0 || r >= nrows) continue;
-      Vec<T>::unpack(reinterpret_cast<const uint4*>(dxp + r * d)[v], tmp);
+  const int64_t n_waves = static_cast<int64_t>(gridDim.x) * 4;
+  for (int64_t un = wave_index(); un < rc.units; un += n_waves) {
+    const int64_t t = un / rc.cpr, v0 = (un - t * rc.cpr) * 64 * U;
+    float acc[U][VN];
 #pragma unroll
-      for (int i = 0; i < VN; ++i) acc[i] += tmp[i];
-    }
-    if (addend) {
-      Vec<T>::unpack(reinterpret_cast<const uint4*>(addend + t * d)[v], tmp);
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int i = 0; i < VN; ++i) acc[i] += tmp[i];
-    }
-    if (addend_f32) {
-      const float* a = addend_f32 + t * d + v * VN;
+      for (int i = 0; i < VN; ++i) acc[u][i] = 0.f;
+    for (int j0 = 0; j0 < k; j0 += KB) {
+      int64_t rr[KB];
+      float ww[KB];
+      slot_batch<KB>(dst_row, nullptr, t, k, j0, nrows, rr, ww);
+      uint4 val[KB][U];
 #pragma unroll
-      for (int i = 0; i < VN; i += 4) {
-        const float4 q = *reinterpret_cast<const float4*>(a + i);
-        acc[i] += q.x; acc[i + 1] += q.y; acc[i + 2] += q.z; acc[i + 3] += q.w;
+      for (int j = 0; j < KB; ++j)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t v = v0 + u * 64 + lane;
+          if (rr[j] >= 0 && v < rc.nvec)
+            val[j][u] = load_stream(reinterpret_cast<const uint4*>(dxp + rr[j] * d) + v);
+        }
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        if (rr[j] < 0) continue;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float tmp[VN];
+          Vec<T>::unpack(val[j][u], tmp);
+#pragma unroll
+          for (int i = 0; i < VN; ++i) acc[u][i] += tmp[i];
+        }
       }
     }
-    reinterpret_cast<uint4*>(dx + t * d)[v] = Vec<T>::pack(acc);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + u * 64 + lane;
+      if (v >= rc.nvec) continue;
+      if (addend) {
+        float tmp[VN];
+        Vec<T>::unpack(load_stream(reinterpret_cast<const uint4*>(addend + t * d) + v), tmp);
+#pragma unroll
+        for (int i = 0; i < VN; ++i) acc[u][i] += tmp[i];
+      }
+      if (addend_f32) {
+        const float4* a = reinterpret_cast<const float4*>(addend_f32 + t * d + v * VN);
+#pragma unroll
+        for (int i = 0; i < VN; i += 4) {
+          const float4 q = a[i / 4];
+          acc[u][i] += q.x; acc[u][i + 1] += q.y; acc[u][i + 2] += q.z; acc[u][i + 3] += q.w;
+        }
+      }
+      reinterpret_cast<uint4*>(dx + t * d)[v] = Vec<T>::pack(acc[u]);
+    }
   }
 }
 
-// out[t] = sum_j w[t, j] * y[dst_row[t, j]] + shared[t]  (w = 1 without topk_w)
-template <typename T>
+// out[t] = sum_j w[t, j] * y[dst_row[t, j]] + shared[t]  (w = 1 without
+// topk_w), fp32 sums in slot order, then the shared row, one rounding.
+template <typename T, int KB, int U>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y,
                                                       const float* __restrict__ topk_w,
                                                       const int32_t* __restrict__ dst_row,
@@ -123,37 +224,68 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y,
                                                       int64_t d, int k, int64_t nrows,
                                                       T* __restrict__ out) {
   constexpr int VN = Vec<T>::N;
-  const int64_t t = wave_token(4);
-  if (t >= T_) return;
+  const RowChunks rc(T_, d, VN, U);
   const int lane = threadIdx.x & 63;
-  const int64_t nvec = d / VN;
-  for (int64_t v = lane; v < nvec; v += 64) {
-    float acc[VN] = {};
-    float tmp[VN];
-    for (int j = 0; j < k; ++j) {
-      const int64_t r = dst_row[t * k + j];
-      if (r < 0 || r >= nrows) continue;
-      Vec<T>::unpack(reinterpret_cast<const uint4*>(y + r * d)[v], tmp);
-      if (topk_w) {
-        const float w = topk_w[t * k + j];
+  const int64_t n_waves = static_cast<int64_t>(gridDim.x) * 4;
+  for (int64_t un = wave_index(); un < rc.units; un += n_waves) {
+    const int64_t t = un / rc.cpr, v0 = (un - t * rc.cpr) * 64 * U;
+    uint4 sh[U];
+    if (shared) {
 #pragma unroll
-        for (int i = 0; i < VN; ++i) acc[i] += w * tmp[i];
-      } else {
-#pragma unroll
-        for (int i = 0; i < VN; ++i) acc[i] += tmp[i];
+      for (int u = 0; u < U; ++u) {
+        const int64_t v = v0 + u * 64 + lane;
+        if (v < rc.nvec) sh[u] = load_stream(reinterpret_cast<const uint4*>(shared + t * d) + v);
       }
     }
-    if (shared) {
-      Vec<T>::unpack(reinterpret_cast<const uint4*>(shared + t * d)[v], tmp);
+    float acc[U][VN];
 #pragma unroll
-      for (int i = 0; i < VN; ++i) acc[i] += tmp[i];
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < VN; ++i) acc[u][i] = 0.f;
+    for (int j0 = 0; j0 < k; j0 += KB) {
+      int64_t rr[KB];
+      float ww[KB];
+      slot_batch<KB>(dst_row, topk_w, t, k, j0, nrows, rr, ww);
+      uint4 val[KB][U];
+#pragma unroll
+      for (int j = 0; j < KB; ++j)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t v = v0 + u * 64 + lane;
+          if (rr[j] >= 0 && v < rc.nvec)
+            val[j][u] = load_stream(reinterpret_cast<const uint4*>(y + rr[j] * d) + v);
+        }
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        if (rr[j] < 0) continue;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float tmp[VN];
+          Vec<T>::unpack(val[j][u], tmp);
+#pragma unroll
+          for (int i = 0; i < VN; ++i) acc[u][i] += ww[j] * tmp[i];
+        }
+      }
     }
-    reinterpret_cast<uint4*>(out + t * d)[v] = Vec<T>::pack(acc);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + u * 64 + lane;
+      if (v >= rc.nvec) continue;
+      if (shared) {
+        float tmp[VN];
+        Vec<T>::unpack(sh[u], tmp);
+#pragma unroll
+        for (int i = 0; i < VN; ++i) acc[u][i] += tmp[i];
+      }
+      reinterpret_cast<uint4*>(out + t * d)[v] = Vec<T>::pack(acc[u]);
+    }
   }
 }
 
 // dy[dst_row[t, j]] = w[t, j] * dout[t];  d_w[t, j] = <dout[t], y[dst_row[t, j]]>
-template <typename T, int KMAX>
+// One wave per token (the dot products need the whole row); slots KB at a
+// time, U vectors per lane, every row load of a step issued before its use.
+template <typename T, int KB, int U>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ dout,
                                                           const T* __restrict__ y,
                                                           const float* __restrict__ topk_w,
@@ -162,38 +294,59 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ 
                                                           int64_t nrows, T* __restrict__ dy,
                                                           float* __restrict__ d_w) {
   constexpr int VN = Vec<T>::N;
-  const int64_t t = wave_token(4);
+  const int64_t t = wave_index();
   if (t >= T_) return;
   const int lane = threadIdx.x & 63;
   const int64_t nvec = d / VN;
-  float dot[KMAX];
+  const uint4* g_row = reinterpret_cast<const uint4*>(dout + t * d);
+  for (int j0 = 0; j0 < k; j0 += KB) {
+    int64_t rr[KB];
+    float ww[KB], dot[KB];
+    slot_batch<KB>(dst_row, topk_w, t, k, j0, nrows, rr, ww);
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) dot[j] = 0.f;
-  for (int64_t v = lane; v < nvec; v += 64) {
-    float g[VN], tmp[VN], o[VN];
-    Vec<T>::unpack(reinterpret_cast<const uint4*>(dout + t * d)[v], g);
+    for (int j = 0; j < KB; ++j) dot[j] = 0.f;
+    for (int64_t v0 = 0; v0 < nvec; v0 += 64 * U) {
+      uint4 gv[U], val[KB][U];
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      if (j >= k) continue;
-      const int64_t r = dst_row[t * k + j];
-      if (r < 0 || r >= nrows) continue;
-      const float w = topk_w[t * k + j];
-      Vec<T>::unpack(reinterpret_cast<const uint4*>(y + r * d)[v], tmp);
-      float s = 0.f;
-#pragma unroll
-      for (int i = 0; i < VN; ++i) {
-        s += g[i] * tmp[i];
-        o[i] = w * g[i];
+      for (int u = 0; u < U; ++u) {
+        const int64_t v = v0 + u * 64 + lane;
+        if (v < nvec) gv[u] = g_row[v];
       }
-      dot[j] += s;
-      reinterpret_cast<uint4*>(dy + r * d)[v] = Vec<T>::pack(o);
-    }
-  }
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    if (j >= k) continue;
-    const float s = wave_sum(dot[j]);
-    if (lane == 0) d_w[t * k + j] = s;
+      for (int j = 0; j < KB; ++j)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t v = v0 + u * 64 + lane;
+          if (rr[j] >= 0 && v < nvec)
+            val[j][u] = load_stream(reinterpret_cast<const uint4*>(y + rr[j] * d) + v);
+        }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t v = v0 + u * 64 + lane;
+        if (v >= nvec) continue;
+        float g[VN];
+        Vec<T>::unpack(gv[u], g);
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+          if (rr[j] < 0) continue;
+          float tmp[VN], o[VN], s = 0.f;
+          Vec<T>::unpack(val[j][u], tmp);
+#pragma unroll
+          for (int i = 0; i < VN; ++i) {
+            s += g[i] * tmp[i];
+            o[i] = ww[j] * g[i];
+          }
+          dot[j] += s;
+          reinterpret_cast<uint4*>(dy + rr[j] * d)[v] = Vec<T>::pack(o);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      if (j0 + j >= k) continue;
+      const float s = wave_sum(dot[j]);
+      if (lane == 0) d_w[t * k + j0 + j] = s;
+    }
   }
 }
 
@@ -275,16 +428,37 @@ static dim3 elem_grid(int64_t n) {
   return dim3(static_cast<unsigned>(b));
 }
 
+// Slot batch size: all of a token's slots at once up to 8, else batches of 8.
+#define MOE_SLOT_BATCH_DISPATCH(k, KERNEL, ...) \
+  do {                                          \
+    if ((k) <= 2) KERNEL(2, __VA_ARGS__);       \
+    else if ((k) <= 4) KERNEL(4, __VA_ARGS__);  \
+    else KERNEL(8, __VA_ARGS__);                \
+  } while (0)
+
 hipError_t launch_permute(const void* x, int dtype, const int32_t* dst_row, int64_t T, int64_t d,
                           int k, int64_t nrows, void* xp, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (dtype == 0)
-    permute_kernel<float><<<token_grid(T), 256, 0, s>>>(static_cast<const float*>(x), dst_row, T, d,
-                                                        k, nrows, static_cast<float*>(xp));
+    permute_kernel<float><<<unit_grid(host_units(T, d, 4, kPermuteU)), 256, 0, s>>>(
+        static_cast<const float*>(x), dst_row, T, d, k, nrows, static_cast<float*>(xp));
   else
-    permute_kernel<bf16_t><<<token_grid(T), 256, 0, s>>>(static_cast<const bf16_t*>(x), dst_row, T,
-                                                         d, k, nrows, static_cast<bf16_t*>(xp));
+    permute_kernel<bf16_t><<<unit_grid(host_units(T, d, 8, kPermuteU)), 256, 0, s>>>(
+        static_cast<const bf16_t*>(x), dst_row, T, d, k, nrows, static_cast<bf16_t*>(xp));
   return hipGetLastError();
+}
+
+constexpr int kPermuteBwdU = 2;
+template <typename T>
+static void permute_bwd_dispatch(const T* dxp, const int32_t* dst, int64_t Tn, int64_t d, int k,
+                                 int64_t nrows, const T* addend, const float* addend_f32, T* dx,
+                                 hipStream_t s) {
+  const dim3 g = unit_grid(host_units(Tn, d, Vec<T>::N, kPermuteBwdU));
+#define MOE_PBWD(KB, ...) \
+  permute_bwd_kernel<T, KB, kPermuteBwdU><<<g, 256, 0, s>>>(dxp, dst, Tn, d, k, nrows, addend, \
+                                                            addend_f32, dx)
+  MOE_SLOT_BATCH_DISPATCH(k, MOE_PBWD, 0);
+#undef MOE_PBWD
 }
 
 hipError_t launch_permute_bwd(const void* dxp, int dtype, const int32_t* dst_row, int64_t T,
@@ -292,14 +466,25 @@ hipError_t launch_permute_bwd(const void* dxp, int dtype, const int32_t* dst_row
                               const float* addend_f32, void* dx, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (dtype == 0)
-    permute_bwd_kernel<float><<<token_grid(T), 256, 0, s>>>(
-        static_cast<const float*>(dxp), dst_row, T, d, k, nrows,
-        static_cast<const float*>(addend), addend_f32, static_cast<float*>(dx));
+    permute_bwd_dispatch<float>(static_cast<const float*>(dxp), dst_row, T, d, k, nrows,
+                                static_cast<const float*>(addend), addend_f32,
+                                static_cast<float*>(dx), s);
   else
-    permute_bwd_kernel<bf16_t><<<token_grid(T), 256, 0, s>>>(
-        static_cast<const bf16_t*>(dxp), dst_row, T, d, k, nrows,
-        static_cast<const bf16_t*>(addend), addend_f32, static_cast<bf16_t*>(dx));
+    permute_bwd_dispatch<bf16_t>(static_cast<const bf16_t*>(dxp), dst_row, T, d, k, nrows,
+                                 static_cast<const bf16_t*>(addend), addend_f32,
+                                 static_cast<bf16_t*>(dx), s);
   return hipGetLastError();
+}
+
+constexpr int kCombineU = 1;
+template <typename T>
+static void combine_dispatch(const T* y, const float* w, const int32_t* dst, const T* shared,
+                             int64_t Tn, int64_t d, int k, int64_t nrows, T* out, hipStream_t s) {
+  const dim3 g = unit_grid(host_units(Tn, d, Vec<T>::N, kCombineU));
+#define MOE_COMB(KB, ...) \
+  combine_kernel<T, KB, kCombineU><<<g, 256, 0, s>>>(y, w, dst, shared, Tn, d, k, nrows, out)
+  MOE_SLOT_BATCH_DISPATCH(k, MOE_COMB, 0);
+#undef MOE_COMB
 }
 
 hipError_t launch_combine(const void* y, int dtype, const float* topk_w, const int32_t* dst_row,
@@ -307,33 +492,26 @@ hipError_t launch_combine(const void* y, int dtype, const float* topk_w, const i
                           void* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (dtype == 0)
-    combine_kernel<float><<<token_grid(T), 256, 0, s>>>(static_cast<const float*>(y), topk_w,
-                                                        dst_row, static_cast<const float*>(shared),
-                                                        T, d, k, nrows, static_cast<float*>(out));
+    combine_dispatch<float>(static_cast<const float*>(y), topk_w, dst_row,
+                            static_cast<const float*>(shared), T, d, k, nrows,
+                            static_cast<float*>(out), s);
   else
-    combine_kernel<bf16_t><<<token_grid(T), 256, 0, s>>>(
-        static_cast<const bf16_t*>(y), topk_w, dst_row, static_cast<const bf16_t*>(shared), T, d,
-        k, nrows, static_cast<bf16_t*>(out));
+    combine_dispatch<bf16_t>(static_cast<const bf16_t*>(y), topk_w, dst_row,
+                             static_cast<const bf16_t*>(shared), T, d, k, nrows,
+                             static_cast<bf16_t*>(out), s);
   return hipGetLastError();
 }
 
+constexpr int kCombineBwdU = 2;
 template <typename T>
 static void combine_bwd_dispatch(const T* dout, const T* y, const float* w, const int32_t* dst,
                                  int64_t Tn, int64_t d, int k, int64_t nrows, T* dy, float* dw,
                                  hipStream_t s) {
   const dim3 g = token_grid(Tn);
-  if (k <= 2)
-    combine_bwd_kernel<T, 2><<<g, 256, 0, s>>>(dout, y, w, dst, Tn, d, k, nrows, dy, dw);
-  else if (k <= 4)
-    combine_bwd_kernel<T, 4><<<g, 256, 0, s>>>(dout, y, w, dst, Tn, d, k, nrows, dy, dw);
-  else if (k <= 8)
-    combine_bwd_kernel<T, 8><<<g, 256, 0, s>>>(dout, y, w, dst, Tn, d, k, nrows, dy, dw);
-  else if (k <= 16)
-    combine_bwd_kernel<T, 16><<<g, 256, 0, s>>>(dout, y, w, dst, Tn, d, k, nrows, dy, dw);
-  else if (k <= 32)
-    combine_bwd_kernel<T, 32><<<g, 256, 0, s>>>(dout, y, w, dst, Tn, d, k, nrows, dy, dw);
-  else
-    combine_bwd_kernel<T, 64><<<g, 256, 0, s>>>(dout, y, w, dst, Tn, d, k, nrows, dy, dw);
+#define MOE_CBWD(KB, ...) \
+  combine_bwd_kernel<T, KB, kCombineBwdU><<<g, 256, 0, s>>>(dout, y, w, dst, Tn, d, k, nrows, dy, dw)
+  MOE_SLOT_BATCH_DISPATCH(k, MOE_CBWD, 0);
+#undef MOE_CBWD
 }
 
 hipError_t launch_combine_bwd(const void* dout, const void* y, int dtype, const float* topk_w,
