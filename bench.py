@@ -310,6 +310,10 @@ def main():
         fl, by = work[name]
         kernels[name] = {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 2) if fl else None,
                          "GB/s": round(by / ms / 1e6, 1), "alg_bytes": int(by), "alg_flops": fl}
+        tr = traffic_for(cfg.name, name)
+        if tr is not None:  # counter-measured HBM bytes of this call
+            kernels[name]["traffic"] = tr
+            kernels[name]["traffic_GB/s"] = round(tr / ms / 1e6, 1)
     total_flops = sum(fl for fl, _ in work.values())
     value = total_flops / (ms_step / 1e3) / 1e12
 
@@ -319,6 +323,8 @@ def main():
     pc_names = [n for n in ("permute", "combine", "combine_bwd", "permute_bwd") if n in kernels]
     pc_ms = sum(kernels[n]["ms"] for n in pc_names)
     pc_bytes = sum(work[n][1] for n in pc_names)
+    pc_tr = [kernels[n].get("traffic") for n in pc_names]
+    pc_traffic = sum(pc_tr) if pc_tr and None not in pc_tr else None
 
     dom = max(kernels, key=lambda n: kernels[n]["ms"])
     fl, by = work[dom]
@@ -363,7 +369,10 @@ def main():
                          "ms": round(gemm_ms, 3)},
         "permute_combine": {"GB/s": round(pc_bytes / pc_ms / 1e6, 1),
                             "frac_hbm_peak": round(pc_bytes / pc_ms / 1e6 / PEAK_HBM_GBS, 4),
-                            "ms": round(pc_ms, 4)},
+                            "ms": round(pc_ms, 4),
+                            "traffic": pc_traffic,
+                            "traffic_GB/s": (round(pc_traffic / pc_ms / 1e6, 1)
+                                             if pc_traffic is not None else None)},
         "roofline": roof,
         "kernels": kernels,
         "cpu_baseline": None,

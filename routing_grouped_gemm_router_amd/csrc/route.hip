@@ -19,6 +19,10 @@
 namespace moe {
 
 constexpr int ROUTE_TILE = 64;  // tokens per tile = bits of one mask word
+// threads of the per-tile selection kernels: 16 waves, 4 tokens each, so the
+// serial k-step selection of one token runs on many waves at once
+constexpr int ROUTE_THREADS = 1024;
+constexpr int ROUTE_WAVES = ROUTE_THREADS / 64;
 
 // Selection-only expert bias (the auxiliary-loss-free biasing that section 7,
 // Load Balancing, lists): the key of expert e is sigmoid(z) + b[e]; the
@@ -58,7 +62,7 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
 }
 
 template <int EPL>
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int64_t T, int E,
+__global__ __launch_bounds__(ROUTE_THREADS) void topk_kernel(const float* __restrict__ logits, int64_t T, int E,
                                                    int k, int score, int renorm,
                                                    const float* __restrict__ sel_bias,
                                                    int32_t* __restrict__ topk_idx,
@@ -67,10 +71,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   __shared__ unsigned long long bits[1024];
   const int tid = threadIdx.x;
   const int64_t tile = blockIdx.x;
-  for (int e = tid; e < E; e += 256) bits[e] = 0ull;
+  for (int e = tid; e < E; e += ROUTE_THREADS) bits[e] = 0ull;
   __syncthreads();
   const int wave = tid >> 6, lane = tid & 63;
-  for (int tt = wave; tt < ROUTE_TILE; tt += 4) {
+  for (int tt = wave; tt < ROUTE_TILE; tt += ROUTE_WAVES) {
     const int64_t t = tile * ROUTE_TILE + tt;
     if (t >= T) break;
     const float* row = logits + t * E;
@@ -141,7 +145,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += 256) tile_bits[tile * E + e] = bits[e];
+  for (int e = tid; e < E; e += ROUTE_THREADS) tile_bits[tile * E + e] = bits[e];
 }
 
 // Router replay: the k experts of every token are given, in slot order; the
@@ -150,7 +154,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 // replaced, in slot order, by the smallest expert the token does not use yet,
 // and *status (if given) is set to 1: the dispatch map stays a bijection.
 template <int EPL>
-__global__ __launch_bounds__(256) void replay_kernel(const float* __restrict__ logits,
+__global__ __launch_bounds__(ROUTE_THREADS) void replay_kernel(const float* __restrict__ logits,
                                                      const int32_t* __restrict__ idx_in,
                                                      int64_t T, int E, int k, int score,
                                                      int renorm, int32_t* __restrict__ topk_idx,
@@ -160,10 +164,10 @@ __global__ __launch_bounds__(256) void replay_kernel(const float* __restrict__ l
   __shared__ unsigned long long bits[1024];
   const int tid = threadIdx.x;
   const int64_t tile = blockIdx.x;
-  for (int e = tid; e < E; e += 256) bits[e] = 0ull;
+  for (int e = tid; e < E; e += ROUTE_THREADS) bits[e] = 0ull;
   __syncthreads();
   const int wave = tid >> 6, lane = tid & 63;
-  for (int tt = wave; tt < ROUTE_TILE; tt += 4) {
+  for (int tt = wave; tt < ROUTE_TILE; tt += ROUTE_WAVES) {
     const int64_t t = tile * ROUTE_TILE + tt;
     if (t >= T) break;
     const float* row = logits + t * E;
@@ -232,7 +236,7 @@ __global__ __launch_bounds__(256) void replay_kernel(const float* __restrict__ l
     }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += 256) tile_bits[tile * E + e] = bits[e];
+  for (int e = tid; e < E; e += ROUTE_THREADS) tile_bits[tile * E + e] = bits[e];
 }
 
 // One block: per expert, the running row count over tiles (tile_base), the
@@ -371,7 +375,7 @@ hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int s
     switch (epl_for(E)) {
 #define MOE_TOPK(n)                                                                               \
   case n:                                                                                         \
-    topk_kernel<n><<<dim3(static_cast<unsigned>(ntiles)), 256, 0, stream>>>(                      \
+    topk_kernel<n><<<dim3(static_cast<unsigned>(ntiles)), ROUTE_THREADS, 0, stream>>>(                      \
         logits, T, E, k, score, renorm, sel_bias, topk_idx, topk_w, tile_bits);                   \
     break;
       MOE_TOPK(1) MOE_TOPK(2) MOE_TOPK(4) MOE_TOPK(8) MOE_TOPK(16)
@@ -398,7 +402,7 @@ hipError_t launch_route_replay(const float* logits, const int32_t* idx_in, int64
     switch (epl_for(E)) {
 #define MOE_REPLAY(n)                                                                             \
   case n:                                                                                         \
-    replay_kernel<n><<<dim3(static_cast<unsigned>(ntiles)), 256, 0, stream>>>(                    \
+    replay_kernel<n><<<dim3(static_cast<unsigned>(ntiles)), ROUTE_THREADS, 0, stream>>>(                    \
         logits, idx_in, T, E, k, score, renorm, topk_idx, topk_w, tile_bits, status);             \
     break;
       MOE_REPLAY(1) MOE_REPLAY(2) MOE_REPLAY(4) MOE_REPLAY(8) MOE_REPLAY(16)
