@@ -1266,8 +1266,12 @@ __global__ __launch_bounds__(512, 1) void wgrad256_kernel(Params p) {
       const LDS_AS char* opB = stage + 2 * SLAB + wn * SLAB;
       const int ra0 = (wm & 1) * 64;  // the wave's first row inside its A slab
       if (Q == P_BF16) {
+        // tokens of the group left in this stage: a 16-token sub-step past
+        // them holds only zero rows, so its MFMAs are skipped
+        const int64_t left = cp_t.nrows - static_cast<int64_t>(cp_kt) * 64;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
+          if (kk * 16 >= left) break;
           bf16x8_t a[2], b[4];
 #pragma unroll
           for (int ii = 0; ii < 2; ++ii) a[ii] = frag_nc(opA, ra0 + ii * 32, kk * 16, lane);
