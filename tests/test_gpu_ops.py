@@ -119,7 +119,8 @@ def _perm_dst(T, k, seed):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-@pytest.mark.parametrize("T,d,k", [(257, 128, 2), (1000, 7168, 8), (3, 8, 1)])
+@pytest.mark.parametrize("T,d,k", [(257, 128, 2), (1000, 7168, 8), (3, 8, 1), (100, 1032, 3),
+                                   (50, 200, 12)])
 def test_permute_exact(gpu, dt, T, d, k):
     tdt = torch.float32 if dt == "f32" else torch.bfloat16
     x = inputs.normal((T, d), 1.0, 11, 0, "cpu", tdt)
@@ -132,7 +133,8 @@ def test_permute_exact(gpu, dt, T, d, k):
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("T,d,k,shared", [(257, 128, 2, True), (1000, 7168, 8, False),
-                                          (64, 64, 4, True)])
+                                          (64, 64, 4, True), (100, 1032, 12, True),
+                                          (33, 200, 20, False), (17, 64, 64, True)])
 def test_unpermute_combine(gpu, dt, T, d, k, shared):
     tdt = torch.float32 if dt == "f32" else torch.bfloat16
     y = inputs.normal((T * k, d), 1.0, 21, 0, "cpu", tdt)
@@ -147,7 +149,8 @@ def test_unpermute_combine(gpu, dt, T, d, k, shared):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-@pytest.mark.parametrize("T,d,k", [(257, 128, 2), (700, 7168, 8), (40, 32, 64)])
+@pytest.mark.parametrize("T,d,k", [(257, 128, 2), (700, 7168, 8), (40, 32, 64), (100, 1032, 3),
+                                   (50, 200, 12), (33, 520, 20)])
 def test_unpermute_combine_bwd(gpu, dt, T, d, k):
     tdt = torch.float32 if dt == "f32" else torch.bfloat16
     y = inputs.normal((T * k, d), 1.0, 31, 0, "cpu", tdt)
@@ -163,7 +166,8 @@ def test_unpermute_combine_bwd(gpu, dt, T, d, k):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-@pytest.mark.parametrize("T,d,k", [(257, 128, 2), (700, 7168, 8)])
+@pytest.mark.parametrize("T,d,k", [(257, 128, 2), (700, 7168, 8), (100, 1032, 3), (50, 200, 12),
+                                   (17, 64, 64)])
 def test_permute_bwd(gpu, dt, T, d, k):
     tdt = torch.float32 if dt == "f32" else torch.bfloat16
     dxp = inputs.normal((T * k, d), 1.0, 41, 0, "cpu", tdt)
@@ -177,6 +181,53 @@ def test_permute_bwd(gpu, dt, T, d, k):
     dx2 = torch.empty((T, d), dtype=tdt, device=DEV)
     abi.moe_permute_bwd(dxp.to(DEV), dst.to(DEV), None, None, dx2)
     assert_close("dx (no addends)", dx2, oracle.permute_bwd(np64(dxp), dst.numpy()), TOL[dt])
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("T,d,k", [(64, 1032, 3), (40, 200, 12)])
+def test_dropped_slots(gpu, dt, T, d, k):
+    """Slots with no permuted row (dst_row -1, as capacity dropping leaves them)
+    contribute nothing to combine and permute_bwd, get a zero routing-weight
+    gradient, and their would-be rows are not written by permute or the combine
+    backward.  The oracle sees them as slots of an extra all-zero row."""
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    dst, _ = _perm_dst(T, k, 9)
+    drop = torch.rand((T, k), generator=torch.Generator().manual_seed(3)) < 0.3
+    dst_g = torch.where(drop, torch.full_like(dst, -1), dst)
+    zrow = T * k                                  # the oracle's extra zero row
+    dst_o = torch.where(drop, torch.full_like(dst, zrow), dst).numpy()
+    kept = dst[~drop].long()
+    x = inputs.normal((T, d), 1.0, 51, 0, "cpu", tdt)
+    y = inputs.normal((T * k, d), 1.0, 52, 0, "cpu", tdt)
+    dout = inputs.normal((T, d), 1.0, 53, 0, "cpu", tdt)
+    w = torch.rand((T, k), generator=torch.Generator().manual_seed(5), dtype=torch.float32)
+    y0 = np.concatenate([np64(y), np.zeros((1, d))])
+    # permute: kept rows exact, the rows of dropped slots untouched
+    xp = torch.full((T * k, d), 7.0, dtype=tdt, device=DEV)
+    abi.moe_permute(x.to(DEV), dst_g.to(DEV), xp)
+    ref = np.full((T * k, d), 7.0)
+    src = np.repeat(np.arange(T), k).reshape(T, k)
+    ref[dst[~drop].numpy()] = x.float().numpy()[src[~drop.numpy()]]
+    np.testing.assert_array_equal(xp.float().cpu().numpy(), ref)
+    # combine
+    out = torch.empty((T, d), dtype=tdt, device=DEV)
+    abi.moe_unpermute_combine(y.to(DEV), w.to(DEV), dst_g.to(DEV), None, out)
+    assert_close("out", out, oracle.unpermute_combine(y0, w.numpy(), dst_o), TOL[dt])
+    # combine backward
+    dy = torch.full((T * k, d), 7.0, dtype=tdt, device=DEV)
+    dw = torch.full((T, k), 7.0, dtype=torch.float32, device=DEV)
+    abi.moe_unpermute_combine_bwd(dout.to(DEV), y.to(DEV), w.to(DEV), dst_g.to(DEV), dy, dw)
+    rdy, rdw = oracle.unpermute_combine_bwd(np64(dout), y0, w.numpy(), dst_o)
+    dyc = dy.float().cpu().numpy()
+    assert_close("dy kept rows", torch.from_numpy(dyc[kept.numpy()]), rdy[kept.numpy()], TOL[dt])
+    untouched = np.setdiff1d(np.arange(T * k), kept.numpy())
+    np.testing.assert_array_equal(dyc[untouched], 7.0)
+    assert_close("d_topk_w", dw, rdw, TOL["f32"] if dt == "f32" else 1e-4)
+    assert float(dw[drop.to(DEV)].abs().max()) == 0.0
+    # permute backward
+    dx = torch.empty((T, d), dtype=tdt, device=DEV)
+    abi.moe_permute_bwd(y.to(DEV), dst_g.to(DEV), None, None, dx)
+    assert_close("dx", dx, oracle.permute_bwd(y0, dst_o), TOL[dt])
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
