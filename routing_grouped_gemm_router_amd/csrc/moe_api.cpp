@@ -503,6 +503,8 @@ int moe_unpermute_combine_bwd(const void* dout, const void* y_perm, int dtype, c
           "moe_unpermute_combine_bwd: T=%lld d=%lld k=%d n_rows=%lld", static_cast<long long>(T),
           static_cast<long long>(d), k, static_cast<long long>(n_rows));
   REQUIRE(k <= 64, MOE_ERR_UNSUPPORTED, "moe_unpermute_combine_bwd: k=%d above 64", k);
+  REQUIRE(T * k < (int64_t(1) << 31), MOE_ERR_UNSUPPORTED,
+          "moe_unpermute_combine_bwd: T*k must be below 2^31");
   int st = check_row_vectors(dtype, d, "moe_unpermute_combine_bwd");
   if (st != MOE_OK) return st;
   if (T == 0) return ok();

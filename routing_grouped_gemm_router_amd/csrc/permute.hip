@@ -161,6 +161,20 @@ __global__ __launch_bounds__(256) void permute_bwd_kernel(const T* __restrict__ 
   const int64_t n_waves = static_cast<int64_t>(gridDim.x) * 4;
   for (int64_t un = wave_index(); un < rc.units; un += n_waves) {
     const int64_t t = un / rc.cpr, v0 = (un - t * rc.cpr) * 64 * U;
+    // the addends' chunks are requested first, with the rows of the first batch
+    uint4 ad[U];
+    uint4 af[U][VN / 4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + u * 64 + lane;
+      if (v >= rc.nvec) continue;
+      if (addend) ad[u] = load_stream(reinterpret_cast<const uint4*>(addend + t * d) + v);
+      if (addend_f32) {
+        const uint4* a = reinterpret_cast<const uint4*>(addend_f32 + t * d + v * VN);
+#pragma unroll
+        for (int i = 0; i < VN / 4; ++i) af[u][i] = load_stream(a + i);
+      }
+    }
     float acc[U][VN];
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -197,16 +211,17 @@ __global__ __launch_bounds__(256) void permute_bwd_kernel(const T* __restrict__ 
       if (v >= rc.nvec) continue;
       if (addend) {
         float tmp[VN];
-        Vec<T>::unpack(load_stream(reinterpret_cast<const uint4*>(addend + t * d) + v), tmp);
+        Vec<T>::unpack(ad[u], tmp);
 #pragma unroll
         for (int i = 0; i < VN; ++i) acc[u][i] += tmp[i];
       }
       if (addend_f32) {
-        const float4* a = reinterpret_cast<const float4*>(addend_f32 + t * d + v * VN);
 #pragma unroll
-        for (int i = 0; i < VN; i += 4) {
-          const float4 q = a[i / 4];
-          acc[u][i] += q.x; acc[u][i + 1] += q.y; acc[u][i + 2] += q.z; acc[u][i + 3] += q.w;
+        for (int i = 0; i < VN / 4; ++i) {
+          acc[u][4 * i] += __uint_as_float(af[u][i].x);
+          acc[u][4 * i + 1] += __uint_as_float(af[u][i].y);
+          acc[u][4 * i + 2] += __uint_as_float(af[u][i].z);
+          acc[u][4 * i + 3] += __uint_as_float(af[u][i].w);
         }
       }
       reinterpret_cast<uint4*>(dx + t * d)[v] = Vec<T>::pack(acc[u]);
@@ -283,8 +298,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y,
 }
 
 // dy[dst_row[t, j]] = w[t, j] * dout[t];  d_w[t, j] = <dout[t], y[dst_row[t, j]]>
-// One wave per token (the dot products need the whole row); slots KB at a
-// time, U vectors per lane, every row load of a step issued before its use.
+// One workgroup per token, its 4 waves on 4 quarters of the row (so each
+// wave's chain of dependent steps is a quarter as long); slots KB at a time,
+// U vectors per lane, every row load of a step issued before its use.  The
+// dot products are summed over each wave, then over the 4 waves in order
+// through LDS (deterministic).
 template <typename T, int KB, int U>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ dout,
                                                           const T* __restrict__ y,
@@ -294,10 +312,12 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ 
                                                           int64_t nrows, T* __restrict__ dy,
                                                           float* __restrict__ d_w) {
   constexpr int VN = Vec<T>::N;
-  const int64_t t = wave_index();
-  if (t >= T_) return;
-  const int lane = threadIdx.x & 63;
+  __shared__ float part[4][KB];
+  const int64_t t = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t nvec = d / VN;
+  const int64_t q = (nvec + 3) / 4;  // vectors of each wave's quarter
+  const int64_t vb = wave * q, ve = min(nvec, vb + q);
   const uint4* g_row = reinterpret_cast<const uint4*>(dout + t * d);
   for (int j0 = 0; j0 < k; j0 += KB) {
     int64_t rr[KB];
@@ -305,48 +325,53 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ 
     slot_batch<KB>(dst_row, topk_w, t, k, j0, nrows, rr, ww);
 #pragma unroll
     for (int j = 0; j < KB; ++j) dot[j] = 0.f;
-    for (int64_t v0 = 0; v0 < nvec; v0 += 64 * U) {
+    for (int64_t v0 = vb; v0 < ve; v0 += 64 * U) {
       uint4 gv[U], val[KB][U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int64_t v = v0 + u * 64 + lane;
-        if (v < nvec) gv[u] = g_row[v];
+        if (v < ve) gv[u] = g_row[v];
       }
 #pragma unroll
       for (int j = 0; j < KB; ++j)
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int64_t v = v0 + u * 64 + lane;
-          if (rr[j] >= 0 && v < nvec)
+          if (rr[j] >= 0 && v < ve)
             val[j][u] = load_stream(reinterpret_cast<const uint4*>(y + rr[j] * d) + v);
         }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int64_t v = v0 + u * 64 + lane;
-        if (v >= nvec) continue;
+        if (v >= ve) continue;
         float g[VN];
         Vec<T>::unpack(gv[u], g);
 #pragma unroll
         for (int j = 0; j < KB; ++j) {
           if (rr[j] < 0) continue;
-          float tmp[VN], o[VN], s = 0.f;
+          float tmp[VN], o[VN], sdot = 0.f;
           Vec<T>::unpack(val[j][u], tmp);
 #pragma unroll
           for (int i = 0; i < VN; ++i) {
-            s += g[i] * tmp[i];
+            sdot += g[i] * tmp[i];
             o[i] = ww[j] * g[i];
           }
-          dot[j] += s;
+          dot[j] += sdot;
           reinterpret_cast<uint4*>(dy + rr[j] * d)[v] = Vec<T>::pack(o);
         }
       }
     }
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
-      if (j0 + j >= k) continue;
-      const float s = wave_sum(dot[j]);
-      if (lane == 0) d_w[t * k + j0 + j] = s;
+      const float sw = wave_sum(dot[j]);
+      if (lane == 0) part[wave][j] = sw;
     }
+    __syncthreads();
+    if (threadIdx.x < KB && j0 + static_cast<int>(threadIdx.x) < k) {
+      const int j = threadIdx.x;
+      d_w[t * k + j0 + j] = ((part[0][j] + part[1][j]) + part[2][j]) + part[3][j];
+    }
+    __syncthreads();
   }
 }
 
@@ -419,8 +444,6 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const T* __restrict__ d
   }
 }
 
-static dim3 token_grid(int64_t T) { return dim3(static_cast<unsigned>((T + 3) / 4)); }
-
 static dim3 elem_grid(int64_t n) {
   int64_t b = (n + 255) / 256;
   if (b > 65536) b = 65536;
@@ -448,7 +471,7 @@ hipError_t launch_permute(const void* x, int dtype, const int32_t* dst_row, int6
   return hipGetLastError();
 }
 
-constexpr int kPermuteBwdU = 2;
+constexpr int kPermuteBwdU = 1;
 template <typename T>
 static void permute_bwd_dispatch(const T* dxp, const int32_t* dst, int64_t Tn, int64_t d, int k,
                                  int64_t nrows, const T* addend, const float* addend_f32, T* dx,
@@ -507,7 +530,7 @@ template <typename T>
 static void combine_bwd_dispatch(const T* dout, const T* y, const float* w, const int32_t* dst,
                                  int64_t Tn, int64_t d, int k, int64_t nrows, T* dy, float* dw,
                                  hipStream_t s) {
-  const dim3 g = token_grid(Tn);
+  const dim3 g(static_cast<unsigned>(Tn));  // one workgroup per token
 #define MOE_CBWD(KB, ...) \
   combine_bwd_kernel<T, KB, kCombineBwdU><<<g, 256, 0, s>>>(dout, y, w, dst, Tn, d, k, nrows, dy, dw)
   MOE_SLOT_BATCH_DISPATCH(k, MOE_CBWD, 0);
