@@ -59,15 +59,17 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_work(cfg, n_nonempty, gated=False):
+def kernel_work(cfg, n_nonempty, gated=False, n_rows=None):
     """Algorithmic FLOPs and HBM bytes per call of every span.
 
-    FLOPs: 2 per multiply-add over the routed rows only.  Bytes: every
-    operand read once and every result written once; an expert's weights
-    count once per GEMM pass when the expert received rows; index and
-    routing-weight arrays included."""
+    FLOPs: 2 per multiply-add over the routed rows only: the (token, slot)
+    pairs that have a row, n_rows (T * k when dropless; the kept pairs under
+    a capacity, whose padding rows are not counted).  Bytes: every operand
+    read once and every result written once; an expert's weights count once
+    per GEMM pass when the expert received rows; index and routing-weight
+    arrays included."""
     T, d, E, k, f, fs = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.fs
-    N = T * k
+    N = T * k if n_rows is None else n_rows
     s = 2 if cfg.dtype == "bf16" else 4      # activation / weight element bytes
     w13 = n_nonempty * d * 2 * f * s
     w2 = n_nonempty * f * d * s
@@ -91,7 +93,7 @@ def kernel_work(cfg, n_nonempty, gated=False):
         "permute_bwd": (0.0, N * d * s + idx + T * d * (s + 4 + (s if fs else 0))),
     }
     if cfg.gemm in ("fp8", "mxfp8"):
-        w.update(fp8_work(cfg, n_nonempty, mx=cfg.gemm == "mxfp8"))
+        w.update(fp8_work(cfg, n_nonempty, mx=cfg.gemm == "mxfp8", n_rows=N))
         return w
     if gated:
         # routing weight inside the expert: the combine backward is a gather of
@@ -115,7 +117,7 @@ def kernel_work(cfg, n_nonempty, gated=False):
     return w
 
 
-def fp8_work(cfg, n_nonempty, mx=False):
+def fp8_work(cfg, n_nonempty, mx=False, n_rows=None):
     """FLOPs and bytes of the spans of the fp8 expert paths.  Activations are
     stored in bf16 (2 bytes) and quantized to 1-byte E4M3 codes before each
     GEMM, with one fp32 scale per 128 elements (blockwise) or one E8M0 byte per
@@ -124,7 +126,7 @@ def fp8_work(cfg, n_nonempty, mx=False):
     bf16.  MXFP8 gathers x through the permutation inside its quantizers (x
     read once, the row map read, no permuted bf16 copy)."""
     T, d, E, k, f, fs = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.fs
-    N = T * k
+    N = T * k if n_rows is None else n_rows
 
     def q(n):            # bytes of n fp8 codes with their scales
         return n + (n / 32 if mx else n / 128 * 4)
@@ -304,7 +306,8 @@ def main():
     spans = timer.summary()
     counts = layer.counts.cpu()
     n_nonempty = int((counts > 0).sum())
-    work = kernel_work(cfg, n_nonempty, gated=args.gate_in_ffn)
+    n_rows = int(counts.sum())  # (token, slot) pairs with a row: T * k unless dropped
+    work = kernel_work(cfg, n_nonempty, gated=args.gate_in_ffn, n_rows=n_rows)
     kernels = {}
     for name, (ms, n) in spans.items():
         fl, by = work[name]
@@ -362,6 +365,7 @@ def main():
                    "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
                    "ffn": cfg.f, "shared_ffn": cfg.fs, "score": cfg.score, "renorm": cfg.renorm,
                    "router_bias": cfg.bias, "experts_with_rows": n_nonempty,
+                   "routed_rows": n_rows,
                    "max_rows_per_expert": int(counts.max())},
         "grouped_gemm": {"TFLOP/s": round(gemm_flops / gemm_ms / 1e9, 1),
                          "frac_peak": round(gemm_flops / gemm_ms / 1e9 / gemm_peak, 4),
