@@ -1,7 +1,8 @@
-// fp32 vector-ALU GEMM family: the router projection and its backward (the
-// router stays in FP32 -- "Scalable Training of Mixture-of-Experts Models with
-// Megatron Core", section 5, Selective precision) and the fp32 grouped expert
-// GEMMs (section 2, Expert Computation).
+// fp32 GEMM family: the router projection and its backward (the router stays
+// in FP32 -- "Scalable Training of Mixture-of-Experts Models with Megatron
+// Core", section 5, Selective precision: fp32-accurate products on the matrix
+// cores) and the fp32 grouped expert GEMMs (section 2, Expert Computation, on
+// the vector ALUs).
 //
 //   C[m, n] (+)= sum_k Aop(m, k) * Bop(k, n)
 //   Aop(m, k) = A[m * lda + k]            (A_MC = false: k contiguous)
@@ -430,16 +431,259 @@ static hipError_t run_f32(const TA* A, int64_t lda, const float* B, int64_t ldb,
   return hipGetLastError();
 }
 
+// ---- router products on the bf16 matrix cores, fp32-accurate ----------------
+// An fp32 operand v is split exactly into three bf16 terms, v = hi + mid + lo
+// + r: hi = bf16(v), mid = bf16(v - hi), lo = bf16(v - hi - mid), each
+// rounded to nearest even; both residuals are exact in fp32 (each is v with
+// its leading bits removed), and |r| is about 2^-24 |v|, the rounding of an
+// fp32 value.  A product of two split operands keeps the term pairs whose
+// combined weight is at least 2^-16 (hi.hi, hi.mid, mid.hi, hi.lo, lo.hi,
+// mid.mid); every bf16 product is exact in the fp32 accumulator.  So the
+// result carries fp32 accuracy while the matrix cores run at their bf16 rate
+// (the router stays FP32 in what it computes).  Activations that are already
+// bf16 need no split (one term).
+//
+// C[m, n] = sum_k A[m, k] B(k, n), one wave per 64 x 64 tile as 2 x 2 MFMA
+// 32x32x16 blocks, operands loaded straight into the MFMA fragments: lane
+// half h of a 16-deep step holds k = 8 h .. 8 h + 7 of its row (A) or column
+// (B).  A is k-contiguous (x: bf16 or fp32; d_logits: fp32).  B is W_r: for
+// the logits W_r[k, n] (k strided: eight scalar loads per fragment, L2
+// resident), for the router's dx W_r[n, k] (k-contiguous).  SK = 8: the 8
+// waves of a workgroup split the contraction of one tile and add their
+// partials in wave order through LDS.
+typedef __bf16 bf16x8_rt __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_rt __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo_f(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// eight fp32 values -> their hi, mid and lo bf16 terms
+__device__ __forceinline__ void split3x8(const float (&v)[8], bf16x8_rt (&t)[3]) {
+#pragma clang fp contract(off)
+  u32x4_rt h, m, l;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = v[2 * i], b = v[2 * i + 1];
+    const uint32_t hw = f32x2_to_bf16x2(a, b);
+    const float ra = a - bf16_lo_f(hw), rb = b - bf16_hi_f(hw);
+    const uint32_t mw = f32x2_to_bf16x2(ra, rb);
+    const float sa = ra - bf16_lo_f(mw), sb = rb - bf16_hi_f(mw);
+    h[i] = hw;
+    m[i] = mw;
+    l[i] = f32x2_to_bf16x2(sa, sb);
+  }
+  t[0] = __builtin_bit_cast(bf16x8_rt, h);
+  t[1] = __builtin_bit_cast(bf16x8_rt, m);
+  t[2] = __builtin_bit_cast(bf16x8_rt, l);
+}
+
+__device__ __forceinline__ float4 ld4g(const float* p, bool ok) {
+  return ok ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// One lane's raw operand values of one 16-deep step: for each of its two rows
+// of A and two columns of B, the 8 values k = k0 .. k0 + 7 of its lane half.
+struct RawAB {
+  float4 a[2][2];  // fp32 A; a bf16 A keeps its 8 values in a[mi][0] as raw bits
+  float b[2][8];
+};
+
+// A row m, k = k0 .. k0 + 7 (k0 a multiple of 8; k_hi a multiple of 8 for a
+// bf16 A and of 4 for an fp32 A, so every vector lies wholly in or out)
+template <bool AF32>
+__device__ __forceinline__ void load_a_raw(const void* A, int64_t lda, int64_t m, int64_t M,
+                                           int64_t k0, int64_t k_hi, float4 (&a)[2]) {
+  const bool ok = m < M && k0 < k_hi;
+  if (AF32) {
+    const float* p = static_cast<const float*>(A) + m * lda + k0;
+    a[0] = ld4g(p, ok);
+    a[1] = ld4g(p + 4, ok && k0 + 8 <= k_hi);
+  } else {
+    const bf16_t* p = static_cast<const bf16_t*>(A) + m * lda + k0;
+    const uint4 u = ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0u, 0u, 0u, 0u);
+    a[0] = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                       __uint_as_float(u.w));
+  }
+}
+
+// B column n, k = k0 .. k0 + 7.  BT: B(k, n) = W[k * ldb + n]; else
+// B(k, n) = W[n * ldb + k] (k_hi a multiple of 4)
+template <bool BT>
+__device__ __forceinline__ void load_b_raw(const float* W, int64_t ldb, int64_t n, int64_t N,
+                                           int64_t k0, int64_t k_hi, float (&v)[8]) {
+  if (BT) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      v[i] = (n < N && k0 + i < k_hi) ? W[(k0 + i) * ldb + n] : 0.f;
+  } else {
+    const bool ok = n < N && k0 < k_hi;
+    const float* p = W + n * ldb + k0;
+    const float4 u = ld4g(p, ok), w = ld4g(p + 4, ok && k0 + 8 <= k_hi);
+    v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+    v[4] = w.x; v[5] = w.y; v[6] = w.z; v[7] = w.w;
+  }
+}
+
+template <bool AF32>
+__device__ __forceinline__ void split_a(const float4 (&a)[2], bf16x8_rt (&t)[3]) {
+  if (AF32) {
+    const float v[8] = {a[0].x, a[0].y, a[0].z, a[0].w, a[1].x, a[1].y, a[1].z, a[1].w};
+    split3x8(v, t);
+  } else {
+    u32x4_rt u;
+    u[0] = __float_as_uint(a[0].x); u[1] = __float_as_uint(a[0].y);
+    u[2] = __float_as_uint(a[0].z); u[3] = __float_as_uint(a[0].w);
+    t[0] = __builtin_bit_cast(bf16x8_rt, u);
+  }
+}
+
+template <bool AF32, bool BT, int SK, bool BIAS>
+__global__ __launch_bounds__(512) void router_mc_kernel(const void* __restrict__ A, int64_t lda,
+                                                        const float* __restrict__ W, int64_t ldb,
+                                                        float* __restrict__ C, int64_t ldc,
+                                                        int64_t M, int64_t N, int64_t K,
+                                                        const float* __restrict__ bias) {
+  __shared__ __attribute__((aligned(16))) float part_lds[8][32][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t ntn = (N + 63) / 64;
+  const int64_t tile = SK > 1 ? static_cast<int64_t>(blockIdx.x)
+                              : static_cast<int64_t>(blockIdx.x) * 8 + wave;
+  const int64_t m0 = (tile / ntn) * 64, n0 = (tile % ntn) * 64;
+  int64_t k_lo = 0, k_hi = K;
+  if (SK > 1) {
+    const int64_t per = ((K + SK - 1) / SK + 15) / 16 * 16;
+    k_lo = min(K, wave * per);
+    k_hi = min(K, k_lo + per);
+  }
+  // term pairs (A term, B term) in a fixed order: a split A keeps the six
+  // pairs of weight 2^-16 or more, a bf16 A (one term) meets all three B terms
+  constexpr int NP = AF32 ? 6 : 3;
+  constexpr int PA[6] = {0, 0, 1, 0, 2, 1};
+  constexpr int PB[6] = {0, 1, 0, 2, 0, 1};
+  constexpr int PA1[3] = {0, 0, 0};
+  constexpr int PB1[3] = {0, 1, 2};
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
+  const int r = lane & 31, h = lane >> 5;
+
+  if (m0 < M) {  // SK == 1: trailing waves of the last block may have no tile
+    // the raw values of the next two steps are in flight while one computes
+    RawAB raw[2];
+    auto load_raw = [&](int64_t k0, RawAB& rw) {
+      const int64_t kk = k0 + 8 * h;
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) load_a_raw<AF32>(A, lda, m0 + 32 * mi + r, M, kk, k_hi, rw.a[mi]);
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) load_b_raw<BT>(W, ldb, n0 + 32 * ni + r, N, kk, k_hi, rw.b[ni]);
+    };
+    if (k_lo < k_hi) load_raw(k_lo, raw[0]);
+    if (k_lo + 16 < k_hi) load_raw(k_lo + 16, raw[1]);
+    for (int64_t k0 = k_lo; k0 < k_hi; k0 += 32) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int64_t ks = k0 + 16 * sub;
+        if (ks >= k_hi) break;
+        bf16x8_rt a[2][3], b[2][3];
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) split_a<AF32>(raw[sub].a[mi], a[mi]);
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) split3x8(raw[sub].b[ni], b[ni]);
+        if (ks + 32 < k_hi) load_raw(ks + 32, raw[sub]);
+#pragma unroll
+        for (int q = 0; q < NP; ++q)
+#pragma unroll
+          for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  b[ni][AF32 ? PB[q] : PB1[q]], a[mi][AF32 ? PA[q] : PA1[q]], acc[mi][ni], 0, 0,
+                  0);
+      }
+    }
+  }
+
+  // columns 32 ni + 8 g + 4 h .. + 3 of row 32 mi + r
+  auto quad = [&](int mi, int ni, int g) {
+    return make_float4(acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2],
+                       acc[mi][ni][4 * g + 3]);
+  };
+  if (SK == 1) {
+    if (m0 >= M) return;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+      const int64_t m = m0 + 32 * mi + r;
+      if (m >= M) continue;
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t n = n0 + 32 * ni + 8 * g + 4 * h;
+          if (n >= N) continue;
+          float4 v = quad(mi, ni, g);
+          if (BIAS) {
+            v.x += bias[n]; v.y += bias[n + 1]; v.z += bias[n + 2]; v.w += bias[n + 3];
+          }
+          *reinterpret_cast<float4*>(C + m * ldc + n) = v;
+        }
+    }
+    return;
+  }
+  // SK > 1: two rounds of 32 rows; wave w's partials in its own 8 KiB as [32][64]
+  float* part = &part_lds[wave][0][0];
+#pragma unroll
+  for (int rnd = 0; rnd < 2; ++rnd) {
+    __syncthreads();
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(part + r * 64 + 32 * ni + 8 * g + 4 * h) = quad(rnd, ni, g);
+    __syncthreads();
+    // thread t sums elements 4t .. 4t+3 of the 32 x 64 half over the waves in order
+    const int e = 4 * static_cast<int>(threadIdx.x);
+    float4 sum = *reinterpret_cast<const float4*>(&part_lds[0][0][0] + e);
+#pragma unroll
+    for (int w = 1; w < 8; ++w) {
+      const float4 q = *reinterpret_cast<const float4*>(&part_lds[w][0][0] + e);
+      sum.x += q.x; sum.y += q.y; sum.z += q.z; sum.w += q.w;
+    }
+    const int64_t m = m0 + 32 * rnd + e / 64, n = n0 + (e % 64);
+    if (m < M && n < N) {
+      if (BIAS) {
+        sum.x += bias[n]; sum.y += bias[n + 1]; sum.z += bias[n + 2]; sum.w += bias[n + 3];
+      }
+      *reinterpret_cast<float4*>(C + m * ldc + n) = sum;
+    }
+  }
+}
+
+template <bool AF32, bool BT, int SK, bool BIAS>
+static hipError_t run_router_mc(const void* A, int64_t lda, const float* W, int64_t ldb, float* C,
+                                int64_t ldc, int64_t M, int64_t N, int64_t K, const float* bias,
+                                hipStream_t s) {
+  const int64_t tiles = ((M + 63) / 64) * ((N + 63) / 64);
+  const int64_t blocks = SK > 1 ? tiles : (tiles + 7) / 8;
+  if (blocks <= 0) return hipSuccess;
+  router_mc_kernel<AF32, BT, SK, BIAS><<<dim3(static_cast<unsigned>(blocks)), 512, 0, s>>>(
+      A, lda, W, ldb, C, ldc, M, N, K, bias);
+  return hipGetLastError();
+}
+
 hipError_t launch_router_fwd(const void* x, int x_dtype, const float* w_r, const float* bias,
                              int64_t T, int64_t d, int E, float* logits, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (d % 8 == 0 && E % 4 == 0 && aligned16p(x) && aligned16p(w_r) && aligned16p(logits)) {
     // logits [T, E] = x [T, d] . W_r [d, E] (+ bias): contraction split over the 8 waves
     if (x_dtype == 0)
-      return bias ? run_router<RA_KC_F32, RB_NC, 8, true>(x, d, w_r, E, logits, E, T, E, d, bias, s)
-                  : run_router<RA_KC_F32, RB_NC, 8, false>(x, d, w_r, E, logits, E, T, E, d, bias, s);
-    return bias ? run_router<RA_KC_BF16, RB_NC, 8, true>(x, d, w_r, E, logits, E, T, E, d, bias, s)
-                : run_router<RA_KC_BF16, RB_NC, 8, false>(x, d, w_r, E, logits, E, T, E, d, bias, s);
+      return bias ? run_router_mc<true, true, 8, true>(x, d, w_r, E, logits, E, T, E, d, bias, s)
+                  : run_router_mc<true, true, 8, false>(x, d, w_r, E, logits, E, T, E, d, bias, s);
+    return bias ? run_router_mc<false, true, 8, true>(x, d, w_r, E, logits, E, T, E, d, bias, s)
+                : run_router_mc<false, true, 8, false>(x, d, w_r, E, logits, E, T, E, d, bias, s);
   }
   if (x_dtype == 0)
     return run_f32<float, false, false, GRP_NONE, EPI_BIAS, float>(
@@ -469,7 +713,7 @@ hipError_t launch_router_bwd(const void* x, int x_dtype, const float* w_r, const
     }
     if (dx_r && T > 0)
       // dx_r [T, d] = dz [T, E] . W_r^T (Bop(k = e, n = i) = W_r[i * E + e])
-      err = run_router<RA_KC_F32, RB_KC, 1, false>(dz, E, w_r, E, dx_r, d, T, d, E, nullptr, s);
+      err = run_router_mc<true, false, 1, false>(dz, E, w_r, E, dx_r, d, T, d, E, nullptr, s);
     return err;
   }
   if (dw_r) {
