@@ -212,6 +212,93 @@ __device__ __forceinline__ void ld8_bf16(const bf16_t* p, bool ok, float4& lo, f
                    __uint_as_float(v.w << 16), __uint_as_float(v.w & 0xffff0000u));
 }
 
+// ---- router products on the bf16 matrix cores, fp32-accurate ----------------
+// An fp32 operand v is split exactly into three bf16 terms, v = hi + mid + lo
+// + r: hi = bf16(v), mid = bf16(v - hi), lo = bf16(v - hi - mid), each
+// rounded to nearest even; both residuals are exact in fp32 (each is v with
+// its leading bits removed), and |r| is about 2^-24 |v|, the rounding of an
+// fp32 value.  A product of two split operands keeps the term pairs whose
+// combined weight is at least 2^-16 (hi.hi, hi.mid, mid.hi, hi.lo, lo.hi,
+// mid.mid); every bf16 product is exact in the fp32 accumulator.  So the
+// result carries fp32 accuracy while the matrix cores run at their bf16 rate
+// (the router stays FP32 in what it computes).  Activations that are already
+// bf16 need no split (one term).
+//
+// C[m, n] = sum_k A[m, k] B(k, n), one wave per 64 x 64 tile as 2 x 2 MFMA
+// 32x32x16 blocks, operands loaded straight into the MFMA fragments: lane
+// half h of a 16-deep step holds k = 8 h .. 8 h + 7 of its row (A) or column
+// (B).  A is k-contiguous (x: bf16 or fp32; d_logits: fp32).  B is W_r: for
+// the logits W_r[k, n] (k strided: eight scalar loads per fragment, L2
+// resident), for the router's dx W_r[n, k] (k-contiguous).  SK = 8: the 8
+// waves of a workgroup split the contraction of one tile and add their
+// partials in wave order through LDS.
+typedef __bf16 bf16x8_rt __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_rt __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo_f(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// eight fp32 values -> their hi, mid and lo bf16 terms
+__device__ __forceinline__ void split3x8(const float (&v)[8], bf16x8_rt (&t)[3]) {
+#pragma clang fp contract(off)
+  u32x4_rt h, m, l;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = v[2 * i], b = v[2 * i + 1];
+    const uint32_t hw = f32x2_to_bf16x2(a, b);
+    const float ra = a - bf16_lo_f(hw), rb = b - bf16_hi_f(hw);
+    const uint32_t mw = f32x2_to_bf16x2(ra, rb);
+    const float sa = ra - bf16_lo_f(mw), sb = rb - bf16_hi_f(mw);
+    h[i] = hw;
+    m[i] = mw;
+    l[i] = f32x2_to_bf16x2(sa, sb);
+  }
+  t[0] = __builtin_bit_cast(bf16x8_rt, h);
+  t[1] = __builtin_bit_cast(bf16x8_rt, m);
+  t[2] = __builtin_bit_cast(bf16x8_rt, l);
+}
+
+// One 16-deep LDS slice ([k][64] fp32 for A and for B) through bf16 MFMAs:
+// lane half h takes k = 8 h .. 8 h + 7 of column r and 32 + r of each operand.
+template <bool A_BF16>
+__device__ __forceinline__ void mc16_slice(f32x16_t (&acc)[2][2], const float (*As)[64],
+                                           const float (*Bs)[64], int r, int h) {
+  float va[2][8], vb[2][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int kk = 8 * h + i;
+    va[0][i] = As[kk][r]; va[1][i] = As[kk][32 + r];
+    vb[0][i] = Bs[kk][r]; vb[1][i] = Bs[kk][32 + r];
+  }
+  bf16x8_rt a[2][3], b[2][3];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+    if (A_BF16) {  // bf16 values: exact in one term
+      u32x4_rt u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) u[i] = f32x2_to_bf16x2(va[mi][2 * i], va[mi][2 * i + 1]);
+      a[mi][0] = __builtin_bit_cast(bf16x8_rt, u);
+    } else {
+      split3x8(va[mi], a[mi]);
+    }
+  }
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni) split3x8(vb[ni], b[ni]);
+  constexpr int NP = A_BF16 ? 3 : 6;
+  constexpr int PA[6] = {0, 0, 1, 0, 2, 1};
+  constexpr int PB[6] = {0, 1, 0, 2, 0, 1};
+  constexpr int PA1[3] = {0, 0, 0};
+  constexpr int PB1[3] = {0, 1, 2};
+#pragma unroll
+  for (int q = 0; q < NP; ++q)
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            b[ni][A_BF16 ? PB1[q] : PB[q]], a[mi][A_BF16 ? PA1[q] : PA[q]], acc[mi][ni], 0, 0, 0);
+}
+
 template <int AL, int BL>
 __device__ __forceinline__ void router_load(RSlice& r, const void* A, int64_t lda, const float* B,
                                             int64_t ldb, int64_t m0, int64_t n0, int64_t k0,
@@ -288,7 +375,11 @@ __device__ __forceinline__ void router_stage(const RSlice& r, float (*As)[64], f
   }
 }
 
-template <int AL, int BL, int SK, bool BIAS>
+// MC16: the products on the bf16 matrix cores with fp32 accuracy (B split
+// into three bf16 terms, A too unless its values are bf16; see the split
+// below), reading each lane's 8 contraction values of a column from the LDS
+// slice; else one fp32 MFMA 32x32x2 per contraction position.
+template <int AL, int BL, int SK, bool BIAS, bool MC16 = false>
 __global__ __launch_bounds__(512) void router_gemm_kernel(const void* __restrict__ A, int64_t lda,
                                                           const float* __restrict__ B,
                                                           int64_t ldb, float* __restrict__ C,
@@ -329,15 +420,19 @@ __global__ __launch_bounds__(512) void router_gemm_kernel(const void* __restrict
       router_stage<AL, BL>(rs, As, Bs, lane);
       __builtin_amdgcn_wave_barrier();
       if (k0 + 16 < k_hi) router_load<AL, BL>(rs, A, lda, B, ldb, m0, n0, k0 + 16, k_hi, M, N, lane);
+      if constexpr (MC16) {
+        mc16_slice<AL == RA_KC_BF16 || AL == RA_MC_BF16>(acc, As, Bs, r, h);
+      } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int kk = 8 * h + i;
-        const float a0 = As[kk][r], a1 = As[kk][32 + r];
-        const float b0 = Bs[kk][r], b1 = Bs[kk][32 + r];
-        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(b0, a0, acc[0][0], 0, 0, 0);
-        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(b1, a0, acc[0][1], 0, 0, 0);
-        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(b0, a1, acc[1][0], 0, 0, 0);
-        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(b1, a1, acc[1][1], 0, 0, 0);
+        for (int i = 0; i < 8; ++i) {
+          const int kk = 8 * h + i;
+          const float a0 = As[kk][r], a1 = As[kk][32 + r];
+          const float b0 = Bs[kk][r], b1 = Bs[kk][32 + r];
+          acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(b0, a0, acc[0][0], 0, 0, 0);
+          acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(b1, a0, acc[0][1], 0, 0, 0);
+          acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(b0, a1, acc[1][0], 0, 0, 0);
+          acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(b1, a1, acc[1][1], 0, 0, 0);
+        }
       }
       __builtin_amdgcn_wave_barrier();
     }
@@ -398,14 +493,14 @@ __global__ __launch_bounds__(512) void router_gemm_kernel(const void* __restrict
   }
 }
 
-template <int AL, int BL, int SK, bool BIAS>
+template <int AL, int BL, int SK, bool BIAS, bool MC16 = false>
 static hipError_t run_router(const void* A, int64_t lda, const float* B, int64_t ldb, float* C,
                              int64_t ldc, int64_t M, int64_t N, int64_t K, const float* bias,
                              hipStream_t s) {
   const int64_t tiles = ((M + 63) / 64) * ((N + 63) / 64);
   const int64_t blocks = SK > 1 ? tiles : (tiles + 7) / 8;
   if (blocks <= 0) return hipSuccess;
-  router_gemm_kernel<AL, BL, SK, BIAS><<<dim3(static_cast<unsigned>(blocks)), 512, 0, s>>>(
+  router_gemm_kernel<AL, BL, SK, BIAS, MC16><<<dim3(static_cast<unsigned>(blocks)), 512, 0, s>>>(
       A, lda, B, ldb, C, ldc, M, N, K, bias);
   return hipGetLastError();
 }
@@ -429,52 +524,6 @@ static hipError_t run_f32(const TA* A, int64_t lda, const float* B, int64_t ldb,
   gemm_f32_kernel<TA, A_MC, B_KC, GRP, EPI, TC><<<grid, 256, 0, s>>>(
       A, lda, B, ldb, strideB, C, ldc, strideC, off, G, M, N, K, bias, ab, H, accumulate);
   return hipGetLastError();
-}
-
-// ---- router products on the bf16 matrix cores, fp32-accurate ----------------
-// An fp32 operand v is split exactly into three bf16 terms, v = hi + mid + lo
-// + r: hi = bf16(v), mid = bf16(v - hi), lo = bf16(v - hi - mid), each
-// rounded to nearest even; both residuals are exact in fp32 (each is v with
-// its leading bits removed), and |r| is about 2^-24 |v|, the rounding of an
-// fp32 value.  A product of two split operands keeps the term pairs whose
-// combined weight is at least 2^-16 (hi.hi, hi.mid, mid.hi, hi.lo, lo.hi,
-// mid.mid); every bf16 product is exact in the fp32 accumulator.  So the
-// result carries fp32 accuracy while the matrix cores run at their bf16 rate
-// (the router stays FP32 in what it computes).  Activations that are already
-// bf16 need no split (one term).
-//
-// C[m, n] = sum_k A[m, k] B(k, n), one wave per 64 x 64 tile as 2 x 2 MFMA
-// 32x32x16 blocks, operands loaded straight into the MFMA fragments: lane
-// half h of a 16-deep step holds k = 8 h .. 8 h + 7 of its row (A) or column
-// (B).  A is k-contiguous (x: bf16 or fp32; d_logits: fp32).  B is W_r: for
-// the logits W_r[k, n] (k strided: eight scalar loads per fragment, L2
-// resident), for the router's dx W_r[n, k] (k-contiguous).  SK = 8: the 8
-// waves of a workgroup split the contraction of one tile and add their
-// partials in wave order through LDS.
-typedef __bf16 bf16x8_rt __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4_rt __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float bf16_lo_f(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// eight fp32 values -> their hi, mid and lo bf16 terms
-__device__ __forceinline__ void split3x8(const float (&v)[8], bf16x8_rt (&t)[3]) {
-#pragma clang fp contract(off)
-  u32x4_rt h, m, l;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float a = v[2 * i], b = v[2 * i + 1];
-    const uint32_t hw = f32x2_to_bf16x2(a, b);
-    const float ra = a - bf16_lo_f(hw), rb = b - bf16_hi_f(hw);
-    const uint32_t mw = f32x2_to_bf16x2(ra, rb);
-    const float sa = ra - bf16_lo_f(mw), sb = rb - bf16_hi_f(mw);
-    h[i] = hw;
-    m[i] = mw;
-    l[i] = f32x2_to_bf16x2(sa, sb);
-  }
-  t[0] = __builtin_bit_cast(bf16x8_rt, h);
-  t[1] = __builtin_bit_cast(bf16x8_rt, m);
-  t[2] = __builtin_bit_cast(bf16x8_rt, l);
 }
 
 __device__ __forceinline__ float4 ld4g(const float* p, bool ok) {
@@ -706,9 +755,9 @@ hipError_t launch_router_bwd(const void* x, int x_dtype, const float* w_r, const
       if (T == 0)
         err = launch_fill_zero(dw_r, d * E, s);
       else if (x_dtype == 0)
-        err = run_router<RA_MC_F32, RB_NC, 8, false>(x, d, dz, E, dw_r, E, d, E, T, nullptr, s);
+        err = run_router<RA_MC_F32, RB_NC, 8, false, true>(x, d, dz, E, dw_r, E, d, E, T, nullptr, s);
       else
-        err = run_router<RA_MC_BF16, RB_NC, 8, false>(x, d, dz, E, dw_r, E, d, E, T, nullptr, s);
+        err = run_router<RA_MC_BF16, RB_NC, 8, false, true>(x, d, dz, E, dw_r, E, d, E, T, nullptr, s);
       if (err != hipSuccess) return err;
     }
     if (dx_r && T > 0)
