@@ -179,17 +179,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const TA* __restrict__ A,
 }
 
 
-// ---- router GEMMs: one wave per 64 x 64 output tile ---------------------------
-// The router projection and its two backward products on the fp32 matrix
-// cores (MFMA 32x32x2 fp32: fp32 products and sums, twice the rate of
-// unpacked fp32 FMAs): a wave owns a 64 x 64 tile as 2 x 2 MFMA blocks.  Each
-// wave stages its own 16-deep operand slices in its own 8 KiB of LDS as
-// [k][64] and prefetches the next slice into registers while it computes, so
-// the main loop has no workgroup barrier.  SK = 8: the workgroup's 8 waves
-// split the contraction of one tile and add their partial sums through LDS in
-// wave order (deterministic, no workspace); SK = 1: the 8 waves take 8 tiles.
-// Requires 16-byte aligned operands, the A and B contiguous extents multiples
-// of 8 (bf16) or 4 (fp32) elements.
+// ---- router GEMMs --------------------------------------------------------------
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 enum { RA_KC_BF16 = 0, RA_KC_F32 = 1, RA_MC_BF16 = 2, RA_MC_F32 = 3 };  // A: k- or m-contiguous
 enum { RB_NC = 0, RB_KC = 1 };                                          // B (fp32): n- or k-contiguous
@@ -299,6 +289,17 @@ __device__ __forceinline__ void mc16_slice(f32x16_t (&acc)[2][2], const float (*
             b[ni][A_BF16 ? PB1[q] : PB[q]], a[mi][A_BF16 ? PA1[q] : PA[q]], acc[mi][ni], 0, 0, 0);
 }
 
+// ---- router weight gradient: one wave per 64 x 64 output tile, LDS slices ----
+// dW_r = x^T . d_logits contracts over tokens, and both operands are strided
+// along it, so each wave stages its own 16-deep operand slices in its own
+// 8 KiB of LDS as [k][64] (prefetching the next slice into registers while it
+// computes, so the main loop has no workgroup barrier) and feeds the split
+// bf16 products below from them: a wave owns a 64 x 64 tile as 2 x 2 MFMA
+// blocks.  SK = 8: the workgroup's 8 waves split the contraction of one tile
+// and add their partial sums through LDS in wave order (deterministic, no
+// workspace); SK = 1: the 8 waves take 8 tiles.  Requires 16-byte aligned
+// operands, the A and B contiguous extents multiples of 8 (bf16) or 4 (fp32)
+// elements.
 template <int AL, int BL>
 __device__ __forceinline__ void router_load(RSlice& r, const void* A, int64_t lda, const float* B,
                                             int64_t ldb, int64_t m0, int64_t n0, int64_t k0,
@@ -375,11 +376,7 @@ __device__ __forceinline__ void router_stage(const RSlice& r, float (*As)[64], f
   }
 }
 
-// MC16: the products on the bf16 matrix cores with fp32 accuracy (B split
-// into three bf16 terms, A too unless its values are bf16; see the split
-// below), reading each lane's 8 contraction values of a column from the LDS
-// slice; else one fp32 MFMA 32x32x2 per contraction position.
-template <int AL, int BL, int SK, bool BIAS, bool MC16 = false>
+template <int AL, int BL, int SK, bool BIAS>
 __global__ __launch_bounds__(512) void router_gemm_kernel(const void* __restrict__ A, int64_t lda,
                                                           const float* __restrict__ B,
                                                           int64_t ldb, float* __restrict__ C,
@@ -400,10 +397,10 @@ __global__ __launch_bounds__(512) void router_gemm_kernel(const void* __restrict
   }
   float(*As)[64] = lds[wave][0];
   float(*Bs)[64] = lds[wave][1];
-  // MFMA 32x32x2 fp32, computed as D[n][m] so that lane r of a block holds
+  // MFMA 32x32x16 bf16, computed as D[n][m] so that lane r of a block holds
   // output row m = r: acc[mi][ni][v] is C[32 mi + r][32 ni + 8 (v / 4) +
   // 4 h + v % 4], h = lane / 32.  Lane half h feeds contraction positions
-  // 8 h .. 8 h + 7 of each 16-deep slice, one per MFMA, for A and for B alike.
+  // 8 h .. 8 h + 7 of each 16-deep slice, for A and for B alike.
   f32x16_t acc[2][2];
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
@@ -420,20 +417,7 @@ __global__ __launch_bounds__(512) void router_gemm_kernel(const void* __restrict
       router_stage<AL, BL>(rs, As, Bs, lane);
       __builtin_amdgcn_wave_barrier();
       if (k0 + 16 < k_hi) router_load<AL, BL>(rs, A, lda, B, ldb, m0, n0, k0 + 16, k_hi, M, N, lane);
-      if constexpr (MC16) {
-        mc16_slice<AL == RA_KC_BF16 || AL == RA_MC_BF16>(acc, As, Bs, r, h);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int kk = 8 * h + i;
-          const float a0 = As[kk][r], a1 = As[kk][32 + r];
-          const float b0 = Bs[kk][r], b1 = Bs[kk][32 + r];
-          acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(b0, a0, acc[0][0], 0, 0, 0);
-          acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(b1, a0, acc[0][1], 0, 0, 0);
-          acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(b0, a1, acc[1][0], 0, 0, 0);
-          acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(b1, a1, acc[1][1], 0, 0, 0);
-        }
-      }
+      mc16_slice<AL == RA_KC_BF16 || AL == RA_MC_BF16>(acc, As, Bs, r, h);
       __builtin_amdgcn_wave_barrier();
     }
   }
@@ -493,14 +477,14 @@ __global__ __launch_bounds__(512) void router_gemm_kernel(const void* __restrict
   }
 }
 
-template <int AL, int BL, int SK, bool BIAS, bool MC16 = false>
+template <int AL, int BL, int SK, bool BIAS>
 static hipError_t run_router(const void* A, int64_t lda, const float* B, int64_t ldb, float* C,
                              int64_t ldc, int64_t M, int64_t N, int64_t K, const float* bias,
                              hipStream_t s) {
   const int64_t tiles = ((M + 63) / 64) * ((N + 63) / 64);
   const int64_t blocks = SK > 1 ? tiles : (tiles + 7) / 8;
   if (blocks <= 0) return hipSuccess;
-  router_gemm_kernel<AL, BL, SK, BIAS, MC16><<<dim3(static_cast<unsigned>(blocks)), 512, 0, s>>>(
+  router_gemm_kernel<AL, BL, SK, BIAS><<<dim3(static_cast<unsigned>(blocks)), 512, 0, s>>>(
       A, lda, B, ldb, C, ldc, M, N, K, bias);
   return hipGetLastError();
 }
@@ -755,9 +739,9 @@ hipError_t launch_router_bwd(const void* x, int x_dtype, const float* w_r, const
       if (T == 0)
         err = launch_fill_zero(dw_r, d * E, s);
       else if (x_dtype == 0)
-        err = run_router<RA_MC_F32, RB_NC, 8, false, true>(x, d, dz, E, dw_r, E, d, E, T, nullptr, s);
+        err = run_router<RA_MC_F32, RB_NC, 8, false>(x, d, dz, E, dw_r, E, d, E, T, nullptr, s);
       else
-        err = run_router<RA_MC_BF16, RB_NC, 8, false, true>(x, d, dz, E, dw_r, E, d, E, T, nullptr, s);
+        err = run_router<RA_MC_BF16, RB_NC, 8, false>(x, d, dz, E, dw_r, E, d, E, T, nullptr, s);
       if (err != hipSuccess) return err;
     }
     if (dx_r && T > 0)
