@@ -345,6 +345,33 @@ def test_router_logits(gpu, dt, T, d, E, bias):
     assert_close("dx_router", dxr, rx, TOL["f32"])
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_router_fp32_accuracy(gpu, dt):
+    """The router products keep fp32 accuracy although they run on the bf16
+    matrix cores: operands whose 24 mantissa bits all matter (a spread of
+    magnitudes, values just off bf16 rounding boundaries) must come out within
+    a few fp32 roundings of the fp64 products -- a single bf16 term per
+    operand would be off by ~2^-9."""
+    T, d, E = 256, 1024, 64
+    g = torch.Generator().manual_seed(71)
+    mag = torch.exp2(torch.randint(-8, 9, (d, E), generator=g).float())
+    frac = 1.0 + torch.rand((d, E), generator=g) * 2.0 ** -7 + torch.rand((d, E), generator=g) * 2.0 ** -16
+    sign = torch.where(torch.rand((d, E), generator=g) < 0.5, -1.0, 1.0)
+    w_r = (sign * mag * frac).float().contiguous()
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    x = inputs.normal((T, d), 1.0, 72, 0, "cpu", tdt)
+    dz = (torch.randn((T, E), generator=g) * (1.0 + torch.rand((T, E), generator=g) * 2.0 ** -12)).float()
+    lg = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    abi.moe_router_logits(x.to(DEV), w_r.to(DEV), None, lg)
+    assert_close("logits", lg, oracle.router_logits(np64(x), w_r.numpy(), None), 2e-6)
+    dwr = torch.empty((d, E), dtype=torch.float32, device=DEV)
+    dxr = torch.empty((T, d), dtype=torch.float32, device=DEV)
+    abi.moe_router_logits_bwd(x.to(DEV), w_r.to(DEV), dz.to(DEV), dwr, dxr)
+    rw, rx = oracle.router_logits_bwd(np64(x), w_r.numpy(), dz.numpy())
+    assert_close("dW_r", dwr, rw, 2e-6)
+    assert_close("dx_router", dxr, rx, 2e-6)
+
+
 def test_bf16_rounding_bit_exact(gpu):
     """The kernels' fp32 -> bf16 rounding is round-to-nearest-even, pinned bit-exactly
     against torch's CPU cast: permute backward with k = 1, a zero gradient and an fp32
