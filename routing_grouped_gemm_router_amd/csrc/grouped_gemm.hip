@@ -283,12 +283,17 @@ __device__ __forceinline__ void tile_in_group(uint32_t tl, uint32_t mt_g, uint32
 }
 
 // Of a paired launch, the 256 x 256 tiling does the work when it needs at most
-// 20/31 of the row tiles of the 128-row tiling.  A 256 x 256 tile costs about
-// 1.8 times a 128 x 256 one and its ragged last tile rather less (a wave with
-// no rows idles); over 256 groups with 7168 x 2048 and 4096 x 7168 weights the
-// 256-row tiling measured faster at every tile ratio from 1.59 up and slower
-// at 1.5 and below.
+// 20/31 of the row tiles of the 128-row tiling (plain epilogue), or at most
+// 10/19 of them (SwiGLU and its backward).  A 256 x 256 tile costs about 1.8
+// times a 128 x 256 one and its ragged last tile rather less (a wave with no
+// rows idles); over 256 groups with 7168 x 2048 and 4096 x 7168 weights the
+// 256-row tiling of the plain epilogue measured faster at every tile ratio
+// from 1.59 up and slower at 1.5 and below.  With the SwiGLU epilogues it was
+// 16 % (forward) and 9 % (backward) slower at a ratio of 1.56, and 5 % and
+// 12 % faster at 2 (one group of 8192 rows).
+template <int MODE>
 __device__ __forceinline__ bool rows256_preferred(int t128, int t256) {
+  if (MODE == FWD_SWIGLU || MODE == DGRAD_SWIGLU_BWD) return 10LL * t128 >= 19LL * t256;
   return 20LL * t128 >= 31LL * t256;
 }
 
@@ -949,7 +954,7 @@ __global__ __launch_bounds__(Cfg<WN>::THREADS, Cfg<WN>::WG_PER_CU) void gg_kerne
         run += (s_off[g + 1] - s_off[g] + BM - 1) / BM;
       }
       if (lane == 63) s_pre[p.G] = incl;
-      if (MODE == FWD || MODE == DGRAD) {
+      if (MODE != WGRAD) {
         int t256 = 0;
         for (int g = g0; g < g1; ++g) t256 += (s_off[g + 1] - s_off[g] + 255) / 256;
         t256 = wave_sum(t256);
@@ -957,7 +962,7 @@ __global__ __launch_bounds__(Cfg<WN>::THREADS, Cfg<WN>::WG_PER_CU) void gg_kerne
       }
     }
     __syncthreads();
-    if ((MODE == FWD || MODE == DGRAD) && p.pair256 && rows256_preferred(s_pre[p.G], s_t256))
+    if (MODE != WGRAD && p.pair256 && rows256_preferred<MODE>(s_pre[p.G], s_t256))
       return;  // the paired 256-row launch does the work
     NT = p.Nout / BN;
     total = static_cast<int64_t>(s_pre[p.G]) * NT;
@@ -1052,8 +1057,8 @@ static hipError_t run_cfg(const Params& p, int64_t tiles_upper_bound, hipStream_
   return hipGetLastError();
 }
 
-// bf16 forward / dgrad without epilogue in 256 x 256 tiles (defined below);
-// false when the shape does not fit them
+// bf16 row-group modes in 256 x 256 tiles (defined below); false when the
+// shape does not fit them
 template <int MODE>
 static bool launch_rows256(const Params& p, hipStream_t s, hipError_t& err);
 
@@ -1063,7 +1068,7 @@ static bool launch_rows256(const Params& p, hipStream_t s, hipError_t& err);
 template <int MODE, int Q>
 static hipError_t run_rows(const Params& p, hipStream_t s) {
   const int64_t mt = p.M / BM + p.G;
-  if constexpr (Q == P_BF16 && (MODE == FWD || MODE == DGRAD)) {
+  if constexpr (Q == P_BF16) {
     // both tilings are launched; from the group sizes each kernel finds on
     // the device which of the two does the work, and the other one exits
     Params q = p;
@@ -1428,11 +1433,14 @@ __global__ __launch_bounds__(512, 1) void wgrad256_kernel(Params p) {
 // ---- bf16 row-group GEMMs (forward, dgrad), 256 x 256 tiles ------------------
 // The forward (B = W_g [K, N] read in the [k][col] layout) and the data
 // gradient (B = W_g [N, K] rows, k-contiguous) in tiles of 256 rows of a group
-// x 256 product columns, waves and ring as in the weight-gradient kernel.  A
-// group's last row tile is ragged (its rows past the group read as zero, so
-// nothing is fetched for them); the larger tile halves the row tiles of a
-// large group, hence its re-reads of the weight slabs, and moves a third
-// fewer operand bytes per FLOP into LDS.
+// x 256 product columns, waves and ring as in the weight-gradient kernel, with
+// the same epilogues as the 128-row tiles: plain, SwiGLU (a tile holds 128
+// gate columns and the matching 128 up columns, each wave 64 + 64 of them, so
+// that H is formed in registers) and SwiGLU backward.  A group's last row tile
+// is ragged (its rows past the group read as zero, so nothing is fetched for
+// them); the larger tile halves the row tiles of a large group, hence its
+// re-reads of the weight slabs, and moves a third fewer operand bytes per FLOP
+// into LDS.
 template <int MODE>
 __global__ __launch_bounds__(512, 1) void rows256_kernel(Params p) {
   using namespace w256;
@@ -1490,7 +1498,7 @@ __global__ __launch_bounds__(512, 1) void rows256_kernel(Params p) {
     if (lane == 0) s_t128 = t128;
   }
   __syncthreads();
-  if (p.pair256 && !rows256_preferred(s_t128, s_pre[p.G])) return;  // the 128-row launch works
+  if (p.pair256 && !rows256_preferred<MODE>(s_t128, s_pre[p.G])) return;  // the 128-row launch works
 
   const uint32_t NT = static_cast<uint32_t>(p.Nout / BMN);
   const int64_t total = static_cast<int64_t>(s_pre[p.G]) * NT;
@@ -1536,7 +1544,13 @@ __global__ __launch_bounds__(512, 1) void rows256_kernel(Params p) {
       for (int i = 0; i < 4; ++i) {
         const int q = wave * 4 + i, slab = q >> 4;
         const int kr = 4 * (q & 15) + (lane >> 4), c = (lane & 15) ^ swz_nc(kr);
-        vb[i] = static_cast<uint32_t>((kr * N + t.col0 + slab * 128 + 8 * c) * 2);
+        // SwiGLU: tile n holds gate columns 128 n .. + 127 and the matching up
+        // columns; slab s (one wave column) its gate columns 128 n + 64 s ..
+        // + 63 as chunks 0-7 and the up columns as chunks 8-15
+        const int64_t col = MODE == FWD_SWIGLU
+                                ? (c >> 3) * (N / 2) + t.col0 / 2 + slab * 64 + (c & 7) * 8
+                                : t.col0 + slab * 128 + 8 * c;
+        vb[i] = static_cast<uint32_t>((kr * N + col) * 2);
       }
     } else {  // W_g [N, Kc]: rows col0 + 128 slab + 8 (q % 16) ..
       rb = make_rsrc(p.B + static_cast<int64_t>(t.g) * N * Kc * 2, static_cast<uint64_t>(N) * Kc * 2);
@@ -1633,27 +1647,107 @@ __global__ __launch_bounds__(512, 1) void rows256_kernel(Params p) {
         LDS_AS char* stg = lring + cp_slot * STAGE + wave * 8192;
         bf16_t* out = static_cast<bf16_t*>(p.C);
         const int64_t row_w = cp_t.row0 + wm * 64, col_w = cp_t.col0 + wn * 128;
+        const int64_t fh = N / 2;
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii) {
           if (ii * 32 >= rows_w) break;
+          if (MODE != FWD_SWIGLU || out != nullptr) {
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
+            for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-            for (int vg = 0; vg < 4; ++vg) {
+              for (int vg = 0; vg < 4; ++vg) {
+                const int m = lane & 31;
+                const int n = jj * 32 + vg * 8 + (lane >> 5) * 4;
+                u32x2_t w;
+                w.x = pack2(acc[ii][jj][vg * 4 + 0], acc[ii][jj][vg * 4 + 1]);
+                w.y = pack2(acc[ii][jj][vg * 4 + 2], acc[ii][jj][vg * 4 + 3]);
+                *(LDS_AS u32x2_t*)(stg + stg_off16(m, n >> 3) + (n & 7) * 2) = w;
+              }
+            // 32 rows x 16 chunks; lane handles chunks lane + 64 i
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int idx = lane + 64 * i;
+              const int m = idx >> 4, c = idx & 15;
+              const bool valid = ii * 32 + m < rows_w;
+              const int64_t row = row_w + ii * 32 + m;
+              if (MODE == DGRAD_SWIGLU_BWD) {
+                // v = dH[row, col .. col+7] (times the row's routing weight when
+                // it is applied inside the expert); read the matching a and b,
+                // write dA and dB, and with the weight the partial <dH', h> of
+                // the row over each 64 columns (8 consecutive lanes hold them)
+                const int64_t col = col_w + 8 * c;
+                const int64_t w2 = 2 * N;
+                float dot = 0.0f;
+                if (valid) {
+                  const u32x4_t vv = *(const LDS_AS u32x4_t*)(stg + stg_off16(m, c));
+                  float dh[8], a[8], b[8], da[8], db[8];
+                  unpack8(make_uint4(vv.x, vv.y, vv.z, vv.w), dh);
+                  unpack8(*reinterpret_cast<const uint4*>(p.ab + row * w2 + col), a);
+                  unpack8(*reinterpret_cast<const uint4*>(p.ab + row * w2 + N + col), b);
+                  const float rs = p.row_scale ? p.row_scale[row] : 1.0f;
+#pragma unroll
+                  for (int e = 0; e < 8; ++e) {
+                    const float sg = 1.0f / (1.0f + expf(-a[e]));
+                    dot += dh[e] * (a[e] * sg * b[e]);
+                    const float d = rs * dh[e];
+                    da[e] = d * b[e] * sg * (1.0f + a[e] * (1.0f - sg));
+                    db[e] = d * a[e] * sg;
+                  }
+                  *reinterpret_cast<uint4*>(out + row * w2 + col) = pack8(da);
+                  *reinterpret_cast<uint4*>(out + row * w2 + N + col) = pack8(db);
+                }
+                if (p.row_scale) {
+                  dot += __shfl_xor(dot, 1, 64);
+                  dot += __shfl_xor(dot, 2, 64);
+                  dot += __shfl_xor(dot, 4, 64);
+                  if (valid && (c & 7) == 0) p.gate_part[row * (N / 64) + col / 64] = dot;
+                }
+                continue;
+              }
+              if (!valid) continue;
+              const u32x4_t vv = *(const LDS_AS u32x4_t*)(stg + stg_off16(m, c));
+              const int64_t col = MODE == FWD_SWIGLU
+                                      ? (c >> 3) * fh + cp_t.col0 / 2 + wn * 64 + (c & 7) * 8
+                                      : col_w + 8 * c;
+              *reinterpret_cast<u32x4_t*>(out + row * N + col) = vv;
+            }
+          }
+          if (MODE == FWD_SWIGLU) {
+            // H = silu(gate) * up (times the row's routing weight when it is
+            // applied inside the expert) for these 32 rows: blocks jj and
+            // jj + 2 hold matching gate and up columns, 64 per wave
+            float rs = 1.0f;
+            if (p.row_scale) {
               const int m = lane & 31;
-              const int n = jj * 32 + vg * 8 + (lane >> 5) * 4;
-              u32x2_t w;
-              w.x = pack2(acc[ii][jj][vg * 4 + 0], acc[ii][jj][vg * 4 + 1]);
-              w.y = pack2(acc[ii][jj][vg * 4 + 2], acc[ii][jj][vg * 4 + 3]);
-              *(LDS_AS u32x2_t*)(stg + stg_off16(m, n >> 3) + (n & 7) * 2) = w;
+              rs = ii * 32 + m < rows_w ? p.row_scale[row_w + ii * 32 + m] : 0.0f;
             }
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int idx = lane + 64 * i;
-            const int m = idx >> 4, c = idx & 15;
-            if (ii * 32 + m >= rows_w) continue;
-            const u32x4_t vv = *(const LDS_AS u32x4_t*)(stg + stg_off16(m, c));
-            *reinterpret_cast<u32x4_t*>(out + (row_w + ii * 32 + m) * N + col_w + 8 * c) = vv;
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+              for (int vg = 0; vg < 4; ++vg) {
+                const int m = lane & 31;
+                const int n = jj * 32 + vg * 8 + (lane >> 5) * 4;
+                float h[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const float g = acc[ii][jj][vg * 4 + e], u = acc[ii][jj + 2][vg * 4 + e];
+                  h[e] = g / (1.0f + expf(-g)) * u * rs;
+                }
+                u32x2_t w;
+                w.x = pack2(h[0], h[1]);
+                w.y = pack2(h[2], h[3]);
+                *(LDS_AS u32x2_t*)(stg + stg_off16(m, n >> 3) + (n & 7) * 2) = w;
+              }
+            // 32 rows x 8 chunks
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int idx = lane + 64 * i;
+              const int m = idx >> 3, c = idx & 7;
+              if (ii * 32 + m >= rows_w) continue;
+              const u32x4_t vv = *(const LDS_AS u32x4_t*)(stg + stg_off16(m, c));
+              *reinterpret_cast<u32x4_t*>(p.H + (row_w + ii * 32 + m) * fh + cp_t.col0 / 2 + wn * 64 +
+                                          8 * c) = vv;
+            }
           }
         }
       }

@@ -296,11 +296,31 @@ def test_grouped_gemm(gpu, dt, M, G, K, N, empty_frac, skew):
     assert_close("dB accumulate", dB32, 2 * ref_dB, TOL[dt])
 
 
+def _row_tiling(off, n_cols, swiglu):
+    """The row tiling the bf16 row-group kernels pick for these groups: 256-row
+    tiles when the product width is a multiple of 256 and they need at most
+    20/31 (plain epilogue) or 10/19 (SwiGLU epilogues) of the 128-row tiles,
+    else 128-row tiles.  Tests use it only to show that their cases cover both
+    tilings."""
+    c = np.diff(off.numpy())
+    t128, t256 = int(np.ceil(c / 128).sum()), int(np.ceil(c / 256).sum())
+    num, den = (19, 10) if swiglu else (31, 20)
+    return 256 if n_cols % 256 == 0 and den * t128 >= num * t256 else 128
+
+
+# M, G, d, f, row tiling of GEMM 1 forward, of GEMM 2 dgrad (product width f)
+SWIGLU_CASES = [(1000, 1, 256, 256, 256, 256), (900, 6, 256, 256, 128, 128),
+                (1000, 1, 512, 384, 256, 128)]
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_grouped_gemm_swiglu_epilogues(gpu, dt):
+@pytest.mark.parametrize("M,G,d,f,tile_fwd,tile_dgrad", SWIGLU_CASES)
+def test_grouped_gemm_swiglu_epilogues(gpu, dt, M, G, d, f, tile_fwd, tile_dgrad):
+    print(f"swiglu epilogues {dt} M={M} G={G} d={d} f={f}", flush=True)
     tdt = torch.float32 if dt == "f32" else torch.bfloat16
-    M, G, d, f = 900, 6, 256, 256
     off, X, W13, _ = _gemm_inputs(M, G, d, 2 * f, 0.2, 0.0, tdt, seed=10)
+    if dt == "bf16":
+        assert (_row_tiling(off, 2 * f, True), _row_tiling(off, f, True)) == (tile_fwd, tile_dgrad)
     dH = inputs.normal((M, f), 1.0, 99, 0, "cpu", tdt)
     W2 = inputs.normal((G, f, d), f ** -0.5, 98, 0, "cpu", tdt)
     dY = inputs.normal((M, d), 1.0, 97, 0, "cpu", tdt)
@@ -444,7 +464,7 @@ def test_route_replay_bit_exact(gpu, E, k, score, renorm, kind):
     assert r["changed"] == (kind == "corrupt")
 
 
-@pytest.mark.parametrize("M,G,d,f", [(900, 6, 256, 256), (3000, 9, 512, 384)])
+@pytest.mark.parametrize("M,G,d,f", [(900, 6, 256, 256), (3000, 9, 512, 384), (1500, 2, 256, 256)])
 def test_gated_ffn_ops(gpu, M, G, d, f):
     """Routing weight applied inside the expert: the permuted-row weights
     (bit copy), GEMM 1 with H' = w * silu(a) * b, GEMM 2's dgrad with
