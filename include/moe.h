@@ -272,8 +272,9 @@ int moe_permute_bwd(const void* dx_perm, int dtype, const int32_t* dst_row, int6
  *   epilogue MOE_EPI_SWIGLU: N = 2f, columns [0, f) are the gate a and [f, 2f)
  *     the up projection b; write C (may be NULL to skip) and
  *     H [M, f] = silu(a) * b, silu(a) = a / (1 + exp(-a)), from the fp32 sums.
- * Limits (bf16): K % 64 == 0, N % 128 == 0 (SWIGLU: f % 64 == 0);
- *        (fp32): none beyond sizes >= 1.  G <= 1024. */
+ * Limits (bf16): K % 64 == 0, N % 128 == 0 (SWIGLU: f % 64 == 0), K * N < 2^31
+ *        (one expert's weights under 4 GiB); (fp32): none beyond sizes >= 1.
+ *        G <= 1024. */
 int moe_grouped_gemm_fwd(const void* A, const void* B, const int64_t* offsets, int32_t G, int64_t M,
                          int64_t K, int64_t N, int dtype, int epilogue, void* C, void* H,
                          void* stream);
@@ -283,7 +284,8 @@ int moe_grouped_gemm_fwd(const void* A, const void* B, const int64_t* offsets, i
  *     pre-activations are ab [M, 2K] (a = ab[:, :K], b = ab[:, K:]); write
  *     dA = dAB [M, 2K] with dAB[:, :K] = dH * b * s * (1 + a (1 - s)),
  *     dAB[:, K:] = dH * silu(a), s = sigmoid(a).  `ab` is NULL otherwise.
- * Limits (bf16): N % 64 == 0, K % 128 == 0.  (fp32): none.  G <= 1024. */
+ * Limits (bf16): N % 64 == 0, K % 128 == 0, K * N < 2^31.  (fp32): none.
+ * G <= 1024. */
 int moe_grouped_gemm_dgrad(const void* dC, const void* B, const int64_t* offsets, int32_t G,
                            int64_t M, int64_t K, int64_t N, int dtype, int epilogue,
                            const void* ab, void* dA, void* stream);
@@ -291,7 +293,8 @@ int moe_grouped_gemm_dgrad(const void* dC, const void* B, const int64_t* offsets
 /* Weight gradient: dB[g] = A[rows g]^T . dC[rows g]   A [M, K], dC [M, N], dB [G, K, N].
  * The contraction runs over each group's rows (ragged).  dB_dtype is `dtype`
  * or MOE_F32.  accumulate != 0 adds into dB instead of overwriting it.
- * Limits (bf16): K % 128 == 0, N % 128 == 0.  (fp32): none.  G <= 1024. */
+ * Limits (bf16): K % 128 == 0, N % 128 == 0, M * K < 2^31, M * N < 2^31.
+ * (fp32): none.  G <= 1024. */
 int moe_grouped_gemm_wgrad(const void* A, const void* dC, const int64_t* offsets, int32_t G,
                            int64_t M, int64_t K, int64_t N, int dtype, int dB_dtype,
                            int accumulate, void* dB, void* stream);
@@ -357,7 +360,8 @@ int moe_quant_fp8_token_tiles(const void* x, const int64_t* offsets, const int64
  *            [N/128, M]; B (q_dgrad, s_dgrad)
  *   wgrad:   dB[g] = deq(A)^T . deq(dC) over group g's padded rows; A_t [K, ldm],
  *            dC_t [N, ldm] and scales from moe_quant_fp8_token_tiles
- * Limits: K % 128 == 0, N % 128 == 0 (forward SWIGLU: N / 2 % 64 == 0). */
+ * Limits: K % 128 == 0, N % 128 == 0 (forward SWIGLU: N / 2 % 64 == 0),
+ * K * N < 2^32 (one expert's weight codes under 4 GiB). */
 int moe_grouped_gemm_fp8_fwd(const uint8_t* A, const float* a_scale_t, const uint8_t* B_fwd,
                              const float* b_scale_fwd, const int64_t* offsets, int32_t G,
                              int64_t M, int64_t K, int64_t N, int epilogue, void* C, void* H,
@@ -431,7 +435,8 @@ int moe_quant_mxfp8_token_tiles(const void* x, int64_t x_rows, const int32_t* sr
  *   wgrad:   dB[g] = deq(A)^T . deq(dC) over group g's padded rows; A_t
  *            [K, ldm], dC_t [N, ldm] and their scales from
  *            moe_quant_mxfp8_token_tiles
- * Limits: K % 128 == 0, N % 128 == 0 (forward SWIGLU: N / 2 % 64 == 0). */
+ * Limits: K % 128 == 0, N % 128 == 0 (forward SWIGLU: N / 2 % 64 == 0),
+ * K * N < 2^32 (one expert's weight codes under 4 GiB). */
 int moe_grouped_gemm_mxfp8_fwd(const uint8_t* A, const uint8_t* a_scale, const uint8_t* B_fwd,
                                const uint8_t* b_scale_fwd, const int64_t* offsets, int32_t G,
                                int64_t M, int64_t K, int64_t N, int epilogue, void* C, void* H,

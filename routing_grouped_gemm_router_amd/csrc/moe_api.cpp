@@ -324,6 +324,11 @@ int moe_permute_bwd(const void* dx_perm, int dtype, const int32_t* dst_row, int6
                     "moe_permute_bwd");
 }
 
+// a * b < lim for non-negative a, b, without forming the product
+static bool prod_below(int64_t a, int64_t b, int64_t lim) {
+  return a >= 0 && b >= 0 && (b == 0 || a <= (lim - 1) / b);
+}
+
 static int check_gemm(const char* fn, const void* p0, const void* p1, const int64_t* off, int32_t G,
                       int64_t M, int64_t K, int64_t N, int dtype) {
   REQUIRE(valid_dtype(dtype), MOE_ERR_DTYPE, "%s: bad dtype %d", fn, dtype);
@@ -331,6 +336,9 @@ static int check_gemm(const char* fn, const void* p0, const void* p1, const int6
           G, static_cast<long long>(M), static_cast<long long>(K), static_cast<long long>(N));
   REQUIRE(G <= 1024, MOE_ERR_UNSUPPORTED, "%s: G=%d above 1024", fn, G);
   REQUIRE(M / 64 + G < (int64_t(1) << 31) / 64, MOE_ERR_UNSUPPORTED, "%s: M too large", fn);
+  // the bf16 kernels address one expert's weights with 32-bit byte offsets
+  REQUIRE(dtype != MOE_BF16 || prod_below(K, N, int64_t(1) << 31), MOE_ERR_UNSUPPORTED,
+          "%s: K*N must be below 2^31 (one expert's bf16 weights under 4 GiB)", fn);
   if (M == 0) return MOE_OK;  // nothing to read or write
   REQUIRE(p0 && p1 && off, MOE_ERR_NULL, "%s: operands and offsets are required", fn);
   REQUIRE(aligned16(p0) && aligned16(p1), MOE_ERR_UNSUPPORTED, "%s: operands must be 16-byte aligned",
@@ -413,6 +421,9 @@ int moe_grouped_gemm_wgrad(const void* A, const void* dC, const int64_t* offsets
     REQUIRE(K % 128 == 0 && N % 128 == 0, MOE_ERR_UNSUPPORTED,
             "%s: bf16 needs K %% 128 == 0 and N %% 128 == 0 (K=%lld N=%lld)", fn,
             static_cast<long long>(K), static_cast<long long>(N));
+    // a group's rows of A and dC are addressed with 32-bit byte offsets
+    REQUIRE(prod_below(M, K, int64_t(1) << 31) && prod_below(M, N, int64_t(1) << 31),
+            MOE_ERR_UNSUPPORTED, "%s: M*K and M*N must be below 2^31 for bf16", fn);
     REQUIRE(aligned16(A) && aligned16(dC), MOE_ERR_UNSUPPORTED, "%s: operands must be 16-byte aligned",
             fn);
   }
@@ -634,6 +645,9 @@ static int check_gemm_fp8(const char* fn, const void* a, const void* sa, const v
   REQUIRE(K % 128 == 0 && N % 128 == 0, MOE_ERR_UNSUPPORTED, "%s: K and N must be multiples of 128",
           fn);
   REQUIRE(M / 64 + G < (int64_t(1) << 31) / 64, MOE_ERR_UNSUPPORTED, "%s: M too large", fn);
+  // one expert's weight codes are addressed with 32-bit byte offsets
+  REQUIRE(prod_below(K, N, int64_t(1) << 32), MOE_ERR_UNSUPPORTED,
+          "%s: K*N must be below 2^32 (one expert's weight codes under 4 GiB)", fn);
   if (M == 0) return MOE_OK;
   REQUIRE(a && sa && b && sb && off, MOE_ERR_NULL, "%s: operands, scales and offsets are required",
           fn);

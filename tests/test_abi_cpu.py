@@ -66,6 +66,12 @@ def _fake(n=1 << 20):
     (("moe_grouped_gemm_fwd", (_fake(), _fake(), _fake(), 4, 100, 128, 256, 1, 2, _fake(), None, None)), -2),
     (("moe_grouped_gemm_fwd", (_fake(), _fake(), _fake(), 2000, 100, 128, 256, 1, 0, _fake(), None, None)), -4),
     (("moe_grouped_gemm_fwd", (None, _fake(), _fake(), 4, 100, 128, 256, 1, 0, _fake(), None, None)), -1),
+    # one expert's bf16 weights at 4 GiB or more (32-bit offsets inside the kernels)
+    (("moe_grouped_gemm_fwd", (_fake(), _fake(), _fake(), 4, 100, 65536, 32768, 1, 0, _fake(), None, None)), -4),
+    (("moe_grouped_gemm_dgrad", (_fake(), _fake(), _fake(), 4, 100, 65536, 32768, 1, 0, None, _fake(), None)), -4),
+    (("moe_grouped_gemm_wgrad", (_fake(), _fake(), _fake(), 4, 1 << 20, 4096, 128, 1, 1, 0, _fake(), None)), -4),
+    (("moe_grouped_gemm_fp8_fwd", (_fake(), _fake(), _fake(), _fake(), _fake(), 4, 100, 65536, 65536, 0,
+                                   _fake(), None, None)), -4),
     (("moe_grouped_gemm_dgrad", (_fake(), _fake(), _fake(), 4, 100, 96, 128, 1, 0, None, _fake(), None)), -4),
     (("moe_grouped_gemm_dgrad", (_fake(), _fake(), _fake(), 4, 100, 128, 128, 1, 2, None, _fake(), None)), -1),
     (("moe_grouped_gemm_wgrad", (_fake(), _fake(), _fake(), 4, 100, 128, 96, 1, 1, 0, _fake(), None)), -4),
