@@ -499,7 +499,10 @@ def grouped_gemm_wgrad(A, dC, offsets):
 
 def silu(a):
     a = f64(a)
-    return a / (1.0 + np.exp(-a))
+    # exp(-a) overflows to inf for a below about -709; a / inf is then the
+    # function's limit (-0.0), so the overflow is expected and not reported
+    with np.errstate(over="ignore"):
+        return a / (1.0 + np.exp(-a))
 
 
 def swiglu(ab):
