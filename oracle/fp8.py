@@ -182,7 +182,7 @@ def dequantize_token_tiles(q, s, block=128):
 
 
 def layer_fp8(x, w_r, w13, w2, dout, k, score, renorm, logit_bias=None, shared=None,
-              quantize=True, block=128, recipe="block"):
+              quantize=True, block=128, recipe="block", trace=None):
     """Forward and backward of the MoE layer with every expert-GEMM input
     quantized blockwise to E4M3 (the fp8 recipe above), computed as fp64
     grouped GEMMs on the dequantized values.
@@ -198,7 +198,10 @@ def layer_fp8(x, w_r, w13, w2, dout, k, score, renorm, logit_bias=None, shared=N
     identity (the exact layer).  ``recipe="mx"``: MXFP8 instead (1 x 32
     blocks along every operand's contraction axis, E8M0 scales; a weight then
     has one quantization per GEMM that reads it).  Returns a dict of outputs
-    and gradients.
+    and gradients.  ``trace``, if a dict, receives every GEMM's operands as
+    fed to it (dequantized), keyed "<gemm>.A" / "<gemm>.B", together with the
+    tensors they were quantized from ("src.<name>") and the padded offsets;
+    recording changes nothing that is computed.
     """
     from . import moe_oracle as o
 
@@ -235,51 +238,65 @@ def layer_fp8(x, w_r, w13, w2, dout, k, score, renorm, logit_bias=None, shared=N
         qq, ss, poff = quantize_token_tiles(to_bf16(a), offsets, block)
         return dequantize_token_tiles(qq, ss, block), poff
 
+    def rec(name, a):
+        if trace is not None:
+            trace[name] = a
+        return a
+
     x = o.f64(x)
     T = x.shape[0]
     z = o.router_logits(x, w_r, logit_bias)
     r = o.route(z, k, score, renorm)
     off = r["offsets"]
-    w13d, w2d = q_weights(w13), q_weights(w2)
+    w13d, w2d = rec("fwd1.B", q_weights(w13)), rec("fwd2.B", q_weights(w2))
     w13g, w2g = (q_weights(w13, "dgrad"), q_weights(w2, "dgrad")) if mx else (w13d, w2d)
-    xp = o.permute(x, r["src_token"])
-    ab = o.grouped_gemm_fwd(q_rows(xp), w13d, off)
-    h = o.swiglu(ab)
-    y = o.grouped_gemm_fwd(q_rows(h), w2d, off)
+    rec("dgrad1.B", w13g)
+    rec("dgrad2.B", w2g)
+    xp = rec("src.xp", o.permute(x, r["src_token"]))
+    ab = o.grouped_gemm_fwd(rec("fwd1.A", q_rows(xp)), w13d, off)
+    h = rec("src.h", o.swiglu(ab))
+    y = o.grouped_gemm_fwd(rec("fwd2.A", q_rows(h)), w2d, off)
     ys = None
     if shared is not None:
         ws13d, ws2d = q_weights(np.asarray(shared[0])[None]), q_weights(np.asarray(shared[1])[None])
         ws13g, ws2g = ((q_weights(np.asarray(shared[0])[None], "dgrad"),
                         q_weights(np.asarray(shared[1])[None], "dgrad")) if mx else (ws13d, ws2d))
+        rec("s.fwd1.B", ws13d)
+        rec("s.fwd2.B", ws2d)
+        rec("s.dgrad1.B", ws13g)
+        rec("s.dgrad2.B", ws2g)
         all_rows = np.array([0, T])
-        abs_ = o.grouped_gemm_fwd(q_rows(x), ws13d, all_rows)
-        hs = o.swiglu(abs_)
-        ys = o.grouped_gemm_fwd(q_rows(hs), ws2d, all_rows)
+        abs_ = o.grouped_gemm_fwd(rec("s.fwd1.A", q_rows(x)), ws13d, all_rows)
+        hs = rec("src.hs", o.swiglu(abs_))
+        ys = o.grouped_gemm_fwd(rec("s.fwd2.A", q_rows(hs)), ws2d, all_rows)
     out = o.unpermute_combine(y, r["topk_w"], r["dst_row"], ys)
 
     dout = o.f64(dout)
     dy, dw = o.unpermute_combine_bwd(dout, y, r["topk_w"], r["dst_row"])
-    dh = o.grouped_gemm_dgrad(q_rows(dy), w2g, off)
-    dab = o.swiglu_bwd(dh, ab)
-    dxp = o.grouped_gemm_dgrad(q_rows(dab), w13g, off)
+    rec("src.dy", dy)
+    dh = o.grouped_gemm_dgrad(rec("dgrad2.A", q_rows(dy)), w2g, off)
+    dab = rec("src.dab", o.swiglu_bwd(dh, ab))
+    dxp = o.grouped_gemm_dgrad(rec("dgrad1.A", q_rows(dab)), w13g, off)
     hp, poff = q_tiles(h, off)
     dyp, _ = q_tiles(dy, off)
-    dW2 = o.grouped_gemm_wgrad(hp, dyp, poff)
+    rec("poff", poff)
+    dW2 = o.grouped_gemm_wgrad(rec("wgrad2.A", hp), rec("wgrad2.B", dyp), poff)
     xpp, _ = q_tiles(xp, off)
     dabp, _ = q_tiles(dab, off)
-    dW13 = o.grouped_gemm_wgrad(xpp, dabp, poff)
+    dW13 = o.grouped_gemm_wgrad(rec("wgrad1.A", xpp), rec("wgrad1.B", dabp), poff)
     res = {}
     addends = []
     if shared is not None:
-        dhs = o.grouped_gemm_dgrad(q_rows(dout), ws2g, all_rows)
-        dabs = o.swiglu_bwd(dhs, abs_)
-        addends.append(o.grouped_gemm_dgrad(q_rows(dabs), ws13g, all_rows))
+        dhs = o.grouped_gemm_dgrad(rec("s.dgrad2.A", q_rows(dout)), ws2g, all_rows)
+        dabs = rec("src.dabs", o.swiglu_bwd(dhs, abs_))
+        addends.append(o.grouped_gemm_dgrad(rec("s.dgrad1.A", q_rows(dabs)), ws13g, all_rows))
         hsp, ps = q_tiles(hs, all_rows)
         doutp, _ = q_tiles(dout, all_rows)
         xsp, _ = q_tiles(x, all_rows)
         dabsp, _ = q_tiles(dabs, all_rows)
-        res["dWs2"] = o.grouped_gemm_wgrad(hsp, doutp, ps)[0]
-        res["dWs13"] = o.grouped_gemm_wgrad(xsp, dabsp, ps)[0]
+        rec("s.poff", ps)
+        res["dWs2"] = o.grouped_gemm_wgrad(rec("s.wgrad2.A", hsp), rec("s.wgrad2.B", doutp), ps)[0]
+        res["dWs13"] = o.grouped_gemm_wgrad(rec("s.wgrad1.A", xsp), rec("s.wgrad1.B", dabsp), ps)[0]
     dz = o.route_bwd(z, r["topk_idx"], r["topk_w"], dw, score, renorm)
     dWr, dxr = o.router_logits_bwd(x, w_r, dz)
     addends.append(dxr)

@@ -370,3 +370,43 @@ def test_pad_to_max_is_capacity_in_a_static_layout(C):
                 e = r["topk_idx"][t, j]
                 assert e * C <= row < e * C + p["counts"][e] and p["src_token"][row] == t
     assert (p["src_token"] < 0).sum() == E * C - p["counts"].sum()
+
+
+def _hexrows(rows):
+    return np.array([[float.fromhex(v) for v in r] for r in rows])
+
+
+def test_router_logits_golden_hand_worked():
+    """Hand-worked fixture (tests/golden/router_logits.txt): a dot product on
+    an exact fp32 rounding tie, the bias added by one fp32 addition after
+    that rounding, float64 accumulation rounded once, and the [d, E] layout
+    of W_r.  Each case's expected key and choice differ from what the named
+    mistakes produce (checked below on the same inputs)."""
+    from golden_io import read_sections
+    g = read_sections("router_logits.txt")
+    # case A
+    x = _hexrows(g["a_x"]).astype(np.float32)
+    w = _hexrows(g["a_w"]).astype(np.float32)
+    b = _hexrows(g["a_bias"]).astype(np.float32)[0]
+    l0 = oracle.router_logits(x, w)
+    z = oracle.router_logits(x, w, b)
+    np.testing.assert_array_equal(l0, _hexrows(g["a_logits_nobias"]).astype(np.float32))
+    np.testing.assert_array_equal(z, _hexrows(g["a_keys"]).astype(np.float32))
+    assert oracle.select_topk(z, 1).tolist() == [[int(g["a_top1"][0][0])]]
+    # the mistakes this case tells apart
+    exact = x.astype(np.float64) @ w.astype(np.float64)
+    bias_before_rounding = (exact + b).astype(np.float32)
+    assert oracle.select_topk(bias_before_rounding, 1).tolist() == [[1]]
+    assert oracle.select_topk(exact + b, 1).tolist() == [[1]]          # float64 keys
+    # case B
+    x = _hexrows(g["b_x"]).astype(np.float32)
+    w = _hexrows(g["b_w"]).astype(np.float32)
+    z = oracle.router_logits(x, w)
+    np.testing.assert_array_equal(z, _hexrows(g["b_keys"]).astype(np.float32))
+    assert oracle.select_topk(z, 2).tolist() == [[int(v) for v in g["b_top2"][0]]]
+    f32_running = np.zeros((1, 3), np.float32)
+    for i in range(3):
+        f32_running = (f32_running + x[:, i:i + 1] * w[i]).astype(np.float32)
+    assert f32_running[0, 0] == 1.0 and z[0, 0] != f32_running[0, 0]
+    transposed = (x.astype(np.float64) @ w.T.astype(np.float64)).astype(np.float32)
+    assert oracle.select_topk(transposed, 2).tolist() == [[1, 0]]
