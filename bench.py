@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--gate-in-ffn", action="store_true",
                     help="apply the routing weight before W2 (unweighted combine, no Y in the "
                          "backward)")
+    ap.add_argument("--cold-reps", type=int, default=5,
+                    help="repetitions of each permute / combine call timed after a 512 MiB "
+                         "write that evicts its operands from the caches (0: skip)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the CPU oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -198,6 +201,49 @@ def traffic_for(workload, kernel):
     return rec["bytes_per_launch"]
 
 
+def cold_data_movement(layer, dout, work, reps):
+    """Each permute / combine call of the layer timed on its own, after a
+    512 MiB write (twice the memory-side cache) that evicts its operands, so
+    that its reads come from HBM; the write sits outside the call's events.
+    Returns name -> {ms (median), GB/s, frac of the HBM peak}."""
+    import statistics
+
+    import torch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    calls = layer.data_movement_calls(dout)
+    res = {}
+    for name, call in calls.items():
+        times = []
+        for _ in range(reps):
+            flush.fill_(1)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            call()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        ms = statistics.median(times)
+        by = work[name][1]
+        res[name] = {"ms": round(ms, 4), "GB/s": round(by / ms / 1e6, 1),
+                     "frac_hbm_peak": round(by / ms / 1e6 / PEAK_HBM_GBS, 4)}
+    del flush
+    return res
+
+
+def cpu_identity():
+    """Cores this process may run on, and the host CPU's model name."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return len(os.sched_getaffinity(0)), model
+
+
 def cpu_baseline(cfg, inp, budget_s):
     """The CPU oracle (untuned, one thread) on the first tokens of the same
     workload: routing, each token's k experts forward and backward, the
@@ -242,10 +288,13 @@ def cpu_baseline(cfg, inp, budget_s):
             oracle.router_logits_bwd(x_t, w_r, dz)
             spent += time.perf_counter() - c0
             ntok += 1
+    avail, model = cpu_identity()
     return {
         "value": per_token * ntok / spent / 1e12,
         "unit": "TFLOP/s",
         "cores": 1,
+        "cores_available": avail,
+        "cpu_model": model,
         "kind": "oracle",
         "sample": (f"first {ntok} tokens of the {cfg.name} layer through the oracle's per-token "
                    f"loop (routing, {ntok * k} token-expert SwiGLU forward+backward pairs, shared "
@@ -346,6 +395,17 @@ def main():
     roof["ms_per_launch"] = ms
     roof["traffic"] = traffic_for(cfg.name, dom)
 
+    router = [n for n in ("router_logits", "router_logits_bwd") if n in kernels]
+    router_ms = sum(kernels[n]["ms"] for n in router)
+    router_fl = sum(work[n][0] for n in router)
+    cold = None
+    if args.cold_reps > 0:
+        cold = cold_data_movement(layer, dout, work, args.cold_reps)
+        c_ms = sum(v["ms"] for v in cold.values())
+        c_by = sum(work[n][1] for n in cold)
+        cold["total"] = {"ms": round(c_ms, 4), "GB/s": round(c_by / c_ms / 1e6, 1),
+                         "frac_hbm_peak": round(c_by / c_ms / 1e6 / PEAK_HBM_GBS, 4)}
+
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -376,7 +436,13 @@ def main():
                             "ms": round(pc_ms, 4),
                             "traffic": pc_traffic,
                             "traffic_GB/s": (round(pc_traffic / pc_ms / 1e6, 1)
-                                             if pc_traffic is not None else None)},
+                                             if pc_traffic is not None else None),
+                            "cold": cold},
+        "router": {"TFLOP/s": round(router_fl / router_ms / 1e9, 1) if router_ms else None,
+                   "frac_peak": (round(router_fl / router_ms / 1e9 / PEAK_F32_TFLOPS, 4)
+                                 if router_ms else None),
+                   "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s", "ms": round(router_ms, 4),
+                   "engine": "fp32 vector ALUs"},
         "roofline": roof,
         "kernels": kernels,
         "cpu_baseline": None,

@@ -27,7 +27,10 @@
  *     inside the kernels: entries outside the valid range are skipped, never
  *     dereferenced.  Results for such inputs are unspecified.
  *   - Identical inputs give bit-identical outputs (no order-deciding atomics).
- *   - Sizes are 64-bit; the kernels address with 64-bit offsets.
+ *   - Sizes are 64-bit.  The kernels address with 64-bit offsets, except the
+ *     grouped GEMMs (bf16, fp8, MXFP8), whose buffer resources take 32-bit
+ *     byte offsets inside one group's slab: hence their per-expert limits
+ *     (K * N, M * K, M * N below 2^31 or 2^32 bytes, as stated per call).
  *   - Zero-sized problems (T == 0, M == 0) are valid; a weight gradient of an
  *     empty group is written as zeros (or left unchanged when accumulating).
  */
@@ -69,9 +72,11 @@ int moe_abi_version(void);
 /* ---------------------------------------------------------------- Route -- */
 
 /* Router projection, forward (section 2, Route: token hidden states to expert
- * logits; section 5, Selective precision: FP32).
+ * logits; section 5, Selective precision: the router stays in FP32).
  *   logits[t, e] = fp32( sum_i x[t, i] * w_r[i, e] ) + logit_bias[e]
- * fp32 multiply-add on the vector ALUs (bf16 x widened exactly).
+ * fp32 multiply-adds on the vector ALUs (bf16 x widened exactly), each output
+ * one sequential sum in a fixed order (deterministic); the bias is one fp32
+ * addition after the sum.  The matrix cores are not used.
  *   x          [T, d]  x_dtype (MOE_F32 or MOE_BF16)
  *   w_r        [d, E]  fp32
  *   logit_bias [E]     fp32 or NULL: a per-expert constant added to the
@@ -82,11 +87,19 @@ int moe_router_logits(const void* x, int x_dtype, const float* w_r, const float*
                       int64_t T, int64_t d, int32_t E, float* logits, void* stream);
 
 /* Router projection, backward: d_w_r = x^T d_logits ([d, E], fp32, overwritten)
- * and dx_router = d_logits w_r^T ([T, d], fp32, overwritten).  Either output
- * may be NULL to skip it. */
+ * and dx_router = d_logits w_r^T ([T, d], fp32, overwritten), fp32
+ * multiply-adds on the vector ALUs as in the forward.  Either output may be
+ * NULL to skip it. */
 int moe_router_logits_bwd(const void* x, int x_dtype, const float* w_r, const float* d_logits,
                           int64_t T, int64_t d, int32_t E, float* d_w_r, float* dx_router,
                           void* stream);
+
+/* Non-finite logits are a caller error (the routing of such a token is
+ * unspecified).  This check flags them: *status (device int32) is set to 1
+ * when any of x[0 .. n) is a NaN or an infinity, and is never cleared by the
+ * library.  x must be 16-byte aligned.  The layer calls it on the logits
+ * when the environment variable MOE_CHECK_FINITE is set. */
+int moe_check_finite(const float* x, int64_t n, int32_t* status, void* stream);
 
 /* Bytes of workspace moe_route_topk needs (device memory, any contents). */
 size_t moe_route_topk_workspace_bytes(int64_t T, int32_t E, int32_t k);

@@ -73,6 +73,7 @@ SIGNATURES = {
     "moe_route_topk_expert_bias": (_int, [_p, _p, _i64, _i32, _i32, _int, _p, _p, _p, _p, _p,
                                           _p, _p, _sz, _p]),
     "moe_expert_bias_update": (_int, [_p, _i32, _f32, _p, _p]),
+    "moe_check_finite": (_int, [_p, _i64, _p, _p]),
     "moe_pad_to_max": (_int, [_p, _p, _p, _p, _p, _i64, _i32, _i32, _i64, _p, _p, _p, _p, _p]),
     "moe_zero_unmapped_rows": (_int, [_p, _int, _p, _i64, _i64, _p]),
     "moe_quant_mxfp8_rows": (_int, [_p, _i64, _i64, _p, _p, _p]),
@@ -169,6 +170,10 @@ def moe_router_logits_bwd(x, w_r, d_logits, d_w_r, dx_router, stream=None):
     T, d = x.shape
     _call("moe_router_logits_bwd", _ptr(x), dtype_code(x), _ptr(w_r), _ptr(d_logits), T, d,
           w_r.shape[1], _ptr(d_w_r), _ptr(dx_router), _stream(stream))
+
+
+def moe_check_finite(x, status, stream=None):
+    _call("moe_check_finite", _ptr(x), x.numel(), _ptr(status), _stream(stream))
 
 
 def moe_route_topk_workspace_bytes(T, E, k):

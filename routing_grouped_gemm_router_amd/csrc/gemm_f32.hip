@@ -1,8 +1,7 @@
-// fp32 GEMM family: the router projection and its backward (the router stays
-// in FP32 -- "Scalable Training of Mixture-of-Experts Models with Megatron
-// Core", section 5, Selective precision: fp32-accurate products on the matrix
-// cores) and the fp32 grouped expert GEMMs (section 2, Expert Computation, on
-// the vector ALUs).
+// fp32 GEMM family on the vector ALUs: the router projection and its backward
+// (the router stays in FP32 -- "Scalable Training of Mixture-of-Experts Models
+// with Megatron Core", section 5, Selective precision) and the fp32 grouped
+// expert GEMMs (section 2, Expert Computation).
 //
 //   C[m, n] (+)= sum_k Aop(m, k) * Bop(k, n)
 //   Aop(m, k) = A[m * lda + k]            (A_MC = false: k contiguous)
@@ -179,314 +178,247 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const TA* __restrict__ A,
 }
 
 
-// ---- router GEMMs --------------------------------------------------------------
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-enum { RA_KC_BF16 = 0, RA_KC_F32 = 1, RA_MC_BF16 = 2, RA_MC_F32 = 3 };  // A: k- or m-contiguous
-enum { RB_NC = 0, RB_KC = 1 };                                          // B (fp32): n- or k-contiguous
+// ---- router products on the fp32 vector ALUs --------------------------------
+// The router stays in FP32 (section 5, Selective precision): x . W_r, its
+// weight gradient x^T . d_logits and the router's input gradient
+// d_logits . W_r^T are fp32 multiply-adds on the vector ALUs; the matrix
+// cores serve the expert contractions only.
+//
+//   C[m, n] = sum_k Aop(m, k) Bop(k, n) (+ bias[n], one fp32 addition after the sum)
+//   Aop(m, k) = A[m lda + k]  (AL = RA_KC_*: k contiguous; x or d_logits)
+//             = A[k lda + m]  (AL = RA_MC_*: m contiguous; x read as x^T)
+//   Bop(k, n) = B[k ldb + n]  (BL = RB_NC: W_r, or d_logits for dW_r)
+//             = B[n ldb + k]  (BL = RB_KC: W_r read as W_r^T)
+//
+// 256 threads per BM x BN tile; thread (tx, ty) owns TM x 8 outputs: rows
+// ty*4 .. +3 (and BM/2 + ty*4 .. +3 when TM = 8), columns tx*4 .. +3 and
+// BN/2 + tx*4 .. +3, so that every LDS fragment read is one 16-byte vector
+// and neighbouring lanes read neighbouring vectors.  Operands are staged as
+// [k][m] and [k][n] fp32 in two LDS buffers: the next BK-deep slice is loaded
+// into registers while the current one is consumed, one barrier per slice.
+// Each output is one thread's sequential fp32 sum, in fixed k order
+// (deterministic), taken in two levels (a sum per BK slice, then the running
+// total) so that the rounding error grows with BK + K/BK instead of K.
+enum { RA_KC_BF16 = 0, RA_KC_F32 = 1, RA_MC_BF16 = 2, RA_MC_F32 = 3 };
+enum { RB_NC = 0, RB_KC = 1 };
 
-struct RSlice {  // one lane's share of a 16-deep slice of A and B
-  float4 a[4];
-  float4 b[4];
+template <int AL> struct RouterA {
+  static constexpr bool BF16 = AL == RA_KC_BF16 || AL == RA_MC_BF16;
+  static constexpr bool MC = AL == RA_MC_BF16 || AL == RA_MC_F32;
+  static constexpr int VEC = BF16 ? 8 : 4;  // elements per 16-byte load
 };
 
-__device__ __forceinline__ float4 ld4_f32(const float* p, bool ok) {
-  return ok ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
-}
+template <int BM, int BN, int BK, int TM, int AL, int BL>
+struct RouterTile {
+  static constexpr int NX = BN / 8, NY = BM / 4 / (TM / 4);
+  static_assert(NX * NY == 256, "256 threads per tile");
+  static constexpr int AV = RouterA<AL>::VEC;
+  static constexpr int A_VECS = BM * BK / AV;               // 16-byte vectors of the A slice
+  static constexpr int B_VECS = BN * BK / 4;                // of the B slice
+  static constexpr int A_PER = (A_VECS + 255) / 256;
+  static constexpr int B_PER = (B_VECS + 255) / 256;
+};
 
-// 8 bf16 -> two float4
-__device__ __forceinline__ void ld8_bf16(const bf16_t* p, bool ok, float4& lo, float4& hi) {
-  uint4 v = ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
-  lo = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
-                   __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
-  hi = make_float4(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xffff0000u),
-                   __uint_as_float(v.w << 16), __uint_as_float(v.w & 0xffff0000u));
-}
+template <int BM, int BN, int BK, int TM, int AL, int BL>
+struct RouterRegs {
+  uint4 a[RouterTile<BM, BN, BK, TM, AL, BL>::A_PER];
+  float4 b[RouterTile<BM, BN, BK, TM, AL, BL>::B_PER];
+};
 
-// ---- router products on the bf16 matrix cores, fp32-accurate ----------------
-// An fp32 operand v is split exactly into three bf16 terms, v = hi + mid + lo
-// + r: hi = bf16(v), mid = bf16(v - hi), lo = bf16(v - hi - mid), each
-// rounded to nearest even; both residuals are exact in fp32 (each is v with
-// its leading bits removed), and |r| is about 2^-24 |v|, the rounding of an
-// fp32 value.  A product of two split operands keeps the term pairs whose
-// combined weight is at least 2^-16 (hi.hi, hi.mid, mid.hi, hi.lo, lo.hi,
-// mid.mid); every bf16 product is exact in the fp32 accumulator.  So the
-// result carries fp32 accuracy while the matrix cores run at their bf16 rate
-// (the router stays FP32 in what it computes).  Activations that are already
-// bf16 need no split (one term).
-//
-// C[m, n] = sum_k A[m, k] B(k, n), one wave per 64 x 64 tile as 2 x 2 MFMA
-// 32x32x16 blocks, operands loaded straight into the MFMA fragments: lane
-// half h of a 16-deep step holds k = 8 h .. 8 h + 7 of its row (A) or column
-// (B).  A is k-contiguous (x: bf16 or fp32; d_logits: fp32).  B is W_r: for
-// the logits W_r[k, n] (k strided: eight scalar loads per fragment, L2
-// resident), for the router's dx W_r[n, k] (k-contiguous).  SK = 8: the 8
-// waves of a workgroup split the contraction of one tile and add their
-// partials in wave order through LDS.
-typedef __bf16 bf16x8_rt __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4_rt __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float bf16_lo_f(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// eight fp32 values -> their hi, mid and lo bf16 terms
-__device__ __forceinline__ void split3x8(const float (&v)[8], bf16x8_rt (&t)[3]) {
-#pragma clang fp contract(off)
-  u32x4_rt h, m, l;
+template <int BM, int BN, int BK, int TM, int AL, int BL>
+__device__ __forceinline__ void router_fetch(RouterRegs<BM, BN, BK, TM, AL, BL>& r, const void* A,
+                                             int64_t lda, const float* B, int64_t ldb, int64_t m0,
+                                             int64_t n0, int64_t k0, int64_t M, int64_t N,
+                                             int64_t K, int tid) {
+  using TL = RouterTile<BM, BN, BK, TM, AL, BL>;
+  constexpr int AV = TL::AV;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float a = v[2 * i], b = v[2 * i + 1];
-    const uint32_t hw = f32x2_to_bf16x2(a, b);
-    const float ra = a - bf16_lo_f(hw), rb = b - bf16_hi_f(hw);
-    const uint32_t mw = f32x2_to_bf16x2(ra, rb);
-    const float sa = ra - bf16_lo_f(mw), sb = rb - bf16_hi_f(mw);
-    h[i] = hw;
-    m[i] = mw;
-    l[i] = f32x2_to_bf16x2(sa, sb);
+  for (int i = 0; i < TL::A_PER; ++i) {
+    const int v = tid + 256 * i;
+    r.a[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (v >= TL::A_VECS) continue;
+    int64_t m, k;
+    if (RouterA<AL>::MC) {  // vectors along m: [k][m / AV]
+      m = m0 + (v % (BM / AV)) * AV;
+      k = k0 + v / (BM / AV);
+      if (m + AV > M || k >= K) continue;
+    } else {                // vectors along k: [m][k / AV]
+      m = m0 + v / (BK / AV);
+      k = k0 + (v % (BK / AV)) * AV;
+      if (m >= M || k + AV > K) continue;
+    }
+    const int64_t e = RouterA<AL>::MC ? k * lda + m : m * lda + k;
+    r.a[i] = RouterA<AL>::BF16 ? *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(A) + e)
+                               : *reinterpret_cast<const uint4*>(static_cast<const float*>(A) + e);
   }
-  t[0] = __builtin_bit_cast(bf16x8_rt, h);
-  t[1] = __builtin_bit_cast(bf16x8_rt, m);
-  t[2] = __builtin_bit_cast(bf16x8_rt, l);
+#pragma unroll
+  for (int i = 0; i < TL::B_PER; ++i) {
+    const int v = tid + 256 * i;
+    r.b[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (v >= TL::B_VECS) continue;
+    if (BL == RB_NC) {  // vectors along n: [k][n / 4]
+      const int64_t n = n0 + (v % (BN / 4)) * 4, k = k0 + v / (BN / 4);
+      if (n + 4 > N || k >= K) continue;
+      r.b[i] = *reinterpret_cast<const float4*>(B + k * ldb + n);
+    } else {            // vectors along k: [n][k / 4]
+      const int64_t n = n0 + v / (BK / 4), k = k0 + (v % (BK / 4)) * 4;
+      if (n >= N || k + 4 > K) continue;
+      r.b[i] = *reinterpret_cast<const float4*>(B + n * ldb + k);
+    }
+  }
 }
 
-// One 16-deep LDS slice ([k][64] fp32 for A and for B) through bf16 MFMAs:
-// lane half h takes k = 8 h .. 8 h + 7 of column r and 32 + r of each operand.
-template <bool A_BF16>
-__device__ __forceinline__ void mc16_slice(f32x16_t (&acc)[2][2], const float (*As)[64],
-                                           const float (*Bs)[64], int r, int h) {
-  float va[2][8], vb[2][8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int kk = 8 * h + i;
-    va[0][i] = As[kk][r]; va[1][i] = As[kk][32 + r];
-    vb[0][i] = Bs[kk][r]; vb[1][i] = Bs[kk][32 + r];
+__device__ __forceinline__ void unpack_vec(const uint4& u, bool bf16, float (&v)[8]) {
+  if (bf16) {
+    v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+    v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+    v[4] = __uint_as_float(u.z << 16); v[5] = __uint_as_float(u.z & 0xffff0000u);
+    v[6] = __uint_as_float(u.w << 16); v[7] = __uint_as_float(u.w & 0xffff0000u);
+  } else {
+    v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
+    v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
   }
-  bf16x8_rt a[2][3], b[2][3];
+}
+
+template <int BM, int BN, int BK, int TM, int AL, int BL>
+__device__ __forceinline__ void router_stage(const RouterRegs<BM, BN, BK, TM, AL, BL>& r,
+                                             float (*As)[BM], float (*Bs)[BN], int tid) {
+  using TL = RouterTile<BM, BN, BK, TM, AL, BL>;
+  constexpr int AV = TL::AV;
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
-    if (A_BF16) {  // bf16 values: exact in one term
-      u32x4_rt u;
+  for (int i = 0; i < TL::A_PER; ++i) {
+    const int v = tid + 256 * i;
+    if (v >= TL::A_VECS) continue;
+    float e[8];
+    unpack_vec(r.a[i], RouterA<AL>::BF16, e);
+    if (RouterA<AL>::MC) {
+      const int m = (v % (BM / AV)) * AV, k = v / (BM / AV);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) u[i] = f32x2_to_bf16x2(va[mi][2 * i], va[mi][2 * i + 1]);
-      a[mi][0] = __builtin_bit_cast(bf16x8_rt, u);
+      for (int j = 0; j < AV; j += 4)
+        *reinterpret_cast<float4*>(&As[k][m + j]) = make_float4(e[j], e[j + 1], e[j + 2], e[j + 3]);
     } else {
-      split3x8(va[mi], a[mi]);
+      const int m = v / (BK / AV), k = (v % (BK / AV)) * AV;
+#pragma unroll
+      for (int j = 0; j < AV; ++j) As[k + j][m] = e[j];
     }
   }
 #pragma unroll
-  for (int ni = 0; ni < 2; ++ni) split3x8(vb[ni], b[ni]);
-  constexpr int NP = A_BF16 ? 3 : 6;
-  constexpr int PA[6] = {0, 0, 1, 0, 2, 1};
-  constexpr int PB[6] = {0, 1, 0, 2, 0, 1};
-  constexpr int PA1[3] = {0, 0, 0};
-  constexpr int PB1[3] = {0, 1, 2};
-#pragma unroll
-  for (int q = 0; q < NP; ++q)
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            b[ni][A_BF16 ? PB1[q] : PB[q]], a[mi][A_BF16 ? PA1[q] : PA[q]], acc[mi][ni], 0, 0, 0);
-}
-
-// ---- router weight gradient: one wave per 64 x 64 output tile, LDS slices ----
-// dW_r = x^T . d_logits contracts over tokens, and both operands are strided
-// along it, so each wave stages its own 16-deep operand slices in its own
-// 8 KiB of LDS as [k][64] (prefetching the next slice into registers while it
-// computes, so the main loop has no workgroup barrier) and feeds the split
-// bf16 products below from them: a wave owns a 64 x 64 tile as 2 x 2 MFMA
-// blocks.  SK = 8: the workgroup's 8 waves split the contraction of one tile
-// and add their partial sums through LDS in wave order (deterministic, no
-// workspace); SK = 1: the 8 waves take 8 tiles.  Requires 16-byte aligned
-// operands, the A and B contiguous extents multiples of 8 (bf16) or 4 (fp32)
-// elements.
-template <int AL, int BL>
-__device__ __forceinline__ void router_load(RSlice& r, const void* A, int64_t lda, const float* B,
-                                            int64_t ldb, int64_t m0, int64_t n0, int64_t k0,
-                                            int64_t k_hi, int64_t M, int64_t N, int lane) {
-  if (AL == RA_KC_BF16 || AL == RA_KC_F32) {
-    // lane = row m0 + lane, k0 .. k0 + 15
-    const int64_t m = m0 + lane;
-    const bool row_ok = m < M;
-    if (AL == RA_KC_BF16) {
-      const bf16_t* p = static_cast<const bf16_t*>(A) + m * lda + k0;
-      ld8_bf16(p, row_ok && k0 + 8 <= k_hi, r.a[0], r.a[1]);
-      ld8_bf16(p + 8, row_ok && k0 + 16 <= k_hi, r.a[2], r.a[3]);
+  for (int i = 0; i < TL::B_PER; ++i) {
+    const int v = tid + 256 * i;
+    if (v >= TL::B_VECS) continue;
+    if (BL == RB_NC) {
+      const int n = (v % (BN / 4)) * 4, k = v / (BN / 4);
+      *reinterpret_cast<float4*>(&Bs[k][n]) = r.b[i];
     } else {
-      const float* p = static_cast<const float*>(A) + m * lda + k0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) r.a[j] = ld4_f32(p + 4 * j, row_ok && k0 + 4 * j + 4 <= k_hi);
-    }
-  } else {
-    // lane -> k row k0 + (lane >> 2), rows m0 + 16 (lane & 3) .. + 15
-    const int64_t k = k0 + (lane >> 2), m = m0 + 16 * (lane & 3);
-    const bool k_ok = k < k_hi;
-    if (AL == RA_MC_BF16) {
-      const bf16_t* p = static_cast<const bf16_t*>(A) + k * lda + m;
-      ld8_bf16(p, k_ok && m + 8 <= M, r.a[0], r.a[1]);
-      ld8_bf16(p + 8, k_ok && m + 16 <= M, r.a[2], r.a[3]);
-    } else {
-      const float* p = static_cast<const float*>(A) + k * lda + m;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) r.a[j] = ld4_f32(p + 4 * j, k_ok && m + 4 * j + 4 <= M);
-    }
-  }
-  if (BL == RB_NC) {
-    const int64_t k = k0 + (lane >> 2), n = n0 + 16 * (lane & 3);
-    const float* p = B + k * ldb + n;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) r.b[j] = ld4_f32(p + 4 * j, k < k_hi && n + 4 * j + 4 <= N);
-  } else {
-    const int64_t n = n0 + lane;
-    const float* p = B + n * ldb + k0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) r.b[j] = ld4_f32(p + 4 * j, n < N && k0 + 4 * j + 4 <= k_hi);
-  }
-}
-
-// slice -> LDS as [k][64] for A and for B
-template <int AL, int BL>
-__device__ __forceinline__ void router_stage(const RSlice& r, float (*As)[64], float (*Bs)[64],
-                                             int lane) {
-  if (AL == RA_KC_BF16 || AL == RA_KC_F32) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      As[4 * j + 0][lane] = r.a[j].x;
-      As[4 * j + 1][lane] = r.a[j].y;
-      As[4 * j + 2][lane] = r.a[j].z;
-      As[4 * j + 3][lane] = r.a[j].w;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<float4*>(&As[lane >> 2][16 * (lane & 3) + 4 * j]) = r.a[j];
-  }
-  if (BL == RB_NC) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<float4*>(&Bs[lane >> 2][16 * (lane & 3) + 4 * j]) = r.b[j];
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      Bs[4 * j + 0][lane] = r.b[j].x;
-      Bs[4 * j + 1][lane] = r.b[j].y;
-      Bs[4 * j + 2][lane] = r.b[j].z;
-      Bs[4 * j + 3][lane] = r.b[j].w;
+      const int n = v / (BK / 4), k = (v % (BK / 4)) * 4;
+      Bs[k][n] = r.b[i].x; Bs[k + 1][n] = r.b[i].y; Bs[k + 2][n] = r.b[i].z; Bs[k + 3][n] = r.b[i].w;
     }
   }
 }
 
-template <int AL, int BL, int SK, bool BIAS>
-__global__ __launch_bounds__(512) void router_gemm_kernel(const void* __restrict__ A, int64_t lda,
-                                                          const float* __restrict__ B,
-                                                          int64_t ldb, float* __restrict__ C,
-                                                          int64_t ldc, int64_t M, int64_t N,
-                                                          int64_t K,
+template <int BM, int BN, int BK, int TM, int AL, int BL, bool BIAS>
+__global__ __launch_bounds__(256) void router_valu_kernel(const void* __restrict__ A, int64_t lda,
+                                                          const float* __restrict__ B, int64_t ldb,
+                                                          float* __restrict__ C, int64_t ldc,
+                                                          int64_t M, int64_t N, int64_t K,
                                                           const float* __restrict__ bias) {
-  __shared__ __attribute__((aligned(16))) float lds[8][2][16][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t ntn = (N + 63) / 64;
-  const int64_t tile = SK > 1 ? static_cast<int64_t>(blockIdx.x)
-                              : static_cast<int64_t>(blockIdx.x) * 8 + wave;
-  const int64_t m0 = (tile / ntn) * 64, n0 = (tile % ntn) * 64;
-  int64_t k_lo = 0, k_hi = K;
-  if (SK > 1) {
-    const int64_t per = ((K + SK - 1) / SK + 15) / 16 * 16;
-    k_lo = min(K, wave * per);
-    k_hi = min(K, k_lo + per);
-  }
-  float(*As)[64] = lds[wave][0];
-  float(*Bs)[64] = lds[wave][1];
-  // MFMA 32x32x16 bf16, computed as D[n][m] so that lane r of a block holds
-  // output row m = r: acc[mi][ni][v] is C[32 mi + r][32 ni + 8 (v / 4) +
-  // 4 h + v % 4], h = lane / 32.  Lane half h feeds contraction positions
-  // 8 h .. 8 h + 7 of each 16-deep slice, for A and for B alike.
-  f32x16_t acc[2][2];
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
-  const int r = lane & 31, h = lane >> 5;
+  using TL = RouterTile<BM, BN, BK, TM, AL, BL>;
+  __shared__ __attribute__((aligned(16))) float As[2][BK][BM];
+  __shared__ __attribute__((aligned(16))) float Bs[2][BK][BN];
+  const int tid = threadIdx.x;
+  const int tx = tid % TL::NX, ty = tid / TL::NX;
+  const int64_t ntn = (N + BN - 1) / BN;
+  const int64_t m0 = (static_cast<int64_t>(blockIdx.x) / ntn) * BM;
+  const int64_t n0 = (static_cast<int64_t>(blockIdx.x) % ntn) * BN;
 
-  if (m0 < M) {  // SK == 1: trailing waves of the last block may have no tile
-    RSlice rs;
-    if (k_lo < k_hi) router_load<AL, BL>(rs, A, lda, B, ldb, m0, n0, k_lo, k_hi, M, N, lane);
-    for (int64_t k0 = k_lo; k0 < k_hi; k0 += 16) {
-      router_stage<AL, BL>(rs, As, Bs, lane);
-      __builtin_amdgcn_wave_barrier();
-      if (k0 + 16 < k_hi) router_load<AL, BL>(rs, A, lda, B, ldb, m0, n0, k0 + 16, k_hi, M, N, lane);
-      mc16_slice<AL == RA_KC_BF16 || AL == RA_MC_BF16>(acc, As, Bs, r, h);
-      __builtin_amdgcn_wave_barrier();
-    }
-  }
+  float acc[TM][8];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
 
-  // columns 32 ni + 8 g + 4 h .. + 3 of row 32 mi + r
-  auto quad = [&](int mi, int ni, int g) {
-    return make_float4(acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2],
-                       acc[mi][ni][4 * g + 3]);
-  };
-  if (SK == 1) {
-    if (m0 >= M) return;
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-      const int64_t m = m0 + 32 * mi + r;
-      if (m >= M) continue;
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int64_t n = n0 + 32 * ni + 8 * g + 4 * h;
-          if (n >= N) continue;
-          float4 v = quad(mi, ni, g);
-          if (BIAS) {
-            v.x += bias[n]; v.y += bias[n + 1]; v.z += bias[n + 2]; v.w += bias[n + 3];
-          }
-          *reinterpret_cast<float4*>(C + m * ldc + n) = v;
-        }
-    }
-    return;
+  const int64_t nslices = (K + BK - 1) / BK;
+  RouterRegs<BM, BN, BK, TM, AL, BL> regs;
+  if (nslices > 0) {
+    router_fetch<BM, BN, BK, TM, AL, BL>(regs, A, lda, B, ldb, m0, n0, 0, M, N, K, tid);
+    router_stage<BM, BN, BK, TM, AL, BL>(regs, As[0], Bs[0], tid);
   }
-  // SK > 1: two rounds of 32 rows; wave w's partials in its own 8 KiB as [32][64]
-  float* part = &lds[wave][0][0][0];
+  __syncthreads();
+  for (int64_t s = 0; s < nslices; ++s) {
+    const int buf = static_cast<int>(s & 1);
+    if (s + 1 < nslices)
+      router_fetch<BM, BN, BK, TM, AL, BL>(regs, A, lda, B, ldb, m0, n0, (s + 1) * BK, M, N, K,
+                                           tid);
+    float part[TM][8];
 #pragma unroll
-  for (int rnd = 0; rnd < 2; ++rnd) {
-    __syncthreads();  // every wave is done with its slices / the previous round
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<float4*>(part + r * 64 + 32 * ni + 8 * g + 4 * h) = quad(rnd, ni, g);
-    __syncthreads();
-    // thread t sums elements 4t .. 4t+3 of the 32 x 64 half over the waves in order
-    const int e = 4 * static_cast<int>(threadIdx.x);
-    float4 sum = *reinterpret_cast<const float4*>(&lds[0][0][0][0] + e);
-#pragma unroll
-    for (int w = 1; w < 8; ++w) {
-      const float4 q = *reinterpret_cast<const float4*>(&lds[w][0][0][0] + e);
-      sum.x += q.x; sum.y += q.y; sum.z += q.z; sum.w += q.w;
-    }
-    const int64_t m = m0 + 32 * rnd + e / 64, n = n0 + (e % 64);
-    if (m < M && n < N) {
-      if (BIAS) {
-        sum.x += bias[n]; sum.y += bias[n + 1]; sum.z += bias[n + 2]; sum.w += bias[n + 3];
+      for (int j = 0; j < 8; ++j) part[i][j] = 0.f;
+#pragma unroll 4
+    for (int kk = 0; kk < BK; ++kk) {
+      float a[TM], b[8];
+      const float4 a0 = *reinterpret_cast<const float4*>(&As[buf][kk][ty * 4]);
+      a[0] = a0.x; a[1] = a0.y; a[2] = a0.z; a[3] = a0.w;
+      if (TM == 8) {
+        const float4 a1 = *reinterpret_cast<const float4*>(&As[buf][kk][BM / 2 + ty * 4]);
+        a[TM - 4] = a1.x; a[TM - 3] = a1.y; a[TM - 2] = a1.z; a[TM - 1] = a1.w;
       }
-      *reinterpret_cast<float4*>(C + m * ldc + n) = sum;
+      const float4 b0 = *reinterpret_cast<const float4*>(&Bs[buf][kk][tx * 4]);
+      const float4 b1 = *reinterpret_cast<const float4*>(&Bs[buf][kk][BN / 2 + tx * 4]);
+      b[0] = b0.x; b[1] = b0.y; b[2] = b0.z; b[3] = b0.w;
+      b[4] = b1.x; b[5] = b1.y; b[6] = b1.z; b[7] = b1.w;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) part[i][j] = fmaf(a[i], b[j], part[i][j]);
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] += part[i][j];
+    if (s + 1 < nslices) router_stage<BM, BN, BK, TM, AL, BL>(regs, As[buf ^ 1], Bs[buf ^ 1], tid);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int64_t m = m0 + (i < 4 ? ty * 4 + i : BM / 2 + ty * 4 + (i - 4));
+    if (m >= M) continue;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t n = n0 + h * (BN / 2) + tx * 4;
+      if (n + 4 > N) continue;
+      float4 v = make_float4(acc[i][4 * h], acc[i][4 * h + 1], acc[i][4 * h + 2], acc[i][4 * h + 3]);
+      if (BIAS) {
+        v.x += bias[n]; v.y += bias[n + 1]; v.z += bias[n + 2]; v.w += bias[n + 3];
+      }
+      *reinterpret_cast<float4*>(C + m * ldc + n) = v;
     }
   }
 }
 
-template <int AL, int BL, int SK, bool BIAS>
-static hipError_t run_router(const void* A, int64_t lda, const float* B, int64_t ldb, float* C,
-                             int64_t ldc, int64_t M, int64_t N, int64_t K, const float* bias,
-                             hipStream_t s) {
-  const int64_t tiles = ((M + 63) / 64) * ((N + 63) / 64);
-  const int64_t blocks = SK > 1 ? tiles : (tiles + 7) / 8;
-  if (blocks <= 0) return hipSuccess;
-  router_gemm_kernel<AL, BL, SK, BIAS><<<dim3(static_cast<unsigned>(blocks)), 512, 0, s>>>(
+template <int BM, int BN, int BK, int TM, int AL, int BL, bool BIAS>
+static hipError_t run_router_valu(const void* A, int64_t lda, const float* B, int64_t ldb,
+                                  float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                                  const float* bias, hipStream_t s) {
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  if (tiles <= 0) return hipSuccess;
+  router_valu_kernel<BM, BN, BK, TM, AL, BL, BIAS><<<dim3(static_cast<unsigned>(tiles)), 256, 0, s>>>(
       A, lda, B, ldb, C, ldc, M, N, K, bias);
   return hipGetLastError();
+}
+
+// Products whose output width is the expert count E (logits, dW_r): the tile
+// spans up to 256 experts, 256 / 128 / 64 columns by E.
+template <int AL, int BL, bool BIAS>
+static hipError_t run_router_e(const void* A, int64_t lda, const float* B, int64_t ldb, float* C,
+                               int64_t ldc, int64_t M, int64_t N, int64_t K, const float* bias,
+                               hipStream_t s) {
+  if (N > 128)
+    return run_router_valu<32, 256, 32, 4, AL, BL, BIAS>(A, lda, B, ldb, C, ldc, M, N, K, bias, s);
+  if (N > 64)
+    return run_router_valu<64, 128, 32, 4, AL, BL, BIAS>(A, lda, B, ldb, C, ldc, M, N, K, bias, s);
+  return run_router_valu<128, 64, 32, 4, AL, BL, BIAS>(A, lda, B, ldb, C, ldc, M, N, K, bias, s);
 }
 
 static bool aligned16p(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -510,213 +442,16 @@ static hipError_t run_f32(const TA* A, int64_t lda, const float* B, int64_t ldb,
   return hipGetLastError();
 }
 
-__device__ __forceinline__ float4 ld4g(const float* p, bool ok) {
-  return ok ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
-}
-
-// One lane's raw operand values of one 16-deep step: for each of its two rows
-// of A and two columns of B, the 8 values k = k0 .. k0 + 7 of its lane half.
-struct RawAB {
-  float4 a[2][2];  // fp32 A; a bf16 A keeps its 8 values in a[mi][0] as raw bits
-  float b[2][8];
-};
-
-// A row m, k = k0 .. k0 + 7 (k0 a multiple of 8; k_hi a multiple of 8 for a
-// bf16 A and of 4 for an fp32 A, so every vector lies wholly in or out)
-template <bool AF32>
-__device__ __forceinline__ void load_a_raw(const void* A, int64_t lda, int64_t m, int64_t M,
-                                           int64_t k0, int64_t k_hi, float4 (&a)[2]) {
-  const bool ok = m < M && k0 < k_hi;
-  if (AF32) {
-    const float* p = static_cast<const float*>(A) + m * lda + k0;
-    a[0] = ld4g(p, ok);
-    a[1] = ld4g(p + 4, ok && k0 + 8 <= k_hi);
-  } else {
-    const bf16_t* p = static_cast<const bf16_t*>(A) + m * lda + k0;
-    const uint4 u = ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0u, 0u, 0u, 0u);
-    a[0] = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
-                       __uint_as_float(u.w));
-  }
-}
-
-// B column n, k = k0 .. k0 + 7.  BT: B(k, n) = W[k * ldb + n]; else
-// B(k, n) = W[n * ldb + k] (k_hi a multiple of 4)
-template <bool BT>
-__device__ __forceinline__ void load_b_raw(const float* W, int64_t ldb, int64_t n, int64_t N,
-                                           int64_t k0, int64_t k_hi, float (&v)[8]) {
-  if (BT) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      v[i] = (n < N && k0 + i < k_hi) ? W[(k0 + i) * ldb + n] : 0.f;
-  } else {
-    const bool ok = n < N && k0 < k_hi;
-    const float* p = W + n * ldb + k0;
-    const float4 u = ld4g(p, ok), w = ld4g(p + 4, ok && k0 + 8 <= k_hi);
-    v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
-    v[4] = w.x; v[5] = w.y; v[6] = w.z; v[7] = w.w;
-  }
-}
-
-template <bool AF32>
-__device__ __forceinline__ void split_a(const float4 (&a)[2], bf16x8_rt (&t)[3]) {
-  if (AF32) {
-    const float v[8] = {a[0].x, a[0].y, a[0].z, a[0].w, a[1].x, a[1].y, a[1].z, a[1].w};
-    split3x8(v, t);
-  } else {
-    u32x4_rt u;
-    u[0] = __float_as_uint(a[0].x); u[1] = __float_as_uint(a[0].y);
-    u[2] = __float_as_uint(a[0].z); u[3] = __float_as_uint(a[0].w);
-    t[0] = __builtin_bit_cast(bf16x8_rt, u);
-  }
-}
-
-template <bool AF32, bool BT, int SK, bool BIAS>
-__global__ __launch_bounds__(512) void router_mc_kernel(const void* __restrict__ A, int64_t lda,
-                                                        const float* __restrict__ W, int64_t ldb,
-                                                        float* __restrict__ C, int64_t ldc,
-                                                        int64_t M, int64_t N, int64_t K,
-                                                        const float* __restrict__ bias) {
-  __shared__ __attribute__((aligned(16))) float part_lds[8][32][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t ntn = (N + 63) / 64;
-  const int64_t tile = SK > 1 ? static_cast<int64_t>(blockIdx.x)
-                              : static_cast<int64_t>(blockIdx.x) * 8 + wave;
-  const int64_t m0 = (tile / ntn) * 64, n0 = (tile % ntn) * 64;
-  int64_t k_lo = 0, k_hi = K;
-  if (SK > 1) {
-    const int64_t per = ((K + SK - 1) / SK + 15) / 16 * 16;
-    k_lo = min(K, wave * per);
-    k_hi = min(K, k_lo + per);
-  }
-  // term pairs (A term, B term) in a fixed order: a split A keeps the six
-  // pairs of weight 2^-16 or more, a bf16 A (one term) meets all three B terms
-  constexpr int NP = AF32 ? 6 : 3;
-  constexpr int PA[6] = {0, 0, 1, 0, 2, 1};
-  constexpr int PB[6] = {0, 1, 0, 2, 0, 1};
-  constexpr int PA1[3] = {0, 0, 0};
-  constexpr int PB1[3] = {0, 1, 2};
-  f32x16_t acc[2][2];
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
-  const int r = lane & 31, h = lane >> 5;
-
-  if (m0 < M) {  // SK == 1: trailing waves of the last block may have no tile
-    // the raw values of the next two steps are in flight while one computes
-    RawAB raw[2];
-    auto load_raw = [&](int64_t k0, RawAB& rw) {
-      const int64_t kk = k0 + 8 * h;
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi) load_a_raw<AF32>(A, lda, m0 + 32 * mi + r, M, kk, k_hi, rw.a[mi]);
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) load_b_raw<BT>(W, ldb, n0 + 32 * ni + r, N, kk, k_hi, rw.b[ni]);
-    };
-    if (k_lo < k_hi) load_raw(k_lo, raw[0]);
-    if (k_lo + 16 < k_hi) load_raw(k_lo + 16, raw[1]);
-    for (int64_t k0 = k_lo; k0 < k_hi; k0 += 32) {
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const int64_t ks = k0 + 16 * sub;
-        if (ks >= k_hi) break;
-        bf16x8_rt a[2][3], b[2][3];
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi) split_a<AF32>(raw[sub].a[mi], a[mi]);
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) split3x8(raw[sub].b[ni], b[ni]);
-        if (ks + 32 < k_hi) load_raw(ks + 32, raw[sub]);
-#pragma unroll
-        for (int q = 0; q < NP; ++q)
-#pragma unroll
-          for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
-              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  b[ni][AF32 ? PB[q] : PB1[q]], a[mi][AF32 ? PA[q] : PA1[q]], acc[mi][ni], 0, 0,
-                  0);
-      }
-    }
-  }
-
-  // columns 32 ni + 8 g + 4 h .. + 3 of row 32 mi + r
-  auto quad = [&](int mi, int ni, int g) {
-    return make_float4(acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2],
-                       acc[mi][ni][4 * g + 3]);
-  };
-  if (SK == 1) {
-    if (m0 >= M) return;
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-      const int64_t m = m0 + 32 * mi + r;
-      if (m >= M) continue;
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int64_t n = n0 + 32 * ni + 8 * g + 4 * h;
-          if (n >= N) continue;
-          float4 v = quad(mi, ni, g);
-          if (BIAS) {
-            v.x += bias[n]; v.y += bias[n + 1]; v.z += bias[n + 2]; v.w += bias[n + 3];
-          }
-          *reinterpret_cast<float4*>(C + m * ldc + n) = v;
-        }
-    }
-    return;
-  }
-  // SK > 1: two rounds of 32 rows; wave w's partials in its own 8 KiB as [32][64]
-  float* part = &part_lds[wave][0][0];
-#pragma unroll
-  for (int rnd = 0; rnd < 2; ++rnd) {
-    __syncthreads();
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<float4*>(part + r * 64 + 32 * ni + 8 * g + 4 * h) = quad(rnd, ni, g);
-    __syncthreads();
-    // thread t sums elements 4t .. 4t+3 of the 32 x 64 half over the waves in order
-    const int e = 4 * static_cast<int>(threadIdx.x);
-    float4 sum = *reinterpret_cast<const float4*>(&part_lds[0][0][0] + e);
-#pragma unroll
-    for (int w = 1; w < 8; ++w) {
-      const float4 q = *reinterpret_cast<const float4*>(&part_lds[w][0][0] + e);
-      sum.x += q.x; sum.y += q.y; sum.z += q.z; sum.w += q.w;
-    }
-    const int64_t m = m0 + 32 * rnd + e / 64, n = n0 + (e % 64);
-    if (m < M && n < N) {
-      if (BIAS) {
-        sum.x += bias[n]; sum.y += bias[n + 1]; sum.z += bias[n + 2]; sum.w += bias[n + 3];
-      }
-      *reinterpret_cast<float4*>(C + m * ldc + n) = sum;
-    }
-  }
-}
-
-template <bool AF32, bool BT, int SK, bool BIAS>
-static hipError_t run_router_mc(const void* A, int64_t lda, const float* W, int64_t ldb, float* C,
-                                int64_t ldc, int64_t M, int64_t N, int64_t K, const float* bias,
-                                hipStream_t s) {
-  const int64_t tiles = ((M + 63) / 64) * ((N + 63) / 64);
-  const int64_t blocks = SK > 1 ? tiles : (tiles + 7) / 8;
-  if (blocks <= 0) return hipSuccess;
-  router_mc_kernel<AF32, BT, SK, BIAS><<<dim3(static_cast<unsigned>(blocks)), 512, 0, s>>>(
-      A, lda, W, ldb, C, ldc, M, N, K, bias);
-  return hipGetLastError();
-}
-
 hipError_t launch_router_fwd(const void* x, int x_dtype, const float* w_r, const float* bias,
                              int64_t T, int64_t d, int E, float* logits, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (d % 8 == 0 && E % 4 == 0 && aligned16p(x) && aligned16p(w_r) && aligned16p(logits)) {
-    // logits [T, E] = x [T, d] . W_r [d, E] (+ bias): contraction split over the 8 waves
+    // logits [T, E] = x [T, d] . W_r [d, E] (+ bias)
     if (x_dtype == 0)
-      return bias ? run_router_mc<true, true, 8, true>(x, d, w_r, E, logits, E, T, E, d, bias, s)
-                  : run_router_mc<true, true, 8, false>(x, d, w_r, E, logits, E, T, E, d, bias, s);
-    return bias ? run_router_mc<false, true, 8, true>(x, d, w_r, E, logits, E, T, E, d, bias, s)
-                : run_router_mc<false, true, 8, false>(x, d, w_r, E, logits, E, T, E, d, bias, s);
+      return bias ? run_router_e<RA_KC_F32, RB_NC, true>(x, d, w_r, E, logits, E, T, E, d, bias, s)
+                  : run_router_e<RA_KC_F32, RB_NC, false>(x, d, w_r, E, logits, E, T, E, d, bias, s);
+    return bias ? run_router_e<RA_KC_BF16, RB_NC, true>(x, d, w_r, E, logits, E, T, E, d, bias, s)
+                : run_router_e<RA_KC_BF16, RB_NC, false>(x, d, w_r, E, logits, E, T, E, d, bias, s);
   }
   if (x_dtype == 0)
     return run_f32<float, false, false, GRP_NONE, EPI_BIAS, float>(
@@ -735,18 +470,19 @@ hipError_t launch_router_bwd(const void* x, int x_dtype, const float* w_r, const
                     aligned16p(dz) && aligned16p(dw_r) && aligned16p(dx_r);
   if (fast) {
     if (dw_r) {
-      // dW_r [d, E] = x^T [d, T] . dz [T, E]: contraction over tokens split over the 8 waves
+      // dW_r [d, E] = x^T [d, T] . dz [T, E]
       if (T == 0)
         err = launch_fill_zero(dw_r, d * E, s);
       else if (x_dtype == 0)
-        err = run_router<RA_MC_F32, RB_NC, 8, false>(x, d, dz, E, dw_r, E, d, E, T, nullptr, s);
+        err = run_router_e<RA_MC_F32, RB_NC, false>(x, d, dz, E, dw_r, E, d, E, T, nullptr, s);
       else
-        err = run_router<RA_MC_BF16, RB_NC, 8, false>(x, d, dz, E, dw_r, E, d, E, T, nullptr, s);
+        err = run_router_e<RA_MC_BF16, RB_NC, false>(x, d, dz, E, dw_r, E, d, E, T, nullptr, s);
       if (err != hipSuccess) return err;
     }
     if (dx_r && T > 0)
       // dx_r [T, d] = dz [T, E] . W_r^T (Bop(k = e, n = i) = W_r[i * E + e])
-      err = run_router_mc<true, false, 1, false>(dz, E, w_r, E, dx_r, d, T, d, E, nullptr, s);
+      err = run_router_valu<128, 128, 32, 8, RA_KC_F32, RB_KC, false>(dz, E, w_r, E, dx_r, d, T, d,
+                                                                       E, nullptr, s);
     return err;
   }
   if (dw_r) {

@@ -26,6 +26,7 @@ hipError_t launch_zero_unmapped_rows(void* buf, int64_t row_bytes, const int32_t
                                      int64_t M, hipStream_t s);
 hipError_t launch_expert_bias_update(const int32_t* counts, int E, float rate, float* bias,
                                      hipStream_t stream);
+hipError_t launch_check_finite(const float* p, int64_t n, int32_t* status, hipStream_t stream);
 hipError_t launch_route_replay(const float* logits, const int32_t* idx_in, int64_t T, int E, int k,
                                int score, int renorm, int32_t* topk_idx, float* topk_w,
                                int32_t* counts, int64_t* offsets, int32_t* dst_row,

@@ -208,6 +208,15 @@ int moe_expert_bias_update(const int32_t* counts, int32_t E, float rate, float* 
                     fn);
 }
 
+int moe_check_finite(const float* x, int64_t n, int32_t* status, void* stream) {
+  const char* fn = "moe_check_finite";
+  REQUIRE(n >= 0, MOE_ERR_SHAPE, "%s: n=%lld", fn, static_cast<long long>(n));
+  if (n == 0) return ok();
+  REQUIRE(x && status, MOE_ERR_NULL, "%s: x and status are required", fn);
+  REQUIRE(aligned16(x), MOE_ERR_UNSUPPORTED, "%s: x must be 16-byte aligned", fn);
+  return hip_status(moe::launch_check_finite(x, n, status, as_stream(stream)), fn);
+}
+
 int moe_route_replay(const float* logits, const int32_t* topk_idx_in, int64_t T, int32_t E,
                      int32_t k, int score, int renorm, int32_t* topk_idx, float* topk_w,
                      int32_t* counts, int64_t* offsets, int32_t* dst_row, int32_t* src_token,

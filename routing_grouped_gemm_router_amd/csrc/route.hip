@@ -667,6 +667,33 @@ hipError_t launch_expert_bias_update(const int32_t* counts, int E, float rate, f
   return hipGetLastError();
 }
 
+// status |= 1 when any of the n values is a NaN or an infinity (exponent
+// field all ones).  Only the value 1 is ever written, so concurrent writers
+// agree and the result does not depend on their order.
+__global__ __launch_bounds__(256) void check_finite_kernel(const float* __restrict__ p, int64_t n,
+                                                           int32_t* __restrict__ status) {
+  const int64_t nvec = n / 4;
+  bool bad = false;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < nvec; i += stride) {
+    const uint4 u = reinterpret_cast<const uint4*>(p)[i];
+    bad |= ((u.x & 0x7f800000u) == 0x7f800000u) | ((u.y & 0x7f800000u) == 0x7f800000u) |
+           ((u.z & 0x7f800000u) == 0x7f800000u) | ((u.w & 0x7f800000u) == 0x7f800000u);
+  }
+  if (blockIdx.x == 0 && threadIdx.x < n - nvec * 4)
+    bad |= (__float_as_uint(p[nvec * 4 + threadIdx.x]) & 0x7f800000u) == 0x7f800000u;
+  if (__ballot(bad) != 0 && (threadIdx.x & 63) == 0) *status = 1;
+}
+
+hipError_t launch_check_finite(const float* p, int64_t n, int32_t* status, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n / 4 + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 2048) blocks = 2048;
+  check_finite_kernel<<<dim3(static_cast<unsigned>(blocks)), 256, 0, stream>>>(p, n, status);
+  return hipGetLastError();
+}
+
 }  // namespace moe
 
 namespace moe {

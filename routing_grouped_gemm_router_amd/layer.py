@@ -31,8 +31,8 @@ and every buffer is sized from T * k.  Buffers are allocated once per layer
 and reused across steps.  Python here only allocates and orders the calls.
 """
 import contextlib
-
 import math
+import os
 
 import torch
 
@@ -99,6 +99,11 @@ class MoELayer:
             self.route_status = torch.zeros(1, dtype=torch.int32, device=device)
         self.timer = None
         self.dev = torch.device(device)
+        # MOE_CHECK_FINITE set: non-finite router logits (a caller error) raise
+        # the device word finite_status to 1 (read it with finite_ok())
+        self.check_finite = os.environ.get("MOE_CHECK_FINITE", "") not in ("", "0")
+        if self.check_finite:
+            self.finite_status = torch.zeros(1, dtype=torch.int32, device=self.dev)
         self.w = weights
         T, d, E, k, f = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f
         N = T * k
@@ -338,6 +343,13 @@ class MoELayer:
             with self._span("shared_gemm1_wgrad"):
                 gm["wgrad"](a, sa, b, sb, self.poff_all, self.dws13)
 
+    def finite_ok(self):
+        """False once a forward met a non-finite logit (MOE_CHECK_FINITE set);
+        reads the device status word, so it synchronises."""
+        if not self.check_finite:
+            raise RuntimeError("MOE_CHECK_FINITE was not set when the layer was built")
+        return int(self.finite_status.item()) == 0
+
     # ------------------------------------------------------------ forward --
     def _span(self, name):
         return self.timer.span(name) if self.timer is not None else _NO_SPAN
@@ -347,6 +359,8 @@ class MoELayer:
         self.x = x
         with self._span("router_logits"):
             abi.moe_router_logits(x, w["w_r"], w.get("logit_bias"), self.logits)
+        if self.check_finite:
+            abi.moe_check_finite(self.logits, self.finite_status)
         with self._span("route_topk"):
             m = self.full if self.capacity is not None else dict(
                 counts=self.counts, offsets=self.offsets, dst_row=self.dst_row,
@@ -488,6 +502,26 @@ class MoELayer:
         with self._span("permute_bwd"):
             abi.moe_permute_bwd(self.dx_perm, self.dst_row, dxs, self.dx_router, self.dx)
         return self.dx
+
+    def data_movement_calls(self, dout):
+        """The layer's permute / combine calls and their backward, as issued in
+        the last step (same buffers, same arguments), one closure each, for
+        timing them on their own.  Valid after a forward and a backward."""
+        calls = {}
+        if self.x_perm is not None and not self.pad:
+            calls["permute"] = lambda: abi.moe_permute(self.x, self.dst_row, self.x_perm)
+        ys = self.ys if self.shared else None
+        calls["combine"] = lambda: abi.moe_unpermute_combine(
+            self.y, None if self.gated else self.topk_w, self.dst_row, ys, self.out)
+        if self.gated:
+            calls["combine_bwd"] = lambda: abi.moe_permute(dout, self.dst_row, self.dy)
+        else:
+            calls["combine_bwd"] = lambda: abi.moe_unpermute_combine_bwd(
+                dout, self.y, self.topk_w, self.dst_row, self.dy, self.d_topk_w)
+        dxs = self.dxs if self.shared else None
+        calls["permute_bwd"] = lambda: abi.moe_permute_bwd(self.dx_perm, self.dst_row, dxs,
+                                                           self.dx_router, self.dx)
+        return calls
 
     def grads(self):
         g = dict(dx=self.dx, d_logits=self.d_logits, dW_r=self.dw_r, dW13=self.dw13, dW2=self.dw2,

@@ -49,6 +49,9 @@ def _fake(n=1 << 20):
 
 @pytest.mark.parametrize("case,expect", [
     # (function, args) -> status
+    (("moe_check_finite", (None, 16, None, None)), -1),
+    (("moe_check_finite", (_fake(), -1, _fake(), None)), -2),
+    (("moe_check_finite", (_fake((1 << 20) + 4), 16, _fake(), None)), -4),
     (("moe_permute", (None, 1, None, 10, 64, 2, 20, None, None)), -1),
     (("moe_permute", (None, 7, None, 10, 64, 2, 20, None, None)), -3),
     (("moe_permute", (None, 1, None, -1, 64, 2, 20, None, None)), -2),
@@ -110,6 +113,7 @@ def test_validation_rejects_before_launch(lib, case, expect):
 
 def test_zero_sized_calls_are_noops(lib):
     assert lib.moe_permute(None, 1, None, 0, 64, 2, 0, None, None) == 0
+    assert lib.moe_check_finite(None, 0, None, None) == 0
     assert lib.moe_unpermute_combine(None, 1, None, None, None, 0, 64, 2, 0, None, None) == 0
     assert lib.moe_swiglu(None, 1, 0, 64, None, None) == 0
     assert lib.moe_router_logits(None, 1, None, None, 0, 64, 8, None, None) == 0

@@ -346,8 +346,12 @@ def test_grouped_gemm_swiglu_epilogues(gpu, dt, M, G, d, f, tile_fwd, tile_dgrad
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("T,d,E,bias", [(64, 128, 4, False), (1000, 4096, 128, True),
-                                        (515, 7168, 256, True)])
+                                        (515, 7168, 256, True), (300, 1000, 8, True),
+                                        (77, 40, 6, True), (129, 4096, 64, False)])
 def test_router_logits(gpu, dt, T, d, E, bias):
+    """The router's fp32 vector-ALU products against the fp64 oracle: each of
+    the three tile widths (E up to 64, 128, 256), ragged token, contraction
+    and column tiles, and the generic path (E % 4 != 0)."""
     tdt = torch.float32 if dt == "f32" else torch.bfloat16
     x = inputs.normal((T, d), 1.0, 61, 0, "cpu", tdt)
     w_r = inputs.normal((d, E), d ** -0.5, 62, 0, "cpu", torch.float32)
@@ -367,11 +371,10 @@ def test_router_logits(gpu, dt, T, d, E, bias):
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_router_fp32_accuracy(gpu, dt):
-    """The router products keep fp32 accuracy although they run on the bf16
-    matrix cores: operands whose 24 mantissa bits all matter (a spread of
-    magnitudes, values just off bf16 rounding boundaries) must come out within
-    a few fp32 roundings of the fp64 products -- a single bf16 term per
-    operand would be off by ~2^-9."""
+    """The router products carry fp32 accuracy: operands whose 24 mantissa
+    bits all matter (a spread of magnitudes, values just off bf16 rounding
+    boundaries) come out within a few fp32 roundings of the fp64 products --
+    any product rounded through bf16 would be off by ~2^-9."""
     T, d, E = 256, 1024, 64
     g = torch.Generator().manual_seed(71)
     mag = torch.exp2(torch.randint(-8, 9, (d, E), generator=g).float())
@@ -390,6 +393,26 @@ def test_router_fp32_accuracy(gpu, dt):
     rw, rx = oracle.router_logits_bwd(np64(x), w_r.numpy(), dz.numpy())
     assert_close("dW_r", dwr, rw, 2e-6)
     assert_close("dx_router", dxr, rx, 2e-6)
+
+
+@pytest.mark.parametrize("n,pos,val", [(8192 * 256, None, None), (8192 * 256, 5, float("nan")),
+                                       (8192 * 256, 8192 * 256 - 1, float("inf")),
+                                       (1003, 1001, float("-inf")), (1003, None, None),
+                                       (3, 2, float("nan"))])
+def test_check_finite(gpu, n, pos, val):
+    """The finite-logit status word: set to 1 by a NaN or an infinity anywhere
+    (first element, last element of a ragged tail), left alone otherwise, and
+    never cleared by a later clean call."""
+    x = torch.randn(n, dtype=torch.float32, device=DEV) * 1e30
+    if pos is not None:
+        x[pos] = val
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    abi.moe_check_finite(x, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == (0 if pos is None else 1)
+    abi.moe_check_finite(torch.zeros(64, dtype=torch.float32, device=DEV), status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == (0 if pos is None else 1)
 
 
 def test_bf16_rounding_bit_exact(gpu):
