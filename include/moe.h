@@ -127,6 +127,20 @@ int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int sco
                    int32_t* dst_row, int32_t* src_token, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* moe_route_topk for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same results, with the workspace taken from a fixed 4 MiB array that
+ * the library holds on each device until the process ends (no hipMalloc,
+ * hipFree or allocating library call).  Arguments as moe_route_topk, without
+ * the workspace.  Limit: ceil(T / 64) * E * 12 + 256 <= 4 MiB (e.g. T up to
+ * 87,000 tokens at E = 256), else MOE_ERR_UNSUPPORTED.  Every call on a GPU
+ * shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other host threads) race and must be serialised by the caller.  The first
+ * call on a device looks the array's address up (hipGetSymbolAddress). */
+int moe_route_topk_noalloc(const float* logits, int64_t T, int32_t E, int32_t k, int score,
+                           int renorm, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                           int64_t* offsets, int32_t* dst_row, int32_t* src_token, void* stream);
+
 /* Top-k with a selection-only expert bias on sigmoid scores (the
  * auxiliary-loss-free biasing of section 7, Load Balancing): the key of
  * expert e is sigmoid_spec(logits[t, e]) + sel_bias[e] (one fp32 addition);

@@ -74,6 +74,8 @@ SIGNATURES = {
                                           _p, _p, _sz, _p]),
     "moe_expert_bias_update": (_int, [_p, _i32, _f32, _p, _p]),
     "moe_check_finite": (_int, [_p, _i64, _p, _p]),
+    "moe_route_topk_noalloc": (_int, [_p, _i64, _i32, _i32, _int, _int, _p, _p, _p, _p, _p, _p,
+                                      _p]),
     "moe_pad_to_max": (_int, [_p, _p, _p, _p, _p, _i64, _i32, _i32, _i64, _p, _p, _p, _p, _p]),
     "moe_zero_unmapped_rows": (_int, [_p, _int, _p, _i64, _i64, _p]),
     "moe_quant_mxfp8_rows": (_int, [_p, _i64, _i64, _p, _p, _p]),
@@ -186,6 +188,14 @@ def moe_route_topk(logits, k, score, renorm, topk_idx, topk_w, counts, offsets, 
     _call("moe_route_topk", _ptr(logits), T, E, k, score, int(renorm), _ptr(topk_idx),
           _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(dst_row), _ptr(src_token),
           _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def moe_route_topk_noalloc(logits, k, score, renorm, topk_idx, topk_w, counts, offsets, dst_row,
+                           src_token, stream=None):
+    T, E = logits.shape
+    _call("moe_route_topk_noalloc", _ptr(logits), T, E, k, score, int(renorm), _ptr(topk_idx),
+          _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(dst_row), _ptr(src_token),
+          _stream(stream))
 
 
 def moe_route_topk_expert_bias(logits, sel_bias, k, renorm, topk_idx, topk_w, counts, offsets,

@@ -13,6 +13,10 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 
 // route.hip
 size_t route_topk_workspace(int64_t T, int E);
+// the allocation-free route's per-device scratch: its size, and its device
+// address on the current device (looked up once per device)
+size_t route_noalloc_scratch_bytes();
+hipError_t route_scratch_ptr(void** out);
 hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int score, int renorm,
                              const float* sel_bias, int32_t* topk_idx, float* topk_w,
                              int32_t* counts, int64_t* offsets, int32_t* dst_row,

@@ -208,6 +208,28 @@ int moe_expert_bias_update(const int32_t* counts, int32_t E, float rate, float* 
                     fn);
 }
 
+int moe_route_topk_noalloc(const float* logits, int64_t T, int32_t E, int32_t k, int score,
+                           int renorm, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                           int64_t* offsets, int32_t* dst_row, int32_t* src_token, void* stream) {
+  const char* fn = "moe_route_topk_noalloc";
+  int st = check_route_shape(fn, T, E, k, score);
+  if (st != MOE_OK) return st;
+  REQUIRE(counts && offsets, MOE_ERR_NULL, "%s: counts and offsets are required", fn);
+  REQUIRE(T == 0 || (logits && topk_idx && topk_w && dst_row && src_token), MOE_ERR_NULL,
+          "%s: logits, topk_idx, topk_w, dst_row and src_token are required", fn);
+  const size_t need = moe::route_topk_workspace(T, E);
+  REQUIRE(need <= moe::route_noalloc_scratch_bytes(), MOE_ERR_UNSUPPORTED,
+          "%s: needs %zu bytes of scratch, above the fixed %zu (ceil(T/64) * E * 12 + 256)", fn,
+          need, moe::route_noalloc_scratch_bytes());
+  void* scratch = nullptr;
+  hipError_t e = moe::route_scratch_ptr(&scratch);
+  if (e != hipSuccess) return hip_status(e, fn);
+  return hip_status(moe::launch_route_topk(logits, T, E, k, score, renorm != 0, nullptr, topk_idx,
+                                           topk_w, counts, offsets, dst_row, src_token, scratch,
+                                           as_stream(stream)),
+                    fn);
+}
+
 int moe_check_finite(const float* x, int64_t n, int32_t* status, void* stream) {
   const char* fn = "moe_check_finite";
   REQUIRE(n >= 0, MOE_ERR_SHAPE, "%s: n=%lld", fn, static_cast<long long>(n));

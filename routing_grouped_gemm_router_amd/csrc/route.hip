@@ -13,6 +13,8 @@
 // expert (built with LDS bitwise OR, which is order independent).  A scan over
 // tiles gives each (tile, expert) its base row; a token's rank inside its tile
 // is the popcount of the mask below its bit.
+#include <atomic>
+
 #include "common.h"
 #include "internal.h"
 
@@ -389,6 +391,39 @@ hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int s
         topk_idx, tile_bits, tile_base, offsets, T, E, k, dst_row, src_token);
   }
   return hipGetLastError();
+}
+
+// ---- the allocation-free route -----------------------------------------------
+// Scratch of moe_route_topk_noalloc: the tile masks and per-tile row bases
+// that moe_route_topk keeps in the caller's workspace, in a fixed array that
+// each device holds for the life of the process.  Host code reaches it only
+// through the device address hipGetSymbolAddress returns (the array's name on
+// the host is not a device address), looked up once per device.
+constexpr size_t kRouteScratchBytes = size_t(4) << 20;
+__device__ __align__(256) unsigned char scratch[kRouteScratchBytes];
+
+size_t route_noalloc_scratch_bytes() { return kRouteScratchBytes; }
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t route_scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // every caller on this device gets the same address, so a race only repeats the lookup
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
 }
 
 hipError_t launch_route_replay(const float* logits, const int32_t* idx_in, int64_t T, int E, int k,

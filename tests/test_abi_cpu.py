@@ -50,6 +50,12 @@ def _fake(n=1 << 20):
 @pytest.mark.parametrize("case,expect", [
     # (function, args) -> status
     (("moe_check_finite", (None, 16, None, None)), -1),
+    (("moe_route_topk_noalloc", (_fake(), 1 << 20, 1024, 1, 0, 1, _fake(), _fake(), _fake(),
+                                 _fake(), _fake(), _fake(), None)), -4),
+    (("moe_route_topk_noalloc", (_fake(), 10, 2000, 2, 0, 1, _fake(), _fake(), _fake(), _fake(),
+                                 _fake(), _fake(), None)), -4),
+    (("moe_route_topk_noalloc", (None, 10, 8, 2, 0, 1, None, None, _fake(), _fake(), None, None,
+                                 None)), -1),
     (("moe_check_finite", (_fake(), -1, _fake(), None)), -2),
     (("moe_check_finite", (_fake((1 << 20) + 4), 16, _fake(), None)), -4),
     (("moe_permute", (None, 1, None, 10, 64, 2, 20, None, None)), -1),
