@@ -90,21 +90,30 @@ def block_scale(amax):
     return scale, inv
 
 
+def _scales(amax):
+    """(scale, inv) of an array of block maxima: the same fp32 divisions as
+    ``block_scale``, element by element (NumPy's float32 division is the IEEE
+    one), and 1 where amax == 0."""
+    amax = np.asarray(amax, dtype=np.float32)
+    zero = amax == 0
+    safe = np.where(zero, np.float32(1.0), amax).astype(np.float32)
+    scale = np.where(zero, np.float32(1.0), safe / np.float32(E4M3_MAX)).astype(np.float32)
+    inv = np.where(zero, np.float32(1.0), np.float32(E4M3_MAX) / safe).astype(np.float32)
+    return scale, inv
+
+
 def quantize_rows(x, block=128):
     """1 x ``block`` tiles along the last axis of x [M, K] (K % block == 0).
-    Returns codes uint8 [M, K] and fp32 scales [M, K / block]."""
+    Returns codes uint8 [M, K] and fp32 scales [M, K / block].  Every tile at
+    once: amax per tile, ``block_scale``'s fp32 scale and inverse, one fp32
+    product per element, then ``encode``."""
     x = np.asarray(x, dtype=np.float32)
     M, K = x.shape
     assert K % block == 0
-    q = np.empty((M, K), dtype=np.uint8)
-    s = np.empty((M, K // block), dtype=np.float32)
-    for i in range(M):
-        for b in range(K // block):
-            v = x[i, b * block:(b + 1) * block]
-            scale, inv = block_scale(np.max(np.abs(v)))
-            q[i, b * block:(b + 1) * block] = encode((v * inv).astype(np.float32))
-            s[i, b] = scale
-    return q, s
+    t = x.reshape(M, K // block, block)
+    scale, inv = _scales(np.abs(t).max(axis=2) if M else np.zeros((0, K // block), np.float32))
+    q = encode((t * inv[:, :, None]).astype(np.float32)).reshape(M, K)
+    return q, scale
 
 
 def quantize_blocks(w, block=128):
@@ -113,15 +122,10 @@ def quantize_blocks(w, block=128):
     w = np.asarray(w, dtype=np.float32)
     K, N = w.shape
     assert K % block == 0 and N % block == 0
-    q = np.empty((K, N), dtype=np.uint8)
-    s = np.empty((K // block, N // block), dtype=np.float32)
-    for i in range(K // block):
-        for j in range(N // block):
-            v = w[i * block:(i + 1) * block, j * block:(j + 1) * block]
-            scale, inv = block_scale(np.max(np.abs(v)))
-            q[i * block:(i + 1) * block, j * block:(j + 1) * block] = encode((v * inv).astype(np.float32))
-            s[i, j] = scale
-    return q, s
+    t = w.reshape(K // block, block, N // block, block)
+    scale, inv = _scales(np.abs(t).max(axis=(1, 3)))
+    q = encode((t * inv[:, None, :, None]).astype(np.float32)).reshape(K, N)
+    return q, scale
 
 
 def dequantize_rows(q, s, block=128):
@@ -156,25 +160,20 @@ def quantize_token_tiles(x, offsets, block=128):
     rows [offsets[g], offsets[g+1]), each group zero-padded to a multiple of
     ``block`` rows (the contraction axis of a weight gradient is the tokens).
     Returns codes uint8 [M_pad, K], fp32 scales [M_pad / block, K] and the
-    padded offsets."""
+    padded offsets.  Padding rows are zeros, so they change no tile's amax
+    and get code 0."""
     x = np.asarray(x, dtype=np.float32)
     M, K = x.shape
     poff = padded_offsets(offsets, block)
     M_pad = int(poff[-1])
-    q = np.zeros((M_pad, K), dtype=np.uint8)
-    s = np.ones((M_pad // block, K), dtype=np.float32)
+    xp = np.zeros((M_pad, K), dtype=np.float32)
     for g in range(len(offsets) - 1):
-        lo, hi, plo = int(offsets[g]), int(offsets[g + 1]), int(poff[g])
-        for b in range((hi - lo + block - 1) // block):
-            r0 = lo + b * block
-            r1 = min(hi, r0 + block)
-            tile = x[r0:r1]                                   # [rows, K]
-            for col in range(K):
-                scale, inv = block_scale(np.max(np.abs(tile[:, col])))
-                q[plo + b * block:plo + b * block + (r1 - r0), col] = \
-                    encode((tile[:, col] * inv).astype(np.float32))
-                s[plo // block + b, col] = scale
-    return q, s, poff
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        xp[poff[g]:poff[g] + hi - lo] = x[lo:hi]
+    t = xp.reshape(M_pad // block, block, K)
+    scale, inv = _scales(np.abs(t).max(axis=1) if M_pad else np.zeros((0, K), np.float32))
+    q = encode((t * inv[:, None, :]).astype(np.float32)).reshape(M_pad, K)
+    return q, scale, poff
 
 
 def dequantize_token_tiles(q, s, block=128):
@@ -182,7 +181,7 @@ def dequantize_token_tiles(q, s, block=128):
 
 
 def layer_fp8(x, w_r, w13, w2, dout, k, score, renorm, logit_bias=None, shared=None,
-              quantize=True, block=128, recipe="block", trace=None):
+              quantize=True, block=128, recipe="block", trace=None, z=None):
     """Forward and backward of the MoE layer with every expert-GEMM input
     quantized blockwise to E4M3 (the fp8 recipe above), computed as fp64
     grouped GEMMs on the dequantized values.
@@ -201,7 +200,8 @@ def layer_fp8(x, w_r, w13, w2, dout, k, score, renorm, logit_bias=None, shared=N
     and gradients.  ``trace``, if a dict, receives every GEMM's operands as
     fed to it (dequantized), keyed "<gemm>.A" / "<gemm>.B", together with the
     tensors they were quantized from ("src.<name>") and the padded offsets;
-    recording changes nothing that is computed.
+    recording changes nothing that is computed.  ``z`` may give the fp32 keys
+    directly (by default they are computed with ``router_logits``).
     """
     from . import moe_oracle as o
 
@@ -245,7 +245,8 @@ def layer_fp8(x, w_r, w13, w2, dout, k, score, renorm, logit_bias=None, shared=N
 
     x = o.f64(x)
     T = x.shape[0]
-    z = o.router_logits(x, w_r, logit_bias)
+    if z is None:
+        z = o.router_logits(x, w_r, logit_bias)
     r = o.route(z, k, score, renorm)
     off = r["offsets"]
     w13d, w2d = rec("fwd1.B", q_weights(w13)), rec("fwd2.B", q_weights(w2))

@@ -16,7 +16,7 @@ import oracle
 from oracle import fp8
 from routing_grouped_gemm_router_amd import abi, inputs
 from routing_grouped_gemm_router_amd.layer import MoELayer
-from gpu_util import TOL, assert_close, layer_inputs_without_near_ties, np64
+from gpu_util import TOL, assert_close, np64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -166,7 +166,7 @@ SMALL_FP8 = inputs.LayerConfig("small_fp8_shared", T=400, d=256, E=8, k=2, f=256
                          ids=lambda c: c.name)
 def test_layer_fp8(gpu, cfg):
     print(f"fp8 layer {cfg.name}", flush=True)
-    inp = layer_inputs_without_near_ties(cfg, 0)
+    inp = inputs.layer_inputs(cfg, 0)
     w = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
     layer = MoELayer(cfg, w, DEV)
     layer.forward(w["x"])
@@ -176,7 +176,9 @@ def test_layer_fp8(gpu, cfg):
     bias = None if inp["logit_bias"] is None else inp["logit_bias"].numpy()
     ref = fp8.layer_fp8(np64(inp["x"]), inp["w_r"].numpy(), np64(inp["w13"]), np64(inp["w2"]),
                         np64(inp["dout"]), cfg.k, cfg.score, cfg.renorm, logit_bias=bias,
-                        shared=shared)
+                        shared=shared, z=layer.logits.cpu().numpy())
+    assert_close("logits (oracle's own)", layer.logits,
+                 oracle.router_logits(np64(inp["x"]), inp["w_r"].numpy(), bias), TOL["f32"])
     r = ref["route"]
     np.testing.assert_array_equal(layer.dst_row.cpu().numpy(), r["dst_row"])
     np.testing.assert_array_equal(layer.offsets.cpu().numpy(), r["offsets"])
@@ -184,3 +186,76 @@ def test_layer_fp8(gpu, cfg):
     g = layer.grads()
     for name in ["dx", "d_logits", "dW_r", "dW13", "dW2"] + (["dWs13", "dWs2"] if cfg.fs else []):
         assert_close(name, g[name], ref[name], TOL["fp8"])
+
+
+def _bf16_neighbours(v):
+    """The bf16 values just below and just above each of v (positive, finite)."""
+    b = torch.from_numpy(np.asarray(v, np.float32)).to(torch.bfloat16)
+    u = b.view(torch.int16).to(torch.int32)
+    lo = (u - 1).to(torch.int16).view(torch.bfloat16)
+    hi = (u + 1).to(torch.int16).view(torch.bfloat16)
+    return lo.float().numpy(), hi.float().numpy()
+
+
+def _e4m3_sweep(limit):
+    """bf16 values probing every rounding decision of E4M3 up to ``limit``:
+    all finite E4M3 magnitudes, every midpoint between neighbours (including
+    the subnormal ones and the one between 0 and the least subnormal), the
+    bf16 neighbours of each, far-underflowing values, and both signs."""
+    vals = np.unique(np.abs(fp8.decode(np.arange(0x7F))))            # 0 .. 448
+    mids = (vals[1:] + vals[:-1]) / 2
+    pts = np.concatenate([vals, mids])
+    pts = pts[pts > 0]
+    lo, hi = _bf16_neighbours(pts)
+    extra = [2.0 ** -20, 2.0 ** -126, 2.0 ** -133, 0.0]
+    pos = np.concatenate([pts, lo, hi, extra])
+    pos = pos[(pos >= 0) & (pos <= limit)]
+    v = np.concatenate([pos, -pos]).astype(np.float32)
+    return torch.from_numpy(v).to(torch.bfloat16).float().numpy()   # exactly bf16 values
+
+
+def test_e4m3_dense_sweep_rows(gpu):
+    """The hardware E4M3 conversion in moe_quant_fp8_rows against the
+    definition encoder, bit for bit, at unit scale: every 128-tile carries
+    448 (so scale = inv = 1 exactly and each code is encode(v) itself) and
+    127 values of the sweep (midpoints with ties to even, their bf16
+    neighbours, subnormal midpoints, +-0, underflow)."""
+    v = _e4m3_sweep(448.0)
+    n_tiles = (len(v) + 126) // 127
+    x = np.zeros((n_tiles, 128), np.float32)
+    x[:, 0] = 448.0
+    x.reshape(-1)[np.concatenate([np.arange(1 + 128 * i, 128 * (i + 1)) for i in range(n_tiles)])[:len(v)]] = v
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    assert torch.equal(xb.float(), torch.from_numpy(x))
+    q = torch.empty((n_tiles, 128), dtype=torch.uint8, device=DEV)
+    sT = torch.empty((1, n_tiles), dtype=torch.float32, device=DEV)
+    abi.moe_quant_fp8_rows(xb.to(DEV), q, sT)
+    assert (sT.cpu().numpy() == 1.0).all()
+    got = q.cpu().numpy()
+    np.testing.assert_array_equal(got, fp8.encode(x))
+    assert len(v) > 1000
+
+
+def test_e4m3_dense_sweep_mx_rows(gpu):
+    """The same sweep through moe_quant_mxfp8_rows at shared exponent 0: every
+    32-block carries 256 (X = floor(log2 256) - 8 = 0, an exact scaling by 1),
+    so the codes are encode(v); here the sweep also spans the saturating band
+    [448, 512) (bf16 values 448, 450, ..., 510 -> 448)."""
+    band = np.arange(448.0, 512.0, 2.0)
+    v = np.concatenate([_e4m3_sweep(448.0), band, -band]).astype(np.float32)
+    n_blk = (len(v) + 30) // 31
+    x = np.zeros((n_blk, 32), np.float32)
+    x[:, 0] = 256.0
+    flat = np.concatenate([np.arange(1 + 32 * i, 32 * (i + 1)) for i in range(n_blk)])[:len(v)]
+    x.reshape(-1)[flat] = v
+    pad = (-x.size) % 128                      # rows of K = 128 (4 blocks each)
+    xr = np.concatenate([x.reshape(-1), np.tile(np.array([256.0] + [0.0] * 31, np.float32),
+                                                 pad // 32)]).reshape(-1, 128)
+    xb = torch.from_numpy(xr).to(torch.bfloat16)
+    assert torch.equal(xb.float(), torch.from_numpy(xr))
+    M = xr.shape[0]
+    q = torch.empty((M, 128), dtype=torch.uint8, device=DEV)
+    s = torch.empty((M, 4), dtype=torch.uint8, device=DEV)
+    abi.moe_quant_mxfp8_rows(xb.to(DEV), q, s)
+    assert (s.cpu().numpy() == 127).all()
+    np.testing.assert_array_equal(q.cpu().numpy(), fp8.encode(xr))

@@ -1,12 +1,24 @@
 """Parity at the workloads' full sizes, in the launch configuration bench.py
 times (MoELayer forward + backward on GPU-resident inputs).
 
-Routing, counts, offsets and the permutation are compared in full and
-bit-exactly (inputs are drawn with no near-tie at the top-k boundary).  The
-oracle then recomputes, one by one, the output, dx and router gradient of a
-sample of tokens (including tokens of the largest, a median and the smallest
-non-empty expert), and full columns of dW1 / dW3 and rows of dW2 of a sample
-of experts; each compared by max|err| / max|ref| within the bf16 bound."""
+Routing: the oracle's own fp32 logits are compared with the GPU's (1e-5 of
+max|ref|), and the oracle then routes from the GPU's logits tensor, so the
+routing indices, routing weights, counts, offsets and permutation are
+compared in full and bit-exactly without re-drawing near-tie tokens.
+
+Outputs and gradients are recomputed by the oracle on exact subsets:
+  * out, dx and d_logits of sampled tokens with the full hidden size (bf16
+    layers: 128 tokens, including the first token of the largest, median and
+    smallest non-empty expert and tokens at 128- and 256-row tile boundaries
+    and in the ragged last tile of the largest expert);
+  * whole columns of dW1 / dW3 and rows of dW2 (64 ffn indices including 0
+    and f - 1) of 5 experts: the largest, the smallest non-empty, the median
+    and 2 random ones, each over all of the expert's rows.
+A column of dW1 depends only on that column's activations and a token's
+output only on its own row, so each subset is exact.  Each tensor is
+compared by max|err| / max|ref| within the stated bound of its arithmetic."""
+import concurrent.futures as cf
+
 import numpy as np
 import pytest
 import torch
@@ -14,137 +26,169 @@ import torch
 import oracle
 from routing_grouped_gemm_router_amd import inputs
 from routing_grouped_gemm_router_amd.layer import MoELayer
-from gpu_util import TOL, assert_close, near_tie_tokens, np64
+from gpu_util import TOL, assert_close, np64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
+POOL = 8
 
 
-def _inputs_without_near_ties(cfg, seed, rel_gap=1e-4, attempts=10):
+def _run(cfg, seed=0):
     inp = inputs.layer_inputs(cfg, seed, DEV)
-    w_r = inp["w_r"].cpu().numpy()
-    bias = None if inp["logit_bias"] is None else inp["logit_bias"].cpu().numpy()
-    for attempt in range(attempts):
-        z = oracle.router_logits(np64(inp["x"]), w_r, bias)
-        bad = near_tie_tokens(z, cfg.k, rel_gap)
-        if len(bad) == 0:
-            return inp, z
-        print(f"  resampling {len(bad)} near-tie token rows", flush=True)
-        inputs.resample_rows(inp["x"], [int(t) for t in bad], seed, attempt)
-    raise RuntimeError("could not draw inputs without near-ties")
-
-
-def _sample_tokens(r, n_random, seed):
-    counts = r["counts"]
-    nz = np.nonzero(counts)[0]
-    big, small = nz[np.argmax(counts[nz])], nz[np.argmin(counts[nz])]
-    med = nz[np.argsort(counts[nz])[len(nz) // 2]]
-    toks = set()
-    for e in (big, med, small):
-        seg = r["src_token"][r["offsets"][e]:r["offsets"][e + 1]]
-        toks.update(int(t) for t in seg[:1])
-    rng = np.random.default_rng(seed)
-    T = r["topk_idx"].shape[0]
-    toks.update(int(t) for t in rng.choice(T, n_random, replace=False))
-    toks.add(T - 1)
-    return sorted(toks), [int(big), int(med), int(small)]
-
-
-@pytest.mark.parametrize("name,n_tok,n_exp_rand", [
-    ("llama3_8b_e8k2", 5, 1),
-    ("qwen3_235b_e128k8", 5, 1),
-    ("deepseek_v3_e256k8", 4, 1),
-])
-def test_fullsize_layer(gpu, name, n_tok, n_exp_rand):
-    cfg = inputs.CONFIGS[name]
-    print(f"full-size layer {name}", flush=True)
-    inp, z = _inputs_without_near_ties(cfg, seed=0)
     layer = MoELayer(cfg, inp, DEV)
     layer.forward(inp["x"])
     layer.backward(inp["dout"])
     torch.cuda.synchronize()
+    return layer, inp
 
-    # ---- routing, in full and bit-exact
-    assert_close("logits", layer.logits, z, TOL["f32"])
+
+def _routing(layer, inp, cfg):
+    """The oracle's logits against the GPU's, then the oracle's routing from
+    the GPU's logits, compared bit for bit.  Returns (z, route)."""
+    w_r = inp["w_r"].cpu().numpy()
+    bias = None if inp["logit_bias"] is None else inp["logit_bias"].cpu().numpy()
+    assert_close("logits (oracle's own)", layer.logits,
+                 oracle.router_logits(np64(inp["x"]), w_r, bias), TOL["f32"])
+    z = layer.logits.cpu().numpy()
     r = oracle.route(z, cfg.k, cfg.score, cfg.renorm)
-    np.testing.assert_array_equal(layer.topk_idx.cpu().numpy(), r["topk_idx"])
-    np.testing.assert_array_equal(layer.counts.cpu().numpy(), r["counts"])
-    np.testing.assert_array_equal(layer.offsets.cpu().numpy(), r["offsets"])
-    np.testing.assert_array_equal(layer.dst_row.cpu().numpy(), r["dst_row"])
-    np.testing.assert_array_equal(layer.src_token.cpu().numpy(), r["src_token"])
+    for name in ("topk_idx", "counts", "offsets", "dst_row", "src_token"):
+        np.testing.assert_array_equal(getattr(layer, name).cpu().numpy(), r[name], err_msg=name)
     assert_close("topk_w", layer.topk_w, r["topk_w"], TOL["f32"])
+    return z, r
 
+
+def _expert_sizes(r):
+    counts = r["counts"]
+    nz = np.nonzero(counts)[0]
+    order = nz[np.argsort(counts[nz], kind="stable")]
+    return int(order[-1]), int(order[len(order) // 2]), int(order[0]), nz
+
+
+def _sample_tokens(r, n, seed):
+    """n tokens: the first of the largest, median and smallest non-empty
+    experts; the tokens at rows 0, 127, 128, 255, 256 and the last three rows
+    of the largest expert's segment (tile boundaries and its ragged last
+    tile); the last token; then random ones."""
+    big, med, small, _ = _expert_sizes(r)
+    toks = []
+    for e, pos in [(big, [0, 127, 128, 255, 256, -3, -2, -1]), (med, [0]), (small, [0])]:
+        seg = r["src_token"][r["offsets"][e]:r["offsets"][e + 1]]
+        toks += [int(seg[p]) for p in pos if -len(seg) <= p < len(seg)]
+    T = r["topk_idx"].shape[0]
+    toks.append(T - 1)
+    rng = np.random.default_rng(seed)
+    for t in rng.permutation(T):
+        if len(set(toks)) >= n:
+            break
+        toks.append(int(t))
+    return sorted(set(toks))
+
+
+def _greedy_tokens(r, n, seed, must=()):
+    """n tokens chosen to share experts (each next token adds the fewest new
+    experts among 4000 random candidates), starting from ``must``: a sample
+    whose per-token oracle needs few experts' quantized weights."""
+    idx = r["topk_idx"]
+    rng = np.random.default_rng(seed)
+    cand = rng.choice(idx.shape[0], min(4000, idx.shape[0]), replace=False)
+    chosen = list(dict.fromkeys(int(t) for t in must))
+    used = set(int(e) for t in chosen for e in idx[t])
+    while len(chosen) < n:
+        best = min((int(t) for t in cand if int(t) not in chosen),
+                   key=lambda t: len(set(int(e) for e in idx[t]) - used))
+        chosen.append(best)
+        used |= set(int(e) for e in idx[best])
+    return sorted(chosen)
+
+
+def _prepared_experts(inp, experts, prep):
+    """Yields (e, prep(w13_e, w2_e)) for the experts, prepared POOL at a time
+    on host threads (expert weights widened to float64 one by one)."""
+    experts = [int(e) for e in experts]
+    for i in range(0, len(experts), POOL):
+        batch = experts[i:i + POOL]
+        raw = {e: (np64(inp["w13"][e]), np64(inp["w2"][e])) for e in batch}
+        with cf.ThreadPoolExecutor(POOL) as ex:
+            done = list(ex.map(lambda e: (e, prep(*raw[e])), batch))
+        del raw
+        yield from done
+
+
+def _token_reference(cfg, inp, z, r, toks, prep, chain, shared_w):
+    """The oracle's out, dx and d_logits of the sampled tokens, one expert at
+    a time over the (token, slot) pairs routed to it.  ``chain(x_rows,
+    dy_rows, w) -> (y, dx_rows)`` is one expert's forward output and data
+    gradient; ``prep`` turns an expert's float64 weights into w."""
+    S = np.asarray(toks)
+    n, k = len(S), cfg.k
+    x_s, dout_s = np64(inp["x"][torch.from_numpy(S).to(DEV)]), np64(
+        inp["dout"][torch.from_numpy(S).to(DEV)])
+    out = np.zeros((n, cfg.d))
+    dx = np.zeros((n, cfg.d))
+    dw = np.zeros((n, k))
+    idx = r["topk_idx"][S]
+    for e, w in _prepared_experts(inp, np.unique(idx), prep):
+        ii, jj = np.nonzero(idx == e)
+        wt = r["topk_w"][S[ii], jj]
+        y, dxe = chain(x_s[ii], wt[:, None] * dout_s[ii], w)
+        dw[ii, jj] = (dout_s[ii] * y).sum(axis=1)
+        out[ii] += wt[:, None] * y
+        dx[ii] += dxe
+    if shared_w is not None:
+        ys, dxs = chain(x_s, dout_s, shared_w)
+        out += ys
+        dx += dxs
+    dz = oracle.route_bwd(z[S], r["topk_idx"][S], r["topk_w"][S], dw, cfg.score, cfg.renorm)
+    dx += dz @ inp["w_r"].cpu().numpy().astype(np.float64).T
+    return out, dx, dz
+
+
+def _bf16_chain(x_rows, dy_rows, w):
+    w13e, w2e = w
+    a, b, h, y = oracle.expert_ffn(x_rows, w13e, w2e)
+    dab = oracle.swiglu_bwd(dy_rows @ w2e.T, np.concatenate([a, b], axis=1))
+    return y, dab @ w13e.T
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["llama3_8b_e8k2", "qwen3_235b_e128k8", "deepseek_v3_e256k8"])
+def test_fullsize_layer(gpu, name):
+    cfg = inputs.CONFIGS[name]
+    print(f"full-size layer {name}", flush=True)
+    layer, inp = _run(cfg)
+    z, r = _routing(layer, inp, cfg)
     tol = TOL[cfg.gemm]
-    toks, experts = _sample_tokens(r, n_tok, seed=1)
-    print(f"  sampled tokens {toks}; experts {experts}", flush=True)
-    w_r = inp["w_r"].cpu().numpy().astype(np.float64)
-    shared = None
-    if cfg.fs:
-        shared = (np64(inp["ws13"]), np64(inp["ws2"]))
-    cache = {}
-
-    def expert(e):
-        if e not in cache:
-            cache.clear() if len(cache) > 8 else None
-            cache[e] = (np64(inp["w13"][e]), np64(inp["w2"][e]))
-        return cache[e]
-
-    # ---- per-token outputs, dx and router gradient
-    out_ref, dx_ref, dz_ref = [], [], []
-    for t in toks:
-        x_t = np64(inp["x"][t])
-        dout_t = np64(inp["dout"][t])
-        o = np.zeros(cfg.d)
-        dx = np.zeros(cfg.d)
-        dw = np.zeros((1, cfg.k))
-        for j in range(cfg.k):
-            e = int(r["topk_idx"][t, j])
-            w13e, w2e = expert(e)
-            a, b, h, y = oracle.expert_ffn(x_t, w13e, w2e)
-            o += r["topk_w"][t, j] * y
-            dw[0, j] = dout_t @ y
-            dxe, _, _ = oracle.expert_ffn_bwd(x_t, w13e, w2e, a, b, h, r["topk_w"][t, j] * dout_t)
-            dx += dxe
-        if shared is not None:
-            a, b, h, y = oracle.expert_ffn(x_t, *shared)
-            o += y
-            dxs, _, _ = oracle.expert_ffn_bwd(x_t, shared[0], shared[1], a, b, h, dout_t)
-            dx += dxs
-        dz = oracle.route_bwd(z[t:t + 1], r["topk_idx"][t:t + 1], r["topk_w"][t:t + 1], dw,
-                              cfg.score, cfg.renorm)
-        dx += (dz @ w_r.T)[0]
-        out_ref.append(o)
-        dx_ref.append(dx)
-        dz_ref.append(dz[0])
+    toks = _sample_tokens(r, 128, seed=1)
+    big, med, small, nz = _expert_sizes(r)
+    print(f"  {len(toks)} tokens over {len(np.unique(r['topk_idx'][toks]))} experts; "
+          f"experts largest {big} ({r['counts'][big]} rows), median {med}, smallest {small}",
+          flush=True)
+    shared = (np64(inp["ws13"]), np64(inp["ws2"])) if cfg.fs else None
+    out, dx, dz = _token_reference(cfg, inp, z, r, toks, lambda a, b: (a, b), _bf16_chain, shared)
     idx = torch.tensor(toks, device=DEV)
-    assert_close("out (sampled tokens)", layer.out[idx], np.stack(out_ref), tol)
-    assert_close("dx (sampled tokens)", layer.dx[idx], np.stack(dx_ref), tol)
-    assert_close("d_logits (sampled tokens)", layer.d_logits[idx], np.stack(dz_ref), tol)
+    assert_close("out (sampled tokens)", layer.out[idx], out, tol)
+    assert_close("dx (sampled tokens)", layer.dx[idx], dx, tol)
+    assert_close("d_logits (sampled tokens)", layer.d_logits[idx], dz, tol)
 
-    # ---- weight gradients: whole columns / rows of sampled experts
+    # weight gradients: 64 whole columns / rows of 5 experts
     rng = np.random.default_rng(2)
-    nz = np.nonzero(r["counts"])[0]
-    exps = experts + [int(e) for e in rng.choice(nz, n_exp_rand, replace=False)]
-    cols = np.unique(np.concatenate([[0, cfg.f - 1], rng.choice(cfg.f, 14, replace=False)]))
-    x_all = None
-    for e in exps:
+    rest = [int(e) for e in nz if int(e) not in (big, med, small)]
+    exps = list(dict.fromkeys([big, small, med] + [int(e) for e in rng.choice(rest, 2, replace=False)]))
+    cols = np.unique(np.concatenate([[0, cfg.f - 1], rng.choice(cfg.f, 62, replace=False)]))
+    c = torch.from_numpy(cols).to(DEV)
+    for e, (w13e, w2e) in _prepared_experts(inp, exps, lambda a, b: (a, b)):
         lo, hi = r["offsets"][e], r["offsets"][e + 1]
         toks_e = r["src_token"][lo:hi].astype(np.int64)
         slots = np.array([int(np.nonzero(r["topk_idx"][t] == e)[0][0]) for t in toks_e])
-        x_rows = np64(inp["x"][torch.from_numpy(toks_e).to(DEV)])
-        dout_rows = np64(inp["dout"][torch.from_numpy(toks_e).to(DEV)])
-        dy_rows = r["topk_w"][toks_e, slots][:, None] * dout_rows
-        w13e, w2e = expert(e)
-        d1, d3, d2 = oracle.expert_wgrad_columns(x_rows, dy_rows, w13e, w2e, cols)
-        c = torch.from_numpy(cols).to(DEV)
+        rows = torch.from_numpy(toks_e).to(DEV)
+        dy_rows = r["topk_w"][toks_e, slots][:, None] * np64(inp["dout"][rows])
+        d1, d3, d2 = oracle.expert_wgrad_columns(np64(inp["x"][rows]), dy_rows, w13e, w2e, cols)
         assert_close(f"dW1[{e}] cols ({hi - lo} rows)", layer.dw13[e][:, c], d1, tol)
         assert_close(f"dW3[{e}] cols", layer.dw13[e][:, cfg.f + c], d3, tol)
         assert_close(f"dW2[{e}] rows", layer.dw2[e][c, :], d2, tol)
     if shared is not None:
-        x_all = np64(inp["x"])
-        d1, d3, d2 = oracle.expert_wgrad_columns(x_all, np64(inp["dout"]), shared[0], shared[1],
-                                                 cols)
-        c = torch.from_numpy(cols).to(DEV)
+        d1, d3, d2 = oracle.expert_wgrad_columns(np64(inp["x"]), np64(inp["dout"]), shared[0],
+                                                 shared[1], cols)
         assert_close("dWs1 cols", layer.dws13[0][:, c], d1, tol)
         assert_close("dWs3 cols", layer.dws13[0][:, cfg.fs + c], d3, tol)
         assert_close("dWs2 rows", layer.dws2[0][c, :], d2, tol)
@@ -152,105 +196,123 @@ def test_fullsize_layer(gpu, name, n_tok, n_exp_rand):
     torch.cuda.empty_cache()
 
 
-def test_fullsize_fp8_layer(gpu):
-    """The blockwise-fp8 DeepSeek-V3 layer at its full size (T = 32768), in
-    the launch configuration bench.py times.  Routing in full and bit-exact;
-    then the oracle's quantize-at-every-GEMM-input chain (oracle.fp8, the
-    blockwise recipe) recomputed one token at a time -- 1 x 128 activation
-    tiles are row-local, and each involved expert's weights are quantized in
-    128 x 128 blocks -- for the output and dx of a sampled token; and, for
-    the smallest non-empty expert, its whole segment quantized in 128-token
-    tiles for columns of dW1 / dW3 and rows of dW2.  Within the fp8 bound."""
+# ---------------------------------------------------------------- fp8 --------
+def _lowp_ops(mx):
+    """Quantize-dequantize helpers of the oracle's recipe: rows of an
+    activation or gradient (stored bf16, then 1 x 128 tiles or 1 x 32 MX
+    blocks), a weight for the forward and for the data gradient, and token
+    tiles of one expert's segment."""
     from oracle import fp8
 
-    cfg = inputs.CONFIGS["deepseek_v3_fp8"]
-    print("full-size fp8 layer", flush=True)
-    inp, z = _inputs_without_near_ties(cfg, seed=0)
-    layer = MoELayer(cfg, inp, DEV)
-    layer.forward(inp["x"])
-    layer.backward(inp["dout"])
-    torch.cuda.synchronize()
-    r = oracle.route(z, cfg.k, cfg.score, cfg.renorm)
-    for name in ("topk_idx", "counts", "offsets", "dst_row", "src_token"):
-        np.testing.assert_array_equal(getattr(layer, name).cpu().numpy(), r[name], err_msg=name)
-    tol = TOL["fp8"]
+    def rows(a):
+        a = fp8.to_bf16(np.atleast_2d(a))
+        if mx:
+            return fp8.dequantize_mx_rows(*fp8.quantize_mx_rows(a))
+        return fp8.dequantize_rows(*fp8.quantize_rows(a))
 
-    def q_rows(a):  # bf16 storage, then 1 x 128 tiles
-        q, s = fp8.quantize_rows(fp8.to_bf16(np.atleast_2d(a)))
-        return fp8.dequantize_rows(q, s)
-
-    def q_weight(w):  # 128 x 128 blocks (the same blocks serve the forward and dgrad)
-        q, s = fp8.quantize_blocks(fp8.to_bf16(w))
-        return fp8.dequantize_blocks(q, s)
-
-    cache = {}
-
-    def expert(e):
-        if e not in cache:
-            cache[e] = (q_weight(np64(inp["w13"][e])), q_weight(np64(inp["w2"][e])))
-        return cache[e]
-
-    def chain(x_rows, dy_rows, w13q, w2q):
-        """Forward and data gradient of one expert on rows (oracle.fp8's chain)."""
-        ab = q_rows(x_rows) @ w13q
-        h = oracle.swiglu(ab)
-        y = q_rows(h) @ w2q
-        dh = q_rows(dy_rows) @ w2q.T
-        dab = oracle.swiglu_bwd(dh, ab)
-        dx = q_rows(dab) @ w13q.T
-        return h, y, dab, dx
-
-    counts = r["counts"]
-    nz = np.nonzero(counts)[0]
-    med = nz[np.argsort(counts[nz])[len(nz) // 2]]
-    t = int(r["src_token"][r["offsets"][med]])
-    print(f"  sampled token {t}", flush=True)
-    x_t, dout_t = np64(inp["x"][t])[None], np64(inp["dout"][t])[None]
-    o = np.zeros((1, cfg.d))
-    dx = np.zeros((1, cfg.d))
-    dw = np.zeros((1, cfg.k))
-    for j in range(cfg.k):
-        e = int(r["topk_idx"][t, j])
-        w13q, w2q = expert(e)
-        _, y, _, _ = chain(x_t, np.zeros((1, cfg.d)), w13q, w2q)
-        dw[0, j] = (dout_t @ y.T)[0, 0]
-        _, y, _, dxe = chain(x_t, fp8.to_bf16(r["topk_w"][t, j] * dout_t), w13q, w2q)
-        o += r["topk_w"][t, j] * y
-        dx += dxe
-    ws = (q_weight(np64(inp["ws13"])), q_weight(np64(inp["ws2"])))
-    _, ys, _, dxs = chain(x_t, dout_t, *ws)
-    o += ys
-    dx += dxs
-    dz = oracle.route_bwd(z[t:t + 1], r["topk_idx"][t:t + 1], r["topk_w"][t:t + 1], dw, cfg.score,
-                          cfg.renorm)
-    dx += dz @ inp["w_r"].cpu().numpy().astype(np.float64).T
-    assert_close("out (sampled token)", layer.out[t:t + 1], o, tol)
-    assert_close("dx (sampled token)", layer.dx[t:t + 1], dx, tol)
-    assert_close("d_logits (sampled token)", layer.d_logits[t:t + 1], dz, tol)
-
-    # weight gradients of the smallest non-empty expert, whole segment
-    e = int(nz[np.argmin(counts[nz])])
-    lo, hi = int(r["offsets"][e]), int(r["offsets"][e + 1])
-    toks_e = r["src_token"][lo:hi].astype(np.int64)
-    slots = np.array([int(np.nonzero(r["topk_idx"][u] == e)[0][0]) for u in toks_e])
-    x_rows = np64(inp["x"][torch.from_numpy(toks_e).to(DEV)])
-    dy_rows = fp8.to_bf16(r["topk_w"][toks_e, slots][:, None]
-                          * np64(inp["dout"][torch.from_numpy(toks_e).to(DEV)]))
-    w13q, w2q = expert(e)
-    h, _, dab, _ = chain(x_rows, dy_rows, w13q, w2q)
-    seg = np.array([0, hi - lo])
+    def weight(w13, w2):
+        if mx:  # blocks along K for the forward, along N for the data gradient
+            out = []
+            for w in (w13, w2):
+                qf, sf, qd, sd = fp8.quantize_mx_weight(fp8.to_bf16(w))
+                out.append((fp8.dequantize_mx_rows(qf, sf).T, fp8.dequantize_mx_rows(qd, sd)))
+            return out
+        out = []
+        for w in (w13, w2):
+            d = fp8.dequantize_blocks(*fp8.quantize_blocks(fp8.to_bf16(w)))
+            out.append((d, d))  # the same 128 x 128 blocks serve both GEMMs
+        return out
 
     def tiles(a):
-        q, s, _ = fp8.quantize_token_tiles(fp8.to_bf16(a), seg)
+        a = fp8.to_bf16(a)
+        seg = np.array([0, a.shape[0]])
+        if mx:
+            q, s, _ = fp8.quantize_mx_token_tiles(a, seg)
+            return fp8.dequantize_mx_token_tiles(q, s)
+        q, s, _ = fp8.quantize_token_tiles(a, seg)
         return fp8.dequantize_token_tiles(q, s)
 
+    def chain(x_rows, dy_rows, w):
+        """One expert's forward output and data gradient with every GEMM input
+        quantized (the oracle's layer chain, rows of one expert)."""
+        (w13f, w13d), (w2f, w2d) = w
+        ab = rows(x_rows) @ w13f
+        y = rows(oracle.swiglu(ab)) @ w2f
+        dab = oracle.swiglu_bwd(rows(fp8.to_bf16(dy_rows)) @ w2d.T, ab)
+        return y, rows(dab) @ w13d.T
+
+    return rows, weight, tiles, chain
+
+
+def _rows_parallel(rows_fn, a):
+    """rows_fn over row blocks of a on host threads (rows are independent)."""
+    parts = np.array_split(a, POOL)
+    with cf.ThreadPoolExecutor(POOL) as ex:
+        return np.concatenate(list(ex.map(rows_fn, parts)), axis=0)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["deepseek_v3_fp8", "deepseek_v3_mxfp8"])
+def test_fullsize_lowp_layer(gpu, name):
+    """The DeepSeek-V3 layer at T = 32768 with blockwise-fp8 or MXFP8 expert
+    GEMMs, in the launch configuration bench.py times.  Routing in full and
+    bit-exact.  Tokens: 32, including the first
+    token of the largest, median and smallest non-empty expert and the last
+    token of the largest, chosen to share experts so that few experts'
+    weights need quantizing on the host; their out, dx and d_logits through
+    the oracle's quantize-at-every-GEMM-input chain (1 x 128 tiles or 1 x 32
+    MX blocks are row-local, so one token's chain is exact).  Weight
+    gradients of the LARGEST expert (about 10.7K rows, 84 token tiles) on 64
+    hidden x 64 ffn indices: a token tile is one column of one 128- (MX: 32-)
+    token block, so those columns quantize exactly as in the whole
+    gradient.  Within the fp8 bound."""
+    from oracle import fp8
+
+    cfg = inputs.CONFIGS[name]
+    mx = cfg.gemm == "mxfp8"
+    print(f"full-size {cfg.gemm} layer", flush=True)
+    layer, inp = _run(cfg)
+    z, r = _routing(layer, inp, cfg)
+    tol = TOL[cfg.gemm]
+    rows, weight, tiles, chain = _lowp_ops(mx)
+    big, med, small, _ = _expert_sizes(r)
+    must = [int(r["src_token"][r["offsets"][e]]) for e in (big, med, small)]
+    must.append(int(r["src_token"][r["offsets"][big + 1] - 1]))
+    toks = _greedy_tokens(r, 32, seed=1, must=must)
+    print(f"  tokens {toks} over {len(np.unique(r['topk_idx'][toks]))} experts", flush=True)
+    shared = weight(np64(inp["ws13"]), np64(inp["ws2"]))
+    out, dx, dz = _token_reference(cfg, inp, z, r, toks, weight, chain, shared)
+    idx = torch.tensor(toks, device=DEV)
+    assert_close("out (sampled tokens)", layer.out[idx], out, tol)
+    assert_close("dx (sampled tokens)", layer.dx[idx], dx, tol)
+    assert_close("d_logits (sampled tokens)", layer.d_logits[idx], dz, tol)
+
+    # weight gradients of the largest expert on 64 x 64 indices
+    e = big
+    lo, hi = int(r["offsets"][e]), int(r["offsets"][e + 1])
+    toks_e = r["src_token"][lo:hi].astype(np.int64)
+    slots = np.array([int(np.nonzero(r["topk_idx"][t] == e)[0][0]) for t in toks_e])
+    rows_e = torch.from_numpy(toks_e).to(DEV)
+    x_rows = np64(inp["x"][rows_e])
+    dy_rows = fp8.to_bf16(r["topk_w"][toks_e, slots][:, None] * np64(inp["dout"][rows_e]))
     rng = np.random.default_rng(2)
-    cols = np.unique(np.concatenate([[0, cfg.f - 1], rng.choice(cfg.f, 14, replace=False)]))
-    xt, dabt, ht, dyt = tiles(x_rows), tiles(dab), tiles(h), tiles(dy_rows)
-    c = torch.from_numpy(cols).to(DEV)
+    cols = np.unique(np.concatenate([[0, cfg.f - 1], rng.choice(cfg.f, 62, replace=False)]))
+    hid = np.unique(np.concatenate([[0, cfg.d - 1], rng.choice(cfg.d, 62, replace=False)]))
+    (w13f, _), (w2f, w2d) = weight(np64(inp["w13"][e]), np64(inp["w2"][e]))
     print(f"  expert {e}: {hi - lo} rows", flush=True)
-    assert_close(f"dW1[{e}] cols", layer.dw13[e][:, c], xt.T @ dabt[:, cols], tol)
-    assert_close(f"dW3[{e}] cols", layer.dw13[e][:, cfg.f + c], xt.T @ dabt[:, cfg.f + cols], tol)
-    assert_close(f"dW2[{e}] rows", layer.dw2[e][c, :], ht[:, cols].T @ dyt, tol)
+    xq = _rows_parallel(rows, x_rows)                 # the forward's row-quantized X
+    ab = xq @ w13f[:, np.concatenate([cols, cfg.f + cols])]  # [A | B] at the sampled columns
+    dyq = _rows_parallel(rows, dy_rows)               # the data gradient's row-quantized dY
+    dh_c = dyq @ w2d[cols, :].T
+    h_c = oracle.swiglu(ab)
+    dab_c = oracle.swiglu_bwd(dh_c, ab)
+    xt, dabt = tiles(x_rows[:, hid]), tiles(dab_c)
+    ht, dyt = tiles(h_c), tiles(dy_rows[:, hid])
+    c, hh = torch.from_numpy(cols).to(DEV), torch.from_numpy(hid).to(DEV)
+    assert_close(f"dW1[{e}] ({len(hid)} x {len(cols)})", layer.dw13[e][hh][:, c],
+                 xt.T @ dabt[:, :len(cols)], tol)
+    assert_close(f"dW3[{e}] ({len(hid)} x {len(cols)})", layer.dw13[e][hh][:, cfg.f + c],
+                 xt.T @ dabt[:, len(cols):], tol)
+    assert_close(f"dW2[{e}] ({len(cols)} x {len(hid)})", layer.dw2[e][c][:, hh], ht.T @ dyt, tol)
     del layer, inp
     torch.cuda.empty_cache()

@@ -1,8 +1,9 @@
 """Whole-layer parity, forward and backward, of the HIP path (MoELayer, all
 C-ABI calls in sequence) against the oracle's per-token loop on the same
-seeded inputs.  Inputs are drawn so that no token's k-th and (k+1)-th keys
-are closer than the fp32 router's rounding could flip; routing is then
-compared bit-exactly and every output and gradient by max|err|/max|ref|."""
+seeded inputs.  The oracle's own fp32 logits are compared with the GPU's
+(1e-5 of max|ref|); the oracle then routes from the GPU's logits tensor, so
+routing is compared bit-exactly with no re-drawn inputs, and every output
+and gradient by max|err|/max|ref|."""
 import dataclasses
 
 import numpy as np
@@ -12,7 +13,7 @@ import torch
 import oracle
 from routing_grouped_gemm_router_amd import inputs
 from routing_grouped_gemm_router_amd.layer import MoELayer
-from gpu_util import TOL, assert_close, layer_inputs_without_near_ties, np64
+from gpu_util import TOL, assert_close, np64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -26,8 +27,7 @@ SMALL_BF16_SOFTMAX = inputs.LayerConfig("small_bf16_zipf", T=513, d=128, E=16, k
 def _run(cfg, seed, recompute_act=False, gate_in_ffn=False):
     print(f"layer {cfg.name} seed={seed} recompute={recompute_act} gated={gate_in_ffn}",
           flush=True)
-    inp = (inputs.layer_inputs(cfg, seed) if cfg.routing == "balanced"
-           else layer_inputs_without_near_ties(cfg, seed))
+    inp = inputs.layer_inputs(cfg, seed)
     w = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
     layer = MoELayer(cfg, w, DEV, recompute_act=recompute_act, gate_in_ffn=gate_in_ffn)
     layer.forward(w["x"])
@@ -36,10 +36,11 @@ def _run(cfg, seed, recompute_act=False, gate_in_ffn=False):
     shared = (np64(inp["ws13"]), np64(inp["ws2"])) if cfg.fs else None
     bias = None if inp["logit_bias"] is None else inp["logit_bias"].numpy()
     given = inp["topk_idx_in"].numpy() if cfg.routing == "balanced" else None
+    z_own = oracle.router_logits(np64(inp["x"]), inp["w_r"].numpy(), bias)
+    z = layer.logits.cpu().numpy()  # the oracle routes from the GPU's fp32 logits
     if cfg.expert_bias_std > 0:
         # the experts chosen on the biased keys; the oracle layer then takes
         # the routing weights from the unbiased scores, as the route does
-        z = oracle.router_logits(np64(inp["x"]), inp["w_r"].numpy(), bias)
         given = oracle.route_expert_bias(z, inp["expert_bias"].numpy(), cfg.k,
                                          cfg.renorm)["topk_idx"]
     fwd = oracle.layer_forward_gated if gate_in_ffn else oracle.layer_forward
@@ -47,8 +48,9 @@ def _run(cfg, seed, recompute_act=False, gate_in_ffn=False):
     cap = (oracle.capacity_of(cfg.capacity_factor, cfg.T, cfg.k, cfg.E)
            if cfg.capacity_factor > 0 else None)
     c = fwd(np64(inp["x"]), inp["w_r"].numpy(), np64(inp["w13"]), np64(inp["w2"]), cfg.k,
-            cfg.score, cfg.renorm, logit_bias=bias, shared=shared, given_experts=given,
+            cfg.score, cfg.renorm, logit_bias=bias, shared=shared, z=z, given_experts=given,
             capacity=cap)
+    c["z_own"] = z_own
     g = bwd(c, np64(inp["dout"]))
     if cfg.pad_to_max:  # the same kept pairs, in the static padded layout
         routed = (oracle.route(c["z"], cfg.k, cfg.score, cfg.renorm) if given is None
@@ -70,7 +72,7 @@ def _check(cfg, layer, c, g):
     np.testing.assert_array_equal(layer.dst_row.cpu().numpy(), r["dst_row"])
     n_rows = int(r["offsets"][-1])
     np.testing.assert_array_equal(layer.src_token.cpu().numpy()[:n_rows], r["src_token"])
-    assert_close("logits", layer.logits, c["z"], TOL["f32"])
+    assert_close("logits (oracle's own)", layer.logits, c["z_own"], TOL["f32"])
     assert_close("out", layer.out, c["out"], tol)
     grads = layer.grads()
     for name in ["dx", "d_logits", "dW_r", "dW13", "dW2"] + (["dWs13", "dWs2"] if cfg.fs else []):

@@ -18,7 +18,7 @@ import oracle
 from oracle import fp8
 from routing_grouped_gemm_router_amd import abi, inputs
 from routing_grouped_gemm_router_amd.layer import MoELayer
-from gpu_util import TOL, assert_close, layer_inputs_without_near_ties, np64, rel_err
+from gpu_util import TOL, assert_close, np64, rel_err
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -210,7 +210,7 @@ SMALL_MX = inputs.LayerConfig("small_mxfp8_shared", T=1600, d=256, E=8, k=2, f=2
 ], ids=lambda c: c.name if hasattr(c, "name") else f"recompute={c}")
 def test_layer_mxfp8(gpu, cfg, recompute):
     print(f"mxfp8 layer {cfg.name} recompute={recompute}", flush=True)
-    inp = layer_inputs_without_near_ties(cfg, 0)
+    inp = inputs.layer_inputs(cfg, 0)
     w = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
     layer = MoELayer(cfg, w, DEV, recompute_act=recompute)
     assert layer.x_perm is None
@@ -221,7 +221,9 @@ def test_layer_mxfp8(gpu, cfg, recompute):
     bias = None if inp["logit_bias"] is None else inp["logit_bias"].numpy()
     ref = fp8.layer_fp8(np64(inp["x"]), inp["w_r"].numpy(), np64(inp["w13"]), np64(inp["w2"]),
                         np64(inp["dout"]), cfg.k, cfg.score, cfg.renorm, logit_bias=bias,
-                        shared=shared, recipe="mx")
+                        shared=shared, recipe="mx", z=layer.logits.cpu().numpy())
+    assert_close("logits (oracle's own)", layer.logits,
+                 oracle.router_logits(np64(inp["x"]), inp["w_r"].numpy(), bias), TOL["f32"])
     r = ref["route"]
     np.testing.assert_array_equal(layer.dst_row.cpu().numpy(), r["dst_row"])
     np.testing.assert_array_equal(layer.offsets.cpu().numpy(), r["offsets"])

@@ -273,3 +273,48 @@ def test_mx_layer_chain_close_to_exact_layer():
     assert 1e-3 < rel(e["out"], c["out"]) < 0.2
     for name in ["dx", "dW13", "dW2", "dWs13", "dWs2"]:
         assert 1e-3 < rel(e[name], g[name]) < 0.2, name
+
+
+def _brute_tile(v):
+    """One tile by the definition, scalar by scalar: block_scale of its amax,
+    then encode of each fp32 product."""
+    scale, inv = fp8.block_scale(np.max(np.abs(v)))
+    codes = np.array([fp8.encode(np.float32(e * inv)) for e in v.ravel()], np.uint8).reshape(v.shape)
+    return codes, scale
+
+
+def test_quantizers_equal_tile_by_tile_definition():
+    """The whole-array quantizers give, tile for tile, the codes and scales of
+    the definition applied to each tile alone (scalar fp32 arithmetic),
+    including zero tiles, saturating values and subnormal codes."""
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal((3, 256)) * np.array([[1e-3], [1.0], [300.0]])).astype(np.float32)
+    x[0, 128:] = 0.0
+    x[2, 5] = 3.0e38
+    q, s = fp8.quantize_rows(x)
+    for i in range(3):
+        for b in range(2):
+            c, sc = _brute_tile(x[i, b * 128:(b + 1) * 128])
+            np.testing.assert_array_equal(q[i, b * 128:(b + 1) * 128], c)
+            assert s[i, b] == sc
+    w = (rng.standard_normal((256, 128)) * rng.uniform(1e-4, 10, (256, 1))).astype(np.float32)
+    w[:128] = 0.0
+    qw, sw = fp8.quantize_blocks(w)
+    for i in range(2):
+        c, sc = _brute_tile(w[i * 128:(i + 1) * 128])
+        np.testing.assert_array_equal(qw[i * 128:(i + 1) * 128], c)
+        assert sw[i, 0] == sc
+    off = np.array([0, 3, 3, 140])
+    xt = (rng.standard_normal((140, 2)) * 7).astype(np.float32)
+    qt, st, poff = fp8.quantize_token_tiles(xt, off)
+    assert list(poff) == [0, 128, 128, 384]
+    for g, (lo, hi) in enumerate([(0, 3), (3, 140)]):
+        plo = [0, 128][g]
+        for b in range((hi - lo + 127) // 128):
+            for col in range(2):
+                v = np.zeros(128, np.float32)
+                r1 = min(hi, lo + 128 * (b + 1))
+                v[:r1 - lo - 128 * b] = xt[lo + 128 * b:r1, col]
+                c, sc = _brute_tile(v)
+                np.testing.assert_array_equal(qt[plo + 128 * b:plo + 128 * b + 128, col], c)
+                assert st[plo // 128 + b, col] == sc
