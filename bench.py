@@ -52,8 +52,8 @@ def parse():
                     help="apply the routing weight before W2 (unweighted combine, no Y in the "
                          "backward)")
     ap.add_argument("--cold-reps", type=int, default=5,
-                    help="repetitions of each permute / combine call timed after a 512 MiB "
-                         "write that evicts its operands from the caches (0: skip)")
+                    help="repetitions of each permute / combine call timed after a flush that "
+                         "evicts its operands from the caches (0: skip)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the CPU oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -201,21 +201,27 @@ def traffic_for(workload, kernel):
     return rec["bytes_per_launch"]
 
 
-def cold_data_movement(layer, dout, work, reps):
-    """Each permute / combine call of the layer timed on its own, after a
-    512 MiB write (twice the memory-side cache) that evicts its operands, so
-    that its reads come from HBM; the write sits outside the call's events.
-    Returns name -> {ms (median), GB/s, frac of the HBM peak}."""
+def cold_data_movement(layer, dout, work, reps, clean=True):
+    """Each permute / combine call of the layer timed on its own after a
+    flush that evicts its operands from the caches, so that its reads come
+    from HBM; the flush sits outside the call's events.  The flush writes
+    512 MiB (twice the memory-side cache); with ``clean`` it then reads
+    another 512 MiB, so the caches hold no dirty lines whose write-back the
+    timed call would pay for.  Returns name -> {ms (median), GB/s, frac of
+    the HBM peak}, plus their total."""
     import statistics
 
     import torch
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    fa = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    fb = torch.ones(512 << 20, dtype=torch.uint8, device="cuda") if clean else None
     calls = layer.data_movement_calls(dout)
     res = {}
     for name, call in calls.items():
         times = []
         for _ in range(reps):
-            flush.fill_(1)
+            fa.fill_(1)
+            if clean:
+                fb.sum(dtype=torch.int64)
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record()
@@ -227,7 +233,11 @@ def cold_data_movement(layer, dout, work, reps):
         by = work[name][1]
         res[name] = {"ms": round(ms, 4), "GB/s": round(by / ms / 1e6, 1),
                      "frac_hbm_peak": round(by / ms / 1e6 / PEAK_HBM_GBS, 4)}
-    del flush
+    c_ms = sum(v["ms"] for v in res.values())
+    c_by = sum(work[n][1] for n in res)
+    res["total"] = {"ms": round(c_ms, 4), "GB/s": round(c_by / c_ms / 1e6, 1),
+                    "frac_hbm_peak": round(c_by / c_ms / 1e6 / PEAK_HBM_GBS, 4)}
+    del fa, fb
     return res
 
 
@@ -398,13 +408,10 @@ def main():
     router = [n for n in ("router_logits", "router_logits_bwd") if n in kernels]
     router_ms = sum(kernels[n]["ms"] for n in router)
     router_fl = sum(work[n][0] for n in router)
-    cold = None
+    cold = cold_dirty = None
     if args.cold_reps > 0:
-        cold = cold_data_movement(layer, dout, work, args.cold_reps)
-        c_ms = sum(v["ms"] for v in cold.values())
-        c_by = sum(work[n][1] for n in cold)
-        cold["total"] = {"ms": round(c_ms, 4), "GB/s": round(c_by / c_ms / 1e6, 1),
-                         "frac_hbm_peak": round(c_by / c_ms / 1e6 / PEAK_HBM_GBS, 4)}
+        cold = cold_data_movement(layer, dout, work, args.cold_reps, clean=True)
+        cold_dirty = cold_data_movement(layer, dout, work, args.cold_reps, clean=False)["total"]
 
     line = {
         "metric": METRIC,
@@ -437,7 +444,7 @@ def main():
                             "traffic": pc_traffic,
                             "traffic_GB/s": (round(pc_traffic / pc_ms / 1e6, 1)
                                              if pc_traffic is not None else None),
-                            "cold": cold},
+                            "cold": cold, "cold_after_dirty_flush": cold_dirty},
         "router": {"TFLOP/s": round(router_fl / router_ms / 1e9, 1) if router_ms else None,
                    "frac_peak": (round(router_fl / router_ms / 1e9 / PEAK_F32_TFLOPS, 4)
                                  if router_ms else None),

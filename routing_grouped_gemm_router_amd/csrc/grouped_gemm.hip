@@ -594,9 +594,11 @@ __device__ __forceinline__ void compute_stage_bf16(f32x16_t (&acc)[2][2], const 
 }
 
 // fp8: one 128-wide scale block per stage, as two MFMAs of 64 k per output
-// block; each partial is promoted as acc += partial * scale_A(row) *
-// scale_B(column) (the scale is constant over the block, so promoting the two
-// halves separately is the same sum and keeps half the fragments live)
+// block chained into one fp32 partial, which is then promoted once as
+// acc += partial * scale_A(row) * scale_B(column) (the scales are constant
+// over the block).  One promotion per 128 k halves the vector-ALU work per
+// MFMA against promoting each 64-k half, and the first MFMA takes a zero
+// accumulator operand, so the partial needs no clearing.
 __device__ __forceinline__ void compute_stage_fp8(f32x16_t (&acc)[2][2], const LDS_AS char* opA,
                                                   const LDS_AS char* opB, const LDS_AS float* sA,
                                                   int wm, int wn, int wnl, int lane) {
@@ -605,32 +607,34 @@ __device__ __forceinline__ void compute_stage_fp8(f32x16_t (&acc)[2][2], const L
   float sa[2];
 #pragma unroll
   for (int ii = 0; ii < 2; ++ii) sa[ii] = sA[wm * 64 + ii * 32 + (lane & 31)];
-#pragma unroll 1
+  i32x8_t a[2][2], b[2][2];  // [64-k half][block]
+#pragma unroll
   for (int s = 0; s < 2; ++s) {
-    i32x8_t a[2], b[2];
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii) a[ii] = frag_kc8(opA, wm * 64 + ii * 32 + (lane & 31), 4 * s + 2 * h);
+    for (int ii = 0; ii < 2; ++ii)
+      a[s][ii] = frag_kc8(opA, wm * 64 + ii * 32 + (lane & 31), 4 * s + 2 * h);
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) b[jj] = frag_kc8(opB, wnl * 64 + jj * 32 + (lane & 31), 4 * s + 2 * h);
+    for (int jj = 0; jj < 2; ++jj)
+      b[s][jj] = frag_kc8(opB, wnl * 64 + jj * 32 + (lane & 31), 4 * s + 2 * h);
+  }
+  const f32x16_t zero = {};
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      f32x4 sb[4];
+  for (int jj = 0; jj < 2; ++jj) {
+    f32x4 sb[4];
 #pragma unroll
-      for (int vg = 0; vg < 4; ++vg) sb[vg] = *(const LDS_AS f32x4*)(sB + wn * 64 + jj * 32 + vg * 8 + h * 4);
+    for (int vg = 0; vg < 4; ++vg) sb[vg] = *(const LDS_AS f32x4*)(sB + wn * 64 + jj * 32 + vg * 8 + h * 4);
 #pragma unroll
-      for (int ii = 0; ii < 2; ++ii) {
-        f32x16_t part;
+    for (int ii = 0; ii < 2; ++ii) {
+      // format 0 = E4M3 for both operands; E8M0 scale 127 = 1.0
+      f32x16_t part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[0][jj], a[0][ii], zero, 0, 0,
+                                                                      0, 127, 0, 127);
+      part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[1][jj], a[1][ii], part, 0, 0, 0, 127,
+                                                             0, 127);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) part[v] = 0.f;
-        // format 0 = E4M3 for both operands; E8M0 scale 127 = 1.0
-        part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[jj], a[ii], part, 0, 0, 0, 127, 0,
-                                                               127);
+      for (int vg = 0; vg < 4; ++vg)
 #pragma unroll
-        for (int vg = 0; vg < 4; ++vg)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc[ii][jj][vg * 4 + e] += part[vg * 4 + e] * (sa[ii] * sb[vg][e]);
-      }
+        for (int e = 0; e < 4; ++e)
+          acc[ii][jj][vg * 4 + e] += part[vg * 4 + e] * (sa[ii] * sb[vg][e]);
     }
   }
 }
