@@ -94,6 +94,25 @@ int moe_router_logits_bwd(const void* x, int x_dtype, const float* w_r, const fl
                           int64_t T, int64_t d, int32_t E, float* d_w_r, float* dx_router,
                           void* stream);
 
+/* The same two products as moe_router_logits_bwd when every row of d_logits
+ * is zero outside the token's k chosen experts -- what moe_route_topk_bwd
+ * gives for renormalised routing or sigmoid scores, and not for softmax
+ * without renormalisation or with the auxiliary loss added (use
+ * moe_router_logits_bwd for those).  Reads d_logits only at the chosen
+ * entries: T k d multiply-adds per product instead of T E d, fp32 on the
+ * vector ALUs, each output summed in a fixed order:
+ *   dx_router[t] = sum_j d_logits[t, e_j] w_r[:, e_j]   (slots in order)
+ *   d_w_r[:, e]  = sum over expert e's rows r (ascending) of
+ *                  x[src_token[r]] d_logits[src_token[r], e]
+ * topk_idx [T, k]; offsets [E+1] and src_token [T*k]: the DROPLESS dispatch
+ * map of the route (before any capacity dropping, whose dropped pairs still
+ * carry gradient to their keys).  Entries outside range are skipped.
+ * Limits: E <= 256, k <= 64, d % 8 == 0, x 16-byte aligned. */
+int moe_router_logits_bwd_topk(const void* x, int x_dtype, const float* w_r, const float* d_logits,
+                               const int32_t* topk_idx, const int64_t* offsets,
+                               const int32_t* src_token, int64_t T, int64_t d, int32_t E,
+                               int32_t k, float* d_w_r, float* dx_router, void* stream);
+
 /* Non-finite logits are a caller error (the routing of such a token is
  * unspecified).  This check flags them: *status (device int32) is set to 1
  * when any of x[0 .. n) is a NaN or an infinity, and is never cleared by the
@@ -140,6 +159,24 @@ int moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int sco
 int moe_route_topk_noalloc(const float* logits, int64_t T, int32_t E, int32_t k, int score,
                            int renorm, int32_t* topk_idx, float* topk_w, int32_t* counts,
                            int64_t* offsets, int32_t* dst_row, int32_t* src_token, void* stream);
+
+/* Debug check of a dispatch map (moe_route_topk, _replay, _expert_bias,
+ * moe_apply_capacity, moe_pad_to_max): each violated invariant ORs one bit
+ * into *status (device int32, never cleared by the library):
+ *   1  offsets[0] != 0, decreasing offsets, a segment shorter than its
+ *      count, or offsets[E] > n_rows
+ *   2  a pair's row outside its expert's filled segment
+ *      [offsets[e], offsets[e] + counts[e]) (row -1, a dropped pair, is allowed)
+ *   4  src_token[row] is not the pair's token
+ *   8  a segment's tokens not in ascending order
+ *   16 a pair's expert outside [0, E)
+ * n_rows: rows of the permuted buffers (T*k dropless, E*capacity padded).
+ * Reads only, every index range-checked first, so a corrupt map is safe to
+ * check.  The layer runs it after each route when the environment variable
+ * MOE_DEBUG is set. */
+int moe_check_dispatch(const int32_t* topk_idx, const int32_t* counts, const int64_t* offsets,
+                       const int32_t* dst_row, const int32_t* src_token, int64_t T, int32_t E,
+                       int32_t k, int64_t n_rows, int32_t* status, void* stream);
 
 /* Top-k with a selection-only expert bias on sigmoid scores (the
  * auxiliary-loss-free biasing of section 7, Load Balancing): the key of
@@ -362,7 +399,7 @@ int moe_quant_fp8_weights(const void* w, int32_t G, int64_t K, int64_t N, uint8_
 
 /* Host helper: rows a padded layout of M rows in G groups can need,
  * M + G * (align - 1) rounded up to align (the row length `ldm` of the
- * token-tile operands). */
+ * token-tile operands); 0 for M < 0, G < 1, align < 1 or M > 2^60. */
 int64_t moe_padded_rows_bound(int64_t M, int32_t G, int32_t align);
 
 /* padded [G+1] (device): padded[0] = 0, padded[g+1] = padded[g] +

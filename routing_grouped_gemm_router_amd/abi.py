@@ -74,6 +74,9 @@ SIGNATURES = {
                                           _p, _p, _sz, _p]),
     "moe_expert_bias_update": (_int, [_p, _i32, _f32, _p, _p]),
     "moe_check_finite": (_int, [_p, _i64, _p, _p]),
+    "moe_router_logits_bwd_topk": (_int, [_p, _int, _p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _p,
+                                          _p, _p]),
+    "moe_check_dispatch": (_int, [_p, _p, _p, _p, _p, _i64, _i32, _i32, _i64, _p, _p]),
     "moe_route_topk_noalloc": (_int, [_p, _i64, _i32, _i32, _int, _int, _p, _p, _p, _p, _p, _p,
                                       _p]),
     "moe_pad_to_max": (_int, [_p, _p, _p, _p, _p, _i64, _i32, _i32, _i64, _p, _p, _p, _p, _p]),
@@ -174,8 +177,22 @@ def moe_router_logits_bwd(x, w_r, d_logits, d_w_r, dx_router, stream=None):
           w_r.shape[1], _ptr(d_w_r), _ptr(dx_router), _stream(stream))
 
 
+def moe_router_logits_bwd_topk(x, w_r, d_logits, topk_idx, offsets, src_token, d_w_r, dx_router,
+                               stream=None):
+    T, d = x.shape
+    _call("moe_router_logits_bwd_topk", _ptr(x), dtype_code(x), _ptr(w_r), _ptr(d_logits),
+          _ptr(topk_idx), _ptr(offsets), _ptr(src_token), T, d, w_r.shape[1], topk_idx.shape[1],
+          _ptr(d_w_r), _ptr(dx_router), _stream(stream))
+
+
 def moe_check_finite(x, status, stream=None):
     _call("moe_check_finite", _ptr(x), x.numel(), _ptr(status), _stream(stream))
+
+
+def moe_check_dispatch(topk_idx, counts, offsets, dst_row, src_token, n_rows, status, stream=None):
+    T, k = topk_idx.shape
+    _call("moe_check_dispatch", _ptr(topk_idx), _ptr(counts), _ptr(offsets), _ptr(dst_row),
+          _ptr(src_token), T, counts.numel(), k, int(n_rows), _ptr(status), _stream(stream))
 
 
 def moe_route_topk_workspace_bytes(T, E, k):

@@ -571,6 +571,185 @@ hipError_t launch_router_bwd(const void* x, int x_dtype, const float* w_r, const
   return err;
 }
 
+// ---- router backward when d_logits lives on each token's chosen experts ------
+// With renormalised or sigmoid routing (and no auxiliary loss) the route's
+// backward leaves d_logits zero outside each token's k chosen experts, so the
+// two products need only those entries: T k d multiply-adds each instead of
+// T E d, still fp32 on the vector ALUs and summed in a fixed order.
+
+// dx_router[t, i] = sum_j d_logits[t, e_j] * W_r[i, e_j], slots in order.
+// Block: 64 columns i0 .. i0+63 (lane = column) x a chunk of tokens, 16
+// waves, wave w taking every 16th token.  W_r's 64 rows are staged in LDS as
+// [64][E + 1] so that lanes reading one expert's column hit distinct banks.
+// A wave fetches the experts and key gradients of 64 / k tokens at once (lane
+// = token, slot) and broadcasts them with shuffles, the next batch already in
+// flight, so the dependent index -> gradient loads are not paid per slot;
+// (token, slot) is uniform over the wave, so the broadcasts are lane reads
+// into scalar registers and only the W_r reads use the LDS.
+constexpr int kDxCols = 64, kDxTokens = 1024, kDxWaves = 16;
+__global__ __launch_bounds__(1024) void router_dx_topk_kernel(const float* __restrict__ w_r,
+                                                              const float* __restrict__ dz,
+                                                              const int32_t* __restrict__ topk_idx,
+                                                              int64_t T, int64_t d, int E, int k,
+                                                              float* __restrict__ dx) {
+  __shared__ float wl[kDxCols * 257];  // [kDxCols][E + 1], E <= 256
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * kDxCols;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.y) * kDxTokens;
+  const int cols = static_cast<int>(min<int64_t>(kDxCols, d - i0));
+  for (int q = threadIdx.x; q < cols * E; q += 64 * kDxWaves) {
+    const int r = q / E, e = q - r * E;
+    wl[r * (E + 1) + e] = w_r[(i0 + r) * E + e];
+  }
+  __syncthreads();
+  const int64_t t1 = min<int64_t>(T, t0 + kDxTokens);
+  const int nb = 64 / k;                      // tokens per batch
+  const int u = lane / k, j = lane - u * k;   // this lane's (token, slot) of a batch
+  auto fetch = [&](int64_t tb, int& e, float& g) {
+    const int64_t t = tb + static_cast<int64_t>(u) * kDxWaves;
+    e = -1;
+    g = 0.f;
+    if (u < nb && t < t1) {
+      const int ee = topk_idx[t * k + j];
+      if (ee >= 0 && ee < E) {
+        e = ee;
+        g = dz[t * E + ee];
+      }
+    }
+  };
+  int e_cur, e_nxt;
+  float g_cur, g_nxt;
+  int64_t tb = t0 + wave;
+  if (tb < t1) fetch(tb, e_cur, g_cur);
+  for (; tb < t1; tb += static_cast<int64_t>(nb) * kDxWaves) {
+    const int64_t tn = tb + static_cast<int64_t>(nb) * kDxWaves;
+    if (tn < t1) fetch(tn, e_nxt, g_nxt);
+    for (int uu = 0; uu < nb; ++uu) {
+      const int64_t t = tb + static_cast<int64_t>(uu) * kDxWaves;
+      if (t >= t1) break;
+      float acc = 0.f;
+      for (int jj = 0; jj < k; ++jj) {
+        const int e = __builtin_amdgcn_readlane(e_cur, uu * k + jj);
+        const float g = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g_cur), uu * k + jj));
+        if (e >= 0 && lane < cols) acc = fmaf(g, wl[lane * (E + 1) + e], acc);
+      }
+      if (lane < cols) dx[t * d + i0 + lane] = acc;
+    }
+    e_cur = e_nxt;
+    g_cur = g_nxt;
+  }
+}
+
+// dW_r[i, e] = sum over expert e's rows r (ascending) of x[src_token[r], i] *
+// d_logits[src_token[r], e].  Block: expert e x 64 VN columns (VN per lane,
+// one 16-byte load), 16 waves, wave w taking every 16th row of the segment.
+// A wave gathers the tokens and key gradients of its next 64 rows at once
+// (lane = row), then keeps 8 rows' x loads in flight; the 16 waves' sums are
+// added through LDS in wave order.
+constexpr int kDwWaves = 16;
+template <int VN>
+__global__ __launch_bounds__(1024) void router_dw_topk_kernel(const void* __restrict__ x,
+                                                              const float* __restrict__ dz,
+                                                              const int64_t* __restrict__ offsets,
+                                                              const int32_t* __restrict__ src_token,
+                                                              int64_t T, int64_t d, int E,
+                                                              int64_t n_rows,
+                                                              float* __restrict__ dw) {
+  __shared__ float part[kDwWaves - 1][64 * VN];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e = blockIdx.y;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 64 * VN + lane * VN;
+  const bool col_ok = c0 + VN <= d;
+  int64_t lo = offsets[e], hi = offsets[e + 1];
+  lo = lo < 0 ? 0 : (lo > n_rows ? n_rows : lo);
+  hi = hi < lo ? lo : (hi > n_rows ? n_rows : hi);
+  float acc[VN];
+#pragma unroll
+  for (int v = 0; v < VN; ++v) acc[v] = 0.f;
+  constexpr int UNR = 8;
+  for (int64_t rb = lo + wave; rb < hi; rb += 64 * kDwWaves) {
+    // this wave's next 64 rows: rb, rb + 16, ...; lane l gathers row rb + 16 l
+    const int64_t rl = rb + static_cast<int64_t>(lane) * kDwWaves;
+    int tok = -1;
+    float gl = 0.f;
+    if (rl < hi) {
+      const int32_t t = src_token[rl];
+      if (t >= 0 && t < T) {
+        tok = t;
+        gl = dz[static_cast<int64_t>(t) * E + e];
+      }
+    }
+    const int cnt = static_cast<int>(min<int64_t>(64, (hi - rb + kDwWaves - 1) / kDwWaves));
+    for (int u0 = 0; u0 < cnt; u0 += UNR) {
+      uint4 raw[UNR];
+      float g[UNR];
+#pragma unroll
+      for (int uu = 0; uu < UNR; ++uu) {
+        const int t = __builtin_amdgcn_readlane(tok, (u0 + uu) & 63);
+        g[uu] = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gl), (u0 + uu) & 63));
+        raw[uu] = make_uint4(0u, 0u, 0u, 0u);
+        if (u0 + uu < cnt && t >= 0 && col_ok)
+          raw[uu] = VN == 8
+                        ? *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(x) +
+                                                          static_cast<int64_t>(t) * d + c0)
+                        : *reinterpret_cast<const uint4*>(static_cast<const float*>(x) +
+                                                          static_cast<int64_t>(t) * d + c0);
+        if (!(u0 + uu < cnt && t >= 0)) g[uu] = 0.f;
+      }
+#pragma unroll
+      for (int uu = 0; uu < UNR; ++uu) {
+        float v[8];
+        unpack_vec(raw[uu], VN == 8, v);
+#pragma unroll
+        for (int q = 0; q < VN; ++q) acc[q] = fmaf(v[q], g[uu], acc[q]);
+      }
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int q = 0; q < VN; ++q) part[wave - 1][lane * VN + q] = acc[q];
+  }
+  __syncthreads();
+  if (wave != 0 || !col_ok) return;
+  for (int w = 0; w < kDwWaves - 1; ++w)
+#pragma unroll
+    for (int q = 0; q < VN; ++q) acc[q] += part[w][lane * VN + q];
+#pragma unroll
+  for (int q = 0; q < VN; ++q) dw[(c0 + q) * E + e] = acc[q];
+}
+
+hipError_t launch_router_bwd_topk(const void* x, int x_dtype, const float* w_r, const float* dz,
+                                  const int32_t* topk_idx, const int64_t* offsets,
+                                  const int32_t* src_token, int64_t T, int64_t d, int E, int k,
+                                  float* dw_r, float* dx_r, hipStream_t s) {
+  if (dw_r) {
+    if (T == 0) {
+      hipError_t err = launch_fill_zero(dw_r, d * E, s);
+      if (err != hipSuccess) return err;
+    } else {
+      const int vn = x_dtype == 0 ? 4 : 8;
+      const dim3 g(static_cast<unsigned>((d + 64 * vn - 1) / (64 * vn)), static_cast<unsigned>(E));
+      if (x_dtype == 0)
+        router_dw_topk_kernel<4><<<g, 64 * kDwWaves, 0, s>>>(x, dz, offsets, src_token, T, d, E,
+                                                             T * k, dw_r);
+      else
+        router_dw_topk_kernel<8><<<g, 64 * kDwWaves, 0, s>>>(x, dz, offsets, src_token, T, d, E,
+                                                             T * k, dw_r);
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
+  }
+  if (dx_r && T > 0) {
+    const dim3 g(static_cast<unsigned>((d + kDxCols - 1) / kDxCols),
+                 static_cast<unsigned>((T + kDxTokens - 1) / kDxTokens));
+    router_dx_topk_kernel<<<g, 64 * kDxWaves, 0, s>>>(w_r, dz, topk_idx, T, d, E, k, dx_r);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_gg_f32_fwd(const float* A, const float* B, const int64_t* off, int G, int64_t M,
                              int64_t K, int64_t N, int epi, float* C, float* H, hipStream_t s) {
   if (M == 0) return hipSuccess;

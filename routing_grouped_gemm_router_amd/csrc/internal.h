@@ -31,6 +31,10 @@ hipError_t launch_zero_unmapped_rows(void* buf, int64_t row_bytes, const int32_t
 hipError_t launch_expert_bias_update(const int32_t* counts, int E, float rate, float* bias,
                                      hipStream_t stream);
 hipError_t launch_check_finite(const float* p, int64_t n, int32_t* status, hipStream_t stream);
+hipError_t launch_check_dispatch(const int32_t* topk_idx, const int32_t* counts,
+                                 const int64_t* offsets, const int32_t* dst_row,
+                                 const int32_t* src_token, int64_t T, int E, int k, int64_t n_rows,
+                                 int32_t* status, hipStream_t stream);
 hipError_t launch_route_replay(const float* logits, const int32_t* idx_in, int64_t T, int E, int k,
                                int score, int renorm, int32_t* topk_idx, float* topk_w,
                                int32_t* counts, int64_t* offsets, int32_t* dst_row,
@@ -70,6 +74,10 @@ hipError_t launch_router_fwd(const void* x, int x_dtype, const float* w_r, const
                              int64_t T, int64_t d, int E, float* logits, hipStream_t s);
 hipError_t launch_router_bwd(const void* x, int x_dtype, const float* w_r, const float* dz,
                              int64_t T, int64_t d, int E, float* dw_r, float* dx_r, hipStream_t s);
+hipError_t launch_router_bwd_topk(const void* x, int x_dtype, const float* w_r, const float* dz,
+                                  const int32_t* topk_idx, const int64_t* offsets,
+                                  const int32_t* src_token, int64_t T, int64_t d, int E, int k,
+                                  float* dw_r, float* dx_r, hipStream_t s);
 hipError_t launch_gg_f32_fwd(const float* A, const float* B, const int64_t* off, int G, int64_t M,
                              int64_t K, int64_t N, int epi, float* C, float* H, hipStream_t s);
 hipError_t launch_gg_f32_dgrad(const float* dC, const float* B, const int64_t* off, int G,

@@ -34,6 +34,12 @@ int hip_status(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// a * b < lim for non-negative a and b, without forming the product (which
+// could overflow for sizes a caller got wrong)
+bool prod_below(int64_t a, int64_t b, int64_t lim) {
+  return a >= 0 && b >= 0 && (b == 0 || a <= (lim - 1) / b);
+}
+
 bool valid_dtype(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
@@ -102,6 +108,35 @@ int moe_router_logits_bwd(const void* x, int x_dtype, const float* w_r, const fl
                     "moe_router_logits_bwd");
 }
 
+int moe_router_logits_bwd_topk(const void* x, int x_dtype, const float* w_r, const float* d_logits,
+                               const int32_t* topk_idx, const int64_t* offsets,
+                               const int32_t* src_token, int64_t T, int64_t d, int32_t E,
+                               int32_t k, float* d_w_r, float* dx_router, void* stream) {
+  const char* fn = "moe_router_logits_bwd_topk";
+  REQUIRE(valid_dtype(x_dtype), MOE_ERR_DTYPE, "%s: bad x dtype %d", fn, x_dtype);
+  REQUIRE(T >= 0 && d >= 1 && E >= 1 && k >= 1 && k <= E, MOE_ERR_SHAPE,
+          "%s: T=%lld d=%lld E=%d k=%d", fn, static_cast<long long>(T), static_cast<long long>(d), E,
+          k);
+  REQUIRE(E <= 256, MOE_ERR_UNSUPPORTED, "%s: E=%d above 256 (use moe_router_logits_bwd)", fn, E);
+  REQUIRE(k <= 64, MOE_ERR_UNSUPPORTED, "%s: k=%d above 64 (use moe_router_logits_bwd)", fn, k);
+  REQUIRE(prod_below(T, k, int64_t(1) << 31) && d < (int64_t(1) << 40), MOE_ERR_UNSUPPORTED,
+          "%s: T*k must be below 2^31", fn);
+  REQUIRE(d % 8 == 0, MOE_ERR_UNSUPPORTED, "%s: d=%lld must be a multiple of 8", fn,
+          static_cast<long long>(d));
+  if (!d_w_r && !dx_router) return ok();
+  REQUIRE(T == 0 || (d_logits && topk_idx), MOE_ERR_NULL, "%s: d_logits and topk_idx are required",
+          fn);
+  REQUIRE(!d_w_r || T == 0 || (x && offsets && src_token), MOE_ERR_NULL,
+          "%s: x, offsets and src_token are required for d_w_r", fn);
+  REQUIRE(!dx_router || T == 0 || w_r, MOE_ERR_NULL, "%s: w_r is required for dx_router", fn);
+  REQUIRE(!d_w_r || T == 0 || aligned16(x), MOE_ERR_UNSUPPORTED, "%s: x must be 16-byte aligned",
+          fn);
+  return hip_status(moe::launch_router_bwd_topk(x, x_dtype, w_r, d_logits, topk_idx, offsets,
+                                                src_token, T, d, E, k, d_w_r, dx_router,
+                                                as_stream(stream)),
+                    fn);
+}
+
 size_t moe_route_topk_workspace_bytes(int64_t T, int32_t E, int32_t k) {
   (void)k;
   if (T < 0 || E < 1) return 0;
@@ -113,7 +148,7 @@ static int check_route_shape(const char* fn, int64_t T, int32_t E, int32_t k, in
   REQUIRE(E >= 1 && E <= 1024, MOE_ERR_UNSUPPORTED, "%s: E=%d outside [1, 1024]", fn, E);
   REQUIRE(k >= 1 && k <= E, MOE_ERR_SHAPE, "%s: k=%d outside [1, E=%d]", fn, k, E);
   REQUIRE(k <= 64, MOE_ERR_UNSUPPORTED, "%s: k=%d above 64", fn, k);
-  REQUIRE(T * k < (int64_t(1) << 31), MOE_ERR_UNSUPPORTED, "%s: T*k must be below 2^31", fn);
+  REQUIRE(prod_below(T, k, int64_t(1) << 31), MOE_ERR_UNSUPPORTED, "%s: T*k must be below 2^31", fn);
   REQUIRE(score == MOE_SOFTMAX || score == MOE_SIGMOID, MOE_ERR_SHAPE, "%s: bad score %d", fn,
           score);
   return MOE_OK;
@@ -171,7 +206,7 @@ int moe_pad_to_max(const int32_t* topk_idx, const int32_t* counts, const int64_t
           "%s: T=%lld E=%d k=%d capacity=%lld", fn, static_cast<long long>(T), E, k,
           static_cast<long long>(capacity));
   REQUIRE(E <= 1024, MOE_ERR_UNSUPPORTED, "%s: E=%d above 1024", fn, E);
-  REQUIRE(static_cast<int64_t>(E) * capacity < (int64_t(1) << 31), MOE_ERR_UNSUPPORTED,
+  REQUIRE(prod_below(E, capacity, int64_t(1) << 31), MOE_ERR_UNSUPPORTED,
           "%s: E * capacity must be below 2^31", fn);
   REQUIRE(counts && offsets && counts_out && offsets_out && src_token_out, MOE_ERR_NULL,
           "%s: counts, offsets and the outputs are required", fn);
@@ -189,6 +224,8 @@ int moe_zero_unmapped_rows(void* buf, int dtype, const int32_t* src_token, int64
   REQUIRE(M >= 0 && d >= 1, MOE_ERR_SHAPE, "%s: M=%lld d=%lld", fn, static_cast<long long>(M),
           static_cast<long long>(d));
   REQUIRE(dtype == MOE_F32 || dtype == MOE_BF16, MOE_ERR_DTYPE, "%s: dtype %d", fn, dtype);
+  REQUIRE(d < (int64_t(1) << 40), MOE_ERR_UNSUPPORTED, "%s: row length %lld", fn,
+          static_cast<long long>(d));
   const int64_t row_bytes = d * (dtype == MOE_F32 ? 4 : 2);
   REQUIRE(row_bytes % 16 == 0, MOE_ERR_UNSUPPORTED, "%s: rows must be multiples of 16 bytes", fn);
   if (M == 0) return ok();
@@ -239,6 +276,23 @@ int moe_check_finite(const float* x, int64_t n, int32_t* status, void* stream) {
   return hip_status(moe::launch_check_finite(x, n, status, as_stream(stream)), fn);
 }
 
+int moe_check_dispatch(const int32_t* topk_idx, const int32_t* counts, const int64_t* offsets,
+                       const int32_t* dst_row, const int32_t* src_token, int64_t T, int32_t E,
+                       int32_t k, int64_t n_rows, int32_t* status, void* stream) {
+  const char* fn = "moe_check_dispatch";
+  REQUIRE(T >= 0 && E >= 1 && k >= 1 && n_rows >= 0, MOE_ERR_SHAPE, "%s: T=%lld E=%d k=%d", fn,
+          static_cast<long long>(T), E, k);
+  REQUIRE(E <= 1024 && prod_below(T, k, int64_t(1) << 31), MOE_ERR_UNSUPPORTED,
+          "%s: E=%d, T*k must be below 2^31", fn, E);
+  REQUIRE(counts && offsets && status, MOE_ERR_NULL, "%s: counts, offsets and status are required",
+          fn);
+  REQUIRE(T == 0 || (topk_idx && dst_row && (n_rows == 0 || src_token)), MOE_ERR_NULL,
+          "%s: topk_idx, dst_row and src_token are required", fn);
+  return hip_status(moe::launch_check_dispatch(topk_idx, counts, offsets, dst_row, src_token, T, E,
+                                               k, n_rows, status, as_stream(stream)),
+                    fn);
+}
+
 int moe_route_replay(const float* logits, const int32_t* topk_idx_in, int64_t T, int32_t E,
                      int32_t k, int score, int renorm, int32_t* topk_idx, float* topk_w,
                      int32_t* counts, int64_t* offsets, int32_t* dst_row, int32_t* src_token,
@@ -266,7 +320,7 @@ int moe_apply_capacity(const int32_t* topk_idx, const int32_t* counts, const int
                        int32_t* counts_out, int64_t* offsets_out, int32_t* dst_row_out,
                        int32_t* src_token_out, void* stream) {
   const char* fn = "moe_apply_capacity";
-  REQUIRE(T >= 0 && E >= 1 && k >= 1 && k <= E && T * k < (int64_t(1) << 31), MOE_ERR_SHAPE,
+  REQUIRE(T >= 0 && E >= 1 && k >= 1 && k <= E && prod_below(T, k, int64_t(1) << 31), MOE_ERR_SHAPE,
           "%s: T=%lld E=%d k=%d", fn, static_cast<long long>(T), E, k);
   REQUIRE(E <= 1024, MOE_ERR_UNSUPPORTED, "%s: E=%d above 1024", fn, E);
   REQUIRE(capacity >= 0, MOE_ERR_SHAPE, "%s: capacity=%lld", fn, static_cast<long long>(capacity));
@@ -356,10 +410,6 @@ int moe_permute_bwd(const void* dx_perm, int dtype, const int32_t* dst_row, int6
 }
 
 // a * b < lim for non-negative a, b, without forming the product
-static bool prod_below(int64_t a, int64_t b, int64_t lim) {
-  return a >= 0 && b >= 0 && (b == 0 || a <= (lim - 1) / b);
-}
-
 static int check_gemm(const char* fn, const void* p0, const void* p1, const int64_t* off, int32_t G,
                       int64_t M, int64_t K, int64_t N, int dtype) {
   REQUIRE(valid_dtype(dtype), MOE_ERR_DTYPE, "%s: bad dtype %d", fn, dtype);
@@ -516,7 +566,7 @@ int moe_unpermute_combine(const void* y_perm, int dtype, const float* topk_w,
 
 int moe_permute_weights(const float* topk_w, const int32_t* dst_row, int64_t T, int32_t k,
                         float* w_perm, void* stream) {
-  REQUIRE(T >= 0 && k >= 1 && T * k < (int64_t(1) << 31), MOE_ERR_SHAPE,
+  REQUIRE(T >= 0 && k >= 1 && prod_below(T, k, int64_t(1) << 31), MOE_ERR_SHAPE,
           "moe_permute_weights: T=%lld k=%d", static_cast<long long>(T), k);
   if (T == 0) return ok();
   REQUIRE(topk_w && dst_row && w_perm, MOE_ERR_NULL, "moe_permute_weights: all pointers are required");
@@ -526,7 +576,7 @@ int moe_permute_weights(const float* topk_w, const int32_t* dst_row, int64_t T, 
 
 int moe_gate_grad(const float* gate_partials, int64_t P, const int32_t* dst_row, int64_t T,
                   int32_t k, float* d_topk_w, void* stream) {
-  REQUIRE(T >= 0 && k >= 1 && P >= 1 && T * k < (int64_t(1) << 31), MOE_ERR_SHAPE,
+  REQUIRE(T >= 0 && k >= 1 && P >= 1 && prod_below(T, k, int64_t(1) << 31), MOE_ERR_SHAPE,
           "moe_gate_grad: T=%lld k=%d P=%lld", static_cast<long long>(T), k,
           static_cast<long long>(P));
   if (T == 0) return ok();
@@ -545,7 +595,7 @@ int moe_unpermute_combine_bwd(const void* dout, const void* y_perm, int dtype, c
           "moe_unpermute_combine_bwd: T=%lld d=%lld k=%d n_rows=%lld", static_cast<long long>(T),
           static_cast<long long>(d), k, static_cast<long long>(n_rows));
   REQUIRE(k <= 64, MOE_ERR_UNSUPPORTED, "moe_unpermute_combine_bwd: k=%d above 64", k);
-  REQUIRE(T * k < (int64_t(1) << 31), MOE_ERR_UNSUPPORTED,
+  REQUIRE(prod_below(T, k, int64_t(1) << 31), MOE_ERR_UNSUPPORTED,
           "moe_unpermute_combine_bwd: T*k must be below 2^31");
   int st = check_row_vectors(dtype, d, "moe_unpermute_combine_bwd");
   if (st != MOE_OK) return st;
@@ -631,7 +681,7 @@ int moe_quant_fp8_weights(const void* w, int32_t G, int64_t K, int64_t N, uint8_
 }
 
 int64_t moe_padded_rows_bound(int64_t M, int32_t G, int32_t align) {
-  if (M < 0 || G < 1 || align < 1) return 0;
+  if (M < 0 || G < 1 || align < 1 || M > (int64_t(1) << 60)) return 0;
   const int64_t n = M + static_cast<int64_t>(G) * (align - 1);
   return (n + align - 1) / align * align;
 }

@@ -720,6 +720,63 @@ __global__ __launch_bounds__(256) void check_finite_kernel(const float* __restri
   if (__ballot(bad) != 0 && (threadIdx.x & 63) == 0) *status = 1;
 }
 
+// Invariants of a dispatch map (counts, offsets, dst_row, src_token of the
+// route, capacity or pad-to-max calls), each violation OR-ed into *status as
+// one bit (OR is order-independent, so the word is deterministic):
+//   1  offsets[0] != 0, offsets decreasing, a segment shorter than its count,
+//      or offsets[E] beyond the rows
+//   2  a pair's row outside its expert's filled segment [offsets[e],
+//      offsets[e] + counts[e]) (dropped pairs, row -1, are allowed)
+//   4  src_token[row] is not the pair's token
+//   8  a segment's tokens not in ascending order
+//   16 a pair's expert outside [0, E)
+// Every index is range-checked before it is dereferenced.
+__global__ __launch_bounds__(256) void check_dispatch_kernel(
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ counts,
+    const int64_t* __restrict__ offsets, const int32_t* __restrict__ dst_row,
+    const int32_t* __restrict__ src_token, int64_t T, int E, int k, int64_t n_rows,
+    int32_t* __restrict__ status) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  int bits = 0;
+  if (i <= E) {  // per expert (and the end of the offsets)
+    const int64_t lo = offsets[i];
+    if (i == 0 && lo != 0) bits |= 1;
+    if (i == E) {
+      if (lo < 0 || lo > n_rows) bits |= 1;
+    } else {
+      const int64_t hi = offsets[i + 1];
+      const int64_t c = counts[i];
+      if (c < 0 || lo < 0 || hi < lo || hi - lo < c || hi > n_rows) bits |= 1;
+      else
+        for (int64_t r = lo + 1; r < lo + c; ++r)
+          if (src_token[r] <= src_token[r - 1]) { bits |= 8; break; }
+    }
+  }
+  if (i < T * k) {  // per (token, slot) pair
+    const int64_t t = i / k;
+    const int e = topk_idx[i];
+    const int64_t r = dst_row[i];
+    if (e < 0 || e >= E) {
+      bits |= 16;
+    } else if (r != -1) {
+      const int64_t lo = offsets[e], c = counts[e];
+      if (r < lo || r >= lo + c || r < 0 || r >= n_rows) bits |= 2;
+      else if (src_token[r] != t) bits |= 4;
+    }
+  }
+  if (bits) atomicOr(status, bits);
+}
+
+hipError_t launch_check_dispatch(const int32_t* topk_idx, const int32_t* counts,
+                                 const int64_t* offsets, const int32_t* dst_row,
+                                 const int32_t* src_token, int64_t T, int E, int k, int64_t n_rows,
+                                 int32_t* status, hipStream_t stream) {
+  const int64_t n = T * k > E + 1 ? T * k : E + 1;
+  check_dispatch_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), 256, 0, stream>>>(
+      topk_idx, counts, offsets, dst_row, src_token, T, E, k, n_rows, status);
+  return hipGetLastError();
+}
+
 hipError_t launch_check_finite(const float* p, int64_t n, int32_t* status, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   int64_t blocks = (n / 4 + 255) / 256;

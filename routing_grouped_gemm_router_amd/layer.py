@@ -104,12 +104,23 @@ class MoELayer:
         self.check_finite = os.environ.get("MOE_CHECK_FINITE", "") not in ("", "0")
         if self.check_finite:
             self.finite_status = torch.zeros(1, dtype=torch.int32, device=self.dev)
+        # MOE_DEBUG set: every route's dispatch map is checked against its
+        # invariants before the permute and the GEMMs use it (moe_check_dispatch);
+        # violations accumulate as bits in debug_status (read with dispatch_ok())
+        self.debug = os.environ.get("MOE_DEBUG", "") not in ("", "0")
+        if self.debug:
+            self.debug_status = torch.zeros(1, dtype=torch.int32, device=self.dev)
         self.w = weights
         T, d, E, k, f = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f
         N = T * k
         dt = cfg.torch_dtype()
         dev = self.dev
         self.score = abi.SOFTMAX if cfg.score == "softmax" else abi.SIGMOID
+        # the route's backward leaves d_logits zero off each token's chosen
+        # experts with renormalised routing or sigmoid scores, unless the
+        # auxiliary loss adds its dense gradient
+        self.sparse_dz = ((cfg.renorm or cfg.score == "sigmoid") and cfg.aux_loss_coeff <= 0
+                          and cfg.E <= 256 and cfg.d % 8 == 0)
         emp = lambda *s, dtype=dt: torch.empty(s, dtype=dtype, device=dev)  # noqa: E731
         # forward state
         self.logits = emp(T, E, dtype=torch.float32)
@@ -343,6 +354,13 @@ class MoELayer:
             with self._span("shared_gemm1_wgrad"):
                 gm["wgrad"](a, sa, b, sb, self.poff_all, self.dws13)
 
+    def dispatch_ok(self):
+        """The bits moe_check_dispatch raised in every forward so far (0: none);
+        MOE_DEBUG must have been set when the layer was built.  Synchronises."""
+        if not self.debug:
+            raise RuntimeError("MOE_DEBUG was not set when the layer was built")
+        return int(self.debug_status.item())
+
     def finite_ok(self):
         """False once a forward met a non-finite logit (MOE_CHECK_FINITE set);
         reads the device status word, so it synchronises."""
@@ -387,7 +405,11 @@ class MoELayer:
                 abi.moe_apply_capacity(self.topk_idx, m["counts"], m["offsets"], m["dst_row"],
                                        self.capacity, self.counts, self.offsets, self.dst_row,
                                        self.src_token)
+        if self.debug:
+            abi.moe_check_dispatch(self.topk_idx, self.counts, self.offsets, self.dst_row,
+                                   self.src_token, self.src_token.numel(), self.debug_status)
         self.routed_counts = m["counts"]  # before any dropping
+        self.route_map = m                # the dropless dispatch map
         if self.ebias and c.expert_bias_rate > 0:  # the next route sees the moved bias
             with self._span("expert_bias_update"):
                 abi.moe_expert_bias_update(self.routed_counts, c.expert_bias_rate, self.sel_bias)
@@ -498,7 +520,14 @@ class MoELayer:
                 abi.moe_aux_loss(self.logits, self.routed_counts, c.k, self.score,
                                  c.aux_loss_coeff, d_logits=self.d_logits)
         with self._span("router_logits_bwd"):
-            abi.moe_router_logits_bwd(x, w["w_r"], self.d_logits, self.dw_r, self.dx_router)
+            if self.sparse_dz:
+                # d_logits is zero off each token's chosen experts: only those entries are read
+                abi.moe_router_logits_bwd_topk(x, w["w_r"], self.d_logits, self.topk_idx,
+                                               self.route_map["offsets"],
+                                               self.route_map["src_token"], self.dw_r,
+                                               self.dx_router)
+            else:
+                abi.moe_router_logits_bwd(x, w["w_r"], self.d_logits, self.dw_r, self.dx_router)
         with self._span("permute_bwd"):
             abi.moe_permute_bwd(self.dx_perm, self.dst_row, dxs, self.dx_router, self.dx)
         return self.dx

@@ -47,9 +47,22 @@ def _fake(n=1 << 20):
     return ctypes.c_void_p(n)
 
 
-@pytest.mark.parametrize("case,expect", [
-    # (function, args) -> status
+# (function, args) -> status: calls that validation must reject before any HIP call
+VALIDATION_CASES = [
     (("moe_check_finite", (None, 16, None, None)), -1),
+    (("moe_router_logits_bwd_topk", (None, 1, None, None, None, None, None, 10, 64, 300, 8, _fake(),
+                                     None, None)), -4),
+    (("moe_router_logits_bwd_topk", (None, 1, None, None, None, None, None, 10, 60, 16, 8, _fake(),
+                                     None, None)), -4),
+    (("moe_router_logits_bwd_topk", (None, 1, None, None, None, None, None, 10, 64, 16, 8, _fake(),
+                                     None, None)), -1),
+    (("moe_router_logits_bwd_topk", (None, 1, None, None, None, None, None, 10, 64, 128, 65,
+                                     _fake(), None, None)), -4),
+    (("moe_check_dispatch", (None, None, None, None, None, 10, 8, 2, 20, None, None)), -1),
+    (("moe_check_dispatch", (_fake(), _fake(), _fake(), _fake(), _fake(), 10, 2000, 2, 20, _fake(),
+                             None)), -4),
+    (("moe_check_dispatch", (_fake(), _fake(), _fake(), _fake(), _fake(), -1, 8, 2, 20, _fake(),
+                             None)), -2),
     (("moe_route_topk_noalloc", (_fake(), 1 << 20, 1024, 1, 0, 1, _fake(), _fake(), _fake(),
                                  _fake(), _fake(), _fake(), None)), -4),
     (("moe_route_topk_noalloc", (_fake(), 10, 2000, 2, 0, 1, _fake(), _fake(), _fake(), _fake(),
@@ -109,7 +122,10 @@ def _fake(n=1 << 20):
     (("moe_router_logits", (None, 1, None, None, 10, 64, 2000, None, None)), -4),
     (("moe_router_logits", (None, 1, None, None, 10, 64, 8, None, None)), -1),
     (("moe_router_logits_bwd", (None, 1, None, None, 10, 64, 8, _fake(), None, None)), -1),
-])
+]
+
+
+@pytest.mark.parametrize("case,expect", VALIDATION_CASES)
 def test_validation_rejects_before_launch(lib, case, expect):
     name, args = case
     st = getattr(lib, name)(*args)

@@ -370,6 +370,39 @@ def test_router_logits(gpu, dt, T, d, E, bias):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("T,d,E,k,score,renorm", [(515, 7168, 256, 8, "sigmoid", True),
+                                                  (300, 1000, 8, 2, "softmax", True),
+                                                  (77, 128, 64, 4, "sigmoid", False),
+                                                  (1, 256, 4, 2, "softmax", True)])
+def test_router_bwd_on_chosen_experts(gpu, dt, T, d, E, k, score, renorm):
+    """moe_router_logits_bwd_topk (reading d_logits only at each token's chosen
+    experts) against the oracle's dense products, and against the dense GPU
+    call, on the d_logits that moe_route_topk_bwd produces."""
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    x = inputs.normal((T, d), 1.0, 81, 0, "cpu", tdt)
+    w_r = inputs.normal((d, E), d ** -0.5, 82, 0, "cpu", torch.float32)
+    z = (np64(x) @ w_r.numpy().astype(np.float64)).astype(np.float32)
+    zz, o = _route_gpu(z, k, score, renorm)
+    dw = inputs.normal((T, k), 1.0, 83, 0, "cpu", torch.float32).to(DEV)
+    dz = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    abi.moe_route_topk_bwd(zz, o["topk_idx"], o["topk_w"], dw, abi.SOFTMAX if score == "softmax"
+                           else abi.SIGMOID, renorm, dz)
+    xd, wd = x.to(DEV), w_r.to(DEV)
+    dwr = torch.full((d, E), float("nan"), dtype=torch.float32, device=DEV)
+    dxr = torch.full((T, d), float("nan"), dtype=torch.float32, device=DEV)
+    abi.moe_router_logits_bwd_topk(xd, wd, dz, o["topk_idx"], o["offsets"], o["src_token"], dwr,
+                                   dxr)
+    rw, rx = oracle.router_logits_bwd(np64(x), w_r.numpy(), np64(dz))
+    assert_close("dW_r (chosen entries)", dwr, rw, TOL["f32"])
+    assert_close("dx_router (chosen entries)", dxr, rx, TOL["f32"])
+    dwr2 = torch.empty_like(dwr)
+    dxr2 = torch.empty_like(dxr)
+    abi.moe_router_logits_bwd(xd, wd, dz, dwr2, dxr2)
+    assert_close("dW_r vs dense call", dwr, np64(dwr2), TOL["f32"])
+    assert_close("dx_router vs dense call", dxr, np64(dxr2), TOL["f32"])
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_router_fp32_accuracy(gpu, dt):
     """The router products carry fp32 accuracy: operands whose 24 mantissa
     bits all matter (a spread of magnitudes, values just off bf16 rounding
@@ -413,6 +446,76 @@ def test_check_finite(gpu, n, pos, val):
     abi.moe_check_finite(torch.zeros(64, dtype=torch.float32, device=DEV), status)
     torch.cuda.synchronize()
     assert int(status.item()) == (0 if pos is None else 1)
+
+
+def test_check_dispatch_flags_each_broken_invariant(gpu):
+    """A valid map (dropless, capacity, pad-to-max) raises no bit; each planted
+    corruption of a copy raises the bit of the invariant it breaks."""
+    T, E, k = 3000, 16, 4
+    z = _keys(T, E, 91, "normal")
+    _, o = _route_gpu(z, k, "softmax", True)
+    n = T * k
+
+    def check(m, n_rows=n):
+        st = torch.zeros(1, dtype=torch.int32, device=DEV)
+        abi.moe_check_dispatch(m["topk_idx"], m["counts"], m["offsets"], m["dst_row"],
+                               m["src_token"], n_rows, st)
+        torch.cuda.synchronize()
+        return int(st.item())
+
+    assert check(o) == 0
+    cap = 600
+    capm = dict(topk_idx=o["topk_idx"], counts=torch.empty_like(o["counts"]),
+                offsets=torch.empty_like(o["offsets"]), dst_row=torch.empty_like(o["dst_row"]),
+                src_token=torch.empty_like(o["src_token"]))
+    abi.moe_apply_capacity(o["topk_idx"], o["counts"], o["offsets"], o["dst_row"], cap,
+                           capm["counts"], capm["offsets"], capm["dst_row"], capm["src_token"])
+    assert check(capm) == 0 and int((capm["dst_row"] < 0).sum()) > 0
+    pad = dict(topk_idx=o["topk_idx"], counts=torch.empty_like(o["counts"]),
+               offsets=torch.empty_like(o["offsets"]), dst_row=torch.empty_like(o["dst_row"]),
+               src_token=torch.empty(E * cap, dtype=torch.int32, device=DEV))
+    abi.moe_pad_to_max(o["topk_idx"], o["counts"], o["offsets"], o["dst_row"], o["src_token"], cap,
+                       pad["counts"], pad["offsets"], pad["dst_row"], pad["src_token"])
+    assert check(pad, E * cap) == 0
+
+    def broken(**kw):
+        m = {key: v.clone() for key, v in o.items()}
+        for key, fn in kw.items():
+            fn(m[key])
+        return m
+
+    def swap_experts_rows(d):
+        a, b = d.view(-1)[0].item(), d.view(-1)[k * 7 + 1].item()
+        d.view(-1)[0], d.view(-1)[k * 7 + 1] = b, a
+    assert check(broken(dst_row=swap_experts_rows)) & 6
+    off = o["offsets"].cpu()
+    assert check(broken(offsets=lambda d: d.__setitem__(5, int(off[4]) - 1))) & 1
+    assert check(broken(offsets=lambda d: d.__setitem__(0, 1))) & 1
+
+    def swap_in_segment(s):
+        lo = int(off[3])
+        a, b = s[lo].item(), s[lo + 1].item()
+        s[lo], s[lo + 1] = b, a
+    bits = check(broken(src_token=swap_in_segment))
+    assert bits & 8 and bits & 4
+    assert check(broken(topk_idx=lambda d: d.view(-1).__setitem__(11, E))) & 16
+    assert check(broken(dst_row=lambda d: d.view(-1).__setitem__(13, n + 5))) & 2
+
+
+@pytest.mark.parametrize("name", ["small_capacity", "small_pad_to_max", "small_expert_bias"])
+def test_layer_debug_mode_finds_its_maps_valid(gpu, name, monkeypatch):
+    """With MOE_DEBUG and MOE_CHECK_FINITE set, a layer's routes pass the
+    dispatch-map check and its logits the finite check."""
+    monkeypatch.setenv("MOE_DEBUG", "1")
+    monkeypatch.setenv("MOE_CHECK_FINITE", "1")
+    from routing_grouped_gemm_router_amd.layer import MoELayer
+    cfg = inputs.CONFIGS[name]
+    w = {key: (None if v is None else v.to(DEV)) for key, v in inputs.layer_inputs(cfg, 0).items()}
+    layer = MoELayer(cfg, w, DEV)
+    for _ in range(2):
+        layer.forward(w["x"])
+        layer.backward(w["dout"])
+    assert layer.dispatch_ok() == 0 and layer.finite_ok()
 
 
 def test_bf16_rounding_bit_exact(gpu):
