@@ -290,9 +290,14 @@ __device__ __forceinline__ void tile_in_group(uint32_t tl, uint32_t mt_g, uint32
 // 256-row tiling of the plain epilogue measured faster at every tile ratio
 // from 1.59 up and slower at 1.5 and below.  With the SwiGLU epilogues it was
 // 16 % (forward) and 9 % (backward) slower at a ratio of 1.56, and 5 % and
-// 12 % faster at 2 (one group of 8192 rows).
-template <int MODE>
+// 12 % faster at 2 (one group of 8192 rows).  MXFP8 moves twice the FLOPs
+// per operand byte of bf16, so its 128-row tiles are held back by the LDS
+// DMA rate: the 256-row tiles ran 1.2 times faster per executed FLOP there,
+// which pays for the larger ragged tails from a tile ratio of about 1.65 in
+// every mode.
+template <int MODE, int Q>
 __device__ __forceinline__ bool rows256_preferred(int t128, int t256) {
+  if (Q == P_MX) return 20LL * t128 >= 33LL * t256;
   if (MODE == FWD_SWIGLU || MODE == DGRAD_SWIGLU_BWD) return 10LL * t128 >= 19LL * t256;
   return 20LL * t128 >= 31LL * t256;
 }
@@ -966,7 +971,7 @@ __global__ __launch_bounds__(Cfg<WN>::THREADS, Cfg<WN>::WG_PER_CU) void gg_kerne
       }
     }
     __syncthreads();
-    if (MODE != WGRAD && p.pair256 && rows256_preferred<MODE>(s_pre[p.G], s_t256))
+    if (MODE != WGRAD && p.pair256 && rows256_preferred<MODE, Q>(s_pre[p.G], s_t256))
       return;  // the paired 256-row launch does the work
     NT = p.Nout / BN;
     total = static_cast<int64_t>(s_pre[p.G]) * NT;
@@ -1063,7 +1068,7 @@ static hipError_t run_cfg(const Params& p, int64_t tiles_upper_bound, hipStream_
 
 // bf16 row-group modes in 256 x 256 tiles (defined below); false when the
 // shape does not fit them
-template <int MODE>
+template <int MODE, int Q>
 static bool launch_rows256(const Params& p, hipStream_t s, hipError_t& err);
 
 // Row-group modes: tiles of BM rows of a group x BN product columns (SwiGLU:
@@ -1072,13 +1077,13 @@ static bool launch_rows256(const Params& p, hipStream_t s, hipError_t& err);
 template <int MODE, int Q>
 static hipError_t run_rows(const Params& p, hipStream_t s) {
   const int64_t mt = p.M / BM + p.G;
-  if constexpr (Q == P_BF16) {
+  if constexpr (Q != P_FP8) {
     // both tilings are launched; from the group sizes each kernel finds on
     // the device which of the two does the work, and the other one exits
     Params q = p;
     q.pair256 = 1;
     hipError_t err = hipSuccess;
-    if (launch_rows256<MODE>(q, s, err)) {
+    if (launch_rows256<MODE, Q>(q, s, err)) {
       if (err != hipSuccess) return err;
       return run_cfg<MODE, Q, 4>(q, mt * (p.Nout / 256), s);
     }
@@ -1445,11 +1450,13 @@ __global__ __launch_bounds__(512, 1) void wgrad256_kernel(Params p) {
 // them); the larger tile halves the row tiles of a large group, hence its
 // re-reads of the weight slabs, and moves a third fewer operand bytes per FLOP
 // into LDS.
-template <int MODE>
+template <int MODE, int Q>
 __global__ __launch_bounds__(512, 1) void rows256_kernel(Params p) {
   using namespace w256;
-  constexpr int STAGE = OPS;
-  constexpr bool B_NC = MODE == FWD || MODE == FWD_SWIGLU;
+  constexpr bool MX = Q == P_MX;
+  constexpr int STAGE = stage_bytes<Q>();
+  constexpr bool B_NC = !MX && (MODE == FWD || MODE == FWD_SWIGLU);
+  constexpr int ES = MX ? 1 : 2;  // operand element bytes
   __shared__ __attribute__((aligned(1024))) char ring[STAGES * STAGE];
   __shared__ int s_pre[MAX_GROUPS + 1];
   __shared__ int s_off[MAX_GROUPS + 1];
@@ -1502,12 +1509,12 @@ __global__ __launch_bounds__(512, 1) void rows256_kernel(Params p) {
     if (lane == 0) s_t128 = t128;
   }
   __syncthreads();
-  if (p.pair256 && !rows256_preferred<MODE>(s_t128, s_pre[p.G])) return;  // the 128-row launch works
+  if (p.pair256 && !rows256_preferred<MODE, Q>(s_t128, s_pre[p.G])) return;  // the 128-row launch works
 
   const uint32_t NT = static_cast<uint32_t>(p.Nout / BMN);
   const int64_t total = static_cast<int64_t>(s_pre[p.G]) * NT;
   const int64_t Kc = p.Kc, N = p.Nout;
-  const int nk = static_cast<int>(Kc / 64);
+  const int nk = static_cast<int>(Kc / KStep<MX>::value);
 
   struct TR {
     int g;
@@ -1532,15 +1539,23 @@ __global__ __launch_bounds__(512, 1) void rows256_kernel(Params p) {
     t.col0 = static_cast<int64_t>(n) * BMN;
     t.rows = static_cast<int>(min<int64_t>(BMN, hi - t.row0));
   };
-  i32x4_t ra, rb;
-  uint32_t va[4], vb[4];
+  // MXFP8: B row (output column) of tile row rho; with SwiGLU slab s (one
+  // wave column) holds gate columns col0 / 2 + 64 s .. + 63 in rows 0-63 and
+  // the matching up columns in rows 64-127
+  auto b_row_kc = [&](const TR& t, int rho) -> int64_t {
+    if (MODE == FWD_SWIGLU)
+      return ((rho & 127) >= 64 ? N / 2 : 0) + t.col0 / 2 + (rho >> 7) * 64 + (rho & 63);
+    return t.col0 + rho;
+  };
+  i32x4_t ra, rb, rs;
+  uint32_t va[4], vb[4], vs = 0;
   auto setup = [&](const TR& t) {
-    ra = make_rsrc(p.A + t.row0 * Kc * 2, static_cast<uint64_t>(t.rows) * Kc * 2);
+    ra = make_rsrc(p.A + t.row0 * Kc * ES, static_cast<uint64_t>(t.rows) * Kc * ES);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {  // A: rows 8 (q % 16) .. + 7 of slab q / 16
       const int q = wave * 4 + i, slab = q >> 4;
       const int r = 8 * (q & 15) + (lane >> 3), c = (lane & 7) ^ swz_kc(r);
-      va[i] = static_cast<uint32_t>((slab * 128 + r) * Kc * 2 + c * 16);
+      va[i] = static_cast<uint32_t>((slab * 128 + r) * Kc * ES + c * 16);
     }
     if (B_NC) {  // W_g [Kc, N]: k rows 4 (q % 16) .. + 3, columns col0 + 128 slab ..
       rb = make_rsrc(p.B + static_cast<int64_t>(t.g) * Kc * N * 2, static_cast<uint64_t>(Kc) * N * 2);
@@ -1556,13 +1571,27 @@ __global__ __launch_bounds__(512, 1) void rows256_kernel(Params p) {
                                 : t.col0 + slab * 128 + 8 * c;
         vb[i] = static_cast<uint32_t>((kr * N + col) * 2);
       }
-    } else {  // W_g [N, Kc]: rows col0 + 128 slab + 8 (q % 16) ..
-      rb = make_rsrc(p.B + static_cast<int64_t>(t.g) * N * Kc * 2, static_cast<uint64_t>(N) * Kc * 2);
+    } else {  // B rows k-contiguous: bf16 W_g [N, Kc]; MXFP8 W_g^T / W_g codes [N, Kc]
+      rb = make_rsrc(p.B + static_cast<int64_t>(t.g) * N * Kc * ES,
+                     static_cast<uint64_t>(N) * Kc * ES);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int q = wave * 4 + i, slab = q >> 4;
         const int r = 8 * (q & 15) + (lane >> 3), c = (lane & 7) ^ swz_kc(r);
-        vb[i] = static_cast<uint32_t>((t.col0 + slab * 128 + r) * Kc * 2 + c * 16);
+        vb[i] = static_cast<uint32_t>(b_row_kc(t, slab * 128 + r) * Kc * ES + c * 16);
+      }
+    }
+    if (MX) {
+      // E8M0 bytes, one per 32 k: A [M][Kc/32] (rows past the group read as
+      // zero), B [G][N][Kc/32]; dword kt of each row.  Waves 0-3 fetch the
+      // 256 rows of A, waves 4-7 those of B.
+      const int64_t nb = Kc / 32;
+      if (wave < 4) {
+        rs = make_rsrc(p.ea + t.row0 * nb, static_cast<uint64_t>(t.rows) * nb);
+        vs = static_cast<uint32_t>((wave * 64 + lane) * nb);
+      } else {
+        rs = make_rsrc(p.eb + static_cast<int64_t>(t.g) * N * nb, static_cast<uint64_t>(N) * nb);
+        vs = static_cast<uint32_t>(b_row_kc(t, (wave - 4) * 64 + lane) * nb);
       }
     }
   };
@@ -1572,6 +1601,7 @@ __global__ __launch_bounds__(512, 1) void rows256_kernel(Params p) {
     for (int i = 0; i < 4; ++i) dma16(ra, stage + (wave * 4 + i) * 1024, va[i] + kt * da);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma16(rb, stage + 2 * SLAB + (wave * 4 + i) * 1024, vb[i] + kt * db);
+    if (MX) dma4(rs, stage + OPS + wave * 256, vs + kt * 4);
   };
 
   const Walk walk = make_walk(total);
@@ -1625,21 +1655,48 @@ __global__ __launch_bounds__(512, 1) void rows256_kernel(Params p) {
       const LDS_AS char* opA = stage + (wm >> 1) * SLAB;
       const LDS_AS char* opB = stage + 2 * SLAB + wn * SLAB;
       const int ra0 = (wm & 1) * 64;
+      if constexpr (MX) {
+        // scale dwords: A rows at 0.., B rows at 256..; see compute_stage_mx
+        const LDS_AS uint32_t* eA = (const LDS_AS uint32_t*)(stage + OPS);
+        const int h = lane >> 5;
+        uint32_t xa[2], xb[4];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        bf16x8_t a[2], b[4];
+        for (int ii = 0; ii < 2; ++ii) xa[ii] = eA[wm * 64 + ii * 32 + (lane & 31)] >> (8 * h);
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii)
-          a[ii] = frag_kc(opA, ra0 + ii * 32 + (lane & 31), kk * 2 + (lane >> 5));
+        for (int jj = 0; jj < 4; ++jj) xb[jj] = eA[256 + wn * 128 + jj * 32 + (lane & 31)] >> (8 * h);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          b[jj] = B_NC ? frag_nc(opB, jj * 32, kk * 16, lane)
-                       : frag_kc(opB, jj * 32 + (lane & 31), kk * 2 + (lane >> 5));
+        for (int s2 = 0; s2 < 2; ++s2) {
+          i32x8_t a[2], b[4];
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii)
+          for (int ii = 0; ii < 2; ++ii) a[ii] = frag_mx(opA, ra0 + ii * 32 + (lane & 31), s2, h);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) b[jj] = frag_mx(opB, jj * 32 + (lane & 31), s2, h);
+#pragma unroll
+          for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+              // format 0 = E4M3 for both; byte 0 of each scale operand is used
+              acc[ii][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  b[jj], a[ii], acc[ii][jj], 0, 0, 0, static_cast<int>(xb[jj] >> (16 * s2)), 0,
+                  static_cast<int>(xa[ii] >> (16 * s2)));
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          bf16x8_t a[2], b[4];
+#pragma unroll
+          for (int ii = 0; ii < 2; ++ii)
+            a[ii] = frag_kc(opA, ra0 + ii * 32 + (lane & 31), kk * 2 + (lane >> 5));
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj)
-            acc[ii][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[jj], a[ii], acc[ii][jj], 0, 0, 0);
+            b[jj] = B_NC ? frag_nc(opB, jj * 32, kk * 16, lane)
+                         : frag_kc(opB, jj * 32 + (lane & 31), kk * 2 + (lane >> 5));
+#pragma unroll
+          for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+              acc[ii][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[jj], a[ii], acc[ii][jj], 0, 0, 0);
+        }
       }
     }
     if (++cp_kt == nk) {
@@ -1772,14 +1829,15 @@ __global__ __launch_bounds__(512, 1) void rows256_kernel(Params p) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int MODE>
+template <int MODE, int Q>
 static bool launch_rows256(const Params& p, hipStream_t s, hipError_t& err) {
-  if (p.Nout % w256::BMN != 0 || p.Kc % 64 != 0 || p.Kc < 64 || !p.pair256) return false;
+  constexpr int BK = KStep<Q != P_BF16>::value;
+  if (p.Nout % w256::BMN != 0 || p.Kc % BK != 0 || p.Kc < BK || !p.pair256) return false;
   const int64_t tiles = (p.M / w256::BMN + p.G) * (p.Nout / w256::BMN);
   int64_t grid = cu_count();  // persistent, one workgroup per CU
   if (tiles < grid) grid = tiles;
   if (grid < 1) grid = 1;
-  rows256_kernel<MODE><<<dim3(static_cast<unsigned>(grid)), 512, 0, s>>>(p);
+  rows256_kernel<MODE, Q><<<dim3(static_cast<unsigned>(grid)), 512, 0, s>>>(p);
   err = hipGetLastError();
   return true;
 }

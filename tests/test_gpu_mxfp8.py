@@ -136,8 +136,11 @@ def _oracle_mx_rows(A):
     return fp8.dequantize_mx_rows(q, s), torch.from_numpy(q), torch.from_numpy(s)
 
 
+# the last two have groups of over a thousand rows, so that the 256-row tiles
+# do the work in every mode (forward, SwiGLU forward, both data gradients)
 @pytest.mark.parametrize("M,G,K,N,swiglu", [(1000, 5, 256, 384, False), (2600, 8, 512, 512, True),
-                                             (129, 1, 128, 256, True), (700, 3, 384, 256, False)])
+                                             (129, 1, 128, 256, True), (700, 3, 384, 256, False),
+                                             (3000, 2, 512, 512, True), (3100, 3, 512, 768, False)])
 def test_mx_grouped_gemm_fwd_dgrad(gpu, M, G, K, N, swiglu):
     print(f"mxfp8 gemm M={M} G={G} K={K} N={N} swiglu={swiglu}", flush=True)
     off = inputs.random_segments(M, G, 7, empty_frac=0.2)
