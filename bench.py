@@ -125,8 +125,9 @@ def fp8_work(cfg, n_nonempty, mx=False, n_rows=None):
     stored in bf16 (2 bytes) and quantized to 1-byte E4M3 codes before each
     GEMM, with one fp32 scale per 128 elements (blockwise) or one E8M0 byte per
     32 (MXFP8); weights are re-quantized every step (they change every step),
-    to two copies (k-contiguous along each GEMM's reduction); GEMM outputs are
-    bf16.  MXFP8 gathers x through the permutation inside its quantizers (x
+    blockwise to one code array in the weight's own layout (the forward reads
+    it transposed) with the block scale expanded for each GEMM, MXFP8 to two
+    copies (E8M0 scales along each GEMM's reduction); GEMM outputs are bf16.  MXFP8 gathers x through the permutation inside its quantizers (x
     read once, the row map read, no permuted bf16 copy)."""
     T, d, E, k, f, fs = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.fs
     N = T * k if n_rows is None else n_rows
@@ -137,8 +138,8 @@ def fp8_work(cfg, n_nonempty, mx=False, n_rows=None):
     def rows(m, n):      # bf16 in, fp8 rows out
         return m * n * 2 + q(m * n)
 
-    def wq(n):           # bf16 weight in, two quantized copies out
-        return n * 2 + 2 * q(n)
+    def wq(n):           # bf16 weight in; codes once (MXFP8: twice) and both scale vectors out
+        return n * 2 + (2 * q(n) if mx else n + 2 * (n / 128 * 4))
 
     w13, w2 = n_nonempty * d * 2 * f, n_nonempty * f * d
     w = {

@@ -66,7 +66,7 @@ typedef enum {
 const char* moe_status_string(int status);
 /* Detail of the last failing call on this host thread ("" if none). */
 const char* moe_last_error(void);
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2. */
 int moe_abi_version(void);
 
 /* ---------------------------------------------------------------- Route -- */
@@ -390,12 +390,14 @@ int moe_swiglu_bwd(const void* dh, const void* ab, int dtype, int64_t M, int64_t
 int moe_quant_fp8_rows(const void* x, int64_t M, int64_t K, uint8_t* q, float* scale_t,
                        void* stream);
 
-/* 128 x 128 blocks of w [G, K, N], written in both GEMM operand layouts from
- * the same block scale s[g][kb][nb]:
- *   q_fwd [G, N, K] (transposed) with s_fwd [G, K/128, N] = s[g][kb][n / 128]
- *   q_dgrad [G, K, N]           with s_dgrad [G, N/128, K] = s[g][k / 128][nb] */
-int moe_quant_fp8_weights(const void* w, int32_t G, int64_t K, int64_t N, uint8_t* q_fwd,
-                          float* s_fwd, uint8_t* q_dgrad, float* s_dgrad, void* stream);
+/* 128 x 128 blocks of w [G, K, N]: ONE code array q [G, K, N] in w's own
+ * layout, which both GEMMs read (a block's scale serves either orientation),
+ * and the block scale s[g][kb][nb] expanded along each GEMM's output columns:
+ *   s_fwd [G, K/128, N] = s[g][kb][n / 128]   (forward)
+ *   s_dgrad [G, N/128, K] = s[g][k / 128][nb]  (dgrad)
+ * w 16-byte and q 8-byte aligned. */
+int moe_quant_fp8_weights(const void* w, int32_t G, int64_t K, int64_t N, uint8_t* q,
+                          float* s_fwd, float* s_dgrad, void* stream);
 
 /* Host helper: rows a padded layout of M rows in G groups can need,
  * M + G * (align - 1) rounded up to align (the row length `ldm` of the
@@ -419,14 +421,15 @@ int moe_quant_fp8_token_tiles(const void* x, const int64_t* offsets, const int64
  * its two scales; outputs bf16 (dB: bf16 or fp32).  Groups as in the bf16
  * calls.  Epilogues as in the bf16 calls.
  *   forward: C[rows g] = deq(A)[rows g] . deq(B_g)   A [M, K] + scale_t [K/128, M]
- *            from moe_quant_fp8_rows; B from moe_quant_fp8_weights (q_fwd, s_fwd)
+ *            from moe_quant_fp8_rows; B = q [G, K, N] from moe_quant_fp8_weights
+ *            with s_fwd (the weights' own layout, read transposed)
  *   dgrad:   dA[rows g] = deq(dC)[rows g] . deq(B_g)^T   dC [M, N] + scale_t
- *            [N/128, M]; B (q_dgrad, s_dgrad)
+ *            [N/128, M]; B = the same q [G, K, N] with s_dgrad
  *   wgrad:   dB[g] = deq(A)^T . deq(dC) over group g's padded rows; A_t [K, ldm],
  *            dC_t [N, ldm] and scales from moe_quant_fp8_token_tiles
  * Limits: K % 128 == 0, N % 128 == 0 (forward SWIGLU: N / 2 % 64 == 0),
  * K * N < 2^32 (one expert's weight codes under 4 GiB). */
-int moe_grouped_gemm_fp8_fwd(const uint8_t* A, const float* a_scale_t, const uint8_t* B_fwd,
+int moe_grouped_gemm_fp8_fwd(const uint8_t* A, const float* a_scale_t, const uint8_t* B,
                              const float* b_scale_fwd, const int64_t* offsets, int32_t G,
                              int64_t M, int64_t K, int64_t N, int epilogue, void* C, void* H,
                              void* stream);

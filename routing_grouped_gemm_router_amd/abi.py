@@ -60,7 +60,7 @@ SIGNATURES = {
     "moe_unpermute_combine_bwd": (_int, [_p, _p, _int, _p, _p, _i64, _i64, _i32, _i64, _p, _p,
                                          _p]),
     "moe_quant_fp8_rows": (_int, [_p, _i64, _i64, _p, _p, _p]),
-    "moe_quant_fp8_weights": (_int, [_p, _i32, _i64, _i64, _p, _p, _p, _p, _p]),
+    "moe_quant_fp8_weights": (_int, [_p, _i32, _i64, _i64, _p, _p, _p, _p]),
     "moe_padded_rows_bound": (_i64, [_i64, _i32, _i32]),
     "moe_padded_offsets": (_int, [_p, _i32, _i64, _i32, _p, _p]),
     "moe_quant_fp8_token_tiles": (_int, [_p, _p, _p, _i32, _i64, _i64, _i64, _p, _p, _p]),
@@ -363,10 +363,10 @@ def moe_quant_fp8_rows(x, q, scale_t, stream=None):
     _call("moe_quant_fp8_rows", _ptr(x), M, K, _ptr(q), _ptr(scale_t), _stream(stream))
 
 
-def moe_quant_fp8_weights(w, q_fwd, s_fwd, q_dgrad, s_dgrad, stream=None):
+def moe_quant_fp8_weights(w, q, s_fwd, s_dgrad, stream=None):
     G, K, N = w.shape
-    _call("moe_quant_fp8_weights", _ptr(w), G, K, N, _ptr(q_fwd), _ptr(s_fwd), _ptr(q_dgrad),
-          _ptr(s_dgrad), _stream(stream))
+    _call("moe_quant_fp8_weights", _ptr(w), G, K, N, _ptr(q), _ptr(s_fwd), _ptr(s_dgrad),
+          _stream(stream))
 
 
 def moe_padded_rows_bound(M, G, align=128):
@@ -384,10 +384,11 @@ def moe_quant_fp8_token_tiles(x, offsets, padded, q_t, scale, stream=None):
           M, K, q_t.shape[1], _ptr(q_t), _ptr(scale), _stream(stream))
 
 
-def moe_grouped_gemm_fp8_fwd(A, a_scale_t, B_fwd, b_scale_fwd, offsets, C, H=None,
+def moe_grouped_gemm_fp8_fwd(A, a_scale_t, B, b_scale_fwd, offsets, C, H=None,
                              epilogue=EPI_NONE, stream=None):
-    G, N, K = B_fwd.shape
-    _call("moe_grouped_gemm_fp8_fwd", _ptr(A), _ptr(a_scale_t), _ptr(B_fwd), _ptr(b_scale_fwd),
+    # B: the weight codes in the weight's own layout [G, K, N]
+    G, K, N = B.shape
+    _call("moe_grouped_gemm_fp8_fwd", _ptr(A), _ptr(a_scale_t), _ptr(B), _ptr(b_scale_fwd),
           _ptr(offsets), G, A.shape[0], K, N, epilogue, _ptr(C), _ptr(H), _stream(stream))
 
 

@@ -42,11 +42,15 @@
 //    the ring slot just consumed and writes 16-byte vectors, 128 bytes per row.
 //  * Epilogues: SwiGLU (AB and H = silu(A) * B from the fp32 sums; a tile holds
 //    matching gate and up columns) and SwiGLU backward (dH -> dAB, reading AB).
-//  * fp8: every operand arrives k-contiguous (the quantizers write the layouts
-//    the GEMM wants), a k step is one 128-wide scale block, and each step's
-//    MFMA partial is promoted into the fp32 accumulator times the row scale of
-//    A and the row scale of B, both DMA'd into LDS with the stage.
-//  * MXFP8: the same operand path; each row's four E8M0 bytes of a stage (one
+//  * fp8: a k step is one 128-wide scale block.  Activations and gradients
+//    arrive k-contiguous; the weights keep ONE code array in their own [K, N]
+//    layout (a 128 x 128 block's scale serves both orientations), which the
+//    data gradient reads k-contiguous and the forward as [k][column] slabs
+//    through 8-bit transposing LDS reads.  Each step's MFMA partial is
+//    promoted into the fp32 accumulator times the row scale of A and the row
+//    scale of B, both DMA'd into LDS with the stage.
+//  * MXFP8: every operand k-contiguous (its weight scales run along k, so the
+//    weights keep one copy per orientation); each row's four E8M0 bytes of a stage (one
 //    per 32 k) arrive as one dword DMA'd like the fp8 scales, and every lane
 //    hands one block's byte to the MFMA, which applies both operands' scales
 //    itself: the partials go straight into the accumulator.
@@ -366,6 +370,11 @@ template <int MODE, bool F8> struct Layout {
   static constexpr bool A_KC = F8 || MODE != WGRAD;
   static constexpr bool B_KC = F8 || MODE == DGRAD || MODE == DGRAD_SWIGLU_BWD;
 };
+// blockwise fp8 forward: B is the weight's own code layout [Kc, Nout], read
+// in [k][column] slabs (MXFP8 keeps a k-contiguous copy: its scales run along k)
+template <int MODE, int Q> constexpr bool fp8_b_nc() {
+  return Q == P_FP8 && (MODE == FWD || MODE == FWD_SWIGLU);
+}
 
 // B-operand row of tile row rho (0..BN-1): the forward with SwiGLU pairs BN/2
 // gate columns with the matching BN/2 up columns, 32 + 32 per wave
@@ -468,7 +477,20 @@ __device__ __forceinline__ void setup_loader(const Params& p, const Tile& t, int
     L.va[i] = static_cast<uint32_t>(r * Kc * ES + c * 16);
   }
   L.da = 128;
-  if (Layout<MODE, F8>::B_KC) {
+  if (fp8_b_nc<MODE, Q>()) {
+    // B = W_g codes [Kc, Nout]: slab q / 16 holds k rows 8 (q % 16) .. + 7 of
+    // 128 columns, 128-byte rows with 16-byte chunks swizzled by k as in the
+    // [row][k] layout; a chunk is 16 consecutive product columns
+    const int64_t N = p.Nout;
+    L.rb = make_rsrc(p.B + static_cast<int64_t>(t.g) * Kc * N, static_cast<uint64_t>(Kc) * N);
+#pragma unroll
+    for (int i = 0; i < C::B_PER; ++i) {
+      const int q = wave * C::B_PER + i, slab = q >> 4;
+      const int kr = 8 * (q & 15) + (lane >> 3), c = (lane & 7) ^ swz_kc(kr);
+      L.vb[i] = static_cast<uint32_t>(kr * N + b_row<MODE, BN>(t, slab * 128 + 16 * c, fh));
+    }
+    L.db = static_cast<uint32_t>(128 * N);
+  } else if (Layout<MODE, F8>::B_KC) {
     // B rows (output columns) are k-contiguous: bf16 dgrad W_g [Nout, Kc];
     // fp8 forward W_g^T codes [Nout, Kc]; fp8 dgrad W_g codes [Nout, Kc]
     const char* bg = p.B + static_cast<int64_t>(t.g) * p.Nout * Kc * ES;
@@ -556,6 +578,28 @@ __device__ __forceinline__ i32x8_t frag_kc8(const LDS_AS char* op, int r, int c0
   return __builtin_bit_cast(i32x8_t, v);
 }
 
+// fp8 [k][col] layout (128-byte rows of 128 columns, chunks swizzled by k as
+// in the [row][k] layout): the 32 k codes k_base + 32 h .. + 31 of this lane's
+// column, as four transposing reads of 8 k rows x 16 columns.  In each group
+// of 16 lanes, lane j names row j / 2 and bytes 8 (j % 2) .. + 7 of the
+// group's 16 columns, and receives column j's 8 codes in row order (checked
+// with a one-wave probe of distinct byte values).
+__device__ __forceinline__ i32x8_t frag_nc8(const LDS_AS char* op, int col_base, int k_base,
+                                            int lane) {
+  typedef int32_t i32x2_t __attribute__((ext_vector_type(2)));
+  const int j = lane & 15;
+  const int cc = (col_base >> 4) + ((lane >> 4) & 1);
+  const int half = (j & 1) * 8;
+  i32x2_t v[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int k = k_base + (lane >> 5) * 32 + 8 * r + (j >> 1);
+    v[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (LDS_AS i32x2_t*)(op + k * 128 + ((cc ^ swz_kc(k)) << 4) + half));
+  }
+  return __builtin_bit_cast(i32x8_t, v);
+}
+
 // [k][col] layout: 8 k values (k0 .. k0+7 of this lane's half) of one column,
 // with two transpose reads of 4 k x 16 columns each
 __device__ __forceinline__ bf16x8_t frag_nc(const LDS_AS char* op, int col_base, int k_base,
@@ -604,6 +648,7 @@ __device__ __forceinline__ void compute_stage_bf16(f32x16_t (&acc)[2][2], const 
 // over the block).  One promotion per 128 k halves the vector-ALU work per
 // MFMA against promoting each 64-k half, and the first MFMA takes a zero
 // accumulator operand, so the partial needs no clearing.
+template <bool B_NC>
 __device__ __forceinline__ void compute_stage_fp8(f32x16_t (&acc)[2][2], const LDS_AS char* opA,
                                                   const LDS_AS char* opB, const LDS_AS float* sA,
                                                   int wm, int wn, int wnl, int lane) {
@@ -620,7 +665,8 @@ __device__ __forceinline__ void compute_stage_fp8(f32x16_t (&acc)[2][2], const L
       a[s][ii] = frag_kc8(opA, wm * 64 + ii * 32 + (lane & 31), 4 * s + 2 * h);
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
-      b[s][jj] = frag_kc8(opB, wnl * 64 + jj * 32 + (lane & 31), 4 * s + 2 * h);
+      b[s][jj] = B_NC ? frag_nc8(opB, wnl * 64 + jj * 32, 64 * s, lane)
+                      : frag_kc8(opB, wnl * 64 + jj * 32 + (lane & 31), 4 * s + 2 * h);
   }
   const f32x16_t zero = {};
 #pragma unroll
@@ -697,7 +743,7 @@ __device__ __forceinline__ void compute_stage(f32x16_t (&acc)[2][2], const LDS_A
                      (const LDS_AS uint32_t*)(stage + (1 + Cfg<WN>::B_SLABS) * OP_BYTES), wm, wn,
                      wn & 1, lane);
   else if (Q == P_FP8)
-    compute_stage_fp8(acc, opA, opB,
+    compute_stage_fp8<fp8_b_nc<MODE, Q>()>(acc, opA, opB,
                       (const LDS_AS float*)(stage + (1 + Cfg<WN>::B_SLABS) * OP_BYTES), wm, wn,
                       wn & 1, lane);
   else

@@ -131,8 +131,8 @@ hipError_t launch_gg_mx_wgrad(const uint8_t* At, const uint8_t* ea, const uint8_
 // quant.hip
 hipError_t launch_quant_rows(const void* x, int64_t M, int64_t K, uint8_t* q, float* sT,
                              hipStream_t s);
-hipError_t launch_quant_weights(const void* w, int G, int64_t K, int64_t N, uint8_t* qf, float* sf,
-                                uint8_t* qd, float* sd, hipStream_t s);
+hipError_t launch_quant_weights(const void* w, int G, int64_t K, int64_t N, uint8_t* q, float* sf,
+                                float* sd, hipStream_t s);
 hipError_t launch_padded_offsets(const int64_t* off, int G, int64_t M, int64_t align,
                                  int64_t* poff, hipStream_t s);
 hipError_t launch_quant_mx_rows(const void* x, int64_t x_rows, const int32_t* src,

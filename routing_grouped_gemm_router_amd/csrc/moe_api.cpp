@@ -75,7 +75,7 @@ const char* moe_status_string(int status) {
 
 const char* moe_last_error(void) { return g_err; }
 
-int moe_abi_version(void) { return 1; }
+int moe_abi_version(void) { return 2; }
 
 int moe_router_logits(const void* x, int x_dtype, const float* w_r, const float* logit_bias,
                       int64_t T, int64_t d, int32_t E, float* logits, void* stream) {
@@ -663,20 +663,17 @@ int moe_quant_fp8_rows(const void* x, int64_t M, int64_t K, uint8_t* q, float* s
   return hip_status(moe::launch_quant_rows(x, M, K, q, scale_t, as_stream(stream)), fn);
 }
 
-int moe_quant_fp8_weights(const void* w, int32_t G, int64_t K, int64_t N, uint8_t* q_fwd,
-                          float* s_fwd, uint8_t* q_dgrad, float* s_dgrad, void* stream) {
+int moe_quant_fp8_weights(const void* w, int32_t G, int64_t K, int64_t N, uint8_t* q,
+                          float* s_fwd, float* s_dgrad, void* stream) {
   const char* fn = "moe_quant_fp8_weights";
   REQUIRE(G >= 1 && K >= 1 && N >= 1, MOE_ERR_SHAPE, "%s: G=%d K=%lld N=%lld", fn, G,
           static_cast<long long>(K), static_cast<long long>(N));
   REQUIRE(K % 128 == 0 && N % 128 == 0, MOE_ERR_UNSUPPORTED, "%s: K and N must be multiples of 128",
           fn);
-  REQUIRE(w && q_fwd && s_fwd && q_dgrad && s_dgrad, MOE_ERR_NULL, "%s: all pointers are required",
-          fn);
-  REQUIRE(aligned16(w) && (reinterpret_cast<uintptr_t>(q_fwd) & 7u) == 0 &&
-              (reinterpret_cast<uintptr_t>(q_dgrad) & 7u) == 0,
-          MOE_ERR_UNSUPPORTED, "%s: alignment", fn);
-  return hip_status(moe::launch_quant_weights(w, G, K, N, q_fwd, s_fwd, q_dgrad, s_dgrad,
-                                              as_stream(stream)),
+  REQUIRE(w && q && s_fwd && s_dgrad, MOE_ERR_NULL, "%s: all pointers are required", fn);
+  REQUIRE(aligned16(w) && (reinterpret_cast<uintptr_t>(q) & 7u) == 0, MOE_ERR_UNSUPPORTED,
+          "%s: w must be 16-byte and q 8-byte aligned", fn);
+  return hip_status(moe::launch_quant_weights(w, G, K, N, q, s_fwd, s_dgrad, as_stream(stream)),
                     fn);
 }
 

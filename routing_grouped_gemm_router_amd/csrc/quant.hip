@@ -26,12 +26,13 @@
 // (the permutation's src_token), so that the permuted bf16 activations are
 // never written.
 //
-// Output layouts are chosen for the fp8 GEMM, which reads every operand
-// k-contiguous and every scale as a contiguous vector over a tile's rows:
+// Output layouts are chosen for the fp8 GEMM, which reads every scale as a
+// contiguous vector over a tile's rows and every operand k-contiguous except
+// the forward's weights (read transposed through LDS):
 //   rows         q [M, K],           scales [K/128, M]
-//   weights      qf [G, N, K] with sf [G, K/128, N]  (forward operand)
-//                qd [G, K, N] with sd [G, N/128, K]  (dgrad operand)
-//                (one 128 x 128 block scale, repeated along the block's rows)
+//   weights      q [G, K, N] (w's own layout, both GEMMs) with
+//                sf [G, K/128, N] (forward) and sd [G, N/128, K] (dgrad):
+//                one 128 x 128 block scale, repeated along the block's rows
 //   token tiles  qT [K, ldm],        scales [ldm/128, K], rows of group g at
 //                padded offsets poff[g] .. poff[g+1]-1
 #include "common.h"
@@ -108,14 +109,15 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const bf16_t* __restric
   }
 }
 
-// ---- 128 x 128 weight blocks, written in both operand layouts ----------------
+// ---- 128 x 128 weight blocks --------------------------------------------------
+// One code layout serves both GEMMs: the data gradient reads w's own layout
+// k-contiguous, the forward reads it transposed through LDS.  The block scale
+// is written expanded along each GEMM's output columns.
 __global__ __launch_bounds__(256) void quant_weights_kernel(const bf16_t* __restrict__ w, int G,
                                                             int64_t K, int64_t N,
-                                                            uint8_t* __restrict__ qf,
+                                                            uint8_t* __restrict__ q,
                                                             float* __restrict__ sf,
-                                                            uint8_t* __restrict__ qd,
                                                             float* __restrict__ sd) {
-  __shared__ uint8_t tile[128][128 + 8];
   __shared__ float red[4];
   const int64_t nkb = K / 128, nnb = N / 128;
   const int64_t blk = blockIdx.x;
@@ -123,12 +125,12 @@ __global__ __launch_bounds__(256) void quant_weights_kernel(const bf16_t* __rest
   const int64_t kb = (blk / nnb) % nkb, nb = blk % nnb;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int c8 = (t & 15) * 8, r8 = (t >> 4) * 8;  // 8 columns x 8 rows per thread
-  const bf16_t* src = w + (g * K + kb * 128) * N + nb * 128;
+  const int64_t base = (g * K + kb * 128) * N + nb * 128;
   float f[8][8];
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    unpack8(*reinterpret_cast<const uint4*>(src + (r8 + i) * N + c8), f[i]);
+    unpack8(*reinterpret_cast<const uint4*>(w + base + (r8 + i) * N + c8), f[i]);
 #pragma unroll
     for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[i][j]));
   }
@@ -139,29 +141,9 @@ __global__ __launch_bounds__(256) void quant_weights_kernel(const bf16_t* __rest
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   float scale, inv;
   block_scale(amax, scale, inv);
-  // dgrad layout: same as the input
-  uint8_t* dq = qd + (g * K + kb * 128) * N + nb * 128;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint2 c = encode8(f[i], inv);
-    *reinterpret_cast<uint2*>(dq + (r8 + i) * N + c8) = c;
-    *reinterpret_cast<uint2*>(&tile[r8 + i][c8]) = c;
-  }
-  __syncthreads();
-  // forward layout: transposed through LDS, row n holds 128 k codes
-  uint8_t* fq = qf + (g * N + nb * 128) * K + kb * 128;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int n = (t >> 4) * 8 + i;  // 0..127
-    const int k0 = (t & 15) * 8;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      lo |= static_cast<uint32_t>(tile[k0 + j][n]) << (8 * j);
-      hi |= static_cast<uint32_t>(tile[k0 + 4 + j][n]) << (8 * j);
-    }
-    *reinterpret_cast<uint2*>(fq + static_cast<int64_t>(n) * K + k0) = make_uint2(lo, hi);
-  }
+  for (int i = 0; i < 8; ++i)
+    *reinterpret_cast<uint2*>(q + base + (r8 + i) * N + c8) = encode8(f[i], inv);
   if (t < 128) {
     sf[(g * nkb + kb) * N + nb * 128 + t] = scale;
     sd[(g * nnb + nb) * K + kb * 128 + t] = scale;
@@ -520,12 +502,12 @@ hipError_t launch_quant_rows(const void* x, int64_t M, int64_t K, uint8_t* q, fl
   return hipGetLastError();
 }
 
-hipError_t launch_quant_weights(const void* w, int G, int64_t K, int64_t N, uint8_t* qf, float* sf,
-                                uint8_t* qd, float* sd, hipStream_t s) {
+hipError_t launch_quant_weights(const void* w, int G, int64_t K, int64_t N, uint8_t* q, float* sf,
+                                float* sd, hipStream_t s) {
   const int64_t blocks = static_cast<int64_t>(G) * (K / 128) * (N / 128);
   if (blocks == 0) return hipSuccess;
   quant_weights_kernel<<<dim3(static_cast<unsigned>(blocks)), 256, 0, s>>>(
-      static_cast<const bf16_t*>(w), G, K, N, qf, sf, qd, sd);
+      static_cast<const bf16_t*>(w), G, K, N, q, sf, sd);
   return hipGetLastError();
 }
 

@@ -204,12 +204,13 @@ class MoELayer:
                               dgrad=abi.moe_grouped_gemm_fp8_dgrad,
                               wgrad=abi.moe_grouped_gemm_fp8_wgrad)
 
-        def wq(G, K, Nn):  # both operand layouts of a [G, K, N] weight
+        def wq(G, K, Nn):  # the operands of a [G, K, N] weight in each GEMM
             if mx:  # E8M0 bytes per 32 along each layout's contraction axis
                 return dict(qf=u8(G, Nn, K), sf=u8(G, Nn, K // 32), qd=u8(G, K, Nn),
                             sd=u8(G, K, Nn // 32))
-            return dict(qf=u8(G, Nn, K), sf=f32(G, K // 128, Nn), qd=u8(G, K, Nn),
-                        sd=f32(G, Nn // 128, K))
+            # blockwise: one code array in the weight's own layout serves both
+            q = u8(G, K, Nn)
+            return dict(qf=q, sf=f32(G, K // 128, Nn), qd=q, sd=f32(G, Nn // 128, K))
 
         def rows(M, K):  # 1 x 128 row tiles (MX: 1 x 32 blocks)
             if mx:
@@ -259,7 +260,7 @@ class MoELayer:
         if self.mx:
             abi.moe_quant_mxfp8_weights(w, t["qf"], t["sf"], t["qd"], t["sd"])
         else:
-            abi.moe_quant_fp8_weights(w, t["qf"], t["sf"], t["qd"], t["sd"])
+            abi.moe_quant_fp8_weights(w, t["qd"], t["sf"], t["sd"])
 
     def _forward_lowp(self, x):
         c, w, q, gm = self.cfg, self.w, self.q, self._gemm

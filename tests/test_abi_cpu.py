@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    assert abi.moe_abi_version() == 1
+    assert abi.moe_abi_version() == 2
     for code in range(-6, 1):
         assert abi.moe_status_string(code)
     assert abi.moe_status_string(-99) == "unknown status"

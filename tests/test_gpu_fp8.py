@@ -49,15 +49,13 @@ def test_quant_rows_bit_exact(gpu, M, K):
 def test_quant_weights_bit_exact(gpu, G, K, N):
     w = _bf16_data((G, K, N), 2) * 0.05
     w[0, :128, :128] = 0.0
-    qf = torch.empty((G, N, K), dtype=torch.uint8, device=DEV)
+    q = torch.empty((G, K, N), dtype=torch.uint8, device=DEV)
     sf = torch.empty((G, K // 128, N), dtype=torch.float32, device=DEV)
-    qd = torch.empty((G, K, N), dtype=torch.uint8, device=DEV)
     sd = torch.empty((G, N // 128, K), dtype=torch.float32, device=DEV)
-    abi.moe_quant_fp8_weights(w.to(DEV), qf, sf, qd, sd)
+    abi.moe_quant_fp8_weights(w.to(DEV), q, sf, sd)
     for g in range(G):
         rq, rs = fp8.quantize_blocks(w[g].float().numpy())
-        np.testing.assert_array_equal(qd[g].cpu().numpy(), rq)
-        np.testing.assert_array_equal(qf[g].cpu().numpy(), rq.T)
+        np.testing.assert_array_equal(q[g].cpu().numpy(), rq)
         np.testing.assert_array_equal(sf[g].cpu().numpy(), np.repeat(rs, 128, axis=1))
         np.testing.assert_array_equal(sd[g].cpu().numpy(), np.repeat(rs.T, 128, axis=1))
 
@@ -80,14 +78,14 @@ def test_quant_token_tiles_bit_exact(gpu, M, G, K):
 
 
 def _oracle_weights(W):
-    """Oracle block codes of W [G, K, N] in the GEMM's two layouts."""
+    """Oracle block codes of W [G, K, N] (one layout, W's own, for both GEMMs)
+    and the block scale expanded along each GEMM's output columns."""
     qs = [fp8.quantize_blocks(W[g].float().numpy()) for g in range(W.shape[0])]
     deq = np.stack([fp8.dequantize_blocks(q, s) for q, s in qs])
-    qf = torch.from_numpy(np.stack([q.T for q, _ in qs]).copy())
+    q = torch.from_numpy(np.stack([q for q, _ in qs]).copy())
     sf = torch.from_numpy(np.stack([np.repeat(s, 128, axis=1) for _, s in qs]).copy())
-    qd = torch.from_numpy(np.stack([q for q, _ in qs]).copy())
     sd = torch.from_numpy(np.stack([np.repeat(s.T, 128, axis=1) for _, s in qs]).copy())
-    return deq, qf, sf, qd, sd
+    return deq, q, sf, sd
 
 
 def _oracle_rows(A):
@@ -96,7 +94,7 @@ def _oracle_rows(A):
 
 
 @pytest.mark.parametrize("M,G,K,N,swiglu", [(1000, 5, 256, 384, False), (2600, 8, 512, 512, True),
-                                             (129, 1, 128, 256, True)])
+                                             (129, 1, 128, 256, True), (700, 3, 256, 384, True)])
 def test_fp8_grouped_gemm_fwd_dgrad(gpu, M, G, K, N, swiglu):
     print(f"fp8 gemm M={M} G={G} K={K} N={N} swiglu={swiglu}", flush=True)
     off = inputs.random_segments(M, G, 7, empty_frac=0.2)
@@ -104,10 +102,10 @@ def test_fp8_grouped_gemm_fwd_dgrad(gpu, M, G, K, N, swiglu):
     A = _bf16_data((M, K), 8)
     W = (_bf16_data((G, K, N), 9) * K ** -0.5)
     Ad, Aq, As = _oracle_rows(A)
-    Wd, qf, sf, qd, sd = _oracle_weights(W)
+    Wd, qw, sf, sd = _oracle_weights(W)
     C = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
     H = torch.empty((M, N // 2), dtype=torch.bfloat16, device=DEV) if swiglu else None
-    abi.moe_grouped_gemm_fp8_fwd(Aq.to(DEV), As.to(DEV), qf.to(DEV), sf.to(DEV), off.to(DEV), C, H,
+    abi.moe_grouped_gemm_fp8_fwd(Aq.to(DEV), As.to(DEV), qw.to(DEV), sf.to(DEV), off.to(DEV), C, H,
                                  epilogue=abi.EPI_SWIGLU if swiglu else abi.EPI_NONE)
     ref = oracle.grouped_gemm_fwd(Ad, Wd, o)
     assert_close("C", C, ref, TOL["fp8"])
@@ -118,7 +116,7 @@ def test_fp8_grouped_gemm_fwd_dgrad(gpu, M, G, K, N, swiglu):
     dC = _bf16_data((M, N), 10)
     dCd, dCq, dCs = _oracle_rows(dC)
     dA = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
-    abi.moe_grouped_gemm_fp8_dgrad(dCq.to(DEV), dCs.to(DEV), qd.to(DEV), sd.to(DEV), off.to(DEV), dA)
+    abi.moe_grouped_gemm_fp8_dgrad(dCq.to(DEV), dCs.to(DEV), qw.to(DEV), sd.to(DEV), off.to(DEV), dA)
     refd = oracle.grouped_gemm_dgrad(dCd, Wd, o)
     assert_close("dA", dA, refd, TOL["fp8"])
     assert rel_small(dA, refd)
