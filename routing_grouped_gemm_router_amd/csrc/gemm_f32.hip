@@ -477,6 +477,120 @@ static hipError_t run_router_e(const void* A, int64_t lda, const float* B, int64
                                                                        N, K, bias, s);
 }
 
+// Logits for few experts (E <= 32, E % 4 == 0): a tile as wide as 64 experts
+// would leave most columns empty and the launch a few dozen workgroups.  Here
+// a workgroup takes 8 rows; 8 lanes of a wave share a row, and the 4 waves
+// split the row's 16-byte pieces: lane slice s of wave w reads the pieces
+// k = 8 s + 64 (w + 4 i) (8 consecutive x values), so that the 8 lanes of a
+// row read 128 contiguous bytes and every W_r value fetched from cache serves
+// 8 rows.  Each piece's 8 products per expert are summed and added to the
+// lane's running sum; the 8 lanes of a row are added in a fixed tree and the
+// 4 waves' sums in wave order: the result does not depend on scheduling.
+template <int EP, bool XF32, bool BIAS>
+__global__ __launch_bounds__(256) void router_narrow_kernel(const void* __restrict__ x,
+                                                            const float* __restrict__ w,
+                                                            const float* __restrict__ bias,
+                                                            float* __restrict__ out, int64_t T,
+                                                            int64_t d, int E) {
+  __shared__ float part_w[3][8][EP];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane >> 3, sl = lane & 7;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 8 + r;
+  const bool ok = row < T;
+  const int64_t xr = ok ? row : 0;
+  float acc[EP];
+#pragma unroll
+  for (int e = 0; e < EP; ++e) acc[e] = 0.f;
+#pragma unroll 2
+  for (int64_t k0 = sl * 8 + 64 * wave; k0 < d; k0 += 256) {
+    float xv[8];
+    if (XF32) {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + xr * d + k0);
+      const float4 a = p[0], b = p[1];
+      xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
+      xv[4] = b.x; xv[5] = b.y; xv[6] = b.z; xv[7] = b.w;
+    } else {
+      const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(x) + xr * d + k0);
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xv[2 * i] = __uint_as_float(u[i] << 16);
+        xv[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+      }
+    }
+    float part[EP];
+#pragma unroll
+    for (int e = 0; e < EP; ++e) part[e] = 0.f;
+    // the piece's W_r rows are fetched before any is used (half of them at a
+    // time for 32 expert slots), so that the loads are in flight together;
+    // slots past E repeat the last four experts (in bounds, no branch between
+    // the loads) and their sums are never stored
+    constexpr int RH = EP > 16 ? 4 : 8;  // W_r rows per batch
+#pragma unroll
+    for (int i0 = 0; i0 < 8; i0 += RH) {
+      float4 q[RH][EP / 4];
+#pragma unroll
+      for (int i = 0; i < RH; ++i)
+#pragma unroll
+        for (int e = 0; e < EP; e += 4)
+          q[i][e / 4] = *reinterpret_cast<const float4*>(w + (k0 + i0 + i) * E + min(e, E - 4));
+#pragma unroll
+      for (int i = 0; i < RH; ++i)
+#pragma unroll
+        for (int e = 0; e < EP; e += 4) {
+          const float xi = xv[i0 + i];
+          part[e] = fmaf(xi, q[i][e / 4].x, part[e]);
+          part[e + 1] = fmaf(xi, q[i][e / 4].y, part[e + 1]);
+          part[e + 2] = fmaf(xi, q[i][e / 4].z, part[e + 2]);
+          part[e + 3] = fmaf(xi, q[i][e / 4].w, part[e + 3]);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < EP; ++e) acc[e] += part[e];
+  }
+#pragma unroll
+  for (int e = 0; e < EP; ++e) {
+    float v = acc[e];
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    v += __shfl_xor(v, 4, 64);
+    acc[e] = v;
+  }
+  if (wave > 0 && sl == 0) {
+#pragma unroll
+    for (int e = 0; e < EP; ++e) part_w[wave - 1][r][e] = acc[e];
+  }
+  __syncthreads();
+  if (wave != 0 || !ok || sl != 0) return;
+#pragma unroll
+  for (int q = 0; q < 3; ++q)
+#pragma unroll
+    for (int e = 0; e < EP; ++e) acc[e] += part_w[q][r][e];
+#pragma unroll
+  for (int e = 0; e < EP; e += 4) {
+    if (e < E) {
+      float4 v = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+      if (BIAS) {
+        v.x += bias[e]; v.y += bias[e + 1]; v.z += bias[e + 2]; v.w += bias[e + 3];
+      }
+      *reinterpret_cast<float4*>(out + row * E + e) = v;
+    }
+  }
+}
+
+template <int EP, bool XF32>
+static hipError_t run_router_narrow(const void* x, const float* w, const float* bias, float* out,
+                                    int64_t T, int64_t d, int E, hipStream_t s) {
+  const int64_t blocks = (T + 7) / 8;
+  if (bias)
+    router_narrow_kernel<EP, XF32, true><<<dim3(static_cast<unsigned>(blocks)), 256, 0, s>>>(
+        x, w, bias, out, T, d, E);
+  else
+    router_narrow_kernel<EP, XF32, false><<<dim3(static_cast<unsigned>(blocks)), 256, 0, s>>>(
+        x, w, bias, out, T, d, E);
+  return hipGetLastError();
+}
+
 static bool aligned16p(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 template <typename TA, bool A_MC, bool B_KC, int GRP, int EPI, typename TC>
@@ -503,6 +617,16 @@ hipError_t launch_router_fwd(const void* x, int x_dtype, const float* w_r, const
   if (T == 0) return hipSuccess;
   if (d % 8 == 0 && E % 4 == 0 && aligned16p(x) && aligned16p(w_r) && aligned16p(logits)) {
     // logits [T, E] = x [T, d] . W_r [d, E] (+ bias)
+    if (E <= 32) {
+      if (E <= 8)
+        return x_dtype == 0 ? run_router_narrow<8, true>(x, w_r, bias, logits, T, d, E, s)
+                            : run_router_narrow<8, false>(x, w_r, bias, logits, T, d, E, s);
+      if (E <= 16)
+        return x_dtype == 0 ? run_router_narrow<16, true>(x, w_r, bias, logits, T, d, E, s)
+                            : run_router_narrow<16, false>(x, w_r, bias, logits, T, d, E, s);
+      return x_dtype == 0 ? run_router_narrow<32, true>(x, w_r, bias, logits, T, d, E, s)
+                          : run_router_narrow<32, false>(x, w_r, bias, logits, T, d, E, s);
+    }
     if (x_dtype == 0)
       return bias ? run_router_e<8, 4, RA_KC_F32, RB_NC, true>(x, d, w_r, E, logits, E, T, E, d,
                                                                bias, s)

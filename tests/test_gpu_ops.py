@@ -347,11 +347,14 @@ def test_grouped_gemm_swiglu_epilogues(gpu, dt, M, G, d, f, tile_fwd, tile_dgrad
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("T,d,E,bias", [(64, 128, 4, False), (1000, 4096, 128, True),
                                         (515, 7168, 256, True), (300, 1000, 8, True),
-                                        (77, 40, 6, True), (129, 4096, 64, False)])
+                                        (77, 40, 6, True), (129, 4096, 64, False),
+                                        (257, 4096, 16, True), (130, 2048, 20, False),
+                                        (1025, 4096, 32, True), (40, 7168, 12, True)])
 def test_router_logits(gpu, dt, T, d, E, bias):
     """The router's fp32 vector-ALU products against the fp64 oracle: each of
-    the three tile widths (E up to 64, 128, 256), ragged token, contraction
-    and column tiles, and the generic path (E % 4 != 0)."""
+    the three tile widths (E up to 64, 128, 256), the narrow forward for E up
+    to 32 (8, 16 and 32 expert slots, partly filled at E = 4, 12, 20), ragged
+    token, contraction and column tiles, and the generic path (E % 4 != 0)."""
     tdt = torch.float32 if dt == "f32" else torch.bfloat16
     x = inputs.normal((T, d), 1.0, 61, 0, "cpu", tdt)
     w_r = inputs.normal((d, E), d ** -0.5, 62, 0, "cpu", torch.float32)
@@ -403,12 +406,14 @@ def test_router_bwd_on_chosen_experts(gpu, dt, T, d, E, k, score, renorm):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_router_fp32_accuracy(gpu, dt):
+@pytest.mark.parametrize("E", [64, 8])
+def test_router_fp32_accuracy(gpu, dt, E):
     """The router products carry fp32 accuracy: operands whose 24 mantissa
     bits all matter (a spread of magnitudes, values just off bf16 rounding
     boundaries) come out within a few fp32 roundings of the fp64 products --
-    any product rounded through bf16 would be off by ~2^-9."""
-    T, d, E = 256, 1024, 64
+    any product rounded through bf16 would be off by ~2^-9.  E = 8 takes the
+    narrow forward."""
+    T, d = 256, 1024
     g = torch.Generator().manual_seed(71)
     mag = torch.exp2(torch.randint(-8, 9, (d, E), generator=g).float())
     frac = 1.0 + torch.rand((d, E), generator=g) * 2.0 ** -7 + torch.rand((d, E), generator=g) * 2.0 ** -16
