@@ -62,7 +62,7 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_work(cfg, n_nonempty, gated=False, n_rows=None):
+def kernel_work(cfg, n_nonempty, gated=False, n_rows=None, sparse_router_bwd=False):
     """Algorithmic FLOPs and HBM bytes per call of every span.
 
     FLOPs: 2 per multiply-add over the routed rows only: the (token, slot)
@@ -70,7 +70,10 @@ def kernel_work(cfg, n_nonempty, gated=False, n_rows=None):
     a capacity, whose padding rows are not counted).  Bytes: every operand
     read once and every result written once; an expert's weights count once
     per GEMM pass when the expert received rows; index and routing-weight
-    arrays included."""
+    arrays included.  With sparse_router_bwd (d_logits zero outside each
+    token's k chosen experts, as the layer's renormalised or sigmoid routing
+    without the auxiliary loss gives) the router's backward products count
+    the T * k chosen entries only: the others are exact zeros."""
     T, d, E, k, f, fs = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.fs
     N = T * k if n_rows is None else n_rows
     s = 2 if cfg.dtype == "bf16" else 4      # activation / weight element bytes
@@ -92,7 +95,9 @@ def kernel_work(cfg, n_nonempty, gated=False, n_rows=None):
         "route_topk_bwd": (0.0, T * E * 4 * 2 + 3 * idx),
         "expert_bias_update": (0.0, E * 4 * 3),
         "swiglu_recompute": (0.0, N * 2 * f * s + N * f * s),
-        "router_logits_bwd": (4.0 * T * d * E, T * d * s + T * E * 4 + d * E * 4 * 2 + T * d * 4),
+        "router_logits_bwd": ((4.0 * T * k * d, T * d * s + 3 * idx + N * 4 + d * E * 4 * 2 + T * d * 4)
+                              if sparse_router_bwd else
+                              (4.0 * T * d * E, T * d * s + T * E * 4 + d * E * 4 * 2 + T * d * 4)),
         "permute_bwd": (0.0, N * d * s + idx + T * d * (s + 4 + (s if fs else 0))),
     }
     if cfg.gemm in ("fp8", "mxfp8"):
@@ -367,7 +372,8 @@ def main():
     counts = layer.counts.cpu()
     n_nonempty = int((counts > 0).sum())
     n_rows = int(counts.sum())  # (token, slot) pairs with a row: T * k unless dropped
-    work = kernel_work(cfg, n_nonempty, gated=args.gate_in_ffn, n_rows=n_rows)
+    work = kernel_work(cfg, n_nonempty, gated=args.gate_in_ffn, n_rows=n_rows,
+                       sparse_router_bwd=layer.sparse_dz)
     kernels = {}
     for name, (ms, n) in spans.items():
         fl, by = work[name]
@@ -430,6 +436,7 @@ def main():
         "config": {"workload": cfg.name, "routing": cfg.routing,
                    "expert_bias": cfg.expert_bias_std > 0,
                    "recompute_act": bool(args.recompute_act), "gate_in_ffn": bool(args.gate_in_ffn),
+                   "router_bwd": "chosen experts" if layer.sparse_dz else "dense",
                    "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
                    "ffn": cfg.f, "shared_ffn": cfg.fs, "score": cfg.score, "renorm": cfg.renorm,
                    "router_bias": cfg.bias, "experts_with_rows": n_nonempty,
