@@ -1143,9 +1143,9 @@ static hipError_t run_rows(const Params& p, hipStream_t s) {
 // 256 (no ragged output dimension, so the larger tile wastes nothing): 8 waves
 // in a 4 x 2 arrangement, each 64 x 128 (2 x 4 MFMA 32x32 blocks), a 2-stage
 // ring of 64 KiB operand stages.  bf16: A is 64 tokens x 256 columns, B the
-// same, both in the [k][col] layout read with ds_read_b64_tr_b16.  fp8 / MX:
+// same, both in the [k][col] layout read with ds_read_b64_tr_b16.  MXFP8:
 // the transposed token tiles, 256 rows x 128 tokens each in the [row][k]
-// layout, plus one scale (fp32) or E8M0 dword per row and stage.  Against the
+// layout, plus one E8M0 dword per row and stage.  Against the
 // 128 x 256 tile this halves the per-tile work of decoding, loader set-up and
 // epilogue synchronisation per FLOP (a group's token range is short, so a
 // tile is a few k steps), reads a quarter fewer LDS fragments per MFMA, and
@@ -1167,6 +1167,9 @@ __device__ __forceinline__ int stg_off16(int m, int chunk) {
 template <int Q>
 __global__ __launch_bounds__(512, 1) void wgrad256_kernel(Params p) {
   using namespace w256;
+  // blockwise fp8 keeps the 128-row tiles: its promotion of each partial by
+  // two scales on the vector ALUs takes as long as the MFMAs in this tiling
+  static_assert(Q != P_FP8, "bf16 and MXFP8 only");
   constexpr bool F8 = Q != P_BF16;
   constexpr int STAGE = stage_bytes<Q>();
   __shared__ __attribute__((aligned(1024))) char ring[STAGES * STAGE];
@@ -1220,8 +1223,8 @@ __global__ __launch_bounds__(512, 1) void wgrad256_kernel(Params p) {
   };
   // loader of a tile: DMA instruction q = wave * 4 + i of each operand fills
   // 1 KiB of slab q / 16 -- bf16: k rows 4 (q % 16) .. + 3 (256 bytes each);
-  // fp8: rows 8 (q % 16) .. + 7 (128 bytes each) -- and, fp8 / MX, one scale
-  // word per row: waves 0-3 the 256 rows of A, waves 4-7 those of B
+  // MXFP8: rows 8 (q % 16) .. + 7 (128 bytes each) -- and, MXFP8, one E8M0
+  // dword per row: waves 0-3 the 256 rows of A, waves 4-7 those of B
   i32x4_t ra, rb, rs;
   uint32_t va[4], vb[4], vs = 0, ds = 0;
   const int64_t ldm = p.ldm;
@@ -1252,16 +1255,10 @@ __global__ __launch_bounds__(512, 1) void wgrad256_kernel(Params p) {
     }
     const bool for_a = wave < 4;
     const int64_t row = (for_a ? t.row0 : t.col0) + (wave & 3) * 64 + lane;
-    if (Q == P_MX) {  // E8M0 [K][ldm/32] / [N][ldm/32]: dword lo/128 + kt of each row
-      rs = make_rsrc(for_a ? p.ea : p.eb, static_cast<uint64_t>(for_a ? K : N) * (ldm / 32));
-      vs = static_cast<uint32_t>(row * (ldm / 32) + t.lo / 32);
-      ds = 4;
-    } else {  // fp32 [ldm/128][K] / [ldm/128][N]: block lo/128 + kt
-      const int64_t W = for_a ? K : N;
-      rs = make_rsrc(for_a ? p.sa : p.sb, static_cast<uint64_t>(ldm / 128) * W * 4);
-      vs = static_cast<uint32_t>(((t.lo / 128) * W + row) * 4);
-      ds = static_cast<uint32_t>(W * 4);
-    }
+    // E8M0 [K][ldm/32] / [N][ldm/32]: dword lo/128 + kt of each row
+    rs = make_rsrc(for_a ? p.ea : p.eb, static_cast<uint64_t>(for_a ? K : N) * (ldm / 32));
+    vs = static_cast<uint32_t>(row * (ldm / 32) + t.lo / 32);
+    ds = 4;
   };
   const uint32_t da = F8 ? 128u : static_cast<uint32_t>(64 * K * 2);
   const uint32_t db = F8 ? 128u : static_cast<uint32_t>(64 * N * 2);
@@ -1366,42 +1363,6 @@ __global__ __launch_bounds__(512, 1) void wgrad256_kernel(Params p) {
               acc[ii][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                   b[jj], a[ii], acc[ii][jj], 0, 0, 0, static_cast<int>(xb[jj] >> (16 * s2)), 0,
                   static_cast<int>(xa[ii] >> (16 * s2)));
-        }
-      } else {
-        // fp8 with fp32 scales: each 64-k MFMA partial promoted into the
-        // accumulator times the row scale of A and the column scale of B
-        const LDS_AS float* sA = (const LDS_AS float*)(stage + OPS);
-        const LDS_AS float* sB = sA + 256;
-        const int h = lane >> 5;
-        float sa[2];
-#pragma unroll
-        for (int ii = 0; ii < 2; ++ii) sa[ii] = sA[wm * 64 + ii * 32 + (lane & 31)];
-#pragma unroll 1
-        for (int s2 = 0; s2 < 2; ++s2) {
-          i32x8_t a[2];
-#pragma unroll
-          for (int ii = 0; ii < 2; ++ii) a[ii] = frag_kc8(opA, ra0 + ii * 32 + (lane & 31), 4 * s2 + 2 * h);
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const i32x8_t b = frag_kc8(opB, jj * 32 + (lane & 31), 4 * s2 + 2 * h);
-            f32x4 sb[4];
-#pragma unroll
-            for (int vg = 0; vg < 4; ++vg)
-              sb[vg] = *(const LDS_AS f32x4*)(sB + wn * 128 + jj * 32 + vg * 8 + h * 4);
-#pragma unroll
-            for (int ii = 0; ii < 2; ++ii) {
-              f32x16_t part;
-#pragma unroll
-              for (int v = 0; v < 16; ++v) part[v] = 0.f;
-              part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a[ii], part, 0, 0, 0, 127, 0,
-                                                                     127);
-#pragma unroll
-              for (int vg = 0; vg < 4; ++vg)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                  acc[ii][jj][vg * 4 + e] += part[vg * 4 + e] * (sa[ii] * sb[vg][e]);
-            }
-          }
         }
       }
     }
@@ -1890,8 +1851,9 @@ static bool launch_rows256(const Params& p, hipStream_t s, hipError_t& err) {
 
 template <int Q>
 static hipError_t run_wgrad(const Params& p, hipStream_t s) {
-  // (fp8 with fp32 scales keeps the 128-row tiles: its VALU promotion needs
-  // a whole extra accumulator block live, more registers than a wave has)
+  // (blockwise fp8 keeps the 128-row tiles: in the 256 x 256 tiling its
+  // promotion of each partial on the vector ALUs takes as long as the MFMAs,
+  // and the weight gradients measured 1.4 times slower)
   if (Q != P_FP8 && p.Kc % w256::BMN == 0 && p.Nout % w256::BMN == 0) {
     const int64_t tiles = static_cast<int64_t>(p.G) * (p.Kc / w256::BMN) * (p.Nout / w256::BMN);
     if (tiles <= 0) return hipSuccess;
