@@ -132,8 +132,9 @@ def fp8_work(cfg, n_nonempty, mx=False, n_rows=None):
     32 (MXFP8); weights are re-quantized every step (they change every step),
     blockwise to one code array in the weight's own layout (the forward reads
     it transposed) with the block scale expanded for each GEMM, MXFP8 to two
-    copies (E8M0 scales along each GEMM's reduction); GEMM outputs are bf16.  MXFP8 gathers x through the permutation inside its quantizers (x
-    read once, the row map read, no permuted bf16 copy)."""
+    copies (E8M0 scales along each GEMM's reduction); GEMM outputs are bf16.
+    MXFP8 fuses the permutation into its quantizers of x (x read once, the
+    row map read, no permuted bf16 copy)."""
     T, d, E, k, f, fs = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.fs
     N = T * k if n_rows is None else n_rows
 

@@ -472,6 +472,21 @@ int moe_permute_quant_mxfp8(const void* x, int64_t T, int64_t K, const int32_t* 
                             const int64_t* offsets, int32_t G, int64_t M, uint8_t* q,
                             uint8_t* scale, void* stream);
 
+/* The same dispatch driven from the token side (section 2, Dispatch): each
+ * token of x [T, K] is read and quantized once, and its codes and scale bytes
+ * are written to every row dst_row[t k + j] (dst_row [T, k] int32, the map of
+ * moe_route_topk / moe_apply_capacity) that lies in [0, min(M, offsets[G])).
+ * A slot whose row is outside that range (a dropped slot, -1) is skipped, and
+ * rows named by no slot are not written: on a map where every row below
+ * offsets[G] has exactly one slot (dropless, or capacity-limited) the result
+ * equals moe_permute_quant_mxfp8's byte for byte, while reading x once
+ * instead of k times.  A map with padding rows (moe_pad_to_max) needs
+ * moe_permute_quant_mxfp8, which writes them as zero rows.  q [M, K] and
+ * scale [M, K/32] out. */
+int moe_scatter_quant_mxfp8(const void* x, int64_t T, int64_t K, const int32_t* dst_row,
+                            int32_t k, const int64_t* offsets, int32_t G, int64_t M, uint8_t* q,
+                            uint8_t* scale, void* stream);
+
 /* Both GEMM operand layouts of w [G, K, N], each blocked along the axis its
  * GEMM contracts:
  *   q_fwd [G, N, K] (transposed) with s_fwd [G, N, K/32]  (blocks along K)

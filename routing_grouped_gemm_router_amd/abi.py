@@ -83,6 +83,7 @@ SIGNATURES = {
     "moe_zero_unmapped_rows": (_int, [_p, _int, _p, _i64, _i64, _p]),
     "moe_quant_mxfp8_rows": (_int, [_p, _i64, _i64, _p, _p, _p]),
     "moe_permute_quant_mxfp8": (_int, [_p, _i64, _i64, _p, _p, _i32, _i64, _p, _p, _p]),
+    "moe_scatter_quant_mxfp8": (_int, [_p, _i64, _i64, _p, _i32, _p, _i32, _i64, _p, _p, _p]),
     "moe_quant_mxfp8_weights": (_int, [_p, _i32, _i64, _i64, _p, _p, _p, _p, _p]),
     "moe_quant_mxfp8_token_tiles": (_int, [_p, _i64, _p, _p, _p, _i32, _i64, _i64, _i64, _p, _p,
                                            _p]),
@@ -419,6 +420,12 @@ def moe_permute_quant_mxfp8(x, src_token, offsets, q, scale, stream=None):
     T, K = x.shape
     _call("moe_permute_quant_mxfp8", _ptr(x), T, K, _ptr(src_token), _ptr(offsets),
           offsets.numel() - 1, q.shape[0], _ptr(q), _ptr(scale), _stream(stream))
+
+
+def moe_scatter_quant_mxfp8(x, dst_row, offsets, q, scale, stream=None):
+    T, K = x.shape
+    _call("moe_scatter_quant_mxfp8", _ptr(x), T, K, _ptr(dst_row), dst_row.shape[1],
+          _ptr(offsets), offsets.numel() - 1, q.shape[0], _ptr(q), _ptr(scale), _stream(stream))
 
 
 def moe_quant_mxfp8_weights(w, q_fwd, s_fwd, q_dgrad, s_dgrad, stream=None):

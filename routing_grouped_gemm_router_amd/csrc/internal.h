@@ -138,6 +138,9 @@ hipError_t launch_padded_offsets(const int64_t* off, int G, int64_t M, int64_t a
 hipError_t launch_quant_mx_rows(const void* x, int64_t x_rows, const int32_t* src,
                                 const int64_t* rows_end, int64_t M, int64_t K, uint8_t* q,
                                 uint8_t* e, hipStream_t s);
+hipError_t launch_quant_mx_scatter(const void* x, int64_t T, int64_t K, const int32_t* dst_row,
+                                   int k, const int64_t* rows_end, int64_t M, uint8_t* q,
+                                   uint8_t* e, hipStream_t s);
 hipError_t launch_quant_mx_weights(const void* w, int G, int64_t K, int64_t N, uint8_t* qf,
                                    uint8_t* ef, uint8_t* qd, uint8_t* ed, hipStream_t s);
 hipError_t launch_quant_mx_token_tiles(const void* x, int64_t x_rows, const int32_t* src,

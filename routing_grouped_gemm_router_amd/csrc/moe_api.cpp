@@ -823,6 +823,22 @@ int moe_permute_quant_mxfp8(const void* x, int64_t T, int64_t K, const int32_t* 
                     fn);
 }
 
+int moe_scatter_quant_mxfp8(const void* x, int64_t T, int64_t K, const int32_t* dst_row,
+                            int32_t k, const int64_t* offsets, int32_t G, int64_t M, uint8_t* q,
+                            uint8_t* scale, void* stream) {
+  const char* fn = "moe_scatter_quant_mxfp8";
+  REQUIRE(T >= 0 && K >= 1 && k >= 1 && G >= 1 && M >= 0, MOE_ERR_SHAPE,
+          "%s: T=%lld K=%lld k=%d G=%d M=%lld", fn, static_cast<long long>(T),
+          static_cast<long long>(K), k, G, static_cast<long long>(M));
+  REQUIRE(K % 128 == 0, MOE_ERR_UNSUPPORTED, "%s: K %% 128 != 0", fn);
+  if (T == 0 || M == 0) return ok();
+  REQUIRE(x && dst_row && offsets && q && scale, MOE_ERR_NULL, "%s: pointers are required", fn);
+  REQUIRE(aligned16(x) && aligned8(q) && aligned4(scale), MOE_ERR_UNSUPPORTED, "%s: alignment", fn);
+  return hip_status(moe::launch_quant_mx_scatter(x, T, K, dst_row, k, offsets + G, M, q, scale,
+                                                 as_stream(stream)),
+                    fn);
+}
+
 int moe_quant_mxfp8_weights(const void* w, int32_t G, int64_t K, int64_t N, uint8_t* q_fwd,
                             uint8_t* s_fwd, uint8_t* q_dgrad, uint8_t* s_dgrad, void* stream) {
   const char* fn = "moe_quant_mxfp8_weights";

@@ -272,7 +272,10 @@ class MoELayer:
                 self._qweights("ws2", self.ws2)
         if self.mx:
             with self._span("permute_quant_x"):
-                abi.moe_permute_quant_mxfp8(x, self.src_token, self.offsets, q["x"]["q"],
+                # every row below offsets[E] has exactly one slot (no padding
+                # rows: pad-to-max is bf16 / fp32 only), so the token-side
+                # scatter gives the gather's bytes with one read of x
+                abi.moe_scatter_quant_mxfp8(x, self.dst_row, self.offsets, q["x"]["q"],
                                             q["x"]["s"])
                 xq, xs = q["x"]["q"], q["x"]["s"]
         else:

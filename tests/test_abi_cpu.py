@@ -113,6 +113,9 @@ VALIDATION_CASES = [
     (("moe_expert_bias_update", (None, 2000, 0.001, None, None)), -4),
     (("moe_quant_mxfp8_rows", (None, 10, 100, None, None, None)), -4),
     (("moe_permute_quant_mxfp8", (None, 10, 128, None, None, 4, 40, None, None, None)), -1),
+    (("moe_scatter_quant_mxfp8", (None, 10, 128, None, 2, None, 4, 40, None, None, None)), -1),
+    (("moe_scatter_quant_mxfp8", (None, 10, 100, None, 2, None, 4, 40, None, None, None)), -4),
+    (("moe_scatter_quant_mxfp8", (None, 10, 128, None, 0, None, 4, 40, None, None, None)), -2),
     (("moe_quant_mxfp8_token_tiles", (None, 10, None, None, None, 4, 20, 128, 128, None, None,
                                       None)), -2),
     (("moe_grouped_gemm_mxfp8_fwd", (None, None, None, None, None, 4, 10, 100, 128, 0, None, None,

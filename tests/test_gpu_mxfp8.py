@@ -79,6 +79,31 @@ def test_mx_permute_quant_bit_exact(gpu, T, K, G, M):
     assert (q[end:].cpu() == 0xAA).all() and (s[end:].cpu() == 0xAA).all()
 
 
+@pytest.mark.parametrize("T,K,k,G", [(200, 256, 3, 6), (1000, 7168, 8, 16), (77, 128, 1, 1)])
+def test_mx_scatter_quant_bit_exact(gpu, T, K, k, G):
+    """Token-side dispatch: every kept slot's row holds the quantization of its
+    token; dropped slots (-1) and slots past offsets[G] write nothing, so rows
+    at and past offsets[G] are left alone."""
+    x = _bf16_data((T, K), 4, special=True)
+    gen = torch.Generator().manual_seed(5)
+    keep = torch.rand(T * k, generator=gen) > 0.1
+    kept = int(keep.sum())
+    rows = torch.full((T * k,), -1, dtype=torch.int32)
+    rows[keep] = torch.randperm(kept, generator=gen).to(torch.int32)
+    end = kept - 9                                  # 9 kept slots past the last group
+    off = inputs.random_segments(end, G, 6, empty_frac=0.2)
+    M = kept + 20
+    q, s = _u8(M, K), _u8(M, K // 32)
+    abi.moe_scatter_quant_mxfp8(x.to(DEV), rows.view(T, k).to(DEV), off.to(DEV), q, s)
+    src = torch.zeros(end, dtype=torch.long)
+    live = keep & (rows < end)
+    src[rows[live].long()] = torch.arange(T * k)[live] // k
+    rq, rs = fp8.quantize_mx_rows(x[src].float().numpy())
+    np.testing.assert_array_equal(q[:end].cpu().numpy(), rq)
+    np.testing.assert_array_equal(s[:end].cpu().numpy(), rs)
+    assert (q[end:].cpu() == 0xAA).all() and (s[end:].cpu() == 0xAA).all()
+
+
 @pytest.mark.parametrize("G,K,N", [(3, 256, 384), (2, 7168, 256)])
 def test_mx_quant_weights_bit_exact(gpu, G, K, N):
     w = _bf16_data((G, K, N), 2, special=True) * 0.05
