@@ -59,7 +59,71 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only copy BYTES once device to device (the reference that scales the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--vendor-grouped-mm", action="store_true",
+                    help="only time torch._grouped_mm (the vendor grouped GEMM) beside this "
+                         "library's bf16 grouped GEMMs (plain epilogue) on the layer's own "
+                         "routing of --config, print one JSON line and exit")
     return ap.parse_args()
+
+
+def vendor_grouped_mm(cfg, seed, reps=5):
+    """GEMM 1's three products (forward, data and weight gradient) on the
+    routed rows of one forward, by this library and by torch._grouped_mm,
+    HIP-event timed (median of `reps` after 2 warm-ups), with the largest
+    difference between the two results relative to the largest magnitude."""
+    import torch
+    from routing_grouped_gemm_router_amd import abi, inputs
+    from routing_grouped_gemm_router_amd.layer import MoELayer
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return sorted(ts)[len(ts) // 2]
+
+    inp = inputs.layer_inputs(cfg, seed, "cuda")
+    layer = MoELayer(cfg, inp, "cuda")
+    layer.forward(inp["x"])
+    torch.cuda.synchronize()
+    off, A, W = layer.offsets, layer.x_perm, layer.w["w13"]  # A [N, d], W [E, d, 2f]
+    N, d, E, f2 = A.shape[0], cfg.d, cfg.E, 2 * cfg.f
+    ends = off[1:].to(torch.int32).contiguous()
+    flops = 2.0 * N * d * f2
+    g = torch.Generator(device="cuda").manual_seed(seed + 1)
+    dC = torch.randn(N, f2, device="cuda", generator=g).to(torch.bfloat16)
+    C = torch.empty(N, f2, dtype=torch.bfloat16, device="cuda")
+    dA = torch.empty(N, d, dtype=torch.bfloat16, device="cuda")
+    dW = torch.empty(E, d, f2, dtype=torch.bfloat16, device="cuda")
+    WT = W.transpose(1, 2).contiguous()  # both libraries get contiguous operands
+    AT = A.t().contiguous()
+    cases = {
+        "fwd": (lambda: abi.moe_grouped_gemm_fwd(A, W, off, C), C,
+                lambda: torch._grouped_mm(A, W, offs=ends)),
+        "dgrad": (lambda: abi.moe_grouped_gemm_dgrad(dC, W, off, dA), dA,
+                  lambda: torch._grouped_mm(dC, WT, offs=ends)),
+        "wgrad": (lambda: abi.moe_grouped_gemm_wgrad(A, dC, off, dW), dW,
+                  lambda: torch._grouped_mm(AT, dC, offs=ends)),
+    }
+    rec = {"workload": cfg.name, "rows": N, "d": d, "E": E, "2f": f2}
+    for name, (ours, out, vendor) in cases.items():
+        t = timed(ours)
+        rec[f"{name}_ms"] = round(t, 3)
+        rec[f"{name}_TFLOP/s"] = round(flops / t / 1e9, 1)
+        ref = vendor()
+        torch.cuda.synchronize()
+        rec[f"{name}_rel_diff"] = float((out.float() - ref.float()).abs().max()
+                                        / ref.float().abs().max())
+        t = timed(vendor)
+        rec[f"vendor_{name}_ms"] = round(t, 3)
+        rec[f"vendor_{name}_TFLOP/s"] = round(flops / t / 1e9, 1)
+    return rec
 
 
 def kernel_work(cfg, n_nonempty, gated=False, n_rows=None, sparse_router_bwd=False):
@@ -343,6 +407,12 @@ def main():
         return 0
 
     cfg = inputs.CONFIGS[args.config]
+    if args.vendor_grouped_mm:
+        if cfg.gemm != "bf16":
+            print(f"{cfg.name}: the vendor comparison runs the bf16 layers", file=sys.stderr)
+            return 2
+        print(json.dumps(vendor_grouped_mm(cfg, args.seed)), flush=True)
+        return 0
     if cfg.gemm not in ("bf16", "fp8", "mxfp8"):
         print(f"{cfg.name}: bench.py times the bf16, fp8 and mxfp8 expert paths", file=sys.stderr)
         return 2
