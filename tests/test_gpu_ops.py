@@ -376,7 +376,9 @@ def test_router_logits(gpu, dt, T, d, E, bias):
 @pytest.mark.parametrize("T,d,E,k,score,renorm", [(515, 7168, 256, 8, "sigmoid", True),
                                                   (300, 1000, 8, 2, "softmax", True),
                                                   (77, 128, 64, 4, "sigmoid", False),
-                                                  (1, 256, 4, 2, "softmax", True)])
+                                                  (1, 256, 4, 2, "softmax", True),
+                                                  (1100, 320, 64, 6, "sigmoid", True),
+                                                  (130, 256, 128, 16, "softmax", True)])
 def test_router_bwd_on_chosen_experts(gpu, dt, T, d, E, k, score, renorm):
     """moe_router_logits_bwd_topk (reading d_logits only at each token's chosen
     experts) against the oracle's dense products, and against the dense GPU
