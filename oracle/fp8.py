@@ -181,7 +181,7 @@ def dequantize_token_tiles(q, s, block=128):
 
 
 def layer_fp8(x, w_r, w13, w2, dout, k, score, renorm, logit_bias=None, shared=None,
-              quantize=True, block=128, recipe="block", trace=None, z=None):
+              quantize=True, block=128, recipe="block", trace=None, z=None, capacity=None):
     """Forward and backward of the MoE layer with every expert-GEMM input
     quantized blockwise to E4M3 (the fp8 recipe above), computed as fp64
     grouped GEMMs on the dequantized values.
@@ -202,6 +202,9 @@ def layer_fp8(x, w_r, w13, w2, dout, k, score, renorm, logit_bias=None, shared=N
     tensors they were quantized from ("src.<name>") and the padded offsets;
     recording changes nothing that is computed.  ``z`` may give the fp32 keys
     directly (by default they are computed with ``router_logits``).
+    ``capacity`` drops what exceeds it (``apply_capacity``, the capacity-limited
+    dropping of section 7, Load Balancing): a dropped (token, slot) pair has no
+    row, adds nothing to the output and gets no gradient.
     """
     from . import moe_oracle as o
 
@@ -248,7 +251,17 @@ def layer_fp8(x, w_r, w13, w2, dout, k, score, renorm, logit_bias=None, shared=N
     if z is None:
         z = o.router_logits(x, w_r, logit_bias)
     r = o.route(z, k, score, renorm)
+    if capacity is not None:
+        r = o.apply_capacity(r, capacity)
     off = r["offsets"]
+    # a dropped slot (dst_row -1) reads and writes an extra all-zero row past
+    # the kept rows, so combine, its backward and permute_bwd add nothing for it
+    n_rows = int(off[-1])
+    dst = np.where(r["dst_row"] < 0, n_rows, r["dst_row"])
+
+    def zero_row(a):
+        return np.concatenate([a, np.zeros((1, a.shape[1]))])
+
     w13d, w2d = rec("fwd1.B", q_weights(w13)), rec("fwd2.B", q_weights(w2))
     w13g, w2g = (q_weights(w13, "dgrad"), q_weights(w2, "dgrad")) if mx else (w13d, w2d)
     rec("dgrad1.B", w13g)
@@ -270,10 +283,11 @@ def layer_fp8(x, w_r, w13, w2, dout, k, score, renorm, logit_bias=None, shared=N
         abs_ = o.grouped_gemm_fwd(rec("s.fwd1.A", q_rows(x)), ws13d, all_rows)
         hs = rec("src.hs", o.swiglu(abs_))
         ys = o.grouped_gemm_fwd(rec("s.fwd2.A", q_rows(hs)), ws2d, all_rows)
-    out = o.unpermute_combine(y, r["topk_w"], r["dst_row"], ys)
+    out = o.unpermute_combine(zero_row(y), r["topk_w"], dst, ys)
 
     dout = o.f64(dout)
-    dy, dw = o.unpermute_combine_bwd(dout, y, r["topk_w"], r["dst_row"])
+    dy, dw = o.unpermute_combine_bwd(dout, zero_row(y), r["topk_w"], dst)
+    dy = dy[:n_rows]
     rec("src.dy", dy)
     dh = o.grouped_gemm_dgrad(rec("dgrad2.A", q_rows(dy)), w2g, off)
     dab = rec("src.dab", o.swiglu_bwd(dh, ab))
@@ -301,7 +315,7 @@ def layer_fp8(x, w_r, w13, w2, dout, k, score, renorm, logit_bias=None, shared=N
     dz = o.route_bwd(z, r["topk_idx"], r["topk_w"], dw, score, renorm)
     dWr, dxr = o.router_logits_bwd(x, w_r, dz)
     addends.append(dxr)
-    dx = o.permute_bwd(dxp, r["dst_row"], addends=tuple(addends))
+    dx = o.permute_bwd(zero_row(dxp), dst, addends=tuple(addends))
     res.update(out=out, dx=dx, d_logits=dz, dW_r=dWr, dW13=dW13, dW2=dW2, z=z, route=r)
     return res
 

@@ -159,6 +159,8 @@ SMALL_FP8 = inputs.LayerConfig("small_fp8_shared", T=400, d=256, E=8, k=2, f=256
 
 
 @pytest.mark.parametrize("cfg", [SMALL_FP8,
+                                 dataclasses.replace(SMALL_FP8, name="small_fp8_capacity",
+                                                     capacity_factor=0.8, bias="zipf"),
                                  dataclasses.replace(SMALL_FP8, name="small_fp8_softmax", fs=0,
                                                      score="softmax", bias="none", k=4)],
                          ids=lambda c: c.name)
@@ -174,7 +176,11 @@ def test_layer_fp8(gpu, cfg):
     bias = None if inp["logit_bias"] is None else inp["logit_bias"].numpy()
     ref = fp8.layer_fp8(np64(inp["x"]), inp["w_r"].numpy(), np64(inp["w13"]), np64(inp["w2"]),
                         np64(inp["dout"]), cfg.k, cfg.score, cfg.renorm, logit_bias=bias,
-                        shared=shared, z=layer.logits.cpu().numpy())
+                        shared=shared, z=layer.logits.cpu().numpy(),
+                        capacity=(oracle.capacity_of(cfg.capacity_factor, cfg.T, cfg.k, cfg.E)
+                                  if cfg.capacity_factor else None))
+    if cfg.capacity_factor:
+        assert (layer.dst_row < 0).sum() > 0  # some pairs are dropped
     assert_close("logits (oracle's own)", layer.logits,
                  oracle.router_logits(np64(inp["x"]), inp["w_r"].numpy(), bias), TOL["f32"])
     r = ref["route"]

@@ -235,6 +235,8 @@ SMALL_MX = inputs.LayerConfig("small_mxfp8_shared", T=1600, d=256, E=8, k=2, f=2
                          bias="none", k=4, T=800), False),
     (dataclasses.replace(SMALL_MX, name="small_mxfp8_zipf_recompute", bias="zipf",
                          score="softmax"), True),
+    (dataclasses.replace(SMALL_MX, name="small_mxfp8_capacity", bias="zipf", score="softmax",
+                         capacity_factor=0.8), False),
 ], ids=lambda c: c.name if hasattr(c, "name") else f"recompute={c}")
 def test_layer_mxfp8(gpu, cfg, recompute):
     print(f"mxfp8 layer {cfg.name} recompute={recompute}", flush=True)
@@ -249,7 +251,11 @@ def test_layer_mxfp8(gpu, cfg, recompute):
     bias = None if inp["logit_bias"] is None else inp["logit_bias"].numpy()
     ref = fp8.layer_fp8(np64(inp["x"]), inp["w_r"].numpy(), np64(inp["w13"]), np64(inp["w2"]),
                         np64(inp["dout"]), cfg.k, cfg.score, cfg.renorm, logit_bias=bias,
-                        shared=shared, recipe="mx", z=layer.logits.cpu().numpy())
+                        shared=shared, recipe="mx", z=layer.logits.cpu().numpy(),
+                        capacity=(oracle.capacity_of(cfg.capacity_factor, cfg.T, cfg.k, cfg.E)
+                                  if cfg.capacity_factor else None))
+    if cfg.capacity_factor:
+        assert (layer.dst_row < 0).sum() > 0  # some pairs are dropped
     assert_close("logits (oracle's own)", layer.logits,
                  oracle.router_logits(np64(inp["x"]), inp["w_r"].numpy(), bias), TOL["f32"])
     r = ref["route"]

@@ -156,6 +156,27 @@ def test_fp8_layer_chain_without_quantization_is_the_exact_layer():
             np.testing.assert_allclose(e[name], g[name], rtol=0, atol=1e-11, err_msg=name)
 
 
+@pytest.mark.parametrize("recipe", ["block", "mx"])
+def test_fp8_layer_unquantized_with_capacity_is_the_exact_layer(recipe):
+    """With capacity-limited dropping the grouped chain (kept rows only, dropped
+    pairs skipped in combine and its backward) equals the per-token layer that
+    skips the dropped pairs; the capacity is small enough that pairs drop."""
+    from test_oracle_layer import _make
+    x, w_r, w13, w2, b, shared, dout = _make(8, T=48, d=12, E=4, k=2, f=10, fs=6, bias=True)
+    cap = oracle.capacity_of(0.75, 48, 2, 4)
+    for score, renorm in [(oracle.SIGMOID, True), (oracle.SOFTMAX, False)]:
+        c = oracle.layer_forward(x, w_r, w13, w2, 2, score, renorm, logit_bias=b, shared=shared,
+                                 capacity=cap)
+        assert (c["route"]["dst_row"] < 0).sum() > 0
+        g = oracle.layer_backward(c, dout)
+        e = fp8.layer_fp8(x, w_r, w13, w2, dout, 2, score, renorm, logit_bias=b, shared=shared,
+                          quantize=False, recipe=recipe, capacity=cap)
+        np.testing.assert_array_equal(e["route"]["dst_row"], c["route"]["dst_row"])
+        np.testing.assert_allclose(e["out"], c["out"], rtol=0, atol=1e-12)
+        for name in ["dx", "d_logits", "dW_r", "dW13", "dW2", "dWs13", "dWs2"]:
+            np.testing.assert_allclose(e[name], g[name], rtol=0, atol=1e-11, err_msg=name)
+
+
 def test_fp8_layer_chain_close_to_exact_layer():
     """Sanity check of the chain's quantization error against the exact layer:
     E4M3 keeps 3 mantissa bits, so a few per cent of max|ref|, well below 20 %.
