@@ -120,6 +120,20 @@ __device__ __forceinline__ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) {
   return v < lo ? lo : (v > hi ? hi : v);
 }
 
+// The lane id through an empty asm: values computed from it are recomputed
+// where they are used instead of being hoisted out of the k loop, where
+// they would hold registers across it.  The tile epilogues whose hoisted
+// addresses pushed their kernel past 256 registers take it: the spill
+// reloads inside the k loop then waited on vmcnt, i.e. on the stage's own
+// prefetch DMA, and serialised the loads with the MFMAs.  Kernels that fit
+// keep the plain lane id (recomputing there changed their schedule for the
+// worse).
+__device__ __forceinline__ int opaque_lane() {
+  int v = static_cast<int>(threadIdx.x) & 63;
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // chunk swizzles: KC layout [row][8 chunks], NC layout [k][16 chunks]
 __device__ __forceinline__ int swz_kc(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int swz_nc(int kr) { return (kr & 3) << 2; }
@@ -1083,7 +1097,9 @@ __global__ __launch_bounds__(Cfg<WN>::THREADS, Cfg<WN>::WG_PER_CU) void gg_kerne
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      epilogue<MODE, BN>(p, cp_t, acc, lring + cp_slot * SB + wave * 4096, wm, wn, lane);
+      // blockwise fp8 row groups otherwise spill inside the k loop
+      epilogue<MODE, BN>(p, cp_t, acc, lring + cp_slot * SB + wave * 4096, wm, wn,
+                         Q == P_FP8 && MODE != WGRAD ? opaque_lane() : lane);
 #pragma unroll
       for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
@@ -1372,6 +1388,7 @@ __global__ __launch_bounds__(512, 1) void wgrad256_kernel(Params p) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
+      const int lane = Q == P_MX ? opaque_lane() : threadIdx.x & 63;  // MXFP8 spills otherwise
       const int64_t row_w = cp_t.row0 + wm * 64, col_w = cp_t.col0 + wn * 128;
       if (p.out_f32) {
         float* out = static_cast<float*>(p.C) + static_cast<int64_t>(cp_t.g) * K * N;
@@ -1712,6 +1729,8 @@ __global__ __launch_bounds__(512, 1) void rows256_kernel(Params p) {
       asm volatile("" ::: "memory");
       const int rows_w = cp_t.rows - wm * 64;  // valid rows of this wave
       if (rows_w > 0) {
+        // MXFP8 and the SwiGLU forward spill inside the k loop otherwise
+        const int lane = MX || MODE == FWD_SWIGLU ? opaque_lane() : threadIdx.x & 63;
         LDS_AS char* stg = lring + cp_slot * STAGE + wave * 8192;
         bf16_t* out = static_cast<bf16_t*>(p.C);
         const int64_t row_w = cp_t.row0 + wm * 64, col_w = cp_t.col0 + wn * 128;
