@@ -49,7 +49,7 @@ typedef enum {
   MOE_ERR_NULL = -1,        /* a required pointer is NULL */
   MOE_ERR_SHAPE = -2,       /* a size is negative or inconsistent */
   MOE_ERR_DTYPE = -3,       /* unknown dtype or unsupported dtype combination */
-  MOE_ERR_UNSUPPORTED = -4, /* valid request outside this build's limits */
+  MOE_ERR_UNSUPPORTED = -4, /* valid request outside the library's limits */
   MOE_ERR_WORKSPACE = -5,   /* workspace missing or too small */
   MOE_ERR_HIP = -6          /* a HIP runtime call or launch failed */
 } moe_status;
