@@ -388,7 +388,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures the single-GPU hot path only: the library has no multi-GPU path "
+        print("bench.py measures the single-GPU hot path only: the library runs on one GPU "
               "(no collectives); run it with --gpus 1.", file=sys.stderr)
         return 2
 
