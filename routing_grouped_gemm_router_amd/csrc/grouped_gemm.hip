@@ -302,14 +302,15 @@ __device__ __forceinline__ void tile_in_group(uint32_t tl, uint32_t mt_g, uint32
 
 // Of a paired launch, the 256 x 256 tiling does the work when it needs at most
 // 20/31 of the row tiles of the 128-row tiling (plain and SwiGLU epilogues),
-// or at most 10/19 of them (SwiGLU backward).  A 256 x 256 tile costs about
+// or at most 10/17 of them (SwiGLU backward).  A 256 x 256 tile costs about
 // 1.8 times a 128 x 256 one and its ragged last tile rather less (a wave with
 // no rows idles); over 256 groups with 7168 x 2048 and 4096 x 7168 weights
 // the 256-row tiling of the plain epilogue measured faster at every tile
 // ratio from 1.59 up and slower at 1.5 and below.  The SwiGLU forward ties at
 // a ratio of 1.56 (256 groups) and is 10 % faster at about 1.8 (128 groups
-// of 4096 x 3072); the SwiGLU backward was 9 % slower at 1.56 and 12 %
-// faster at 2 (one group of 8192 rows).  MXFP8 moves twice the FLOPs
+// of 4096 x 3072); the SwiGLU backward is 6 % slower at 1.57, 9 % faster at
+// 1.84 (the same 128 groups) and 12 % faster at 2 (one group of 8192 rows),
+// a crossover near 1.7.  MXFP8 moves twice the FLOPs
 // per operand byte of bf16, so its 128-row tiles are held back by the LDS
 // DMA rate: the 256-row tiles ran 1.2 times faster per executed FLOP there,
 // which pays for the larger ragged tails from a tile ratio of about 1.65 in
@@ -317,7 +318,7 @@ __device__ __forceinline__ void tile_in_group(uint32_t tl, uint32_t mt_g, uint32
 template <int MODE, int Q>
 __device__ __forceinline__ bool rows256_preferred(int t128, int t256) {
   if (Q == P_MX) return 20LL * t128 >= 33LL * t256;
-  if (MODE == DGRAD_SWIGLU_BWD) return 10LL * t128 >= 19LL * t256;
+  if (MODE == DGRAD_SWIGLU_BWD) return 10LL * t128 >= 17LL * t256;
   return 20LL * t128 >= 31LL * t256;
 }
 
