@@ -143,6 +143,9 @@ def test_zero_sized_calls_are_noops(lib):
     assert lib.moe_swiglu(None, 1, 0, 64, None, None) == 0
     assert lib.moe_router_logits(None, 1, None, None, 0, 64, 8, None, None) == 0
     assert lib.moe_route_topk_bwd(None, None, None, None, 0, 8, 2, 0, 1, None, None) == 0
+    assert lib.moe_scatter_quant_mxfp8(None, 0, 128, None, 8, None, 4, 40, None, None, None) == 0
+    assert lib.moe_scatter_quant_mxfp8(None, 10, 128, None, 8, None, 4, 0, None, None, None) == 0
+    assert lib.moe_permute_quant_mxfp8(None, 10, 128, None, None, 4, 0, None, None, None) == 0
 
 
 def test_workspace_size_grows_with_tokens(lib):
