@@ -30,6 +30,16 @@ def test_more_than_one_gpu_is_refused(gpus):
     assert r.stdout == ""
 
 
+def test_vendor_comparison_refuses_low_precision_layers():
+    """The vendor grouped-GEMM comparison times bf16 products only; an fp8
+    workload is refused before anything touches a GPU."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--config", "deepseek_v3_fp8",
+                        "--vendor-grouped-mm"], capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "bf16" in r.stderr
+    assert r.stdout == ""
+
+
 def test_traffic_is_used_only_for_the_measured_sources(tmp_path):
     bench = _bench_module()
     # a private tree: one kernel source and a traffic record for it
